@@ -1,0 +1,214 @@
+"""Plain fp64 CPU oracle of one SVD-decomposed transformer layer.
+
+TEST INFRASTRUCTURE. Only tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg may import this module; the library's HIP path never
+imports, links or calls anything here, and this module imports nothing from
+the library.
+
+It is written from "DeInfer: Efficient Parallel Inferencing for Decomposed
+Large Language Models" (Huang, Huang, Liao, Wen; DAC '26):
+  * section 2.1, Eq. (1): W ~ A B, A = U_k sqrt(S_k) (m x k),
+    B = sqrt(S_k) V_k^T (k x n); a projection y = x W becomes y = (x A) B.
+  * section 2.1: the low-rank intermediates of the K and V pairs are the
+    KV cache.
+  * section 4.1 / Fig. 3: down factors of q, k, v (and gate, up) read the
+    same normalised activations; the k and v latents are stored as cache.
+  * section 4.2 / Fig. 4(b): attention rebuilds K and V by multiplying the
+    cached latents with the up factors, applies rotary position embedding to
+    the rebuilt keys, then attends.
+  * Table 2: MHA, MQA and GQA attention, GLU-based MLP, rotary embedding;
+    Fig. 3(b) shows SiLU as the MLP activation.
+
+Readings where the paper is silent (each also listed in the design notes):
+  * row-vector convention, head-major projection outputs (head j occupies
+    columns [j*d, (j+1)*d)); GQA maps query head h to kv head
+    h // (n_q / n_kv);
+  * LLaMA pre-norm block: RMSNorm -> attention -> residual -> RMSNorm ->
+    SwiGLU MLP (silu(x A_g B_g) * (x A_u B_u)) -> residual;
+  * RoPE pairs (i, i + d/2) rotated by pos * theta^(-2i/d), applied to the
+    query and to the rebuilt keys, never to the cached latents; theta == 0
+    disables it;
+  * softmax scale 1/sqrt(d) unless given; causal: a query at position p sees
+    keys 0..p.
+
+Every function upcasts its inputs to float64 and never rounds internally.
+Parity of every function is pinned by tests/test_oracle_pins.py.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+F64 = np.float64
+
+
+def _f(a) -> np.ndarray:
+    return np.asarray(a, dtype=F64)
+
+
+# ----------------------------------------------------------------------------
+# Factor pairs (section 2.1, Eq. (1))
+# ----------------------------------------------------------------------------
+def svd_factors(W, k: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Truncated-SVD factor pair of W (m x n): A = U_k sqrt(S_k),
+    B = sqrt(S_k) V_k^T, so that A @ B is the best rank-k approximation."""
+    U, s, Vt = np.linalg.svd(_f(W), full_matrices=False)
+    root = np.sqrt(s[:k])
+    return U[:, :k] * root[None, :], root[:, None] * Vt[:k, :]
+
+
+def lowrank_linear(x, A, B) -> np.ndarray:
+    """y = (x A) B for row vectors x [..., m], A [m, k], B [k, n]."""
+    return (_f(x) @ _f(A)) @ _f(B)
+
+
+# ----------------------------------------------------------------------------
+# Low-rank KV cache (section 2.1; section 4.1)
+# ----------------------------------------------------------------------------
+def kv_append(x, A_k, A_v, ck, cv, past_lens) -> Tuple[np.ndarray, np.ndarray]:
+    """Store the k/v latents of T new tokens per sequence.
+
+    x [Bsz, T, m]; ck [Bsz, L_max, r_k]; cv [Bsz, L_max, r_v];
+    past_lens [Bsz]. Row past_lens[b] + t of ck[b] becomes x[b, t] A_k and the
+    same row of cv[b] becomes x[b, t] A_v. Returns updated float64 copies;
+    every other row is copied unchanged."""
+    x = _f(x)
+    ck2, cv2 = _f(ck).copy(), _f(cv).copy()
+    Ak, Av = _f(A_k), _f(A_v)
+    Bsz, T, _ = x.shape
+    for b in range(Bsz):
+        p = int(past_lens[b])
+        for t in range(T):
+            ck2[b, p + t] = x[b, t] @ Ak
+            cv2[b, p + t] = x[b, t] @ Av
+    return ck2, cv2
+
+
+# ----------------------------------------------------------------------------
+# Rotary position embedding (Table 2; section 4.2 applies it to rebuilt keys)
+# ----------------------------------------------------------------------------
+def rope_frequencies(d: int, theta: float) -> np.ndarray:
+    i = np.arange(d // 2, dtype=F64)
+    return float(theta) ** (-2.0 * i / d)
+
+
+def rope(v, pos, theta: float) -> np.ndarray:
+    """Rotate pairs (v_i, v_{i+d/2}) of the last axis by angle pos * w_i,
+    w_i = theta^(-2i/d). pos broadcasts against v.shape[:-1]. theta == 0
+    returns v unchanged."""
+    v = _f(v)
+    if theta == 0:
+        return v.copy()
+    d = v.shape[-1]
+    half = d // 2
+    ang = np.asarray(pos, dtype=F64)[..., None] * rope_frequencies(d, theta)
+    c, s = np.cos(ang), np.sin(ang)
+    lo, hi = v[..., :half], v[..., half:]
+    return np.concatenate([lo * c - hi * s, lo * s + hi * c], axis=-1)
+
+
+# ----------------------------------------------------------------------------
+# Attention over rebuilt K/V (section 4.2)
+# ----------------------------------------------------------------------------
+def reconstruct_kv(ck_b, cv_b, B_k, B_v, n_kv: int, d: int,
+                   theta: float) -> Tuple[np.ndarray, np.ndarray]:
+    """K = RoPE(C_k B_k) with row index as position, V = C_v B_v, both
+    reshaped to [L, n_kv, d]."""
+    ck_b, cv_b = _f(ck_b), _f(cv_b)
+    L = ck_b.shape[0]
+    K = (ck_b @ _f(B_k)).reshape(L, n_kv, d)
+    K = rope(K, np.arange(L, dtype=F64)[:, None], theta)
+    V = (cv_b @ _f(B_v)).reshape(L, n_kv, d)
+    return K, V
+
+
+def softmax_attend(q_rot, q_pos, K, V, sm_scale: float) -> np.ndarray:
+    """q_rot [T, n_q, d] (already rotated), q_pos [T]; K, V [L, n_kv, d].
+    Query t attends keys 0..q_pos[t] with a max-subtracted softmax."""
+    T, n_q, d = q_rot.shape
+    n_kv = K.shape[1]
+    group = n_q // n_kv
+    out = np.zeros((T, n_q, d), dtype=F64)
+    for t in range(T):
+        p = int(q_pos[t])
+        for h in range(n_q):
+            g = h // group
+            s = (K[:p + 1, g, :] @ q_rot[t, h]) * sm_scale
+            s = s - s.max()
+            w = np.exp(s)
+            w = w / w.sum()
+            out[t, h] = w @ V[:p + 1, g, :]
+    return out
+
+
+def _scale(d: int, sm_scale: Optional[float]) -> float:
+    return 1.0 / np.sqrt(d) if sm_scale is None else float(sm_scale)
+
+
+def attn_prefill(q, ck, cv, B_k, B_v, past_lens, n_kv: int, theta: float,
+                 sm_scale: Optional[float] = None) -> np.ndarray:
+    """q [Bsz, T, n_q, d] un-rotated. Query t of sequence b sits at position
+    past_lens[b] + t and sees cache rows 0..past_lens[b] + t (those rows must
+    already hold the latents). Returns [Bsz, T, n_q, d]."""
+    q = _f(q)
+    Bsz, T, n_q, d = q.shape
+    out = np.zeros_like(q)
+    for b in range(Bsz):
+        L = int(past_lens[b]) + T
+        K, V = reconstruct_kv(_f(ck[b])[:L], _f(cv[b])[:L], B_k, B_v, n_kv, d, theta)
+        pos = int(past_lens[b]) + np.arange(T)
+        q_rot = rope(q[b], pos[:, None], theta)
+        out[b] = softmax_attend(q_rot, pos, K, V, _scale(d, sm_scale))
+    return out
+
+
+def attn_decode(q, ck, cv, B_k, B_v, ctx_lens, n_kv: int, theta: float,
+                sm_scale: Optional[float] = None) -> np.ndarray:
+    """q [Bsz, n_q, d] un-rotated; sequence b has ctx_lens[b] cached rows and
+    its query sits at position ctx_lens[b] - 1. Returns [Bsz, n_q, d]."""
+    q = _f(q)
+    past = np.asarray(ctx_lens, dtype=np.int64) - 1
+    return attn_prefill(q[:, None], ck, cv, B_k, B_v, past, n_kv, theta,
+                        sm_scale)[:, 0]
+
+
+# ----------------------------------------------------------------------------
+# The layer
+# ----------------------------------------------------------------------------
+def rmsnorm(x, gamma, eps: float) -> np.ndarray:
+    x = _f(x)
+    r = np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    y = x / r
+    return y if gamma is None else y * _f(gamma)
+
+
+def silu(z) -> np.ndarray:
+    z = _f(z)
+    return z / (1.0 + np.exp(-z))
+
+
+def decomposed_layer(factors: Dict[str, Tuple[np.ndarray, np.ndarray]], x, ck, cv,
+                     past_lens, n_q: int, n_kv: int, head_dim: int,
+                     rope_theta: float, rms_eps: float, attn_norm=None,
+                     mlp_norm=None) -> Dict[str, np.ndarray]:
+    """Forward pass of one decomposed pre-norm layer for T new tokens per
+    sequence. x [Bsz, T, h]; the T new latents are stored at rows
+    past_lens[b] .. past_lens[b] + T - 1 before attention reads them.
+
+    Returns y (layer output), x2 (residual stream after attention), attn
+    (attention output before the o pair) and the updated caches."""
+    x = _f(x)
+    Bsz, T, h = x.shape
+    F = {p: (_f(A), _f(B)) for p, (A, B) in factors.items()}
+    a = rmsnorm(x, attn_norm, rms_eps)
+    ck2, cv2 = kv_append(a, F["k"][0], F["v"][0], ck, cv, past_lens)
+    q = lowrank_linear(a, *F["q"]).reshape(Bsz, T, n_q, head_dim)
+    att = attn_prefill(q, ck2, cv2, F["k"][1], F["v"][1], past_lens, n_kv,
+                       rope_theta)
+    att = att.reshape(Bsz, T, n_q * head_dim)
+    x2 = x + lowrank_linear(att, *F["o"])
+    b2 = rmsnorm(x2, mlp_norm, rms_eps)
+    hidden = silu(lowrank_linear(b2, *F["gate"])) * lowrank_linear(b2, *F["up"])
+    y = x2 + lowrank_linear(hidden, *F["down"])
+    return {"y": y, "x2": x2, "attn": att, "ck": ck2, "cv": cv2}
