@@ -1,0 +1,186 @@
+/*
+ * dl.h -- C ABI of the decomposed-layer forward pass on one MI355X (gfx950).
+ *
+ * The method is the one of "DeInfer: Efficient Parallel Inferencing for
+ * Decomposed Large Language Models" (Huang, Huang, Liao, Wen; DAC '26):
+ *   - section 2.1, Eq. (1): every projection W (m x n) is replaced by a factor
+ *     pair A (m x k), B (k x n), W ~ A B, so a row vector maps as
+ *     y = (x A) B;
+ *   - section 2.1: the low-rank intermediates x A_k and x A_v of the key and
+ *     value pairs are stored as the KV cache ("low-rank cache");
+ *   - section 4.2: attention rebuilds K = C_k B_k and V = C_v B_v from the
+ *     cache, applies rotary position embedding to the rebuilt keys, then
+ *     attends;
+ *   - Table 2: MHA / MQA / GQA attention, GLU-based MLP, rotary embedding.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are dense, row-major, contiguous. Every pointer argument is a
+ *     device pointer owned by the caller, 16-byte aligned.
+ *   - dtype DL_F32: every tensor is float32 and arithmetic is float32.
+ *     dtype DL_BF16: activations, factors, caches and outputs are bfloat16,
+ *     products accumulate in float32; intermediates may be rounded to bf16.
+ *   - Outputs have the dtype of the inputs (bf16 stores round to nearest
+ *     even), except x2_out of dl_decomposed_layer_fwd which is float32.
+ *   - Projection outputs are head-major: head j owns columns [j*d, (j+1)*d).
+ *     Query head h reads kv head h / (n_q / n_kv).
+ *   - Rotary embedding rotates the pair (v_i, v_{i+d/2}) by the angle
+ *     pos * theta^(-2i/d). It is applied to the query and to rebuilt keys,
+ *     never to the cache. rope_theta == 0 disables it.
+ *   - sm_scale == 0 selects 1/sqrt(d).
+ *   - `stream` is a hipStream_t (NULL = the null stream). Every call only
+ *     enqueues work on it and returns without synchronising. The library
+ *     never allocates, frees or synchronises device memory.
+ *   - `ws` is a caller-owned device workspace of at least the size the
+ *     matching *_workspace() query returns; its contents on entry are
+ *     ignored and on return are unspecified. Calls that overlap in time
+ *     must not share a workspace.
+ *   - Host-side validation runs before any launch. On failure nothing is
+ *     enqueued and a status is returned; dl_last_error() then describes it.
+ *   - Device-resident lengths (past_lens, ctx_lens) are not checked (that
+ *     would need a synchronisation); their stated ranges are preconditions.
+ */
+#ifndef DL_H
+#define DL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DL_OK = 0,
+  DL_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, n_q % n_kv != 0, bad dtype */
+  DL_ERR_UNSUPPORTED = 2,  /* a shape this build does not implement (see each call) */
+  DL_ERR_ALIGNMENT = 3,    /* a tensor pointer is not 16-byte aligned */
+  DL_ERR_WORKSPACE = 4,    /* ws is NULL or ws_bytes is below the required size */
+  DL_ERR_HIP = 5           /* a HIP launch failed; dl_last_error() has the text */
+} dl_status;
+
+typedef enum { DL_F32 = 0, DL_BF16 = 1 } dl_dtype;
+
+/* Description of the last non-OK status returned on the calling thread. */
+const char *dl_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Factor-pair projection -- section 2.1, Eq. (1).
+ *   y[M, n] = (x[M, m] A[m, k]) B[k, n]
+ * The rank-k intermediate x A lives only in the workspace. For M <= 64 the
+ * pair runs as two weight-streaming MFMA GEMV passes; for larger M as two
+ * MFMA GEMMs.
+ * DL_BF16 requires m, k, n to be multiples of 64 (else UNSUPPORTED).
+ * ------------------------------------------------------------------------ */
+size_t dl_lowrank_linear_workspace(int64_t M, int64_t m, int64_t k, int64_t n,
+                                   dl_dtype dt);
+dl_status dl_lowrank_linear(const void *x, const void *A, const void *B, void *y,
+                            int64_t M, int64_t m, int64_t k, int64_t n,
+                            dl_dtype dt, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Low-rank KV-cache append -- section 2.1 (the k/v latents are the cache)
+ * and section 4.1 (they are stored as KV cache).
+ *   Ck[b, past_lens[b] + t, :] = x[b, t, :] A_k     x   : [Bsz, T, m]
+ *   Cv[b, past_lens[b] + t, :] = x[b, t, :] A_v     A_k : [m, r_k], A_v: [m, r_v]
+ *                                                    Ck  : [Bsz, L_max, r_k]
+ *                                                    Cv  : [Bsz, L_max, r_v]
+ * past_lens: device int32 [Bsz]; precondition past_lens[b] + T <= L_max.
+ * No other cache row is written.
+ * DL_BF16 requires m, r_k, r_v to be multiples of 64.
+ * ------------------------------------------------------------------------ */
+size_t dl_kv_append_workspace(int64_t Bsz, int64_t T, int64_t m, int64_t r_k,
+                              int64_t r_v, dl_dtype dt);
+dl_status dl_lowrank_kv_append(const void *x, const void *A_k, const void *A_v,
+                               void *Ck, void *Cv, const int32_t *past_lens,
+                               int64_t Bsz, int64_t T, int64_t m, int64_t r_k,
+                               int64_t r_v, int64_t L_max, dl_dtype dt,
+                               void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Decode attention over the low-rank cache -- section 4.2.
+ *   q   : [Bsz, n_q, d] un-rotated queries
+ *   Ck  : [Bsz, L_max, r_k], Cv: [Bsz, L_max, r_v] latent caches
+ *   B_k : [r_k, n_kv*d], B_v: [r_v, n_kv*d] up factors of the k and v pairs
+ *   ctx_lens: device int32 [Bsz], 1 <= ctx_lens[b] <= L_max
+ *   out : [Bsz, n_q, d]
+ * Sequence b attends rows 0 .. ctx_lens[b]-1 and its query sits at position
+ * ctx_lens[b]-1. K and V tiles are rebuilt on chip (never written to memory),
+ * keys are rotated by their row index, softmax is computed online.
+ * DL_BF16 requires d in {64, 128}, r_k and r_v multiples of 64 and
+ * n_q / n_kv <= 16. DL_F32 requires even d <= 256.
+ * ------------------------------------------------------------------------ */
+size_t dl_attn_decode_workspace(int64_t Bsz, int64_t n_q, int64_t n_kv,
+                                int64_t d, int64_t r_k, int64_t r_v,
+                                int64_t L_max, dl_dtype dt);
+dl_status dl_lowrank_attn_decode(const void *q, const void *Ck, const void *Cv,
+                                 const void *B_k, const void *B_v,
+                                 const int32_t *ctx_lens, void *out,
+                                 int64_t Bsz, int64_t n_q, int64_t n_kv,
+                                 int64_t d, int64_t r_k, int64_t r_v,
+                                 int64_t L_max, float sm_scale,
+                                 float rope_theta, dl_dtype dt, void *ws,
+                                 size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Causal prefill attention over the low-rank cache -- section 4.2.
+ *   q   : [Bsz, T, n_q, d] un-rotated; out: [Bsz, T, n_q, d]
+ * Query t of sequence b sits at position past_lens[b] + t and attends rows
+ * 0 .. past_lens[b] + t, which must already hold the latents (append
+ * first). Precondition past_lens[b] + T <= L_max. Same shape rules as
+ * decode.
+ * ------------------------------------------------------------------------ */
+size_t dl_attn_prefill_workspace(int64_t Bsz, int64_t T, int64_t n_q,
+                                 int64_t n_kv, int64_t d, int64_t r_k,
+                                 int64_t r_v, int64_t L_max, dl_dtype dt);
+dl_status dl_lowrank_attn_prefill(const void *q, const void *Ck, const void *Cv,
+                                  const void *B_k, const void *B_v,
+                                  const int32_t *past_lens, void *out,
+                                  int64_t Bsz, int64_t T, int64_t n_q,
+                                  int64_t n_kv, int64_t d, int64_t r_k,
+                                  int64_t r_v, int64_t L_max, float sm_scale,
+                                  float rope_theta, dl_dtype dt, void *ws,
+                                  size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * One decomposed pre-norm transformer layer (LLaMA block; the paper names
+ * no norm or residual, this is the plain reading of Fig. 3 on a LLaMA
+ * model):
+ *   a   = RMSNorm(x) * attn_norm
+ *   Ck/Cv rows past..past+T-1 = a A_k, a A_v            (append)
+ *   q   = (a A_q) B_q ; o = attention(q, Ck, Cv, B_k, B_v)
+ *   x2  = x + (o A_o) B_o
+ *   b   = RMSNorm(x2) * mlp_norm
+ *   y   = x2 + ((silu((b A_gate) B_gate) * ((b A_up) B_up)) A_down) B_down
+ * x, y: [Bsz, T, hidden]. T == 1 uses decode attention (query at position
+ * past_lens[b]), T > 1 causal prefill attention. past_lens is not advanced
+ * (the caller does). x2_out (optional, float32 [Bsz, T, hidden]) receives
+ * x2. Factor shapes follow dl_factor; norm gains may be NULL (= 1).
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  const void *A;   /* [m, k] */
+  const void *B;   /* [k, n] */
+  int64_t k;
+} dl_factor;
+
+typedef struct {
+  int64_t hidden, n_q, n_kv, head_dim, ffn;
+  dl_factor q, k, v, o, gate, up, down;
+  const void *attn_norm;  /* [hidden] or NULL */
+  const void *mlp_norm;   /* [hidden] or NULL */
+  float rms_eps;
+  float rope_theta;
+  dl_dtype dt;
+} dl_layer;
+
+size_t dl_layer_workspace(const dl_layer *L, int64_t Bsz, int64_t T,
+                          int64_t L_max);
+dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y,
+                                  void *x2_out, void *Ck, void *Cv,
+                                  const int32_t *past_lens, int64_t Bsz,
+                                  int64_t T, int64_t L_max, void *ws,
+                                  size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DL_H */

@@ -1,0 +1,235 @@
+"""Thin Python binding of libdlayer.so (the C ABI in include/dl.h).
+
+Argument marshalling only: every function here checks tensor placement,
+allocates the caller-side workspace with torch, and calls the C entry point
+of the same name on the current torch stream. All arithmetic runs in the
+library's HIP kernels. If the library is not built or cannot be loaded, the
+functions raise; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdlayer.so")
+
+DL_F32, DL_BF16 = 0, 1
+STATUS = {0: "DL_OK", 1: "DL_ERR_INVALID_ARG", 2: "DL_ERR_UNSUPPORTED", 3: "DL_ERR_ALIGNMENT",
+          4: "DL_ERR_WORKSPACE", 5: "DL_ERR_HIP"}
+
+EXPORTS = (
+    "dl_last_error",
+    "dl_lowrank_linear_workspace", "dl_lowrank_linear",
+    "dl_kv_append_workspace", "dl_lowrank_kv_append",
+    "dl_attn_decode_workspace", "dl_lowrank_attn_decode",
+    "dl_attn_prefill_workspace", "dl_lowrank_attn_prefill",
+    "dl_layer_workspace", "dl_decomposed_layer_fwd",
+)
+
+
+class DLError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class Factor(ctypes.Structure):
+    _fields_ = [("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("k", ctypes.c_int64)]
+
+
+class Layer(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int64), ("n_q", ctypes.c_int64), ("n_kv", ctypes.c_int64),
+                ("head_dim", ctypes.c_int64), ("ffn", ctypes.c_int64),
+                ("q", Factor), ("k", Factor), ("v", Factor), ("o", Factor),
+                ("gate", Factor), ("up", Factor), ("down", Factor),
+                ("attn_norm", ctypes.c_void_p), ("mlp_norm", ctypes.c_void_p),
+                ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
+                ("dt", ctypes.c_int)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+_i64, _vp, _sz, _f = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
+
+
+def load() -> ctypes.CDLL:
+    """Load libdlayer.so (built in-tree by rank_decomposed_linear_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m rank_decomposed_linear_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.dl_last_error.restype = ctypes.c_char_p
+    lib.dl_last_error.argtypes = []
+    lib.dl_lowrank_linear_workspace.restype = _sz
+    lib.dl_lowrank_linear_workspace.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int]
+    lib.dl_lowrank_linear.restype = ctypes.c_int
+    lib.dl_lowrank_linear.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int,
+                                      _vp, _sz, _vp]
+    lib.dl_kv_append_workspace.restype = _sz
+    lib.dl_kv_append_workspace.argtypes = [_i64, _i64, _i64, _i64, _i64, ctypes.c_int]
+    lib.dl_lowrank_kv_append.restype = ctypes.c_int
+    lib.dl_lowrank_kv_append.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                         _i64, _i64, ctypes.c_int, _vp, _sz, _vp]
+    lib.dl_attn_decode_workspace.restype = _sz
+    lib.dl_attn_decode_workspace.argtypes = [_i64] * 7 + [ctypes.c_int]
+    lib.dl_lowrank_attn_decode.restype = ctypes.c_int
+    lib.dl_lowrank_attn_decode.argtypes = [_vp] * 7 + [_i64] * 7 + [_f, _f, ctypes.c_int, _vp,
+                                                                     _sz, _vp]
+    lib.dl_attn_prefill_workspace.restype = _sz
+    lib.dl_attn_prefill_workspace.argtypes = [_i64] * 8 + [ctypes.c_int]
+    lib.dl_lowrank_attn_prefill.restype = ctypes.c_int
+    lib.dl_lowrank_attn_prefill.argtypes = [_vp] * 7 + [_i64] * 8 + [_f, _f, ctypes.c_int, _vp,
+                                                                      _sz, _vp]
+    lib.dl_layer_workspace.restype = _sz
+    lib.dl_layer_workspace.argtypes = [ctypes.POINTER(Layer), _i64, _i64, _i64]
+    lib.dl_decomposed_layer_fwd.restype = ctypes.c_int
+    lib.dl_decomposed_layer_fwd.argtypes = [ctypes.POINTER(Layer), _vp, _vp, _vp, _vp, _vp, _vp,
+                                            _i64, _i64, _i64, _vp, _sz, _vp]
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise DLError(status, load().dl_last_error().decode())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DL_BF16
+    if t.dtype == torch.float32:
+        return DL_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def lowrank_linear(x, A, B, y=None, ws=None):
+    """y = (x A) B for x [M, m], A [m, k], B [k, n] (section 2.1, Eq. (1))."""
+    lib = load()
+    M, m = x.shape
+    k, n = B.shape
+    dt = _dt(x)
+    if y is None:
+        y = torch.empty((M, n), dtype=x.dtype, device=x.device)
+    need = lib.dl_lowrank_linear_workspace(M, m, k, n, dt)
+    ws = ws if ws is not None else _ws(need, x.device)
+    _check(lib.dl_lowrank_linear(_ptr(x), _ptr(A), _ptr(B), _ptr(y), M, m, k, n, dt, _ptr(ws),
+                                 ws.numel(), _stream(x.device)))
+    return y
+
+
+def lowrank_kv_append(x, A_k, A_v, ck, cv, past_lens, ws=None):
+    """ck[b, past[b]+t] = x[b, t] A_k and cv likewise; x [Bsz, T, m]."""
+    lib = load()
+    Bsz, T, m = x.shape
+    r_k, r_v, L_max = A_k.shape[1], A_v.shape[1], ck.shape[1]
+    dt = _dt(x)
+    need = lib.dl_kv_append_workspace(Bsz, T, m, r_k, r_v, dt)
+    ws = ws if ws is not None else _ws(need, x.device)
+    _check(lib.dl_lowrank_kv_append(_ptr(x), _ptr(A_k), _ptr(A_v), _ptr(ck), _ptr(cv),
+                                    _ptr(past_lens), Bsz, T, m, r_k, r_v, L_max, dt, _ptr(ws),
+                                    ws.numel(), _stream(x.device)))
+
+
+def lowrank_attn_decode(q, ck, cv, B_k, B_v, ctx_lens, n_kv, sm_scale=0.0, rope_theta=0.0,
+                        out=None, ws=None):
+    """q [Bsz, n_q, d] -> out [Bsz, n_q, d] (section 4.2)."""
+    lib = load()
+    Bsz, n_q, d = q.shape
+    L_max, r_k, r_v = ck.shape[1], ck.shape[2], cv.shape[2]
+    dt = _dt(q)
+    if out is None:
+        out = torch.empty_like(q)
+    need = lib.dl_attn_decode_workspace(Bsz, n_q, n_kv, d, r_k, r_v, L_max, dt)
+    ws = ws if ws is not None else _ws(need, q.device)
+    _check(lib.dl_lowrank_attn_decode(_ptr(q), _ptr(ck), _ptr(cv), _ptr(B_k), _ptr(B_v),
+                                      _ptr(ctx_lens), _ptr(out), Bsz, n_q, n_kv, d, r_k, r_v,
+                                      L_max, sm_scale, rope_theta, dt, _ptr(ws), ws.numel(),
+                                      _stream(q.device)))
+    return out
+
+
+def lowrank_attn_prefill(q, ck, cv, B_k, B_v, past_lens, n_kv, sm_scale=0.0, rope_theta=0.0,
+                         out=None, ws=None):
+    """q [Bsz, T, n_q, d] -> out [Bsz, T, n_q, d], causal (section 4.2)."""
+    lib = load()
+    Bsz, T, n_q, d = q.shape
+    L_max, r_k, r_v = ck.shape[1], ck.shape[2], cv.shape[2]
+    dt = _dt(q)
+    if out is None:
+        out = torch.empty_like(q)
+    need = lib.dl_attn_prefill_workspace(Bsz, T, n_q, n_kv, d, r_k, r_v, L_max, dt)
+    ws = ws if ws is not None else _ws(need, q.device)
+    _check(lib.dl_lowrank_attn_prefill(_ptr(q), _ptr(ck), _ptr(cv), _ptr(B_k), _ptr(B_v),
+                                       _ptr(past_lens), _ptr(out), Bsz, T, n_q, n_kv, d, r_k, r_v,
+                                       L_max, sm_scale, rope_theta, dt, _ptr(ws), ws.numel(),
+                                       _stream(q.device)))
+    return out
+
+
+class DecomposedLayer:
+    """Device-resident factor pairs of one layer plus the dl_layer descriptor.
+
+    factors: dict name -> (A [m, k], B [k, n]) torch tensors on the GPU for
+    q, k, v, o, gate, up, down; norm gains optional."""
+
+    NAMES = ("q", "k", "v", "o", "gate", "up", "down")
+
+    def __init__(self, factors, hidden, n_q, n_kv, head_dim, ffn, rope_theta, rms_eps=1e-5,
+                 attn_norm=None, mlp_norm=None):
+        self.factors = factors
+        self.attn_norm, self.mlp_norm = attn_norm, mlp_norm
+        dt = _dt(factors["q"][0])
+        L = Layer()
+        L.hidden, L.n_q, L.n_kv, L.head_dim, L.ffn = hidden, n_q, n_kv, head_dim, ffn
+        for nm in self.NAMES:
+            A, B = factors[nm]
+            setattr(L, nm, Factor(_ptr(A), _ptr(B), A.shape[1]))
+        L.attn_norm = _ptr(attn_norm)
+        L.mlp_norm = _ptr(mlp_norm)
+        L.rms_eps = rms_eps
+        L.rope_theta = rope_theta
+        L.dt = dt
+        self.desc = L
+        self.device = factors["q"][0].device
+
+    def workspace_bytes(self, Bsz, T, L_max) -> int:
+        return load().dl_layer_workspace(ctypes.byref(self.desc), Bsz, T, L_max)
+
+    def forward(self, x, ck, cv, past_lens, y=None, x2_out=None, ws=None, stream=None):
+        """y = layer(x) for x [Bsz, T, hidden]; appends T latent rows per
+        sequence at past_lens (not advanced)."""
+        lib = load()
+        Bsz, T, _ = x.shape
+        L_max = ck.shape[1]
+        if y is None:
+            y = torch.empty_like(x)
+        if ws is None:
+            ws = _ws(self.workspace_bytes(Bsz, T, L_max), x.device)
+        s = stream.cuda_stream if stream is not None else _stream(x.device)
+        _check(lib.dl_decomposed_layer_fwd(ctypes.byref(self.desc), _ptr(x), _ptr(y),
+                                           _ptr(x2_out), _ptr(ck), _ptr(cv), _ptr(past_lens),
+                                           Bsz, T, L_max, _ptr(ws), ws.numel(), s))
+        return y

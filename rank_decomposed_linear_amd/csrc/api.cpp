@@ -1,0 +1,954 @@
+// C ABI of the decomposed-layer library: host-side validation, workspace
+// carving and the launch sequences of the five entry points declared in
+// include/dl.h.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <algorithm>
+#include <string>
+
+#include "../../include/dl.h"
+#include "common.h"
+#include "kernels.h"
+
+using namespace dl;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dl_status fail(dl_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+#define DL_CHECK(cond, st, ...) \
+  do {                          \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+#define DL_HIP(expr)                                                                   \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess) return fail(DL_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Bump allocator over the caller's workspace. With base == nullptr it only
+// measures.
+struct Carver {
+  char *base;
+  size_t off = 0;
+  explicit Carver(void *b) : base(static_cast<char *>(b)) {}
+  template <typename T>
+  T *take(size_t count) {
+    T *p = base ? reinterpret_cast<T *>(base + off) : nullptr;
+    off = align_up(off + count * sizeof(T));
+    return p;
+  }
+};
+
+int env_int(const char *name, int dflt) {
+  const char *v = getenv(name);
+  if (!v || !*v) return dflt;
+  return atoi(v);
+}
+
+hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+bool valid_dtype(dl_dtype dt) { return dt == DL_F32 || dt == DL_BF16; }
+
+// ---------------------------------------------------------------------------
+// GEMV / GEMM helpers
+// ---------------------------------------------------------------------------
+int gemv_ksplit(int strips, int K) {
+  const int target = env_int("DL_GEMV_TARGET_WGS", 768);
+  const int ksteps = K / 32;
+  int ks = (target + strips - 1) / strips;
+  const int maxks = std::max(1, ksteps / 8);
+  return std::max(1, std::min(ks, maxks));
+}
+
+hipError_t gemv(GemvArgs &a, hipStream_t s) {
+  int strips = 0;
+  for (int i = 0; i < a.nseg; ++i) {
+    a.seg[i].strip_begin = strips;
+    strips += gemv_strips(a.seg[i].N);
+  }
+  return launch_gemv_bf16(a, gemv_ksplit(strips, a.K), s);
+}
+
+GemvSeg gseg(const void *W, const void *X, const float *X2, float *out, int N, int ldx, int ldo) {
+  GemvSeg g{};
+  g.W = static_cast<const uint16_t *>(W);
+  g.X = X;
+  g.X2 = X2;
+  g.out = out;
+  g.N = N;
+  g.ldx = ldx;
+  g.ldo = ldo;
+  return g;
+}
+
+hipError_t gemm(GemmArgs &a, hipStream_t s) {
+  int tiles = 0;
+  for (int i = 0; i < a.nseg; ++i) {
+    a.seg[i].tile_begin = tiles;
+    tiles += gemm_ntiles(a.seg[i].N);
+  }
+  return launch_gemm_bf16(a, s);
+}
+
+GemmSeg mseg(const void *W, const void *X, void *C, int N, int ldx, int ldc) {
+  GemmSeg g{};
+  g.W = static_cast<const uint16_t *>(W);
+  g.X = static_cast<const uint16_t *>(X);
+  g.C = C;
+  g.N = N;
+  g.ldx = ldx;
+  g.ldc = ldc;
+  return g;
+}
+
+hipError_t gemm_f32(const float *X, const float *X2, const void *W, float *C, int M, int N, int K,
+                    int ldx, int ldc, int omode, const float *R, int ldr, const int32_t *past,
+                    int T, int L_max, hipStream_t s) {
+  GemmF32Args a{};
+  a.X = X;
+  a.X2 = X2;
+  a.W = static_cast<const float *>(W);
+  a.C = C;
+  a.R = R;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.ldx = ldx;
+  a.ldc = ldc;
+  a.ldr = ldr;
+  a.omode = omode;
+  a.past_lens = past;
+  a.T = T;
+  a.L_max = L_max;
+  return launch_gemm_f32(a, s);
+}
+
+// ---------------------------------------------------------------------------
+// Attention planning
+// ---------------------------------------------------------------------------
+struct DecodePlan {
+  int nsplit, tiles_per_split;
+};
+DecodePlan plan_decode(int64_t Bsz, int64_t n_kv, int64_t L_max) {
+  const int tiles = static_cast<int>((L_max + 127) / 128);
+  const int target = env_int("DL_ATTN_TARGET_WGS", 2048);
+  int ns = static_cast<int>((target + Bsz * n_kv - 1) / (Bsz * n_kv));
+  ns = std::max(1, std::min(ns, tiles));
+  const int tps = (tiles + ns - 1) / ns;
+  ns = (tiles + tps - 1) / tps;
+  return {ns, tps};
+}
+
+size_t attn_bf16_ws(int64_t Bsz, int64_t n_q, int64_t n_kv, int64_t d, int64_t r_k, int64_t r_v,
+                    int64_t L_max, bool decode) {
+  Carver c(nullptr);
+  c.take<uint16_t>(static_cast<size_t>(n_kv * d * r_k));
+  c.take<uint16_t>(static_cast<size_t>(n_kv * d * r_v));
+  if (decode) {
+    const DecodePlan p = plan_decode(Bsz, n_kv, L_max);
+    c.take<float>(static_cast<size_t>(Bsz * n_q * p.nsplit * (d + 2)));
+  }
+  return c.off;
+}
+
+dl_status check_attn_shape(int64_t n_q, int64_t n_kv, int64_t d, int64_t r_k, int64_t r_v,
+                           dl_dtype dt, bool prefill) {
+  DL_CHECK(n_q > 0 && n_kv > 0 && d > 0 && r_k > 0 && r_v > 0, DL_ERR_INVALID_ARG,
+           "attention dims must be positive");
+  DL_CHECK(n_q % n_kv == 0, DL_ERR_INVALID_ARG, "n_q (%lld) must be a multiple of n_kv (%lld)",
+           (long long)n_q, (long long)n_kv);
+  if (dt == DL_BF16) {
+    DL_CHECK(d == 64 || d == 128, DL_ERR_UNSUPPORTED, "bf16 attention needs head_dim 64 or 128");
+    DL_CHECK(r_k % 64 == 0 && r_v % 64 == 0, DL_ERR_UNSUPPORTED,
+             "bf16 attention needs r_k, r_v multiples of 64");
+    const int64_t G = n_q / n_kv;
+    DL_CHECK(G <= 16, DL_ERR_UNSUPPORTED, "bf16 attention needs n_q / n_kv <= 16");
+    if (prefill)
+      DL_CHECK(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, DL_ERR_UNSUPPORTED,
+               "bf16 prefill attention needs n_q / n_kv in {1, 2, 4, 8, 16}");
+  } else {
+    DL_CHECK(d % 2 == 0 && d <= 256, DL_ERR_UNSUPPORTED, "f32 attention needs even head_dim <= 256");
+  }
+  return DL_OK;
+}
+
+// Runs the bf16 attention kernels; q is bf16 (q_f32 = 0) or f32.
+hipError_t run_attn_bf16(const void *q, int q_f32, int ldq, const void *Ck, const void *Cv,
+                         const void *B_k, const void *B_v, const int32_t *lens, int ctx_offset,
+                         bool decode, void *out, int out_f32, int Bsz, int T, int n_q, int n_kv,
+                         int d, int r_k, int r_v, int L_max, float sm_scale, float theta,
+                         Carver &c, hipStream_t s) {
+  uint16_t *pk = c.take<uint16_t>(static_cast<size_t>(n_kv) * d * r_k);
+  uint16_t *pv = c.take<uint16_t>(static_cast<size_t>(n_kv) * d * r_v);
+  hipError_t e = launch_pack_up_factor(static_cast<const uint16_t *>(B_k), pk, r_k, n_kv, d, s);
+  if (e != hipSuccess) return e;
+  e = launch_pack_up_factor(static_cast<const uint16_t *>(B_v), pv, r_v, n_kv, d, s);
+  if (e != hipSuccess) return e;
+  const float scale = (sm_scale != 0.f ? sm_scale : 1.0f / sqrtf(static_cast<float>(d))) * kLog2e;
+  if (decode) {
+    const DecodePlan p = plan_decode(Bsz, n_kv, L_max);
+    AttnDecodeArgs a{};
+    a.q = q;
+    a.q_f32 = q_f32;
+    a.ck = static_cast<const uint16_t *>(Ck);
+    a.cv = static_cast<const uint16_t *>(Cv);
+    a.bk_packed = pk;
+    a.bv_packed = pv;
+    a.ctx_lens = lens;
+    a.ctx_offset = ctx_offset;
+    a.part = c.take<float>(static_cast<size_t>(Bsz) * n_q * p.nsplit * (d + 2));
+    a.Bsz = Bsz;
+    a.n_q = n_q;
+    a.n_kv = n_kv;
+    a.d = d;
+    a.r_k = r_k;
+    a.r_v = r_v;
+    a.L_max = L_max;
+    a.nsplit = p.nsplit;
+    a.tiles_per_split = p.tiles_per_split;
+    a.scale_log2 = scale;
+    a.theta = theta;
+    e = launch_attn_decode_bf16(a, s);
+    if (e != hipSuccess) return e;
+    return launch_attn_combine(a.part, out, Bsz, n_q, p.nsplit, d, out_f32, s);
+  }
+  AttnPrefillArgs a{};
+  a.q = q;
+  a.q_f32 = q_f32;
+  a.ldq = ldq;
+  a.ck = static_cast<const uint16_t *>(Ck);
+  a.cv = static_cast<const uint16_t *>(Cv);
+  a.bk_packed = pk;
+  a.bv_packed = pv;
+  a.past_lens = lens;
+  a.out = static_cast<uint16_t *>(out);
+  a.Bsz = Bsz;
+  a.T = T;
+  a.n_q = n_q;
+  a.n_kv = n_kv;
+  a.d = d;
+  a.r_k = r_k;
+  a.r_v = r_v;
+  a.L_max = L_max;
+  a.scale_log2 = scale;
+  a.theta = theta;
+  return launch_attn_prefill_bf16(a, s);
+}
+
+// ---------------------------------------------------------------------------
+// Layer workspace layout
+// ---------------------------------------------------------------------------
+struct LayerDims {
+  int M, T, Bsz, h, nq, nkv, d, f, rq, rk, rv, ro, rg, ru, rd, L_max;
+  int qd() const { return nq * d; }
+};
+
+bool use_gemv(int M) { return M <= 64; }
+
+}  // namespace
+
+extern "C" {
+
+const char *dl_last_error(void) { return g_last_error.c_str(); }
+
+// ===========================================================================
+// dl_lowrank_linear
+// ===========================================================================
+size_t dl_lowrank_linear_workspace(int64_t M, int64_t m, int64_t k, int64_t n, dl_dtype dt) {
+  (void)m;
+  if (M <= 0 || k <= 0 || n <= 0) return 0;
+  Carver c(nullptr);
+  if (dt == DL_F32) {
+    c.take<float>(static_cast<size_t>(M * k));
+  } else if (use_gemv(static_cast<int>(M))) {
+    c.take<float>(static_cast<size_t>(M * k));
+    c.take<float>(static_cast<size_t>(M * n));
+  } else {
+    c.take<uint16_t>(static_cast<size_t>(M * k));
+  }
+  return c.off;
+}
+
+dl_status dl_lowrank_linear(const void *x, const void *A, const void *B, void *y, int64_t M,
+                            int64_t m, int64_t k, int64_t n, dl_dtype dt, void *ws,
+                            size_t ws_bytes, void *stream) {
+  DL_CHECK(valid_dtype(dt), DL_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  DL_CHECK(x && A && B && y, DL_ERR_INVALID_ARG, "null tensor pointer");
+  DL_CHECK(M > 0 && m > 0 && k > 0 && n > 0, DL_ERR_INVALID_ARG, "dims must be positive");
+  DL_CHECK(M <= INT32_MAX / 2 && m * k <= INT32_MAX && k * n <= INT32_MAX, DL_ERR_UNSUPPORTED,
+           "dims too large");
+  if (dt == DL_BF16)
+    DL_CHECK(m % 64 == 0 && k % 64 == 0 && n % 64 == 0, DL_ERR_UNSUPPORTED,
+             "bf16 factor pairs need m, k, n multiples of 64");
+  DL_CHECK(aligned16(x) && aligned16(A) && aligned16(B) && aligned16(y), DL_ERR_ALIGNMENT,
+           "tensor pointers must be 16-byte aligned");
+  const size_t need = dl_lowrank_linear_workspace(M, m, k, n, dt);
+  DL_CHECK(ws && aligned16(ws) && ws_bytes >= need, DL_ERR_WORKSPACE,
+           "workspace of %zu bytes required, %zu given", need, ws_bytes);
+  hipStream_t s = as_stream(stream);
+  Carver c(ws);
+  const int Mi = static_cast<int>(M), mi = static_cast<int>(m), ki = static_cast<int>(k),
+            ni = static_cast<int>(n);
+  if (dt == DL_F32) {
+    float *t = c.take<float>(static_cast<size_t>(M * k));
+    DL_HIP(gemm_f32(static_cast<const float *>(x), nullptr, A, t, Mi, ki, mi, mi, ki,
+                    F32_OUT_STORE, nullptr, 0, nullptr, 1, 0, s));
+    DL_HIP(gemm_f32(t, nullptr, B, static_cast<float *>(y), Mi, ni, ki, ki, ni, F32_OUT_STORE,
+                    nullptr, 0, nullptr, 1, 0, s));
+    return DL_OK;
+  }
+  if (use_gemv(Mi)) {
+    float *t = c.take<float>(static_cast<size_t>(M * k));
+    float *yacc = c.take<float>(static_cast<size_t>(M * n));
+    FillRegion z[2] = {{t, nullptr, 0, M * k}, {yacc, nullptr, 0, M * n}};
+    DL_HIP(launch_fill(z, 2, s));
+    GemvArgs a{};
+    a.nseg = 1;
+    a.M = Mi;
+    a.K = mi;
+    a.xmode = GEMV_X_BF16;
+    a.seg[0] = gseg(A, x, nullptr, t, ki, mi, ki);
+    DL_HIP(gemv(a, s));
+    GemvArgs b{};
+    b.nseg = 1;
+    b.M = Mi;
+    b.K = ki;
+    b.xmode = GEMV_X_F32;
+    b.seg[0] = gseg(B, t, nullptr, yacc, ni, ki, ni);
+    DL_HIP(gemv(b, s));
+    DL_HIP(launch_convert_f32(yacc, y, 1, M * n, s));
+    return DL_OK;
+  }
+  uint16_t *t = c.take<uint16_t>(static_cast<size_t>(M * k));
+  GemmArgs a{};
+  a.nseg = 1;
+  a.M = Mi;
+  a.K = mi;
+  a.xmode = GEMM_X_BF16;
+  a.omode = GEMM_OUT_BF16;
+  a.seg[0] = mseg(A, x, t, ki, mi, ki);
+  DL_HIP(gemm(a, s));
+  GemmArgs b{};
+  b.nseg = 1;
+  b.M = Mi;
+  b.K = ki;
+  b.xmode = GEMM_X_BF16;
+  b.omode = GEMM_OUT_BF16;
+  b.seg[0] = mseg(B, t, y, ni, ki, ni);
+  DL_HIP(gemm(b, s));
+  return DL_OK;
+}
+
+// ===========================================================================
+// dl_lowrank_kv_append
+// ===========================================================================
+size_t dl_kv_append_workspace(int64_t Bsz, int64_t T, int64_t m, int64_t r_k, int64_t r_v,
+                              dl_dtype dt) {
+  (void)m;
+  if (Bsz <= 0 || T <= 0) return 0;
+  const int64_t M = Bsz * T;
+  if (dt == DL_BF16 && use_gemv(static_cast<int>(M))) {
+    Carver c(nullptr);
+    c.take<float>(static_cast<size_t>(M * (r_k + r_v)));
+    return c.off;
+  }
+  return 0;
+}
+
+dl_status dl_lowrank_kv_append(const void *x, const void *A_k, const void *A_v, void *Ck,
+                               void *Cv, const int32_t *past_lens, int64_t Bsz, int64_t T,
+                               int64_t m, int64_t r_k, int64_t r_v, int64_t L_max, dl_dtype dt,
+                               void *ws, size_t ws_bytes, void *stream) {
+  DL_CHECK(valid_dtype(dt), DL_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  DL_CHECK(x && A_k && A_v && Ck && Cv && past_lens, DL_ERR_INVALID_ARG, "null pointer");
+  DL_CHECK(Bsz > 0 && T > 0 && m > 0 && r_k > 0 && r_v > 0 && L_max > 0, DL_ERR_INVALID_ARG,
+           "dims must be positive");
+  DL_CHECK(T <= L_max, DL_ERR_INVALID_ARG, "T exceeds L_max");
+  DL_CHECK(Bsz * T <= INT32_MAX / 2 && Bsz * L_max * std::max(r_k, r_v) <= ((int64_t)1 << 40),
+           DL_ERR_UNSUPPORTED, "dims too large");
+  if (dt == DL_BF16)
+    DL_CHECK(m % 64 == 0 && r_k % 64 == 0 && r_v % 64 == 0, DL_ERR_UNSUPPORTED,
+             "bf16 append needs m, r_k, r_v multiples of 64");
+  DL_CHECK(aligned16(x) && aligned16(A_k) && aligned16(A_v) && aligned16(Ck) && aligned16(Cv) &&
+               aligned16(past_lens),
+           DL_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+  const size_t need = dl_kv_append_workspace(Bsz, T, m, r_k, r_v, dt);
+  DL_CHECK(need == 0 || (ws && aligned16(ws) && ws_bytes >= need), DL_ERR_WORKSPACE,
+           "workspace of %zu bytes required, %zu given", need, ws_bytes);
+  hipStream_t s = as_stream(stream);
+  const int M = static_cast<int>(Bsz * T), mi = static_cast<int>(m), rk = static_cast<int>(r_k),
+            rv = static_cast<int>(r_v), Ti = static_cast<int>(T), Lm = static_cast<int>(L_max);
+  if (dt == DL_F32) {
+    DL_HIP(gemm_f32(static_cast<const float *>(x), nullptr, A_k, static_cast<float *>(Ck), M, rk,
+                    mi, mi, rk, F32_OUT_CACHE, nullptr, 0, past_lens, Ti, Lm, s));
+    DL_HIP(gemm_f32(static_cast<const float *>(x), nullptr, A_v, static_cast<float *>(Cv), M, rv,
+                    mi, mi, rv, F32_OUT_CACHE, nullptr, 0, past_lens, Ti, Lm, s));
+    return DL_OK;
+  }
+  if (use_gemv(M)) {
+    Carver c(ws);
+    float *acc = c.take<float>(static_cast<size_t>(M) * (rk + rv));
+    FillRegion z[1] = {{acc, nullptr, 0, static_cast<int64_t>(M) * (rk + rv)}};
+    DL_HIP(launch_fill(z, 1, s));
+    GemvArgs a{};
+    a.nseg = 2;
+    a.M = M;
+    a.K = mi;
+    a.xmode = GEMV_X_BF16;
+    a.seg[0] = gseg(A_k, x, nullptr, acc, rk, mi, rk + rv);
+    a.seg[1] = gseg(A_v, x, nullptr, acc + rk, rv, mi, rk + rv);
+    DL_HIP(gemv(a, s));
+    DL_HIP(launch_store_cache_rows(acc, rk + rv, Ck, 1, past_lens, static_cast<int>(Bsz), Ti, rk,
+                                   Lm, s));
+    DL_HIP(launch_store_cache_rows(acc + rk, rk + rv, Cv, 1, past_lens, static_cast<int>(Bsz), Ti,
+                                   rv, Lm, s));
+    return DL_OK;
+  }
+  GemmArgs a{};
+  a.nseg = 2;
+  a.M = M;
+  a.K = mi;
+  a.xmode = GEMM_X_BF16;
+  a.omode = GEMM_OUT_CACHE;
+  a.past_lens = past_lens;
+  a.T = Ti;
+  a.L_max = Lm;
+  a.seg[0] = mseg(A_k, x, Ck, rk, mi, rk);
+  a.seg[1] = mseg(A_v, x, Cv, rv, mi, rv);
+  DL_HIP(gemm(a, s));
+  return DL_OK;
+}
+
+// ===========================================================================
+// Attention entry points
+// ===========================================================================
+size_t dl_attn_decode_workspace(int64_t Bsz, int64_t n_q, int64_t n_kv, int64_t d, int64_t r_k,
+                                int64_t r_v, int64_t L_max, dl_dtype dt) {
+  if (dt != DL_BF16 || Bsz <= 0 || n_kv <= 0 || L_max <= 0) return 0;
+  return attn_bf16_ws(Bsz, n_q, n_kv, d, r_k, r_v, L_max, true);
+}
+
+size_t dl_attn_prefill_workspace(int64_t Bsz, int64_t T, int64_t n_q, int64_t n_kv, int64_t d,
+                                 int64_t r_k, int64_t r_v, int64_t L_max, dl_dtype dt) {
+  (void)T;
+  if (dt != DL_BF16 || Bsz <= 0 || n_kv <= 0 || L_max <= 0) return 0;
+  return attn_bf16_ws(Bsz, n_q, n_kv, d, r_k, r_v, L_max, false);
+}
+
+static dl_status attn_common(const void *q, const void *Ck, const void *Cv, const void *B_k,
+                             const void *B_v, const int32_t *lens, void *out, int64_t Bsz,
+                             int64_t T, int64_t n_q, int64_t n_kv, int64_t d, int64_t r_k,
+                             int64_t r_v, int64_t L_max, float sm_scale, float rope_theta,
+                             dl_dtype dt, void *ws, size_t ws_bytes, void *stream, bool decode) {
+  DL_CHECK(valid_dtype(dt), DL_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  DL_CHECK(q && Ck && Cv && B_k && B_v && lens && out, DL_ERR_INVALID_ARG, "null pointer");
+  DL_CHECK(Bsz > 0 && T > 0 && L_max > 0, DL_ERR_INVALID_ARG, "dims must be positive");
+  DL_CHECK(T <= L_max, DL_ERR_INVALID_ARG, "T exceeds L_max");
+  dl_status st = check_attn_shape(n_q, n_kv, d, r_k, r_v, dt, !decode);
+  if (st != DL_OK) return st;
+  DL_CHECK(Bsz * L_max * std::max(r_k, r_v) <= ((int64_t)1 << 40) && Bsz * T * n_q * d <= INT32_MAX &&
+               L_max <= INT32_MAX / 2,
+           DL_ERR_UNSUPPORTED, "dims too large");
+  DL_CHECK(isfinite(sm_scale) && sm_scale >= 0.f && isfinite(rope_theta) && rope_theta >= 0.f,
+           DL_ERR_INVALID_ARG, "sm_scale and rope_theta must be finite and non-negative");
+  DL_CHECK(aligned16(q) && aligned16(Ck) && aligned16(Cv) && aligned16(B_k) && aligned16(B_v) &&
+               aligned16(lens) && aligned16(out),
+           DL_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+  const size_t need = decode ? dl_attn_decode_workspace(Bsz, n_q, n_kv, d, r_k, r_v, L_max, dt)
+                             : dl_attn_prefill_workspace(Bsz, T, n_q, n_kv, d, r_k, r_v, L_max, dt);
+  DL_CHECK(need == 0 || (ws && aligned16(ws) && ws_bytes >= need), DL_ERR_WORKSPACE,
+           "workspace of %zu bytes required, %zu given", need, ws_bytes);
+  hipStream_t s = as_stream(stream);
+  if (dt == DL_F32) {
+    AttnF32Args a{};
+    a.q = static_cast<const float *>(q);
+    a.ck = static_cast<const float *>(Ck);
+    a.cv = static_cast<const float *>(Cv);
+    a.bk = static_cast<const float *>(B_k);
+    a.bv = static_cast<const float *>(B_v);
+    a.lens = lens;
+    a.out = static_cast<float *>(out);
+    a.decode = decode ? 1 : 0;
+    a.Bsz = static_cast<int>(Bsz);
+    a.T = static_cast<int>(T);
+    a.n_q = static_cast<int>(n_q);
+    a.n_kv = static_cast<int>(n_kv);
+    a.d = static_cast<int>(d);
+    a.r_k = static_cast<int>(r_k);
+    a.r_v = static_cast<int>(r_v);
+    a.L_max = static_cast<int>(L_max);
+    a.ldq = static_cast<int>(n_q * d);
+    a.sm_scale = sm_scale != 0.f ? sm_scale : 1.0f / sqrtf(static_cast<float>(d));
+    a.theta = rope_theta;
+    DL_HIP(launch_attn_f32(a, s));
+    return DL_OK;
+  }
+  Carver c(ws);
+  DL_HIP(run_attn_bf16(q, 0, static_cast<int>(n_q * d), Ck, Cv, B_k, B_v, lens, 0, decode, out, 0,
+                       static_cast<int>(Bsz), static_cast<int>(T), static_cast<int>(n_q),
+                       static_cast<int>(n_kv), static_cast<int>(d), static_cast<int>(r_k),
+                       static_cast<int>(r_v), static_cast<int>(L_max), sm_scale, rope_theta, c, s));
+  return DL_OK;
+}
+
+dl_status dl_lowrank_attn_decode(const void *q, const void *Ck, const void *Cv, const void *B_k,
+                                 const void *B_v, const int32_t *ctx_lens, void *out, int64_t Bsz,
+                                 int64_t n_q, int64_t n_kv, int64_t d, int64_t r_k, int64_t r_v,
+                                 int64_t L_max, float sm_scale, float rope_theta, dl_dtype dt,
+                                 void *ws, size_t ws_bytes, void *stream) {
+  return attn_common(q, Ck, Cv, B_k, B_v, ctx_lens, out, Bsz, 1, n_q, n_kv, d, r_k, r_v, L_max,
+                     sm_scale, rope_theta, dt, ws, ws_bytes, stream, true);
+}
+
+dl_status dl_lowrank_attn_prefill(const void *q, const void *Ck, const void *Cv, const void *B_k,
+                                  const void *B_v, const int32_t *past_lens, void *out,
+                                  int64_t Bsz, int64_t T, int64_t n_q, int64_t n_kv, int64_t d,
+                                  int64_t r_k, int64_t r_v, int64_t L_max, float sm_scale,
+                                  float rope_theta, dl_dtype dt, void *ws, size_t ws_bytes,
+                                  void *stream) {
+  return attn_common(q, Ck, Cv, B_k, B_v, past_lens, out, Bsz, T, n_q, n_kv, d, r_k, r_v, L_max,
+                     sm_scale, rope_theta, dt, ws, ws_bytes, stream, false);
+}
+
+// ===========================================================================
+// dl_decomposed_layer_fwd
+// ===========================================================================
+static dl_status layer_dims(const dl_layer *L, int64_t Bsz, int64_t T, int64_t L_max,
+                            LayerDims *o) {
+  DL_CHECK(L, DL_ERR_INVALID_ARG, "null layer");
+  DL_CHECK(valid_dtype(L->dt), DL_ERR_INVALID_ARG, "unknown dtype %d", (int)L->dt);
+  DL_CHECK(Bsz > 0 && T > 0 && L_max > 0, DL_ERR_INVALID_ARG, "Bsz, T, L_max must be positive");
+  DL_CHECK(T <= L_max, DL_ERR_INVALID_ARG, "T exceeds L_max");
+  DL_CHECK(L->hidden > 0 && L->n_q > 0 && L->n_kv > 0 && L->head_dim > 0 && L->ffn > 0,
+           DL_ERR_INVALID_ARG, "layer dims must be positive");
+  const dl_factor *fs[7] = {&L->q, &L->k, &L->v, &L->o, &L->gate, &L->up, &L->down};
+  for (const dl_factor *f : fs) {
+    DL_CHECK(f->A && f->B, DL_ERR_INVALID_ARG, "null factor pointer");
+    DL_CHECK(f->k > 0, DL_ERR_INVALID_ARG, "factor rank must be positive");
+  }
+  dl_status st = check_attn_shape(L->n_q, L->n_kv, L->head_dim, L->k.k, L->v.k, L->dt, T > 1);
+  if (st != DL_OK) return st;
+  if (L->dt == DL_BF16) {
+    bool ok = L->hidden % 64 == 0 && L->ffn % 64 == 0;
+    for (const dl_factor *f : fs) ok = ok && f->k % 64 == 0;
+    DL_CHECK(ok, DL_ERR_UNSUPPORTED, "bf16 layer needs hidden, ffn and every rank multiples of 64");
+  }
+  DL_CHECK(Bsz * T <= (1 << 24) && L->hidden <= (1 << 20) && L->ffn <= (1 << 20) &&
+               Bsz * L_max * std::max(L->k.k, L->v.k) <= ((int64_t)1 << 40),
+           DL_ERR_UNSUPPORTED, "dims too large");
+  DL_CHECK(isfinite(L->rms_eps) && L->rms_eps >= 0.f && isfinite(L->rope_theta) &&
+               L->rope_theta >= 0.f,
+           DL_ERR_INVALID_ARG, "rms_eps and rope_theta must be finite and non-negative");
+  o->M = static_cast<int>(Bsz * T);
+  o->T = static_cast<int>(T);
+  o->Bsz = static_cast<int>(Bsz);
+  o->h = static_cast<int>(L->hidden);
+  o->nq = static_cast<int>(L->n_q);
+  o->nkv = static_cast<int>(L->n_kv);
+  o->d = static_cast<int>(L->head_dim);
+  o->f = static_cast<int>(L->ffn);
+  o->rq = static_cast<int>(L->q.k);
+  o->rk = static_cast<int>(L->k.k);
+  o->rv = static_cast<int>(L->v.k);
+  o->ro = static_cast<int>(L->o.k);
+  o->rg = static_cast<int>(L->gate.k);
+  o->ru = static_cast<int>(L->up.k);
+  o->rd = static_cast<int>(L->down.k);
+  o->L_max = static_cast<int>(L_max);
+  return DL_OK;
+}
+
+// Workspace regions, in carve order (measuring and running use the same code).
+struct LayerWS {
+  // f32 path
+  float *a, *tq, *qf, *att, *to, *x2, *b, *tg, *tu, *G, *U, *td;
+  // bf16 GEMV path (f32 accumulators + bf16 activations)
+  float *acc0;  // start of the zero-initialised accumulators
+  float *t_qkv, *q32, *t_o, *t_gu, *G32, *U32, *t_d;
+  int64_t acc_len;
+  float *x2f;
+  uint16_t *a16, *b16, *att16;
+  // bf16 GEMM path
+  uint16_t *tq16, *q16, *to16, *tg16, *tu16, *G16, *U16, *td16;
+};
+
+static void carve_layer(Carver &c, const LayerDims &D, dl_dtype dt, LayerWS &w) {
+  const size_t M = D.M;
+  if (dt == DL_F32) {
+    w.a = c.take<float>(M * D.h);
+    w.tq = c.take<float>(M * D.rq);
+    w.qf = c.take<float>(M * D.qd());
+    w.att = c.take<float>(M * D.qd());
+    w.to = c.take<float>(M * D.ro);
+    w.x2 = c.take<float>(M * D.h);
+    w.b = c.take<float>(M * D.h);
+    w.tg = c.take<float>(M * D.rg);
+    w.tu = c.take<float>(M * D.ru);
+    w.G = c.take<float>(M * D.f);
+    w.U = c.take<float>(M * D.f);
+    w.td = c.take<float>(M * D.rd);
+    return;
+  }
+  if (use_gemv(D.M)) {
+    // accumulators are carved as one contiguous block so a single fill zeroes them
+    const size_t rqkv = D.rq + D.rk + D.rv;
+    const size_t n_acc = M * (rqkv + D.qd() + D.ro + D.rg + D.ru + 2 * (size_t)D.f + D.rd);
+    w.acc0 = c.take<float>(n_acc);
+    w.acc_len = static_cast<int64_t>(n_acc);
+    if (w.acc0) {
+      float *p = w.acc0;
+      w.t_qkv = p; p += M * rqkv;
+      w.q32 = p; p += M * D.qd();
+      w.t_o = p; p += M * D.ro;
+      w.t_gu = p; p += M * (D.rg + D.ru);
+      w.G32 = p; p += M * D.f;
+      w.U32 = p; p += M * D.f;
+      w.t_d = p;
+    }
+    w.x2f = c.take<float>(M * D.h);
+    w.a16 = c.take<uint16_t>(M * D.h);
+    w.b16 = c.take<uint16_t>(M * D.h);
+    w.att16 = c.take<uint16_t>(M * D.qd());
+    return;
+  }
+  w.a16 = c.take<uint16_t>(M * D.h);
+  w.tq16 = c.take<uint16_t>(M * D.rq);
+  w.q16 = c.take<uint16_t>(M * D.qd());
+  w.att16 = c.take<uint16_t>(M * D.qd());
+  w.to16 = c.take<uint16_t>(M * D.ro);
+  w.x2f = c.take<float>(M * D.h);
+  w.b16 = c.take<uint16_t>(M * D.h);
+  w.tg16 = c.take<uint16_t>(M * D.rg);
+  w.tu16 = c.take<uint16_t>(M * D.ru);
+  w.G16 = c.take<uint16_t>(M * D.f);
+  w.U16 = c.take<uint16_t>(M * D.f);
+  w.td16 = c.take<uint16_t>(M * D.rd);
+}
+
+size_t dl_layer_workspace(const dl_layer *L, int64_t Bsz, int64_t T, int64_t L_max) {
+  LayerDims D{};
+  if (layer_dims(L, Bsz, T, L_max, &D) != DL_OK) return 0;
+  Carver c(nullptr);
+  LayerWS w{};
+  carve_layer(c, D, L->dt, w);
+  if (L->dt == DL_BF16)
+    c.off += attn_bf16_ws(D.Bsz, D.nq, D.nkv, D.d, D.rk, D.rv, D.L_max, D.T == 1) + kAlign;
+  return c.off;
+}
+
+dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, void *x2_out,
+                                  void *Ck, void *Cv, const int32_t *past_lens, int64_t Bsz,
+                                  int64_t T, int64_t L_max, void *ws, size_t ws_bytes,
+                                  void *stream) {
+  LayerDims D{};
+  dl_status st = layer_dims(L, Bsz, T, L_max, &D);
+  if (st != DL_OK) return st;
+  DL_CHECK(x && y && Ck && Cv && past_lens, DL_ERR_INVALID_ARG, "null pointer");
+  const dl_factor *fs[7] = {&L->q, &L->k, &L->v, &L->o, &L->gate, &L->up, &L->down};
+  bool al = aligned16(x) && aligned16(y) && aligned16(Ck) && aligned16(Cv) && aligned16(past_lens);
+  for (const dl_factor *f : fs) al = al && aligned16(f->A) && aligned16(f->B);
+  al = al && (!x2_out || aligned16(x2_out)) && (!L->attn_norm || aligned16(L->attn_norm)) &&
+       (!L->mlp_norm || aligned16(L->mlp_norm));
+  DL_CHECK(al, DL_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+  const size_t need = dl_layer_workspace(L, Bsz, T, L_max);
+  DL_CHECK(ws && aligned16(ws) && ws_bytes >= need, DL_ERR_WORKSPACE,
+           "workspace of %zu bytes required, %zu given", need, ws_bytes);
+
+  hipStream_t s = as_stream(stream);
+  Carver c(ws);
+  LayerWS w{};
+  carve_layer(c, D, L->dt, w);
+  const int M = D.M, h = D.h, qd = D.qd();
+  const float eps = L->rms_eps;
+  const int gf32 = L->dt == DL_F32;
+
+  if (L->dt == DL_F32) {
+    const float *xf = static_cast<const float *>(x);
+    DL_HIP(launch_rmsnorm(x, 1, L->attn_norm, 1, w.a, 1, M, h, eps, s));
+    DL_HIP(gemm_f32(w.a, nullptr, L->k.A, static_cast<float *>(Ck), M, D.rk, h, h, D.rk,
+                    F32_OUT_CACHE, nullptr, 0, past_lens, D.T, D.L_max, s));
+    DL_HIP(gemm_f32(w.a, nullptr, L->v.A, static_cast<float *>(Cv), M, D.rv, h, h, D.rv,
+                    F32_OUT_CACHE, nullptr, 0, past_lens, D.T, D.L_max, s));
+    DL_HIP(gemm_f32(w.a, nullptr, L->q.A, w.tq, M, D.rq, h, h, D.rq, F32_OUT_STORE, nullptr, 0,
+                    nullptr, 1, 0, s));
+    DL_HIP(gemm_f32(w.tq, nullptr, L->q.B, w.qf, M, qd, D.rq, D.rq, qd, F32_OUT_STORE, nullptr, 0,
+                    nullptr, 1, 0, s));
+    AttnF32Args a{};
+    a.q = w.qf;
+    a.ck = static_cast<const float *>(Ck);
+    a.cv = static_cast<const float *>(Cv);
+    a.bk = static_cast<const float *>(L->k.B);
+    a.bv = static_cast<const float *>(L->v.B);
+    a.lens = past_lens;
+    a.out = w.att;
+    a.decode = 0;
+    a.Bsz = D.Bsz;
+    a.T = D.T;
+    a.n_q = D.nq;
+    a.n_kv = D.nkv;
+    a.d = D.d;
+    a.r_k = D.rk;
+    a.r_v = D.rv;
+    a.L_max = D.L_max;
+    a.ldq = qd;
+    a.sm_scale = 1.0f / sqrtf(static_cast<float>(D.d));
+    a.theta = L->rope_theta;
+    DL_HIP(launch_attn_f32(a, s));
+    DL_HIP(gemm_f32(w.att, nullptr, L->o.A, w.to, M, D.ro, qd, qd, D.ro, F32_OUT_STORE, nullptr, 0,
+                    nullptr, 1, 0, s));
+    float *x2 = x2_out ? static_cast<float *>(x2_out) : w.x2;
+    DL_HIP(gemm_f32(w.to, nullptr, L->o.B, x2, M, h, D.ro, D.ro, h, F32_OUT_RESID, xf, h, nullptr,
+                    1, 0, s));
+    DL_HIP(launch_rmsnorm(x2, 1, L->mlp_norm, 1, w.b, 1, M, h, eps, s));
+    DL_HIP(gemm_f32(w.b, nullptr, L->gate.A, w.tg, M, D.rg, h, h, D.rg, F32_OUT_STORE, nullptr, 0,
+                    nullptr, 1, 0, s));
+    DL_HIP(gemm_f32(w.b, nullptr, L->up.A, w.tu, M, D.ru, h, h, D.ru, F32_OUT_STORE, nullptr, 0,
+                    nullptr, 1, 0, s));
+    DL_HIP(gemm_f32(w.tg, nullptr, L->gate.B, w.G, M, D.f, D.rg, D.rg, D.f, F32_OUT_STORE, nullptr,
+                    0, nullptr, 1, 0, s));
+    DL_HIP(gemm_f32(w.tu, nullptr, L->up.B, w.U, M, D.f, D.ru, D.ru, D.f, F32_OUT_STORE, nullptr, 0,
+                    nullptr, 1, 0, s));
+    DL_HIP(gemm_f32(w.G, w.U, L->down.A, w.td, M, D.rd, D.f, D.f, D.rd, F32_OUT_STORE, nullptr, 0,
+                    nullptr, 1, 0, s));
+    DL_HIP(gemm_f32(w.td, nullptr, L->down.B, static_cast<float *>(y), M, h, D.rd, D.rd, h,
+                    F32_OUT_RESID, x2, h, nullptr, 1, 0, s));
+    return DL_OK;
+  }
+
+  if (use_gemv(M)) {
+    const int rqkv = D.rq + D.rk + D.rv;
+    FillRegion init[2] = {{w.acc0, nullptr, 0, w.acc_len}, {w.x2f, x, 1, (int64_t)M * h}};
+    DL_HIP(launch_fill(init, 2, s));
+    DL_HIP(launch_rmsnorm(x, 0, L->attn_norm, gf32, w.a16, 0, M, h, eps, s));
+    {  // grouped down-projections of q, k, v: one pass over the normed activations
+      GemvArgs a{};
+      a.nseg = 3;
+      a.M = M;
+      a.K = h;
+      a.xmode = GEMV_X_BF16;
+      a.seg[0] = gseg(L->q.A, w.a16, nullptr, w.t_qkv, D.rq, h, rqkv);
+      a.seg[1] = gseg(L->k.A, w.a16, nullptr, w.t_qkv + D.rq, D.rk, h, rqkv);
+      a.seg[2] = gseg(L->v.A, w.a16, nullptr, w.t_qkv + D.rq + D.rk, D.rv, h, rqkv);
+      DL_HIP(gemv(a, s));
+    }
+    DL_HIP(launch_store_cache_rows(w.t_qkv + D.rq, rqkv, Ck, 1, past_lens, D.Bsz, D.T, D.rk,
+                                   D.L_max, s));
+    DL_HIP(launch_store_cache_rows(w.t_qkv + D.rq + D.rk, rqkv, Cv, 1, past_lens, D.Bsz, D.T, D.rv,
+                                   D.L_max, s));
+    {
+      GemvArgs a{};
+      a.nseg = 1;
+      a.M = M;
+      a.K = D.rq;
+      a.xmode = GEMV_X_F32;
+      a.seg[0] = gseg(L->q.B, w.t_qkv, nullptr, w.q32, qd, rqkv, qd);
+      DL_HIP(gemv(a, s));
+    }
+    DL_HIP(run_attn_bf16(w.q32, 1, qd, Ck, Cv, L->k.B, L->v.B, past_lens, 1, D.T == 1, w.att16, 0,
+                         D.Bsz, D.T, D.nq, D.nkv, D.d, D.rk, D.rv, D.L_max, 0.f, L->rope_theta, c,
+                         s));
+    {
+      GemvArgs a{};
+      a.nseg = 1;
+      a.M = M;
+      a.K = qd;
+      a.xmode = GEMV_X_BF16;
+      a.seg[0] = gseg(L->o.A, w.att16, nullptr, w.t_o, D.ro, qd, D.ro);
+      DL_HIP(gemv(a, s));
+      GemvArgs b{};
+      b.nseg = 1;
+      b.M = M;
+      b.K = D.ro;
+      b.xmode = GEMV_X_F32;
+      b.seg[0] = gseg(L->o.B, w.t_o, nullptr, w.x2f, h, D.ro, h);
+      DL_HIP(gemv(b, s));
+    }
+    if (x2_out) {
+      FillRegion cp[1] = {{static_cast<float *>(x2_out), w.x2f, 0, (int64_t)M * h}};
+      DL_HIP(launch_fill(cp, 1, s));
+    }
+    DL_HIP(launch_rmsnorm(w.x2f, 1, L->mlp_norm, gf32, w.b16, 0, M, h, eps, s));
+    {
+      GemvArgs a{};
+      a.nseg = 2;
+      a.M = M;
+      a.K = h;
+      a.xmode = GEMV_X_BF16;
+      a.seg[0] = gseg(L->gate.A, w.b16, nullptr, w.t_gu, D.rg, h, D.rg + D.ru);
+      a.seg[1] = gseg(L->up.A, w.b16, nullptr, w.t_gu + D.rg, D.ru, h, D.rg + D.ru);
+      DL_HIP(gemv(a, s));
+    }
+    if (D.rg == D.ru) {
+      GemvArgs a{};
+      a.nseg = 2;
+      a.M = M;
+      a.K = D.rg;
+      a.xmode = GEMV_X_F32;
+      a.seg[0] = gseg(L->gate.B, w.t_gu, nullptr, w.G32, D.f, D.rg + D.ru, D.f);
+      a.seg[1] = gseg(L->up.B, w.t_gu + D.rg, nullptr, w.U32, D.f, D.rg + D.ru, D.f);
+      DL_HIP(gemv(a, s));
+    } else {
+      GemvArgs a{};
+      a.nseg = 1;
+      a.M = M;
+      a.K = D.rg;
+      a.xmode = GEMV_X_F32;
+      a.seg[0] = gseg(L->gate.B, w.t_gu, nullptr, w.G32, D.f, D.rg + D.ru, D.f);
+      DL_HIP(gemv(a, s));
+      a.K = D.ru;
+      a.seg[0] = gseg(L->up.B, w.t_gu + D.rg, nullptr, w.U32, D.f, D.rg + D.ru, D.f);
+      DL_HIP(gemv(a, s));
+    }
+    {
+      GemvArgs a{};
+      a.nseg = 1;
+      a.M = M;
+      a.K = D.f;
+      a.xmode = GEMV_X_SWIGLU_F32;
+      a.seg[0] = gseg(L->down.A, w.G32, w.U32, w.t_d, D.rd, D.f, D.rd);
+      DL_HIP(gemv(a, s));
+      GemvArgs b{};
+      b.nseg = 1;
+      b.M = M;
+      b.K = D.rd;
+      b.xmode = GEMV_X_F32;
+      b.seg[0] = gseg(L->down.B, w.t_d, nullptr, w.x2f, h, D.rd, h);  // x2 + MLP = y
+      DL_HIP(gemv(b, s));
+    }
+    DL_HIP(launch_convert_f32(w.x2f, y, 1, (int64_t)M * h, s));
+    return DL_OK;
+  }
+
+  // bf16 GEMM path
+  DL_HIP(launch_rmsnorm(x, 0, L->attn_norm, gf32, w.a16, 0, M, h, eps, s));
+  {
+    GemmArgs a{};
+    a.nseg = 1;
+    a.M = M;
+    a.K = h;
+    a.omode = GEMM_OUT_BF16;
+    a.seg[0] = mseg(L->q.A, w.a16, w.tq16, D.rq, h, D.rq);
+    DL_HIP(gemm(a, s));
+    GemmArgs b{};
+    b.nseg = 2;
+    b.M = M;
+    b.K = h;
+    b.omode = GEMM_OUT_CACHE;
+    b.past_lens = past_lens;
+    b.T = D.T;
+    b.L_max = D.L_max;
+    b.seg[0] = mseg(L->k.A, w.a16, Ck, D.rk, h, D.rk);
+    b.seg[1] = mseg(L->v.A, w.a16, Cv, D.rv, h, D.rv);
+    DL_HIP(gemm(b, s));
+    GemmArgs q{};
+    q.nseg = 1;
+    q.M = M;
+    q.K = D.rq;
+    q.omode = GEMM_OUT_BF16;
+    q.seg[0] = mseg(L->q.B, w.tq16, w.q16, qd, D.rq, qd);
+    DL_HIP(gemm(q, s));
+  }
+  DL_HIP(run_attn_bf16(w.q16, 0, qd, Ck, Cv, L->k.B, L->v.B, past_lens, 1, D.T == 1, w.att16, 0,
+                       D.Bsz, D.T, D.nq, D.nkv, D.d, D.rk, D.rv, D.L_max, 0.f, L->rope_theta, c,
+                       s));
+  {
+    GemmArgs a{};
+    a.nseg = 1;
+    a.M = M;
+    a.K = qd;
+    a.omode = GEMM_OUT_BF16;
+    a.seg[0] = mseg(L->o.A, w.att16, w.to16, D.ro, qd, D.ro);
+    DL_HIP(gemm(a, s));
+    GemmArgs b{};
+    b.nseg = 1;
+    b.M = M;
+    b.K = D.ro;
+    b.omode = GEMM_OUT_F32_RES_BF16;
+    b.seg[0] = mseg(L->o.B, w.to16, nullptr, h, D.ro, h);
+    b.seg[0].C32 = w.x2f;
+    b.seg[0].R = x;
+    b.seg[0].ldr = h;
+    DL_HIP(gemm(b, s));
+  }
+  if (x2_out) {
+    FillRegion cp[1] = {{static_cast<float *>(x2_out), w.x2f, 0, (int64_t)M * h}};
+    DL_HIP(launch_fill(cp, 1, s));
+  }
+  DL_HIP(launch_rmsnorm(w.x2f, 1, L->mlp_norm, gf32, w.b16, 0, M, h, eps, s));
+  {
+    GemmArgs a{};
+    a.nseg = 2;
+    a.M = M;
+    a.K = h;
+    a.omode = GEMM_OUT_BF16;
+    a.seg[0] = mseg(L->gate.A, w.b16, w.tg16, D.rg, h, D.rg);
+    a.seg[1] = mseg(L->up.A, w.b16, w.tu16, D.ru, h, D.ru);
+    DL_HIP(gemm(a, s));
+  }
+  if (D.rg == D.ru) {
+    GemmArgs a{};
+    a.nseg = 2;
+    a.M = M;
+    a.K = D.rg;
+    a.omode = GEMM_OUT_BF16;
+    a.seg[0] = mseg(L->gate.B, w.tg16, w.G16, D.f, D.rg, D.f);
+    a.seg[1] = mseg(L->up.B, w.tu16, w.U16, D.f, D.ru, D.f);
+    DL_HIP(gemm(a, s));
+  } else {
+    GemmArgs a{};
+    a.nseg = 1;
+    a.M = M;
+    a.K = D.rg;
+    a.omode = GEMM_OUT_BF16;
+    a.seg[0] = mseg(L->gate.B, w.tg16, w.G16, D.f, D.rg, D.f);
+    DL_HIP(gemm(a, s));
+    a.K = D.ru;
+    a.seg[0] = mseg(L->up.B, w.tu16, w.U16, D.f, D.ru, D.f);
+    DL_HIP(gemm(a, s));
+  }
+  {
+    GemmArgs a{};
+    a.nseg = 1;
+    a.M = M;
+    a.K = D.f;
+    a.xmode = GEMM_X_SWIGLU;
+    a.omode = GEMM_OUT_BF16;
+    a.seg[0] = mseg(L->down.A, w.G16, w.td16, D.rd, D.f, D.rd);
+    a.seg[0].X2 = w.U16;
+    DL_HIP(gemm(a, s));
+    GemmArgs b{};
+    b.nseg = 1;
+    b.M = M;
+    b.K = D.rd;
+    b.omode = GEMM_OUT_BF16_RES_F32;
+    b.seg[0] = mseg(L->down.B, w.td16, y, h, D.rd, h);
+    b.seg[0].R = w.x2f;
+    b.seg[0].ldr = h;
+    DL_HIP(gemm(b, s));
+  }
+  return DL_OK;
+}
+
+}  // extern "C"

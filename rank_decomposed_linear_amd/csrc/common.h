@@ -1,0 +1,85 @@
+// Shared device helpers for the gfx950 kernels: bf16 conversion, MFMA
+// operand types, warp-level reductions, rotary-angle evaluation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dl {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf2f(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ float bflo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bfhi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round two floats to bf16 (nearest even, hardware v_cvt_pk_bf16_f32) and
+// pack them: `lo` in bits 0..15, `hi` in bits 16..31.
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  bf16x2_t v;
+  v.x = static_cast<__bf16>(lo);
+  v.y = static_cast<__bf16>(hi);
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// D(16x16, f32) += A(16x32, bf16) * B(32x16, bf16).
+// Operand registers: lane l holds 8 consecutive-slot values of row/column
+// (l % 16) for reduction slots 8*(l/16) .. 8*(l/16)+7. The accumulator lane
+// l holds D[4*(l/16) + r][l % 16], r = 0..3.
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Pack the four accumulator values of two 16x16 blocks into one operand
+// register set: slots 0..3 from `x`, 4..7 from `y`.
+__device__ __forceinline__ u32x4 pack_acc(f32x4 x, f32x4 y) {
+  u32x4 r;
+  r.x = pack2(x[0], x[1]);
+  r.y = pack2(x[2], x[3]);
+  r.z = pack2(y[0], y[1]);
+  r.w = pack2(y[2], y[3]);
+  return r;
+}
+
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+__device__ __forceinline__ float wave_sum_xor(float v, int mask) {
+  return v + __shfl_xor(v, mask, 64);
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+// Rotary angle pos * w, returned as (cos, sin). `rev` is w / (2*pi) in
+// float64; the product is reduced to a fraction of a turn in float64 so the
+// float32 evaluation sees an argument in [-pi, pi] regardless of pos.
+__device__ __forceinline__ void rope_cs(int pos, double rev, float &c, float &s) {
+  double t = static_cast<double>(pos) * rev;
+  t -= rint(t);
+  const float a = static_cast<float>(t * 6.283185307179586);
+  __sincosf(a, &s, &c);
+}
+
+__device__ __forceinline__ double rope_rev(int i, int d, float theta) {
+  // theta^(-2i/d) / (2*pi)
+  return exp(-2.0 * i / d * log(static_cast<double>(theta))) * 0.15915494309189535;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+}  // namespace dl

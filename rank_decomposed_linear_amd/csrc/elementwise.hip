@@ -1,0 +1,122 @@
+// Small memory-bound helpers of the layer: RMSNorm, accumulator
+// initialisation, conversion and the decode-time cache row store.
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace dl {
+
+namespace {
+
+__device__ __forceinline__ float load_elem(const void *p, int is_f32, size_t i) {
+  return is_f32 ? static_cast<const float *>(p)[i] : bf2f(static_cast<const uint16_t *>(p)[i]);
+}
+
+// One workgroup per row: y = x / sqrt(mean(x^2) + eps) * gamma.
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const void *x, int x_f32, const void *gamma,
+                                                      int gamma_f32, void *y, int y_f32, int n,
+                                                      float eps) {
+  __shared__ float part[4];
+  const size_t row = blockIdx.x;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const float v = load_elem(x, x_f32, row * n + i);
+    ss = fmaf(v, v, ss);
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = part[0] + part[1] + part[2] + part[3];
+  const float rstd = 1.0f / sqrtf(tot / n + eps);
+  for (int i = threadIdx.x; i < n; i += 256) {
+    float v = load_elem(x, x_f32, row * n + i) * rstd;
+    if (gamma) v *= load_elem(gamma, gamma_f32, i);
+    if (y_f32)
+      static_cast<float *>(y)[row * n + i] = v;
+    else
+      static_cast<uint16_t *>(y)[row * n + i] = f2bf(v);
+  }
+}
+
+struct FillPack {
+  FillRegion r[4];
+  int nreg;
+};
+
+__global__ void fill_kernel(FillPack p) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int k = 0; k < p.nreg; ++k) {
+    const FillRegion &rg = p.r[k];
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < rg.n;
+         i += stride) {
+      float v = 0.f;
+      if (rg.src) v = load_elem(rg.src, !rg.src_bf16, static_cast<size_t>(i));
+      rg.dst[i] = v;
+    }
+  }
+}
+
+__global__ void convert_kernel(const float *src, void *dst, int dst_bf16, int64_t n) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+    if (dst_bf16)
+      static_cast<uint16_t *>(dst)[i] = f2bf(src[i]);
+    else
+      static_cast<float *>(dst)[i] = src[i];
+  }
+}
+
+__global__ void store_cache_rows_kernel(const float *src, int ld, void *cache, int cache_bf16,
+                                        const int32_t *past, int T, int r, int L_max) {
+  const int b = blockIdx.x / T, t = blockIdx.x % T;
+  const size_t row = static_cast<size_t>(b) * L_max + past[b] + t;
+  for (int i = threadIdx.x; i < r; i += blockDim.x) {
+    const float v = src[static_cast<size_t>(blockIdx.x) * ld + i];
+    if (cache_bf16)
+      static_cast<uint16_t *>(cache)[row * r + i] = f2bf(v);
+    else
+      static_cast<float *>(cache)[row * r + i] = v;
+  }
+}
+
+int grid_for(int64_t n) {
+  int64_t g = (n + 255) / 256;
+  if (g > 4096) g = 4096;
+  if (g < 1) g = 1;
+  return static_cast<int>(g);
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm(const void *x, int x_f32, const void *gamma, int gamma_f32, void *y,
+                          int y_f32, int M, int n, float eps, hipStream_t s) {
+  rmsnorm_kernel<<<M, 256, 0, s>>>(x, x_f32, gamma, gamma_f32, y, y_f32, n, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill(const FillRegion *r, int nreg, hipStream_t s) {
+  FillPack p{};
+  int64_t mx = 0;
+  for (int i = 0; i < nreg && i < 4; ++i) {
+    p.r[i] = r[i];
+    if (r[i].n > mx) mx = r[i].n;
+  }
+  p.nreg = nreg < 4 ? nreg : 4;
+  fill_kernel<<<grid_for(mx), 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_convert_f32(const float *src, void *dst, int dst_bf16, int64_t n, hipStream_t s) {
+  convert_kernel<<<grid_for(n), 256, 0, s>>>(src, dst, dst_bf16, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_store_cache_rows(const float *src, int ld, void *cache, int cache_bf16,
+                                   const int32_t *past, int Bsz, int T, int r, int L_max,
+                                   hipStream_t s) {
+  store_cache_rows_kernel<<<Bsz * T, 256, 0, s>>>(src, ld, cache, cache_bf16, past, T, r, L_max);
+  return hipGetLastError();
+}
+
+}  // namespace dl

@@ -310,3 +310,9 @@ def factor_pair_flops(shape: LayerShape, tokens: int) -> Dict[str, int]:
     """2*M*(m*k + k*n) per projection pair for M tokens."""
     return {p: 2 * tokens * (m * shape.rank(p) + shape.rank(p) * n)
             for p, (m, n) in shape.shapes().items()}
+
+
+def random_array(rng: np.random.Generator, shape, std: float, dtype: str) -> np.ndarray:
+    """A seeded N(0, std^2) array in storage encoding ("bf16" -> uint16 bits,
+    "f32" -> float32), for tests of single entry points."""
+    return _encode(_normal(rng, shape, std), dtype)
