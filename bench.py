@@ -1,0 +1,359 @@
+#!/usr/bin/env python3
+"""Throughput of one SVD-decomposed transformer layer on one MI355X.
+
+Headline: decode tokens/s of a LLaMA-3-8B-shaped decomposed layer at 40%
+compression (batch 16, 1024 cached tokens, one new token per sequence per
+step), every projection a factor pair (W ~ A B) and attention rebuilding K/V
+from the low-rank cache. The same JSON line carries the prefill figure of a
+LLaMA-3-70B-shaped layer at 50% (8 sequences x 2048 tokens, TFLOP/s), the
+roofline of the dominant decode kernel, a per-kernel breakdown, and the fp64
+CPU oracle timed on a bounded sample of the decode workload.
+
+A "step" is one dl_decomposed_layer_fwd call over the whole batch. Inputs
+are seeded synthetic data resident in HBM before timing starts; two
+independent device copies of weights and cache are used in turn so the
+256 MB Infinity Cache cannot serve one step from the previous one. Steps are
+replayed from a HIP graph (one per copy) unless --no-graph.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decomposed-layer decode tokens/s + % HBM peak; prefill TFLOP/s + % MFMA peak"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="llama3_8b_c40_decode_b16_l1024")
+    p.add_argument("--prefill-workload", default="llama3_70b_c50_prefill_8x2048")
+    p.add_argument("--prefill-steps", type=int, default=4)
+    p.add_argument("--trace-steps", type=int, default=20)
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--no-graph", action="store_true")
+    p.add_argument("--sets", type=int, default=2)
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# algorithmic work per launch role (bytes moved at minimum / flops of the method)
+# ----------------------------------------------------------------------------
+def decode_role_work(shape, M, ctx_total):
+    """Per-step algorithmic bytes of each GEMV role and of the attention
+    kernel (bf16 weights / cache, f32 latent accumulators), and attention
+    flops. ctx_total = sum over sequences of the rows attended."""
+    h, f, qd, kvd = shape.hidden, shape.ffn, shape.n_q * shape.head_dim, shape.n_kv * shape.head_dim
+    r = {p: shape.rank(p) for p in ("q", "k", "v", "o", "gate", "up", "down")}
+    es, acc = 2, 4
+    gemv = {
+        "qkv_down": es * h * (r["q"] + r["k"] + r["v"]) + M * h * es + M * (r["q"] + r["k"] + r["v"]) * acc,
+        "q_up": es * r["q"] * qd + M * r["q"] * acc + M * qd * acc,
+        "o_down": es * qd * r["o"] + M * qd * es + M * r["o"] * acc,
+        "o_up": es * r["o"] * h + M * r["o"] * acc + M * h * acc,
+        "gate_up_down": es * h * (r["gate"] + r["up"]) + M * h * es + M * (r["gate"] + r["up"]) * acc,
+        "gate_up_up": es * (r["gate"] + r["up"]) * f + M * (r["gate"] + r["up"]) * acc + 2 * M * f * acc,
+        "down_down": es * f * r["down"] + 2 * M * f * acc + M * r["down"] * acc,
+        "down_up": es * r["down"] * h + M * r["down"] * acc + M * h * acc,
+    }
+    attn_bytes = ctx_total * (r["k"] + r["v"]) * es + es * kvd * (r["k"] + r["v"]) + M * qd * acc
+    attn_flops = ctx_total * (2 * (r["k"] + r["v"]) * kvd + 4 * qd)
+    return gemv, attn_bytes, attn_flops
+
+
+def prefill_flops(shape, Bsz, T):
+    """Algorithmic flops of one prefill step: all factor pairs over M = Bsz*T
+    tokens (the k/v up halves are the one-time rebuild of every cached row)
+    plus the causal attention core 4 * n_q * d per (query, visible key)."""
+    M = Bsz * T
+    pairs = sum(2 * M * (m * shape.rank(p) + shape.rank(p) * n) for p, (m, n) in shape.shapes().items())
+    core = Bsz * (T * (T + 1) // 2) * 4 * shape.n_q * shape.head_dim
+    gemm = pairs - sum(2 * M * shape.rank(p) * n for p, (m, n) in shape.shapes().items() if p in ("k", "v"))
+    return pairs + core, gemm, core
+
+
+# ----------------------------------------------------------------------------
+# GPU runs
+# ----------------------------------------------------------------------------
+def to_dev(torch, a):
+    import numpy as np
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+    if a.dtype == np.int32:
+        return torch.from_numpy(a).to("cuda:0")
+    return torch.from_numpy(a.astype(np.float32)).to("cuda:0")
+
+
+def make_sets(torch, binding, weights, inp, nsets):
+    shp = weights.shape
+    Bsz, T = inp.x.shape[0], inp.x.shape[1]
+    L_max = inp.ck.shape[1]
+    sets = []
+    for _ in range(nsets):
+        facs = {p: (to_dev(torch, a), to_dev(torch, b)) for p, (a, b) in weights.factors.items()}
+        layer = binding.DecomposedLayer(facs, shp.hidden, shp.n_q, shp.n_kv, shp.head_dim, shp.ffn,
+                                        shp.rope_theta, shp.rms_eps)
+        st = dict(layer=layer, x=to_dev(torch, inp.x), ck=to_dev(torch, inp.ck),
+                  cv=to_dev(torch, inp.cv), past=to_dev(torch, inp.past_lens))
+        st["y"] = torch.empty_like(st["x"])
+        st["ws"] = torch.empty(max(layer.workspace_bytes(Bsz, T, L_max), 16), dtype=torch.uint8,
+                               device="cuda:0")
+        sets.append(st)
+    return sets
+
+
+def run_step(st):
+    st["layer"].forward(st["x"], st["ck"], st["cv"], st["past"], y=st["y"], ws=st["ws"])
+
+
+def capture_graphs(torch, sets):
+    graphs = []
+    side = torch.cuda.Stream()
+    for st in sets:
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run_step(st)
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run_step(st)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def timed(torch, fn, steps, warmup):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        fn(i)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    return t0.elapsed_time(t1) / steps, wall
+
+
+def trace_breakdown(torch, binding, sets, nsteps):
+    """Per-kernel durations from hipEvents recorded around every library
+    launch, over nsteps eager steps. Returns {(kind, role): [ms, ...]}."""
+    tr = binding.KernelTrace(capacity=64 * nsteps + 64)
+    torch.cuda.synchronize()
+    with tr:
+        for i in range(nsteps):
+            run_step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    per = {}
+    for kind, role, ms in tr.records():
+        per.setdefault((kind, role), []).append(ms)
+    tr.close()
+    return per
+
+
+def decode_bench(args, torch, binding, W):
+    w = W.by_name(args.workload)
+    log(f"decode workload {w.name}: drawing inputs")
+    weights, inp = W.draw(w)
+    sets = make_sets(torch, binding, weights, inp, args.sets)
+    Bsz = w.batch
+    # eager reference output of set 0, then (optionally) graphs
+    run_step(sets[0])
+    torch.cuda.synchronize()
+    y_eager = sets[0]["y"].float().clone()
+    use_graph = not args.no_graph
+    graphs = None
+    if use_graph:
+        try:
+            graphs = capture_graphs(torch, sets)
+            for _ in range(3):
+                graphs[0].replay()
+                torch.cuda.synchronize()
+                err = (sets[0]["y"].float() - y_eager).abs().max().item()
+                if not err <= 1e-2 * y_eager.abs().max().item():
+                    raise RuntimeError(f"graph replay differs from eager output by {err}")
+        except Exception as e:  # keep the eager figure if capture is refused
+            log(f"graph capture disabled: {e}")
+            use_graph, graphs = False, None
+    if graphs:
+        fn = lambda i: graphs[i % len(graphs)].replay()
+    else:
+        fn = lambda i: run_step(sets[i % len(sets)])
+    log(f"timing {args.steps} steps after {args.warmup} warmup (graph={use_graph})")
+    ms, wall = timed(torch, fn, args.steps, args.warmup)
+
+    per = trace_breakdown(torch, binding, sets, args.trace_steps)
+    ctx_total = int(sum(int(p) + 1 for p in inp.past_lens))
+    gemv_bytes, attn_bytes, attn_flops = decode_role_work(w.shape, Bsz, ctx_total)
+    n = args.trace_steps
+    kinds = {}
+    for (kind, role), lst in per.items():
+        k = kinds.setdefault(kind, {"ms_per_step": 0.0, "launches_per_step": 0, "bytes_per_step": 0,
+                                    "flops_per_step": 0})
+        k["ms_per_step"] += sum(lst) / n
+        k["launches_per_step"] += len(lst) // n
+        if kind == "gemv_bf16":
+            k["bytes_per_step"] += gemv_bytes.get(role, 0) * (len(lst) // n)
+        if kind == "attn_decode_bf16":
+            k["bytes_per_step"] += attn_bytes
+            k["flops_per_step"] += attn_flops
+    breakdown = {}
+    for kind, k in sorted(kinds.items(), key=lambda kv: -kv[1]["ms_per_step"]):
+        e = {"us_per_step": round(k["ms_per_step"] * 1e3, 2), "launches_per_step": k["launches_per_step"],
+             "avg_us": round(k["ms_per_step"] * 1e3 / max(k["launches_per_step"], 1), 2)}
+        if k["bytes_per_step"]:
+            gbs = k["bytes_per_step"] / (k["ms_per_step"] * 1e-3) / 1e9
+            e["GB_per_s"] = round(gbs, 1)
+            e["hbm_frac"] = round(gbs / HBM_PEAK_GBS, 4)
+        if k["flops_per_step"]:
+            tf = k["flops_per_step"] / (k["ms_per_step"] * 1e-3) / 1e12
+            e["TFLOP_per_s"] = round(tf, 2)
+            e["mfma_frac"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
+        breakdown[kind] = e
+    roles = {f"{kind}/{role}": round(sum(lst) / n * 1e3, 2) for (kind, role), lst in sorted(per.items())}
+
+    # dominant kernel of the step
+    dom = max(kinds.items(), key=lambda kv: kv[1]["ms_per_step"])
+    dname, dk = dom
+    nl = max(dk["launches_per_step"], 1)
+    avg_s = dk["ms_per_step"] * 1e-3 / nl
+    if dname == "attn_decode_bf16":
+        achieved = dk["flops_per_step"] / nl / avg_s / 1e12
+        roof = {"kernel": dname, "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "avg_us": round(avg_s * 1e6, 2), "launches_per_step": nl}
+    else:
+        achieved = dk["bytes_per_step"] / nl / avg_s / 1e9
+        roof = {"kernel": dname, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "avg_us": round(avg_s * 1e6, 2), "launches_per_step": nl,
+                "algorithmic_bytes_per_launch": int(dk["bytes_per_step"] / nl)}
+    step_bytes = W.algorithmic_decode_bytes(w.shape, Bsz, ctx_total // Bsz)["total"]
+    result = {
+        "value": Bsz / (ms * 1e-3), "ms_per_step": ms, "wall_s": wall, "graph": use_graph,
+        "roofline": roof, "kernels": breakdown, "roles_us_per_step": roles,
+        "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "config": {"workload": w.name, "batch": Bsz, "context": int(inp.past_lens[0]) + 1,
+                   "hidden": w.shape.hidden, "n_q": w.shape.n_q, "n_kv": w.shape.n_kv,
+                   "head_dim": w.shape.head_dim, "ffn": w.shape.ffn,
+                   "compression_pct": w.compression_pct, "ranks": dict(w.shape.ranks),
+                   "weight_sets": args.sets},
+    }
+    return result, weights, inp
+
+
+def prefill_bench(args, torch, binding, W):
+    w = W.by_name(args.prefill_workload)
+    log(f"prefill workload {w.name}: drawing inputs")
+    weights, inp = W.draw(w)
+    sets = make_sets(torch, binding, weights, inp, 1)
+    fn = lambda i: run_step(sets[0])
+    ms, wall = timed(torch, fn, args.prefill_steps, 1)
+    per = trace_breakdown(torch, binding, sets, 1)
+    total, gemm, core = prefill_flops(w.shape, w.batch, w.prefill)
+    gemm_ms = sum(sum(v) for (k, _), v in per.items() if k == "gemm_bf16")
+    attn_ms = sum(sum(v) for (k, _), v in per.items() if k == "attn_prefill_bf16")
+    tf = total / (ms * 1e-3) / 1e12
+    gemm_tf = gemm / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None
+    out = {"workload": w.name, "TFLOP_per_s": round(tf, 2),
+           "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "ms_per_step": round(ms, 3),
+           "algorithmic_TFLOP_per_step": round(total / 1e12, 3),
+           "gemm_TFLOP_per_s": round(gemm_tf, 2) if gemm_tf else None,
+           "gemm_mfma_frac": round(gemm_tf / MFMA_BF16_PEAK_TFLOPS, 4) if gemm_tf else None,
+           "gemm_ms": round(gemm_ms, 3), "attention_ms": round(attn_ms, 3),
+           "steps": args.prefill_steps}
+    del sets
+    torch.cuda.empty_cache()
+    return out
+
+
+# ----------------------------------------------------------------------------
+# CPU oracle baseline
+# ----------------------------------------------------------------------------
+def cpu_baseline(args, W, weights, inp):
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from oracle import ref
+
+    ncores = len(os.sched_getaffinity(0))
+    F = {p: (W.decode_array(a).astype(np.float64), W.decode_array(b).astype(np.float64))
+         for p, (a, b) in weights.factors.items()}
+    x, ck, cv = (W.decode_array(a).astype(np.float64) for a in (inp.x, inp.ck, inp.cv))
+    shp = weights.shape
+    with threadpool_limits(limits=ncores):
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        steps, t0 = 0, time.perf_counter()
+        while True:
+            ref.decomposed_layer(F, x, ck, cv, inp.past_lens, shp.n_q, shp.n_kv, shp.head_dim,
+                                 shp.rope_theta, shp.rms_eps)
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or steps >= 1000:
+                break
+    Bsz = inp.x.shape[0]
+    return {"value": round(Bsz * steps / el, 3), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{steps} full decode steps of the same workload (batch {Bsz}, "
+                      f"context {int(inp.past_lens[0]) + 1}), fp64 numpy, {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(requested --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from rank_decomposed_linear_amd import binding, workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    binding.load()
+    dec, weights, inp = decode_bench(args, torch, binding, W)
+    log(f"decode: {dec['value']:.0f} tokens/s, {dec['ms_per_step'] * 1e3:.1f} us/step")
+    pre = None
+    if not args.no_prefill:
+        pre = prefill_bench(args, torch, binding, W)
+        log(f"prefill: {pre['TFLOP_per_s']} TFLOP/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        cpu = cpu_baseline(args, W, weights, inp)
+    line = {
+        "metric": METRIC, "value": round(dec["value"], 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(dec["ms_per_step"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; random-init factors, pre-filled low-rank cache)",
+        "config": dec["config"], "graph": dec["graph"],
+        "roofline": dec["roofline"], "step_hbm_frac": dec["step_hbm_frac"],
+        "cpu_baseline": cpu, "prefill": pre, "kernels": dec["kernels"],
+        "roles_us_per_step": dec["roles_us_per_step"],
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -180,6 +180,28 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y,
                                   int64_t T, int64_t L_max, void *ws,
                                   size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Kernel timing hook (instrumentation; not part of the method).
+ * While a trace is installed, every kernel the library enqueues is
+ * bracketed by hipEventRecord(events[2i]) and hipEventRecord(events[2i+1])
+ * on the call's stream, where i counts traced launches; kinds[i] names the
+ * kernel (dl_kernel_kind_name) and roles[i] the step of the layer it serves
+ * (dl_role_name). Launches beyond `capacity` run untraced. The events are
+ * hipEvent_t created by the caller; the library only records them.
+ * Installation is process-wide and not thread-safe; NULL uninstalls.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  void **events;     /* 2 * capacity hipEvent_t */
+  int32_t *kinds;    /* capacity entries */
+  int32_t *roles;    /* capacity entries */
+  int32_t capacity;
+  int32_t count;     /* traced launches so far (advanced by the library) */
+} dl_trace;
+
+void dl_trace_install(dl_trace *t);
+const char *dl_kernel_kind_name(int32_t kind);
+const char *dl_role_name(int32_t role);
+
 #ifdef __cplusplus
 }
 #endif

@@ -129,16 +129,18 @@ def softmax_attend(q_rot, q_pos, K, V, sm_scale: float) -> np.ndarray:
     T, n_q, d = q_rot.shape
     n_kv = K.shape[1]
     group = n_q // n_kv
+    Kh = np.ascontiguousarray(np.transpose(K, (1, 0, 2)))   # [n_kv, L, d]
+    Vh = np.ascontiguousarray(np.transpose(V, (1, 0, 2)))
     out = np.zeros((T, n_q, d), dtype=F64)
     for t in range(T):
         p = int(q_pos[t])
-        for h in range(n_q):
-            g = h // group
-            s = (K[:p + 1, g, :] @ q_rot[t, h]) * sm_scale
-            s = s - s.max()
+        for g in range(n_kv):
+            heads = slice(g * group, (g + 1) * group)        # query heads reading kv head g
+            s = (Kh[g, :p + 1] @ q_rot[t, heads].T) * sm_scale   # [p+1, group]
+            s = s - s.max(axis=0, keepdims=True)
             w = np.exp(s)
-            w = w / w.sum()
-            out[t, h] = w @ V[:p + 1, g, :]
+            w = w / w.sum(axis=0, keepdims=True)
+            out[t, heads] = w.T @ Vh[g, :p + 1]
     return out
 
 

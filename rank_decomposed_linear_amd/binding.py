@@ -28,6 +28,7 @@ EXPORTS = (
     "dl_attn_decode_workspace", "dl_lowrank_attn_decode",
     "dl_attn_prefill_workspace", "dl_lowrank_attn_prefill",
     "dl_layer_workspace", "dl_decomposed_layer_fwd",
+    "dl_trace_install", "dl_kernel_kind_name", "dl_role_name",
 )
 
 
@@ -49,6 +50,13 @@ class Layer(ctypes.Structure):
                 ("attn_norm", ctypes.c_void_p), ("mlp_norm", ctypes.c_void_p),
                 ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
                 ("dt", ctypes.c_int)]
+
+
+class TraceStruct(ctypes.Structure):
+    _fields_ = [("events", ctypes.POINTER(ctypes.c_void_p)),
+                ("kinds", ctypes.POINTER(ctypes.c_int32)),
+                ("roles", ctypes.POINTER(ctypes.c_int32)),
+                ("capacity", ctypes.c_int32), ("count", ctypes.c_int32)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -90,8 +98,71 @@ def load() -> ctypes.CDLL:
     lib.dl_decomposed_layer_fwd.restype = ctypes.c_int
     lib.dl_decomposed_layer_fwd.argtypes = [ctypes.POINTER(Layer), _vp, _vp, _vp, _vp, _vp, _vp,
                                             _i64, _i64, _i64, _vp, _sz, _vp]
+    lib.dl_trace_install.restype = None
+    lib.dl_trace_install.argtypes = [ctypes.POINTER(TraceStruct)]
+    lib.dl_kernel_kind_name.restype = ctypes.c_char_p
+    lib.dl_kernel_kind_name.argtypes = [ctypes.c_int32]
+    lib.dl_role_name.restype = ctypes.c_char_p
+    lib.dl_role_name.argtypes = [ctypes.c_int32]
     _lib = lib
     return lib
+
+
+def _hip_runtime() -> ctypes.CDLL:
+    """The HIP runtime already loaded by torch (same soname as libdlayer's)."""
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    return hip
+
+
+class KernelTrace:
+    """Records a hipEvent pair around every kernel the library launches
+    while installed (dl_trace_install). Use as a context manager; after a
+    device synchronisation, records() yields (kind, role, milliseconds)."""
+
+    def __init__(self, capacity: int = 4096):
+        torch.cuda.init()
+        self.hip = _hip_runtime()
+        self.capacity = capacity
+        self.events = (ctypes.c_void_p * (2 * capacity))()
+        for i in range(2 * capacity):
+            ev = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.events[i] = ev.value
+        self.kinds = (ctypes.c_int32 * capacity)()
+        self.roles = (ctypes.c_int32 * capacity)()
+        self.st = TraceStruct(self.events, self.kinds, self.roles, capacity, 0)
+
+    def __enter__(self):
+        self.st.count = 0
+        load().dl_trace_install(ctypes.byref(self.st))
+        return self
+
+    def __exit__(self, *exc):
+        load().dl_trace_install(None)
+        return False
+
+    def records(self):
+        lib = load()
+        out = []
+        for i in range(self.st.count):
+            ms = ctypes.c_float()
+            if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.events[2 * i],
+                                            self.events[2 * i + 1]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed (synchronise first)")
+            out.append((lib.dl_kernel_kind_name(self.kinds[i]).decode(),
+                        lib.dl_role_name(self.roles[i]).decode(), float(ms.value)))
+        return out
+
+    def close(self):
+        for i in range(2 * self.capacity):
+            if self.events[i]:
+                self.hip.hipEventDestroy(self.events[i])
+                self.events[i] = None
 
 
 def _check(status: int) -> None:

@@ -14,8 +14,44 @@
 #include "../../include/dl.h"
 #include "common.h"
 #include "kernels.h"
+#include "trace.h"
 
 using namespace dl;
+
+// ---------------------------------------------------------------------------
+// Launch tracing (dl_trace)
+// ---------------------------------------------------------------------------
+namespace {
+dl_trace *g_trace = nullptr;
+int g_role = R_OTHER;
+bool g_open = false;
+
+const char *const kKindNames[K_NUM_KINDS] = {
+    "rmsnorm",       "fill",        "convert",      "store_cache_rows",
+    "gemv_bf16",     "gemm_bf16",   "gemm_f32",     "pack_up_factor",
+    "attn_decode_bf16", "attn_combine", "attn_prefill_bf16", "attn_f32"};
+const char *const kRoleNames[R_NUM_ROLES] = {
+    "other",        "attn_norm",    "qkv_down", "kv_store",  "q_up",
+    "attention",    "o_down",       "o_up",     "mlp_norm",  "gate_up_down",
+    "gate_up_up",   "down_down",    "down_up",  "output",    "init"};
+}  // namespace
+
+namespace dl {
+void set_role(int role) { g_role = role; }
+void trace_begin(int kind, hipStream_t s) {
+  g_open = g_trace && g_trace->count < g_trace->capacity;
+  if (!g_open) return;
+  g_trace->kinds[g_trace->count] = kind;
+  (void)hipEventRecord(static_cast<hipEvent_t>(g_trace->events[2 * g_trace->count]), s);
+}
+void trace_end(hipStream_t s) {
+  if (!g_open) return;
+  (void)hipEventRecord(static_cast<hipEvent_t>(g_trace->events[2 * g_trace->count + 1]), s);
+  g_trace->roles[g_trace->count] = g_role;
+  g_trace->count++;
+  g_open = false;
+}
+}  // namespace dl
 
 namespace {
 
@@ -273,6 +309,17 @@ extern "C" {
 
 const char *dl_last_error(void) { return g_last_error.c_str(); }
 
+void dl_trace_install(dl_trace *t) {
+  g_trace = t;
+  g_open = false;
+}
+const char *dl_kernel_kind_name(int32_t kind) {
+  return (kind >= 0 && kind < K_NUM_KINDS) ? kKindNames[kind] : "unknown";
+}
+const char *dl_role_name(int32_t role) {
+  return (role >= 0 && role < R_NUM_ROLES) ? kRoleNames[role] : "unknown";
+}
+
 // ===========================================================================
 // dl_lowrank_linear
 // ===========================================================================
@@ -294,6 +341,7 @@ size_t dl_lowrank_linear_workspace(int64_t M, int64_t m, int64_t k, int64_t n, d
 dl_status dl_lowrank_linear(const void *x, const void *A, const void *B, void *y, int64_t M,
                             int64_t m, int64_t k, int64_t n, dl_dtype dt, void *ws,
                             size_t ws_bytes, void *stream) {
+  set_role(R_OTHER);
   DL_CHECK(valid_dtype(dt), DL_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
   DL_CHECK(x && A && B && y, DL_ERR_INVALID_ARG, "null tensor pointer");
   DL_CHECK(M > 0 && m > 0 && k > 0 && n > 0, DL_ERR_INVALID_ARG, "dims must be positive");
@@ -381,6 +429,7 @@ dl_status dl_lowrank_kv_append(const void *x, const void *A_k, const void *A_v, 
                                void *Cv, const int32_t *past_lens, int64_t Bsz, int64_t T,
                                int64_t m, int64_t r_k, int64_t r_v, int64_t L_max, dl_dtype dt,
                                void *ws, size_t ws_bytes, void *stream) {
+  set_role(R_OTHER);
   DL_CHECK(valid_dtype(dt), DL_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
   DL_CHECK(x && A_k && A_v && Ck && Cv && past_lens, DL_ERR_INVALID_ARG, "null pointer");
   DL_CHECK(Bsz > 0 && T > 0 && m > 0 && r_k > 0 && r_v > 0 && L_max > 0, DL_ERR_INVALID_ARG,
@@ -462,6 +511,7 @@ static dl_status attn_common(const void *q, const void *Ck, const void *Cv, cons
                              int64_t T, int64_t n_q, int64_t n_kv, int64_t d, int64_t r_k,
                              int64_t r_v, int64_t L_max, float sm_scale, float rope_theta,
                              dl_dtype dt, void *ws, size_t ws_bytes, void *stream, bool decode) {
+  set_role(R_OTHER);
   DL_CHECK(valid_dtype(dt), DL_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
   DL_CHECK(q && Ck && Cv && B_k && B_v && lens && out, DL_ERR_INVALID_ARG, "null pointer");
   DL_CHECK(Bsz > 0 && T > 0 && L_max > 0, DL_ERR_INVALID_ARG, "dims must be positive");
@@ -662,6 +712,7 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
                                   void *Ck, void *Cv, const int32_t *past_lens, int64_t Bsz,
                                   int64_t T, int64_t L_max, void *ws, size_t ws_bytes,
                                   void *stream) {
+  set_role(R_OTHER);
   LayerDims D{};
   dl_status st = layer_dims(L, Bsz, T, L_max, &D);
   if (st != DL_OK) return st;
@@ -686,13 +737,17 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
 
   if (L->dt == DL_F32) {
     const float *xf = static_cast<const float *>(x);
+    set_role(R_ATTN_NORM);
     DL_HIP(launch_rmsnorm(x, 1, L->attn_norm, 1, w.a, 1, M, h, eps, s));
+    set_role(R_QKV_DOWN);
     DL_HIP(gemm_f32(w.a, nullptr, L->k.A, static_cast<float *>(Ck), M, D.rk, h, h, D.rk,
                     F32_OUT_CACHE, nullptr, 0, past_lens, D.T, D.L_max, s));
     DL_HIP(gemm_f32(w.a, nullptr, L->v.A, static_cast<float *>(Cv), M, D.rv, h, h, D.rv,
                     F32_OUT_CACHE, nullptr, 0, past_lens, D.T, D.L_max, s));
+    set_role(R_QKV_DOWN);
     DL_HIP(gemm_f32(w.a, nullptr, L->q.A, w.tq, M, D.rq, h, h, D.rq, F32_OUT_STORE, nullptr, 0,
                     nullptr, 1, 0, s));
+    set_role(R_Q_UP);
     DL_HIP(gemm_f32(w.tq, nullptr, L->q.B, w.qf, M, qd, D.rq, D.rq, qd, F32_OUT_STORE, nullptr, 0,
                     nullptr, 1, 0, s));
     AttnF32Args a{};
@@ -715,23 +770,31 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
     a.ldq = qd;
     a.sm_scale = 1.0f / sqrtf(static_cast<float>(D.d));
     a.theta = L->rope_theta;
+    set_role(R_ATTENTION);
     DL_HIP(launch_attn_f32(a, s));
+    set_role(R_O_DOWN);
     DL_HIP(gemm_f32(w.att, nullptr, L->o.A, w.to, M, D.ro, qd, qd, D.ro, F32_OUT_STORE, nullptr, 0,
                     nullptr, 1, 0, s));
     float *x2 = x2_out ? static_cast<float *>(x2_out) : w.x2;
+    set_role(R_O_UP);
     DL_HIP(gemm_f32(w.to, nullptr, L->o.B, x2, M, h, D.ro, D.ro, h, F32_OUT_RESID, xf, h, nullptr,
                     1, 0, s));
+    set_role(R_MLP_NORM);
     DL_HIP(launch_rmsnorm(x2, 1, L->mlp_norm, 1, w.b, 1, M, h, eps, s));
+    set_role(R_GATE_UP_DOWN);
     DL_HIP(gemm_f32(w.b, nullptr, L->gate.A, w.tg, M, D.rg, h, h, D.rg, F32_OUT_STORE, nullptr, 0,
                     nullptr, 1, 0, s));
     DL_HIP(gemm_f32(w.b, nullptr, L->up.A, w.tu, M, D.ru, h, h, D.ru, F32_OUT_STORE, nullptr, 0,
                     nullptr, 1, 0, s));
+    set_role(R_GATE_UP_UP);
     DL_HIP(gemm_f32(w.tg, nullptr, L->gate.B, w.G, M, D.f, D.rg, D.rg, D.f, F32_OUT_STORE, nullptr,
                     0, nullptr, 1, 0, s));
     DL_HIP(gemm_f32(w.tu, nullptr, L->up.B, w.U, M, D.f, D.ru, D.ru, D.f, F32_OUT_STORE, nullptr, 0,
                     nullptr, 1, 0, s));
+    set_role(R_DOWN_DOWN);
     DL_HIP(gemm_f32(w.G, w.U, L->down.A, w.td, M, D.rd, D.f, D.f, D.rd, F32_OUT_STORE, nullptr, 0,
                     nullptr, 1, 0, s));
+    set_role(R_DOWN_UP);
     DL_HIP(gemm_f32(w.td, nullptr, L->down.B, static_cast<float *>(y), M, h, D.rd, D.rd, h,
                     F32_OUT_RESID, x2, h, nullptr, 1, 0, s));
     return DL_OK;
@@ -740,7 +803,9 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
   if (use_gemv(M)) {
     const int rqkv = D.rq + D.rk + D.rv;
     FillRegion init[2] = {{w.acc0, nullptr, 0, w.acc_len}, {w.x2f, x, 1, (int64_t)M * h}};
+    set_role(R_INIT);
     DL_HIP(launch_fill(init, 2, s));
+    set_role(R_ATTN_NORM);
     DL_HIP(launch_rmsnorm(x, 0, L->attn_norm, gf32, w.a16, 0, M, h, eps, s));
     {  // grouped down-projections of q, k, v: one pass over the normed activations
       GemvArgs a{};
@@ -751,8 +816,10 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
       a.seg[0] = gseg(L->q.A, w.a16, nullptr, w.t_qkv, D.rq, h, rqkv);
       a.seg[1] = gseg(L->k.A, w.a16, nullptr, w.t_qkv + D.rq, D.rk, h, rqkv);
       a.seg[2] = gseg(L->v.A, w.a16, nullptr, w.t_qkv + D.rq + D.rk, D.rv, h, rqkv);
+      set_role(R_QKV_DOWN);
       DL_HIP(gemv(a, s));
     }
+    set_role(R_KV_STORE);
     DL_HIP(launch_store_cache_rows(w.t_qkv + D.rq, rqkv, Ck, 1, past_lens, D.Bsz, D.T, D.rk,
                                    D.L_max, s));
     DL_HIP(launch_store_cache_rows(w.t_qkv + D.rq + D.rk, rqkv, Cv, 1, past_lens, D.Bsz, D.T, D.rv,
@@ -764,8 +831,10 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
       a.K = D.rq;
       a.xmode = GEMV_X_F32;
       a.seg[0] = gseg(L->q.B, w.t_qkv, nullptr, w.q32, qd, rqkv, qd);
+      set_role(R_Q_UP);
       DL_HIP(gemv(a, s));
     }
+    set_role(R_ATTENTION);
     DL_HIP(run_attn_bf16(w.q32, 1, qd, Ck, Cv, L->k.B, L->v.B, past_lens, 1, D.T == 1, w.att16, 0,
                          D.Bsz, D.T, D.nq, D.nkv, D.d, D.rk, D.rv, D.L_max, 0.f, L->rope_theta, c,
                          s));
@@ -776,6 +845,7 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
       a.K = qd;
       a.xmode = GEMV_X_BF16;
       a.seg[0] = gseg(L->o.A, w.att16, nullptr, w.t_o, D.ro, qd, D.ro);
+      set_role(R_O_DOWN);
       DL_HIP(gemv(a, s));
       GemvArgs b{};
       b.nseg = 1;
@@ -783,12 +853,15 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
       b.K = D.ro;
       b.xmode = GEMV_X_F32;
       b.seg[0] = gseg(L->o.B, w.t_o, nullptr, w.x2f, h, D.ro, h);
+      set_role(R_O_UP);
       DL_HIP(gemv(b, s));
     }
     if (x2_out) {
       FillRegion cp[1] = {{static_cast<float *>(x2_out), w.x2f, 0, (int64_t)M * h}};
+      set_role(R_OUTPUT);
       DL_HIP(launch_fill(cp, 1, s));
     }
+    set_role(R_MLP_NORM);
     DL_HIP(launch_rmsnorm(w.x2f, 1, L->mlp_norm, gf32, w.b16, 0, M, h, eps, s));
     {
       GemvArgs a{};
@@ -798,6 +871,7 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
       a.xmode = GEMV_X_BF16;
       a.seg[0] = gseg(L->gate.A, w.b16, nullptr, w.t_gu, D.rg, h, D.rg + D.ru);
       a.seg[1] = gseg(L->up.A, w.b16, nullptr, w.t_gu + D.rg, D.ru, h, D.rg + D.ru);
+      set_role(R_GATE_UP_DOWN);
       DL_HIP(gemv(a, s));
     }
     if (D.rg == D.ru) {
@@ -808,6 +882,7 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
       a.xmode = GEMV_X_F32;
       a.seg[0] = gseg(L->gate.B, w.t_gu, nullptr, w.G32, D.f, D.rg + D.ru, D.f);
       a.seg[1] = gseg(L->up.B, w.t_gu + D.rg, nullptr, w.U32, D.f, D.rg + D.ru, D.f);
+      set_role(R_GATE_UP_UP);
       DL_HIP(gemv(a, s));
     } else {
       GemvArgs a{};
@@ -816,6 +891,7 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
       a.K = D.rg;
       a.xmode = GEMV_X_F32;
       a.seg[0] = gseg(L->gate.B, w.t_gu, nullptr, w.G32, D.f, D.rg + D.ru, D.f);
+      set_role(R_GATE_UP_UP);
       DL_HIP(gemv(a, s));
       a.K = D.ru;
       a.seg[0] = gseg(L->up.B, w.t_gu + D.rg, nullptr, w.U32, D.f, D.rg + D.ru, D.f);
@@ -828,6 +904,7 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
       a.K = D.f;
       a.xmode = GEMV_X_SWIGLU_F32;
       a.seg[0] = gseg(L->down.A, w.G32, w.U32, w.t_d, D.rd, D.f, D.rd);
+      set_role(R_DOWN_DOWN);
       DL_HIP(gemv(a, s));
       GemvArgs b{};
       b.nseg = 1;
@@ -835,13 +912,16 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
       b.K = D.rd;
       b.xmode = GEMV_X_F32;
       b.seg[0] = gseg(L->down.B, w.t_d, nullptr, w.x2f, h, D.rd, h);  // x2 + MLP = y
+      set_role(R_DOWN_UP);
       DL_HIP(gemv(b, s));
     }
+    set_role(R_OUTPUT);
     DL_HIP(launch_convert_f32(w.x2f, y, 1, (int64_t)M * h, s));
     return DL_OK;
   }
 
   // bf16 GEMM path
+  set_role(R_ATTN_NORM);
   DL_HIP(launch_rmsnorm(x, 0, L->attn_norm, gf32, w.a16, 0, M, h, eps, s));
   {
     GemmArgs a{};
@@ -850,6 +930,7 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
     a.K = h;
     a.omode = GEMM_OUT_BF16;
     a.seg[0] = mseg(L->q.A, w.a16, w.tq16, D.rq, h, D.rq);
+    set_role(R_QKV_DOWN);
     DL_HIP(gemm(a, s));
     GemmArgs b{};
     b.nseg = 2;
@@ -868,8 +949,10 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
     q.K = D.rq;
     q.omode = GEMM_OUT_BF16;
     q.seg[0] = mseg(L->q.B, w.tq16, w.q16, qd, D.rq, qd);
+    set_role(R_Q_UP);
     DL_HIP(gemm(q, s));
   }
+  set_role(R_ATTENTION);
   DL_HIP(run_attn_bf16(w.q16, 0, qd, Ck, Cv, L->k.B, L->v.B, past_lens, 1, D.T == 1, w.att16, 0,
                        D.Bsz, D.T, D.nq, D.nkv, D.d, D.rk, D.rv, D.L_max, 0.f, L->rope_theta, c,
                        s));
@@ -880,6 +963,7 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
     a.K = qd;
     a.omode = GEMM_OUT_BF16;
     a.seg[0] = mseg(L->o.A, w.att16, w.to16, D.ro, qd, D.ro);
+    set_role(R_O_DOWN);
     DL_HIP(gemm(a, s));
     GemmArgs b{};
     b.nseg = 1;
@@ -890,12 +974,15 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
     b.seg[0].C32 = w.x2f;
     b.seg[0].R = x;
     b.seg[0].ldr = h;
+    set_role(R_O_UP);
     DL_HIP(gemm(b, s));
   }
   if (x2_out) {
     FillRegion cp[1] = {{static_cast<float *>(x2_out), w.x2f, 0, (int64_t)M * h}};
+    set_role(R_OUTPUT);
     DL_HIP(launch_fill(cp, 1, s));
   }
+  set_role(R_MLP_NORM);
   DL_HIP(launch_rmsnorm(w.x2f, 1, L->mlp_norm, gf32, w.b16, 0, M, h, eps, s));
   {
     GemmArgs a{};
@@ -905,6 +992,7 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
     a.omode = GEMM_OUT_BF16;
     a.seg[0] = mseg(L->gate.A, w.b16, w.tg16, D.rg, h, D.rg);
     a.seg[1] = mseg(L->up.A, w.b16, w.tu16, D.ru, h, D.ru);
+    set_role(R_GATE_UP_DOWN);
     DL_HIP(gemm(a, s));
   }
   if (D.rg == D.ru) {
@@ -915,6 +1003,7 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
     a.omode = GEMM_OUT_BF16;
     a.seg[0] = mseg(L->gate.B, w.tg16, w.G16, D.f, D.rg, D.f);
     a.seg[1] = mseg(L->up.B, w.tu16, w.U16, D.f, D.ru, D.f);
+    set_role(R_GATE_UP_UP);
     DL_HIP(gemm(a, s));
   } else {
     GemmArgs a{};
@@ -923,6 +1012,7 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
     a.K = D.rg;
     a.omode = GEMM_OUT_BF16;
     a.seg[0] = mseg(L->gate.B, w.tg16, w.G16, D.f, D.rg, D.f);
+    set_role(R_GATE_UP_UP);
     DL_HIP(gemm(a, s));
     a.K = D.ru;
     a.seg[0] = mseg(L->up.B, w.tu16, w.U16, D.f, D.ru, D.f);
@@ -937,6 +1027,7 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
     a.omode = GEMM_OUT_BF16;
     a.seg[0] = mseg(L->down.A, w.G16, w.td16, D.rd, D.f, D.rd);
     a.seg[0].X2 = w.U16;
+    set_role(R_DOWN_DOWN);
     DL_HIP(gemm(a, s));
     GemmArgs b{};
     b.nseg = 1;
@@ -946,6 +1037,7 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
     b.seg[0] = mseg(L->down.B, w.td16, y, h, D.rd, h);
     b.seg[0].R = w.x2f;
     b.seg[0].ldr = h;
+    set_role(R_DOWN_UP);
     DL_HIP(gemm(b, s));
   }
   return DL_OK;

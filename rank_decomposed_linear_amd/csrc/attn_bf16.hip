@@ -24,6 +24,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "trace.h"
 
 namespace dl {
 
@@ -542,6 +543,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
 
 hipError_t launch_pack_up_factor(const uint16_t *B, uint16_t *packed, int r, int n_kv, int d,
                                  hipStream_t s) {
+  TraceGuard trace_guard(K_PACK_UP, s);
   const int64_t total = static_cast<int64_t>(n_kv) * (r / 32) * (d / 16) * 64;
   const int threads = 256;
   pack_up_factor_kernel<<<static_cast<unsigned>((total + threads - 1) / threads), threads, 0, s>>>(
@@ -550,6 +552,7 @@ hipError_t launch_pack_up_factor(const uint16_t *B, uint16_t *packed, int r, int
 }
 
 hipError_t launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s) {
+  TraceGuard trace_guard(K_ATTN_DECODE, s);
   const int total = a.Bsz * a.n_kv * a.nsplit;
   const int nwork = (total + 7) / 8 * 8;
   if (a.d == 128)
@@ -561,11 +564,13 @@ hipError_t launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s) {
 
 hipError_t launch_attn_combine(const float *part, void *out, int Bsz, int n_q, int nsplit, int d,
                                int out_f32, hipStream_t s) {
+  TraceGuard trace_guard(K_ATTN_COMBINE, s);
   attn_combine_kernel<<<Bsz * n_q, d, 0, s>>>(part, out, nsplit, d, out_f32);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_prefill_bf16(const AttnPrefillArgs &a, hipStream_t s) {
+  TraceGuard trace_guard(K_ATTN_PREFILL, s);
   const int G = a.n_q / a.n_kv;
   const int QT = 256 / G;
   dim3 grid((a.T + QT - 1) / QT, a.n_kv, a.Bsz);

@@ -4,6 +4,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "trace.h"
 
 namespace dl {
 
@@ -91,11 +92,13 @@ int grid_for(int64_t n) {
 
 hipError_t launch_rmsnorm(const void *x, int x_f32, const void *gamma, int gamma_f32, void *y,
                           int y_f32, int M, int n, float eps, hipStream_t s) {
+  TraceGuard trace_guard(K_RMSNORM, s);
   rmsnorm_kernel<<<M, 256, 0, s>>>(x, x_f32, gamma, gamma_f32, y, y_f32, n, eps);
   return hipGetLastError();
 }
 
 hipError_t launch_fill(const FillRegion *r, int nreg, hipStream_t s) {
+  TraceGuard trace_guard(K_FILL, s);
   FillPack p{};
   int64_t mx = 0;
   for (int i = 0; i < nreg && i < 4; ++i) {
@@ -108,6 +111,7 @@ hipError_t launch_fill(const FillRegion *r, int nreg, hipStream_t s) {
 }
 
 hipError_t launch_convert_f32(const float *src, void *dst, int dst_bf16, int64_t n, hipStream_t s) {
+  TraceGuard trace_guard(K_CONVERT, s);
   convert_kernel<<<grid_for(n), 256, 0, s>>>(src, dst, dst_bf16, n);
   return hipGetLastError();
 }
@@ -115,6 +119,7 @@ hipError_t launch_convert_f32(const float *src, void *dst, int dst_bf16, int64_t
 hipError_t launch_store_cache_rows(const float *src, int ld, void *cache, int cache_bf16,
                                    const int32_t *past, int Bsz, int T, int r, int L_max,
                                    hipStream_t s) {
+  TraceGuard trace_guard(K_STORE_CACHE, s);
   store_cache_rows_kernel<<<Bsz * T, 256, 0, s>>>(src, ld, cache, cache_bf16, past, T, r, L_max);
   return hipGetLastError();
 }

@@ -8,6 +8,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "trace.h"
 
 namespace dl {
 
@@ -174,12 +175,14 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnF32Args a) {
 }  // namespace
 
 hipError_t launch_gemm_f32(const GemmF32Args &a, hipStream_t s) {
+  TraceGuard trace_guard(K_GEMM_F32, s);
   dim3 grid((a.N + TN - 1) / TN, (a.M + TM - 1) / TM);
   gemm_f32_kernel<<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_f32(const AttnF32Args &a, hipStream_t s) {
+  TraceGuard trace_guard(K_ATTN_F32, s);
   attn_f32_kernel<<<a.Bsz * a.T * a.n_q, 64, 0, s>>>(a);
   return hipGetLastError();
 }

@@ -15,6 +15,7 @@
 // blocks; LDS double-buffered (64 KB).
 #include "common.h"
 #include "kernels.h"
+#include "trace.h"
 
 namespace dl {
 
@@ -215,6 +216,7 @@ hipError_t launch_x(const GemmArgs &a, dim3 grid, hipStream_t s) {
 int gemm_ntiles(int N) { return (N + BN - 1) / BN; }
 
 hipError_t launch_gemm_bf16(const GemmArgs &a, hipStream_t s) {
+  TraceGuard trace_guard(K_GEMM_BF16, s);
   int tiles = 0;
   for (int i = 0; i < a.nseg; ++i) tiles += gemm_ntiles(a.seg[i].N);
   dim3 grid(tiles, (a.M + BM - 1) / BM);

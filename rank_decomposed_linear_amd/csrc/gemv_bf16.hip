@@ -20,6 +20,7 @@
 //    sums into the f32 output with hardware float atomics.
 #include "common.h"
 #include "kernels.h"
+#include "trace.h"
 
 namespace dl {
 
@@ -161,6 +162,7 @@ hipError_t launch_mb(const GemvArgs &a, dim3 grid, hipStream_t s) {
 int gemv_strips(int N) { return (N + kCols - 1) / kCols; }
 
 hipError_t launch_gemv_bf16(const GemvArgs &a, int ksplit, hipStream_t s) {
+  TraceGuard trace_guard(K_GEMV_BF16, s);
   int strips = 0;
   for (int i = 0; i < a.nseg; ++i) strips += gemv_strips(a.seg[i].N);
   dim3 grid(strips, ksplit);
