@@ -58,23 +58,25 @@ def log(msg):
 # algorithmic work per launch role (bytes moved at minimum / flops of the method)
 # ----------------------------------------------------------------------------
 def decode_role_work(shape, M, ctx_total):
-    """Per-step algorithmic bytes of each GEMV role and of the attention
-    kernel (bf16 weights / cache, f32 latent accumulators), and attention
-    flops. ctx_total = sum over sequences of the rows attended."""
+    """Per-step algorithmic bytes of each GEMV launch (bf16 weights read once,
+    activations in and out at the dtype the layer passes between launches)
+    and of the attention kernel, plus attention flops. ctx_total = sum over
+    sequences of the rows attended."""
     h, f, qd, kvd = shape.hidden, shape.ffn, shape.n_q * shape.head_dim, shape.n_kv * shape.head_dim
     r = {p: shape.rank(p) for p in ("q", "k", "v", "o", "gate", "up", "down")}
-    es, acc = 2, 4
+    b16, f32 = 2, 4
+    rqkv, rgu = r["q"] + r["k"] + r["v"], r["gate"] + r["up"]
     gemv = {
-        "qkv_down": es * h * (r["q"] + r["k"] + r["v"]) + M * h * es + M * (r["q"] + r["k"] + r["v"]) * acc,
-        "q_up": es * r["q"] * qd + M * r["q"] * acc + M * qd * acc,
-        "o_down": es * qd * r["o"] + M * qd * es + M * r["o"] * acc,
-        "o_up": es * r["o"] * h + M * r["o"] * acc + M * h * acc,
-        "gate_up_down": es * h * (r["gate"] + r["up"]) + M * h * es + M * (r["gate"] + r["up"]) * acc,
-        "gate_up_up": es * (r["gate"] + r["up"]) * f + M * (r["gate"] + r["up"]) * acc + 2 * M * f * acc,
-        "down_down": es * f * r["down"] + 2 * M * f * acc + M * r["down"] * acc,
-        "down_up": es * r["down"] * h + M * r["down"] * acc + M * h * acc,
+        "qkv_down": b16 * h * rqkv + M * h * b16 + M * rqkv * b16,
+        "q_up": b16 * r["q"] * qd + M * r["q"] * b16 + M * qd * f32,
+        "o_down": b16 * qd * r["o"] + M * qd * b16 + M * r["o"] * b16,
+        "o_up": b16 * r["o"] * h + M * r["o"] * b16 + M * h * b16 + M * h * f32,
+        "gate_up_down": b16 * h * rgu + M * h * f32 + M * rgu * b16,
+        "gate_up_up": b16 * rgu * f + M * rgu * b16 + M * f * b16,
+        "down_down": b16 * f * r["down"] + M * f * b16 + M * r["down"] * b16,
+        "down_up": b16 * r["down"] * h + M * r["down"] * b16 + M * h * f32 + M * h * b16,
     }
-    attn_bytes = ctx_total * (r["k"] + r["v"]) * es + es * kvd * (r["k"] + r["v"]) + M * qd * acc
+    attn_bytes = ctx_total * (r["k"] + r["v"]) * b16 + b16 * kvd * (r["k"] + r["v"]) + M * qd * (f32 + b16)
     attn_flops = ctx_total * (2 * (r["k"] + r["v"]) * kvd + 4 * qd)
     return gemv, attn_bytes, attn_flops
 

@@ -110,33 +110,44 @@ bool valid_dtype(dl_dtype dt) { return dt == DL_F32 || dt == DL_BF16; }
 // ---------------------------------------------------------------------------
 // GEMV / GEMM helpers
 // ---------------------------------------------------------------------------
-int gemv_ksplit(int strips, int K) {
-  const int target = env_int("DL_GEMV_TARGET_WGS", 768);
-  const int ksteps = K / 32;
-  int ks = (target + strips - 1) / strips;
-  const int maxks = std::max(1, ksteps / 8);
-  return std::max(1, std::min(ks, maxks));
-}
-
-hipError_t gemv(GemvArgs &a, hipStream_t s) {
-  int strips = 0;
-  for (int i = 0; i < a.nseg; ++i) {
-    a.seg[i].strip_begin = strips;
-    strips += gemv_strips(a.seg[i].N);
-  }
-  return launch_gemv_bf16(a, gemv_ksplit(strips, a.K), s);
-}
-
-GemvSeg gseg(const void *W, const void *X, const float *X2, float *out, int N, int ldx, int ldo) {
-  GemvSeg g{};
+GvSeg gvseg(const void *W, const void *X, int ldx, void *out, int ldo, int N, int omode) {
+  GvSeg g{};
   g.W = static_cast<const uint16_t *>(W);
   g.X = X;
-  g.X2 = X2;
-  g.out = out;
-  g.N = N;
   g.ldx = ldx;
+  g.out = out;
   g.ldo = ldo;
+  g.N = N;
+  g.omode = omode;
   return g;
+}
+
+GvArgs gvargs(int M, int K, int nseg) {
+  GvArgs a{};
+  a.M = M;
+  a.K = K;
+  a.nseg = nseg;
+  a.T = 1;
+  return a;
+}
+
+// Sizes of the shared split-K scratch of a sequence of GEMV launches: the
+// launches run one after another on one stream, so they share one partial
+// buffer and one counter array (each launch leaves its counters at zero).
+struct GvScratch {
+  size_t part_floats = 0;
+  int counters = 0;
+  void add(GvArgs &a) {
+    part_floats = std::max(part_floats, gemv_plan(a));
+    counters = std::max(counters, a.nstrips);
+  }
+};
+
+hipError_t gemv_run(GvArgs &a, float *part, int *counters, hipStream_t s) {
+  gemv_plan(a);
+  a.part = part;
+  a.counters = counters;
+  return launch_gemv(a, s);
 }
 
 hipError_t gemm(GemmArgs &a, hipStream_t s) {
@@ -187,25 +198,47 @@ hipError_t gemm_f32(const float *X, const float *X2, const void *W, float *C, in
 struct DecodePlan {
   int nsplit, tiles_per_split;
 };
+// Context splits of decode attention: enough (sequence, kv head, split)
+// work items to cover the chip, at most 64 splits.
 DecodePlan plan_decode(int64_t Bsz, int64_t n_kv, int64_t L_max) {
-  const int tiles = static_cast<int>((L_max + 127) / 128);
-  const int target = env_int("DL_ATTN_TARGET_WGS", 2048);
+  const int per_tile = attn_decode_positions_per_tile();
+  const int tiles = static_cast<int>((L_max + per_tile - 1) / per_tile);
+  const int target = env_int("DL_ATTN_TARGET_WGS", 512);
   int ns = static_cast<int>((target + Bsz * n_kv - 1) / (Bsz * n_kv));
-  ns = std::max(1, std::min(ns, tiles));
+  ns = std::max(1, std::min(ns, std::min(tiles, 64)));
   const int tps = (tiles + ns - 1) / ns;
   ns = (tiles + tps - 1) / tps;
   return {ns, tps};
 }
 
+// Attention scratch: packed up factors (prefill), split partials and
+// merge counters (decode). The counters must be zero before the launch.
+struct AttnWS {
+  uint16_t *pk = nullptr, *pv = nullptr;
+  float *part = nullptr;
+  int *counters = nullptr;
+  int n_counters = 0;
+};
+
+AttnWS carve_attn(Carver &c, int64_t Bsz, int64_t n_q, int64_t n_kv, int64_t d, int64_t r_k,
+                  int64_t r_v, int64_t L_max, bool decode) {
+  AttnWS w;
+  if (decode) {
+    const DecodePlan p = plan_decode(Bsz, n_kv, L_max);
+    w.part = c.take<float>(static_cast<size_t>(Bsz * n_q * p.nsplit * (d + 2)));
+    w.n_counters = static_cast<int>(Bsz * n_kv);
+    w.counters = c.take<int>(static_cast<size_t>(w.n_counters));
+  } else {
+    w.pk = c.take<uint16_t>(static_cast<size_t>(n_kv * d * r_k));
+    w.pv = c.take<uint16_t>(static_cast<size_t>(n_kv * d * r_v));
+  }
+  return w;
+}
+
 size_t attn_bf16_ws(int64_t Bsz, int64_t n_q, int64_t n_kv, int64_t d, int64_t r_k, int64_t r_v,
                     int64_t L_max, bool decode) {
   Carver c(nullptr);
-  c.take<uint16_t>(static_cast<size_t>(n_kv * d * r_k));
-  c.take<uint16_t>(static_cast<size_t>(n_kv * d * r_v));
-  if (decode) {
-    const DecodePlan p = plan_decode(Bsz, n_kv, L_max);
-    c.take<float>(static_cast<size_t>(Bsz * n_q * p.nsplit * (d + 2)));
-  }
+  carve_attn(c, Bsz, n_q, n_kv, d, r_k, r_v, L_max, decode);
   return c.off;
 }
 
@@ -230,18 +263,13 @@ dl_status check_attn_shape(int64_t n_q, int64_t n_kv, int64_t d, int64_t r_k, in
   return DL_OK;
 }
 
-// Runs the bf16 attention kernels; q is bf16 (q_f32 = 0) or f32.
+// Runs the bf16 attention kernels; q is bf16 (q_f32 = 0) or f32. For
+// decode, w.counters must be zero.
 hipError_t run_attn_bf16(const void *q, int q_f32, int ldq, const void *Ck, const void *Cv,
                          const void *B_k, const void *B_v, const int32_t *lens, int ctx_offset,
                          bool decode, void *out, int out_f32, int Bsz, int T, int n_q, int n_kv,
                          int d, int r_k, int r_v, int L_max, float sm_scale, float theta,
-                         Carver &c, hipStream_t s) {
-  uint16_t *pk = c.take<uint16_t>(static_cast<size_t>(n_kv) * d * r_k);
-  uint16_t *pv = c.take<uint16_t>(static_cast<size_t>(n_kv) * d * r_v);
-  hipError_t e = launch_pack_up_factor(static_cast<const uint16_t *>(B_k), pk, r_k, n_kv, d, s);
-  if (e != hipSuccess) return e;
-  e = launch_pack_up_factor(static_cast<const uint16_t *>(B_v), pv, r_v, n_kv, d, s);
-  if (e != hipSuccess) return e;
+                         const AttnWS &w, hipStream_t s) {
   const float scale = (sm_scale != 0.f ? sm_scale : 1.0f / sqrtf(static_cast<float>(d))) * kLog2e;
   if (decode) {
     const DecodePlan p = plan_decode(Bsz, n_kv, L_max);
@@ -250,11 +278,14 @@ hipError_t run_attn_bf16(const void *q, int q_f32, int ldq, const void *Ck, cons
     a.q_f32 = q_f32;
     a.ck = static_cast<const uint16_t *>(Ck);
     a.cv = static_cast<const uint16_t *>(Cv);
-    a.bk_packed = pk;
-    a.bv_packed = pv;
+    a.bk = static_cast<const uint16_t *>(B_k);
+    a.bv = static_cast<const uint16_t *>(B_v);
     a.ctx_lens = lens;
     a.ctx_offset = ctx_offset;
-    a.part = c.take<float>(static_cast<size_t>(Bsz) * n_q * p.nsplit * (d + 2));
+    a.out = out;
+    a.out_f32 = out_f32;
+    a.part = w.part;
+    a.counters = w.counters;
     a.Bsz = Bsz;
     a.n_q = n_q;
     a.n_kv = n_kv;
@@ -266,18 +297,20 @@ hipError_t run_attn_bf16(const void *q, int q_f32, int ldq, const void *Ck, cons
     a.tiles_per_split = p.tiles_per_split;
     a.scale_log2 = scale;
     a.theta = theta;
-    e = launch_attn_decode_bf16(a, s);
-    if (e != hipSuccess) return e;
-    return launch_attn_combine(a.part, out, Bsz, n_q, p.nsplit, d, out_f32, s);
+    return launch_attn_decode_bf16(a, s);
   }
+  hipError_t e = launch_pack_up_factor(static_cast<const uint16_t *>(B_k), w.pk, r_k, n_kv, d, s);
+  if (e != hipSuccess) return e;
+  e = launch_pack_up_factor(static_cast<const uint16_t *>(B_v), w.pv, r_v, n_kv, d, s);
+  if (e != hipSuccess) return e;
   AttnPrefillArgs a{};
   a.q = q;
   a.q_f32 = q_f32;
   a.ldq = ldq;
   a.ck = static_cast<const uint16_t *>(Ck);
   a.cv = static_cast<const uint16_t *>(Cv);
-  a.bk_packed = pk;
-  a.bv_packed = pv;
+  a.bk_packed = w.pk;
+  a.bv_packed = w.pv;
   a.past_lens = lens;
   a.out = static_cast<uint16_t *>(out);
   a.Bsz = Bsz;
@@ -323,15 +356,29 @@ const char *dl_role_name(int32_t role) {
 // ===========================================================================
 // dl_lowrank_linear
 // ===========================================================================
+// GEMV-path plan of the factor pair (shapes only; pointers are filled in later).
+static void linear_gemvs(int M, int m, int k, int n, const void *x, const void *A, const void *B,
+                         void *t, void *y, GvArgs &g1, GvArgs &g2) {
+  g1 = gvargs(M, m, 1);
+  g1.seg[0] = gvseg(A, x, m, t, k, k, GV_OUT_BF16);
+  g2 = gvargs(M, k, 1);
+  g2.seg[0] = gvseg(B, t, k, y, n, n, GV_OUT_BF16);
+}
+
 size_t dl_lowrank_linear_workspace(int64_t M, int64_t m, int64_t k, int64_t n, dl_dtype dt) {
-  (void)m;
-  if (M <= 0 || k <= 0 || n <= 0) return 0;
+  if (M <= 0 || m <= 0 || k <= 0 || n <= 0) return 0;
   Carver c(nullptr);
   if (dt == DL_F32) {
     c.take<float>(static_cast<size_t>(M * k));
   } else if (use_gemv(static_cast<int>(M))) {
-    c.take<float>(static_cast<size_t>(M * k));
-    c.take<float>(static_cast<size_t>(M * n));
+    GvArgs g1, g2;
+    linear_gemvs((int)M, (int)m, (int)k, (int)n, nullptr, nullptr, nullptr, nullptr, nullptr, g1, g2);
+    GvScratch sc;
+    sc.add(g1);
+    sc.add(g2);
+    c.take<int>(sc.counters);
+    c.take<float>(sc.part_floats);
+    c.take<uint16_t>(static_cast<size_t>(M * k));
   } else {
     c.take<uint16_t>(static_cast<size_t>(M * k));
   }
@@ -368,25 +415,19 @@ dl_status dl_lowrank_linear(const void *x, const void *A, const void *B, void *y
     return DL_OK;
   }
   if (use_gemv(Mi)) {
-    float *t = c.take<float>(static_cast<size_t>(M * k));
-    float *yacc = c.take<float>(static_cast<size_t>(M * n));
-    FillRegion z[2] = {{t, nullptr, 0, M * k}, {yacc, nullptr, 0, M * n}};
-    DL_HIP(launch_fill(z, 2, s));
-    GemvArgs a{};
-    a.nseg = 1;
-    a.M = Mi;
-    a.K = mi;
-    a.xmode = GEMV_X_BF16;
-    a.seg[0] = gseg(A, x, nullptr, t, ki, mi, ki);
-    DL_HIP(gemv(a, s));
-    GemvArgs b{};
-    b.nseg = 1;
-    b.M = Mi;
-    b.K = ki;
-    b.xmode = GEMV_X_F32;
-    b.seg[0] = gseg(B, t, nullptr, yacc, ni, ki, ni);
-    DL_HIP(gemv(b, s));
-    DL_HIP(launch_convert_f32(yacc, y, 1, M * n, s));
+    GvArgs g1, g2;
+    linear_gemvs(Mi, mi, ki, ni, nullptr, nullptr, nullptr, nullptr, nullptr, g1, g2);
+    GvScratch sc;
+    sc.add(g1);
+    sc.add(g2);
+    int *counters = c.take<int>(sc.counters);
+    float *part = c.take<float>(sc.part_floats);
+    uint16_t *t = c.take<uint16_t>(static_cast<size_t>(M * k));
+    linear_gemvs(Mi, mi, ki, ni, x, A, B, t, y, g1, g2);
+    FillRegion z[1] = {{reinterpret_cast<float *>(counters), nullptr, 0, sc.counters}};
+    DL_HIP(launch_fill(z, 1, s));
+    DL_HIP(gemv_run(g1, part, counters, s));
+    DL_HIP(gemv_run(g2, part, counters, s));
     return DL_OK;
   }
   uint16_t *t = c.take<uint16_t>(static_cast<size_t>(M * k));
@@ -412,14 +453,30 @@ dl_status dl_lowrank_linear(const void *x, const void *A, const void *B, void *y
 // ===========================================================================
 // dl_lowrank_kv_append
 // ===========================================================================
+static GvArgs append_gemv(int M, int m, int rk, int rv, int T, int L_max, const void *x,
+                          const void *A_k, const void *A_v, void *Ck, void *Cv,
+                          const int32_t *past) {
+  GvArgs a = gvargs(M, m, 2);
+  a.past = past;
+  a.T = T;
+  a.L_max = L_max;
+  a.seg[0] = gvseg(A_k, x, m, Ck, rk, rk, GV_OUT_CACHE);
+  a.seg[1] = gvseg(A_v, x, m, Cv, rv, rv, GV_OUT_CACHE);
+  return a;
+}
+
 size_t dl_kv_append_workspace(int64_t Bsz, int64_t T, int64_t m, int64_t r_k, int64_t r_v,
                               dl_dtype dt) {
-  (void)m;
-  if (Bsz <= 0 || T <= 0) return 0;
+  if (Bsz <= 0 || T <= 0 || m <= 0 || r_k <= 0 || r_v <= 0) return 0;
   const int64_t M = Bsz * T;
   if (dt == DL_BF16 && use_gemv(static_cast<int>(M))) {
+    GvArgs a = append_gemv((int)M, (int)m, (int)r_k, (int)r_v, (int)T, 1, nullptr, nullptr,
+                           nullptr, nullptr, nullptr, nullptr);
+    GvScratch sc;
+    sc.add(a);
     Carver c(nullptr);
-    c.take<float>(static_cast<size_t>(M * (r_k + r_v)));
+    c.take<int>(sc.counters);
+    c.take<float>(sc.part_floats);
     return c.off;
   }
   return 0;
@@ -457,22 +514,15 @@ dl_status dl_lowrank_kv_append(const void *x, const void *A_k, const void *A_v, 
     return DL_OK;
   }
   if (use_gemv(M)) {
+    GvArgs a = append_gemv(M, mi, rk, rv, Ti, Lm, x, A_k, A_v, Ck, Cv, past_lens);
+    GvScratch sc;
+    sc.add(a);
     Carver c(ws);
-    float *acc = c.take<float>(static_cast<size_t>(M) * (rk + rv));
-    FillRegion z[1] = {{acc, nullptr, 0, static_cast<int64_t>(M) * (rk + rv)}};
+    int *counters = c.take<int>(sc.counters);
+    float *part = c.take<float>(sc.part_floats);
+    FillRegion z[1] = {{reinterpret_cast<float *>(counters), nullptr, 0, sc.counters}};
     DL_HIP(launch_fill(z, 1, s));
-    GemvArgs a{};
-    a.nseg = 2;
-    a.M = M;
-    a.K = mi;
-    a.xmode = GEMV_X_BF16;
-    a.seg[0] = gseg(A_k, x, nullptr, acc, rk, mi, rk + rv);
-    a.seg[1] = gseg(A_v, x, nullptr, acc + rk, rv, mi, rk + rv);
-    DL_HIP(gemv(a, s));
-    DL_HIP(launch_store_cache_rows(acc, rk + rv, Ck, 1, past_lens, static_cast<int>(Bsz), Ti, rk,
-                                   Lm, s));
-    DL_HIP(launch_store_cache_rows(acc + rk, rk + rv, Cv, 1, past_lens, static_cast<int>(Bsz), Ti,
-                                   rv, Lm, s));
+    DL_HIP(gemv_run(a, part, counters, s));
     return DL_OK;
   }
   GemmArgs a{};
@@ -556,10 +606,15 @@ static dl_status attn_common(const void *q, const void *Ck, const void *Cv, cons
     return DL_OK;
   }
   Carver c(ws);
+  const AttnWS aw = carve_attn(c, Bsz, n_q, n_kv, d, r_k, r_v, L_max, decode);
+  if (aw.counters) {
+    FillRegion z[1] = {{reinterpret_cast<float *>(aw.counters), nullptr, 0, aw.n_counters}};
+    DL_HIP(launch_fill(z, 1, s));
+  }
   DL_HIP(run_attn_bf16(q, 0, static_cast<int>(n_q * d), Ck, Cv, B_k, B_v, lens, 0, decode, out, 0,
                        static_cast<int>(Bsz), static_cast<int>(T), static_cast<int>(n_q),
                        static_cast<int>(n_kv), static_cast<int>(d), static_cast<int>(r_k),
-                       static_cast<int>(r_v), static_cast<int>(L_max), sm_scale, rope_theta, c, s));
+                       static_cast<int>(r_v), static_cast<int>(L_max), sm_scale, rope_theta, aw, s));
   return DL_OK;
 }
 
@@ -634,19 +689,83 @@ static dl_status layer_dims(const dl_layer *L, int64_t Bsz, int64_t T, int64_t L
 struct LayerWS {
   // f32 path
   float *a, *tq, *qf, *att, *to, *x2, *b, *tg, *tu, *G, *U, *td;
-  // bf16 GEMV path (f32 accumulators + bf16 activations)
-  float *acc0;  // start of the zero-initialised accumulators
-  float *t_qkv, *q32, *t_o, *t_gu, *G32, *U32, *t_d;
-  int64_t acc_len;
-  float *x2f;
-  uint16_t *a16, *b16, *att16;
-  // bf16 GEMM path
-  uint16_t *tq16, *q16, *to16, *tg16, *tu16, *G16, *U16, *td16;
+  // bf16 small-M path: split-K scratch, bf16 latents, f32 query and residual stream
+  int *counters;
+  int n_counters;
+  float *part, *q32, *x2f;
+  uint16_t *att16, *H16;
+  // bf16 large-M (MFMA GEMM) path
+  uint16_t *a16, *b16, *tq16, *q16, *to16, *tg16, *tu16, *G16, *U16, *td16;
 };
 
-static void carve_layer(Carver &c, const LayerDims &D, dl_dtype dt, LayerWS &w) {
+enum { G_QKV, G_QUP, G_ODOWN, G_OUP, G_GUD, G_GUU, G_DD, G_DU, G_NUM };
+
+// The eight GEMV launches of a small-M layer step:
+//   qkv_down  RMSNorm(x) [A_q A_k A_v]; k, v latents scattered into the cache
+//   q_up      t_q B_q -> f32 query
+//   o_down    o A_o
+//   o_up      x2 = x + t_o B_o (f32 residual stream; copy to x2_out)
+//   gate_up   RMSNorm(x2) [A_gate A_up]
+//   gu_up     H = silu(t_g B_gate) * (t_u B_up)   (one paired launch)
+//   down_down H A_down
+//   down_up   y = x2 + t_d B_down
+static void layer_gemvs(const dl_layer *L, const LayerDims &D, const LayerWS &w, const void *x,
+                        void *y, void *x2_out, void *Ck, void *Cv, const int32_t *past,
+                        GvArgs (&g)[G_NUM]) {
+  const int M = D.M, h = D.h, qd = D.qd();
+  const int gf32 = L->dt == DL_F32;
+  g[G_QKV] = gvargs(M, h, 3);
+  g[G_QKV].norm = 1;
+  g[G_QKV].gamma = L->attn_norm;
+  g[G_QKV].gamma_f32 = gf32;
+  g[G_QKV].eps = L->rms_eps;
+  g[G_QKV].past = past;
+  g[G_QKV].T = D.T;
+  g[G_QKV].L_max = D.L_max;
+  g[G_QKV].seg[0] = gvseg(L->q.A, x, h, w.tq16, D.rq, D.rq, GV_OUT_BF16);
+  g[G_QKV].seg[1] = gvseg(L->k.A, x, h, Ck, D.rk, D.rk, GV_OUT_CACHE);
+  g[G_QKV].seg[2] = gvseg(L->v.A, x, h, Cv, D.rv, D.rv, GV_OUT_CACHE);
+
+  g[G_QUP] = gvargs(M, D.rq, 1);
+  g[G_QUP].seg[0] = gvseg(L->q.B, w.tq16, D.rq, w.q32, qd, qd, GV_OUT_F32);
+
+  g[G_ODOWN] = gvargs(M, qd, 1);
+  g[G_ODOWN].seg[0] = gvseg(L->o.A, w.att16, qd, w.to16, D.ro, D.ro, GV_OUT_BF16);
+
+  g[G_OUP] = gvargs(M, D.ro, 1);
+  g[G_OUP].seg[0] = gvseg(L->o.B, w.to16, D.ro, w.x2f, h, h, GV_OUT_RES_F32);
+  g[G_OUP].seg[0].R = x;
+  g[G_OUP].seg[0].ldr = h;
+  g[G_OUP].seg[0].out2 = static_cast<float *>(x2_out);
+
+  g[G_GUD] = gvargs(M, h, 2);
+  g[G_GUD].x_f32 = 1;
+  g[G_GUD].norm = 1;
+  g[G_GUD].gamma = L->mlp_norm;
+  g[G_GUD].gamma_f32 = gf32;
+  g[G_GUD].eps = L->rms_eps;
+  g[G_GUD].seg[0] = gvseg(L->gate.A, w.x2f, h, w.tg16, D.rg, D.rg, GV_OUT_BF16);
+  g[G_GUD].seg[1] = gvseg(L->up.A, w.x2f, h, w.tu16, D.ru, D.ru, GV_OUT_BF16);
+
+  g[G_GUU] = gvargs(M, D.rg, 1);
+  g[G_GUU].K2 = D.ru;
+  g[G_GUU].seg[0] = gvseg(L->gate.B, w.tg16, D.rg, w.H16, D.f, D.f, GV_OUT_SWIGLU);
+  g[G_GUU].seg[0].W2 = static_cast<const uint16_t *>(L->up.B);
+  g[G_GUU].seg[0].X2 = w.tu16;
+  g[G_GUU].seg[0].ldx2 = D.ru;
+
+  g[G_DD] = gvargs(M, D.f, 1);
+  g[G_DD].seg[0] = gvseg(L->down.A, w.H16, D.f, w.td16, D.rd, D.rd, GV_OUT_BF16);
+
+  g[G_DU] = gvargs(M, D.rd, 1);
+  g[G_DU].seg[0] = gvseg(L->down.B, w.td16, D.rd, y, h, h, GV_OUT_RES_BF16);
+  g[G_DU].seg[0].R = w.x2f;
+  g[G_DU].seg[0].ldr = h;
+}
+
+static void carve_layer(Carver &c, const LayerDims &D, const dl_layer *L, LayerWS &w) {
   const size_t M = D.M;
-  if (dt == DL_F32) {
+  if (L->dt == DL_F32) {
     w.a = c.take<float>(M * D.h);
     w.tq = c.take<float>(M * D.rq);
     w.qf = c.take<float>(M * D.qd());
@@ -662,25 +781,23 @@ static void carve_layer(Carver &c, const LayerDims &D, dl_dtype dt, LayerWS &w) 
     return;
   }
   if (use_gemv(D.M)) {
-    // accumulators are carved as one contiguous block so a single fill zeroes them
-    const size_t rqkv = D.rq + D.rk + D.rv;
-    const size_t n_acc = M * (rqkv + D.qd() + D.ro + D.rg + D.ru + 2 * (size_t)D.f + D.rd);
-    w.acc0 = c.take<float>(n_acc);
-    w.acc_len = static_cast<int64_t>(n_acc);
-    if (w.acc0) {
-      float *p = w.acc0;
-      w.t_qkv = p; p += M * rqkv;
-      w.q32 = p; p += M * D.qd();
-      w.t_o = p; p += M * D.ro;
-      w.t_gu = p; p += M * (D.rg + D.ru);
-      w.G32 = p; p += M * D.f;
-      w.U32 = p; p += M * D.f;
-      w.t_d = p;
-    }
-    w.x2f = c.take<float>(M * D.h);
-    w.a16 = c.take<uint16_t>(M * D.h);
-    w.b16 = c.take<uint16_t>(M * D.h);
+    GvArgs g[G_NUM];
+    LayerWS none{};
+    layer_gemvs(L, D, none, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, g);
+    GvScratch sc;
+    for (GvArgs &a : g) sc.add(a);
+    w.n_counters = sc.counters;
+    w.counters = c.take<int>(sc.counters);
+    w.part = c.take<float>(sc.part_floats);
+    w.tq16 = c.take<uint16_t>(M * D.rq);
+    w.q32 = c.take<float>(M * D.qd());
     w.att16 = c.take<uint16_t>(M * D.qd());
+    w.to16 = c.take<uint16_t>(M * D.ro);
+    w.x2f = c.take<float>(M * D.h);
+    w.tg16 = c.take<uint16_t>(M * D.rg);
+    w.tu16 = c.take<uint16_t>(M * D.ru);
+    w.H16 = c.take<uint16_t>(M * D.f);
+    w.td16 = c.take<uint16_t>(M * D.rd);
     return;
   }
   w.a16 = c.take<uint16_t>(M * D.h);
@@ -702,7 +819,7 @@ size_t dl_layer_workspace(const dl_layer *L, int64_t Bsz, int64_t T, int64_t L_m
   if (layer_dims(L, Bsz, T, L_max, &D) != DL_OK) return 0;
   Carver c(nullptr);
   LayerWS w{};
-  carve_layer(c, D, L->dt, w);
+  carve_layer(c, D, L, w);
   if (L->dt == DL_BF16)
     c.off += attn_bf16_ws(D.Bsz, D.nq, D.nkv, D.d, D.rk, D.rv, D.L_max, D.T == 1) + kAlign;
   return c.off;
@@ -730,7 +847,9 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
   hipStream_t s = as_stream(stream);
   Carver c(ws);
   LayerWS w{};
-  carve_layer(c, D, L->dt, w);
+  carve_layer(c, D, L, w);
+  AttnWS aw;
+  if (L->dt == DL_BF16) aw = carve_attn(c, D.Bsz, D.nq, D.nkv, D.d, D.rk, D.rv, D.L_max, D.T == 1);
   const int M = D.M, h = D.h, qd = D.qd();
   const float eps = L->rms_eps;
   const int gf32 = L->dt == DL_F32;
@@ -801,122 +920,32 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
   }
 
   if (use_gemv(M)) {
-    const int rqkv = D.rq + D.rk + D.rv;
-    FillRegion init[2] = {{w.acc0, nullptr, 0, w.acc_len}, {w.x2f, x, 1, (int64_t)M * h}};
+    GvArgs g[G_NUM];
+    layer_gemvs(L, D, w, x, y, x2_out, Ck, Cv, past_lens, g);
+    FillRegion init[2] = {{reinterpret_cast<float *>(w.counters), nullptr, 0, w.n_counters},
+                          {reinterpret_cast<float *>(aw.counters), nullptr, 0, aw.n_counters}};
     set_role(R_INIT);
-    DL_HIP(launch_fill(init, 2, s));
-    set_role(R_ATTN_NORM);
-    DL_HIP(launch_rmsnorm(x, 0, L->attn_norm, gf32, w.a16, 0, M, h, eps, s));
-    {  // grouped down-projections of q, k, v: one pass over the normed activations
-      GemvArgs a{};
-      a.nseg = 3;
-      a.M = M;
-      a.K = h;
-      a.xmode = GEMV_X_BF16;
-      a.seg[0] = gseg(L->q.A, w.a16, nullptr, w.t_qkv, D.rq, h, rqkv);
-      a.seg[1] = gseg(L->k.A, w.a16, nullptr, w.t_qkv + D.rq, D.rk, h, rqkv);
-      a.seg[2] = gseg(L->v.A, w.a16, nullptr, w.t_qkv + D.rq + D.rk, D.rv, h, rqkv);
-      set_role(R_QKV_DOWN);
-      DL_HIP(gemv(a, s));
-    }
-    set_role(R_KV_STORE);
-    DL_HIP(launch_store_cache_rows(w.t_qkv + D.rq, rqkv, Ck, 1, past_lens, D.Bsz, D.T, D.rk,
-                                   D.L_max, s));
-    DL_HIP(launch_store_cache_rows(w.t_qkv + D.rq + D.rk, rqkv, Cv, 1, past_lens, D.Bsz, D.T, D.rv,
-                                   D.L_max, s));
-    {
-      GemvArgs a{};
-      a.nseg = 1;
-      a.M = M;
-      a.K = D.rq;
-      a.xmode = GEMV_X_F32;
-      a.seg[0] = gseg(L->q.B, w.t_qkv, nullptr, w.q32, qd, rqkv, qd);
-      set_role(R_Q_UP);
-      DL_HIP(gemv(a, s));
-    }
+    DL_HIP(launch_fill(init, aw.counters ? 2 : 1, s));
+    set_role(R_QKV_DOWN);
+    DL_HIP(gemv_run(g[G_QKV], w.part, w.counters, s));
+    set_role(R_Q_UP);
+    DL_HIP(gemv_run(g[G_QUP], w.part, w.counters, s));
     set_role(R_ATTENTION);
     DL_HIP(run_attn_bf16(w.q32, 1, qd, Ck, Cv, L->k.B, L->v.B, past_lens, 1, D.T == 1, w.att16, 0,
-                         D.Bsz, D.T, D.nq, D.nkv, D.d, D.rk, D.rv, D.L_max, 0.f, L->rope_theta, c,
+                         D.Bsz, D.T, D.nq, D.nkv, D.d, D.rk, D.rv, D.L_max, 0.f, L->rope_theta, aw,
                          s));
-    {
-      GemvArgs a{};
-      a.nseg = 1;
-      a.M = M;
-      a.K = qd;
-      a.xmode = GEMV_X_BF16;
-      a.seg[0] = gseg(L->o.A, w.att16, nullptr, w.t_o, D.ro, qd, D.ro);
-      set_role(R_O_DOWN);
-      DL_HIP(gemv(a, s));
-      GemvArgs b{};
-      b.nseg = 1;
-      b.M = M;
-      b.K = D.ro;
-      b.xmode = GEMV_X_F32;
-      b.seg[0] = gseg(L->o.B, w.t_o, nullptr, w.x2f, h, D.ro, h);
-      set_role(R_O_UP);
-      DL_HIP(gemv(b, s));
-    }
-    if (x2_out) {
-      FillRegion cp[1] = {{static_cast<float *>(x2_out), w.x2f, 0, (int64_t)M * h}};
-      set_role(R_OUTPUT);
-      DL_HIP(launch_fill(cp, 1, s));
-    }
-    set_role(R_MLP_NORM);
-    DL_HIP(launch_rmsnorm(w.x2f, 1, L->mlp_norm, gf32, w.b16, 0, M, h, eps, s));
-    {
-      GemvArgs a{};
-      a.nseg = 2;
-      a.M = M;
-      a.K = h;
-      a.xmode = GEMV_X_BF16;
-      a.seg[0] = gseg(L->gate.A, w.b16, nullptr, w.t_gu, D.rg, h, D.rg + D.ru);
-      a.seg[1] = gseg(L->up.A, w.b16, nullptr, w.t_gu + D.rg, D.ru, h, D.rg + D.ru);
-      set_role(R_GATE_UP_DOWN);
-      DL_HIP(gemv(a, s));
-    }
-    if (D.rg == D.ru) {
-      GemvArgs a{};
-      a.nseg = 2;
-      a.M = M;
-      a.K = D.rg;
-      a.xmode = GEMV_X_F32;
-      a.seg[0] = gseg(L->gate.B, w.t_gu, nullptr, w.G32, D.f, D.rg + D.ru, D.f);
-      a.seg[1] = gseg(L->up.B, w.t_gu + D.rg, nullptr, w.U32, D.f, D.rg + D.ru, D.f);
-      set_role(R_GATE_UP_UP);
-      DL_HIP(gemv(a, s));
-    } else {
-      GemvArgs a{};
-      a.nseg = 1;
-      a.M = M;
-      a.K = D.rg;
-      a.xmode = GEMV_X_F32;
-      a.seg[0] = gseg(L->gate.B, w.t_gu, nullptr, w.G32, D.f, D.rg + D.ru, D.f);
-      set_role(R_GATE_UP_UP);
-      DL_HIP(gemv(a, s));
-      a.K = D.ru;
-      a.seg[0] = gseg(L->up.B, w.t_gu + D.rg, nullptr, w.U32, D.f, D.rg + D.ru, D.f);
-      DL_HIP(gemv(a, s));
-    }
-    {
-      GemvArgs a{};
-      a.nseg = 1;
-      a.M = M;
-      a.K = D.f;
-      a.xmode = GEMV_X_SWIGLU_F32;
-      a.seg[0] = gseg(L->down.A, w.G32, w.U32, w.t_d, D.rd, D.f, D.rd);
-      set_role(R_DOWN_DOWN);
-      DL_HIP(gemv(a, s));
-      GemvArgs b{};
-      b.nseg = 1;
-      b.M = M;
-      b.K = D.rd;
-      b.xmode = GEMV_X_F32;
-      b.seg[0] = gseg(L->down.B, w.t_d, nullptr, w.x2f, h, D.rd, h);  // x2 + MLP = y
-      set_role(R_DOWN_UP);
-      DL_HIP(gemv(b, s));
-    }
-    set_role(R_OUTPUT);
-    DL_HIP(launch_convert_f32(w.x2f, y, 1, (int64_t)M * h, s));
+    set_role(R_O_DOWN);
+    DL_HIP(gemv_run(g[G_ODOWN], w.part, w.counters, s));
+    set_role(R_O_UP);
+    DL_HIP(gemv_run(g[G_OUP], w.part, w.counters, s));
+    set_role(R_GATE_UP_DOWN);
+    DL_HIP(gemv_run(g[G_GUD], w.part, w.counters, s));
+    set_role(R_GATE_UP_UP);
+    DL_HIP(gemv_run(g[G_GUU], w.part, w.counters, s));
+    set_role(R_DOWN_DOWN);
+    DL_HIP(gemv_run(g[G_DD], w.part, w.counters, s));
+    set_role(R_DOWN_UP);
+    DL_HIP(gemv_run(g[G_DU], w.part, w.counters, s));
     return DL_OK;
   }
 
@@ -953,8 +982,14 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
     DL_HIP(gemm(q, s));
   }
   set_role(R_ATTENTION);
+  if (aw.counters) {
+    FillRegion z[1] = {{reinterpret_cast<float *>(aw.counters), nullptr, 0, aw.n_counters}};
+    set_role(R_INIT);
+    DL_HIP(launch_fill(z, 1, s));
+    set_role(R_ATTENTION);
+  }
   DL_HIP(run_attn_bf16(w.q16, 0, qd, Ck, Cv, L->k.B, L->v.B, past_lens, 1, D.T == 1, w.att16, 0,
-                       D.Bsz, D.T, D.nq, D.nkv, D.d, D.rk, D.rv, D.L_max, 0.f, L->rope_theta, c,
+                       D.Bsz, D.T, D.nq, D.nkv, D.d, D.rk, D.rv, D.L_max, 0.f, L->rope_theta, aw,
                        s));
   {
     GemmArgs a{};

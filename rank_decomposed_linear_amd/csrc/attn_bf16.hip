@@ -7,15 +7,6 @@
 // MFMA-operand order (one 16-byte load per lane per fragment), and the
 // rebuilt tiles live in MFMA accumulators:
 //
-//  decode   Each wave rebuilds K^T for 32 positions x all d (position is the
-//           accumulator column, so the RoPE pair (i, i+d/2) sits in one
-//           lane), turns the accumulators directly into the A operand of
-//           S^T = K Q^T (the reduction slots of an operand may be any
-//           permutation shared by both operands), rebuilds V for the same
-//           positions with position as the accumulator row, and feeds those
-//           accumulators plus the softmax weights straight into O^T += V^T P^T.
-//           No LDS round trip; splits of the context are merged by a second
-//           kernel (flash-decoding style).
 //  prefill  A workgroup owns one kv head and up to 256 (token, head) query
 //           rows; per 64-key tile its eight waves rebuild K (rotated) and
 //           V^T into swizzled LDS, then each wave runs an online-softmax
@@ -60,250 +51,6 @@ __global__ void pack_up_factor_kernel(const uint16_t *__restrict__ B, uint16_t *
 }
 
 __device__ __forceinline__ u32x4 ld16(const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
-
-// XCD-aware remap of a 1-D grid: dispatch hands consecutive workgroups to
-// the 8 XCDs in turn; give each XCD a contiguous run of work items so items
-// that share cache lines (the kv heads of one context span) share an L2.
-__device__ __forceinline__ int xcd_remap(int L, int n) {
-  const int per = n >> 3;  // n is a multiple of 8
-  return (L & 7) * per + (L >> 3);
-}
-
-// ---------------------------------------------------------------------------
-// Decode
-// ---------------------------------------------------------------------------
-template <int DB>
-__global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a, int nwork) {
-  constexpr int D = DB * 16, HALF = DB / 2;
-  __shared__ __attribute__((aligned(16))) uint16_t qs[16 * D];
-  __shared__ double revs[D / 2];
-  __shared__ float mrg_m[4][16], mrg_l[4][16];
-  __shared__ float mrg_o[4][16 * D];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int j = lane & 15, grp = lane >> 4;
-  const int w = xcd_remap(blockIdx.x, nwork);
-  const int total = a.Bsz * a.n_kv * a.nsplit;
-  if (w >= total) return;
-  const int g = w % a.n_kv;
-  const int split = (w / a.n_kv) % a.nsplit;
-  const int b = w / (a.n_kv * a.nsplit);
-  const int G = a.n_q / a.n_kv;
-  const int ctx = a.ctx_lens[b] + a.ctx_offset;
-  const int qpos = ctx - 1;
-  const int p_begin = split * a.tiles_per_split * 128;
-  const int p_end = min(p_begin + a.tiles_per_split * 128, ctx);
-  const bool rope_on = a.theta != 0.f;
-
-  for (int i = tid; i < D / 2; i += 256) revs[i] = rope_on ? rope_rev(i, D, a.theta) : 0.0;
-  __syncthreads();
-  for (int idx = tid; idx < 16 * (D / 2); idx += 256) {
-    const int hl = idx / (D / 2), i = idx % (D / 2);
-    float x = 0.f, y = 0.f;
-    if (hl < G) {
-      const size_t off = (static_cast<size_t>(b) * a.n_q + g * G + hl) * D;
-      if (a.q_f32) {
-        x = static_cast<const float *>(a.q)[off + i];
-        y = static_cast<const float *>(a.q)[off + i + D / 2];
-      } else {
-        x = bf2f(static_cast<const uint16_t *>(a.q)[off + i]);
-        y = bf2f(static_cast<const uint16_t *>(a.q)[off + i + D / 2]);
-      }
-      if (rope_on) {
-        float c, s;
-        rope_cs(qpos, revs[i], c, s);
-        const float x2 = x * c - y * s;
-        y = x * s + y * c;
-        x = x2;
-      }
-    }
-    qs[hl * D + i] = f2bf(x * a.scale_log2);
-    qs[hl * D + i + D / 2] = f2bf(y * a.scale_log2);
-  }
-  __syncthreads();
-
-  // Score B operand: lane (h = j, grp) holds q[h][16(2t) + 4grp + 0..3] and
-  // q[h][16(2t+1) + 4grp + 0..3] -- the slot order of the rebuilt-K operand.
-  u32x4 qf[HALF];
-#pragma unroll
-  for (int t = 0; t < HALF; ++t) {
-    const u32x2 lo = *reinterpret_cast<const u32x2 *>(&qs[j * D + 16 * (2 * t) + 4 * grp]);
-    const u32x2 hi = *reinterpret_cast<const u32x2 *>(&qs[j * D + 16 * (2 * t + 1) + 4 * grp]);
-    qf[t] = u32x4{lo.x, lo.y, hi.x, hi.y};
-  }
-
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 accO[DB];
-#pragma unroll
-  for (int x = 0; x < DB; ++x) accO[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int rsk = a.r_k / 32, rsv = a.r_v / 32;
-  const uint16_t *pk = a.bk_packed + static_cast<size_t>(g) * rsk * DB * 512 + lane * 8;
-  const uint16_t *pv = a.bv_packed + static_cast<size_t>(g) * rsv * DB * 512 + lane * 8;
-
-  for (int t0 = p_begin; t0 < p_end; t0 += 128) {
-    const int pw = t0 + wave * 32;
-    if (pw >= p_end) continue;
-    const int pos0 = pw + j, pos1 = pw + 16 + j;
-    const bool v0 = pos0 < p_end, v1 = pos1 < p_end;
-
-    // ---- K^T[d, pos] = B_k^T C_k^T for 32 positions ----
-    f32x4 accK[DB][2];
-#pragma unroll
-    for (int x = 0; x < DB; ++x) accK[x][0] = accK[x][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    {
-      const uint16_t *c0p = a.ck + (static_cast<size_t>(b) * a.L_max + pos0) * a.r_k + 8 * grp;
-      const uint16_t *c1p = c0p + static_cast<size_t>(16) * a.r_k;
-      for (int rs = 0; rs < rsk; ++rs) {
-        const u32x4 c0 = v0 ? ld16(c0p + rs * 32) : u32x4{0u, 0u, 0u, 0u};
-        const u32x4 c1 = v1 ? ld16(c1p + rs * 32) : u32x4{0u, 0u, 0u, 0u};
-        const uint16_t *fp = pk + static_cast<size_t>(rs) * DB * 512;
-#pragma unroll
-        for (int mb = 0; mb < DB; ++mb) {
-          const u32x4 bk = ld16(fp + mb * 512);
-          accK[mb][0] = mfma_bf16(bk, c0, accK[mb][0]);
-          accK[mb][1] = mfma_bf16(bk, c1, accK[mb][1]);
-        }
-      }
-    }
-    // lane (j, grp) holds K^T[16mb + 4grp + r][pw + 16nb + j]
-    if (rope_on) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int pos = pw + 16 * nb + j;
-#pragma unroll
-        for (int mb = 0; mb < HALF; ++mb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float c, s;
-            rope_cs(pos, revs[16 * mb + 4 * grp + r], c, s);
-            const float x = accK[mb][nb][r], y = accK[mb + HALF][nb][r];
-            accK[mb][nb][r] = x * c - y * s;
-            accK[mb + HALF][nb][r] = x * s + y * c;
-          }
-      }
-    }
-    // ---- S^T[pos, h] ----
-    f32x4 accS[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      accS[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int t = 0; t < HALF; ++t)
-        accS[nb] = mfma_bf16(pack_acc(accK[2 * t][nb], accK[2 * t + 1][nb]), qf[t], accS[nb]);
-    }
-    // lane (h = j, grp) holds S^T[pw + 16nb + 4grp + r][h]
-    float mx = -INFINITY;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pos = pw + 16 * nb + 4 * grp + r;
-        if (pos >= p_end) accS[nb][r] = -INFINITY;
-        mx = fmaxf(mx, accS[nb][r]);
-      }
-    mx = wave_max_xor(mx, 16);
-    mx = wave_max_xor(mx, 32);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
-    float psum = 0.f;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        accS[nb][r] = exp2f(accS[nb][r] - m_new);
-        psum += accS[nb][r];
-      }
-    psum = wave_sum_xor(psum, 16);
-    psum = wave_sum_xor(psum, 32);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int x = 0; x < DB; ++x) accO[x] *= alpha;
-    const u32x4 pf = pack_acc(accS[0], accS[1]);
-
-    // ---- V[pos, d] = C_v B_v for the same 32 positions ----
-    f32x4 accV[2][DB];
-#pragma unroll
-    for (int x = 0; x < DB; ++x) accV[0][x] = accV[1][x] = f32x4{0.f, 0.f, 0.f, 0.f};
-    {
-      const uint16_t *c0p = a.cv + (static_cast<size_t>(b) * a.L_max + pos0) * a.r_v + 8 * grp;
-      const uint16_t *c1p = c0p + static_cast<size_t>(16) * a.r_v;
-      for (int rs = 0; rs < rsv; ++rs) {
-        const u32x4 c0 = v0 ? ld16(c0p + rs * 32) : u32x4{0u, 0u, 0u, 0u};
-        const u32x4 c1 = v1 ? ld16(c1p + rs * 32) : u32x4{0u, 0u, 0u, 0u};
-        const uint16_t *fp = pv + static_cast<size_t>(rs) * DB * 512;
-#pragma unroll
-        for (int nb = 0; nb < DB; ++nb) {
-          const u32x4 bv = ld16(fp + nb * 512);
-          accV[0][nb] = mfma_bf16(c0, bv, accV[0][nb]);
-          accV[1][nb] = mfma_bf16(c1, bv, accV[1][nb]);
-        }
-      }
-    }
-    // lane (d = j, grp) holds V[pw + 16mp + 4grp + r][16nb + j]
-#pragma unroll
-    for (int x = 0; x < DB; ++x) accO[x] = mfma_bf16(pack_acc(accV[0][x], accV[1][x]), pf, accO[x]);
-  }
-
-  // ---- merge the four waves ----
-  if (grp == 0) {
-    mrg_m[wave][j] = m_run;
-    mrg_l[wave][j] = l_run;
-  }
-  // lane (h = j, grp) holds O^T[16x + 4grp + r][h]
-#pragma unroll
-  for (int x = 0; x < DB; ++x)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) mrg_o[wave][j * D + 16 * x + 4 * grp + r] = accO[x][r];
-  __syncthreads();
-  const int D2 = D + 2;
-  for (int idx = tid; idx < G * D; idx += 256) {
-    const int h = idx / D, dd = idx % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int wv = 0; wv < 4; ++wv) M = fmaxf(M, mrg_m[wv][h]);
-    float o = 0.f, L = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int wv = 0; wv < 4; ++wv) {
-        const float sc = exp2f(mrg_m[wv][h] - M);
-        o += sc * mrg_o[wv][h * D + dd];
-        L += sc * mrg_l[wv][h];
-      }
-    }
-    float *dst = a.part + ((static_cast<size_t>(b) * a.n_q + g * G + h) * a.nsplit + split) * D2;
-    dst[dd] = o;
-    if (dd == 0) {
-      dst[D] = M;
-      dst[D + 1] = L;
-    }
-  }
-}
-
-__global__ void attn_combine_kernel(const float *__restrict__ part, void *out, int nsplit, int D,
-                                    int out_f32) {
-  const int bh = blockIdx.x;
-  const int D2 = D + 2;
-  const float *p = part + static_cast<size_t>(bh) * nsplit * D2;
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, p[s * D2 + D]);
-  for (int dd = threadIdx.x; dd < D; dd += blockDim.x) {
-    float o = 0.f, L = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float m = p[s * D2 + D];
-      if (m == -INFINITY) continue;
-      const float sc = exp2f(m - M);
-      o += sc * p[s * D2 + dd];
-      L += sc * p[s * D2 + D + 1];
-    }
-    const float v = o / L;
-    if (out_f32)
-      static_cast<float *>(out)[static_cast<size_t>(bh) * D + dd] = v;
-    else
-      static_cast<uint16_t *>(out)[static_cast<size_t>(bh) * D + dd] = f2bf(v);
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Prefill
@@ -548,24 +295,6 @@ hipError_t launch_pack_up_factor(const uint16_t *B, uint16_t *packed, int r, int
   const int threads = 256;
   pack_up_factor_kernel<<<static_cast<unsigned>((total + threads - 1) / threads), threads, 0, s>>>(
       B, packed, r, n_kv, d);
-  return hipGetLastError();
-}
-
-hipError_t launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s) {
-  TraceGuard trace_guard(K_ATTN_DECODE, s);
-  const int total = a.Bsz * a.n_kv * a.nsplit;
-  const int nwork = (total + 7) / 8 * 8;
-  if (a.d == 128)
-    attn_decode_kernel<8><<<nwork, 256, 0, s>>>(a, nwork);
-  else
-    attn_decode_kernel<4><<<nwork, 256, 0, s>>>(a, nwork);
-  return hipGetLastError();
-}
-
-hipError_t launch_attn_combine(const float *part, void *out, int Bsz, int n_q, int nsplit, int d,
-                               int out_f32, hipStream_t s) {
-  TraceGuard trace_guard(K_ATTN_COMBINE, s);
-  attn_combine_kernel<<<Bsz * n_q, d, 0, s>>>(part, out, nsplit, d, out_f32);
   return hipGetLastError();
 }
 

@@ -1,23 +1,38 @@
 // Weight-streaming factor GEMV for decode-sized M (M <= 64), bf16 MFMA.
 //
-// One projection factor of a decomposed layer (W ~ A B, DeInfer section 2.1,
-// Eq. (1)) applied to a handful of token rows reads every weight once and
-// does M multiply-adds per weight: at M = 16 that is 16 flop/byte, above the
-// float32 VALU ridge of MI355X (~10 flop/byte without packed math) and far
-// below the bf16 MFMA ridge. So the product runs on MFMA with the token rows
-// padded to 16, and the kernel is organised to keep HBM busy:
+// One factor of a decomposed projection (W ~ A B, DeInfer section 2.1,
+// Eq. (1)) applied to a few token rows reads every weight once and does M
+// multiply-adds per weight: 16 flop/byte at M = 16, above the float32 VALU
+// ridge of MI355X and far below the bf16 MFMA ridge. So the product runs on
+// MFMA with the token rows padded to 16, organised to keep HBM streaming:
 //
-//  * A wave owns a strip of 128 output columns. Per 32-row step, lane
-//    (c = lane%16, g = lane/16) issues eight 16-byte loads W[k0+8g+s][n0+8c ..
-//    n0+8c+7], s = 0..7: each load instruction covers 4 rows x 256
-//    contiguous bytes. The eight registers are transposed in-lane into eight
-//    B operands (one per column offset 0..7), so no LDS staging is needed
-//    for the weights; output column n0 + 8c + e comes out of operand e.
-//  * The A operand (token rows, 16 per block) is a single 16-byte load per
-//    lane, converted from f32 or passed through the SwiGLU prologue.
-//  * Eight waves of a workgroup split the strip's K range; their results are
-//    summed in LDS, and workgroups that split K further (grid.y) add their
-//    sums into the f32 output with hardware float atomics.
+//  * Work item = (64-column strip, K split). A workgroup of four waves owns
+//    one item; its waves take interleaved 32-row steps of the split, so the
+//    workgroup walks a contiguous block of rows, 128 bytes per row.
+//  * Per step, lane (j = lane%16, g = lane/16) issues eight 8-byte loads
+//    W[k0 + 8g + r][n0 + 4j .. 4j+3], r = 0..7, and transposes them in
+//    registers into four MFMA B operands (one per column offset e = 0..3):
+//    no LDS staging of weights. Output column n0 + 4j + e comes out of
+//    operand e. Four steps (16 KB; two for M > 32) are kept in flight per wave; weights
+//    are streamed with non-temporal loads.
+//  * The token rows (A operand) are one 16-byte load per lane and step,
+//    optionally passed through the fused RMSNorm prologue (gain multiply,
+//    sum of squares for the row scale).
+//  * The four waves are summed in LDS in a fixed order. With more than one
+//    K split, each workgroup writes its partial sums through to the
+//    device-coherent level (relaxed agent-scope atomic stores), waits for
+//    them to complete and bumps a per-strip counter; the last workgroup to
+//    arrive reads the partials back with device-coherent loads, sums them
+//    in split order (deterministic) and runs the epilogue. One atomic per
+//    workgroup instead of one per output element, and no L2 writeback or
+//    invalidate (an agent-scope fence would cost both on every workgroup).
+//  * Epilogues: bf16 / f32 store, scatter into the latent KV cache, residual
+//    add, and SwiGLU for paired (gate, up) launches whose two halves share
+//    the output columns.
+#include <stdlib.h>
+
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 #include "trace.h"
@@ -25,44 +40,42 @@
 namespace dl {
 
 namespace {
-constexpr int kCols = 128;   // output columns per strip
-constexpr int kWaves = 8;    // waves per workgroup (all on one strip)
-constexpr int kPitch = 132;  // LDS row pitch (floats) of the reduction tile
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kCols = 64;   // output columns per strip
 
-template <int XM>
-__device__ __forceinline__ u32x4 load_x(const GemvSeg &sg, int M, int m, int k) {
-  u32x4 r = {0u, 0u, 0u, 0u};
-  if (m >= M) return r;
-  if constexpr (XM == GEMV_X_BF16) {
-    r = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(sg.X) +
-                                          static_cast<size_t>(m) * sg.ldx + k);
-  } else {
-    const float *p = static_cast<const float *>(sg.X) + static_cast<size_t>(m) * sg.ldx + k;
-    f32x4 a = *reinterpret_cast<const f32x4 *>(p);
-    f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
-    if constexpr (XM == GEMV_X_SWIGLU_F32) {
-      const float *q = sg.X2 + static_cast<size_t>(m) * sg.ldx + k;
-      f32x4 ua = *reinterpret_cast<const f32x4 *>(q);
-      f32x4 ub = *reinterpret_cast<const f32x4 *>(q + 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[i] = silu(a[i]) * ua[i];
-        b[i] = silu(b[i]) * ub[i];
-      }
-    }
-    r.x = pack2(a[0], a[1]);
-    r.y = pack2(a[2], a[3]);
-    r.z = pack2(b[0], b[1]);
-    r.w = pack2(b[2], b[3]);
-  }
-  return r;
+// Device-coherent 8-byte accesses for the split-K partial sums: relaxed
+// agent-scope atomics compile to plain loads/stores with the system-coherent
+// cache policy (written through to, and read from, the level shared by all
+// XCDs), without the L2 writeback/invalidate of an agent-scope fence.
+__device__ __forceinline__ void store_coherent(float *p, float a, float b) {
+  const uint64_t v = static_cast<uint64_t>(__float_as_uint(a)) |
+                     (static_cast<uint64_t>(__float_as_uint(b)) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void load_coherent(const float *p, float &a, float &b) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  a = __uint_as_float(static_cast<uint32_t>(v));
+  b = __uint_as_float(static_cast<uint32_t>(v >> 32));
+}
+// Wait until every memory access this wave issued has completed; the
+// "memory" clobber keeps the compiler from moving accesses across it.
+__device__ __forceinline__ void wait_memory() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Interleave the 8 XCDs: dispatch hands workgroup b to XCD b % 8; give each
+// XCD a contiguous range of items so one XCD walks neighbouring columns of
+// the same rows.
+__device__ __forceinline__ int xcd_item(int b, int grid) {
+  const int per = grid >> 3;  // grid is a multiple of 8
+  return (b & 7) * per + (b >> 3);
 }
 
-// Transpose eight rows x eight bf16 columns held one row per register into
-// eight operands holding one column (8 rows) each.
-__device__ __forceinline__ void transpose8(const u32x4 (&r)[8], u32x4 (&b)[8]) {
+// rows r = 0..7 of a 8 x 4 bf16 block (one u32x2 per row) -> four operands,
+// operand e holding column e for reduction slots r = 0..7.
+__device__ __forceinline__ void transpose84(const u32x2 (&r)[8], u32x4 (&b)[4]) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
+  for (int e = 0; e < 4; ++e) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint32_t lo = r[2 * q][e >> 1], hi = r[2 * q + 1][e >> 1];
@@ -71,101 +84,361 @@ __device__ __forceinline__ void transpose8(const u32x4 (&r)[8], u32x4 (&b)[8]) {
   }
 }
 
-template <int MB, int XM>
-__global__ __launch_bounds__(kWaves * 64) void gemv_bf16_kernel(GemvArgs a) {
-  __shared__ float red[MB * 16 * kPitch];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c = lane & 15, grp = lane >> 4;
+// Activation rows are loaded raw into the prefetch ring with the weights
+// (so waiting for a step never waits for later prefetches) and converted to
+// the bf16 A operand when the step is computed.
+template <int XF32>
+__device__ __forceinline__ void load_x_raw(const void *X, int ldx, int row, int k,
+                                           u32x4 (&r)[XF32 ? 2 : 1]) {
+  if constexpr (XF32) {
+    const float *p = static_cast<const float *>(X) + static_cast<size_t>(row) * ldx + k;
+    r[0] = *reinterpret_cast<const u32x4 *>(p);
+    r[1] = *reinterpret_cast<const u32x4 *>(p + 4);
+  } else {
+    r[0] = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(X) +
+                                            static_cast<size_t>(row) * ldx + k);
+  }
+}
 
-  const int bx = blockIdx.x;
+// Raw row values -> bf16 operand; with NORM, accumulate the sum of squares
+// of the raw values and multiply by the gains (raw gain words in g).
+template <int XF32, int NORM, int GF32>
+__device__ __forceinline__ u32x4 make_x(const u32x4 (&r)[XF32 ? 2 : 1],
+                                        const u32x4 (&g)[GF32 ? 2 : 1], bool has_gamma,
+                                        float &ssq) {
+  if constexpr (!XF32 && !NORM) {
+    return r[0];
+  } else {
+    float v[8];
+    if constexpr (XF32) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[i] = __uint_as_float(r[0][i]);
+        v[4 + i] = __uint_as_float(r[1][i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bflo(r[0][i]);
+        v[2 * i + 1] = bfhi(r[0][i]);
+      }
+    }
+    if constexpr (NORM) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ssq = fmaf(v[i], v[i], ssq);
+      if (has_gamma) {
+        if constexpr (GF32) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[i] *= __uint_as_float(g[0][i]);
+            v[4 + i] *= __uint_as_float(g[1][i]);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[2 * i] *= bflo(g[0][i]);
+            v[2 * i + 1] *= bfhi(g[0][i]);
+          }
+        }
+      }
+    }
+    return u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
+  }
+}
+
+template <int MB, int XF32, int PAIRED, int NORM, int GF32>
+__global__ __launch_bounds__(kThreads) void gemv_kernel(GvArgs a) {
+  constexpr int HALVES = PAIRED ? 2 : 1;
+  constexpr int NREG = HALVES * MB * 4 * 4;  // accumulator floats per lane
+  constexpr int PART = NREG * 64 + MB * 16;  // floats of one partial (sums + row ssq)
+  __shared__ __attribute__((aligned(16))) float red[NREG * 64 + MB * 16];
+  __shared__ float ssq_w[kWaves][MB * 16];
+  __shared__ int last_flag;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 15, grp = lane >> 4;
+  const int item = xcd_item(blockIdx.x, gridDim.x);
+  if (item >= a.nstrips * a.ksplit) return;
+  const int split = item / a.nstrips;
+  const int strip = item - split * a.nstrips;
   int si = 0;
-  if (a.nseg > 1 && bx >= a.seg[1].strip_begin) si = 1;
-  if (a.nseg > 2 && bx >= a.seg[2].strip_begin) si = 2;
-  const GemvSeg sg = a.seg[si];
-  const int n0 = (bx - sg.strip_begin) * kCols;
-  const int col = n0 + 8 * c;
-  const bool col_ok = col < sg.N;
+  if (a.nseg > 1 && strip >= a.seg[1].strip_begin) si = 1;
+  if (a.nseg > 2 && strip >= a.seg[2].strip_begin) si = 2;
+  const GvSeg sg = a.seg[si];
+  const int n0 = (strip - sg.strip_begin) * kCols;
 
-  const int ksteps = a.K >> 5;
-  const int c0 = static_cast<int>(static_cast<int64_t>(blockIdx.y) * ksteps / gridDim.y);
-  const int c1 = static_cast<int>(static_cast<int64_t>(blockIdx.y + 1) * ksteps / gridDim.y);
-  const int span = c1 - c0;
-  const int s0 = c0 + wave * span / kWaves, s1 = c0 + (wave + 1) * span / kWaves;
+  const int ksteps = (a.K + a.K2) >> 5;
+  const int s_begin = split * a.split_steps;
+  const int s_end = min(s_begin + a.split_steps, ksteps);
+  const size_t ldw = static_cast<size_t>(sg.N);
 
-  f32x4 acc[MB][8];
+  f32x4 acc[HALVES][MB][4];
+#pragma unroll
+  for (int h = 0; h < HALVES; ++h)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[h][mb][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float ssq[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) ssq[mb] = 0.f;
+
+  // 32-row steps (weights + activations) in flight per wave
+  constexpr int kDepth = MB <= 2 ? 4 : 2;
+  constexpr int XW = XF32 ? 2 : 1;   // raw 16-byte words per activation row chunk
+  constexpr int GW = NORM ? (GF32 ? 2 : 1) : 1;
+  struct Stage {
+    u32x2 w[8];
+    u32x4 x[MB][XW];
+    u32x4 g[GW];
+  };
+  const bool has_gamma = NORM && a.gamma != nullptr;
+  // every load below is unconditional (rows clamped, pointers selected), so
+  // the compiler's wait counts stay exact across the prefetch ring
+  const void *gsrc = has_gamma ? a.gamma : sg.X;
+  auto load_stage = [&](Stage &sb, int st) {
+    int krow = st * 32;
+    const bool second = PAIRED && krow >= a.K;
+    const uint16_t *W = second ? sg.W2 : sg.W;
+    const void *X = second ? sg.X2 : sg.X;
+    const int ldx = second ? sg.ldx2 : sg.ldx;
+    krow -= second ? a.K : 0;
+    const uint16_t *p = W + static_cast<size_t>(krow + 8 * grp) * ldw + n0 + 4 * j;
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      sb.w[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p + r * ldw));
+    const int k = krow + 8 * grp;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) load_x_raw<XF32>(X, ldx, min(mb * 16 + j, a.M - 1), k, sb.x[mb]);
+    if constexpr (NORM) {
+      if constexpr (GF32) {
+        const float *gp = static_cast<const float *>(gsrc) + k;
+        sb.g[0] = *reinterpret_cast<const u32x4 *>(gp);
+        sb.g[GW - 1] = *reinterpret_cast<const u32x4 *>(gp + 4);
+      } else {
+        sb.g[0] = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(gsrc) + k);
+      }
+    }
+  };
+  auto compute = [&](const Stage &sb, int st) {
+    u32x4 b[4];
+    transpose84(sb.w, b);
+    if (PAIRED && st * 32 >= a.K) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        u32x4 x = sb.x[mb][0];
+        if (mb * 16 + j >= a.M) x = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[HALVES - 1][mb][e] = mfma_bf16(x, b[e], acc[HALVES - 1][mb][e]);
+      }
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        u32x4 x = make_x<XF32, NORM, GF32>(sb.x[mb], sb.g, has_gamma, ssq[mb]);
+        if (mb * 16 + j >= a.M) x = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[0][mb][e] = mfma_bf16(x, b[e], acc[0][mb][e]);
+      }
+    }
+  };
+
+  // this wave's steps: s_begin + wave + kWaves * i, i < nst; kDepth in flight.
+  // Ring slots past the last step reload the last step (cache hits) so the
+  // loop body has no conditional loads.
+  const int st0 = s_begin + wave;
+  const int nst = st0 < s_end ? (s_end - st0 + kWaves - 1) / kWaves : 0;
+  const int st_last = st0 + kWaves * (nst - 1);
+  if (nst > 0) {
+    Stage ring[kDepth];
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) load_stage(ring[d], min(st0 + kWaves * d, st_last));
+    for (int i = 0; i < nst; i += kDepth) {
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) {
+        if (i + d < nst) compute(ring[d], st0 + kWaves * (i + d));
+        load_stage(ring[d], min(st0 + kWaves * (i + d + kDepth), st_last));
+      }
+    }
+  }
+  // ssq of padded rows stays zero: make_x saw clamped copies of row M-1
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[mb][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (mb * 16 + j >= a.M) ssq[mb] = 0.f;
 
-  const size_t ldw = static_cast<size_t>(sg.N);
-  const uint16_t *wcol = sg.W + col;
-  u32x4 cur[8], nxt[8];
-  auto load_w = [&](u32x4 (&r)[8], int st) {
-    const uint16_t *wp = wcol + static_cast<size_t>(st * 32 + 8 * grp) * ldw;
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-      r[s] = col_ok ? *reinterpret_cast<const u32x4 *>(wp + s * ldw) : u32x4{0u, 0u, 0u, 0u};
-  };
-  auto compute = [&](const u32x4 (&r)[8], int st) {
-    u32x4 b[8];
-    transpose8(r, b);
+  // row sums of squares of this wave: lanes j, j+16, j+32, j+48 hold row j
+  if constexpr (NORM) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const u32x4 x = load_x<XM>(sg, a.M, mb * 16 + c, st * 32 + 8 * grp);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[mb][e] = mfma_bf16(x, b[e], acc[mb][e]);
-    }
-  };
-
-  if (s0 < s1) load_w(cur, s0);
-  for (int st = s0; st < s1; st += 2) {
-    if (st + 1 < s1) load_w(nxt, st + 1);
-    compute(cur, st);
-    if (st + 1 < s1) {
-      if (st + 2 < s1) load_w(cur, st + 2);
-      compute(nxt, st + 1);
+      float v = wave_sum_xor(ssq[mb], 16);
+      v = wave_sum_xor(v, 32);
+      if (grp == 0) ssq_w[wave][mb * 16 + j] = v;
     }
   }
 
-  for (int i = threadIdx.x; i < MB * 16 * kPitch; i += blockDim.x) red[i] = 0.f;
-  __syncthreads();
-  // lane (c, grp) holds D[4*grp + r][c] of operand e = global column 8c + e;
-  // LDS column index e*16 + c keeps the 64 lanes on distinct banks.
+  // fixed-order sum of the four waves: red[reg][lane]
+  for (int w = 0; w < kWaves; ++w) {
+    if (wave == w) {
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+      for (int h = 0; h < HALVES; ++h)
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        atomicAdd(&red[(mb * 16 + 4 * grp + r) * kPitch + e * 16 + c], acc[mb][e][r]);
-  __syncthreads();
-  for (int i = threadIdx.x; i < MB * 16 * kCols; i += blockDim.x) {
-    const int m = i / kCols, cc = i % kCols;
-    if (m < a.M && n0 + cc < sg.N)
-      unsafeAtomicAdd(sg.out + static_cast<size_t>(m) * sg.ldo + n0 + cc,
-                      red[m * kPitch + (cc & 7) * 16 + (cc >> 3)]);
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int reg = ((h * MB + mb) * 4 + e) * 4 + i;
+              const float prev = w == 0 ? 0.f : red[reg * 64 + lane];
+              red[reg * 64 + lane] = prev + acc[h][mb][e][i];
+            }
+    }
+    __syncthreads();
   }
+  if constexpr (NORM) {
+    for (int m = tid; m < MB * 16; m += kThreads) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) v += ssq_w[w][m];
+      red[NREG * 64 + m] = v;
+    }
+    __syncthreads();
+  }
+
+  if (a.ksplit > 1) {
+    float *mine = a.part + (static_cast<size_t>(strip) * a.ksplit + split) * PART;
+    for (int i = tid; i < PART / 2; i += kThreads) store_coherent(mine + 2 * i, red[2 * i], red[2 * i + 1]);
+    wait_memory();
+    __syncthreads();
+    if (tid == 0)
+      last_flag = __hip_atomic_fetch_add(&a.counters[strip], 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT) == a.ksplit - 1;
+    __syncthreads();
+    if (!last_flag) return;
+    // eight partials in flight per thread (indices clamped, loads
+    // unconditional), summed in split order
+    const float *base = a.part + static_cast<size_t>(strip) * a.ksplit * PART;
+    const int ks = a.ksplit;
+    for (int i = tid; i < PART / 2; i += kThreads) {
+      float v0 = 0.f, v1 = 0.f;
+      for (int sp0 = 0; sp0 < ks; sp0 += 8) {
+        float x0[8], x1[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          load_coherent(base + static_cast<size_t>(min(sp0 + u, ks - 1)) * PART + 2 * i, x0[u], x1[u]);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (sp0 + u < ks) {
+            v0 += x0[u];
+            v1 += x1[u];
+          }
+        }
+      }
+      red[2 * i] = v0;
+      red[2 * i + 1] = v1;
+    }
+    if (tid == 0) __hip_atomic_store(&a.counters[strip], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+  }
+
+  // epilogue: thread t writes column n0 + t % 64 of rows t / 64 + 4q
+  const int nl = tid & 63;
+  const int n = n0 + nl;
+  if (n >= sg.N) return;
+  const int e = nl & 3, jj = nl >> 2;
+#pragma unroll
+  for (int q = 0; q < MB * 4; ++q) {
+    const int m = (tid >> 6) + 4 * q;
+    if (m >= a.M) break;
+    const int mb = m >> 4, g4 = (m & 15) >> 2, i = m & 3;
+    const int ln = 16 * g4 + jj;
+    float v = red[(((0 * MB + mb) * 4 + e) * 4 + i) * 64 + ln];
+    if constexpr (NORM) v *= rsqrtf(red[NREG * 64 + m] / static_cast<float>(a.K) + a.eps);
+    switch (sg.omode) {
+      case GV_OUT_BF16:
+        static_cast<uint16_t *>(sg.out)[static_cast<size_t>(m) * sg.ldo + n] = f2bf(v);
+        break;
+      case GV_OUT_F32:
+        static_cast<float *>(sg.out)[static_cast<size_t>(m) * sg.ldo + n] = v;
+        break;
+      case GV_OUT_CACHE: {
+        const int b = m / a.T, t = m - b * a.T;
+        const size_t row = static_cast<size_t>(b) * a.L_max + a.past[b] + t;
+        static_cast<uint16_t *>(sg.out)[row * sg.ldo + n] = f2bf(v);
+        break;
+      }
+      case GV_OUT_RES_F32: {
+        const size_t ri = static_cast<size_t>(m) * sg.ldr + n;
+        v += sg.res_f32 ? static_cast<const float *>(sg.R)[ri]
+                        : bf2f(static_cast<const uint16_t *>(sg.R)[ri]);
+        static_cast<float *>(sg.out)[static_cast<size_t>(m) * sg.ldo + n] = v;
+        if (sg.out2) sg.out2[static_cast<size_t>(m) * sg.ldo + n] = v;
+        break;
+      }
+      case GV_OUT_RES_BF16:
+        v += static_cast<const float *>(sg.R)[static_cast<size_t>(m) * sg.ldr + n];
+        static_cast<uint16_t *>(sg.out)[static_cast<size_t>(m) * sg.ldo + n] = f2bf(v);
+        break;
+      default: {  // GV_OUT_SWIGLU
+        const float u = red[(((1 * MB + mb) * 4 + e) * 4 + i) * 64 + ln];
+        static_cast<uint16_t *>(sg.out)[static_cast<size_t>(m) * sg.ldo + n] = f2bf(silu(v) * u);
+        break;
+      }
+    }
+  }
+}
+
+template <int MB, int XF32, int PAIRED, int NORM, int GF32>
+hipError_t launch_t(const GvArgs &a, int grid, hipStream_t s) {
+  gemv_kernel<MB, XF32, PAIRED, NORM, GF32><<<grid, kThreads, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 template <int MB>
-hipError_t launch_mb(const GemvArgs &a, dim3 grid, hipStream_t s) {
-  switch (a.xmode) {
-    case GEMV_X_BF16: gemv_bf16_kernel<MB, GEMV_X_BF16><<<grid, kWaves * 64, 0, s>>>(a); break;
-    case GEMV_X_F32: gemv_bf16_kernel<MB, GEMV_X_F32><<<grid, kWaves * 64, 0, s>>>(a); break;
-    default: gemv_bf16_kernel<MB, GEMV_X_SWIGLU_F32><<<grid, kWaves * 64, 0, s>>>(a); break;
+hipError_t launch_mb(const GvArgs &a, int grid, hipStream_t s) {
+  if (a.K2 > 0) return launch_t<MB, 0, 1, 0, 0>(a, grid, s);
+  if (a.norm) {
+    if (a.x_f32)
+      return a.gamma_f32 ? launch_t<MB, 1, 0, 1, 1>(a, grid, s) : launch_t<MB, 1, 0, 1, 0>(a, grid, s);
+    return a.gamma_f32 ? launch_t<MB, 0, 0, 1, 1>(a, grid, s) : launch_t<MB, 0, 0, 1, 0>(a, grid, s);
   }
-  return hipGetLastError();
+  return a.x_f32 ? launch_t<MB, 1, 0, 0, 0>(a, grid, s) : launch_t<MB, 0, 0, 0, 0>(a, grid, s);
+}
+
+int env_int(const char *name, int dflt) {
+  const char *v = getenv(name);
+  return (v && *v) ? atoi(v) : dflt;
 }
 }  // namespace
 
-int gemv_strips(int N) { return (N + kCols - 1) / kCols; }
-
-hipError_t launch_gemv_bf16(const GemvArgs &a, int ksplit, hipStream_t s) {
-  TraceGuard trace_guard(K_GEMV_BF16, s);
+size_t gemv_plan(GvArgs &a) {
   int strips = 0;
-  for (int i = 0; i < a.nseg; ++i) strips += gemv_strips(a.seg[i].N);
-  dim3 grid(strips, ksplit);
+  for (int i = 0; i < a.nseg; ++i) {
+    a.seg[i].strip_begin = strips;
+    strips += (a.seg[i].N + kCols - 1) / kCols;
+  }
+  a.nstrips = strips;
+  const int ksteps = (a.K + a.K2) / 32;
+  const int target = env_int("DL_GEMV_WGS", 128);
+  const int min_steps = env_int("DL_GEMV_MIN_STEPS", 16);
+  int ks = (target + strips - 1) / strips;
+  ks = std::min(ks, std::max(1, ksteps / min_steps));
+  ks = std::max(1, std::min(ks, 64));
+  const int sps = (ksteps + ks - 1) / ks;
+  a.split_steps = sps;
+  a.ksplit = (ksteps + sps - 1) / sps;
+  const int MB = (a.M + 15) / 16;
+  const int halves = a.K2 > 0 ? 2 : 1;
+  const size_t part = static_cast<size_t>(halves) * MB * 16 * 64 + MB * 16;
+  return a.ksplit > 1 ? part * a.nstrips * a.ksplit : 0;
+}
+
+int gemv_counters(const GvArgs &a) { return a.nstrips; }
+
+hipError_t launch_gemv(const GvArgs &a, hipStream_t s) {
+  TraceGuard trace_guard(K_GEMV_BF16, s);
+  const int items = a.nstrips * a.ksplit;
+  const int grid = (items + 7) / 8 * 8;
   const int mb = (a.M + 15) / 16;
   switch (mb) {
     case 1: return launch_mb<1>(a, grid, s);

@@ -8,35 +8,56 @@
 namespace dl {
 
 // ---------------------------------------------------------------------------
-// Weight-streaming bf16 GEMV for small M (decode): out_s[M, N_s] += X_s W_s.
-// Up to three segments share M and K; each has its own activations, weight
-// and fp32 output. Outputs are accumulated with atomics, so they must hold
-// their initial value (zero or a residual) before the launch.
+// Weight-streaming bf16 GEMV for small M (decode), M <= 64:
+// out_s = epilogue(X_s[M, K] W_s[K, N_s]) for up to three segments that
+// share M and K. Paired launches (K2 > 0) have one segment whose two halves
+// (X, W, K) and (X2, W2, K2) produce two results for the same output
+// columns, combined by the SwiGLU epilogue.
 // ---------------------------------------------------------------------------
-enum GemvX : int {
-  GEMV_X_BF16 = 0,       // X: bf16 [M, K]
-  GEMV_X_F32 = 1,        // X: f32 [M, K]
-  GEMV_X_SWIGLU_F32 = 2  // X = silu(X) * X2, both f32 [M, K]
+enum GvOut : int {
+  GV_OUT_BF16 = 0,      // out bf16 [m * ldo + n] = v
+  GV_OUT_F32 = 1,       // out f32 [m * ldo + n] = v
+  GV_OUT_CACHE = 2,     // out bf16 row (b * L_max + past[b] + t), m = b * T + t
+  GV_OUT_RES_F32 = 3,   // out f32 = v + R (R f32 if res_f32, else bf16); out2 gets a copy
+  GV_OUT_RES_BF16 = 4,  // out bf16 = v + R (R f32)
+  GV_OUT_SWIGLU = 5     // paired: out bf16 = silu(v_first) * v_second
 };
 
-struct GemvSeg {
-  const uint16_t *W;  // [K, N] bf16
-  const void *X;      // [M, ldx]
-  const float *X2;    // second operand of the SwiGLU prologue
-  float *out;         // [M, ldo] f32
-  int N, ldx, ldo;
-  int strip_begin;    // index of this segment's first 128-column strip
+struct GvSeg {
+  const uint16_t *W;   // [K, N] bf16
+  const uint16_t *W2;  // paired: second half [K2, N]
+  const void *X;       // [M, ldx] bf16 (or f32 with x_f32)
+  const void *X2;      // paired: second-half activations, bf16 [M, ldx2]
+  void *out;
+  float *out2;         // optional copy (GV_OUT_RES_F32)
+  const void *R;       // residual [M, ldr]
+  int N, ldx, ldx2, ldo, ldr;
+  int omode, res_f32;
+  int strip_begin;     // set by gemv_plan
 };
 
-struct GemvArgs {
-  GemvSeg seg[3];
+struct GvArgs {
+  GvSeg seg[3];
   int nseg;
-  int M, K;
-  int xmode;
+  int M, K, K2;           // K2 > 0 only for paired launches (then nseg == 1)
+  int x_f32;              // X is f32 (else bf16); paired launches use bf16
+  int norm;               // fused RMSNorm: X scaled by gamma, rows of the result by
+                          // 1 / sqrt(mean(X^2) + eps) (mean over the K columns)
+  const void *gamma;      // [K] gains or NULL (= 1)
+  int gamma_f32;
+  float eps;
+  const int32_t *past;    // cache scatter (GV_OUT_CACHE)
+  int T, L_max;
+  // set by gemv_plan / the caller
+  int nstrips, ksplit, split_steps;
+  float *part;            // gemv_plan's return value in floats
+  int *counters;          // nstrips ints, zero before the launch (left zero after it)
 };
 
-hipError_t launch_gemv_bf16(const GemvArgs &a, int ksplit, hipStream_t s);
-int gemv_strips(int N);
+// Chooses the K split and strip numbering; returns the partial-sum floats
+// the launch needs (0 when there is no split).
+size_t gemv_plan(GvArgs &a);
+hipError_t launch_gemv(const GvArgs &a, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // bf16 MFMA GEMM for large M (prefill): C_s[M, N_s] = X_s[M, K] W_s[K, N_s]
@@ -89,20 +110,20 @@ hipError_t launch_pack_up_factor(const uint16_t *B, uint16_t *packed, int r, int
 struct AttnDecodeArgs {
   const void *q;       // [Bsz, n_q, d] bf16 or f32 (q_f32)
   const uint16_t *ck, *cv;
-  const uint16_t *bk_packed, *bv_packed;
+  const uint16_t *bk, *bv;  // up factors, row-major [r, n_kv * d]
   const int32_t *ctx_lens;
-  float *part;         // [Bsz, n_q, nsplit, d + 2]
+  void *out;           // [Bsz, n_q, d] bf16 (or f32 with out_f32)
+  float *part;         // [Bsz, n_q, nsplit, d + 2] split partials (nsplit > 1)
+  int *counters;       // [Bsz * n_kv], zero on entry, left zero
   int Bsz, n_q, n_kv, d, r_k, r_v, L_max;
   int ctx_offset;      // context of sequence b = ctx_lens[b] + ctx_offset
-  int nsplit, tiles_per_split;
+  int nsplit, tiles_per_split;  // tiles of attn_decode_positions_per_tile() positions
   float scale_log2;    // sm_scale * log2(e)
   float theta;
-  int q_f32;
+  int q_f32, out_f32;
 };
+int attn_decode_positions_per_tile();
 hipError_t launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s);
-// out[b, h, :] from the split partials; out is bf16 (out_f32 = 0) or f32.
-hipError_t launch_attn_combine(const float *part, void *out, int Bsz, int n_q, int nsplit, int d,
-                               int out_f32, hipStream_t s);
 
 struct AttnPrefillArgs {
   const void *q;       // [Bsz, T, n_q, d] bf16 or f32
