@@ -15,11 +15,26 @@ independent device copies of weights and cache are used in turn so the
 256 MB Infinity Cache cannot serve one step from the previous one. Steps are
 replayed from a HIP graph (one per copy) unless --no-graph.
 
+Per-kernel durations come from hipEvents that the library records around
+each of its launches on the launch stream. A traced step is queued behind a
+spin kernel, so every launch and event is enqueued before the GPU reaches
+them and the events time back-to-back execution, not host launch gaps.
+
+The roofline object describes the kernel kind that takes the largest share
+of the decode step: achieved = algorithmic bytes (or flops) per launch /
+average launch duration. Its "traffic" field is the HBM bytes per launch
+measured by rocprofv3 FETCH_SIZE + WRITE_SIZE counters (scaled by the same
+counters on a plain copy of known size), read from profiles/traffic.json
+only while the kernel sources hash to the value recorded there.
+
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+       python bench.py --calibrate-copy   (one plain device copy of 1 GiB;
+                                           run under rocprofv3 --pmc)
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -47,6 +62,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--sets", type=int, default=2)
+    p.add_argument("--calibrate-copy", action="store_true")
     return p.parse_args()
 
 
@@ -160,18 +176,39 @@ def timed(torch, fn, steps, warmup):
 
 def trace_breakdown(torch, binding, sets, nsteps):
     """Per-kernel durations from hipEvents recorded around every library
-    launch, over nsteps eager steps. Returns {(kind, role): [ms, ...]}."""
+    launch, over nsteps steps, each queued behind a spin kernel so the
+    events time GPU execution only. Returns {(kind, role): [ms, ...]}."""
     tr = binding.KernelTrace(capacity=64 * nsteps + 64)
     torch.cuda.synchronize()
     with tr:
         for i in range(nsteps):
+            torch.cuda._sleep(2_000_000)   # spin so the step's launches queue up behind it
             run_step(sets[i % len(sets)])
-    torch.cuda.synchronize()
+            torch.cuda.synchronize()
     per = {}
     for kind, role, ms in tr.records():
         per.setdefault((kind, role), []).append(ms)
     tr.close()
     return per
+
+
+def kernel_source_hash():
+    from rank_decomposed_linear_amd.profiling import source_hash
+    return source_hash()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    counter summary, or None when absent or taken on other sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("source_hash") != kernel_source_hash() or t.get("workload") != workload:
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
 
 
 def decode_bench(args, torch, binding, W):
@@ -235,27 +272,35 @@ def decode_bench(args, torch, binding, W):
         breakdown[kind] = e
     roles = {f"{kind}/{role}": round(sum(lst) / n * 1e3, 2) for (kind, role), lst in sorted(per.items())}
 
-    # dominant kernel of the step
-    dom = max(kinds.items(), key=lambda kv: kv[1]["ms_per_step"])
-    dname, dk = dom
-    nl = max(dk["launches_per_step"], 1)
-    avg_s = dk["ms_per_step"] * 1e-3 / nl
-    if dname == "attn_decode_bf16":
-        achieved = dk["flops_per_step"] / nl / avg_s / 1e12
-        roof = {"kernel": dname, "bound": "mfma", "achieved": round(achieved, 2),
-                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                "avg_us": round(avg_s * 1e6, 2), "launches_per_step": nl}
-    else:
-        achieved = dk["bytes_per_step"] / nl / avg_s / 1e9
-        roof = {"kernel": dname, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+    # dominant kernel kind of the step (largest share of the step time)
+    def roofline(name):
+        k = kinds[name]
+        nl = max(k["launches_per_step"], 1)
+        avg_s = k["ms_per_step"] * 1e-3 / nl
+        if name == "attn_decode_bf16":
+            achieved = k["flops_per_step"] / nl / avg_s / 1e12
+            return {"kernel": name, "bound": "mfma", "achieved": round(achieved, 2),
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "traffic": measured_traffic(name, w.name),
+                    "avg_us": round(avg_s * 1e6, 2), "launches_per_step": nl,
+                    "algorithmic_flops_per_launch": int(k["flops_per_step"] / nl),
+                    "algorithmic_bytes_per_launch": int(k["bytes_per_step"] / nl)}
+        achieved = k["bytes_per_step"] / nl / avg_s / 1e9
+        return {"kernel": name, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(name, w.name),
                 "avg_us": round(avg_s * 1e6, 2), "launches_per_step": nl,
-                "algorithmic_bytes_per_launch": int(dk["bytes_per_step"] / nl)}
+                "algorithmic_bytes_per_launch": int(k["bytes_per_step"] / nl)}
+
+    dname = max(kinds.items(), key=lambda kv: kv[1]["ms_per_step"])[0]
+    roof = roofline(dname)
+    roof_attn = roofline("attn_decode_bf16") if "attn_decode_bf16" in kinds else None
     step_bytes = W.algorithmic_decode_bytes(w.shape, Bsz, ctx_total // Bsz)["total"]
     result = {
         "value": Bsz / (ms * 1e-3), "ms_per_step": ms, "wall_s": wall, "graph": use_graph,
-        "roofline": roof, "kernels": breakdown, "roles_us_per_step": roles,
+        "roofline": roof, "roofline_attention": roof_attn, "kernels": breakdown,
+        "roles_us_per_step": roles,
         "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "config": {"workload": w.name, "batch": Bsz, "context": int(inp.past_lens[0]) + 1,
                    "hidden": w.shape.hidden, "n_q": w.shape.n_q, "n_kv": w.shape.n_kv,
@@ -333,6 +378,17 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        # one plain device-to-device copy of 1 GiB: the reference for the
+        # FETCH_SIZE / WRITE_SIZE counter scale
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n}), flush=True)
+        return
     binding.load()
     dec, weights, inp = decode_bench(args, torch, binding, W)
     log(f"decode: {dec['value']:.0f} tokens/s, {dec['ms_per_step'] * 1e3:.1f} us/step")
@@ -350,7 +406,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded; random-init factors, pre-filled low-rank cache)",
         "config": dec["config"], "graph": dec["graph"],
-        "roofline": dec["roofline"], "step_hbm_frac": dec["step_hbm_frac"],
+        "roofline": dec["roofline"], "roofline_attention": dec["roofline_attention"],
+        "step_hbm_frac": dec["step_hbm_frac"], "kernel_source_hash": kernel_source_hash(),
         "cpu_baseline": cpu, "prefill": pre, "kernels": dec["kernels"],
         "roles_us_per_step": dec["roles_us_per_step"],
     }
