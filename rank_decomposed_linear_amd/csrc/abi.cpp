@@ -11,7 +11,7 @@
 #include <algorithm>
 #include <string>
 
-#include "../../include/dl.h"
+#include "dl.h"
 #include "common.h"
 #include "kernels.h"
 #include "trace.h"
@@ -196,19 +196,21 @@ hipError_t gemm_f32(const float *X, const float *X2, const void *W, float *C, in
 // Attention planning
 // ---------------------------------------------------------------------------
 struct DecodePlan {
-  int nsplit, tiles_per_split;
+  int nsplit, split_len;
 };
-// Context splits of decode attention: enough (sequence, kv head, split)
-// work items to cover the chip, at most 64 splits.
+// Context splits of decode attention: one workgroup per CU for the
+// (sequence, kv head) work items, splits balanced to the position granule,
+// at most 64 splits.
 DecodePlan plan_decode(int64_t Bsz, int64_t n_kv, int64_t L_max) {
-  const int per_tile = attn_decode_positions_per_tile();
-  const int tiles = static_cast<int>((L_max + per_tile - 1) / per_tile);
-  const int target = env_int("DL_ATTN_TARGET_WGS", 512);
+  const int gran = attn_decode_split_granule();
+  const int target = env_int("DL_ATTN_TARGET_WGS", 256);
   int ns = static_cast<int>((target + Bsz * n_kv - 1) / (Bsz * n_kv));
-  ns = std::max(1, std::min(ns, std::min(tiles, 64)));
-  const int tps = (tiles + ns - 1) / ns;
-  ns = (tiles + tps - 1) / tps;
-  return {ns, tps};
+  ns = std::max(1, std::min(ns, 64));
+  ns = std::min<int64_t>(ns, (L_max + gran - 1) / gran);
+  int len = static_cast<int>((L_max + ns - 1) / ns);
+  len = (len + gran - 1) / gran * gran;
+  ns = static_cast<int>((L_max + len - 1) / len);
+  return {ns, len};
 }
 
 // Attention scratch: packed up factors (prefill), split partials and
@@ -294,7 +296,7 @@ hipError_t run_attn_bf16(const void *q, int q_f32, int ldq, const void *Ck, cons
     a.r_v = r_v;
     a.L_max = L_max;
     a.nsplit = p.nsplit;
-    a.tiles_per_split = p.tiles_per_split;
+    a.split_len = p.split_len;
     a.scale_log2 = scale;
     a.theta = theta;
     return launch_attn_decode_bf16(a, s);

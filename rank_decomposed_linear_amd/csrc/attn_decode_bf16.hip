@@ -134,6 +134,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void attn_decode_kernel(AttnDeco
   __shared__ __attribute__((aligned(16))) float smem[MRG_FLOATS > BS_ELEMS / 2 ? MRG_FLOATS : BS_ELEMS / 2];
   uint16_t *bs = reinterpret_cast<uint16_t *>(smem);
   __shared__ __attribute__((aligned(16))) uint16_t qs[16 * D];
+  __shared__ __attribute__((aligned(16))) u32x4 qfs[NB / 2][64];   // score operands, lane order
   __shared__ double rev64[HALF];
   __shared__ float rev32[HALF];
   __shared__ float mrg_m[NW][16], mrg_l[NW][16];
@@ -152,8 +153,8 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void attn_decode_kernel(AttnDeco
   const int G = a.n_q / a.n_kv;
   const int ctx = a.ctx_lens[b] + a.ctx_offset;
   const int qpos = ctx - 1;
-  const int p_begin = split * a.tiles_per_split * WT;
-  const int p_end = min(p_begin + a.tiles_per_split * WT, ctx);
+  const int p_begin = split * a.split_len;
+  const int p_end = min(p_begin + a.split_len, ctx);
   const bool rope_on = a.theta != 0.f;
   const int ldb = a.n_kv * D;
 
@@ -189,19 +190,23 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void attn_decode_kernel(AttnDeco
   __syncthreads();
   // score B operand: lane (head j, grp) slots 0..3 = q[j][dim(2t, 4grp+r)],
   // slots 4..7 = q[j][dim(2t+1, 4grp+r)]
-  u32x4 qf[NB / 2];
+  if (wave == 0) {
 #pragma unroll
-  for (int t = 0; t < NB / 2; ++t) {
-    uint16_t v[8];
+    for (int t = 0; t < NB / 2; ++t) {
+      uint16_t v[8];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      v[r] = qs[j * D + T::dim(2 * t, 4 * grp + r)];
-      v[4 + r] = qs[j * D + T::dim(2 * t + 1, 4 * grp + r)];
+      for (int r = 0; r < 4; ++r) {
+        v[r] = qs[j * D + T::dim(2 * t, 4 * grp + r)];
+        v[4 + r] = qs[j * D + T::dim(2 * t + 1, 4 * grp + r)];
+      }
+      u32x4 f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        f[q] = static_cast<uint32_t>(v[2 * q]) | (static_cast<uint32_t>(v[2 * q + 1]) << 16);
+      qfs[t][lane] = f;
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      qf[t][q] = static_cast<uint32_t>(v[2 * q]) | (static_cast<uint32_t>(v[2 * q + 1]) << 16);
   }
+  __syncthreads();
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 accO[NB];
 #pragma unroll
@@ -255,12 +260,15 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void attn_decode_kernel(AttnDeco
 #pragma unroll
           for (int r2 = 0; r2 < 2; ++r2) {
             const uint16_t *bsrc = bs + ((buf * 2 + r2) * NB * 64 + lane) * 8;
+            // all operand fragments of the step in flight before the MFMAs
+            u32x4 bop[NB];
 #pragma unroll
-            for (int x = 0; x < NB; ++x) {
-              const u32x4 bop = *reinterpret_cast<const u32x4 *>(bsrc + x * 64 * 8);
+            for (int x = 0; x < NB; ++x) bop[x] = *reinterpret_cast<const u32x4 *>(bsrc + x * 64 * 8);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-              for (int pb = 0; pb < NP; ++pb) acc[x][pb] = mfma_bf16(bop, cf[r2][pb], acc[x][pb]);
-            }
+            for (int x = 0; x < NB; ++x)
+#pragma unroll
+              for (int pb = 0; pb < NP; ++pb) acc[x][pb] = mfma_bf16(bop[x], cf[r2][pb], acc[x][pb]);
           }
         }
         if (loader) factor_store<D>(st, bs + (buf ^ 1) * 2 * NB * 64 * 8, tid);
@@ -299,7 +307,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void attn_decode_kernel(AttnDeco
         sc[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < NB / 2; ++t)
-          sc[pb] = mfma_bf16(pack_acc(acc[2 * t][pb], acc[2 * t + 1][pb]), qf[t], sc[pb]);
+          sc[pb] = mfma_bf16(pack_acc(acc[2 * t][pb], acc[2 * t + 1][pb]), qfs[t][lane], sc[pb]);
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -370,12 +378,15 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void attn_decode_kernel(AttnDeco
 #pragma unroll
           for (int r2 = 0; r2 < 2; ++r2) {
             const uint16_t *bsrc = bs + ((buf * 2 + r2) * NB * 64 + lane) * 8;
+            // all operand fragments of the step in flight before the MFMAs
+            u32x4 bop[NB];
 #pragma unroll
-            for (int x = 0; x < NB; ++x) {
-              const u32x4 bop = *reinterpret_cast<const u32x4 *>(bsrc + x * 64 * 8);
+            for (int x = 0; x < NB; ++x) bop[x] = *reinterpret_cast<const u32x4 *>(bsrc + x * 64 * 8);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-              for (int pb = 0; pb < NP; ++pb) acc[x][pb] = mfma_bf16(cf[r2][pb], bop, acc[x][pb]);
-            }
+            for (int x = 0; x < NB; ++x)
+#pragma unroll
+              for (int pb = 0; pb < NP; ++pb) acc[x][pb] = mfma_bf16(cf[r2][pb], bop[x], acc[x][pb]);
           }
         }
         if (loader) factor_store<D>(st, bs + (buf ^ 1) * 2 * NB * 64 * 8, tid);
@@ -499,6 +510,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void attn_decode_kernel(AttnDeco
 }  // namespace
 
 int attn_decode_positions_per_tile() { return 32 * kDecodeWaves; }
+int attn_decode_split_granule() { return 32; }
 
 hipError_t launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s) {
   TraceGuard trace_guard(K_ATTN_DECODE, s);

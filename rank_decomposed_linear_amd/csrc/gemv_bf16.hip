@@ -40,8 +40,6 @@
 namespace dl {
 
 namespace {
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
 constexpr int kCols = 64;   // output columns per strip
 
 // Device-coherent 8-byte accesses for the split-K partial sums: relaxed
@@ -146,8 +144,9 @@ __device__ __forceinline__ u32x4 make_x(const u32x4 (&r)[XF32 ? 2 : 1],
   }
 }
 
-template <int MB, int XF32, int PAIRED, int NORM, int GF32>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(GvArgs a) {
+template <int MB, int XF32, int PAIRED, int NORM, int GF32, int kWaves>
+__global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
+  constexpr int kThreads = kWaves * 64;
   constexpr int HALVES = PAIRED ? 2 : 1;
   constexpr int NREG = HALVES * MB * 4 * 4;  // accumulator floats per lane
   constexpr int PART = NREG * 64 + MB * 16;  // floats of one partial (sums + row ssq)
@@ -221,14 +220,17 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GvArgs a) {
       }
     }
   };
-  auto compute = [&](const Stage &sb, int st) {
+  // `valid` is false for the padding steps at the end of the ring: their
+  // activation operand is zeroed (a select, not a branch), so the loop body
+  // stays branch-free and the compiler's wait counts stay exact.
+  auto compute = [&](const Stage &sb, int st, bool valid) {
     u32x4 b[4];
     transpose84(sb.w, b);
     if (PAIRED && st * 32 >= a.K) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         u32x4 x = sb.x[mb][0];
-        if (mb * 16 + j >= a.M) x = u32x4{0u, 0u, 0u, 0u};
+        if (!valid || mb * 16 + j >= a.M) x = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           acc[HALVES - 1][mb][e] = mfma_bf16(x, b[e], acc[HALVES - 1][mb][e]);
@@ -236,8 +238,10 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GvArgs a) {
     } else {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        u32x4 x = make_x<XF32, NORM, GF32>(sb.x[mb], sb.g, has_gamma, ssq[mb]);
-        if (mb * 16 + j >= a.M) x = u32x4{0u, 0u, 0u, 0u};
+        float sq = 0.f;
+        u32x4 x = make_x<XF32, NORM, GF32>(sb.x[mb], sb.g, has_gamma, sq);
+        ssq[mb] += valid ? sq : 0.f;
+        if (!valid || mb * 16 + j >= a.M) x = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[0][mb][e] = mfma_bf16(x, b[e], acc[0][mb][e]);
       }
@@ -245,20 +249,27 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GvArgs a) {
   };
 
   // this wave's steps: s_begin + wave + kWaves * i, i < nst; kDepth in flight.
-  // Ring slots past the last step reload the last step (cache hits) so the
-  // loop body has no conditional loads.
+  // Ring slots past the last step reload the last step (cache hits) and
+  // compute with a zero operand, so the loop body has no branches.
   const int st0 = s_begin + wave;
   const int nst = st0 < s_end ? (s_end - st0 + kWaves - 1) / kWaves : 0;
   const int st_last = st0 + kWaves * (nst - 1);
   if (nst > 0) {
     Stage ring[kDepth];
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d) load_stage(ring[d], min(st0 + kWaves * d, st_last));
+    for (int d = 0; d < kDepth; ++d) {
+      load_stage(ring[d], min(st0 + kWaves * d, st_last));
+      __builtin_amdgcn_sched_barrier(0);   // stages issue in ring order
+    }
     for (int i = 0; i < nst; i += kDepth) {
 #pragma unroll
       for (int d = 0; d < kDepth; ++d) {
-        if (i + d < nst) compute(ring[d], st0 + kWaves * (i + d));
+        compute(ring[d], min(st0 + kWaves * (i + d), st_last), i + d < nst);
+        // keep the ring order: the scheduler must not sink this reload
+        // next to its use or hoist it above the compute of an older stage
+        __builtin_amdgcn_sched_barrier(0);
         load_stage(ring[d], min(st0 + kWaves * (i + d + kDepth), st_last));
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
@@ -341,14 +352,14 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GvArgs a) {
     __syncthreads();
   }
 
-  // epilogue: thread t writes column n0 + t % 64 of rows t / 64 + 4q
+  // epilogue: thread t writes column n0 + t % 64 of rows t / 64 + kWaves * q
   const int nl = tid & 63;
   const int n = n0 + nl;
   if (n >= sg.N) return;
   const int e = nl & 3, jj = nl >> 2;
 #pragma unroll
-  for (int q = 0; q < MB * 4; ++q) {
-    const int m = (tid >> 6) + 4 * q;
+  for (int q = 0; q < (MB * 16 + kWaves - 1) / kWaves; ++q) {
+    const int m = (tid >> 6) + kWaves * q;
     if (m >= a.M) break;
     const int mb = m >> 4, g4 = (m & 15) >> 2, i = m & 3;
     const int ln = 16 * g4 + jj;
@@ -390,7 +401,10 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GvArgs a) {
 
 template <int MB, int XF32, int PAIRED, int NORM, int GF32>
 hipError_t launch_t(const GvArgs &a, int grid, hipStream_t s) {
-  gemv_kernel<MB, XF32, PAIRED, NORM, GF32><<<grid, kThreads, 0, s>>>(a);
+  if (a.waves == 8)
+    gemv_kernel<MB, XF32, PAIRED, NORM, GF32, 8><<<grid, 8 * 64, 0, s>>>(a);
+  else
+    gemv_kernel<MB, XF32, PAIRED, NORM, GF32, 4><<<grid, 4 * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -418,6 +432,7 @@ size_t gemv_plan(GvArgs &a) {
     strips += (a.seg[i].N + kCols - 1) / kCols;
   }
   a.nstrips = strips;
+  a.waves = env_int("DL_GEMV_WAVES", 4) == 8 ? 8 : 4;
   const int ksteps = (a.K + a.K2) / 32;
   const int target = env_int("DL_GEMV_WGS", 128);
   const int min_steps = env_int("DL_GEMV_MIN_STEPS", 16);

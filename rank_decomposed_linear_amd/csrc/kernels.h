@@ -50,6 +50,7 @@ struct GvArgs {
   int T, L_max;
   // set by gemv_plan / the caller
   int nstrips, ksplit, split_steps;
+  int waves;              // waves per workgroup (4 or 8)
   float *part;            // gemv_plan's return value in floats
   int *counters;          // nstrips ints, zero before the launch (left zero after it)
 };
@@ -117,12 +118,13 @@ struct AttnDecodeArgs {
   int *counters;       // [Bsz * n_kv], zero on entry, left zero
   int Bsz, n_q, n_kv, d, r_k, r_v, L_max;
   int ctx_offset;      // context of sequence b = ctx_lens[b] + ctx_offset
-  int nsplit, tiles_per_split;  // tiles of attn_decode_positions_per_tile() positions
+  int nsplit, split_len;  // context positions per split (multiple of attn_decode_split_granule())
   float scale_log2;    // sm_scale * log2(e)
   float theta;
   int q_f32, out_f32;
 };
 int attn_decode_positions_per_tile();
+int attn_decode_split_granule();
 hipError_t launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s);
 
 struct AttnPrefillArgs {
