@@ -122,16 +122,19 @@ def to_dev(torch, a):
 
 
 def make_sets(torch, binding, weights, inp, nsets):
+    from rank_decomposed_linear_amd import workloads as W
     shp = weights.shape
     Bsz, T = inp.x.shape[0], inp.x.shape[1]
     L_max = inp.ck.shape[1]
     sets = []
     for _ in range(nsets):
-        facs = {p: (to_dev(torch, a), to_dev(torch, b)) for p, (a, b) in weights.factors.items()}
+        lf = W.to_library_factor
+        facs = {p: (to_dev(torch, lf(a)), to_dev(torch, lf(b))) for p, (a, b) in weights.factors.items()}
         layer = binding.DecomposedLayer(facs, shp.hidden, shp.n_q, shp.n_kv, shp.head_dim, shp.ffn,
                                         shp.rope_theta, shp.rms_eps)
         st = dict(layer=layer, x=to_dev(torch, inp.x), ck=to_dev(torch, inp.ck),
-                  cv=to_dev(torch, inp.cv), past=to_dev(torch, inp.past_lens))
+                  cv=to_dev(torch, W.to_library_value_cache(inp.cv)),
+                  past=to_dev(torch, inp.past_lens))
         st["y"] = torch.empty_like(st["x"])
         st["ws"] = torch.empty(max(layer.workspace_bytes(Bsz, T, L_max), 16), dtype=torch.uint8,
                                device="cuda:0")

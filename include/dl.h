@@ -16,6 +16,15 @@
  * Conventions shared by every entry point
  *   - Tensors are dense, row-major, contiguous. Every pointer argument is a
  *     device pointer owned by the caller, 16-byte aligned.
+ *   - Factor storage: every factor is passed transposed, so that its rows
+ *     run along the reduction index: A (m x k) as At = A^T [k, m] and
+ *     B (k x n) as Bt = B^T [n, k] (the [out, in] layout of the two maps
+ *     x -> x A and t -> t B). The up factors of attention are B_k^T and
+ *     B_v^T, [n_kv * d, r].
+ *   - Latent caches: the key cache Ck is [Bsz, L_max, r_k] (one row per
+ *     position); the value cache Cv is rank-major, [Bsz, r_v, L_max] (one
+ *     row per rank component), because attention reduces the value latents
+ *     over positions. DL_BF16 attention needs L_max % 8 == 0.
  *   - dtype DL_F32: every tensor is float32 and arithmetic is float32.
  *     dtype DL_BF16: activations, factors, caches and outputs are bfloat16,
  *     products accumulate in float32; intermediates may be rounded to bf16.
@@ -65,7 +74,7 @@ const char *dl_last_error(void);
 
 /* ------------------------------------------------------------------------
  * Factor-pair projection -- section 2.1, Eq. (1).
- *   y[M, n] = (x[M, m] A[m, k]) B[k, n]
+ *   y[M, n] = (x[M, m] A[m, k]) B[k, n]      A passed as At [k, m], B as Bt [n, k]
  * The rank-k intermediate x A lives only in the workspace. For M <= 64 the
  * pair runs as two weight-streaming MFMA GEMV passes; for larger M as two
  * MFMA GEMMs.
@@ -81,9 +90,9 @@ dl_status dl_lowrank_linear(const void *x, const void *A, const void *B, void *y
  * Low-rank KV-cache append -- section 2.1 (the k/v latents are the cache)
  * and section 4.1 (they are stored as KV cache).
  *   Ck[b, past_lens[b] + t, :] = x[b, t, :] A_k     x   : [Bsz, T, m]
- *   Cv[b, past_lens[b] + t, :] = x[b, t, :] A_v     A_k : [m, r_k], A_v: [m, r_v]
+ *   Cv[b, :, past_lens[b] + t] = x[b, t, :] A_v     A_k, A_v passed as [r_k, m], [r_v, m]
  *                                                    Ck  : [Bsz, L_max, r_k]
- *                                                    Cv  : [Bsz, L_max, r_v]
+ *                                                    Cv  : [Bsz, r_v, L_max]
  * past_lens: device int32 [Bsz]; precondition past_lens[b] + T <= L_max.
  * No other cache row is written.
  * DL_BF16 requires m, r_k, r_v to be multiples of 64.
@@ -99,15 +108,18 @@ dl_status dl_lowrank_kv_append(const void *x, const void *A_k, const void *A_v,
 /* ------------------------------------------------------------------------
  * Decode attention over the low-rank cache -- section 4.2.
  *   q   : [Bsz, n_q, d] un-rotated queries
- *   Ck  : [Bsz, L_max, r_k], Cv: [Bsz, L_max, r_v] latent caches
- *   B_k : [r_k, n_kv*d], B_v: [r_v, n_kv*d] up factors of the k and v pairs
+ *   Ck  : [Bsz, L_max, r_k], Cv: [Bsz, r_v, L_max] latent caches
+ *   B_k : [r_k, n_kv*d], B_v: [r_v, n_kv*d] up factors of the k and v pairs,
+ *         passed transposed ([n_kv*d, r_k], [n_kv*d, r_v])
  *   ctx_lens: device int32 [Bsz], 1 <= ctx_lens[b] <= L_max
  *   out : [Bsz, n_q, d]
  * Sequence b attends rows 0 .. ctx_lens[b]-1 and its query sits at position
- * ctx_lens[b]-1. K and V tiles are rebuilt on chip (never written to memory),
- * keys are rotated by their row index, softmax is computed online.
- * DL_BF16 requires d in {64, 128}, r_k and r_v multiples of 64 and
- * n_q / n_kv <= 16. DL_F32 requires even d <= 256.
+ * ctx_lens[b]-1. Keys are rebuilt on chip (never written to memory) and
+ * rotated by their row index; the value factor is applied once to the
+ * probability-weighted value latents (softmax(s) C_v B_v, the same product
+ * in another association). Softmax is computed online.
+ * DL_BF16 requires d in {64, 128}, r_k and r_v multiples of 64, r_v <= 1024,
+ * L_max % 8 == 0 and n_q / n_kv <= 16. DL_F32 requires even d <= 256.
  * ------------------------------------------------------------------------ */
 size_t dl_attn_decode_workspace(int64_t Bsz, int64_t n_q, int64_t n_kv,
                                 int64_t d, int64_t r_k, int64_t r_v,
@@ -157,8 +169,8 @@ dl_status dl_lowrank_attn_prefill(const void *q, const void *Ck, const void *Cv,
  * x2. Factor shapes follow dl_factor; norm gains may be NULL (= 1).
  * ------------------------------------------------------------------------ */
 typedef struct {
-  const void *A;   /* [m, k] */
-  const void *B;   /* [k, n] */
+  const void *A;   /* A^T, [k, m] */
+  const void *B;   /* B^T, [n, k] */
   int64_t k;
 } dl_factor;
 

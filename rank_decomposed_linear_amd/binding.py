@@ -5,6 +5,11 @@ allocates the caller-side workspace with torch, and calls the C entry point
 of the same name on the current torch stream. All arithmetic runs in the
 library's HIP kernels. If the library is not built or cannot be loaded, the
 functions raise; there is no fallback.
+
+Storage order is the library's (include/dl.h): every factor is passed
+transposed (At = A^T [k, m], Bt = B^T [n, k]; up factors B_k^T, B_v^T
+[n_kv * d, r]), the key cache is [Bsz, L_max, r_k] and the value cache is
+rank-major, [Bsz, r_v, L_max].
 """
 from __future__ import annotations
 
@@ -196,64 +201,68 @@ def _ws(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
 
-def lowrank_linear(x, A, B, y=None, ws=None):
-    """y = (x A) B for x [M, m], A [m, k], B [k, n] (section 2.1, Eq. (1))."""
+def lowrank_linear(x, At, Bt, y=None, ws=None):
+    """y = (x A) B for x [M, m], At = A^T [k, m], Bt = B^T [n, k]
+    (section 2.1, Eq. (1))."""
     lib = load()
     M, m = x.shape
-    k, n = B.shape
+    k, n = At.shape[0], Bt.shape[0]
     dt = _dt(x)
     if y is None:
         y = torch.empty((M, n), dtype=x.dtype, device=x.device)
     need = lib.dl_lowrank_linear_workspace(M, m, k, n, dt)
     ws = ws if ws is not None else _ws(need, x.device)
-    _check(lib.dl_lowrank_linear(_ptr(x), _ptr(A), _ptr(B), _ptr(y), M, m, k, n, dt, _ptr(ws),
+    _check(lib.dl_lowrank_linear(_ptr(x), _ptr(At), _ptr(Bt), _ptr(y), M, m, k, n, dt, _ptr(ws),
                                  ws.numel(), _stream(x.device)))
     return y
 
 
-def lowrank_kv_append(x, A_k, A_v, ck, cv, past_lens, ws=None):
-    """ck[b, past[b]+t] = x[b, t] A_k and cv likewise; x [Bsz, T, m]."""
+def lowrank_kv_append(x, A_kt, A_vt, ck, cv, past_lens, ws=None):
+    """ck[b, past[b]+t, :] = x[b, t] A_k and cv[b, :, past[b]+t] = x[b, t] A_v;
+    x [Bsz, T, m], A_kt [r_k, m], A_vt [r_v, m]."""
     lib = load()
     Bsz, T, m = x.shape
-    r_k, r_v, L_max = A_k.shape[1], A_v.shape[1], ck.shape[1]
+    r_k, r_v, L_max = A_kt.shape[0], A_vt.shape[0], ck.shape[1]
     dt = _dt(x)
     need = lib.dl_kv_append_workspace(Bsz, T, m, r_k, r_v, dt)
     ws = ws if ws is not None else _ws(need, x.device)
-    _check(lib.dl_lowrank_kv_append(_ptr(x), _ptr(A_k), _ptr(A_v), _ptr(ck), _ptr(cv),
+    _check(lib.dl_lowrank_kv_append(_ptr(x), _ptr(A_kt), _ptr(A_vt), _ptr(ck), _ptr(cv),
                                     _ptr(past_lens), Bsz, T, m, r_k, r_v, L_max, dt, _ptr(ws),
                                     ws.numel(), _stream(x.device)))
 
 
-def lowrank_attn_decode(q, ck, cv, B_k, B_v, ctx_lens, n_kv, sm_scale=0.0, rope_theta=0.0,
+def lowrank_attn_decode(q, ck, cv, B_kt, B_vt, ctx_lens, n_kv, sm_scale=0.0, rope_theta=0.0,
                         out=None, ws=None):
-    """q [Bsz, n_q, d] -> out [Bsz, n_q, d] (section 4.2)."""
+    """q [Bsz, n_q, d] -> out [Bsz, n_q, d] (section 4.2); ck [Bsz, L_max, r_k],
+    cv [Bsz, r_v, L_max], B_kt [n_kv * d, r_k], B_vt [n_kv * d, r_v]."""
     lib = load()
     Bsz, n_q, d = q.shape
-    L_max, r_k, r_v = ck.shape[1], ck.shape[2], cv.shape[2]
+    L_max, r_k, r_v = ck.shape[1], ck.shape[2], cv.shape[1]
     dt = _dt(q)
     if out is None:
         out = torch.empty_like(q)
     need = lib.dl_attn_decode_workspace(Bsz, n_q, n_kv, d, r_k, r_v, L_max, dt)
     ws = ws if ws is not None else _ws(need, q.device)
-    _check(lib.dl_lowrank_attn_decode(_ptr(q), _ptr(ck), _ptr(cv), _ptr(B_k), _ptr(B_v),
+    _check(lib.dl_lowrank_attn_decode(_ptr(q), _ptr(ck), _ptr(cv), _ptr(B_kt), _ptr(B_vt),
                                       _ptr(ctx_lens), _ptr(out), Bsz, n_q, n_kv, d, r_k, r_v,
                                       L_max, sm_scale, rope_theta, dt, _ptr(ws), ws.numel(),
                                       _stream(q.device)))
     return out
 
 
-def lowrank_attn_prefill(q, ck, cv, B_k, B_v, past_lens, n_kv, sm_scale=0.0, rope_theta=0.0,
+def lowrank_attn_prefill(q, ck, cv, B_kt, B_vt, past_lens, n_kv, sm_scale=0.0, rope_theta=0.0,
                          out=None, ws=None):
-    """q [Bsz, T, n_q, d] -> out [Bsz, T, n_q, d], causal (section 4.2)."""
+    """q [Bsz, T, n_q, d] -> out [Bsz, T, n_q, d], causal (section 4.2);
+    cache and factor storage as in lowrank_attn_decode."""
     lib = load()
     Bsz, T, n_q, d = q.shape
-    L_max, r_k, r_v = ck.shape[1], ck.shape[2], cv.shape[2]
+    L_max, r_k, r_v = ck.shape[1], ck.shape[2], cv.shape[1]
     dt = _dt(q)
     if out is None:
         out = torch.empty_like(q)
     need = lib.dl_attn_prefill_workspace(Bsz, T, n_q, n_kv, d, r_k, r_v, L_max, dt)
     ws = ws if ws is not None else _ws(need, q.device)
-    _check(lib.dl_lowrank_attn_prefill(_ptr(q), _ptr(ck), _ptr(cv), _ptr(B_k), _ptr(B_v),
+    _check(lib.dl_lowrank_attn_prefill(_ptr(q), _ptr(ck), _ptr(cv), _ptr(B_kt), _ptr(B_vt),
                                        _ptr(past_lens), _ptr(out), Bsz, T, n_q, n_kv, d, r_k, r_v,
                                        L_max, sm_scale, rope_theta, dt, _ptr(ws), ws.numel(),
                                        _stream(q.device)))
@@ -263,8 +272,9 @@ def lowrank_attn_prefill(q, ck, cv, B_k, B_v, past_lens, n_kv, sm_scale=0.0, rop
 class DecomposedLayer:
     """Device-resident factor pairs of one layer plus the dl_layer descriptor.
 
-    factors: dict name -> (A [m, k], B [k, n]) torch tensors on the GPU for
-    q, k, v, o, gate, up, down; norm gains optional."""
+    factors: dict name -> (At [k, m], Bt [n, k]) torch tensors on the GPU
+    (each factor stored transposed) for q, k, v, o, gate, up, down; norm
+    gains optional."""
 
     NAMES = ("q", "k", "v", "o", "gate", "up", "down")
 
@@ -276,8 +286,8 @@ class DecomposedLayer:
         L = Layer()
         L.hidden, L.n_q, L.n_kv, L.head_dim, L.ffn = hidden, n_q, n_kv, head_dim, ffn
         for nm in self.NAMES:
-            A, B = factors[nm]
-            setattr(L, nm, Factor(_ptr(A), _ptr(B), A.shape[1]))
+            At, Bt = factors[nm]
+            setattr(L, nm, Factor(_ptr(At), _ptr(Bt), At.shape[0]))
         L.attn_norm = _ptr(attn_norm)
         L.mlp_norm = _ptr(mlp_norm)
         L.rms_eps = rms_eps
@@ -291,7 +301,8 @@ class DecomposedLayer:
 
     def forward(self, x, ck, cv, past_lens, y=None, x2_out=None, ws=None, stream=None):
         """y = layer(x) for x [Bsz, T, hidden]; appends T latent rows per
-        sequence at past_lens (not advanced)."""
+        sequence at past_lens (not advanced). ck [Bsz, L_max, r_k],
+        cv [Bsz, r_v, L_max]."""
         lib = load()
         Bsz, T, _ = x.shape
         L_max = ck.shape[1]

@@ -139,7 +139,7 @@ struct GvScratch {
   int counters = 0;
   void add(GvArgs &a) {
     part_floats = std::max(part_floats, gemv_plan(a));
-    counters = std::max(counters, a.nstrips);
+    counters = std::max(counters, a.ntiles);
   }
 };
 
@@ -213,39 +213,34 @@ DecodePlan plan_decode(int64_t Bsz, int64_t n_kv, int64_t L_max) {
   return {ns, len};
 }
 
-// Attention scratch: packed up factors (prefill), split partials and
-// merge counters (decode). The counters must be zero before the launch.
+// Attention scratch: split partials and merge counters (decode). The
+// counters must be zero before the launch.
 struct AttnWS {
-  uint16_t *pk = nullptr, *pv = nullptr;
   float *part = nullptr;
   int *counters = nullptr;
   int n_counters = 0;
 };
 
-AttnWS carve_attn(Carver &c, int64_t Bsz, int64_t n_q, int64_t n_kv, int64_t d, int64_t r_k,
-                  int64_t r_v, int64_t L_max, bool decode) {
+AttnWS carve_attn(Carver &c, int64_t Bsz, int64_t n_q, int64_t n_kv, int64_t d, int64_t L_max,
+                  bool decode) {
   AttnWS w;
   if (decode) {
     const DecodePlan p = plan_decode(Bsz, n_kv, L_max);
     w.part = c.take<float>(static_cast<size_t>(Bsz * n_q * p.nsplit * (d + 2)));
     w.n_counters = static_cast<int>(Bsz * n_kv);
     w.counters = c.take<int>(static_cast<size_t>(w.n_counters));
-  } else {
-    w.pk = c.take<uint16_t>(static_cast<size_t>(n_kv * d * r_k));
-    w.pv = c.take<uint16_t>(static_cast<size_t>(n_kv * d * r_v));
   }
   return w;
 }
 
-size_t attn_bf16_ws(int64_t Bsz, int64_t n_q, int64_t n_kv, int64_t d, int64_t r_k, int64_t r_v,
-                    int64_t L_max, bool decode) {
+size_t attn_bf16_ws(int64_t Bsz, int64_t n_q, int64_t n_kv, int64_t d, int64_t L_max, bool decode) {
   Carver c(nullptr);
-  carve_attn(c, Bsz, n_q, n_kv, d, r_k, r_v, L_max, decode);
+  carve_attn(c, Bsz, n_q, n_kv, d, L_max, decode);
   return c.off;
 }
 
 dl_status check_attn_shape(int64_t n_q, int64_t n_kv, int64_t d, int64_t r_k, int64_t r_v,
-                           dl_dtype dt, bool prefill) {
+                           int64_t L_max, dl_dtype dt, bool prefill) {
   DL_CHECK(n_q > 0 && n_kv > 0 && d > 0 && r_k > 0 && r_v > 0, DL_ERR_INVALID_ARG,
            "attention dims must be positive");
   DL_CHECK(n_q % n_kv == 0, DL_ERR_INVALID_ARG, "n_q (%lld) must be a multiple of n_kv (%lld)",
@@ -254,6 +249,12 @@ dl_status check_attn_shape(int64_t n_q, int64_t n_kv, int64_t d, int64_t r_k, in
     DL_CHECK(d == 64 || d == 128, DL_ERR_UNSUPPORTED, "bf16 attention needs head_dim 64 or 128");
     DL_CHECK(r_k % 64 == 0 && r_v % 64 == 0, DL_ERR_UNSUPPORTED,
              "bf16 attention needs r_k, r_v multiples of 64");
+    DL_CHECK(r_v <= attn_decode_max_rank_v(), DL_ERR_UNSUPPORTED,
+             "bf16 attention needs r_v <= %d", attn_decode_max_rank_v());
+    DL_CHECK(L_max % 8 == 0, DL_ERR_UNSUPPORTED,
+             "bf16 attention needs L_max to be a multiple of 8 (16-byte value cache rows)");
+    DL_CHECK(L_max * std::max(r_k, r_v) < ((int64_t)1 << 31), DL_ERR_UNSUPPORTED,
+             "bf16 attention needs L_max * r < 2^31 per sequence");
     const int64_t G = n_q / n_kv;
     DL_CHECK(G <= 16, DL_ERR_UNSUPPORTED, "bf16 attention needs n_q / n_kv <= 16");
     if (prefill)
@@ -301,18 +302,14 @@ hipError_t run_attn_bf16(const void *q, int q_f32, int ldq, const void *Ck, cons
     a.theta = theta;
     return launch_attn_decode_bf16(a, s);
   }
-  hipError_t e = launch_pack_up_factor(static_cast<const uint16_t *>(B_k), w.pk, r_k, n_kv, d, s);
-  if (e != hipSuccess) return e;
-  e = launch_pack_up_factor(static_cast<const uint16_t *>(B_v), w.pv, r_v, n_kv, d, s);
-  if (e != hipSuccess) return e;
   AttnPrefillArgs a{};
   a.q = q;
   a.q_f32 = q_f32;
   a.ldq = ldq;
   a.ck = static_cast<const uint16_t *>(Ck);
   a.cv = static_cast<const uint16_t *>(Cv);
-  a.bk_packed = w.pk;
-  a.bv_packed = w.pv;
+  a.bk = static_cast<const uint16_t *>(B_k);
+  a.bv = static_cast<const uint16_t *>(B_v);
   a.past_lens = lens;
   a.out = static_cast<uint16_t *>(out);
   a.Bsz = Bsz;
@@ -463,7 +460,7 @@ static GvArgs append_gemv(int M, int m, int rk, int rv, int T, int L_max, const 
   a.T = T;
   a.L_max = L_max;
   a.seg[0] = gvseg(A_k, x, m, Ck, rk, rk, GV_OUT_CACHE);
-  a.seg[1] = gvseg(A_v, x, m, Cv, rv, rv, GV_OUT_CACHE);
+  a.seg[1] = gvseg(A_v, x, m, Cv, rv, rv, GV_OUT_CACHE_T);
   return a;
 }
 
@@ -512,7 +509,7 @@ dl_status dl_lowrank_kv_append(const void *x, const void *A_k, const void *A_v, 
     DL_HIP(gemm_f32(static_cast<const float *>(x), nullptr, A_k, static_cast<float *>(Ck), M, rk,
                     mi, mi, rk, F32_OUT_CACHE, nullptr, 0, past_lens, Ti, Lm, s));
     DL_HIP(gemm_f32(static_cast<const float *>(x), nullptr, A_v, static_cast<float *>(Cv), M, rv,
-                    mi, mi, rv, F32_OUT_CACHE, nullptr, 0, past_lens, Ti, Lm, s));
+                    mi, mi, rv, F32_OUT_CACHE_T, nullptr, 0, past_lens, Ti, Lm, s));
     return DL_OK;
   }
   if (use_gemv(M)) {
@@ -528,7 +525,7 @@ dl_status dl_lowrank_kv_append(const void *x, const void *A_k, const void *A_v, 
     return DL_OK;
   }
   GemmArgs a{};
-  a.nseg = 2;
+  a.nseg = 1;
   a.M = M;
   a.K = mi;
   a.xmode = GEMM_X_BF16;
@@ -537,7 +534,9 @@ dl_status dl_lowrank_kv_append(const void *x, const void *A_k, const void *A_v, 
   a.T = Ti;
   a.L_max = Lm;
   a.seg[0] = mseg(A_k, x, Ck, rk, mi, rk);
-  a.seg[1] = mseg(A_v, x, Cv, rv, mi, rv);
+  DL_HIP(gemm(a, s));
+  a.omode = GEMM_OUT_CACHE_T;
+  a.seg[0] = mseg(A_v, x, Cv, rv, mi, rv);
   DL_HIP(gemm(a, s));
   return DL_OK;
 }
@@ -548,14 +547,18 @@ dl_status dl_lowrank_kv_append(const void *x, const void *A_k, const void *A_v, 
 size_t dl_attn_decode_workspace(int64_t Bsz, int64_t n_q, int64_t n_kv, int64_t d, int64_t r_k,
                                 int64_t r_v, int64_t L_max, dl_dtype dt) {
   if (dt != DL_BF16 || Bsz <= 0 || n_kv <= 0 || L_max <= 0) return 0;
-  return attn_bf16_ws(Bsz, n_q, n_kv, d, r_k, r_v, L_max, true);
+  (void)r_k;
+  (void)r_v;
+  return attn_bf16_ws(Bsz, n_q, n_kv, d, L_max, true);
 }
 
 size_t dl_attn_prefill_workspace(int64_t Bsz, int64_t T, int64_t n_q, int64_t n_kv, int64_t d,
                                  int64_t r_k, int64_t r_v, int64_t L_max, dl_dtype dt) {
   (void)T;
   if (dt != DL_BF16 || Bsz <= 0 || n_kv <= 0 || L_max <= 0) return 0;
-  return attn_bf16_ws(Bsz, n_q, n_kv, d, r_k, r_v, L_max, false);
+  (void)r_k;
+  (void)r_v;
+  return attn_bf16_ws(Bsz, n_q, n_kv, d, L_max, false);
 }
 
 static dl_status attn_common(const void *q, const void *Ck, const void *Cv, const void *B_k,
@@ -568,7 +571,7 @@ static dl_status attn_common(const void *q, const void *Ck, const void *Cv, cons
   DL_CHECK(q && Ck && Cv && B_k && B_v && lens && out, DL_ERR_INVALID_ARG, "null pointer");
   DL_CHECK(Bsz > 0 && T > 0 && L_max > 0, DL_ERR_INVALID_ARG, "dims must be positive");
   DL_CHECK(T <= L_max, DL_ERR_INVALID_ARG, "T exceeds L_max");
-  dl_status st = check_attn_shape(n_q, n_kv, d, r_k, r_v, dt, !decode);
+  dl_status st = check_attn_shape(n_q, n_kv, d, r_k, r_v, L_max, dt, !decode);
   if (st != DL_OK) return st;
   DL_CHECK(Bsz * L_max * std::max(r_k, r_v) <= ((int64_t)1 << 40) && Bsz * T * n_q * d <= INT32_MAX &&
                L_max <= INT32_MAX / 2,
@@ -608,7 +611,7 @@ static dl_status attn_common(const void *q, const void *Ck, const void *Cv, cons
     return DL_OK;
   }
   Carver c(ws);
-  const AttnWS aw = carve_attn(c, Bsz, n_q, n_kv, d, r_k, r_v, L_max, decode);
+  const AttnWS aw = carve_attn(c, Bsz, n_q, n_kv, d, L_max, decode);
   if (aw.counters) {
     FillRegion z[1] = {{reinterpret_cast<float *>(aw.counters), nullptr, 0, aw.n_counters}};
     DL_HIP(launch_fill(z, 1, s));
@@ -655,7 +658,7 @@ static dl_status layer_dims(const dl_layer *L, int64_t Bsz, int64_t T, int64_t L
     DL_CHECK(f->A && f->B, DL_ERR_INVALID_ARG, "null factor pointer");
     DL_CHECK(f->k > 0, DL_ERR_INVALID_ARG, "factor rank must be positive");
   }
-  dl_status st = check_attn_shape(L->n_q, L->n_kv, L->head_dim, L->k.k, L->v.k, L->dt, T > 1);
+  dl_status st = check_attn_shape(L->n_q, L->n_kv, L->head_dim, L->k.k, L->v.k, L_max, L->dt, T > 1);
   if (st != DL_OK) return st;
   if (L->dt == DL_BF16) {
     bool ok = L->hidden % 64 == 0 && L->ffn % 64 == 0;
@@ -726,7 +729,7 @@ static void layer_gemvs(const dl_layer *L, const LayerDims &D, const LayerWS &w,
   g[G_QKV].L_max = D.L_max;
   g[G_QKV].seg[0] = gvseg(L->q.A, x, h, w.tq16, D.rq, D.rq, GV_OUT_BF16);
   g[G_QKV].seg[1] = gvseg(L->k.A, x, h, Ck, D.rk, D.rk, GV_OUT_CACHE);
-  g[G_QKV].seg[2] = gvseg(L->v.A, x, h, Cv, D.rv, D.rv, GV_OUT_CACHE);
+  g[G_QKV].seg[2] = gvseg(L->v.A, x, h, Cv, D.rv, D.rv, GV_OUT_CACHE_T);
 
   g[G_QUP] = gvargs(M, D.rq, 1);
   g[G_QUP].seg[0] = gvseg(L->q.B, w.tq16, D.rq, w.q32, qd, qd, GV_OUT_F32);
@@ -823,7 +826,7 @@ size_t dl_layer_workspace(const dl_layer *L, int64_t Bsz, int64_t T, int64_t L_m
   LayerWS w{};
   carve_layer(c, D, L, w);
   if (L->dt == DL_BF16)
-    c.off += attn_bf16_ws(D.Bsz, D.nq, D.nkv, D.d, D.rk, D.rv, D.L_max, D.T == 1) + kAlign;
+    c.off += attn_bf16_ws(D.Bsz, D.nq, D.nkv, D.d, D.L_max, D.T == 1) + kAlign;
   return c.off;
 }
 
@@ -851,7 +854,7 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
   LayerWS w{};
   carve_layer(c, D, L, w);
   AttnWS aw;
-  if (L->dt == DL_BF16) aw = carve_attn(c, D.Bsz, D.nq, D.nkv, D.d, D.rk, D.rv, D.L_max, D.T == 1);
+  if (L->dt == DL_BF16) aw = carve_attn(c, D.Bsz, D.nq, D.nkv, D.d, D.L_max, D.T == 1);
   const int M = D.M, h = D.h, qd = D.qd();
   const float eps = L->rms_eps;
   const int gf32 = L->dt == DL_F32;
@@ -864,7 +867,7 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
     DL_HIP(gemm_f32(w.a, nullptr, L->k.A, static_cast<float *>(Ck), M, D.rk, h, h, D.rk,
                     F32_OUT_CACHE, nullptr, 0, past_lens, D.T, D.L_max, s));
     DL_HIP(gemm_f32(w.a, nullptr, L->v.A, static_cast<float *>(Cv), M, D.rv, h, h, D.rv,
-                    F32_OUT_CACHE, nullptr, 0, past_lens, D.T, D.L_max, s));
+                    F32_OUT_CACHE_T, nullptr, 0, past_lens, D.T, D.L_max, s));
     set_role(R_QKV_DOWN);
     DL_HIP(gemm_f32(w.a, nullptr, L->q.A, w.tq, M, D.rq, h, h, D.rq, F32_OUT_STORE, nullptr, 0,
                     nullptr, 1, 0, s));
@@ -964,7 +967,7 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
     set_role(R_QKV_DOWN);
     DL_HIP(gemm(a, s));
     GemmArgs b{};
-    b.nseg = 2;
+    b.nseg = 1;
     b.M = M;
     b.K = h;
     b.omode = GEMM_OUT_CACHE;
@@ -972,7 +975,9 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
     b.T = D.T;
     b.L_max = D.L_max;
     b.seg[0] = mseg(L->k.A, w.a16, Ck, D.rk, h, D.rk);
-    b.seg[1] = mseg(L->v.A, w.a16, Cv, D.rv, h, D.rv);
+    DL_HIP(gemm(b, s));
+    b.omode = GEMM_OUT_CACHE_T;
+    b.seg[0] = mseg(L->v.A, w.a16, Cv, D.rv, h, D.rv);
     DL_HIP(gemm(b, s));
     GemmArgs q{};
     q.nseg = 1;

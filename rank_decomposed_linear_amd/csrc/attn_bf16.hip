@@ -2,10 +2,11 @@
 // rebuild K = C_k B_k and V = C_v B_v from the cached latents, rotate the
 // rebuilt keys, attend).
 //
-// Neither K nor V is ever written to memory. The cache is streamed from HBM
-// with 16-byte loads, the up factors B_k / B_v are read in a pre-packed
-// MFMA-operand order (one 16-byte load per lane per fragment), and the
-// rebuilt tiles live in MFMA accumulators:
+// Neither K nor V is ever written to memory. The key cache is streamed from
+// HBM with 16-byte loads; the value cache is stored rank-major ([Bsz, r_v,
+// L_max]) and gathered per key. The up factors are stored transposed,
+// [n_kv * d, r] (rank contiguous), so an MFMA operand fragment is one
+// 16-byte load per lane. The rebuilt tiles live in MFMA accumulators:
 //
 //  prefill  A workgroup owns one kv head and up to 256 (token, head) query
 //           rows; per 64-key tile its eight waves rebuild K (rotated) and
@@ -21,36 +22,13 @@ namespace dl {
 
 namespace {
 
-// ---------------------------------------------------------------------------
-// Up-factor packing: packed[g][rs][blk][lane][e] = B[32rs + 8(lane/16) + e][g*d + 16blk + lane%16]
-// ---------------------------------------------------------------------------
-__global__ void pack_up_factor_kernel(const uint16_t *__restrict__ B, uint16_t *__restrict__ P,
-                                      int r, int n_kv, int d) {
-  const int64_t total = static_cast<int64_t>(n_kv) * (r / 32) * (d / 16) * 64;
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= total) return;
-  const int lane = static_cast<int>(idx & 63);
-  int64_t rest = idx >> 6;
-  const int nblk = d / 16;
-  const int blk = static_cast<int>(rest % nblk);
-  rest /= nblk;
-  const int rsteps = r / 32;
-  const int rs = static_cast<int>(rest % rsteps);
-  const int g = static_cast<int>(rest / rsteps);
-  const int col = g * d + 16 * blk + (lane & 15);
-  const int row0 = 32 * rs + 8 * (lane >> 4);
-  const int64_t ld = static_cast<int64_t>(n_kv) * d;
-  uint32_t w[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t lo = B[(row0 + 2 * q) * ld + col];
-    const uint32_t hi = B[(row0 + 2 * q + 1) * ld + col];
-    w[q] = lo | (hi << 16);
-  }
-  *reinterpret_cast<u32x4 *>(P + idx * 8) = u32x4{w[0], w[1], w[2], w[3]};
-}
-
 __device__ __forceinline__ u32x4 ld16(const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
+
+// operand fragment (rank step rs, d block blk) of an up factor stored
+// [n_kv * d, r]: lane (c, grp) gets B[32rs + 8grp .. +8][16blk + c]
+__device__ __forceinline__ u32x4 frag(const uint16_t *bt_g, int r, int rs, int blk, int lane) {
+  return ld16(bt_g + static_cast<size_t>(16 * blk + (lane & 15)) * r + 32 * rs + 8 * (lane >> 4));
+}
 
 // ---------------------------------------------------------------------------
 // Prefill
@@ -137,8 +115,9 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
   const int qmax_pos = past + min(t0 + QT, a.T) - 1;
   const int nkt = qmax_pos / KT + 1;
   const int rsk = a.r_k / 32, rsv = a.r_v / 32;
-  const uint16_t *pk = a.bk_packed + static_cast<size_t>(g) * rsk * DB * 512 + lane * 8;
-  const uint16_t *pv = a.bv_packed + static_cast<size_t>(g) * rsv * DB * 512 + lane * 8;
+  const uint16_t *bk_g = a.bk + static_cast<size_t>(g) * D * a.r_k;
+  const uint16_t *bv_g = a.bv + static_cast<size_t>(g) * D * a.r_v;
+  const uint16_t *cv_b = a.cv + static_cast<size_t>(b) * a.r_v * a.L_max;
   const int kb = wave >> 1;  // key block rebuilt by this wave
 
   for (int kt = 0; kt < nkt; ++kt) {
@@ -155,11 +134,10 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
       const uint16_t *cp = a.ck + (static_cast<size_t>(b) * a.L_max + keyrow) * a.r_k + 8 * grp;
       for (int rs = 0; rs < rsk; ++rs) {
         const u32x4 c = kvalid ? ld16(cp + rs * 32) : u32x4{0u, 0u, 0u, 0u};
-        const uint16_t *fp = pk + static_cast<size_t>(rs) * DB * 512;
 #pragma unroll
         for (int xi = 0; xi < NX; ++xi) {
-          acc[xi][0] = mfma_bf16(ld16(fp + (xbase + xi) * 512), c, acc[xi][0]);
-          acc[xi][1] = mfma_bf16(ld16(fp + (xbase + xi + HALF) * 512), c, acc[xi][1]);
+          acc[xi][0] = mfma_bf16(frag(bk_g, a.r_k, rs, xbase + xi, lane), c, acc[xi][0]);
+          acc[xi][1] = mfma_bf16(frag(bk_g, a.r_k, rs, xbase + xi + HALF, lane), c, acc[xi][1]);
         }
       }
       // lane (key = j, grp) holds K^T[16blk + 4grp + r][keyrow]
@@ -192,12 +170,19 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
 #pragma unroll
       for (int x = 0; x < HALF; ++x) acc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int nb0 = (wave & 1) * HALF;
-      const uint16_t *cp = a.cv + (static_cast<size_t>(b) * a.L_max + keyrow) * a.r_v + 8 * grp;
+      // C_v[keyrow][32rs + 8grp + e], e = 0..7, gathered from the rank-major cache
+      const uint16_t *cp = cv_b + static_cast<size_t>(8 * grp) * a.L_max + min(keyrow, a.L_max - 1);
       for (int rs = 0; rs < rsv; ++rs) {
-        const u32x4 c = kvalid ? ld16(cp + rs * 32) : u32x4{0u, 0u, 0u, 0u};
-        const uint16_t *fp = pv + static_cast<size_t>(rs) * DB * 512;
+        u32x4 c = {0u, 0u, 0u, 0u};
+        if (kvalid) {
+          const uint16_t *p = cp + static_cast<size_t>(32 * rs) * a.L_max;
 #pragma unroll
-        for (int x = 0; x < HALF; ++x) acc[x] = mfma_bf16(c, ld16(fp + (nb0 + x) * 512), acc[x]);
+          for (int q = 0; q < 4; ++q)
+            c[q] = static_cast<uint32_t>(p[static_cast<size_t>(2 * q) * a.L_max]) |
+                   (static_cast<uint32_t>(p[static_cast<size_t>(2 * q + 1) * a.L_max]) << 16);
+        }
+#pragma unroll
+        for (int x = 0; x < HALF; ++x) acc[x] = mfma_bf16(c, frag(bv_g, a.r_v, rs, nb0 + x, lane), acc[x]);
       }
       // lane (d = j, grp) holds V[16kb + 4grp + r][16(nb0+x) + j]
 #pragma unroll
@@ -287,16 +272,6 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
 }
 
 }  // namespace
-
-hipError_t launch_pack_up_factor(const uint16_t *B, uint16_t *packed, int r, int n_kv, int d,
-                                 hipStream_t s) {
-  TraceGuard trace_guard(K_PACK_UP, s);
-  const int64_t total = static_cast<int64_t>(n_kv) * (r / 32) * (d / 16) * 64;
-  const int threads = 256;
-  pack_up_factor_kernel<<<static_cast<unsigned>((total + threads - 1) / threads), threads, 0, s>>>(
-      B, packed, r, n_kv, d);
-  return hipGetLastError();
-}
 
 hipError_t launch_attn_prefill_bf16(const AttnPrefillArgs &a, hipStream_t s) {
   TraceGuard trace_guard(K_ATTN_PREFILL, s);

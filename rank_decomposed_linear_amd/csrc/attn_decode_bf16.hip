@@ -2,31 +2,46 @@
 // 4.2: rebuild K = C_k B_k and V = C_v B_v from the cached latents, rotate
 // the rebuilt keys, attend). One query token per sequence.
 //
-// Work item = (sequence b, kv head g, context split). A workgroup of eight
-// waves walks its split in iterations of 256 positions, 32 per wave:
+// The value side is never rebuilt: softmax(s) V = (softmax(s) C_v) B_v
+// (associativity of the product; only the rounding order changes), so the
+// probabilities are applied to the r_v-wide latents and the result is
+// multiplied by B_v once per work item. The keys must be rebuilt per
+// position because the rotary embedding acts on them after B_k.
 //
-//  * The up factors are read straight from their row-major [r, n_kv*d]
-//    layout. Per pair of 32-rank steps 256 of the threads cooperatively load
-//    B[32rs + 8grp + s][g*d + (d/2)hh + (d/32)c + 0..] (s = 0..7), transpose
-//    each 8-row block in registers into MFMA operand fragments and store
-//    them in LDS (double buffered); every wave then reads its operands with
-//    one 16-byte ds_read each. Operand e of column group hh holds columns
-//    d(blk, row) = (d/2)hh + (d/32)row + e, so the rotary partners d and
-//    d + d/2 (hh = 0 and 1) land in the same lane and register.
-//  * A wave rebuilds K^T for its 32 positions (accumulator column =
-//    position), 2 MFMAs per operand fragment, rotates the pairs in
-//    registers, feeds the accumulators straight into S^T = K Q^T (the
-//    reduction slots of an operand may be any permutation shared by both
-//    operands), updates an online softmax, rebuilds V for the same
-//    positions and accumulates O^T += V^T P^T. Neither K nor V touches
-//    memory.
+// Work item = (sequence b, kv head g, context split), one workgroup of four
+// waves (one per SIMD, so each wave has the whole register file for deep
+// software pipelining). Per work item:
+//  * B_k^T rows of head g (stored [n_kv * d, r_k], the rank contiguous) are
+//    loaded once into LDS in MFMA operand order, fragment (rank step rs,
+//    d block x) = 64 lanes x 16 bytes. Operand row i of block x holds
+//    dimension dim(x, i) = (d/2)(x / NE) + (d/32) i + x % NE, so the rotary
+//    partners d and d + d/2 land in the same lane and register. (Ranks too
+//    large for LDS are staged in rank chunks, reloaded per context slice.)
+//  * LDS is sized per launch: the resident factor first, then as long a
+//    context chunk as the rest of the 160 KB holds (scores and
+//    probabilities need 4 G + 32 bytes per position), so a split is
+//    normally walked in one chunk:
+//    phase 1: each wave rebuilds K^T for 64-position slices (A = factor
+//      fragment from LDS, read one rank step ahead; B = cache rows
+//      C_k[pos][32rs + 8g ..], one 16-byte load per lane and 16-position
+//      block, eight rank steps ahead), rotates the pairs in registers and
+//      forms S^T = K Q^T straight from the accumulators (the reduction slots
+//      of an operand may be any permutation shared by both operands).
+//      Scores go to LDS. Position of column j of block pb is
+//      32(pb/2) + 8(j/4) + 4(pb%2) + j%4, chosen so that the probabilities
+//      of 8 consecutive positions end up in one operand register set.
+//    softmax: chunk max per head, probabilities in bf16 operand order in
+//      LDS, running max / sum, rescale factor.
+//    phase 2: U^T[r][h] += C_v^T[r][pos] P^T[pos][h] with the value cache
+//      stored rank-major ([Bsz, r_v, L_max]), so every A operand is one
+//      16-byte load of 8 consecutive positions; each wave owns a set of
+//      16-row rank blocks. The loads start before the softmax barrier.
+//  * O^T = B_v^T U^T on MFMA (U rounded to bf16), then the split's partial
+//    (O, max, sum) is merged by the last workgroup of (b, g) to finish
+//    (device-coherent partials, one counter atomic per workgroup).
 //  * Rotary angles: the turn fraction pos * w_i / (2 pi) is split into a
-//    per-iteration base reduced exactly in float64 and a small float32
-//    offset, so float32 sin/cos see an argument in [-pi, pi] at any
-//    position.
-//  * The eight waves merge in LDS; splits are merged by the last workgroup
-//    of each (b, g) to finish (device-coherent partials, one counter
-//    atomic per workgroup), which writes the output row.
+//    per-slice base reduced exactly in float64 and a small float32 offset,
+//    so float32 sin/cos see an argument in [-pi, pi] at any position.
 #include <math.h>
 
 #include "common.h"
@@ -60,85 +75,56 @@ __device__ __forceinline__ void turn_cs(float t, float &c, float &s) {
   __sincosf(t * 6.283185307179586f, &s, &c);
 }
 
-constexpr int kDecodeWaves = 8;
-constexpr int kDecodeThreads = 64 * kDecodeWaves;
+// zero the bf16 elements e >= nv of an 8-element operand
+__device__ __forceinline__ u32x4 keep_first(u32x4 v, int nv) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t m = (2 * q < nv ? 0x0000ffffu : 0u) | (2 * q + 1 < nv ? 0xffff0000u : 0u);
+    v[q] &= m;
+  }
+  return v;
+}
+
+constexpr int kNW = 4;                  // waves per workgroup
+constexpr int kThreads = 64 * kNW;
+constexpr int kSlice = 64;              // positions per wave slice in phase 1
+constexpr int kNP = kSlice / 16;        // 16-position blocks per slice
+constexpr int kMaxPitch = 2048;         // positions per softmax chunk (at most)
+constexpr int kCDepth = 8;              // cache-row prefetch depth (rank steps)
+constexpr int kVDepth = 4;              // value-row prefetch depth (32-position groups)
 
 template <int D>
-struct DecodeTile {
+struct Tile {
   static constexpr int CPL = D / 32;   // columns per lane per column group
   static constexpr int NE = CPL;       // operands per column group
   static constexpr int NB = 2 * NE;    // 16-wide d blocks
   static constexpr int HALF = D / 2;
-  // dimension index of row `row` (0..15) of block blk
   __device__ static constexpr int dim(int blk, int row) {
     return HALF * (blk / NE) + CPL * row + (blk % NE);
   }
 };
 
-// Cooperative load of two 32-rank steps of an up factor for kv head g:
-// thread t handles rows 32(2 round + t/128) + 8 grp + s, columns
-// g*D + HALF*hh + CPL*c .. +CPL-1.
-template <int D>
-struct FactorStage {
-  uint32_t w[8][D / 64];   // 8 rows x CPL bf16 columns
-};
-
-template <int D>
-__device__ __forceinline__ void factor_load(FactorStage<D> &st, const uint16_t *B, int ldb, int g,
-                                            int round, int tid) {
-  using T = DecodeTile<D>;
-  const int rsl = tid >> 7, grp = (tid >> 5) & 3, hh = (tid >> 4) & 1, c = tid & 15;
-  const int row0 = 32 * (2 * round + rsl) + 8 * grp;
-  const uint16_t *p = B + static_cast<size_t>(row0) * ldb + g * D + T::HALF * hh + T::CPL * c;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    if constexpr (D == 128) {
-      const u32x2 v = *reinterpret_cast<const u32x2 *>(p + static_cast<size_t>(s) * ldb);
-      st.w[s][0] = v.x;
-      st.w[s][1] = v.y;
-    } else {
-      st.w[s][0] = *reinterpret_cast<const uint32_t *>(p + static_cast<size_t>(s) * ldb);
-    }
-  }
+// offset of column j of 16-position block pb within a 64-position slice
+__device__ __forceinline__ int slice_pos(int pb, int j) {
+  return 32 * (pb >> 1) + 8 * (j >> 2) + 4 * (pb & 1) + (j & 3);
 }
 
-// transpose to operand fragments and store: bs[rsl][blk][lane][8]
-template <int D>
-__device__ __forceinline__ void factor_store(const FactorStage<D> &st, uint16_t *bs, int tid) {
-  using T = DecodeTile<D>;
-  const int rsl = tid >> 7, grp = (tid >> 5) & 3, hh = (tid >> 4) & 1, c = tid & 15;
-  const int lane = 16 * grp + c;
-#pragma unroll
-  for (int e = 0; e < T::NE; ++e) {
-    u32x4 o;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t lo = st.w[2 * q][e >> 1], hi = st.w[2 * q + 1][e >> 1];
-      o[q] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-    }
-    const int blk = T::NE * hh + e;
-    *reinterpret_cast<u32x4 *>(bs + ((rsl * T::NB + blk) * 64 + lane) * 8) = o;
-  }
-}
-
-template <int D>
-__global__ __launch_bounds__(kDecodeThreads, 1) void attn_decode_kernel(AttnDecodeArgs a) {
-  using T = DecodeTile<D>;
+template <int D, int RBW>
+__global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs a) {
+  using T = Tile<D>;
   constexpr int NB = T::NB, NE = T::NE, HALF = T::HALF;
-  constexpr int PT = 32;         // positions per wave and iteration
-  constexpr int NP = PT / 16;    // 16-position blocks per wave
-  constexpr int NW = kDecodeWaves;
-  constexpr int WT = NW * PT;    // positions per workgroup iteration
-  constexpr int BS_ELEMS = 2 * 2 * NB * 64 * 8;  // [buf][rsl][blk][lane][8] bf16
-  constexpr int MRG_FLOATS = NW * 16 * D;        // [wave][head][d] merge buffer
-  __shared__ __attribute__((aligned(16))) float smem[MRG_FLOATS > BS_ELEMS / 2 ? MRG_FLOATS : BS_ELEMS / 2];
-  uint16_t *bs = reinterpret_cast<uint16_t *>(smem);
-  __shared__ __attribute__((aligned(16))) uint16_t qs[16 * D];
+  constexpr int OBW = NB / kNW;          // output d blocks per wave
+  // dynamic LDS: factor fragments [rs_cap][NB][64][8] bf16, scores
+  // [G][pitch] f32, probabilities [pitch / 32][64] operand words
+  extern __shared__ __attribute__((aligned(16))) char dlds[];
+  uint16_t *bs = reinterpret_cast<uint16_t *>(dlds);
+  float *sS = reinterpret_cast<float *>(dlds + a.lds_bs);
+  u32x4 *pbuf = reinterpret_cast<u32x4 *>(dlds + a.lds_bs + a.lds_s);
   __shared__ __attribute__((aligned(16))) u32x4 qfs[NB / 2][64];   // score operands, lane order
   __shared__ double rev64[HALF];
   __shared__ float rev32[HALF];
-  __shared__ float mrg_m[NW][16], mrg_l[NW][16];
-  __shared__ float cmb_m[16], cmb_l[16];
+  __shared__ float smax[kNW][16], psw[kNW][16];
+  __shared__ float mfin[16], lfin[16], cmb_m[16], cmb_l[16];
   __shared__ int last_flag;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -156,295 +142,325 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void attn_decode_kernel(AttnDeco
   const int p_begin = split * a.split_len;
   const int p_end = min(p_begin + a.split_len, ctx);
   const bool rope_on = a.theta != 0.f;
-  const int ldb = a.n_kv * D;
+  const int nrs = a.r_k / 32;
+  const int rs_cap = a.rs_cap;
+  const int n_rchunks = (nrs + rs_cap - 1) / rs_cap;
+  const int nrb = a.r_v / 16;
+  const int pitch = a.pitch;   // positions per chunk, a multiple of the slice
+  const uint16_t *bk_g = a.bk + static_cast<size_t>(g) * D * a.r_k;
+  const uint16_t *cv_b = a.cv + static_cast<size_t>(b) * a.r_v * a.L_max;
+  const uint16_t *ck_b = a.ck + static_cast<size_t>(b) * a.L_max * a.r_k;
 
-  for (int i = tid; i < HALF; i += kDecodeThreads) {
+  // up-factor fragments of rank steps [rs0, rs0 + cnt) -> bs[rs - rs0][x][lane][8]
+  auto factor_src = [&](int rs0, int u) {
+    const int ln = u & 63, x = (u >> 6) % NB, rs = (u >> 6) / NB;
+    return bk_g + static_cast<size_t>(T::dim(x, ln & 15)) * a.r_k + 32 * (rs0 + rs) + 8 * (ln >> 4);
+  };
+  auto load_factor = [&](int rs0, int cnt) {
+    const int units = cnt * NB * 64;
+    for (int u = tid; u < units; u += kThreads)
+      *reinterpret_cast<u32x4 *>(bs + static_cast<size_t>(u) * 8) = ld16(factor_src(rs0, u));
+  };
+
+  for (int i = tid; i < HALF; i += kThreads) {
     rev64[i] = rope_on ? rope_rev(i, D, a.theta) : 0.0;
     rev32[i] = static_cast<float>(rev64[i]);
   }
-  __syncthreads();
-  // rotated, scaled queries of this kv head's G heads; rows >= G are zero
-  for (int idx = tid; idx < 16 * HALF; idx += kDecodeThreads) {
-    const int hl = idx / HALF, i = idx % HALF;
-    float x = 0.f, y = 0.f;
-    if (hl < G) {
-      const size_t off = (static_cast<size_t>(b) * a.n_q + g * G + hl) * D;
-      if (a.q_f32) {
-        x = static_cast<const float *>(a.q)[off + i];
-        y = static_cast<const float *>(a.q)[off + i + HALF];
-      } else {
-        x = bf2f(static_cast<const uint16_t *>(a.q)[off + i]);
-        y = bf2f(static_cast<const uint16_t *>(a.q)[off + i + HALF]);
-      }
-      if (rope_on) {
-        float c, s;
-        rope_cs(qpos, rev64[i], c, s);
-        const float x2 = x * c - y * s;
-        y = x * s + y * c;
-        x = x2;
-      }
-    }
-    qs[hl * D + i] = f2bf(x * a.scale_log2);
-    qs[hl * D + i + HALF] = f2bf(y * a.scale_log2);
-  }
-  __syncthreads();
-  // score B operand: lane (head j, grp) slots 0..3 = q[j][dim(2t, 4grp+r)],
-  // slots 4..7 = q[j][dim(2t+1, 4grp+r)]
-  if (wave == 0) {
+  if (n_rchunks == 1) {
+    // resident factor: batches of 32 loads in flight before their LDS stores
+    constexpr int kPer = 32;
+    const int units = nrs * NB * 64;
+    for (int u0 = 0; u0 < units; u0 += kPer * kThreads) {
+      u32x4 v[kPer];
 #pragma unroll
-    for (int t = 0; t < NB / 2; ++t) {
-      uint16_t v[8];
+      for (int k = 0; k < kPer; ++k) v[k] = ld16(factor_src(0, min(u0 + tid + kThreads * k, units - 1)));
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        v[r] = qs[j * D + T::dim(2 * t, 4 * grp + r)];
-        v[4 + r] = qs[j * D + T::dim(2 * t + 1, 4 * grp + r)];
-      }
-      u32x4 f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        f[q] = static_cast<uint32_t>(v[2 * q]) | (static_cast<uint32_t>(v[2 * q + 1]) << 16);
-      qfs[t][lane] = f;
+      for (int k = 0; k < kPer; ++k)
+        if (u0 + tid + kThreads * k < units)
+          *reinterpret_cast<u32x4 *>(bs + static_cast<size_t>(u0 + tid + kThreads * k) * 8) = v[k];
     }
   }
   __syncthreads();
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 accO[NB];
+  // rotated, scaled queries of this kv head's G heads (rows >= G are zero),
+  // packed as score B operands: lane (head j, grp) slots 0..3 =
+  // q[j][dim(2t, 4grp+r)], slots 4..7 = q[j][dim(2t+1, 4grp+r)]; one
+  // (t, lane) entry per thread
+  for (int idx = tid; idx < (NB / 2) * 64; idx += kThreads) {
+    const int t = idx >> 6, ln = idx & 63, hj = ln & 15, gq = ln >> 4;
+    float v[8];
 #pragma unroll
-  for (int x = 0; x < NB; ++x) accO[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 acc[NB][NP];
-
-  const size_t seq_row = static_cast<size_t>(b) * a.L_max;
-  for (int T0 = p_begin; T0 < p_end; T0 += WT) {
-    const int P0 = T0 + wave * PT;
-    const bool active = P0 < p_end;
-    const int last = p_end - 1;
-
-    // ---------------- K^T[d, pos] = B_k^T C_k^T for the wave's positions ----------------
-#pragma unroll
-    for (int x = 0; x < NB; ++x)
-#pragma unroll
-      for (int pb = 0; pb < NP; ++pb) acc[x][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    {
-      // One round = two 32-rank steps. The factor fragments and the cache
-      // rows of round r + 1 are loaded while round r computes; loads past
-      // the last round repeat it (unconditional loads keep the wait counts
-      // exact; the extra stage lands in the buffer nobody reads).
-      const int nrounds = a.r_k / 64;
-      const uint16_t *cbase = a.ck + seq_row * a.r_k + 8 * grp;
-      int crow[NP];
-#pragma unroll
-      for (int pb = 0; pb < NP; ++pb) crow[pb] = min(P0 + 16 * pb + j, last) * a.r_k;
-      auto load_rows = [&](u32x4 (&cf)[2][NP], int round) {
-#pragma unroll
-        for (int r2 = 0; r2 < 2; ++r2)
-#pragma unroll
-          for (int pb = 0; pb < NP; ++pb) cf[r2][pb] = ld16(cbase + crow[pb] + (2 * round + r2) * 32);
-      };
-      FactorStage<D> st;
-      u32x4 cf[2][NP], cfn[2][NP];
-      const bool loader = tid < 256;
-      if (loader) factor_load<D>(st, a.bk, ldb, g, 0, tid);
-      load_rows(cfn, 0);
-      if (loader) factor_store<D>(st, bs, tid);
-      __syncthreads();
-      for (int round = 0; round < nrounds; ++round) {
-        const int buf = round & 1;
-#pragma unroll
-        for (int r2 = 0; r2 < 2; ++r2)
-#pragma unroll
-          for (int pb = 0; pb < NP; ++pb) cf[r2][pb] = cfn[r2][pb];
-        const int nxt = min(round + 1, nrounds - 1);
-        if (loader) factor_load<D>(st, a.bk, ldb, g, nxt, tid);
-        load_rows(cfn, nxt);
-        if (active) {
-#pragma unroll
-          for (int r2 = 0; r2 < 2; ++r2) {
-            const uint16_t *bsrc = bs + ((buf * 2 + r2) * NB * 64 + lane) * 8;
-            // all operand fragments of the step in flight before the MFMAs
-            u32x4 bop[NB];
-#pragma unroll
-            for (int x = 0; x < NB; ++x) bop[x] = *reinterpret_cast<const u32x4 *>(bsrc + x * 64 * 8);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int x = 0; x < NB; ++x)
-#pragma unroll
-              for (int pb = 0; pb < NP; ++pb) acc[x][pb] = mfma_bf16(bop[x], cf[r2][pb], acc[x][pb]);
-          }
+    for (int e = 0; e < 8; ++e) {
+      const int dm = T::dim(2 * t + (e >> 2), 4 * gq + (e & 3));
+      float x = 0.f;
+      if (hj < G) {
+        const size_t off = (static_cast<size_t>(b) * a.n_q + g * G + hj) * D;
+        const int i = dm % HALF;
+        float lo, hi;
+        if (a.q_f32) {
+          lo = static_cast<const float *>(a.q)[off + i];
+          hi = static_cast<const float *>(a.q)[off + i + HALF];
+        } else {
+          lo = bf2f(static_cast<const uint16_t *>(a.q)[off + i]);
+          hi = bf2f(static_cast<const uint16_t *>(a.q)[off + i + HALF]);
         }
-        if (loader) factor_store<D>(st, bs + (buf ^ 1) * 2 * NB * 64 * 8, tid);
-        __syncthreads();
+        if (rope_on) {
+          float c, s;
+          rope_cs(qpos, rev64[i], c, s);
+          x = dm < HALF ? lo * c - hi * s : lo * s + hi * c;
+        } else {
+          x = dm < HALF ? lo : hi;
+        }
       }
+      v[e] = x * a.scale_log2;
     }
+    qfs[t][ln] = u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
+  }
+  __syncthreads();
 
-    u32x4 pf[NP / 2];
-    float alpha = 1.f;
-    if (active) {
-      // lane (pos j, grp) holds K^T[dim(x, 4grp + r)][P0 + 16pb + j]
-      if (rope_on) {
+  // running softmax state of head j (every lane tracks its own column)
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 uacc[RBW];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+  for (int i = 0; i < RBW; ++i) uacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // this wave's rank blocks (clamped duplicates of the last one are computed
+  // and discarded, so every load stays unconditional)
+  int rb[RBW];
 #pragma unroll
-          for (int e = 0; e < NE; ++e) {
-            const int fi = T::CPL * (4 * grp + r) + e;
-            double tb = static_cast<double>(P0) * rev64[fi];
-            tb -= rint(tb);
-            const float base = static_cast<float>(tb);
-            const float rf = rev32[fi];
+  for (int i = 0; i < RBW; ++i) rb[i] = min(wave + kNW * i, nrb - 1);
+
+  for (int c0 = p_begin; c0 < p_end; c0 += pitch) {
+    const int c1 = min(c0 + pitch, p_end);
+    const int nslices = (c1 - c0 + kSlice - 1) / kSlice;
+    // ------------------------------ phase 1 ------------------------------
+    float mx = -INFINITY;
+    for (int sl = 0; sl < (nslices + kNW - 1) / kNW; ++sl) {
+      const int slice = wave + kNW * sl;
+      const bool active = slice < nslices;
+      const int P0 = c0 + kSlice * slice;
+      f32x4 acc[NB][kNP];
 #pragma unroll
-            for (int pb = 0; pb < NP; ++pb) {
-              float c, s;
-              turn_cs(base + static_cast<float>(16 * pb + j) * rf, c, s);
-              const float x = acc[e][pb][r], y = acc[NE + e][pb][r];
-              acc[e][pb][r] = x * c - y * s;
-              acc[NE + e][pb][r] = x * s + y * c;
+      for (int x = 0; x < NB; ++x)
+#pragma unroll
+        for (int pb = 0; pb < kNP; ++pb) acc[x][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // element offsets within the sequence's cache (L_max * r < 2^31)
+      int crow[kNP];
+#pragma unroll
+      for (int pb = 0; pb < kNP; ++pb) crow[pb] = min(P0 + slice_pos(pb, j), c1 - 1) * a.r_k + 8 * grp;
+      for (int rc = 0; rc < n_rchunks; ++rc) {
+        const int rs0 = rc * rs_cap, cnt = min(rs_cap, nrs - rs0);
+        if (n_rchunks > 1) {
+          __syncthreads();
+          load_factor(rs0, cnt);
+          __syncthreads();
+        }
+        if (active) {
+          // cache rows kCDepth rank steps ahead, factor fragments one step
+          // ahead; loads past the last step repeat it (every load stays
+          // unconditional) and their products are masked out
+          u32x4 cf[kCDepth][kNP];
+#pragma unroll
+          for (int d = 0; d < kCDepth; ++d) {
+#pragma unroll
+            for (int pb = 0; pb < kNP; ++pb) cf[d][pb] = ld16(ck_b + crow[pb] + 32 * (rs0 + min(d, cnt - 1)));
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          u32x4 bop[2][NB];
+#pragma unroll
+          for (int x = 0; x < NB; ++x)
+            bop[0][x] = *reinterpret_cast<const u32x4 *>(bs + (static_cast<size_t>(x) * 64 + lane) * 8);
+          for (int s0 = 0; s0 < cnt; s0 += kCDepth) {
+#pragma unroll
+            for (int d = 0; d < kCDepth; ++d) {
+              const int s = s0 + d;
+              const bool valid = s < cnt;
+              const uint16_t *fr = bs + (static_cast<size_t>(min(s + 1, cnt - 1) * NB) * 64 + lane) * 8;
+#pragma unroll
+              for (int x = 0; x < NB; ++x) bop[(d + 1) & 1][x] = *reinterpret_cast<const u32x4 *>(fr + x * 64 * 8);
+              __builtin_amdgcn_sched_barrier(0);
+              u32x4 cop[kNP];
+#pragma unroll
+              for (int pb = 0; pb < kNP; ++pb) cop[pb] = valid ? cf[d][pb] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+              for (int x = 0; x < NB; ++x)
+#pragma unroll
+                for (int pb = 0; pb < kNP; ++pb) acc[x][pb] = mfma_bf16(bop[d & 1][x], cop[pb], acc[x][pb]);
+              __builtin_amdgcn_sched_barrier(0);
+              const int sn = rs0 + min(s + kCDepth, cnt - 1);
+#pragma unroll
+              for (int pb = 0; pb < kNP; ++pb) cf[d][pb] = ld16(ck_b + crow[pb] + 32 * sn);
+              __builtin_amdgcn_sched_barrier(0);
             }
           }
-      }
-      // S^T[pos, h]: lane (head j, grp) holds S^T[P0 + 16pb + 4grp + r][j]
-      f32x4 sc[NP];
-#pragma unroll
-      for (int pb = 0; pb < NP; ++pb) {
-        sc[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < NB / 2; ++t)
-          sc[pb] = mfma_bf16(pack_acc(acc[2 * t][pb], acc[2 * t + 1][pb]), qfs[t][lane], sc[pb]);
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int pb = 0; pb < NP; ++pb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (P0 + 16 * pb + 4 * grp + r >= p_end) sc[pb][r] = -INFINITY;
-          mx = fmaxf(mx, sc[pb][r]);
         }
-      mx = wave_max_xor(mx, 16);
-      mx = wave_max_xor(mx, 32);
-      const float m_new = fmaxf(m_run, mx);
-      alpha = exp2f(m_run - m_new);
-      float psum = 0.f;
+      }
+      if (active) {
+        // lane (pos j, grp) holds K^T[dim(x, 4grp + r)][P0 + slice_pos(pb, j)]
+        if (rope_on) {
 #pragma unroll
-      for (int pb = 0; pb < NP; ++pb)
+          for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          sc[pb][r] = exp2f(sc[pb][r] - m_new);
-          psum += sc[pb][r];
+            for (int e = 0; e < NE; ++e) {
+              const int fi = T::CPL * (4 * grp + r) + e;
+              double tb = static_cast<double>(P0) * rev64[fi];
+              tb -= rint(tb);
+              const float base = static_cast<float>(tb);
+              const float rf = rev32[fi];
+#pragma unroll
+              for (int pb = 0; pb < kNP; ++pb) {
+                float c, s;
+                turn_cs(base + static_cast<float>(slice_pos(pb, j)) * rf, c, s);
+                const float x = acc[e][pb][r], y = acc[NE + e][pb][r];
+                acc[e][pb][r] = x * c - y * s;
+                acc[NE + e][pb][r] = x * s + y * c;
+              }
+            }
         }
-      psum = wave_sum_xor(psum, 16);
-      psum = wave_sum_xor(psum, 32);
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
+        // S^T[pos, h]: lane (head j, grp) holds S^T[P0 + slice_pos(pb, 4grp + r)][j]
 #pragma unroll
-      for (int u = 0; u < NP / 2; ++u) pf[u] = pack_acc(sc[2 * u], sc[2 * u + 1]);
-    }
-
-    // ---------------- V[pos, d] = C_v B_v, same positions ----------------
+        for (int pb = 0; pb < kNP; ++pb) {
+          f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int x = 0; x < NB; ++x)
+          for (int t = 0; t < NB / 2; ++t)
+            sc = mfma_bf16(pack_acc(acc[2 * t][pb], acc[2 * t + 1][pb]), qfs[t][lane], sc);
 #pragma unroll
-      for (int pb = 0; pb < NP; ++pb) acc[x][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    {
-      // One round = two 32-rank steps. The factor fragments and the cache
-      // rows of round r + 1 are loaded while round r computes; loads past
-      // the last round repeat it (unconditional loads keep the wait counts
-      // exact; the extra stage lands in the buffer nobody reads).
-      const int nrounds = a.r_v / 64;
-      const uint16_t *cbase = a.cv + seq_row * a.r_v + 8 * grp;
-      int crow[NP];
-#pragma unroll
-      for (int pb = 0; pb < NP; ++pb) crow[pb] = min(P0 + 16 * pb + j, last) * a.r_v;
-      auto load_rows = [&](u32x4 (&cf)[2][NP], int round) {
-#pragma unroll
-        for (int r2 = 0; r2 < 2; ++r2)
-#pragma unroll
-          for (int pb = 0; pb < NP; ++pb) cf[r2][pb] = ld16(cbase + crow[pb] + (2 * round + r2) * 32);
-      };
-      FactorStage<D> st;
-      u32x4 cf[2][NP], cfn[2][NP];
-      const bool loader = tid < 256;
-      if (loader) factor_load<D>(st, a.bv, ldb, g, 0, tid);
-      load_rows(cfn, 0);
-      if (loader) factor_store<D>(st, bs, tid);
-      __syncthreads();
-      for (int round = 0; round < nrounds; ++round) {
-        const int buf = round & 1;
-#pragma unroll
-        for (int r2 = 0; r2 < 2; ++r2)
-#pragma unroll
-          for (int pb = 0; pb < NP; ++pb) cf[r2][pb] = cfn[r2][pb];
-        const int nxt = min(round + 1, nrounds - 1);
-        if (loader) factor_load<D>(st, a.bv, ldb, g, nxt, tid);
-        load_rows(cfn, nxt);
-        if (active) {
-#pragma unroll
-          for (int r2 = 0; r2 < 2; ++r2) {
-            const uint16_t *bsrc = bs + ((buf * 2 + r2) * NB * 64 + lane) * 8;
-            // all operand fragments of the step in flight before the MFMAs
-            u32x4 bop[NB];
-#pragma unroll
-            for (int x = 0; x < NB; ++x) bop[x] = *reinterpret_cast<const u32x4 *>(bsrc + x * 64 * 8);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int x = 0; x < NB; ++x)
-#pragma unroll
-              for (int pb = 0; pb < NP; ++pb) acc[x][pb] = mfma_bf16(cf[r2][pb], bop[x], acc[x][pb]);
+          for (int r = 0; r < 4; ++r) {
+            const int off = P0 - c0 + slice_pos(pb, 4 * grp + r);
+            const float v = c0 + off < c1 ? sc[r] : -INFINITY;
+            mx = fmaxf(mx, v);
+            if (j < G) sS[j * pitch + off] = v;
           }
         }
-        if (loader) factor_store<D>(st, bs + (buf ^ 1) * 2 * NB * 64 * 8, tid);
-        __syncthreads();
       }
     }
-    if (active) {
-      // lane (column j, grp) holds V[P0 + 16pb + 4grp + r][dim(x, j)]
+    mx = wave_max_xor(mx, 16);
+    mx = wave_max_xor(mx, 32);
+    if (grp == 0) smax[wave][j] = mx;
+    // phase-2 value rows do not depend on the probabilities: start them now.
+    // A operand: lane (rank row j, grp) = C_v^T[16 rb + j][c0 + 32u + 8grp ..+8]
+    const int nU = (c1 - c0 + 31) >> 5;
+    auto vload = [&](u32x4 (&dst)[RBW], int u) {
+      const int pc = min(c0 + 32 * u + 8 * grp, a.L_max - 8);
 #pragma unroll
-      for (int x = 0; x < NB; ++x) {
-        accO[x] *= alpha;
+      for (int i = 0; i < RBW; ++i) dst[i] = ld16(cv_b + (16 * rb[i] + j) * a.L_max + pc);
+    };
+    u32x4 vr[kVDepth][RBW];
 #pragma unroll
-        for (int u = 0; u < NP / 2; ++u)
-          accO[x] = mfma_bf16(pack_acc(acc[x][2 * u], acc[x][2 * u + 1]), pf[u], accO[x]);
+    for (int d = 0; d < kVDepth; ++d) {
+      vload(vr[d], min(d, nU - 1));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+    // ------------------------------ softmax ------------------------------
+    float m_new = m_run;
+#pragma unroll
+    for (int wv = 0; wv < kNW; ++wv) m_new = fmaxf(m_new, smax[wv][j]);
+    const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+    m_run = m_new;
+    float ps = 0.f;
+    for (int u = wave; u < nU; u += kNW) {
+      float v[8];
+      const int off = 32 * u + 8 * grp;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[e] = 0.f;
+        if (j < G && c0 + off + e < c1) v[e] = exp2f(sS[j * pitch + off + e] - m_new);
+        ps += v[e];
+      }
+      pbuf[u * 64 + lane] = u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
+    }
+    ps = wave_sum_xor(ps, 16);
+    ps = wave_sum_xor(ps, 32);
+    if (grp == 0) psw[wave][j] = ps;
+    __syncthreads();
+    // ------------------------------ phase 2 ------------------------------
+    float lsum = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < kNW; ++wv) lsum += psw[wv][j];
+    l_run = l_run * alpha + lsum;
+#pragma unroll
+    for (int i = 0; i < RBW; ++i) uacc[i] *= alpha;
+    for (int u0 = 0; u0 < nU; u0 += kVDepth) {
+#pragma unroll
+      for (int d = 0; d < kVDepth; ++d) {
+        const int u = min(u0 + d, nU - 1);
+        u32x4 pop = pbuf[u * 64 + lane];
+        if (u0 + d >= nU) pop = u32x4{0u, 0u, 0u, 0u};
+        // value rows at positions >= ctx (unwritten cache) are zeroed: the
+        // probabilities there are zero, but 0 * NaN would not be
+        const int nv = ctx - (c0 + 32 * u + 8 * grp);
+        const bool ragged = c0 + 32 * u + 32 > ctx;   // uniform across the wave
+#pragma unroll
+        for (int i = 0; i < RBW; ++i) {
+          const u32x4 aop = ragged ? keep_first(vr[d][i], nv) : vr[d][i];
+          uacc[i] = mfma_bf16(aop, pop, uacc[i]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        vload(vr[d], min(u0 + d + kVDepth, nU - 1));
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
 
-  // ---------------- merge the waves (LDS, aliasing the factor stage) ----------------
-  float *mrg_o = smem;   // [NW][16][D]
-  if (grp == 0) {
-    mrg_m[wave][j] = m_run;
-    mrg_l[wave][j] = l_run;
+  // ---------------- O^T = B_v^T U^T (MFMA, U rounded to bf16) ----------------
+  __syncthreads();   // LDS is reused for U
+  float *ulds = reinterpret_cast<float *>(dlds);   // [16][r_v], rows >= G zero
+  // lane (head j, grp) holds U^T[16 rb + 4grp + r][j]
+#pragma unroll
+  for (int i = 0; i < RBW; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ulds[j * a.r_v + 16 * rb[i] + 4 * grp + r] = j < G ? uacc[i][r] : 0.f;
+  if (wave == 0 && grp == 0) {
+    mfin[j] = m_run;
+    lfin[j] = l_run;
   }
-  // lane (head j, grp) holds O^T[dim(x, 4grp + r)][j]
-#pragma unroll
-  for (int x = 0; x < NB; ++x)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) mrg_o[(wave * 16 + j) * D + T::dim(x, 4 * grp + r)] = accO[x][r];
   __syncthreads();
   const int D2 = D + 2;
   float *part = a.part + ((static_cast<size_t>(b) * a.n_q + g * G) * a.nsplit) * D2;
-  for (int idx = tid; idx < G * D; idx += kDecodeThreads) {
-    const int h = idx / D, dd = idx % D;
-    float M = -INFINITY;
+  {
+    // wave owns d blocks OBW * wave .. +OBW; A = B_v^T rows, B = U (bf16)
+    const uint16_t *bv_g = a.bv + static_cast<size_t>(g) * D * a.r_v;
+    f32x4 oacc[OBW];
 #pragma unroll
-    for (int wv = 0; wv < NW; ++wv) M = fmaxf(M, mrg_m[wv][h]);
-    float o = 0.f, L = 0.f;
-    if (M != -INFINITY) {
+    for (int x = 0; x < OBW; ++x) oacc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float *urow = ulds + j * a.r_v + 8 * grp;
+    for (int s0 = 0; s0 < a.r_v / 32; s0 += 2) {   // r_v / 32 is even
+      u32x4 av[2][OBW];
 #pragma unroll
-      for (int wv = 0; wv < NW; ++wv) {
-        const float sc = exp2f(mrg_m[wv][h] - M);
-        o += sc * mrg_o[(wv * 16 + h) * D + dd];
-        L += sc * mrg_l[wv][h];
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int x = 0; x < OBW; ++x)
+          av[q][x] = ld16(bv_g + static_cast<size_t>(16 * (OBW * wave + x) + j) * a.r_v + 32 * (s0 + q) + 8 * grp);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const f32x4 u0 = *reinterpret_cast<const f32x4 *>(urow + 32 * (s0 + q));
+        const f32x4 u1 = *reinterpret_cast<const f32x4 *>(urow + 32 * (s0 + q) + 4);
+        const u32x4 bop = u32x4{pack2(u0[0], u0[1]), pack2(u0[2], u0[3]), pack2(u1[0], u1[1]), pack2(u1[2], u1[3])};
+#pragma unroll
+        for (int x = 0; x < OBW; ++x) oacc[x] = mfma_bf16(av[q][x], bop, oacc[x]);
       }
     }
-    if (a.nsplit == 1) {
-      const size_t oi = (static_cast<size_t>(b) * a.n_q + g * G + h) * D + dd;
-      if (a.out_f32)
-        static_cast<float *>(a.out)[oi] = o / L;
-      else
-        static_cast<uint16_t *>(a.out)[oi] = f2bf(o / L);
-    } else {
-      float *dst = part + (static_cast<size_t>(h) * a.nsplit + split) * D2;
-      store_coherent(dst + dd, o);
-      if (dd == 0) {
-        store_coherent(dst + D, M);
-        store_coherent(dst + D + 1, L);
+    // lane (head j, grp) holds O^T[16 (OBW wave + x) + 4grp + r][j]
+    if (j < G) {
+#pragma unroll
+      for (int x = 0; x < OBW; ++x) {
+        const int dd = 16 * (OBW * wave + x) + 4 * grp;
+        if (a.nsplit == 1) {
+          const float il = 1.f / lfin[j];
+          const size_t oi = (static_cast<size_t>(b) * a.n_q + g * G + j) * D + dd;
+          if (a.out_f32)
+            *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + oi) = oacc[x] * il;
+          else
+            *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(a.out) + oi) =
+                u32x2{pack2(oacc[x][0] * il, oacc[x][1] * il), pack2(oacc[x][2] * il, oacc[x][3] * il)};
+        } else {
+          float *dst = part + (static_cast<size_t>(j) * a.nsplit + split) * D2;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) store_coherent(dst + dd + r, oacc[x][r]);
+          if (dd == 0) {
+            store_coherent(dst + D, mfin[j]);
+            store_coherent(dst + D + 1, lfin[j]);
+          }
+        }
       }
     }
   }
@@ -459,9 +475,9 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void attn_decode_kernel(AttnDeco
                 a.nsplit - 1;
   __syncthreads();
   if (!last_flag) return;
-  // split statistics -> LDS (reuse mrg_o space): sm[h][s], sl[h][s]
-  float *sm = mrg_o, *sl = mrg_o + 16 * a.nsplit;
-  for (int idx = tid; idx < G * a.nsplit; idx += kDecodeThreads) {
+  // split statistics -> LDS (reused): sm[h][s], sl[h][s]
+  float *sm = reinterpret_cast<float *>(dlds), *sl = sm + 16 * a.nsplit;
+  for (int idx = tid; idx < G * a.nsplit; idx += kThreads) {
     const int h = idx / a.nsplit, sp = idx % a.nsplit;
     const float *src = part + (static_cast<size_t>(h) * a.nsplit + sp) * D2;
     sm[idx] = load_coherent(src + D);
@@ -480,7 +496,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void attn_decode_kernel(AttnDeco
     cmb_l[tid] = L;
   }
   __syncthreads();
-  for (int idx = tid; idx < G * D; idx += kDecodeThreads) {
+  for (int idx = tid; idx < G * D; idx += kThreads) {
     const int h = idx / D, dd = idx % D;
     const float M = cmb_m[h];
     float o = 0.f;
@@ -507,20 +523,84 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void attn_decode_kernel(AttnDeco
   if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// LDS of one workgroup on this device (160 KB on gfx950)
+int lds_per_block() {
+  static int bytes = 0;
+  if (bytes == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeSharedMemPerBlockOptin, dev) == hipSuccess && v > 0)
+      bytes = v;
+    else
+      bytes = 65536;
+  }
+  return bytes;
+}
+
+// Dynamic LDS plan: the resident factor (else the largest even number of
+// rank steps that leaves a 512-position chunk), then the longest chunk the
+// rest holds, at most the split length. Returns the dynamic bytes, 0 if the
+// shape does not fit.
+int plan_lds(AttnDecodeArgs &a, int dyn, int nb) {
+  const int G = a.n_q / a.n_kv;
+  const int step_bytes = nb * 1024;
+  const int nrs = a.r_k / 32;
+  const int per_pos = 4 * G + 32;
+  const int want = min(kMaxPitch, (a.split_len + kSlice - 1) / kSlice * kSlice);
+  int rs_cap = nrs;
+  int pitch = ((dyn - nrs * step_bytes) / per_pos) & ~(kSlice - 1);
+  if (pitch < kSlice) {
+    pitch = min(want, 512);
+    rs_cap = ((dyn - pitch * per_pos) / step_bytes) & ~1;
+    if (rs_cap < 2) {
+      rs_cap = 2;
+      pitch = ((dyn - 2 * step_bytes) / per_pos) & ~(kSlice - 1);
+    }
+  }
+  pitch = min(pitch, want);
+  if (pitch < kSlice || rs_cap < 2 || 64 * a.r_v > dyn) return 0;
+  a.rs_cap = rs_cap;
+  a.pitch = pitch;
+  a.lds_bs = rs_cap * step_bytes;
+  a.lds_s = (G * pitch * 4 + 15) / 16 * 16;
+  return dyn;
+}
+
+template <int D, int RBW>
+hipError_t launch_cfg(AttnDecodeArgs a, int grid, hipStream_t s) {
+  const void *fn = reinterpret_cast<const void *>(&attn_decode_kernel<D, RBW>);
+  static int dyn = -1;   // dynamic LDS of this instantiation (set up once)
+  if (dyn < 0) {
+    hipFuncAttributes fa;
+    hipError_t e = hipFuncGetAttributes(&fa, fn);
+    if (e != hipSuccess) return e;
+    const int d = lds_per_block() - static_cast<int>(fa.sharedSizeBytes);
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, d);
+    if (e != hipSuccess) return e;
+    dyn = d;
+  }
+  if (plan_lds(a, dyn, Tile<D>::NB) == 0) return hipErrorInvalidValue;
+  attn_decode_kernel<D, RBW><<<grid, kThreads, dyn, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const AttnDecodeArgs &a, int grid, hipStream_t s) {
+  if (a.r_v / 16 <= 8 * kNW) return launch_cfg<D, 8>(a, grid, s);
+  return launch_cfg<D, 16>(a, grid, s);
+}
+
 }  // namespace
 
-int attn_decode_positions_per_tile() { return 32 * kDecodeWaves; }
-int attn_decode_split_granule() { return 32; }
+int attn_decode_split_granule() { return kSlice; }
+int attn_decode_max_rank_v() { return 16 * 16 * kNW; }
 
 hipError_t launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s) {
   TraceGuard trace_guard(K_ATTN_DECODE, s);
   const int total = a.Bsz * a.n_kv * a.nsplit;
   const int grid = (total + 7) / 8 * 8;
-  if (a.d == 128)
-    attn_decode_kernel<128><<<grid, kDecodeThreads, 0, s>>>(a);
-  else
-    attn_decode_kernel<64><<<grid, kDecodeThreads, 0, s>>>(a);
-  return hipGetLastError();
+  if (a.d == 128) return launch_d<128>(a, grid, s);
+  return launch_d<64>(a, grid, s);
 }
 
 }  // namespace dl

@@ -1,5 +1,5 @@
 // Small memory-bound helpers of the layer: RMSNorm, accumulator
-// initialisation, conversion and the decode-time cache row store.
+// initialisation (fills and copies) and float32 -> storage conversion.
 #include <math.h>
 
 #include "common.h"
@@ -68,19 +68,6 @@ __global__ void convert_kernel(const float *src, void *dst, int dst_bf16, int64_
   }
 }
 
-__global__ void store_cache_rows_kernel(const float *src, int ld, void *cache, int cache_bf16,
-                                        const int32_t *past, int T, int r, int L_max) {
-  const int b = blockIdx.x / T, t = blockIdx.x % T;
-  const size_t row = static_cast<size_t>(b) * L_max + past[b] + t;
-  for (int i = threadIdx.x; i < r; i += blockDim.x) {
-    const float v = src[static_cast<size_t>(blockIdx.x) * ld + i];
-    if (cache_bf16)
-      static_cast<uint16_t *>(cache)[row * r + i] = f2bf(v);
-    else
-      static_cast<float *>(cache)[row * r + i] = v;
-  }
-}
-
 int grid_for(int64_t n) {
   int64_t g = (n + 255) / 256;
   if (g > 4096) g = 4096;
@@ -113,14 +100,6 @@ hipError_t launch_fill(const FillRegion *r, int nreg, hipStream_t s) {
 hipError_t launch_convert_f32(const float *src, void *dst, int dst_bf16, int64_t n, hipStream_t s) {
   TraceGuard trace_guard(K_CONVERT, s);
   convert_kernel<<<grid_for(n), 256, 0, s>>>(src, dst, dst_bf16, n);
-  return hipGetLastError();
-}
-
-hipError_t launch_store_cache_rows(const float *src, int ld, void *cache, int cache_bf16,
-                                   const int32_t *past, int Bsz, int T, int r, int L_max,
-                                   hipStream_t s) {
-  TraceGuard trace_guard(K_STORE_CACHE, s);
-  store_cache_rows_kernel<<<Bsz * T, 256, 0, s>>>(src, ld, cache, cache_bf16, past, T, r, L_max);
   return hipGetLastError();
 }
 

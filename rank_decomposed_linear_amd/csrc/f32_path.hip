@@ -3,7 +3,8 @@
 // -- factor-pair GEMMs (DeInfer section 2.1, Eq. (1)) and attention that
 // rebuilds each key and value from the low-rank cache on the fly (section
 // 4.2) -- in full float32, for shapes too small or too irregular for the
-// MFMA tiling.
+// MFMA tiling. Storage follows the bf16 path: weights transposed (Wt[N, K]),
+// up factors [n_kv * d, r], value cache rank-major [Bsz, r_v, L_max].
 #include <math.h>
 
 #include "common.h"
@@ -35,9 +36,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args a) {
       As[kk][r] = v;
     }
     for (int i = tid; i < TK * TN; i += 256) {
-      const int kk = i / TN, c = i % TN;
+      const int c = i / TK, kk = i % TK;
       const int k = k0 + kk, n = n0 + c;
-      Bs[kk][c] = (k < a.K && n < a.N) ? a.W[static_cast<size_t>(k) * a.N + n] : 0.f;
+      Bs[kk][c] = (k < a.K && n < a.N) ? a.W[static_cast<size_t>(n) * a.K + k] : 0.f;
     }
     __syncthreads();
 #pragma unroll
@@ -58,6 +59,16 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args a) {
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + ty * 4 + i;
     if (m >= a.M) continue;
+    if (a.omode == F32_OUT_CACHE_T) {
+      const int b = m / a.T, t = m - b * a.T;
+      const size_t col = static_cast<size_t>(a.past_lens[b]) + t;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int n = n0 + tx * 4 + jj;
+        if (n < a.N) a.C[(static_cast<size_t>(b) * a.N + n) * a.L_max + col] = acc[i][jj];
+      }
+      continue;
+    }
     size_t rowoff;
     if (a.omode == F32_OUT_CACHE) {
       const int b = m / a.T, t = m - b * a.T;
@@ -87,7 +98,6 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnF32Args a) {
   const int D = a.d, H = D / 2, G = a.n_q / a.n_kv, g = h / G;
   const int pos = a.decode ? a.lens[b] - 1 : a.lens[b] + t;
   const bool rope_on = a.theta != 0.f;
-  const int ld = a.n_kv * D;
 
   float qx[2] = {0.f, 0.f}, qy[2] = {0.f, 0.f};
   double rev[2] = {0.0, 0.0};
@@ -114,26 +124,27 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnF32Args a) {
   float ox[2] = {0.f, 0.f}, oy[2] = {0.f, 0.f};
   for (int key = 0; key <= pos; ++key) {
     const float *ckr = a.ck + (static_cast<size_t>(b) * a.L_max + key) * a.r_k;
-    const float *cvr = a.cv + (static_cast<size_t>(b) * a.L_max + key) * a.r_v;
+    const float *cvc = a.cv + static_cast<size_t>(b) * a.r_v * a.L_max + key;
     float kx[2] = {0.f, 0.f}, ky[2] = {0.f, 0.f}, vx[2] = {0.f, 0.f}, vy[2] = {0.f, 0.f};
+    // up-factor rows of this lane's dimensions (i, i + d/2)
+    const float *bk = a.bk + static_cast<size_t>(g * D) * a.r_k;
+    const float *bv = a.bv + static_cast<size_t>(g * D) * a.r_v;
     for (int r = 0; r < a.r_k; ++r) {
       const float c = ckr[r];
-      const float *bk = a.bk + static_cast<size_t>(r) * ld + g * D;
 #pragma unroll
       for (int u = 0; u < 2; ++u)
         if (ok[u]) {
-          kx[u] = fmaf(c, bk[lane + 64 * u], kx[u]);
-          ky[u] = fmaf(c, bk[lane + 64 * u + H], ky[u]);
+          kx[u] = fmaf(c, bk[static_cast<size_t>(lane + 64 * u) * a.r_k + r], kx[u]);
+          ky[u] = fmaf(c, bk[static_cast<size_t>(lane + 64 * u + H) * a.r_k + r], ky[u]);
         }
     }
     for (int r = 0; r < a.r_v; ++r) {
-      const float c = cvr[r];
-      const float *bv = a.bv + static_cast<size_t>(r) * ld + g * D;
+      const float c = cvc[static_cast<size_t>(r) * a.L_max];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
         if (ok[u]) {
-          vx[u] = fmaf(c, bv[lane + 64 * u], vx[u]);
-          vy[u] = fmaf(c, bv[lane + 64 * u + H], vy[u]);
+          vx[u] = fmaf(c, bv[static_cast<size_t>(lane + 64 * u) * a.r_v + r], vx[u]);
+          vy[u] = fmaf(c, bv[static_cast<size_t>(lane + 64 * u + H) * a.r_v + r], vy[u]);
         }
     }
     float dot = 0.f;

@@ -1,15 +1,12 @@
 // bf16 MFMA GEMM for prefill-sized M: one factor of a decomposed projection
 // (W ~ A B, DeInfer section 2.1, Eq. (1)), C = X W with f32 accumulation.
 //
-// Both factors are stored [in, out] row-major, so the reduction index of the
-// weight operand is its row index: the 16x16x32 MFMA wants eight consecutive
-// reduction values per lane. The weight tile is therefore transposed once
-// per workgroup while it is staged into LDS: a thread loads eight rows x
-// eight columns (eight 16-byte loads covering 4 rows x 256 contiguous bytes
-// per instruction), transposes them in registers and writes eight operand
-// fragments in lane order, so every MFMA operand read from LDS is one
-// conflict-free 16-byte ds_read. The activation tile is staged as rows with
-// an XOR swizzle of its 16-byte chunks.
+// Both factors are stored transposed (Wt[N, K], the reduction index
+// contiguous), which is the order the 16x16x32 MFMA wants: eight
+// consecutive reduction values per lane. Activation and weight tiles are
+// therefore staged the same way, as rows of 16-byte chunks with an XOR
+// swizzle, so every operand read from LDS is one conflict-free 16-byte
+// ds_read.
 //
 // Tile 128 x 128 x 64, 4 waves (2 x 2), each wave 64 x 64 = 4 x 4 MFMA
 // blocks; LDS double-buffered (64 KB).
@@ -23,10 +20,10 @@ namespace {
 constexpr int BM = 128, BN = 128, BK = 64;
 constexpr int kThreads = 256;
 constexpr int kAElems = BM * BK;          // bf16 elements of one A tile
-constexpr int kBElems = BK * BN;          // bf16 elements of one B tile (fragments)
+constexpr int kBElems = BN * BK;          // bf16 elements of one weight tile
 
 struct Stage {
-  u32x4 v[8];
+  u32x4 a[4], b[4];
 };
 
 __device__ __forceinline__ u32x4 swiglu8(u32x4 g, u32x4 u) {
@@ -38,17 +35,6 @@ __device__ __forceinline__ u32x4 swiglu8(u32x4 g, u32x4 u) {
     r[q] = pack2(a0, a1);
   }
   return r;
-}
-
-__device__ __forceinline__ void transpose8(const u32x4 (&r)[8], u32x4 (&b)[8]) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t lo = r[2 * q][e >> 1], hi = r[2 * q + 1][e >> 1];
-      b[e][q] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-    }
-  }
 }
 
 template <int XM, int OM>
@@ -67,60 +53,35 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   const int n0 = (bx - sg.tile_begin) * BN;
   const int m0 = blockIdx.y * BM;
 
-  // Loader roles: threads 0..127 stage A (8 rows x 16 B each),
-  // threads 128..255 stage B (8 k-rows x 8 columns each).
-  const bool loads_a = tid < 128;
-  const int t = tid & 127;
-  // A: chunk kc = t % 8 of rows (t / 8) + 16 * it, it = 0..7
-  const int a_kc = t & 7, a_r0 = t >> 3;
-  // B: k-row group q = t / 16 (rows 8q..8q+7), column group p = t % 16
-  const int b_q = t >> 4, b_p = t & 15;
-  const int b_col = n0 + 8 * b_p;
-  const bool b_ok = b_col < sg.N;
+  // Thread t stages 16-byte chunk (row (t + 256 it) / 8, column chunk t % 8)
+  // of both tiles, it = 0..3.
+  const int kc = tid & 7, r0 = tid >> 3;
 
   auto gload = [&](Stage &st, int k0) {
-    if (loads_a) {
 #pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int row = m0 + a_r0 + 16 * it;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (row < a.M) {
-          const size_t off = static_cast<size_t>(row) * sg.ldx + k0 + 8 * a_kc;
-          v = *reinterpret_cast<const u32x4 *>(sg.X + off);
-          if constexpr (XM == GEMM_X_SWIGLU)
-            v = swiglu8(v, *reinterpret_cast<const u32x4 *>(sg.X2 + off));
-        }
-        st.v[it] = v;
+    for (int it = 0; it < 4; ++it) {
+      const int row = m0 + r0 + 32 * it;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row < a.M) {
+        const size_t off = static_cast<size_t>(row) * sg.ldx + k0 + 8 * kc;
+        v = *reinterpret_cast<const u32x4 *>(sg.X + off);
+        if constexpr (XM == GEMM_X_SWIGLU)
+          v = swiglu8(v, *reinterpret_cast<const u32x4 *>(sg.X2 + off));
       }
-    } else {
-      const uint16_t *wp = sg.W + static_cast<size_t>(k0 + 8 * b_q) * sg.N + b_col;
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-        st.v[s] = b_ok ? *reinterpret_cast<const u32x4 *>(wp + static_cast<size_t>(s) * sg.N)
-                       : u32x4{0u, 0u, 0u, 0u};
+      st.a[it] = v;
+      const int n = n0 + r0 + 32 * it;
+      st.b[it] = n < sg.N ? *reinterpret_cast<const u32x4 *>(sg.W + static_cast<size_t>(n) * a.K + k0 + 8 * kc)
+                          : u32x4{0u, 0u, 0u, 0u};
     }
   };
   auto sstore = [&](const Stage &st, int buf) {
     uint16_t *base = lds[buf];
-    if (loads_a) {
 #pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int row = a_r0 + 16 * it;
-        const int chunk = a_kc ^ (row & 7);
-        *reinterpret_cast<u32x4 *>(base + row * BK + chunk * 8) = st.v[it];
-      }
-    } else {
-      u32x4 f[8];
-      transpose8(st.v, f);
-      // k rows 8q..8q+7 -> kstep ks = q/4, lane group g = q%4;
-      // column 8p + e -> block nb = p/2, lane column jj = 8(p%2) + e
-      const int ks = b_q >> 2, g = b_q & 3, nb = b_p >> 1;
-      uint16_t *fb = base + kAElems + ((ks * (BN / 16) + nb) * 64) * 8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int ln = g * 16 + 8 * (b_p & 1) + e;
-        *reinterpret_cast<u32x4 *>(fb + ln * 8) = f[e];
-      }
+    for (int it = 0; it < 4; ++it) {
+      const int row = r0 + 32 * it;
+      const int chunk = kc ^ (row & 7);
+      *reinterpret_cast<u32x4 *>(base + row * BK + chunk * 8) = st.a[it];
+      *reinterpret_cast<u32x4 *>(base + kAElems + row * BK + chunk * 8) = st.b[it];
     }
   };
 
@@ -150,9 +111,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
       }
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
-        const int gnb = wn * 4 + nb;
-        bfr[nb] = *reinterpret_cast<const u32x4 *>(base + kAElems +
-                                                   ((ks * (BN / 16) + gnb) * 64 + lane) * 8);
+        const int row = wn * 64 + nb * 16 + j;
+        const int chunk = (ks * 4 + grp) ^ (row & 7);
+        bfr[nb] = *reinterpret_cast<const u32x4 *>(base + kAElems + row * BK + chunk * 8);
       }
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
@@ -170,6 +131,17 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
     for (int r = 0; r < 4; ++r) {
       const int m = m0 + wm * 64 + mb * 16 + 4 * grp + r;
       if (m >= a.M) continue;
+      if constexpr (OM == GEMM_OUT_CACHE_T) {
+        const int b = m / a.T, tt = m - b * a.T;
+        uint16_t *col = static_cast<uint16_t *>(sg.C) + static_cast<size_t>(b) * sg.N * a.L_max +
+                        a.past_lens[b] + tt;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const int n = n0 + wn * 64 + nb * 16 + j;
+          if (n < sg.N) col[static_cast<size_t>(n) * a.L_max] = f2bf(acc[mb][nb][r]);
+        }
+        continue;
+      }
       size_t rowoff;
       if constexpr (OM == GEMM_OUT_CACHE) {
         const int b = m / a.T, tt = m - b * a.T;
@@ -207,7 +179,8 @@ hipError_t launch_x(const GemmArgs &a, dim3 grid, hipStream_t s) {
     case GEMM_OUT_F32_RES_BF16:
       gemm_bf16_kernel<XM, GEMM_OUT_F32_RES_BF16><<<grid, kThreads, 0, s>>>(a);
       break;
-    default: gemm_bf16_kernel<XM, GEMM_OUT_CACHE><<<grid, kThreads, 0, s>>>(a); break;
+    case GEMM_OUT_CACHE: gemm_bf16_kernel<XM, GEMM_OUT_CACHE><<<grid, kThreads, 0, s>>>(a); break;
+    default: gemm_bf16_kernel<XM, GEMM_OUT_CACHE_T><<<grid, kThreads, 0, s>>>(a); break;
   }
   return hipGetLastError();
 }

@@ -6,29 +6,31 @@
 // ridge of MI355X and far below the bf16 MFMA ridge. So the product runs on
 // MFMA with the token rows padded to 16, organised to keep HBM streaming:
 //
-//  * Work item = (64-column strip, K split). A workgroup of four waves owns
-//    one item; its waves take interleaved 32-row steps of the split, so the
-//    workgroup walks a contiguous block of rows, 128 bytes per row.
-//  * Per step, lane (j = lane%16, g = lane/16) issues eight 8-byte loads
-//    W[k0 + 8g + r][n0 + 4j .. 4j+3], r = 0..7, and transposes them in
-//    registers into four MFMA B operands (one per column offset e = 0..3):
-//    no LDS staging of weights. Output column n0 + 4j + e comes out of
-//    operand e. Four steps (16 KB; two for M > 32) are kept in flight per wave; weights
-//    are streamed with non-temporal loads.
-//  * The token rows (A operand) are one 16-byte load per lane and step,
-//    optionally passed through the fused RMSNorm prologue (gain multiply,
-//    sum of squares for the row scale).
-//  * The four waves are summed in LDS in a fixed order. With more than one
-//    K split, each workgroup writes its partial sums through to the
-//    device-coherent level (relaxed agent-scope atomic stores), waits for
-//    them to complete and bumps a per-strip counter; the last workgroup to
-//    arrive reads the partials back with device-coherent loads, sums them
-//    in split order (deterministic) and runs the epilogue. One atomic per
-//    workgroup instead of one per output element, and no L2 writeback or
-//    invalidate (an agent-scope fence would cost both on every workgroup).
-//  * Epilogues: bf16 / f32 store, scatter into the latent KV cache, residual
-//    add, and SwiGLU for paired (gate, up) launches whose two halves share
-//    the output columns.
+//  * Weights are stored transposed, Wt[N, K] (the reduction index
+//    contiguous). A work item is a tile of 16 output columns -- 16
+//    consecutive rows of Wt, one contiguous 16 * K * 2-byte block -- times a
+//    K split. Output tiles this narrow give enough work items to fill the
+//    chip without splitting K for most factor shapes.
+//  * Per 32-wide reduction step, lane (i = lane%16, g = lane/16) loads
+//    Wt[n0 + i][k0 + 8g .. 8g+7] with one 16-byte non-temporal load: that is
+//    the MFMA A operand as loaded, no shuffles. The token rows are the B
+//    operand, x[m][k0 + 8g ..] (one 16-byte load), optionally passed through
+//    the fused RMSNorm prologue (gain multiply, sum of squares for the row
+//    scale). The accumulator lane (j, g) holds y[m = j][n0 + 4g + r], so the
+//    epilogue stores four consecutive outputs per lane.
+//  * The waves of a workgroup take interleaved steps of the item's K range
+//    and keep four steps (4 KB of weights) in flight each; their sums
+//    meet in LDS and are added in wave order.
+//  * With more than one K split, each workgroup writes its partial sums
+//    through to the device-coherent level (relaxed agent-scope atomic
+//    stores), waits for them to complete and bumps a per-tile counter; the
+//    last workgroup to arrive reads the partials back with device-coherent
+//    loads, sums them in split order (deterministic) and runs the epilogue.
+//    One atomic per workgroup, and no L2 writeback or invalidate (an
+//    agent-scope fence would cost both on every workgroup).
+//  * Epilogues: bf16 / f32 store, scatter into the latent KV cache (row-major
+//    key cache, rank-major value cache), residual add, and SwiGLU for paired
+//    (gate, up) launches whose two halves share the output columns.
 #include <stdlib.h>
 
 #include <algorithm>
@@ -40,7 +42,7 @@
 namespace dl {
 
 namespace {
-constexpr int kCols = 64;   // output columns per strip
+constexpr int kRows = 16;   // output columns per tile (rows of Wt)
 
 // Device-coherent 8-byte accesses for the split-K partial sums: relaxed
 // agent-scope atomics compile to plain loads/stores with the system-coherent
@@ -62,29 +64,15 @@ __device__ __forceinline__ void load_coherent(const float *p, float &a, float &b
 __device__ __forceinline__ void wait_memory() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Interleave the 8 XCDs: dispatch hands workgroup b to XCD b % 8; give each
-// XCD a contiguous range of items so one XCD walks neighbouring columns of
-// the same rows.
+// XCD a contiguous range of items, i.e. neighbouring weight tiles.
 __device__ __forceinline__ int xcd_item(int b, int grid) {
   const int per = grid >> 3;  // grid is a multiple of 8
   return (b & 7) * per + (b >> 3);
 }
 
-// rows r = 0..7 of a 8 x 4 bf16 block (one u32x2 per row) -> four operands,
-// operand e holding column e for reduction slots r = 0..7.
-__device__ __forceinline__ void transpose84(const u32x2 (&r)[8], u32x4 (&b)[4]) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t lo = r[2 * q][e >> 1], hi = r[2 * q + 1][e >> 1];
-      b[e][q] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-    }
-  }
-}
-
 // Activation rows are loaded raw into the prefetch ring with the weights
 // (so waiting for a step never waits for later prefetches) and converted to
-// the bf16 A operand when the step is computed.
+// the bf16 operand when the step is computed.
 template <int XF32>
 __device__ __forceinline__ void load_x_raw(const void *X, int ldx, int row, int k,
                                            u32x4 (&r)[XF32 ? 2 : 1]) {
@@ -148,9 +136,11 @@ template <int MB, int XF32, int PAIRED, int NORM, int GF32, int kWaves>
 __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
   constexpr int kThreads = kWaves * 64;
   constexpr int HALVES = PAIRED ? 2 : 1;
-  constexpr int NREG = HALVES * MB * 4 * 4;  // accumulator floats per lane
-  constexpr int PART = NREG * 64 + MB * 16;  // floats of one partial (sums + row ssq)
-  __shared__ __attribute__((aligned(16))) float red[NREG * 64 + MB * 16];
+  constexpr int NACC = HALVES * MB;          // f32x4 accumulators per lane
+  constexpr int RED = NACC * 4 * 64;         // floats of one wave's sums
+  constexpr int PART = RED + MB * 16;        // floats of one partial (sums + row ssq)
+  __shared__ __attribute__((aligned(16))) float wsum[kWaves][RED];
+  __shared__ __attribute__((aligned(16))) float red[PART];
   __shared__ float ssq_w[kWaves][MB * 16];
   __shared__ int last_flag;
 
@@ -158,37 +148,35 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 15, grp = lane >> 4;
   const int item = xcd_item(blockIdx.x, gridDim.x);
-  if (item >= a.nstrips * a.ksplit) return;
-  const int split = item / a.nstrips;
-  const int strip = item - split * a.nstrips;
+  if (item >= a.ntiles * a.ksplit) return;
+  const int split = item / a.ntiles;
+  const int tile = item - split * a.ntiles;
   int si = 0;
-  if (a.nseg > 1 && strip >= a.seg[1].strip_begin) si = 1;
-  if (a.nseg > 2 && strip >= a.seg[2].strip_begin) si = 2;
+  if (a.nseg > 1 && tile >= a.seg[1].tile_begin) si = 1;
+  if (a.nseg > 2 && tile >= a.seg[2].tile_begin) si = 2;
   const GvSeg sg = a.seg[si];
-  const int n0 = (strip - sg.strip_begin) * kCols;
+  const int n0 = (tile - sg.tile_begin) * kRows;
+  const int wrow = min(n0 + j, sg.N - 1);    // this lane's weight row
 
   const int ksteps = (a.K + a.K2) >> 5;
   const int s_begin = split * a.split_steps;
   const int s_end = min(s_begin + a.split_steps, ksteps);
-  const size_t ldw = static_cast<size_t>(sg.N);
 
-  f32x4 acc[HALVES][MB][4];
+  f32x4 acc[HALVES][MB];
 #pragma unroll
   for (int h = 0; h < HALVES; ++h)
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[h][mb][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mb = 0; mb < MB; ++mb) acc[h][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float ssq[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) ssq[mb] = 0.f;
 
-  // 32-row steps (weights + activations) in flight per wave
+  // 32-wide steps (weights + activations) in flight per wave
   constexpr int kDepth = MB <= 2 ? 4 : 2;
   constexpr int XW = XF32 ? 2 : 1;   // raw 16-byte words per activation row chunk
   constexpr int GW = NORM ? (GF32 ? 2 : 1) : 1;
   struct Stage {
-    u32x2 w[8];
+    u32x4 w;
     u32x4 x[MB][XW];
     u32x4 g[GW];
   };
@@ -196,18 +184,17 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
   // every load below is unconditional (rows clamped, pointers selected), so
   // the compiler's wait counts stay exact across the prefetch ring
   const void *gsrc = has_gamma ? a.gamma : sg.X;
+  const uint16_t *w1 = sg.W + static_cast<size_t>(wrow) * a.K + 8 * grp;
+  const uint16_t *w2 = PAIRED ? sg.W2 + static_cast<size_t>(wrow) * a.K2 + 8 * grp : w1;
   auto load_stage = [&](Stage &sb, int st) {
-    int krow = st * 32;
-    const bool second = PAIRED && krow >= a.K;
-    const uint16_t *W = second ? sg.W2 : sg.W;
+    int k = st * 32;
+    const bool second = PAIRED && k >= a.K;
     const void *X = second ? sg.X2 : sg.X;
     const int ldx = second ? sg.ldx2 : sg.ldx;
-    krow -= second ? a.K : 0;
-    const uint16_t *p = W + static_cast<size_t>(krow + 8 * grp) * ldw + n0 + 4 * j;
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-      sb.w[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p + r * ldw));
-    const int k = krow + 8 * grp;
+    k -= second ? a.K : 0;
+    const uint16_t *wp = (second ? w2 : w1) + k;
+    sb.w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wp));
+    k += 8 * grp;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) load_x_raw<XF32>(X, ldx, min(mb * 16 + j, a.M - 1), k, sb.x[mb]);
     if constexpr (NORM) {
@@ -224,16 +211,12 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
   // activation operand is zeroed (a select, not a branch), so the loop body
   // stays branch-free and the compiler's wait counts stay exact.
   auto compute = [&](const Stage &sb, int st, bool valid) {
-    u32x4 b[4];
-    transpose84(sb.w, b);
     if (PAIRED && st * 32 >= a.K) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         u32x4 x = sb.x[mb][0];
         if (!valid || mb * 16 + j >= a.M) x = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc[HALVES - 1][mb][e] = mfma_bf16(x, b[e], acc[HALVES - 1][mb][e]);
+        acc[HALVES - 1][mb] = mfma_bf16(sb.w, x, acc[HALVES - 1][mb]);
       }
     } else {
 #pragma unroll
@@ -242,8 +225,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
         u32x4 x = make_x<XF32, NORM, GF32>(sb.x[mb], sb.g, has_gamma, sq);
         ssq[mb] += valid ? sq : 0.f;
         if (!valid || mb * 16 + j >= a.M) x = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[0][mb][e] = mfma_bf16(x, b[e], acc[0][mb][e]);
+        acc[0][mb] = mfma_bf16(sb.w, x, acc[0][mb]);
       }
     }
   };
@@ -287,48 +269,44 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
       if (grp == 0) ssq_w[wave][mb * 16 + j] = v;
     }
   }
-
-  // fixed-order sum of the four waves: red[reg][lane]
-  for (int w = 0; w < kWaves; ++w) {
-    if (wave == w) {
+  // per-wave sums -> LDS, then a fixed-order sum over the waves:
+  // red[(acc * 4 + r) * 64 + lane]
 #pragma unroll
-      for (int h = 0; h < HALVES; ++h)
+  for (int h = 0; h < HALVES; ++h)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
+      for (int r = 0; r < 4; ++r) wsum[wave][((h * MB + mb) * 4 + r) * 64 + lane] = acc[h][mb][r];
+  __syncthreads();
+  for (int idx = tid; idx < RED; idx += kThreads) {
+    float v = wsum[0][idx];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int reg = ((h * MB + mb) * 4 + e) * 4 + i;
-              const float prev = w == 0 ? 0.f : red[reg * 64 + lane];
-              red[reg * 64 + lane] = prev + acc[h][mb][e][i];
-            }
-    }
-    __syncthreads();
+    for (int w = 1; w < kWaves; ++w) v += wsum[w][idx];
+    red[idx] = v;
   }
   if constexpr (NORM) {
     for (int m = tid; m < MB * 16; m += kThreads) {
       float v = 0.f;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) v += ssq_w[w][m];
-      red[NREG * 64 + m] = v;
+      red[RED + m] = v;
     }
-    __syncthreads();
   }
+  __syncthreads();
 
   if (a.ksplit > 1) {
-    float *mine = a.part + (static_cast<size_t>(strip) * a.ksplit + split) * PART;
+    float *mine = a.part + (static_cast<size_t>(tile) * a.ksplit + split) * PART;
     for (int i = tid; i < PART / 2; i += kThreads) store_coherent(mine + 2 * i, red[2 * i], red[2 * i + 1]);
     wait_memory();
     __syncthreads();
     if (tid == 0)
-      last_flag = __hip_atomic_fetch_add(&a.counters[strip], 1, __ATOMIC_RELAXED,
+      last_flag = __hip_atomic_fetch_add(&a.counters[tile], 1, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT) == a.ksplit - 1;
     __syncthreads();
     if (!last_flag) return;
     // eight partials in flight per thread (indices clamped, loads
     // unconditional), summed in split order
-    const float *base = a.part + static_cast<size_t>(strip) * a.ksplit * PART;
+    const float *base = a.part + static_cast<size_t>(tile) * a.ksplit * PART;
     const int ks = a.ksplit;
     for (int i = tid; i < PART / 2; i += kThreads) {
       float v0 = 0.f, v1 = 0.f;
@@ -348,63 +326,91 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
       red[2 * i] = v0;
       red[2 * i + 1] = v1;
     }
-    if (tid == 0) __hip_atomic_store(&a.counters[strip], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(&a.counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
   }
 
-  // epilogue: thread t writes column n0 + t % 64 of rows t / 64 + kWaves * q
-  const int nl = tid & 63;
-  const int n = n0 + nl;
+  // epilogue: thread t writes y[m = t / 4][n0 + 4q .. 4q+3], q = t % 4; the
+  // accumulator lane of (n0 + 4q + r, m) is 16q + m % 16, register r
+  const int m = tid >> 2, q = tid & 3;
+  if (m >= a.M) return;
+  const int n = n0 + 4 * q;
   if (n >= sg.N) return;
-  const int e = nl & 3, jj = nl >> 2;
+  const int mb = m >> 4, ln = 16 * q + (m & 15);
+  float v[4];
 #pragma unroll
-  for (int q = 0; q < (MB * 16 + kWaves - 1) / kWaves; ++q) {
-    const int m = (tid >> 6) + kWaves * q;
-    if (m >= a.M) break;
-    const int mb = m >> 4, g4 = (m & 15) >> 2, i = m & 3;
-    const int ln = 16 * g4 + jj;
-    float v = red[(((0 * MB + mb) * 4 + e) * 4 + i) * 64 + ln];
-    if constexpr (NORM) v *= rsqrtf(red[NREG * 64 + m] / static_cast<float>(a.K) + a.eps);
-    switch (sg.omode) {
-      case GV_OUT_BF16:
-        static_cast<uint16_t *>(sg.out)[static_cast<size_t>(m) * sg.ldo + n] = f2bf(v);
-        break;
-      case GV_OUT_F32:
-        static_cast<float *>(sg.out)[static_cast<size_t>(m) * sg.ldo + n] = v;
-        break;
-      case GV_OUT_CACHE: {
-        const int b = m / a.T, t = m - b * a.T;
-        const size_t row = static_cast<size_t>(b) * a.L_max + a.past[b] + t;
-        static_cast<uint16_t *>(sg.out)[row * sg.ldo + n] = f2bf(v);
-        break;
+  for (int r = 0; r < 4; ++r) v[r] = red[((0 * MB + mb) * 4 + r) * 64 + ln];
+  if constexpr (NORM) {
+    const float sc = rsqrtf(red[RED + m] / static_cast<float>(a.K) + a.eps);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] *= sc;
+  }
+  const size_t oi = static_cast<size_t>(m) * sg.ldo + n;
+  switch (sg.omode) {
+    case GV_OUT_BF16:
+      *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(sg.out) + oi) =
+          u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
+      break;
+    case GV_OUT_F32:
+      *reinterpret_cast<f32x4 *>(static_cast<float *>(sg.out) + oi) = f32x4{v[0], v[1], v[2], v[3]};
+      break;
+    case GV_OUT_CACHE: {
+      const int b = m / a.T, t = m - b * a.T;
+      const size_t row = static_cast<size_t>(b) * a.L_max + a.past[b] + t;
+      *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(sg.out) + row * sg.ldo + n) =
+          u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
+      break;
+    }
+    case GV_OUT_CACHE_T: {
+      const int b = m / a.T, t = m - b * a.T;
+      uint16_t *col = static_cast<uint16_t *>(sg.out) + static_cast<size_t>(b) * sg.N * a.L_max +
+                      a.past[b] + t;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) col[static_cast<size_t>(n + r) * a.L_max] = f2bf(v[r]);
+      break;
+    }
+    case GV_OUT_RES_F32: {
+      const size_t ri = static_cast<size_t>(m) * sg.ldr + n;
+      if (sg.res_f32) {
+        const f32x4 rr = *reinterpret_cast<const f32x4 *>(static_cast<const float *>(sg.R) + ri);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] += rr[r];
+      } else {
+        const u32x2 rr = *reinterpret_cast<const u32x2 *>(static_cast<const uint16_t *>(sg.R) + ri);
+        v[0] += bflo(rr.x);
+        v[1] += bfhi(rr.x);
+        v[2] += bflo(rr.y);
+        v[3] += bfhi(rr.y);
       }
-      case GV_OUT_RES_F32: {
-        const size_t ri = static_cast<size_t>(m) * sg.ldr + n;
-        v += sg.res_f32 ? static_cast<const float *>(sg.R)[ri]
-                        : bf2f(static_cast<const uint16_t *>(sg.R)[ri]);
-        static_cast<float *>(sg.out)[static_cast<size_t>(m) * sg.ldo + n] = v;
-        if (sg.out2) sg.out2[static_cast<size_t>(m) * sg.ldo + n] = v;
-        break;
-      }
-      case GV_OUT_RES_BF16:
-        v += static_cast<const float *>(sg.R)[static_cast<size_t>(m) * sg.ldr + n];
-        static_cast<uint16_t *>(sg.out)[static_cast<size_t>(m) * sg.ldo + n] = f2bf(v);
-        break;
-      default: {  // GV_OUT_SWIGLU
-        const float u = red[(((1 * MB + mb) * 4 + e) * 4 + i) * 64 + ln];
-        static_cast<uint16_t *>(sg.out)[static_cast<size_t>(m) * sg.ldo + n] = f2bf(silu(v) * u);
-        break;
-      }
+      const f32x4 o = f32x4{v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<f32x4 *>(static_cast<float *>(sg.out) + oi) = o;
+      if (sg.out2) *reinterpret_cast<f32x4 *>(sg.out2 + oi) = o;
+      break;
+    }
+    case GV_OUT_RES_BF16: {
+      const f32x4 rr = *reinterpret_cast<const f32x4 *>(static_cast<const float *>(sg.R) +
+                                                         static_cast<size_t>(m) * sg.ldr + n);
+      *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(sg.out) + oi) =
+          u32x2{pack2(v[0] + rr[0], v[1] + rr[1]), pack2(v[2] + rr[2], v[3] + rr[3])};
+      break;
+    }
+    default: {  // GV_OUT_SWIGLU
+      float u[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) u[r] = silu(v[r]) * red[((1 * MB + mb) * 4 + r) * 64 + ln];
+      *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(sg.out) + oi) =
+          u32x2{pack2(u[0], u[1]), pack2(u[2], u[3])};
+      break;
     }
   }
 }
 
 template <int MB, int XF32, int PAIRED, int NORM, int GF32>
 hipError_t launch_t(const GvArgs &a, int grid, hipStream_t s) {
-  if (a.waves == 8)
-    gemv_kernel<MB, XF32, PAIRED, NORM, GF32, 8><<<grid, 8 * 64, 0, s>>>(a);
-  else
+  if (a.waves == 4)
     gemv_kernel<MB, XF32, PAIRED, NORM, GF32, 4><<<grid, 4 * 64, 0, s>>>(a);
+  else
+    gemv_kernel<MB, XF32, PAIRED, NORM, GF32, 8><<<grid, 8 * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -426,33 +432,33 @@ int env_int(const char *name, int dflt) {
 }  // namespace
 
 size_t gemv_plan(GvArgs &a) {
-  int strips = 0;
+  int tiles = 0;
   for (int i = 0; i < a.nseg; ++i) {
-    a.seg[i].strip_begin = strips;
-    strips += (a.seg[i].N + kCols - 1) / kCols;
+    a.seg[i].tile_begin = tiles;
+    tiles += (a.seg[i].N + kRows - 1) / kRows;
   }
-  a.nstrips = strips;
+  a.ntiles = tiles;
   a.waves = env_int("DL_GEMV_WAVES", 4) == 8 ? 8 : 4;
   const int ksteps = (a.K + a.K2) / 32;
-  const int target = env_int("DL_GEMV_WGS", 128);
-  const int min_steps = env_int("DL_GEMV_MIN_STEPS", 16);
-  int ks = (target + strips - 1) / strips;
-  ks = std::min(ks, std::max(1, ksteps / min_steps));
+  // K splits: enough work items for about `target` workgroups, but at least
+  // `min_steps` steps per wave
+  const int target = env_int("DL_GEMV_WGS", 256);
+  const int min_steps = std::max(1, env_int("DL_GEMV_MIN_STEPS", 4));
+  int ks = (target + tiles - 1) / tiles;
+  ks = std::min(ks, std::max(1, ksteps / (min_steps * a.waves)));
   ks = std::max(1, std::min(ks, 64));
   const int sps = (ksteps + ks - 1) / ks;
   a.split_steps = sps;
   a.ksplit = (ksteps + sps - 1) / sps;
   const int MB = (a.M + 15) / 16;
   const int halves = a.K2 > 0 ? 2 : 1;
-  const size_t part = static_cast<size_t>(halves) * MB * 16 * 64 + MB * 16;
-  return a.ksplit > 1 ? part * a.nstrips * a.ksplit : 0;
+  const size_t part = static_cast<size_t>(halves) * MB * 4 * 64 + MB * 16;
+  return a.ksplit > 1 ? part * a.ntiles * a.ksplit : 0;
 }
-
-int gemv_counters(const GvArgs &a) { return a.nstrips; }
 
 hipError_t launch_gemv(const GvArgs &a, hipStream_t s) {
   TraceGuard trace_guard(K_GEMV_BF16, s);
-  const int items = a.nstrips * a.ksplit;
+  const int items = a.ntiles * a.ksplit;
   const int grid = (items + 7) / 8 * 8;
   const int mb = (a.M + 15) / 16;
   switch (mb) {

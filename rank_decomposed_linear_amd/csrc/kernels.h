@@ -9,23 +9,25 @@ namespace dl {
 
 // ---------------------------------------------------------------------------
 // Weight-streaming bf16 GEMV for small M (decode), M <= 64:
-// out_s = epilogue(X_s[M, K] W_s[K, N_s]) for up to three segments that
-// share M and K. Paired launches (K2 > 0) have one segment whose two halves
-// (X, W, K) and (X2, W2, K2) produce two results for the same output
-// columns, combined by the SwiGLU epilogue.
+// out_s = epilogue(X_s[M, K] W_s) for up to three segments that share M
+// and K. Every weight is stored transposed, Wt[N, K] row-major (the
+// reduction index contiguous). Paired launches (K2 > 0) have one segment
+// whose two halves (X, W, K) and (X2, W2, K2) produce two results for the
+// same output columns, combined by the SwiGLU epilogue.
 // ---------------------------------------------------------------------------
 enum GvOut : int {
   GV_OUT_BF16 = 0,      // out bf16 [m * ldo + n] = v
   GV_OUT_F32 = 1,       // out f32 [m * ldo + n] = v
   GV_OUT_CACHE = 2,     // out bf16 row (b * L_max + past[b] + t), m = b * T + t
+  GV_OUT_CACHE_T = 6,   // out bf16 [b][n][L_max] at column past[b] + t (rank-major cache)
   GV_OUT_RES_F32 = 3,   // out f32 = v + R (R f32 if res_f32, else bf16); out2 gets a copy
   GV_OUT_RES_BF16 = 4,  // out bf16 = v + R (R f32)
   GV_OUT_SWIGLU = 5     // paired: out bf16 = silu(v_first) * v_second
 };
 
 struct GvSeg {
-  const uint16_t *W;   // [K, N] bf16
-  const uint16_t *W2;  // paired: second half [K2, N]
+  const uint16_t *W;   // Wt [N, K] bf16
+  const uint16_t *W2;  // paired: second half Wt2 [N, K2]
   const void *X;       // [M, ldx] bf16 (or f32 with x_f32)
   const void *X2;      // paired: second-half activations, bf16 [M, ldx2]
   void *out;
@@ -33,7 +35,7 @@ struct GvSeg {
   const void *R;       // residual [M, ldr]
   int N, ldx, ldx2, ldo, ldr;
   int omode, res_f32;
-  int strip_begin;     // set by gemv_plan
+  int tile_begin;      // set by gemv_plan
 };
 
 struct GvArgs {
@@ -49,20 +51,21 @@ struct GvArgs {
   const int32_t *past;    // cache scatter (GV_OUT_CACHE)
   int T, L_max;
   // set by gemv_plan / the caller
-  int nstrips, ksplit, split_steps;
+  int ntiles, ksplit, split_steps;
   int waves;              // waves per workgroup (4 or 8)
   float *part;            // gemv_plan's return value in floats
-  int *counters;          // nstrips ints, zero before the launch (left zero after it)
+  int *counters;          // ntiles ints, zero before the launch (left zero after it)
 };
 
-// Chooses the K split and strip numbering; returns the partial-sum floats
+// Chooses the K split and tile numbering; returns the partial-sum floats
 // the launch needs (0 when there is no split).
 size_t gemv_plan(GvArgs &a);
 hipError_t launch_gemv(const GvArgs &a, hipStream_t s);
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA GEMM for large M (prefill): C_s[M, N_s] = X_s[M, K] W_s[K, N_s]
-// with a per-launch epilogue. Up to three segments.
+// bf16 MFMA GEMM for large M (prefill): C_s[M, N_s] = X_s[M, K] W_s with
+// W_s stored transposed, Wt[N_s, K] row-major; per-launch epilogue. Up to
+// three segments.
 // ---------------------------------------------------------------------------
 enum GemmX : int {
   GEMM_X_BF16 = 0,     // X bf16 [M, ldx]
@@ -72,11 +75,12 @@ enum GemmOut : int {
   GEMM_OUT_BF16 = 0,        // C bf16 [M, ldc]
   GEMM_OUT_BF16_RES_F32 = 1,// C bf16 = acc + R (f32 [M, ldr]); also C32 (f32) if non-null
   GEMM_OUT_F32_RES_BF16 = 2,// C32 f32 = acc + R (bf16 [M, ldr])
-  GEMM_OUT_CACHE = 3        // C bf16 rows scattered: row b*T+t -> cache[b, past[b]+t]
+  GEMM_OUT_CACHE = 3,       // C bf16 rows scattered: row b*T+t -> cache[b, past[b]+t]
+  GEMM_OUT_CACHE_T = 4      // C bf16 columns: row b*T+t, column n -> cache[b, n, past[b]+t]
 };
 
 struct GemmSeg {
-  const uint16_t *W;  // [K, N]
+  const uint16_t *W;  // Wt [N, K]
   const uint16_t *X;  // [M, ldx]
   const uint16_t *X2; // SwiGLU partner
   void *C;            // output
@@ -102,35 +106,33 @@ int gemm_ntiles(int N);
 // ---------------------------------------------------------------------------
 // Attention over the low-rank cache (bf16 MFMA).
 // ---------------------------------------------------------------------------
-// Rearranges an up factor B[r, n_kv*d] into MFMA operand order:
-// packed[g][r/32][d/16][lane][8], lane = 16*grp + c holds
-// B[32*rs + 8*grp + e][g*d + 16*blk + c], e = 0..7.
-hipError_t launch_pack_up_factor(const uint16_t *B, uint16_t *packed, int r, int n_kv, int d,
-                                 hipStream_t s);
-
 struct AttnDecodeArgs {
   const void *q;       // [Bsz, n_q, d] bf16 or f32 (q_f32)
-  const uint16_t *ck, *cv;
-  const uint16_t *bk, *bv;  // up factors, row-major [r, n_kv * d]
+  const uint16_t *ck;  // [Bsz, L_max, r_k]
+  const uint16_t *cv;  // rank-major [Bsz, r_v, L_max]
+  const uint16_t *bk, *bv;  // up factors stored transposed: [n_kv * d, r]
   const int32_t *ctx_lens;
   void *out;           // [Bsz, n_q, d] bf16 (or f32 with out_f32)
-  float *part;         // [Bsz, n_q, nsplit, d + 2] split partials (nsplit > 1)
+  float *part;         // [Bsz, n_kv, nsplit, 16, d + 2] split partials (nsplit > 1)
   int *counters;       // [Bsz * n_kv], zero on entry, left zero
   int Bsz, n_q, n_kv, d, r_k, r_v, L_max;
   int ctx_offset;      // context of sequence b = ctx_lens[b] + ctx_offset
   int nsplit, split_len;  // context positions per split (multiple of attn_decode_split_granule())
+  // set by the launcher (LDS plan)
+  int rs_cap, pitch, lds_bs, lds_s;
   float scale_log2;    // sm_scale * log2(e)
   float theta;
   int q_f32, out_f32;
 };
-int attn_decode_positions_per_tile();
 int attn_decode_split_granule();
+int attn_decode_max_rank_v();   // largest r_v the decode kernel accepts
 hipError_t launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s);
 
 struct AttnPrefillArgs {
   const void *q;       // [Bsz, T, n_q, d] bf16 or f32
-  const uint16_t *ck, *cv;
-  const uint16_t *bk_packed, *bv_packed;
+  const uint16_t *ck;  // [Bsz, L_max, r_k]
+  const uint16_t *cv;  // rank-major [Bsz, r_v, L_max]
+  const uint16_t *bk, *bv;  // [n_kv * d, r]
   const int32_t *past_lens;
   uint16_t *out;       // [Bsz, T, n_q*d]
   int Bsz, T, n_q, n_kv, d, r_k, r_v, L_max;
@@ -147,11 +149,12 @@ hipError_t launch_attn_prefill_bf16(const AttnPrefillArgs &a, hipStream_t s);
 enum F32Out : int {
   F32_OUT_STORE = 0,     // C = acc
   F32_OUT_RESID = 1,     // C = acc + R
-  F32_OUT_CACHE = 2      // row b*T+t -> cache[b, past[b]+t]
+  F32_OUT_CACHE = 2,     // row b*T+t -> cache[b, past[b]+t]
+  F32_OUT_CACHE_T = 3    // row b*T+t, column n -> cache[b, n, past[b]+t]
 };
 struct GemmF32Args {
   const float *X, *X2;   // X2 non-null: X = silu(X) * X2
-  const float *W;
+  const float *W;        // Wt [N, K]
   float *C;
   const float *R;
   int M, N, K, ldx, ldc, ldr;
@@ -163,7 +166,9 @@ hipError_t launch_gemm_f32(const GemmF32Args &a, hipStream_t s);
 
 struct AttnF32Args {
   const float *q;      // [Bsz, T, n_q, d], token stride ldq
-  const float *ck, *cv, *bk, *bv;
+  const float *ck;     // [Bsz, L_max, r_k]
+  const float *cv;     // [Bsz, r_v, L_max]
+  const float *bk, *bv;  // [n_kv * d, r]
   const int32_t *lens; // decode: ctx_lens; prefill: past_lens
   float *out;          // [Bsz, T, n_q*d]
   int decode;          // 1: query position lens[b]-1 (T == 1)
@@ -190,10 +195,5 @@ struct FillRegion {
 hipError_t launch_fill(const FillRegion *r, int nreg, hipStream_t s);
 // dst (bf16 or f32) = src f32
 hipError_t launch_convert_f32(const float *src, void *dst, int dst_bf16, int64_t n, hipStream_t s);
-// cache[b, past[b] + t, :] = row b*T + t of an f32 [Bsz*T, ld] matrix
-// (columns [0, r)), converted to the cache dtype.
-hipError_t launch_store_cache_rows(const float *src, int ld, void *cache, int cache_bf16,
-                                   const int32_t *past, int Bsz, int T, int r, int L_max,
-                                   hipStream_t s);
 
 }  // namespace dl

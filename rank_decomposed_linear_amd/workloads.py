@@ -156,9 +156,10 @@ class Workload:
 
     @property
     def l_max(self) -> int:
-        if self.phase == "decode":
-            return self.context + 1
-        return self.prefill + self.decode_steps
+        """Cache capacity per sequence: the rows the workload fills, rounded
+        up to whole 64-row pages."""
+        rows = self.context + 1 if self.phase == "decode" else self.prefill + self.decode_steps
+        return (rows + 63) // 64 * 64
 
 
 def _llama3_8b(pct):
@@ -310,6 +311,27 @@ def factor_pair_flops(shape: LayerShape, tokens: int) -> Dict[str, int]:
     """2*M*(m*k + k*n) per projection pair for M tokens."""
     return {p: 2 * tokens * (m * shape.rank(p) + shape.rank(p) * n)
             for p, (m, n) in shape.shapes().items()}
+
+
+# ----------------------------------------------------------------------------
+# Library storage order (data movement only)
+# ----------------------------------------------------------------------------
+def to_library_factor(a: np.ndarray) -> np.ndarray:
+    """A factor in the row-vector convention (A [m, k] or B [k, n]) -> the
+    library's storage, its transpose, whose rows run along the reduction
+    index."""
+    return np.ascontiguousarray(np.swapaxes(a, -1, -2))
+
+
+def to_library_value_cache(cv: np.ndarray) -> np.ndarray:
+    """Value latents [Bsz, L, r_v] -> the library's rank-major cache
+    [Bsz, r_v, L]."""
+    return np.ascontiguousarray(np.swapaxes(cv, -1, -2))
+
+
+def from_library_value_cache(cv_t: np.ndarray) -> np.ndarray:
+    """Inverse of to_library_value_cache."""
+    return np.ascontiguousarray(np.swapaxes(cv_t, -1, -2))
 
 
 def random_array(rng: np.random.Generator, shape, std: float, dtype: str) -> np.ndarray:

@@ -7,7 +7,9 @@ compared separately, so the residual stream cannot hide an error, and the
 appended cache rows are compared too. Tolerance as in test_gpu_ops.
 Full-size decode configurations compare a sample of sequences (each
 sequence's output depends only on its own rows); the prefill configuration
-compares sequence 0 in full."""
+compares sequence 0 in full. Inputs are uploaded in the library's storage
+order (factors transposed, value cache rank-major) and the value cache is
+read back into the oracle's [Bsz, L, r_v] order before comparing."""
 import numpy as np
 import pytest
 
@@ -30,7 +32,8 @@ def B():
 
 def make_gpu_layer(B, weights: W.LayerWeights):
     shp = weights.shape
-    facs = {p: (to_dev(a), to_dev(b)) for p, (a, b) in weights.factors.items()}
+    facs = {p: (to_dev(W.to_library_factor(a)), to_dev(W.to_library_factor(b)))
+            for p, (a, b) in weights.factors.items()}
     return B.DecomposedLayer(facs, shp.hidden, shp.n_q, shp.n_kv, shp.head_dim, shp.ffn,
                              shp.rope_theta, shp.rms_eps)
 
@@ -70,7 +73,7 @@ def check_step(dt, x, y_dev, x2_dev, ck_dev, cv_dev, want, past, T, seqs=None):
         "mlp_delta": delta_err(y - x2, want["y"] - want["x2"], smax, dt),
         "y": relerr(y, want["y"]),
     }
-    gk, gv = to_host(ck_dev)[sl], to_host(cv_dev)[sl]
+    gk, gv = to_host(ck_dev)[sl], W.from_library_value_cache(to_host(cv_dev))[sl]
     pst = np.asarray(past)[sl]
     for i in range(len(pst)):
         rows = slice(pst[i], pst[i] + T)
@@ -96,8 +99,8 @@ SMALL = [
     # (name, dtype, hidden, n_q, n_kv, d, ffn, rank_attn, rank_kv, rank_mlp, Bsz, T, past, L_max, theta)
     ("gemv_decode", "bf16", 512, 8, 2, 128, 1024, 192, 128, 256, 4, 1, [0, 7, 100, 33], 128, 500000.0),
     ("gemv_prefill", "bf16", 256, 4, 2, 64, 512, 128, 64, 192, 2, 8, [0, 20], 40, 10000.0),
-    ("gemm_prefill", "bf16", 512, 8, 2, 128, 768, 256, 128, 320, 2, 100, [0, 20], 130, 10000.0),
-    ("gemm_decode_b80", "bf16", 256, 4, 1, 64, 512, 128, 64, 128, 80, 1, None, 30, 10000.0),
+    ("gemm_prefill", "bf16", 512, 8, 2, 128, 768, 256, 128, 320, 2, 100, [0, 20], 136, 10000.0),
+    ("gemm_decode_b80", "bf16", 256, 4, 1, 64, 512, 128, 64, 128, 80, 1, None, 32, 10000.0),
     ("f32_prefill", "f32", 96, 4, 2, 16, 160, 24, 12, 40, 3, 6, [0, 2, 9], 20, 100.0),
     ("f32_decode", "f32", 96, 6, 3, 16, 160, 24, 12, 40, 3, 1, [0, 2, 9], 20, 100.0),
 ]
@@ -120,7 +123,7 @@ def test_small_layer(B, case):
     ck0 = rand(r, (Bsz, L_max, rkv), 1.0, dt)
     cv0 = rand(r, (Bsz, L_max, rkv), 1.0, dt)
     layer = make_gpu_layer(B, weights)
-    ck, cv = to_dev(ck0), to_dev(cv0)
+    ck, cv = to_dev(ck0), to_dev(W.to_library_value_cache(cv0))
     y, x2 = run_layer(B, layer, x, ck, cv, past)
     want = oracle_layer(weights, x, ck0, cv0, past)
     check_step(dt, x, y, x2, ck, cv, want, past, T)
@@ -136,7 +139,7 @@ def test_tiny_chain_prefill_then_decode(B):
     w = W.TINY
     weights, inp = W.draw(w)
     layer = make_gpu_layer(B, weights)
-    ck, cv = to_dev(inp.ck), to_dev(inp.cv)
+    ck, cv = to_dev(inp.ck), to_dev(W.to_library_value_cache(inp.cv))
     ck_ref, cv_ref = f64(inp.ck), f64(inp.cv)
     past = np.zeros(w.batch, np.int32)
     steps = [inp.x] + [inp.decode_x[s] for s in range(w.decode_steps)]
@@ -156,7 +159,7 @@ def test_tiny_chain_prefill_then_decode(B):
 def _decode_config(B, w, seqs):
     weights, inp = W.draw(w)
     layer = make_gpu_layer(B, weights)
-    ck, cv = to_dev(inp.ck), to_dev(inp.cv)
+    ck, cv = to_dev(inp.ck), to_dev(W.to_library_value_cache(inp.cv))
     y, x2 = run_layer(B, layer, inp.x, ck, cv, inp.past_lens)
     want = oracle_layer(weights, inp.x, inp.ck, inp.cv, inp.past_lens, seqs)
     return check_step("bf16", inp.x, y, x2, ck, cv, want, inp.past_lens, 1, seqs)
@@ -183,7 +186,7 @@ def test_llama3_70b_c50_prefill(B):
     w = W.LLAMA3_70B_C50_PREFILL
     weights, inp = W.draw(w)
     layer = make_gpu_layer(B, weights)
-    ck, cv = to_dev(inp.ck), to_dev(inp.cv)
+    ck, cv = to_dev(inp.ck), to_dev(W.to_library_value_cache(inp.cv))
     y, x2 = run_layer(B, layer, inp.x, ck, cv, inp.past_lens)
     want = oracle_layer(weights, inp.x, inp.ck, inp.cv, inp.past_lens, np.array([0]))
     check_step("bf16", inp.x, y, x2, ck, cv, want, inp.past_lens, w.prefill, np.array([0]))

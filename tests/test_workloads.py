@@ -57,8 +57,24 @@ def test_draws_are_seeded_and_shaped():
     A, B = a_w.factors["gate"]
     assert A.shape == (256, 64) and B.shape == (64, 688) and A.dtype == np.float32
     assert a_in.x.shape == (2, 32, 256) and a_in.decode_x.shape == (8, 2, 1, 256)
-    assert a_in.ck.shape == (2, 40, 64)
+    # 32 prefill + 8 decode rows, rounded up to a 64-row page
+    assert a_in.ck.shape == (2, 64, 64) and W.TINY.l_max == 64
+    assert W.LLAMA3_8B_C40_DECODE.l_max == 1088
     assert abs(float(np.std(A)) - 0.02) < 0.002
+
+
+def test_library_storage_order():
+    """Factors are stored transposed, the value cache rank-major; both are
+    pure data movement and invertible."""
+    a = np.arange(6 * 4, dtype=np.float32).reshape(6, 4)     # A [m=6, k=4]
+    t = W.to_library_factor(a)
+    assert t.shape == (4, 6) and t.flags["C_CONTIGUOUS"]
+    assert t[3, 5] == a[5, 3]
+    cv = np.arange(2 * 5 * 3, dtype=np.float32).reshape(2, 5, 3)  # [Bsz, L, r_v]
+    c = W.to_library_value_cache(cv)
+    assert c.shape == (2, 3, 5) and c.flags["C_CONTIGUOUS"]
+    assert c[1, 2, 4] == cv[1, 4, 2]
+    assert np.array_equal(W.from_library_value_cache(c), cv)
 
 
 def test_b_row_decay_scaling():
