@@ -132,7 +132,7 @@ def make_sets(torch, binding, weights, inp, nsets):
         facs = {p: (to_dev(torch, lf(a)), to_dev(torch, lf(b))) for p, (a, b) in weights.factors.items()}
         layer = binding.DecomposedLayer(facs, shp.hidden, shp.n_q, shp.n_kv, shp.head_dim, shp.ffn,
                                         shp.rope_theta, shp.rms_eps)
-        st = dict(layer=layer, x=to_dev(torch, inp.x), ck=to_dev(torch, inp.ck),
+        st = dict(layer=layer, x=to_dev(torch, inp.x), ck=to_dev(torch, W.to_library_key_cache(inp.ck)),
                   cv=to_dev(torch, W.to_library_value_cache(inp.cv)),
                   past=to_dev(torch, inp.past_lens))
         st["y"] = torch.empty_like(st["x"])

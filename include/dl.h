@@ -24,7 +24,16 @@
  *   - Latent caches: the key cache Ck is [Bsz, L_max, r_k] (one row per
  *     position); the value cache Cv is rank-major, [Bsz, r_v, L_max] (one
  *     row per rank component), because attention reduces the value latents
- *     over positions. DL_BF16 attention needs L_max % 8 == 0.
+ *     over positions.
+ *   - DL_BF16 operand tiles: with DL_BF16 every factor matrix above (At, Bt,
+ *     B_k^T, B_v^T) and each sequence's cache matrix ([L_max, r_k] and
+ *     [r_v, L_max]) is stored in 16 x 32 tiles of 1 KB, in MFMA operand
+ *     order: element (r, c) of an [R, C] matrix sits at element offset
+ *       ((r / 16) * (C / 32) + c / 32) * 512
+ *         + (((c % 32) / 8) * 16 + r % 16) * 8 + c % 8
+ *     (R % 16 == 0, C % 32 == 0; so DL_BF16 caches need L_max % 32 == 0).
+ *     Every operand fragment the kernels read is then one contiguous 1 KB
+ *     block. DL_F32 tensors are plain row-major.
  *   - dtype DL_F32: every tensor is float32 and arithmetic is float32.
  *     dtype DL_BF16: activations, factors, caches and outputs are bfloat16,
  *     products accumulate in float32; intermediates may be rounded to bf16.

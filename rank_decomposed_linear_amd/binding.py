@@ -9,7 +9,9 @@ functions raise; there is no fallback.
 Storage order is the library's (include/dl.h): every factor is passed
 transposed (At = A^T [k, m], Bt = B^T [n, k]; up factors B_k^T, B_v^T
 [n_kv * d, r]), the key cache is [Bsz, L_max, r_k] and the value cache is
-rank-major, [Bsz, r_v, L_max].
+rank-major, [Bsz, r_v, L_max]; for bf16 each of these matrices is stored in
+16 x 32 operand tiles (workloads.tile_operands gives the order). Shapes are
+read from the tensors, which keep the logical shapes above.
 """
 from __future__ import annotations
 

@@ -122,6 +122,14 @@ GvSeg gvseg(const void *W, const void *X, int ldx, void *out, int ldo, int N, in
   return g;
 }
 
+// Segment whose activations are operand-tiled bf16 ([Mpad, K], ldx = K).
+GvSeg gvseg_t(const void *W, const void *X, int K, void *out, int ldo, int N, int omode) {
+  return gvseg(W, X, K, out, ldo, N, omode);
+}
+
+// rows of an operand-tiled activation buffer
+size_t mpad(int64_t M) { return static_cast<size_t>((M + 15) / 16 * 16); }
+
 GvArgs gvargs(int M, int K, int nseg) {
   GvArgs a{};
   a.M = M;
@@ -251,8 +259,8 @@ dl_status check_attn_shape(int64_t n_q, int64_t n_kv, int64_t d, int64_t r_k, in
              "bf16 attention needs r_k, r_v multiples of 64");
     DL_CHECK(r_v <= attn_decode_max_rank_v(), DL_ERR_UNSUPPORTED,
              "bf16 attention needs r_v <= %d", attn_decode_max_rank_v());
-    DL_CHECK(L_max % 8 == 0, DL_ERR_UNSUPPORTED,
-             "bf16 attention needs L_max to be a multiple of 8 (16-byte value cache rows)");
+    DL_CHECK(L_max % 32 == 0, DL_ERR_UNSUPPORTED,
+             "bf16 caches need L_max to be a multiple of 32 (operand tiles)");
     DL_CHECK(L_max * std::max(r_k, r_v) < ((int64_t)1 << 31), DL_ERR_UNSUPPORTED,
              "bf16 attention needs L_max * r < 2^31 per sequence");
     const int64_t G = n_q / n_kv;
@@ -270,9 +278,9 @@ dl_status check_attn_shape(int64_t n_q, int64_t n_kv, int64_t d, int64_t r_k, in
 // decode, w.counters must be zero.
 hipError_t run_attn_bf16(const void *q, int q_f32, int ldq, const void *Ck, const void *Cv,
                          const void *B_k, const void *B_v, const int32_t *lens, int ctx_offset,
-                         bool decode, void *out, int out_f32, int Bsz, int T, int n_q, int n_kv,
-                         int d, int r_k, int r_v, int L_max, float sm_scale, float theta,
-                         const AttnWS &w, hipStream_t s) {
+                         bool decode, void *out, int out_f32, int out_tiled, int Bsz, int T,
+                         int n_q, int n_kv, int d, int r_k, int r_v, int L_max, float sm_scale,
+                         float theta, const AttnWS &w, hipStream_t s) {
   const float scale = (sm_scale != 0.f ? sm_scale : 1.0f / sqrtf(static_cast<float>(d))) * kLog2e;
   if (decode) {
     const DecodePlan p = plan_decode(Bsz, n_kv, L_max);
@@ -287,6 +295,7 @@ hipError_t run_attn_bf16(const void *q, int q_f32, int ldq, const void *Ck, cons
     a.ctx_offset = ctx_offset;
     a.out = out;
     a.out_f32 = out_f32;
+    a.out_tiled = out_tiled;
     a.part = w.part;
     a.counters = w.counters;
     a.Bsz = Bsz;
@@ -358,10 +367,12 @@ const char *dl_role_name(int32_t role) {
 // GEMV-path plan of the factor pair (shapes only; pointers are filled in later).
 static void linear_gemvs(int M, int m, int k, int n, const void *x, const void *A, const void *B,
                          void *t, void *y, GvArgs &g1, GvArgs &g2) {
+  // the rank-k intermediate stays in operand tiles between the two passes
   g1 = gvargs(M, m, 1);
-  g1.seg[0] = gvseg(A, x, m, t, k, k, GV_OUT_BF16);
+  g1.seg[0] = gvseg(A, x, m, t, k, k, GV_OUT_TILED);
   g2 = gvargs(M, k, 1);
-  g2.seg[0] = gvseg(B, t, k, y, n, n, GV_OUT_BF16);
+  g2.x_tiled = 1;
+  g2.seg[0] = gvseg_t(B, t, k, y, n, n, GV_OUT_BF16);
 }
 
 size_t dl_lowrank_linear_workspace(int64_t M, int64_t m, int64_t k, int64_t n, dl_dtype dt) {
@@ -377,7 +388,7 @@ size_t dl_lowrank_linear_workspace(int64_t M, int64_t m, int64_t k, int64_t n, d
     sc.add(g2);
     c.take<int>(sc.counters);
     c.take<float>(sc.part_floats);
-    c.take<uint16_t>(static_cast<size_t>(M * k));
+    c.take<uint16_t>(mpad(M) * k);
   } else {
     c.take<uint16_t>(static_cast<size_t>(M * k));
   }
@@ -421,7 +432,7 @@ dl_status dl_lowrank_linear(const void *x, const void *A, const void *B, void *y
     sc.add(g2);
     int *counters = c.take<int>(sc.counters);
     float *part = c.take<float>(sc.part_floats);
-    uint16_t *t = c.take<uint16_t>(static_cast<size_t>(M * k));
+    uint16_t *t = c.take<uint16_t>(mpad(M) * k);
     linear_gemvs(Mi, mi, ki, ni, x, A, B, t, y, g1, g2);
     FillRegion z[1] = {{reinterpret_cast<float *>(counters), nullptr, 0, sc.counters}};
     DL_HIP(launch_fill(z, 1, s));
@@ -493,9 +504,12 @@ dl_status dl_lowrank_kv_append(const void *x, const void *A_k, const void *A_v, 
   DL_CHECK(T <= L_max, DL_ERR_INVALID_ARG, "T exceeds L_max");
   DL_CHECK(Bsz * T <= INT32_MAX / 2 && Bsz * L_max * std::max(r_k, r_v) <= ((int64_t)1 << 40),
            DL_ERR_UNSUPPORTED, "dims too large");
-  if (dt == DL_BF16)
+  if (dt == DL_BF16) {
     DL_CHECK(m % 64 == 0 && r_k % 64 == 0 && r_v % 64 == 0, DL_ERR_UNSUPPORTED,
              "bf16 append needs m, r_k, r_v multiples of 64");
+    DL_CHECK(L_max % 32 == 0, DL_ERR_UNSUPPORTED,
+             "bf16 caches need L_max to be a multiple of 32 (operand tiles)");
+  }
   DL_CHECK(aligned16(x) && aligned16(A_k) && aligned16(A_v) && aligned16(Ck) && aligned16(Cv) &&
                aligned16(past_lens),
            DL_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
@@ -616,7 +630,7 @@ static dl_status attn_common(const void *q, const void *Ck, const void *Cv, cons
     FillRegion z[1] = {{reinterpret_cast<float *>(aw.counters), nullptr, 0, aw.n_counters}};
     DL_HIP(launch_fill(z, 1, s));
   }
-  DL_HIP(run_attn_bf16(q, 0, static_cast<int>(n_q * d), Ck, Cv, B_k, B_v, lens, 0, decode, out, 0,
+  DL_HIP(run_attn_bf16(q, 0, static_cast<int>(n_q * d), Ck, Cv, B_k, B_v, lens, 0, decode, out, 0, 0,
                        static_cast<int>(Bsz), static_cast<int>(T), static_cast<int>(n_q),
                        static_cast<int>(n_kv), static_cast<int>(d), static_cast<int>(r_k),
                        static_cast<int>(r_v), static_cast<int>(L_max), sm_scale, rope_theta, aw, s));
@@ -727,18 +741,21 @@ static void layer_gemvs(const dl_layer *L, const LayerDims &D, const LayerWS &w,
   g[G_QKV].past = past;
   g[G_QKV].T = D.T;
   g[G_QKV].L_max = D.L_max;
-  g[G_QKV].seg[0] = gvseg(L->q.A, x, h, w.tq16, D.rq, D.rq, GV_OUT_BF16);
+  g[G_QKV].seg[0] = gvseg(L->q.A, x, h, w.tq16, D.rq, D.rq, GV_OUT_TILED);
   g[G_QKV].seg[1] = gvseg(L->k.A, x, h, Ck, D.rk, D.rk, GV_OUT_CACHE);
   g[G_QKV].seg[2] = gvseg(L->v.A, x, h, Cv, D.rv, D.rv, GV_OUT_CACHE_T);
 
   g[G_QUP] = gvargs(M, D.rq, 1);
-  g[G_QUP].seg[0] = gvseg(L->q.B, w.tq16, D.rq, w.q32, qd, qd, GV_OUT_F32);
+  g[G_QUP].x_tiled = 1;
+  g[G_QUP].seg[0] = gvseg_t(L->q.B, w.tq16, D.rq, w.q32, qd, qd, GV_OUT_F32);
 
   g[G_ODOWN] = gvargs(M, qd, 1);
-  g[G_ODOWN].seg[0] = gvseg(L->o.A, w.att16, qd, w.to16, D.ro, D.ro, GV_OUT_BF16);
+  g[G_ODOWN].x_tiled = D.T == 1;   // decode attention writes operand tiles, prefill rows
+  g[G_ODOWN].seg[0] = gvseg_t(L->o.A, w.att16, qd, w.to16, D.ro, D.ro, GV_OUT_TILED);
 
   g[G_OUP] = gvargs(M, D.ro, 1);
-  g[G_OUP].seg[0] = gvseg(L->o.B, w.to16, D.ro, w.x2f, h, h, GV_OUT_RES_F32);
+  g[G_OUP].x_tiled = 1;
+  g[G_OUP].seg[0] = gvseg_t(L->o.B, w.to16, D.ro, w.x2f, h, h, GV_OUT_RES_F32);
   g[G_OUP].seg[0].R = x;
   g[G_OUP].seg[0].ldr = h;
   g[G_OUP].seg[0].out2 = static_cast<float *>(x2_out);
@@ -749,21 +766,24 @@ static void layer_gemvs(const dl_layer *L, const LayerDims &D, const LayerWS &w,
   g[G_GUD].gamma = L->mlp_norm;
   g[G_GUD].gamma_f32 = gf32;
   g[G_GUD].eps = L->rms_eps;
-  g[G_GUD].seg[0] = gvseg(L->gate.A, w.x2f, h, w.tg16, D.rg, D.rg, GV_OUT_BF16);
-  g[G_GUD].seg[1] = gvseg(L->up.A, w.x2f, h, w.tu16, D.ru, D.ru, GV_OUT_BF16);
+  g[G_GUD].seg[0] = gvseg(L->gate.A, w.x2f, h, w.tg16, D.rg, D.rg, GV_OUT_TILED);
+  g[G_GUD].seg[1] = gvseg(L->up.A, w.x2f, h, w.tu16, D.ru, D.ru, GV_OUT_TILED);
 
   g[G_GUU] = gvargs(M, D.rg, 1);
   g[G_GUU].K2 = D.ru;
-  g[G_GUU].seg[0] = gvseg(L->gate.B, w.tg16, D.rg, w.H16, D.f, D.f, GV_OUT_SWIGLU);
+  g[G_GUU].x_tiled = 1;
+  g[G_GUU].seg[0] = gvseg_t(L->gate.B, w.tg16, D.rg, w.H16, D.f, D.f, GV_OUT_SWIGLU_TILED);
   g[G_GUU].seg[0].W2 = static_cast<const uint16_t *>(L->up.B);
   g[G_GUU].seg[0].X2 = w.tu16;
   g[G_GUU].seg[0].ldx2 = D.ru;
 
   g[G_DD] = gvargs(M, D.f, 1);
-  g[G_DD].seg[0] = gvseg(L->down.A, w.H16, D.f, w.td16, D.rd, D.rd, GV_OUT_BF16);
+  g[G_DD].x_tiled = 1;
+  g[G_DD].seg[0] = gvseg_t(L->down.A, w.H16, D.f, w.td16, D.rd, D.rd, GV_OUT_TILED);
 
   g[G_DU] = gvargs(M, D.rd, 1);
-  g[G_DU].seg[0] = gvseg(L->down.B, w.td16, D.rd, y, h, h, GV_OUT_RES_BF16);
+  g[G_DU].x_tiled = 1;
+  g[G_DU].seg[0] = gvseg_t(L->down.B, w.td16, D.rd, y, h, h, GV_OUT_RES_BF16);
   g[G_DU].seg[0].R = w.x2f;
   g[G_DU].seg[0].ldr = h;
 }
@@ -794,15 +814,17 @@ static void carve_layer(Carver &c, const LayerDims &D, const dl_layer *L, LayerW
     w.n_counters = sc.counters;
     w.counters = c.take<int>(sc.counters);
     w.part = c.take<float>(sc.part_floats);
-    w.tq16 = c.take<uint16_t>(M * D.rq);
+    // operand-tiled intermediates ([Mpad, cols], Mpad = M rounded up to 16)
+    const size_t Mp = mpad(D.M);
+    w.tq16 = c.take<uint16_t>(Mp * D.rq);
     w.q32 = c.take<float>(M * D.qd());
-    w.att16 = c.take<uint16_t>(M * D.qd());
-    w.to16 = c.take<uint16_t>(M * D.ro);
+    w.att16 = c.take<uint16_t>(Mp * D.qd());
+    w.to16 = c.take<uint16_t>(Mp * D.ro);
     w.x2f = c.take<float>(M * D.h);
-    w.tg16 = c.take<uint16_t>(M * D.rg);
-    w.tu16 = c.take<uint16_t>(M * D.ru);
-    w.H16 = c.take<uint16_t>(M * D.f);
-    w.td16 = c.take<uint16_t>(M * D.rd);
+    w.tg16 = c.take<uint16_t>(Mp * D.rg);
+    w.tu16 = c.take<uint16_t>(Mp * D.ru);
+    w.H16 = c.take<uint16_t>(Mp * D.f);
+    w.td16 = c.take<uint16_t>(Mp * D.rd);
     return;
   }
   w.a16 = c.take<uint16_t>(M * D.h);
@@ -937,8 +959,8 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
     DL_HIP(gemv_run(g[G_QUP], w.part, w.counters, s));
     set_role(R_ATTENTION);
     DL_HIP(run_attn_bf16(w.q32, 1, qd, Ck, Cv, L->k.B, L->v.B, past_lens, 1, D.T == 1, w.att16, 0,
-                         D.Bsz, D.T, D.nq, D.nkv, D.d, D.rk, D.rv, D.L_max, 0.f, L->rope_theta, aw,
-                         s));
+                         D.T == 1 ? 1 : 0, D.Bsz, D.T, D.nq, D.nkv, D.d, D.rk, D.rv, D.L_max, 0.f,
+                         L->rope_theta, aw, s));
     set_role(R_O_DOWN);
     DL_HIP(gemv_run(g[G_ODOWN], w.part, w.counters, s));
     set_role(R_O_UP);
@@ -995,7 +1017,7 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
     DL_HIP(launch_fill(z, 1, s));
     set_role(R_ATTENTION);
   }
-  DL_HIP(run_attn_bf16(w.q16, 0, qd, Ck, Cv, L->k.B, L->v.B, past_lens, 1, D.T == 1, w.att16, 0,
+  DL_HIP(run_attn_bf16(w.q16, 0, qd, Ck, Cv, L->k.B, L->v.B, past_lens, 1, D.T == 1, w.att16, 0, 0,
                        D.Bsz, D.T, D.nq, D.nkv, D.d, D.rk, D.rv, D.L_max, 0.f, L->rope_theta, aw,
                        s));
   {

@@ -2,11 +2,11 @@
 // rebuild K = C_k B_k and V = C_v B_v from the cached latents, rotate the
 // rebuilt keys, attend).
 //
-// Neither K nor V is ever written to memory. The key cache is streamed from
-// HBM with 16-byte loads; the value cache is stored rank-major ([Bsz, r_v,
-// L_max]) and gathered per key. The up factors are stored transposed,
-// [n_kv * d, r] (rank contiguous), so an MFMA operand fragment is one
-// 16-byte load per lane. The rebuilt tiles live in MFMA accumulators:
+// Neither K nor V is ever written to memory. Caches and factors are stored
+// in 16 x 32 operand tiles (MFMA lane order): a key block of 16 positions x
+// 32 ranks and an up-factor fragment are each one contiguous 1 KB read; the
+// value cache is rank-major ([r_v, L_max] tiles per sequence) and gathered
+// per key. The rebuilt tiles live in MFMA accumulators:
 //
 //  prefill  A workgroup owns one kv head and up to 256 (token, head) query
 //           rows; per 64-key tile its eight waves rebuild K (rotated) and
@@ -24,10 +24,10 @@ namespace {
 
 __device__ __forceinline__ u32x4 ld16(const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
-// operand fragment (rank step rs, d block blk) of an up factor stored
-// [n_kv * d, r]: lane (c, grp) gets B[32rs + 8grp .. +8][16blk + c]
-__device__ __forceinline__ u32x4 frag(const uint16_t *bt_g, int r, int rs, int blk, int lane) {
-  return ld16(bt_g + static_cast<size_t>(16 * blk + (lane & 15)) * r + 32 * rs + 8 * (lane >> 4));
+// operand fragment (rank step rs, d block blk of kv head g) of an up factor
+// stored [n_kv * d, r] in tiles: lane (c, grp) gets B[32rs + 8grp .. +8][16blk + c]
+__device__ __forceinline__ u32x4 frag(const uint16_t *bt, int r, int gblk, int rs, int lane) {
+  return ld16(bt + frag_off(gblk, rs, r, lane));
 }
 
 // ---------------------------------------------------------------------------
@@ -115,8 +115,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
   const int qmax_pos = past + min(t0 + QT, a.T) - 1;
   const int nkt = qmax_pos / KT + 1;
   const int rsk = a.r_k / 32, rsv = a.r_v / 32;
-  const uint16_t *bk_g = a.bk + static_cast<size_t>(g) * D * a.r_k;
-  const uint16_t *bv_g = a.bv + static_cast<size_t>(g) * D * a.r_v;
+  const uint16_t *ck_b = a.ck + static_cast<size_t>(b) * a.L_max * a.r_k;
   const uint16_t *cv_b = a.cv + static_cast<size_t>(b) * a.r_v * a.L_max;
   const int kb = wave >> 1;  // key block rebuilt by this wave
 
@@ -131,13 +130,15 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
 #pragma unroll
       for (int xi = 0; xi < NX; ++xi) acc[xi][0] = acc[xi][1] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int xbase = (wave & 1) * NX;
-      const uint16_t *cp = a.ck + (static_cast<size_t>(b) * a.L_max + keyrow) * a.r_k + 8 * grp;
+      // key tile of this 16-key block (lanes of keys past the last query
+      // position do not load)
+      const uint16_t *cp = ck_b + frag_off((k0 >> 4) + kb, 0, a.r_k, lane);
       for (int rs = 0; rs < rsk; ++rs) {
-        const u32x4 c = kvalid ? ld16(cp + rs * 32) : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 c = kvalid ? ld16(cp + 512 * rs) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int xi = 0; xi < NX; ++xi) {
-          acc[xi][0] = mfma_bf16(frag(bk_g, a.r_k, rs, xbase + xi, lane), c, acc[xi][0]);
-          acc[xi][1] = mfma_bf16(frag(bk_g, a.r_k, rs, xbase + xi + HALF, lane), c, acc[xi][1]);
+          acc[xi][0] = mfma_bf16(frag(a.bk, a.r_k, g * DB + xbase + xi, rs, lane), c, acc[xi][0]);
+          acc[xi][1] = mfma_bf16(frag(a.bk, a.r_k, g * DB + xbase + xi + HALF, rs, lane), c, acc[xi][1]);
         }
       }
       // lane (key = j, grp) holds K^T[16blk + 4grp + r][keyrow]
@@ -170,19 +171,17 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
 #pragma unroll
       for (int x = 0; x < HALF; ++x) acc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int nb0 = (wave & 1) * HALF;
-      // C_v[keyrow][32rs + 8grp + e], e = 0..7, gathered from the rank-major cache
-      const uint16_t *cp = cv_b + static_cast<size_t>(8 * grp) * a.L_max + min(keyrow, a.L_max - 1);
+      // C_v[keyrow][32rs + 8grp + e], e = 0..7, gathered from the value tiles
       for (int rs = 0; rs < rsv; ++rs) {
         u32x4 c = {0u, 0u, 0u, 0u};
         if (kvalid) {
-          const uint16_t *p = cp + static_cast<size_t>(32 * rs) * a.L_max;
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            c[q] = static_cast<uint32_t>(p[static_cast<size_t>(2 * q) * a.L_max]) |
-                   (static_cast<uint32_t>(p[static_cast<size_t>(2 * q + 1) * a.L_max]) << 16);
+            c[q] = static_cast<uint32_t>(cv_b[tile_off(32 * rs + 8 * grp + 2 * q, keyrow, a.L_max)]) |
+                   (static_cast<uint32_t>(cv_b[tile_off(32 * rs + 8 * grp + 2 * q + 1, keyrow, a.L_max)]) << 16);
         }
 #pragma unroll
-        for (int x = 0; x < HALF; ++x) acc[x] = mfma_bf16(c, frag(bv_g, a.r_v, rs, nb0 + x, lane), acc[x]);
+        for (int x = 0; x < HALF; ++x) acc[x] = mfma_bf16(c, frag(a.bv, a.r_v, g * DB + nb0 + x, rs, lane), acc[x]);
       }
       // lane (d = j, grp) holds V[16kb + 4grp + r][16(nb0+x) + j]
 #pragma unroll

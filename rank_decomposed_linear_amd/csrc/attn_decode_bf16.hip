@@ -11,31 +11,30 @@
 // Work item = (sequence b, kv head g, context split), one workgroup of four
 // waves (one per SIMD, so each wave has the whole register file for deep
 // software pipelining). Per work item:
-//  * B_k^T rows of head g (stored [n_kv * d, r_k], the rank contiguous) are
-//    loaded once into LDS in MFMA operand order, fragment (rank step rs,
-//    d block x) = 64 lanes x 16 bytes. Operand row i of block x holds
-//    dimension dim(x, i) = (d/2)(x / NE) + (d/32) i + x % NE, so the rotary
-//    partners d and d + d/2 land in the same lane and register. (Ranks too
-//    large for LDS are staged in rank chunks, reloaded per context slice.)
+//  * Factors and caches are stored in 16 x 32 operand tiles (1 KB, MFMA
+//    lane order): B_k^T / B_v^T as [n_kv * d, r], the key cache per
+//    sequence as [L_max, r_k], the value cache per sequence as
+//    [r_v, L_max]. Every operand fragment below is one contiguous 1 KB read.
+//  * The B_k^T tiles of head g are copied once into LDS, fragment (rank
+//    step rs, d block x) = dimensions 16x .. 16x+15. The rotary partner of
+//    dimension 16x + i is 16(x + d/32) + i: same lane, same register of the
+//    rebuilt keys. (Ranks too large for LDS are staged in rank chunks,
+//    reloaded per context slice.)
 //  * LDS is sized per launch: the resident factor first, then as long a
 //    context chunk as the rest of the 160 KB holds (scores and
 //    probabilities need 4 G + 32 bytes per position), so a split is
 //    normally walked in one chunk:
 //    phase 1: each wave rebuilds K^T for 64-position slices (A = factor
-//      fragment from LDS, read one rank step ahead; B = cache rows
-//      C_k[pos][32rs + 8g ..], one 16-byte load per lane and 16-position
-//      block, eight rank steps ahead), rotates the pairs in registers and
-//      forms S^T = K Q^T straight from the accumulators (the reduction slots
-//      of an operand may be any permutation shared by both operands).
-//      Scores go to LDS. Position of column j of block pb is
-//      32(pb/2) + 8(j/4) + 4(pb%2) + j%4, chosen so that the probabilities
-//      of 8 consecutive positions end up in one operand register set.
+//      fragment from LDS, read one rank step ahead; B = key-cache tile of
+//      16 positions, eight rank steps ahead), rotates the pairs in
+//      registers and forms S^T = K Q^T straight from the accumulators (the
+//      reduction slots of an operand may be any permutation shared by both
+//      operands). Scores go to LDS.
 //    softmax: chunk max per head, probabilities in bf16 operand order in
 //      LDS, running max / sum, rescale factor.
-//    phase 2: U^T[r][h] += C_v^T[r][pos] P^T[pos][h] with the value cache
-//      stored rank-major ([Bsz, r_v, L_max]), so every A operand is one
-//      16-byte load of 8 consecutive positions; each wave owns a set of
-//      16-row rank blocks. The loads start before the softmax barrier.
+//    phase 2: U^T[r][h] += C_v^T[r][pos] P^T[pos][h]; A = value-cache tile
+//      (16 ranks x 32 positions), each wave owns a set of 16-row rank
+//      blocks. The loads start before the softmax barrier.
 //  * O^T = B_v^T U^T on MFMA (U rounded to bf16), then the split's partial
 //    (O, max, sum) is merged by the last workgroup of (b, g) to finish
 //    (device-coherent partials, one counter atomic per workgroup).
@@ -99,15 +98,8 @@ struct Tile {
   static constexpr int NE = CPL;       // operands per column group
   static constexpr int NB = 2 * NE;    // 16-wide d blocks
   static constexpr int HALF = D / 2;
-  __device__ static constexpr int dim(int blk, int row) {
-    return HALF * (blk / NE) + CPL * row + (blk % NE);
-  }
+  __device__ static constexpr int dim(int blk, int row) { return 16 * blk + row; }
 };
-
-// offset of column j of 16-position block pb within a 64-position slice
-__device__ __forceinline__ int slice_pos(int pb, int j) {
-  return 32 * (pb >> 1) + 8 * (j >> 2) + 4 * (pb & 1) + (j & 3);
-}
 
 template <int D, int RBW>
 __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs a) {
@@ -147,14 +139,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
   const int n_rchunks = (nrs + rs_cap - 1) / rs_cap;
   const int nrb = a.r_v / 16;
   const int pitch = a.pitch;   // positions per chunk, a multiple of the slice
-  const uint16_t *bk_g = a.bk + static_cast<size_t>(g) * D * a.r_k;
   const uint16_t *cv_b = a.cv + static_cast<size_t>(b) * a.r_v * a.L_max;
   const uint16_t *ck_b = a.ck + static_cast<size_t>(b) * a.L_max * a.r_k;
 
   // up-factor fragments of rank steps [rs0, rs0 + cnt) -> bs[rs - rs0][x][lane][8]
   auto factor_src = [&](int rs0, int u) {
     const int ln = u & 63, x = (u >> 6) % NB, rs = (u >> 6) / NB;
-    return bk_g + static_cast<size_t>(T::dim(x, ln & 15)) * a.r_k + 32 * (rs0 + rs) + 8 * (ln >> 4);
+    return a.bk + frag_off(g * NB + x, rs0 + rs, a.r_k, ln);
   };
   auto load_factor = [&](int rs0, int cnt) {
     const int units = cnt * NB * 64;
@@ -242,10 +233,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
       for (int x = 0; x < NB; ++x)
 #pragma unroll
         for (int pb = 0; pb < kNP; ++pb) acc[x][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      // element offsets within the sequence's cache (L_max * r < 2^31)
+      // key tiles of the slice's 16-position blocks (element offsets within
+      // the sequence's cache, L_max * r < 2^31); blocks past the chunk end
+      // repeat its last block and their scores are masked
       int crow[kNP];
 #pragma unroll
-      for (int pb = 0; pb < kNP; ++pb) crow[pb] = min(P0 + slice_pos(pb, j), c1 - 1) * a.r_k + 8 * grp;
+      for (int pb = 0; pb < kNP; ++pb)
+        crow[pb] = static_cast<int>(frag_off(min((P0 >> 4) + pb, (c1 - 1) >> 4), 0, a.r_k, lane));
       for (int rc = 0; rc < n_rchunks; ++rc) {
         const int rs0 = rc * rs_cap, cnt = min(rs_cap, nrs - rs0);
         if (n_rchunks > 1) {
@@ -261,7 +255,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
 #pragma unroll
           for (int d = 0; d < kCDepth; ++d) {
 #pragma unroll
-            for (int pb = 0; pb < kNP; ++pb) cf[d][pb] = ld16(ck_b + crow[pb] + 32 * (rs0 + min(d, cnt - 1)));
+            for (int pb = 0; pb < kNP; ++pb) cf[d][pb] = ld16(ck_b + crow[pb] + 512 * (rs0 + min(d, cnt - 1)));
             __builtin_amdgcn_sched_barrier(0);
           }
           u32x4 bop[2][NB];
@@ -287,20 +281,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
               __builtin_amdgcn_sched_barrier(0);
               const int sn = rs0 + min(s + kCDepth, cnt - 1);
 #pragma unroll
-              for (int pb = 0; pb < kNP; ++pb) cf[d][pb] = ld16(ck_b + crow[pb] + 32 * sn);
+              for (int pb = 0; pb < kNP; ++pb) cf[d][pb] = ld16(ck_b + crow[pb] + 512 * sn);
               __builtin_amdgcn_sched_barrier(0);
             }
           }
         }
       }
       if (active) {
-        // lane (pos j, grp) holds K^T[dim(x, 4grp + r)][P0 + slice_pos(pb, j)]
+        // lane (pos j, grp) holds K^T[16x + 4grp + r][P0 + 16pb + j]; block
+        // e < NE pairs with block NE + e
         if (rope_on) {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
 #pragma unroll
             for (int e = 0; e < NE; ++e) {
-              const int fi = T::CPL * (4 * grp + r) + e;
+              const int fi = 16 * e + 4 * grp + r;
               double tb = static_cast<double>(P0) * rev64[fi];
               tb -= rint(tb);
               const float base = static_cast<float>(tb);
@@ -308,14 +303,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
 #pragma unroll
               for (int pb = 0; pb < kNP; ++pb) {
                 float c, s;
-                turn_cs(base + static_cast<float>(slice_pos(pb, j)) * rf, c, s);
+                turn_cs(base + static_cast<float>(16 * pb + j) * rf, c, s);
                 const float x = acc[e][pb][r], y = acc[NE + e][pb][r];
                 acc[e][pb][r] = x * c - y * s;
                 acc[NE + e][pb][r] = x * s + y * c;
               }
             }
         }
-        // S^T[pos, h]: lane (head j, grp) holds S^T[P0 + slice_pos(pb, 4grp + r)][j]
+        // S^T[pos, h]: lane (head j, grp) holds S^T[P0 + 16pb + 4grp + r][j]
 #pragma unroll
         for (int pb = 0; pb < kNP; ++pb) {
           f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -324,7 +319,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
             sc = mfma_bf16(pack_acc(acc[2 * t][pb], acc[2 * t + 1][pb]), qfs[t][lane], sc);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int off = P0 - c0 + slice_pos(pb, 4 * grp + r);
+            const int off = P0 - c0 + 16 * pb + 4 * grp + r;
             const float v = c0 + off < c1 ? sc[r] : -INFINITY;
             mx = fmaxf(mx, v);
             if (j < G) sS[j * pitch + off] = v;
@@ -335,13 +330,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
     mx = wave_max_xor(mx, 16);
     mx = wave_max_xor(mx, 32);
     if (grp == 0) smax[wave][j] = mx;
-    // phase-2 value rows do not depend on the probabilities: start them now.
-    // A operand: lane (rank row j, grp) = C_v^T[16 rb + j][c0 + 32u + 8grp ..+8]
+    // phase-2 value tiles do not depend on the probabilities: start them
+    // now. A operand: lane (rank row j, grp) = C_v^T[16 rb + j][c0 + 32u + 8grp ..+8]
     const int nU = (c1 - c0 + 31) >> 5;
     auto vload = [&](u32x4 (&dst)[RBW], int u) {
-      const int pc = min(c0 + 32 * u + 8 * grp, a.L_max - 8);
 #pragma unroll
-      for (int i = 0; i < RBW; ++i) dst[i] = ld16(cv_b + (16 * rb[i] + j) * a.L_max + pc);
+      for (int i = 0; i < RBW; ++i) dst[i] = ld16(cv_b + frag_off(rb[i], (c0 >> 5) + u, a.L_max, lane));
     };
     u32x4 vr[kVDepth][RBW];
 #pragma unroll
@@ -417,8 +411,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
   const int D2 = D + 2;
   float *part = a.part + ((static_cast<size_t>(b) * a.n_q + g * G) * a.nsplit) * D2;
   {
-    // wave owns d blocks OBW * wave .. +OBW; A = B_v^T rows, B = U (bf16)
-    const uint16_t *bv_g = a.bv + static_cast<size_t>(g) * D * a.r_v;
+    // wave owns d blocks OBW * wave .. +OBW; A = B_v^T tiles, B = U (bf16)
     f32x4 oacc[OBW];
 #pragma unroll
     for (int x = 0; x < OBW; ++x) oacc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -429,7 +422,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
       for (int q = 0; q < 2; ++q)
 #pragma unroll
         for (int x = 0; x < OBW; ++x)
-          av[q][x] = ld16(bv_g + static_cast<size_t>(16 * (OBW * wave + x) + j) * a.r_v + 32 * (s0 + q) + 8 * grp);
+          av[q][x] = ld16(a.bv + frag_off(g * NB + OBW * wave + x, s0 + q, a.r_v, lane));
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const f32x4 u0 = *reinterpret_cast<const f32x4 *>(urow + 32 * (s0 + q));
@@ -446,7 +439,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
         const int dd = 16 * (OBW * wave + x) + 4 * grp;
         if (a.nsplit == 1) {
           const float il = 1.f / lfin[j];
-          const size_t oi = (static_cast<size_t>(b) * a.n_q + g * G + j) * D + dd;
+          const int col = (g * G + j) * D + dd;
+          const size_t oi = a.out_tiled ? tile_off(b, col, a.n_q * D) : static_cast<size_t>(b) * a.n_q * D + col;
           if (a.out_f32)
             *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + oi) = oacc[x] * il;
           else
@@ -514,7 +508,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
         }
       }
     }
-    const size_t oi = (static_cast<size_t>(b) * a.n_q + g * G + h) * D + dd;
+    const int col = (g * G + h) * D + dd;
+    const size_t oi = a.out_tiled ? tile_off(b, col, a.n_q * D) : static_cast<size_t>(b) * a.n_q * D + col;
     if (a.out_f32)
       static_cast<float *>(a.out)[oi] = o / cmb_l[h];
     else

@@ -42,6 +42,20 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// Operand-tile storage of a bf16 matrix [R][C] (R % 16 == 0, C % 32 == 0):
+// 16 x 32 tiles of 1 KB, row-tile major, each in MFMA operand lane order --
+// lane l = (r % 16) + 16 * ((c % 32) / 8) holds columns 8 * ((c % 32) / 8)
+// .. +7 of row r, at byte 16 * l of the tile. One operand fragment is one
+// contiguous 1 KB read.
+__device__ __forceinline__ size_t tile_off(int r, int c, int C) {
+  return (static_cast<size_t>(r >> 4) * (C >> 5) + (c >> 5)) * 512 +
+         ((((c & 31) >> 3) << 4) + (r & 15)) * 8 + (c & 7);
+}
+// first element of operand fragment (row block rb, column step cs) of lane l
+__device__ __forceinline__ size_t frag_off(int rb, int cs, int C, int lane) {
+  return (static_cast<size_t>(rb) * (C >> 5) + cs) * 512 + lane * 8;
+}
+
 // Pack the four accumulator values of two 16x16 blocks into one operand
 // register set: slots 0..3 from `x`, 4..7 from `y`.
 __device__ __forceinline__ u32x4 pack_acc(f32x4 x, f32x4 y) {

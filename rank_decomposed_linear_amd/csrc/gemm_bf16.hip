@@ -1,12 +1,12 @@
 // bf16 MFMA GEMM for prefill-sized M: one factor of a decomposed projection
 // (W ~ A B, DeInfer section 2.1, Eq. (1)), C = X W with f32 accumulation.
 //
-// Both factors are stored transposed (Wt[N, K], the reduction index
-// contiguous), which is the order the 16x16x32 MFMA wants: eight
-// consecutive reduction values per lane. Activation and weight tiles are
-// therefore staged the same way, as rows of 16-byte chunks with an XOR
-// swizzle, so every operand read from LDS is one conflict-free 16-byte
-// ds_read.
+// Both factors are stored transposed (Wt[N, K]) in 16 x 32 operand tiles
+// (1 KB, MFMA lane order): the weight block of a workgroup's k step is
+// sixteen such tiles, copied to LDS with contiguous 16-byte loads and read
+// back one 16-byte ds_read per lane and fragment. The activation rows are
+// staged as 16-byte chunks with an XOR swizzle, so their operand reads are
+// conflict-free too.
 //
 // Tile 128 x 128 x 64, 4 waves (2 x 2), each wave 64 x 64 = 4 x 4 MFMA
 // blocks; LDS double-buffered (64 KB).
@@ -57,6 +57,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   // of both tiles, it = 0..3.
   const int kc = tid & 7, r0 = tid >> 3;
 
+  // weight unit u = tid + 256 it (16 bytes): tile T = u / 64 = 2 nb + ks,
+  // lane u % 64; tiles (nb, 0) and (nb, 1) are adjacent in memory
   auto gload = [&](Stage &st, int k0) {
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
@@ -69,9 +71,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
           v = swiglu8(v, *reinterpret_cast<const u32x4 *>(sg.X2 + off));
       }
       st.a[it] = v;
-      const int n = n0 + r0 + 32 * it;
-      st.b[it] = n < sg.N ? *reinterpret_cast<const u32x4 *>(sg.W + static_cast<size_t>(n) * a.K + k0 + 8 * kc)
-                          : u32x4{0u, 0u, 0u, 0u};
+      const int u = tid + 256 * it, tt = u >> 6, nb = tt >> 1, ks = tt & 1;
+      st.b[it] = n0 + 16 * nb < sg.N
+                     ? *reinterpret_cast<const u32x4 *>(sg.W + frag_off((n0 >> 4) + nb, (k0 >> 5) + ks, a.K, u & 63))
+                     : u32x4{0u, 0u, 0u, 0u};
     }
   };
   auto sstore = [&](const Stage &st, int buf) {
@@ -81,7 +84,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
       const int row = r0 + 32 * it;
       const int chunk = kc ^ (row & 7);
       *reinterpret_cast<u32x4 *>(base + row * BK + chunk * 8) = st.a[it];
-      *reinterpret_cast<u32x4 *>(base + kAElems + row * BK + chunk * 8) = st.b[it];
+      *reinterpret_cast<u32x4 *>(base + kAElems + (tid + 256 * it) * 8) = st.b[it];
     }
   };
 
@@ -110,11 +113,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
         af[mb] = *reinterpret_cast<const u32x4 *>(base + row * BK + chunk * 8);
       }
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int row = wn * 64 + nb * 16 + j;
-        const int chunk = (ks * 4 + grp) ^ (row & 7);
-        bfr[nb] = *reinterpret_cast<const u32x4 *>(base + kAElems + row * BK + chunk * 8);
-      }
+      for (int nb = 0; nb < 4; ++nb)
+        bfr[nb] = *reinterpret_cast<const u32x4 *>(base + kAElems + (((wn * 4 + nb) * 2 + ks) * 64 + lane) * 8);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -131,30 +131,26 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
     for (int r = 0; r < 4; ++r) {
       const int m = m0 + wm * 64 + mb * 16 + 4 * grp + r;
       if (m >= a.M) continue;
-      if constexpr (OM == GEMM_OUT_CACHE_T) {
-        const int b = m / a.T, tt = m - b * a.T;
-        uint16_t *col = static_cast<uint16_t *>(sg.C) + static_cast<size_t>(b) * sg.N * a.L_max +
-                        a.past_lens[b] + tt;
+      if constexpr (OM == GEMM_OUT_CACHE || OM == GEMM_OUT_CACHE_T) {
+        // key cache tiled [L_max, N] / value cache tiled [N, L_max], per sequence
+        const int b = m / a.T, pos = a.past_lens[b] + (m - b * a.T);
+        uint16_t *seq = static_cast<uint16_t *>(sg.C) + static_cast<size_t>(b) * sg.N * a.L_max;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
           const int n = n0 + wn * 64 + nb * 16 + j;
-          if (n < sg.N) col[static_cast<size_t>(n) * a.L_max] = f2bf(acc[mb][nb][r]);
+          if (n < sg.N)
+            seq[OM == GEMM_OUT_CACHE ? tile_off(pos, n, sg.N) : tile_off(n, pos, a.L_max)] =
+                f2bf(acc[mb][nb][r]);
         }
         continue;
       }
-      size_t rowoff;
-      if constexpr (OM == GEMM_OUT_CACHE) {
-        const int b = m / a.T, tt = m - b * a.T;
-        rowoff = (static_cast<size_t>(b) * a.L_max + a.past_lens[b] + tt) * sg.ldc;
-      } else {
-        rowoff = static_cast<size_t>(m) * sg.ldc;
-      }
+      const size_t rowoff = static_cast<size_t>(m) * sg.ldc;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
         const int n = n0 + wn * 64 + nb * 16 + j;
         if (n >= sg.N) continue;
         float v = acc[mb][nb][r];
-        if constexpr (OM == GEMM_OUT_BF16 || OM == GEMM_OUT_CACHE) {
+        if constexpr (OM == GEMM_OUT_BF16) {
           static_cast<uint16_t *>(sg.C)[rowoff + n] = f2bf(v);
         } else if constexpr (OM == GEMM_OUT_BF16_RES_F32) {
           v += static_cast<const float *>(sg.R)[static_cast<size_t>(m) * sg.ldr + n];

@@ -6,18 +6,21 @@
 // ridge of MI355X and far below the bf16 MFMA ridge. So the product runs on
 // MFMA with the token rows padded to 16, organised to keep HBM streaming:
 //
-//  * Weights are stored transposed, Wt[N, K] (the reduction index
-//    contiguous). A work item is a tile of 16 output columns -- 16
-//    consecutive rows of Wt, one contiguous 16 * K * 2-byte block -- times a
-//    K split. Output tiles this narrow give enough work items to fill the
-//    chip without splitting K for most factor shapes.
-//  * Per 32-wide reduction step, lane (i = lane%16, g = lane/16) loads
-//    Wt[n0 + i][k0 + 8g .. 8g+7] with one 16-byte non-temporal load: that is
-//    the MFMA A operand as loaded, no shuffles. The token rows are the B
-//    operand, x[m][k0 + 8g ..] (one 16-byte load), optionally passed through
-//    the fused RMSNorm prologue (gain multiply, sum of squares for the row
-//    scale). The accumulator lane (j, g) holds y[m = j][n0 + 4g + r], so the
-//    epilogue stores four consecutive outputs per lane.
+//  * Weights are stored transposed, Wt[N, K], in 16 x 32 operand tiles
+//    (1 KB each, MFMA lane order). A work item is 16 output columns -- one
+//    row of tiles, a contiguous 16 * K * 2-byte block -- times a K split.
+//    Output tiles this narrow give enough work items to fill the chip
+//    without splitting K for most factor shapes.
+//  * Per 32-wide reduction step a wave reads one weight tile (lane l: bytes
+//    16 l .. 16 l + 15, one contiguous 1 KB per instruction): that is the
+//    MFMA A operand, rows n0 + l % 16. The token rows are the B operand,
+//    x[m][k0 + 8 (l / 16) ..]: from an operand-tiled activation (one
+//    contiguous 1 KB again) or from a plain row-major one, optionally
+//    passed through the fused RMSNorm prologue (gain multiply, sum of
+//    squares for the row scale). The accumulator lane (j, g) holds
+//    y[m = j][n0 + 4g + r], so the epilogue stores four consecutive outputs
+//    per lane, row-major or straight into the operand tiles of the next
+//    GEMV.
 //  * The waves of a workgroup take interleaved steps of the item's K range
 //    and keep four steps (4 KB of weights) in flight each; their sums
 //    meet in LDS and are added in wave order.
@@ -70,16 +73,24 @@ __device__ __forceinline__ int xcd_item(int b, int grid) {
   return (b & 7) * per + (b >> 3);
 }
 
+// Activation modes: row-major bf16, row-major f32, operand-tiled bf16.
+enum XMode : int { XM_BF16 = 0, XM_F32 = 1, XM_TILED = 2 };
+
 // Activation rows are loaded raw into the prefetch ring with the weights
 // (so waiting for a step never waits for later prefetches) and converted to
-// the bf16 operand when the step is computed.
-template <int XF32>
-__device__ __forceinline__ void load_x_raw(const void *X, int ldx, int row, int k,
-                                           u32x4 (&r)[XF32 ? 2 : 1]) {
-  if constexpr (XF32) {
+// the bf16 operand when the step is computed. Row-major modes read row
+// `row` at column k; the tiled mode reads fragment (row block mb, column
+// step k / 32) of an [Mpad, cols] operand-tiled matrix.
+template <int XM>
+__device__ __forceinline__ void load_x_raw(const void *X, int ldx, int row, int mb, int k, int lane,
+                                           u32x4 (&r)[XM == XM_F32 ? 2 : 1]) {
+  if constexpr (XM == XM_F32) {
     const float *p = static_cast<const float *>(X) + static_cast<size_t>(row) * ldx + k;
     r[0] = *reinterpret_cast<const u32x4 *>(p);
     r[1] = *reinterpret_cast<const u32x4 *>(p + 4);
+  } else if constexpr (XM == XM_TILED) {
+    r[0] = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(X) +
+                                            frag_off(mb, k >> 5, ldx, lane));
   } else {
     r[0] = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(X) +
                                             static_cast<size_t>(row) * ldx + k);
@@ -132,8 +143,9 @@ __device__ __forceinline__ u32x4 make_x(const u32x4 (&r)[XF32 ? 2 : 1],
   }
 }
 
-template <int MB, int XF32, int PAIRED, int NORM, int GF32, int kWaves>
+template <int MB, int XM, int PAIRED, int NORM, int GF32, int kWaves>
 __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
+  constexpr int XF32 = XM == XM_F32;
   constexpr int kThreads = kWaves * 64;
   constexpr int HALVES = PAIRED ? 2 : 1;
   constexpr int NACC = HALVES * MB;          // f32x4 accumulators per lane
@@ -156,7 +168,6 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
   if (a.nseg > 2 && tile >= a.seg[2].tile_begin) si = 2;
   const GvSeg sg = a.seg[si];
   const int n0 = (tile - sg.tile_begin) * kRows;
-  const int wrow = min(n0 + j, sg.N - 1);    // this lane's weight row
 
   const int ksteps = (a.K + a.K2) >> 5;
   const int s_begin = split * a.split_steps;
@@ -184,19 +195,26 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
   // every load below is unconditional (rows clamped, pointers selected), so
   // the compiler's wait counts stay exact across the prefetch ring
   const void *gsrc = has_gamma ? a.gamma : sg.X;
-  const uint16_t *w1 = sg.W + static_cast<size_t>(wrow) * a.K + 8 * grp;
-  const uint16_t *w2 = PAIRED ? sg.W2 + static_cast<size_t>(wrow) * a.K2 + 8 * grp : w1;
+  // this item's row of weight tiles (16 rows x K), lane offset included
+  const uint16_t *w1 = sg.W + frag_off(n0 >> 4, 0, a.K, lane);
+  const uint16_t *w2 = PAIRED ? sg.W2 + frag_off(n0 >> 4, 0, a.K2, lane) : w1;
   auto load_stage = [&](Stage &sb, int st) {
     int k = st * 32;
     const bool second = PAIRED && k >= a.K;
     const void *X = second ? sg.X2 : sg.X;
     const int ldx = second ? sg.ldx2 : sg.ldx;
     k -= second ? a.K : 0;
-    const uint16_t *wp = (second ? w2 : w1) + k;
+    const uint16_t *wp = (second ? w2 : w1) + static_cast<size_t>(k >> 5) * 512;
     sb.w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wp));
-    k += 8 * grp;
+    if constexpr (XM == XM_TILED) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) load_x_raw<XF32>(X, ldx, min(mb * 16 + j, a.M - 1), k, sb.x[mb]);
+      for (int mb = 0; mb < MB; ++mb) load_x_raw<XM>(X, ldx, 0, mb, k, lane, sb.x[mb]);
+    }
+    k += 8 * grp;
+    if constexpr (XM != XM_TILED) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) load_x_raw<XM>(X, ldx, min(mb * 16 + j, a.M - 1), mb, k, lane, sb.x[mb]);
+    }
     if constexpr (NORM) {
       if constexpr (GF32) {
         const float *gp = static_cast<const float *>(gsrc) + k;
@@ -354,19 +372,22 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
     case GV_OUT_F32:
       *reinterpret_cast<f32x4 *>(static_cast<float *>(sg.out) + oi) = f32x4{v[0], v[1], v[2], v[3]};
       break;
-    case GV_OUT_CACHE: {
+    case GV_OUT_TILED:
+      *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(sg.out) + tile_off(m, n, sg.N)) =
+          u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
+      break;
+    case GV_OUT_CACHE: {   // key cache: [L_max, N] operand tiles per sequence
       const int b = m / a.T, t = m - b * a.T;
-      const size_t row = static_cast<size_t>(b) * a.L_max + a.past[b] + t;
-      *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(sg.out) + row * sg.ldo + n) =
+      uint16_t *seq = static_cast<uint16_t *>(sg.out) + static_cast<size_t>(b) * a.L_max * sg.N;
+      *reinterpret_cast<u32x2 *>(seq + tile_off(a.past[b] + t, n, sg.N)) =
           u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
       break;
     }
-    case GV_OUT_CACHE_T: {
+    case GV_OUT_CACHE_T: {   // value cache: [N, L_max] operand tiles per sequence
       const int b = m / a.T, t = m - b * a.T;
-      uint16_t *col = static_cast<uint16_t *>(sg.out) + static_cast<size_t>(b) * sg.N * a.L_max +
-                      a.past[b] + t;
+      uint16_t *seq = static_cast<uint16_t *>(sg.out) + static_cast<size_t>(b) * sg.N * a.L_max;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) col[static_cast<size_t>(n + r) * a.L_max] = f2bf(v[r]);
+      for (int r = 0; r < 4; ++r) seq[tile_off(n + r, a.past[b] + t, a.L_max)] = f2bf(v[r]);
       break;
     }
     case GV_OUT_RES_F32: {
@@ -394,35 +415,37 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
           u32x2{pack2(v[0] + rr[0], v[1] + rr[1]), pack2(v[2] + rr[2], v[3] + rr[3])};
       break;
     }
-    default: {  // GV_OUT_SWIGLU
+    default: {  // GV_OUT_SWIGLU, GV_OUT_SWIGLU_TILED
       float u[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) u[r] = silu(v[r]) * red[((1 * MB + mb) * 4 + r) * 64 + ln];
-      *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(sg.out) + oi) =
-          u32x2{pack2(u[0], u[1]), pack2(u[2], u[3])};
+      const size_t o = sg.omode == GV_OUT_SWIGLU_TILED ? tile_off(m, n, sg.N) : oi;
+      *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(sg.out) + o) = u32x2{pack2(u[0], u[1]), pack2(u[2], u[3])};
       break;
     }
   }
 }
 
-template <int MB, int XF32, int PAIRED, int NORM, int GF32>
+template <int MB, int XM, int PAIRED, int NORM, int GF32>
 hipError_t launch_t(const GvArgs &a, int grid, hipStream_t s) {
   if (a.waves == 4)
-    gemv_kernel<MB, XF32, PAIRED, NORM, GF32, 4><<<grid, 4 * 64, 0, s>>>(a);
+    gemv_kernel<MB, XM, PAIRED, NORM, GF32, 4><<<grid, 4 * 64, 0, s>>>(a);
   else
-    gemv_kernel<MB, XF32, PAIRED, NORM, GF32, 8><<<grid, 8 * 64, 0, s>>>(a);
+    gemv_kernel<MB, XM, PAIRED, NORM, GF32, 8><<<grid, 8 * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
 template <int MB>
 hipError_t launch_mb(const GvArgs &a, int grid, hipStream_t s) {
-  if (a.K2 > 0) return launch_t<MB, 0, 1, 0, 0>(a, grid, s);
+  if (a.K2 > 0)
+    return a.x_tiled ? launch_t<MB, XM_TILED, 1, 0, 0>(a, grid, s) : launch_t<MB, XM_BF16, 1, 0, 0>(a, grid, s);
   if (a.norm) {
     if (a.x_f32)
-      return a.gamma_f32 ? launch_t<MB, 1, 0, 1, 1>(a, grid, s) : launch_t<MB, 1, 0, 1, 0>(a, grid, s);
-    return a.gamma_f32 ? launch_t<MB, 0, 0, 1, 1>(a, grid, s) : launch_t<MB, 0, 0, 1, 0>(a, grid, s);
+      return a.gamma_f32 ? launch_t<MB, XM_F32, 0, 1, 1>(a, grid, s) : launch_t<MB, XM_F32, 0, 1, 0>(a, grid, s);
+    return a.gamma_f32 ? launch_t<MB, XM_BF16, 0, 1, 1>(a, grid, s) : launch_t<MB, XM_BF16, 0, 1, 0>(a, grid, s);
   }
-  return a.x_f32 ? launch_t<MB, 1, 0, 0, 0>(a, grid, s) : launch_t<MB, 0, 0, 0, 0>(a, grid, s);
+  if (a.x_tiled) return launch_t<MB, XM_TILED, 0, 0, 0>(a, grid, s);
+  return a.x_f32 ? launch_t<MB, XM_F32, 0, 0, 0>(a, grid, s) : launch_t<MB, XM_BF16, 0, 0, 0>(a, grid, s);
 }
 
 int env_int(const char *name, int dflt) {

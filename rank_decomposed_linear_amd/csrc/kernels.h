@@ -10,26 +10,30 @@ namespace dl {
 // ---------------------------------------------------------------------------
 // Weight-streaming bf16 GEMV for small M (decode), M <= 64:
 // out_s = epilogue(X_s[M, K] W_s) for up to three segments that share M
-// and K. Every weight is stored transposed, Wt[N, K] row-major (the
-// reduction index contiguous). Paired launches (K2 > 0) have one segment
-// whose two halves (X, W, K) and (X2, W2, K2) produce two results for the
-// same output columns, combined by the SwiGLU epilogue.
+// and K. Every weight is stored transposed, Wt[N, K], in 16 x 32 operand
+// tiles (tile_off in common.h). X is row-major bf16 / f32 or operand-tiled
+// bf16 ([Mpad, K] with Mpad = M rounded up to 16). Paired launches
+// (K2 > 0) have one segment whose two halves (X, W, K) and (X2, W2, K2)
+// produce two results for the same output columns, combined by the SwiGLU
+// epilogue.
 // ---------------------------------------------------------------------------
 enum GvOut : int {
   GV_OUT_BF16 = 0,      // out bf16 [m * ldo + n] = v
   GV_OUT_F32 = 1,       // out f32 [m * ldo + n] = v
-  GV_OUT_CACHE = 2,     // out bf16 row (b * L_max + past[b] + t), m = b * T + t
-  GV_OUT_CACHE_T = 6,   // out bf16 [b][n][L_max] at column past[b] + t (rank-major cache)
+  GV_OUT_CACHE = 2,     // key cache: sequence b = m / T, tiled [L_max, N], row past[b] + t
+  GV_OUT_CACHE_T = 6,   // value cache: sequence b, tiled [N, L_max], column past[b] + t
+  GV_OUT_TILED = 7,     // out bf16 operand tiles [Mpad, N]
   GV_OUT_RES_F32 = 3,   // out f32 = v + R (R f32 if res_f32, else bf16); out2 gets a copy
   GV_OUT_RES_BF16 = 4,  // out bf16 = v + R (R f32)
-  GV_OUT_SWIGLU = 5     // paired: out bf16 = silu(v_first) * v_second
+  GV_OUT_SWIGLU = 5,    // paired: out bf16 = silu(v_first) * v_second
+  GV_OUT_SWIGLU_TILED = 8  // paired, stored as operand tiles [Mpad, N]
 };
 
 struct GvSeg {
-  const uint16_t *W;   // Wt [N, K] bf16
+  const uint16_t *W;   // Wt [N, K] bf16, operand tiles
   const uint16_t *W2;  // paired: second half Wt2 [N, K2]
-  const void *X;       // [M, ldx] bf16 (or f32 with x_f32)
-  const void *X2;      // paired: second-half activations, bf16 [M, ldx2]
+  const void *X;       // [M, ldx] bf16 (or f32 with x_f32); tiled: [Mpad, K], ldx = K
+  const void *X2;      // paired: second-half activations, like X with K2
   void *out;
   float *out2;         // optional copy (GV_OUT_RES_F32)
   const void *R;       // residual [M, ldr]
@@ -43,6 +47,7 @@ struct GvArgs {
   int nseg;
   int M, K, K2;           // K2 > 0 only for paired launches (then nseg == 1)
   int x_f32;              // X is f32 (else bf16); paired launches use bf16
+  int x_tiled;            // X (and X2) are operand-tiled bf16
   int norm;               // fused RMSNorm: X scaled by gamma, rows of the result by
                           // 1 / sqrt(mean(X^2) + eps) (mean over the K columns)
   const void *gamma;      // [K] gains or NULL (= 1)
@@ -75,12 +80,12 @@ enum GemmOut : int {
   GEMM_OUT_BF16 = 0,        // C bf16 [M, ldc]
   GEMM_OUT_BF16_RES_F32 = 1,// C bf16 = acc + R (f32 [M, ldr]); also C32 (f32) if non-null
   GEMM_OUT_F32_RES_BF16 = 2,// C32 f32 = acc + R (bf16 [M, ldr])
-  GEMM_OUT_CACHE = 3,       // C bf16 rows scattered: row b*T+t -> cache[b, past[b]+t]
-  GEMM_OUT_CACHE_T = 4      // C bf16 columns: row b*T+t, column n -> cache[b, n, past[b]+t]
+  GEMM_OUT_CACHE = 3,       // key cache: row b*T+t -> tiled [L_max, N] of sequence b, row past[b]+t
+  GEMM_OUT_CACHE_T = 4      // value cache: row b*T+t, column n -> tiled [N, L_max], (n, past[b]+t)
 };
 
 struct GemmSeg {
-  const uint16_t *W;  // Wt [N, K]
+  const uint16_t *W;  // Wt [N, K], operand tiles
   const uint16_t *X;  // [M, ldx]
   const uint16_t *X2; // SwiGLU partner
   void *C;            // output
@@ -108,11 +113,12 @@ int gemm_ntiles(int N);
 // ---------------------------------------------------------------------------
 struct AttnDecodeArgs {
   const void *q;       // [Bsz, n_q, d] bf16 or f32 (q_f32)
-  const uint16_t *ck;  // [Bsz, L_max, r_k]
-  const uint16_t *cv;  // rank-major [Bsz, r_v, L_max]
-  const uint16_t *bk, *bv;  // up factors stored transposed: [n_kv * d, r]
+  const uint16_t *ck;  // key cache, per sequence [L_max, r_k] in operand tiles
+  const uint16_t *cv;  // value cache, per sequence [r_v, L_max] in operand tiles
+  const uint16_t *bk, *bv;  // up factors, [n_kv * d, r] in operand tiles
   const int32_t *ctx_lens;
-  void *out;           // [Bsz, n_q, d] bf16 (or f32 with out_f32)
+  void *out;           // [Bsz, n_q, d] bf16 (or f32 with out_f32); out_tiled: bf16
+                       // operand tiles of the [Bsz (padded to 16), n_q * d] matrix
   float *part;         // [Bsz, n_kv, nsplit, 16, d + 2] split partials (nsplit > 1)
   int *counters;       // [Bsz * n_kv], zero on entry, left zero
   int Bsz, n_q, n_kv, d, r_k, r_v, L_max;
@@ -122,7 +128,7 @@ struct AttnDecodeArgs {
   int rs_cap, pitch, lds_bs, lds_s;
   float scale_log2;    // sm_scale * log2(e)
   float theta;
-  int q_f32, out_f32;
+  int q_f32, out_f32, out_tiled;
 };
 int attn_decode_split_granule();
 int attn_decode_max_rank_v();   // largest r_v the decode kernel accepts
@@ -130,9 +136,9 @@ hipError_t launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s);
 
 struct AttnPrefillArgs {
   const void *q;       // [Bsz, T, n_q, d] bf16 or f32
-  const uint16_t *ck;  // [Bsz, L_max, r_k]
-  const uint16_t *cv;  // rank-major [Bsz, r_v, L_max]
-  const uint16_t *bk, *bv;  // [n_kv * d, r]
+  const uint16_t *ck;  // key cache, per sequence [L_max, r_k] in operand tiles
+  const uint16_t *cv;  // value cache, per sequence [r_v, L_max] in operand tiles
+  const uint16_t *bk, *bv;  // [n_kv * d, r] in operand tiles
   const int32_t *past_lens;
   uint16_t *out;       // [Bsz, T, n_q*d]
   int Bsz, T, n_q, n_kv, d, r_k, r_v, L_max;

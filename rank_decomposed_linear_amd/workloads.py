@@ -316,22 +316,60 @@ def factor_pair_flops(shape: LayerShape, tokens: int) -> Dict[str, int]:
 # ----------------------------------------------------------------------------
 # Library storage order (data movement only)
 # ----------------------------------------------------------------------------
+def tile_operands(a: np.ndarray) -> np.ndarray:
+    """Matrix (or stack of matrices) [..., R, C] -> the library's bf16
+    operand-tile order: 16 x 32 tiles, row-tile major, each tile in MFMA
+    lane order (element (r, c) of a tile at ((c // 8) * 16 + r) * 8 + c % 8).
+    Needs R % 16 == 0 and C % 32 == 0."""
+    *lead, R, C = a.shape
+    if R % 16 or C % 32:
+        raise ValueError(f"operand tiles need rows % 16 == 0 and cols % 32 == 0, got {R} x {C}")
+    t = a.reshape(*lead, R // 16, 16, C // 32, 4, 8)          # [.., rt, r, ct, g, e]
+    t = np.moveaxis(t, -3, -4)                                  # [.., rt, ct, r, g, e]
+    t = np.swapaxes(t, -3, -2)                                  # [.., rt, ct, g, r, e]
+    return np.ascontiguousarray(t).reshape(*lead, R, C)
+
+
+def untile_operands(t: np.ndarray) -> np.ndarray:
+    """Inverse of tile_operands."""
+    *lead, R, C = t.shape
+    a = t.reshape(*lead, R // 16, C // 32, 4, 16, 8)            # [.., rt, ct, g, r, e]
+    a = np.swapaxes(a, -3, -2)                                  # [.., rt, ct, r, g, e]
+    a = np.moveaxis(a, -4, -3)                                  # [.., rt, r, ct, g, e]
+    return np.ascontiguousarray(a).reshape(*lead, R, C)
+
+
 def to_library_factor(a: np.ndarray) -> np.ndarray:
     """A factor in the row-vector convention (A [m, k] or B [k, n]) -> the
-    library's storage, its transpose, whose rows run along the reduction
-    index."""
-    return np.ascontiguousarray(np.swapaxes(a, -1, -2))
+    library's storage: its transpose, whose rows run along the reduction
+    index; bf16 factors (uint16 arrays) in operand-tile order."""
+    t = np.ascontiguousarray(np.swapaxes(a, -1, -2))
+    return tile_operands(t) if a.dtype == np.uint16 else t
+
+
+def to_library_key_cache(ck: np.ndarray) -> np.ndarray:
+    """Key latents [Bsz, L, r_k] -> the library's key cache: the same rows,
+    per sequence in operand-tile order for bf16 (L % 16 == 0)."""
+    return tile_operands(ck) if ck.dtype == np.uint16 else np.ascontiguousarray(ck)
+
+
+def from_library_key_cache(ck: np.ndarray, bf16: bool) -> np.ndarray:
+    """Inverse of to_library_key_cache (bf16: tiled storage order)."""
+    return untile_operands(ck) if bf16 else np.ascontiguousarray(ck)
 
 
 def to_library_value_cache(cv: np.ndarray) -> np.ndarray:
-    """Value latents [Bsz, L, r_v] -> the library's rank-major cache
-    [Bsz, r_v, L]."""
-    return np.ascontiguousarray(np.swapaxes(cv, -1, -2))
+    """Value latents [Bsz, L, r_v] -> the library's rank-major value cache
+    [Bsz, r_v, L], per sequence in operand-tile order for bf16
+    (L % 32 == 0)."""
+    t = np.ascontiguousarray(np.swapaxes(cv, -1, -2))
+    return tile_operands(t) if cv.dtype == np.uint16 else t
 
 
-def from_library_value_cache(cv_t: np.ndarray) -> np.ndarray:
+def from_library_value_cache(cv_t: np.ndarray, bf16: bool) -> np.ndarray:
     """Inverse of to_library_value_cache."""
-    return np.ascontiguousarray(np.swapaxes(cv_t, -1, -2))
+    t = untile_operands(cv_t) if bf16 else cv_t
+    return np.ascontiguousarray(np.swapaxes(t, -1, -2))
 
 
 def random_array(rng: np.random.Generator, shape, std: float, dtype: str) -> np.ndarray:

@@ -68,12 +68,15 @@ def test_lowrank_linear_validation(lib):
 
 def test_kv_append_validation(lib):
     f = lib.dl_lowrank_kv_append
-    assert f(P, P, P, P, P, None, 2, 1, 64, 64, 64, 8, B.DL_BF16, P, 1 << 20, None) == INVALID
-    assert f(P, P, P, P, P, P, 2, 9, 64, 64, 64, 8, B.DL_BF16, P, 1 << 20, None) == INVALID
-    assert f(P, P, P, P, P, P, 2, 1, 64, 96, 64, 8, B.DL_BF16, P, 1 << 20, None) == UNSUPPORTED
-    assert f(P, P, P, BAD, P, P, 2, 1, 64, 64, 64, 8, B.DL_BF16, P, 1 << 20, None) == ALIGN
+    assert f(P, P, P, P, P, None, 2, 1, 64, 64, 64, 32, B.DL_BF16, P, 1 << 20, None) == INVALID
+    assert f(P, P, P, P, P, P, 2, 33, 64, 64, 64, 32, B.DL_BF16, P, 1 << 20, None) == INVALID
+    assert f(P, P, P, P, P, P, 2, 1, 64, 96, 64, 32, B.DL_BF16, P, 1 << 20, None) == UNSUPPORTED
+    # bf16 caches are operand tiles: L_max must be a multiple of 32
+    assert f(P, P, P, P, P, P, 2, 1, 64, 64, 64, 40, B.DL_BF16, P, 1 << 20, None) == UNSUPPORTED
+    assert "operand tiles" in err(lib)
+    assert f(P, P, P, BAD, P, P, 2, 1, 64, 64, 64, 32, B.DL_BF16, P, 1 << 20, None) == ALIGN
     need = lib.dl_kv_append_workspace(2, 1, 64, 64, 64, B.DL_BF16)
-    assert f(P, P, P, P, P, P, 2, 1, 64, 64, 64, 8, B.DL_BF16, P, need - 1, None) == WORKSPACE
+    assert f(P, P, P, P, P, P, 2, 1, 64, 64, 64, 32, B.DL_BF16, P, need - 1, None) == WORKSPACE
 
 
 def test_attention_validation(lib):
@@ -81,8 +84,8 @@ def test_attention_validation(lib):
     args = dict(Bsz=2, n_q=8, n_kv=2, d=128, r_k=64, r_v=64, L=32)
 
     def call(q=P, n_q=8, n_kv=2, d=128, r_k=64, r_v=64, dt=B.DL_BF16, ws=1 << 24, wsp=P,
-             scale=0.0, theta=10000.0):
-        return dec(q, P, P, P, P, P, P, 2, n_q, n_kv, d, r_k, r_v, 32, scale, theta, dt, wsp, ws,
+             scale=0.0, theta=10000.0, L_max=32):
+        return dec(q, P, P, P, P, P, P, 2, n_q, n_kv, d, r_k, r_v, L_max, scale, theta, dt, wsp, ws,
                    None)
 
     assert call(q=None) == INVALID
@@ -90,6 +93,8 @@ def test_attention_validation(lib):
     assert "multiple of n_kv" in err(lib)
     assert call(d=96) == UNSUPPORTED
     assert call(r_k=100) == UNSUPPORTED
+    assert call(L_max=48) == UNSUPPORTED                # bf16 cache tiles need L_max % 32
+    assert call(r_v=1088) == UNSUPPORTED                # above the largest value rank
     assert call(n_q=34, n_kv=2) == UNSUPPORTED          # group of 17 > 16
     assert call(scale=-1.0) == INVALID
     assert call(q=BAD) == ALIGN
@@ -115,20 +120,21 @@ def _layer(dt=B.DL_BF16, rank=64, hidden=256, ffn=512, n_q=4, n_kv=2, d=64):
 def test_layer_validation(lib):
     f = lib.dl_decomposed_layer_fwd
     L = _layer()
-    need = lib.dl_layer_workspace(ctypes.byref(L), 2, 1, 16)
+    need = lib.dl_layer_workspace(ctypes.byref(L), 2, 1, 32)
     assert need > 0
-    assert f(ctypes.byref(L), P, P, None, P, P, P, 2, 1, 16, P, need - 1, None) == WORKSPACE
-    assert f(None, P, P, None, P, P, P, 2, 1, 16, P, need, None) == INVALID
-    assert f(ctypes.byref(L), P, P, None, P, P, P, 2, 0, 16, P, need, None) == INVALID
-    assert f(ctypes.byref(L), P, P, BAD, P, P, P, 2, 1, 16, P, need, None) == ALIGN
+    assert f(ctypes.byref(L), P, P, None, P, P, P, 2, 1, 32, P, need - 1, None) == WORKSPACE
+    assert f(None, P, P, None, P, P, P, 2, 1, 32, P, need, None) == INVALID
+    assert f(ctypes.byref(L), P, P, None, P, P, P, 2, 0, 32, P, need, None) == INVALID
+    assert f(ctypes.byref(L), P, P, BAD, P, P, P, 2, 1, 32, P, need, None) == ALIGN
+    assert f(ctypes.byref(L), P, P, None, P, P, P, 2, 1, 16, P, need, None) == UNSUPPORTED
     L2 = _layer(rank=96)
-    assert f(ctypes.byref(L2), P, P, None, P, P, P, 2, 1, 16, P, need, None) == UNSUPPORTED
+    assert f(ctypes.byref(L2), P, P, None, P, P, P, 2, 1, 32, P, need, None) == UNSUPPORTED
     L3 = _layer()
     L3.gate = B.Factor(None, P, 64)
-    assert f(ctypes.byref(L3), P, P, None, P, P, P, 2, 1, 16, P, need, None) == INVALID
+    assert f(ctypes.byref(L3), P, P, None, P, P, P, 2, 1, 32, P, need, None) == INVALID
     L4 = _layer(n_kv=3)
-    assert f(ctypes.byref(L4), P, P, None, P, P, P, 2, 1, 16, P, need, None) == INVALID
+    assert f(ctypes.byref(L4), P, P, None, P, P, P, 2, 1, 32, P, need, None) == INVALID
     # workspace grows with the batch and is defined for both dtypes
-    assert lib.dl_layer_workspace(ctypes.byref(L), 64, 1, 16) > need
+    assert lib.dl_layer_workspace(ctypes.byref(L), 64, 1, 32) > need
     assert lib.dl_layer_workspace(ctypes.byref(_layer(dt=B.DL_F32, rank=5, hidden=20, ffn=30,
                                                       d=10)), 2, 3, 16) > 0

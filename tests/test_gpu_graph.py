@@ -20,13 +20,14 @@ def test_graph_replays_match_eager():
     ranks = {"q": 192, "k": 128, "v": 128, "o": 192, "gate": 256, "up": 256, "down": 256}
     shp = W.LayerShape(512, 8, 2, 128, 1024, tuple((p, ranks[p]) for p in W.PROJECTIONS), "bf16",
                        500000.0)
-    # factors drawn directly in the library's transposed storage
+    # factors and caches drawn directly in the library's storage (transposed,
+    # operand tiles): random values in any order are random values
     facs = {p: (to_dev(rand(r, (shp.rank(p), m), 0.05, "bf16")),
                 to_dev(rand(r, (n, shp.rank(p)), 0.05, "bf16")))
             for p, (m, n) in shp.shapes().items()}
     layer = binding.DecomposedLayer(facs, shp.hidden, shp.n_q, shp.n_kv, shp.head_dim, shp.ffn,
                                     shp.rope_theta)
-    Bsz, L_max = 16, 304
+    Bsz, L_max = 16, 320
     x = to_dev(rand(r, (Bsz, 1, 512), 1.0, "bf16"))
     ck = to_dev(rand(r, (Bsz, L_max, 128), 1.0, "bf16"))
     cv = to_dev(rand(r, (Bsz, 128, L_max), 1.0, "bf16"))

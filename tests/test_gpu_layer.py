@@ -8,8 +8,9 @@ appended cache rows are compared too. Tolerance as in test_gpu_ops.
 Full-size decode configurations compare a sample of sequences (each
 sequence's output depends only on its own rows); the prefill configuration
 compares sequence 0 in full. Inputs are uploaded in the library's storage
-order (factors transposed, value cache rank-major) and the value cache is
-read back into the oracle's [Bsz, L, r_v] order before comparing."""
+order (factors transposed, value cache rank-major, bf16 factors and caches
+in operand tiles) and the caches are read back into the oracle's
+[Bsz, L, r] order before comparing."""
 import numpy as np
 import pytest
 
@@ -73,7 +74,9 @@ def check_step(dt, x, y_dev, x2_dev, ck_dev, cv_dev, want, past, T, seqs=None):
         "mlp_delta": delta_err(y - x2, want["y"] - want["x2"], smax, dt),
         "y": relerr(y, want["y"]),
     }
-    gk, gv = to_host(ck_dev)[sl], W.from_library_value_cache(to_host(cv_dev))[sl]
+    bf = dt == "bf16"
+    gk = W.from_library_key_cache(to_host(ck_dev), bf)[sl]
+    gv = W.from_library_value_cache(to_host(cv_dev), bf)[sl]
     pst = np.asarray(past)[sl]
     for i in range(len(pst)):
         rows = slice(pst[i], pst[i] + T)
@@ -98,8 +101,8 @@ def run_layer(B, layer, x, ck, cv, past):
 SMALL = [
     # (name, dtype, hidden, n_q, n_kv, d, ffn, rank_attn, rank_kv, rank_mlp, Bsz, T, past, L_max, theta)
     ("gemv_decode", "bf16", 512, 8, 2, 128, 1024, 192, 128, 256, 4, 1, [0, 7, 100, 33], 128, 500000.0),
-    ("gemv_prefill", "bf16", 256, 4, 2, 64, 512, 128, 64, 192, 2, 8, [0, 20], 40, 10000.0),
-    ("gemm_prefill", "bf16", 512, 8, 2, 128, 768, 256, 128, 320, 2, 100, [0, 20], 136, 10000.0),
+    ("gemv_prefill", "bf16", 256, 4, 2, 64, 512, 128, 64, 192, 2, 8, [0, 20], 64, 10000.0),
+    ("gemm_prefill", "bf16", 512, 8, 2, 128, 768, 256, 128, 320, 2, 100, [0, 20], 160, 10000.0),
     ("gemm_decode_b80", "bf16", 256, 4, 1, 64, 512, 128, 64, 128, 80, 1, None, 32, 10000.0),
     ("f32_prefill", "f32", 96, 4, 2, 16, 160, 24, 12, 40, 3, 6, [0, 2, 9], 20, 100.0),
     ("f32_decode", "f32", 96, 6, 3, 16, 160, 24, 12, 40, 3, 1, [0, 2, 9], 20, 100.0),
@@ -123,7 +126,7 @@ def test_small_layer(B, case):
     ck0 = rand(r, (Bsz, L_max, rkv), 1.0, dt)
     cv0 = rand(r, (Bsz, L_max, rkv), 1.0, dt)
     layer = make_gpu_layer(B, weights)
-    ck, cv = to_dev(ck0), to_dev(W.to_library_value_cache(cv0))
+    ck, cv = to_dev(W.to_library_key_cache(ck0)), to_dev(W.to_library_value_cache(cv0))
     y, x2 = run_layer(B, layer, x, ck, cv, past)
     want = oracle_layer(weights, x, ck0, cv0, past)
     check_step(dt, x, y, x2, ck, cv, want, past, T)
@@ -139,7 +142,7 @@ def test_tiny_chain_prefill_then_decode(B):
     w = W.TINY
     weights, inp = W.draw(w)
     layer = make_gpu_layer(B, weights)
-    ck, cv = to_dev(inp.ck), to_dev(W.to_library_value_cache(inp.cv))
+    ck, cv = to_dev(W.to_library_key_cache(inp.ck)), to_dev(W.to_library_value_cache(inp.cv))
     ck_ref, cv_ref = f64(inp.ck), f64(inp.cv)
     past = np.zeros(w.batch, np.int32)
     steps = [inp.x] + [inp.decode_x[s] for s in range(w.decode_steps)]
@@ -153,13 +156,13 @@ def test_tiny_chain_prefill_then_decode(B):
         ck_ref, cv_ref = want["ck"], want["cv"]
         past = past + x.shape[1]
     torch.cuda.synchronize()
-    assert relerr(to_host(ck), ck_ref) <= TOL["f32"]
+    assert relerr(W.from_library_key_cache(to_host(ck), False), ck_ref) <= TOL["f32"]
 
 
 def _decode_config(B, w, seqs):
     weights, inp = W.draw(w)
     layer = make_gpu_layer(B, weights)
-    ck, cv = to_dev(inp.ck), to_dev(W.to_library_value_cache(inp.cv))
+    ck, cv = to_dev(W.to_library_key_cache(inp.ck)), to_dev(W.to_library_value_cache(inp.cv))
     y, x2 = run_layer(B, layer, inp.x, ck, cv, inp.past_lens)
     want = oracle_layer(weights, inp.x, inp.ck, inp.cv, inp.past_lens, seqs)
     return check_step("bf16", inp.x, y, x2, ck, cv, want, inp.past_lens, 1, seqs)
@@ -186,7 +189,7 @@ def test_llama3_70b_c50_prefill(B):
     w = W.LLAMA3_70B_C50_PREFILL
     weights, inp = W.draw(w)
     layer = make_gpu_layer(B, weights)
-    ck, cv = to_dev(inp.ck), to_dev(W.to_library_value_cache(inp.cv))
+    ck, cv = to_dev(W.to_library_key_cache(inp.ck)), to_dev(W.to_library_value_cache(inp.cv))
     y, x2 = run_layer(B, layer, inp.x, ck, cv, inp.past_lens)
     want = oracle_layer(weights, inp.x, inp.ck, inp.cv, inp.past_lens, np.array([0]))
     check_step("bf16", inp.x, y, x2, ck, cv, want, inp.past_lens, w.prefill, np.array([0]))

@@ -4,7 +4,8 @@ through the C ABI. Sizes span several tiles, ragged tails, both the GEMV
 head_dim, RoPE on and off, and both dtypes.
 
 Inputs are drawn in the row-vector convention the oracle uses and uploaded
-in the library's storage order (factors transposed, value cache rank-major).
+in the library's storage order (factors transposed, value cache rank-major,
+bf16 factors and caches in operand tiles).
 
 Tolerance: max|got - ref| / max|ref| <= 1e-4 (f32) and 2e-2 (bf16)."""
 import numpy as np
@@ -15,6 +16,7 @@ from rank_decomposed_linear_amd import workloads as W
 from tests._helpers import TOL, f64, rand, relerr, to_dev, to_host
 
 lib_f = W.to_library_factor
+lib_ck = W.to_library_key_cache
 lib_cv = W.to_library_value_cache
 
 pytestmark = pytest.mark.gpu
@@ -76,11 +78,12 @@ def test_kv_append(B, T, dt):
     x = rand(r, (Bsz, T, m), 1.0, dt)
     Ak, Av = rand(r, (m, rk), 0.02, dt), rand(r, (m, rv), 0.02, dt)
     ck0, cv0 = rand(r, (Bsz, L_max, rk), 1.0, dt), rand(r, (Bsz, L_max, rv), 1.0, dt)
-    ck, cv = to_dev(ck0), to_dev(lib_cv(cv0))
+    ck, cv = to_dev(lib_ck(ck0)), to_dev(lib_cv(cv0))
     B.lowrank_kv_append(to_dev(x), to_dev(lib_f(Ak)), to_dev(lib_f(Av)), ck, cv, to_dev(past))
     torch.cuda.synchronize()
     wk, wv = ref.kv_append(f64(x), f64(Ak), f64(Av), f64(ck0), f64(cv0), past)
-    gk, gv = to_host(ck), W.from_library_value_cache(to_host(cv))
+    bf = dt == "bf16"
+    gk, gv = W.from_library_key_cache(to_host(ck), bf), W.from_library_value_cache(to_host(cv), bf)
     for b in range(Bsz):
         rows = slice(past[b], past[b] + T)
         assert relerr(gk[b, rows], wk[b, rows]) <= TOL[dt]
@@ -97,14 +100,14 @@ def test_kv_append(B, T, dt):
 # ----------------------------------------------------------------------------
 DECODE_CASES = [
     # (Bsz, n_q, n_kv, d, r_k, r_v, L_max, ctx_lens, theta, dtype)
-    (3, 8, 2, 128, 448, 448, 304, [1, 130, 300], 500000.0, "bf16"),
-    (2, 4, 4, 64, 64, 128, 40, [17, 40], 10000.0, "bf16"),
-    (2, 16, 1, 128, 128, 64, 264, [255, 129], 0.0, "bf16"),
-    (1, 64, 8, 128, 448, 448, 1104, [1025], 500000.0, "bf16"),
-    (2, 32, 8, 128, 320, 384, 600, [600, 77], 500000.0, "bf16"),
-    (2, 8, 2, 128, 640, 640, 2056, [2049, 700], 500000.0, "bf16"),   # ranks staged in chunks
-    (1, 40, 8, 128, 64, 128, 520, [515], 10000.0, "bf16"),             # 5 heads per kv head
-    (2, 12, 12, 64, 1024, 960, 136, [130, 64], 10000.0, "bf16"),       # largest ranks
+    (3, 8, 2, 128, 448, 448, 320, [1, 130, 300], 500000.0, "bf16"),
+    (2, 4, 4, 64, 64, 128, 64, [17, 40], 10000.0, "bf16"),
+    (2, 16, 1, 128, 128, 64, 288, [255, 129], 0.0, "bf16"),
+    (1, 64, 8, 128, 448, 448, 1120, [1025], 500000.0, "bf16"),
+    (2, 32, 8, 128, 320, 384, 608, [600, 77], 500000.0, "bf16"),
+    (2, 8, 2, 128, 640, 640, 2080, [2049, 700], 500000.0, "bf16"),   # ranks staged in chunks
+    (1, 40, 8, 128, 64, 128, 544, [515], 10000.0, "bf16"),             # 5 heads per kv head
+    (2, 12, 12, 64, 1024, 960, 160, [130, 64], 10000.0, "bf16"),       # largest ranks
     (2, 4, 4, 64, 64, 64, 40, [33, 40], 10000.0, "f32"),
     (2, 6, 2, 32, 12, 20, 50, [1, 50], 100.0, "f32"),
 ]
@@ -119,7 +122,7 @@ def test_attn_decode(B, case):
     ck, cv = rand(r, (Bsz, L_max, rk), 1.0, dt), rand(r, (Bsz, L_max, rv), 1.0, dt)
     Bk, Bv = rand(r, (rk, n_kv * d), 0.05, dt), rand(r, (rv, n_kv * d), 0.05, dt)
     lens = np.array(lens, np.int32)
-    out = B.lowrank_attn_decode(to_dev(q), to_dev(ck), to_dev(lib_cv(cv)), to_dev(lib_f(Bk)),
+    out = B.lowrank_attn_decode(to_dev(q), to_dev(lib_ck(ck)), to_dev(lib_cv(cv)), to_dev(lib_f(Bk)),
                                 to_dev(lib_f(Bv)), to_dev(lens), n_kv, 0.0, theta)
     want = ref.attn_decode(f64(q), f64(ck), f64(cv), f64(Bk), f64(Bv), lens, n_kv, theta)
     assert relerr(to_host(out), want) <= TOL[dt]
@@ -130,12 +133,12 @@ def test_attn_decode(B, case):
 # ----------------------------------------------------------------------------
 PREFILL_CASES = [
     # (Bsz, T, n_q, n_kv, d, r_k, r_v, L_max, past, theta, dtype)
-    (2, 70, 8, 1, 128, 64, 64, 200, [0, 50], 10000.0, "bf16"),
-    (2, 33, 8, 2, 64, 128, 64, 104, [5, 0], 500000.0, "bf16"),
-    (1, 130, 4, 4, 128, 64, 128, 264, [100], 10000.0, "bf16"),
-    (1, 20, 32, 2, 64, 64, 64, 40, [3], 0.0, "bf16"),
-    (2, 1, 16, 2, 128, 448, 448, 304, [299, 10], 500000.0, "bf16"),
-    (1, 200, 64, 8, 128, 448, 448, 216, [0], 500000.0, "bf16"),
+    (2, 70, 8, 1, 128, 64, 64, 224, [0, 50], 10000.0, "bf16"),
+    (2, 33, 8, 2, 64, 128, 64, 128, [5, 0], 500000.0, "bf16"),
+    (1, 130, 4, 4, 128, 64, 128, 288, [100], 10000.0, "bf16"),
+    (1, 20, 32, 2, 64, 64, 64, 64, [3], 0.0, "bf16"),
+    (2, 1, 16, 2, 128, 448, 448, 320, [299, 10], 500000.0, "bf16"),
+    (1, 200, 64, 8, 128, 448, 448, 224, [0], 500000.0, "bf16"),
     (2, 32, 4, 4, 64, 64, 64, 40, [0, 3], 10000.0, "f32"),
 ]
 
@@ -149,7 +152,7 @@ def test_attn_prefill(B, case):
     ck, cv = rand(r, (Bsz, L_max, rk), 1.0, dt), rand(r, (Bsz, L_max, rv), 1.0, dt)
     Bk, Bv = rand(r, (rk, n_kv * d), 0.05, dt), rand(r, (rv, n_kv * d), 0.05, dt)
     past = np.array(past, np.int32)
-    out = B.lowrank_attn_prefill(to_dev(q), to_dev(ck), to_dev(lib_cv(cv)), to_dev(lib_f(Bk)),
+    out = B.lowrank_attn_prefill(to_dev(q), to_dev(lib_ck(ck)), to_dev(lib_cv(cv)), to_dev(lib_f(Bk)),
                                  to_dev(lib_f(Bv)), to_dev(past), n_kv, 0.0, theta)
     want = ref.attn_prefill(f64(q), f64(ck), f64(cv), f64(Bk), f64(Bv), past, n_kv, theta)
     assert relerr(to_host(out), want) <= TOL[dt]
@@ -157,12 +160,12 @@ def test_attn_prefill(B, case):
 
 def test_explicit_softmax_scale(B):
     r = rng(5)
-    Bsz, n_q, n_kv, d, rk, L_max = 2, 8, 2, 128, 64, 72
+    Bsz, n_q, n_kv, d, rk, L_max = 2, 8, 2, 128, 64, 96
     q = rand(r, (Bsz, n_q, d), 1.0, "bf16")
     ck, cv = rand(r, (Bsz, L_max, rk), 1.0, "bf16"), rand(r, (Bsz, L_max, rk), 1.0, "bf16")
     Bk, Bv = rand(r, (rk, n_kv * d), 0.1, "bf16"), rand(r, (rk, n_kv * d), 0.1, "bf16")
     lens = np.array([70, 3], np.int32)
-    out = B.lowrank_attn_decode(to_dev(q), to_dev(ck), to_dev(lib_cv(cv)), to_dev(lib_f(Bk)),
+    out = B.lowrank_attn_decode(to_dev(q), to_dev(lib_ck(ck)), to_dev(lib_cv(cv)), to_dev(lib_f(Bk)),
                                 to_dev(lib_f(Bv)), to_dev(lens), n_kv, 0.3, 1000.0)
     want = ref.attn_decode(f64(q), f64(ck), f64(cv), f64(Bk), f64(Bv), lens, n_kv, 1000.0, 0.3)
     assert relerr(to_host(out), want) <= TOL["bf16"]

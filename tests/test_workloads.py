@@ -64,8 +64,8 @@ def test_draws_are_seeded_and_shaped():
 
 
 def test_library_storage_order():
-    """Factors are stored transposed, the value cache rank-major; both are
-    pure data movement and invertible."""
+    """f32 factors are stored transposed, the value cache rank-major; pure
+    data movement, invertible."""
     a = np.arange(6 * 4, dtype=np.float32).reshape(6, 4)     # A [m=6, k=4]
     t = W.to_library_factor(a)
     assert t.shape == (4, 6) and t.flags["C_CONTIGUOUS"]
@@ -74,7 +74,32 @@ def test_library_storage_order():
     c = W.to_library_value_cache(cv)
     assert c.shape == (2, 3, 5) and c.flags["C_CONTIGUOUS"]
     assert c[1, 2, 4] == cv[1, 4, 2]
-    assert np.array_equal(W.from_library_value_cache(c), cv)
+    assert np.array_equal(W.from_library_value_cache(c, False), cv)
+
+
+def test_operand_tile_order():
+    """bf16 storage is the transposed matrix in 16 x 32 operand tiles: element
+    (r, c) of an [R, C] matrix at tile (r // 16) * (C // 32) + c // 32, offset
+    ((c % 32) // 8 * 16 + r % 16) * 8 + c % 8 -- MFMA lane l = r % 16 +
+    16 * ((c % 32) // 8) holding 8 consecutive columns."""
+    R, C = 32, 96
+    a = (np.arange(R * C, dtype=np.uint32) % 65521).astype(np.uint16).reshape(R, C)
+    flat = W.tile_operands(a).reshape(-1)
+    for r, c in ((0, 0), (5, 7), (15, 8), (16, 31), (31, 95), (17, 40)):
+        off = ((r // 16) * (C // 32) + c // 32) * 512 + (((c % 32) // 8) * 16 + r % 16) * 8 + c % 8
+        assert flat[off] == a[r, c], (r, c)
+    assert np.array_equal(W.untile_operands(W.tile_operands(a)), a)
+    # a bf16 factor: transpose, then tiles
+    A = a.T.copy()                                            # A [m=96, k=32]
+    assert np.array_equal(W.to_library_factor(A), W.tile_operands(a))
+    # bf16 caches round-trip
+    ck = (np.arange(2 * 64 * 32, dtype=np.uint32) % 60000).astype(np.uint16).reshape(2, 64, 32)
+    assert np.array_equal(W.from_library_key_cache(W.to_library_key_cache(ck), True), ck)
+    cv = (np.arange(2 * 64 * 48, dtype=np.uint32) % 60000).astype(np.uint16).reshape(2, 64, 48)
+    assert np.array_equal(W.from_library_value_cache(W.to_library_value_cache(cv), True), cv)
+    import pytest
+    with pytest.raises(ValueError):
+        W.tile_operands(np.zeros((8, 32), np.uint16))
 
 
 def test_b_row_decay_scaling():
