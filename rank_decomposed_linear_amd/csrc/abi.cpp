@@ -711,8 +711,8 @@ struct LayerWS {
   // bf16 small-M path: split-K scratch, bf16 latents, f32 query and residual stream
   int *counters;
   int n_counters;
-  float *part, *q32, *x2f;
-  uint16_t *att16, *H16;
+  float *part, *q32, *x2f, *x2t;
+  uint16_t *att16, *H16, *a16t;
   // bf16 large-M (MFMA GEMM) path
   uint16_t *a16, *b16, *tq16, *q16, *to16, *tg16, *tu16, *G16, *U16, *td16;
 };
@@ -741,9 +741,12 @@ static void layer_gemvs(const dl_layer *L, const LayerDims &D, const LayerWS &w,
   g[G_QKV].past = past;
   g[G_QKV].T = D.T;
   g[G_QKV].L_max = D.L_max;
-  g[G_QKV].seg[0] = gvseg(L->q.A, x, h, w.tq16, D.rq, D.rq, GV_OUT_TILED);
-  g[G_QKV].seg[1] = gvseg(L->k.A, x, h, Ck, D.rk, D.rk, GV_OUT_CACHE);
-  g[G_QKV].seg[2] = gvseg(L->v.A, x, h, Cv, D.rv, D.rv, GV_OUT_CACHE_T);
+  // x arrives row-major; the step's init launch copies it into operand tiles
+  (void)x;
+  g[G_QKV].x_tiled = 1;
+  g[G_QKV].seg[0] = gvseg_t(L->q.A, w.a16t, h, w.tq16, D.rq, D.rq, GV_OUT_TILED);
+  g[G_QKV].seg[1] = gvseg_t(L->k.A, w.a16t, h, Ck, D.rk, D.rk, GV_OUT_CACHE);
+  g[G_QKV].seg[2] = gvseg_t(L->v.A, w.a16t, h, Cv, D.rv, D.rv, GV_OUT_CACHE_T);
 
   g[G_QUP] = gvargs(M, D.rq, 1);
   g[G_QUP].x_tiled = 1;
@@ -759,15 +762,17 @@ static void layer_gemvs(const dl_layer *L, const LayerDims &D, const LayerWS &w,
   g[G_OUP].seg[0].R = x;
   g[G_OUP].seg[0].ldr = h;
   g[G_OUP].seg[0].out2 = static_cast<float *>(x2_out);
+  g[G_OUP].seg[0].out_t = w.x2t;   // f32 operand tiles for the MLP's down halves
 
   g[G_GUD] = gvargs(M, h, 2);
   g[G_GUD].x_f32 = 1;
+  g[G_GUD].x_tiled = 1;
   g[G_GUD].norm = 1;
   g[G_GUD].gamma = L->mlp_norm;
   g[G_GUD].gamma_f32 = gf32;
   g[G_GUD].eps = L->rms_eps;
-  g[G_GUD].seg[0] = gvseg(L->gate.A, w.x2f, h, w.tg16, D.rg, D.rg, GV_OUT_TILED);
-  g[G_GUD].seg[1] = gvseg(L->up.A, w.x2f, h, w.tu16, D.ru, D.ru, GV_OUT_TILED);
+  g[G_GUD].seg[0] = gvseg_t(L->gate.A, w.x2t, h, w.tg16, D.rg, D.rg, GV_OUT_TILED);
+  g[G_GUD].seg[1] = gvseg_t(L->up.A, w.x2t, h, w.tu16, D.ru, D.ru, GV_OUT_TILED);
 
   g[G_GUU] = gvargs(M, D.rg, 1);
   g[G_GUU].K2 = D.ru;
@@ -816,6 +821,8 @@ static void carve_layer(Carver &c, const LayerDims &D, const dl_layer *L, LayerW
     w.part = c.take<float>(sc.part_floats);
     // operand-tiled intermediates ([Mpad, cols], Mpad = M rounded up to 16)
     const size_t Mp = mpad(D.M);
+    w.a16t = c.take<uint16_t>(Mp * D.h);
+    w.x2t = c.take<float>(Mp * D.h);
     w.tq16 = c.take<uint16_t>(Mp * D.rq);
     w.q32 = c.take<float>(M * D.qd());
     w.att16 = c.take<uint16_t>(Mp * D.qd());
@@ -949,10 +956,13 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
   if (use_gemv(M)) {
     GvArgs g[G_NUM];
     layer_gemvs(L, D, w, x, y, x2_out, Ck, Cv, past_lens, g);
-    FillRegion init[2] = {{reinterpret_cast<float *>(w.counters), nullptr, 0, w.n_counters},
+    FillRegion tiles{reinterpret_cast<float *>(w.a16t), x, 1, static_cast<int64_t>(mpad(M) * h / 8)};
+    tiles.tile_rows = M;
+    tiles.tile_cols = h;
+    FillRegion init[3] = {tiles, {reinterpret_cast<float *>(w.counters), nullptr, 0, w.n_counters},
                           {reinterpret_cast<float *>(aw.counters), nullptr, 0, aw.n_counters}};
     set_role(R_INIT);
-    DL_HIP(launch_fill(init, aw.counters ? 2 : 1, s));
+    DL_HIP(launch_fill(init, aw.counters ? 3 : 2, s));
     set_role(R_QKV_DOWN);
     DL_HIP(gemv_run(g[G_QKV], w.part, w.counters, s));
     set_role(R_Q_UP);

@@ -24,7 +24,8 @@
 //    context chunk as the rest of the 160 KB holds (scores and
 //    probabilities need 4 G + 32 bytes per position), so a split is
 //    normally walked in one chunk:
-//    phase 1: each wave rebuilds K^T for 64-position slices (A = factor
+//    phase 1: each wave rebuilds K^T for up to 64 positions at a time, an
+//      even share of the chunk's 16-position blocks per wave (A = factor
 //      fragment from LDS, read one rank step ahead; B = key-cache tile of
 //      16 positions, eight rank steps ahead), rotates the pairs in
 //      registers and forms S^T = K Q^T straight from the accumulators (the
@@ -115,6 +116,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
   __shared__ __attribute__((aligned(16))) u32x4 qfs[NB / 2][64];   // score operands, lane order
   __shared__ double rev64[HALF];
   __shared__ float rev32[HALF];
+  __shared__ float2 step16[HALF];   // (cos, sin) of the rotation over 16 positions
   __shared__ float smax[kNW][16], psw[kNW][16];
   __shared__ float mfin[16], lfin[16], cmb_m[16], cmb_l[16];
   __shared__ int last_flag;
@@ -156,6 +158,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
   for (int i = tid; i < HALF; i += kThreads) {
     rev64[i] = rope_on ? rope_rev(i, D, a.theta) : 0.0;
     rev32[i] = static_cast<float>(rev64[i]);
+    float c16, s16;
+    rope_cs(16, rev64[i], c16, s16);
+    step16[i] = float2{c16, s16};
   }
   if (n_rchunks == 1) {
     // resident factor: batches of 32 loads in flight before their LDS stores
@@ -221,13 +226,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
 
   for (int c0 = p_begin; c0 < p_end; c0 += pitch) {
     const int c1 = min(c0 + pitch, p_end);
-    const int nslices = (c1 - c0 + kSlice - 1) / kSlice;
     // ------------------------------ phase 1 ------------------------------
+    // the chunk's 16-position blocks are shared out evenly, a contiguous
+    // range per wave, taken kNP blocks at a time (the last group may be
+    // partial: its missing blocks repeat the last one and are not scored)
+    const int nblk = (c1 - c0 + 15) >> 4;
+    const int share = (nblk + kNW - 1) / kNW;
+    const int b_lo = min(wave * share, nblk), b_hi = min(b_lo + share, nblk);
     float mx = -INFINITY;
-    for (int sl = 0; sl < (nslices + kNW - 1) / kNW; ++sl) {
-      const int slice = wave + kNW * sl;
-      const bool active = slice < nslices;
-      const int P0 = c0 + kSlice * slice;
+    for (int gi = 0; gi < (share + kNP - 1) / kNP; ++gi) {   // same count in every wave
+      const int g0 = b_lo + kNP * gi;
+      const int np = max(0, min(kNP, b_hi - g0));          // blocks of this group
+      const bool active = np > 0;
+      const int P0 = c0 + 16 * g0;
       f32x4 acc[NB][kNP];
 #pragma unroll
       for (int x = 0; x < NB; ++x)
@@ -239,7 +250,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
       int crow[kNP];
 #pragma unroll
       for (int pb = 0; pb < kNP; ++pb)
-        crow[pb] = static_cast<int>(frag_off(min((P0 >> 4) + pb, (c1 - 1) >> 4), 0, a.r_k, lane));
+        crow[pb] = static_cast<int>(frag_off((c0 >> 4) + min(g0 + pb, max(b_hi - 1, 0)), 0, a.r_k, lane));
       for (int rc = 0; rc < n_rchunks; ++rc) {
         const int rs0 = rc * rs_cap, cnt = min(rs_cap, nrs - rs0);
         if (n_rchunks > 1) {
@@ -289,7 +300,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
       }
       if (active) {
         // lane (pos j, grp) holds K^T[16x + 4grp + r][P0 + 16pb + j]; block
-        // e < NE pairs with block NE + e
+        // e < NE pairs with block NE + e. The angle of block 0 is evaluated
+        // (exact float64 turn base, float32 offset); each further block
+        // rotates it by the 16-position step.
         if (rope_on) {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
@@ -298,15 +311,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
               const int fi = 16 * e + 4 * grp + r;
               double tb = static_cast<double>(P0) * rev64[fi];
               tb -= rint(tb);
-              const float base = static_cast<float>(tb);
-              const float rf = rev32[fi];
+              float c, s;
+              turn_cs(static_cast<float>(tb) + static_cast<float>(j) * rev32[fi], c, s);
+              const float2 st = step16[fi];
 #pragma unroll
               for (int pb = 0; pb < kNP; ++pb) {
-                float c, s;
-                turn_cs(base + static_cast<float>(16 * pb + j) * rf, c, s);
                 const float x = acc[e][pb][r], y = acc[NE + e][pb][r];
                 acc[e][pb][r] = x * c - y * s;
                 acc[NE + e][pb][r] = x * s + y * c;
+                const float cn = c * st.x - s * st.y;
+                s = c * st.y + s * st.x;
+                c = cn;
               }
             }
         }
@@ -317,12 +332,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
 #pragma unroll
           for (int t = 0; t < NB / 2; ++t)
             sc = mfma_bf16(pack_acc(acc[2 * t][pb], acc[2 * t + 1][pb]), qfs[t][lane], sc);
+          if (pb < np) {   // uniform: blocks past the group repeat its last one
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int off = P0 - c0 + 16 * pb + 4 * grp + r;
-            const float v = c0 + off < c1 ? sc[r] : -INFINITY;
-            mx = fmaxf(mx, v);
-            if (j < G) sS[j * pitch + off] = v;
+            for (int r = 0; r < 4; ++r) {
+              const int off = P0 - c0 + 16 * pb + 4 * grp + r;
+              const float v = c0 + off < c1 ? sc[r] : -INFINITY;
+              mx = fmaxf(mx, v);
+              if (j < G) sS[j * pitch + off] = v;
+            }
           }
         }
       }

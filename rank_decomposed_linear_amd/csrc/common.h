@@ -51,6 +51,13 @@ __device__ __forceinline__ size_t tile_off(int r, int c, int C) {
   return (static_cast<size_t>(r >> 4) * (C >> 5) + (c >> 5)) * 512 +
          ((((c & 31) >> 3) << 4) + (r & 15)) * 8 + (c & 7);
 }
+// float32 variant (2 KB tiles): the eight columns of a lane are split into
+// two 1 KB halves, columns 0..3 of every lane first, so each half of a
+// fragment is again one contiguous 1 KB read.
+__device__ __forceinline__ size_t tile_off_f32(int r, int c, int C) {
+  return (static_cast<size_t>(r >> 4) * (C >> 5) + (c >> 5)) * 512 +
+         ((((c & 7) >> 2) << 6) + (((c & 31) >> 3) << 4) + (r & 15)) * 4 + (c & 3);
+}
 // first element of operand fragment (row block rb, column step cs) of lane l
 __device__ __forceinline__ size_t frag_off(int rb, int cs, int C, int lane) {
   return (static_cast<size_t>(rb) * (C >> 5) + cs) * 512 + lane * 8;

@@ -49,6 +49,23 @@ __global__ void fill_kernel(FillPack p) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int k = 0; k < p.nreg; ++k) {
     const FillRegion &rg = p.r[k];
+    if (rg.tile_cols > 0) {
+      // chunk i = 8 bf16 of tile i / 64, lane i % 64
+      const int cs_n = rg.tile_cols >> 5;
+      for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < rg.n;
+           i += stride) {
+        const int64_t t = i >> 6;
+        const int ln = static_cast<int>(i & 63);
+        const int r = static_cast<int>(t / cs_n) * 16 + (ln & 15);
+        const int c = static_cast<int>(t % cs_n) * 32 + (ln >> 4) * 8;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (r < rg.tile_rows)
+          v = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(rg.src) +
+                                               static_cast<size_t>(r) * rg.tile_cols + c);
+        reinterpret_cast<u32x4 *>(rg.dst)[i] = v;
+      }
+      continue;
+    }
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < rg.n;
          i += stride) {
       float v = 0.f;

@@ -73,8 +73,9 @@ __device__ __forceinline__ int xcd_item(int b, int grid) {
   return (b & 7) * per + (b >> 3);
 }
 
-// Activation modes: row-major bf16, row-major f32, operand-tiled bf16.
-enum XMode : int { XM_BF16 = 0, XM_F32 = 1, XM_TILED = 2 };
+// Activation modes: row-major bf16, row-major f32, operand-tiled bf16,
+// operand-tiled f32.
+enum XMode : int { XM_BF16 = 0, XM_F32 = 1, XM_TILED = 2, XM_F32_TILED = 3 };
 
 // Activation rows are loaded raw into the prefetch ring with the weights
 // (so waiting for a step never waits for later prefetches) and converted to
@@ -83,8 +84,13 @@ enum XMode : int { XM_BF16 = 0, XM_F32 = 1, XM_TILED = 2 };
 // step k / 32) of an [Mpad, cols] operand-tiled matrix.
 template <int XM>
 __device__ __forceinline__ void load_x_raw(const void *X, int ldx, int row, int mb, int k, int lane,
-                                           u32x4 (&r)[XM == XM_F32 ? 2 : 1]) {
-  if constexpr (XM == XM_F32) {
+                                           u32x4 (&r)[(XM == XM_F32 || XM == XM_F32_TILED) ? 2 : 1]) {
+  if constexpr (XM == XM_F32_TILED) {
+    const float *p = static_cast<const float *>(X) +
+                     (static_cast<size_t>(mb) * (ldx >> 5) + (k >> 5)) * 512 + lane * 4;
+    r[0] = *reinterpret_cast<const u32x4 *>(p);
+    r[1] = *reinterpret_cast<const u32x4 *>(p + 256);
+  } else if constexpr (XM == XM_F32) {
     const float *p = static_cast<const float *>(X) + static_cast<size_t>(row) * ldx + k;
     r[0] = *reinterpret_cast<const u32x4 *>(p);
     r[1] = *reinterpret_cast<const u32x4 *>(p + 4);
@@ -145,7 +151,8 @@ __device__ __forceinline__ u32x4 make_x(const u32x4 (&r)[XF32 ? 2 : 1],
 
 template <int MB, int XM, int PAIRED, int NORM, int GF32, int kWaves>
 __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
-  constexpr int XF32 = XM == XM_F32;
+  constexpr int XF32 = XM == XM_F32 || XM == XM_F32_TILED;
+  constexpr bool XT = XM == XM_TILED || XM == XM_F32_TILED;
   constexpr int kThreads = kWaves * 64;
   constexpr int HALVES = PAIRED ? 2 : 1;
   constexpr int NACC = HALVES * MB;          // f32x4 accumulators per lane
@@ -206,12 +213,12 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
     k -= second ? a.K : 0;
     const uint16_t *wp = (second ? w2 : w1) + static_cast<size_t>(k >> 5) * 512;
     sb.w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wp));
-    if constexpr (XM == XM_TILED) {
+    if constexpr (XT) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) load_x_raw<XM>(X, ldx, 0, mb, k, lane, sb.x[mb]);
     }
     k += 8 * grp;
-    if constexpr (XM != XM_TILED) {
+    if constexpr (!XT) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) load_x_raw<XM>(X, ldx, min(mb * 16 + j, a.M - 1), mb, k, lane, sb.x[mb]);
     }
@@ -406,6 +413,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
       const f32x4 o = f32x4{v[0], v[1], v[2], v[3]};
       *reinterpret_cast<f32x4 *>(static_cast<float *>(sg.out) + oi) = o;
       if (sg.out2) *reinterpret_cast<f32x4 *>(sg.out2 + oi) = o;
+      if (sg.out_t) *reinterpret_cast<f32x4 *>(sg.out_t + tile_off_f32(m, n, sg.N)) = o;
       break;
     }
     case GV_OUT_RES_BF16: {
@@ -440,8 +448,13 @@ hipError_t launch_mb(const GvArgs &a, int grid, hipStream_t s) {
   if (a.K2 > 0)
     return a.x_tiled ? launch_t<MB, XM_TILED, 1, 0, 0>(a, grid, s) : launch_t<MB, XM_BF16, 1, 0, 0>(a, grid, s);
   if (a.norm) {
+    if (a.x_f32 && a.x_tiled)
+      return a.gamma_f32 ? launch_t<MB, XM_F32_TILED, 0, 1, 1>(a, grid, s)
+                         : launch_t<MB, XM_F32_TILED, 0, 1, 0>(a, grid, s);
     if (a.x_f32)
       return a.gamma_f32 ? launch_t<MB, XM_F32, 0, 1, 1>(a, grid, s) : launch_t<MB, XM_F32, 0, 1, 0>(a, grid, s);
+    if (a.x_tiled)
+      return a.gamma_f32 ? launch_t<MB, XM_TILED, 0, 1, 1>(a, grid, s) : launch_t<MB, XM_TILED, 0, 1, 0>(a, grid, s);
     return a.gamma_f32 ? launch_t<MB, XM_BF16, 0, 1, 1>(a, grid, s) : launch_t<MB, XM_BF16, 0, 1, 0>(a, grid, s);
   }
   if (a.x_tiled) return launch_t<MB, XM_TILED, 0, 0, 0>(a, grid, s);

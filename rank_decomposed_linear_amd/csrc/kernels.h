@@ -36,6 +36,7 @@ struct GvSeg {
   const void *X2;      // paired: second-half activations, like X with K2
   void *out;
   float *out2;         // optional copy (GV_OUT_RES_F32)
+  float *out_t;        // optional f32 operand-tile copy [Mpad, N] (GV_OUT_RES_F32)
   const void *R;       // residual [M, ldr]
   int N, ldx, ldx2, ldo, ldr;
   int omode, res_f32;
@@ -47,7 +48,7 @@ struct GvArgs {
   int nseg;
   int M, K, K2;           // K2 > 0 only for paired launches (then nseg == 1)
   int x_f32;              // X is f32 (else bf16); paired launches use bf16
-  int x_tiled;            // X (and X2) are operand-tiled bf16
+  int x_tiled;            // X (and X2) are operand-tiled (bf16, or f32 tiles with x_f32)
   int norm;               // fused RMSNorm: X scaled by gamma, rows of the result by
                           // 1 / sqrt(mean(X^2) + eps) (mean over the K columns)
   const void *gamma;      // [K] gains or NULL (= 1)
@@ -191,12 +192,16 @@ hipError_t launch_attn_f32(const AttnF32Args &a, hipStream_t s);
 hipError_t launch_rmsnorm(const void *x, int x_f32, const void *gamma, int gamma_f32, void *y,
                           int y_f32, int M, int n, float eps, hipStream_t s);
 // Up to four f32 regions: region i gets zero (src == NULL) or a copy of a
-// bf16 source (src_bf16 != NULL) or an f32 source.
+// bf16 source (src_bf16 != NULL) or an f32 source. With tile_cols > 0 the
+// region is instead a bf16 operand-tile copy: src bf16 row-major
+// [tile_rows, tile_cols] -> dst bf16 tiles [tile_rows rounded up to 16,
+// tile_cols], padding rows zero; n counts 16-byte chunks of dst.
 struct FillRegion {
   float *dst;
   const void *src;
   int src_bf16;
   int64_t n;
+  int tile_rows = 0, tile_cols = 0;
 };
 hipError_t launch_fill(const FillRegion *r, int nreg, hipStream_t s);
 // dst (bf16 or f32) = src f32
