@@ -234,71 +234,98 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
     const int share = (nblk + kNW - 1) / kNW;
     const int b_lo = min(wave * share, nblk), b_hi = min(b_lo + share, nblk);
     float mx = -INFINITY;
-    for (int gi = 0; gi < (share + kNP - 1) / kNP; ++gi) {   // same count in every wave
-      const int g0 = b_lo + kNP * gi;
-      const int np = max(0, min(kNP, b_hi - g0));          // blocks of this group
-      const bool active = np > 0;
-      const int P0 = c0 + 16 * g0;
-      f32x4 acc[NB][kNP];
-#pragma unroll
-      for (int x = 0; x < NB; ++x)
-#pragma unroll
-        for (int pb = 0; pb < kNP; ++pb) acc[x][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      // key tiles of the slice's 16-position blocks (element offsets within
-      // the sequence's cache, L_max * r < 2^31); blocks past the chunk end
-      // repeat its last block and their scores are masked
-      int crow[kNP];
+    const int ngr = (share + kNP - 1) / kNP;   // same count in every wave
+    // key-tile rows of group gi (element offsets within the sequence's
+    // cache, L_max * r < 2^31); blocks past the wave's range repeat its
+    // last block, are multiplied only inside a group of four and never scored
+    int crow[kNP];
+    auto set_rows = [&](int gi) {
 #pragma unroll
       for (int pb = 0; pb < kNP; ++pb)
-        crow[pb] = static_cast<int>(frag_off((c0 >> 4) + min(g0 + pb, max(b_hi - 1, 0)), 0, a.r_k, lane));
-      for (int rc = 0; rc < n_rchunks; ++rc) {
-        const int rs0 = rc * rs_cap, cnt = min(rs_cap, nrs - rs0);
-        if (n_rchunks > 1) {
-          __syncthreads();
-          load_factor(rs0, cnt);
-          __syncthreads();
-        }
-        if (active) {
-          // cache rows kCDepth rank steps ahead, factor fragments one step
-          // ahead; loads past the last step repeat it (every load stays
-          // unconditional) and their products are masked out
-          u32x4 cf[kCDepth][kNP];
-#pragma unroll
-          for (int d = 0; d < kCDepth; ++d) {
-#pragma unroll
-            for (int pb = 0; pb < kNP; ++pb) cf[d][pb] = ld16(ck_b + crow[pb] + 512 * (rs0 + min(d, cnt - 1)));
-            __builtin_amdgcn_sched_barrier(0);
+        crow[pb] = static_cast<int>(frag_off((c0 >> 4) + min(b_lo + kNP * gi + pb, max(b_hi - 1, 0)), 0, a.r_k, lane));
+    };
+    const bool resident = n_rchunks == 1;   // else staged per rank chunk
+    for (int gi = 0; gi < ngr; ++gi) {
+      const int g0 = b_lo + kNP * gi;
+      const int np = max(0, min(kNP, b_hi - g0));   // blocks of this group; a partial group is the wave's last
+      if (np == 0) {
+        // no blocks: still take part in the workgroup's factor staging
+        if (!resident) {
+          for (int rc = 0; rc < n_rchunks; ++rc) {
+            __syncthreads();
+            load_factor(rc * rs_cap, min(rs_cap, nrs - rc * rs_cap));
+            __syncthreads();
           }
+        }
+        continue;
+      }
+      const int P0 = c0 + 16 * g0;
+      set_rows(gi);
+      // the group: K^T for NPA blocks of 16 positions, rotated, scored
+      auto group = [&](auto npc) {
+        constexpr int NPA = decltype(npc)::value;
+        f32x4 acc[NB][NPA];
+#pragma unroll
+        for (int x = 0; x < NB; ++x)
+#pragma unroll
+          for (int pb = 0; pb < NPA; ++pb) acc[x][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int rc = 0; rc < n_rchunks; ++rc) {
+          const int rs0 = rc * rs_cap, cnt = min(rs_cap, nrs - rs0);
+          if (!resident) {
+            __syncthreads();
+            load_factor(rs0, cnt);
+            __syncthreads();
+          }
+          // cache tiles kCDepth rank steps ahead; prefetches past the last
+          // step repeat it (every load stays unconditional) and are never
+          // multiplied
+          u32x4 cf[kCDepth][NPA];
+#pragma unroll
+          for (int d = 0; d < kCDepth; ++d)
+#pragma unroll
+            for (int pb = 0; pb < NPA; ++pb) cf[d][pb] = ld16(ck_b + crow[pb] + 512 * (rs0 + min(d, cnt - 1)));
+          // factor fragments one rank step ahead
           u32x4 bop[2][NB];
 #pragma unroll
           for (int x = 0; x < NB; ++x)
             bop[0][x] = *reinterpret_cast<const u32x4 *>(bs + (static_cast<size_t>(x) * 64 + lane) * 8);
-          for (int s0 = 0; s0 < cnt; s0 += kCDepth) {
+          // One rank step: next step's factor fragments from LDS, the
+          // products of this step (position block by position block, so
+          // each cache tile is free for its refill after NB products), the
+          // refills. With one wave per SIMD nothing else fills the matrix
+          // pipe, so the LDS reads and loads are spread between the
+          // products instead of issued in runs.
+          auto rank_step = [&](auto dc, int s) {
+            constexpr int d = decltype(dc)::value;
+            const uint16_t *fr = bs + (static_cast<size_t>(min(s + 1, cnt - 1) * NB) * 64 + lane) * 8;
 #pragma unroll
-            for (int d = 0; d < kCDepth; ++d) {
-              const int s = s0 + d;
-              const bool valid = s < cnt;
-              const uint16_t *fr = bs + (static_cast<size_t>(min(s + 1, cnt - 1) * NB) * 64 + lane) * 8;
+            for (int x = 0; x < NB; ++x) bop[(d + 1) & 1][x] = *reinterpret_cast<const u32x4 *>(fr + x * 64 * 8);
 #pragma unroll
-              for (int x = 0; x < NB; ++x) bop[(d + 1) & 1][x] = *reinterpret_cast<const u32x4 *>(fr + x * 64 * 8);
-              __builtin_amdgcn_sched_barrier(0);
-              u32x4 cop[kNP];
+            for (int pb = 0; pb < NPA; ++pb)
 #pragma unroll
-              for (int pb = 0; pb < kNP; ++pb) cop[pb] = valid ? cf[d][pb] : u32x4{0u, 0u, 0u, 0u};
+              for (int x = 0; x < NB; ++x) acc[x][pb] = mfma_bf16(bop[d & 1][x], cf[d][pb], acc[x][pb]);
+            const int sn = rs0 + min(s + kCDepth, cnt - 1);
 #pragma unroll
-              for (int x = 0; x < NB; ++x)
+            for (int pb = 0; pb < NPA; ++pb) cf[d][pb] = ld16(ck_b + crow[pb] + 512 * sn);
 #pragma unroll
-                for (int pb = 0; pb < kNP; ++pb) acc[x][pb] = mfma_bf16(bop[d & 1][x], cop[pb], acc[x][pb]);
-              __builtin_amdgcn_sched_barrier(0);
-              const int sn = rs0 + min(s + kCDepth, cnt - 1);
+            for (int pb = 0; pb < NPA; ++pb) {
 #pragma unroll
-              for (int pb = 0; pb < kNP; ++pb) cf[d][pb] = ld16(ck_b + crow[pb] + 512 * sn);
-              __builtin_amdgcn_sched_barrier(0);
+              for (int q = 0; q < NB / NPA; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, NPA, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // LDS read
+              }
+              __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);   // VALU (load address)
+              __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
             }
+          };
+          int s0 = 0;
+          for (; s0 + kCDepth <= cnt; s0 += kCDepth) {
+            static_for<kCDepth>([&](auto dc) { rank_step(dc, s0 + decltype(dc)::value); });
           }
+          static_for<kCDepth>([&](auto dc) {
+            if (s0 + decltype(dc)::value < cnt) rank_step(dc, s0 + decltype(dc)::value);
+          });
         }
-      }
-      if (active) {
         // lane (pos j, grp) holds K^T[16x + 4grp + r][P0 + 16pb + j]; block
         // e < NE pairs with block NE + e. The angle of block 0 is evaluated
         // (exact float64 turn base, float32 offset); each further block
@@ -311,28 +338,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
               const int fi = 16 * e + 4 * grp + r;
               double tb = static_cast<double>(P0) * rev64[fi];
               tb -= rint(tb);
-              float c, s;
-              turn_cs(static_cast<float>(tb) + static_cast<float>(j) * rev32[fi], c, s);
+              float c, sn;
+              turn_cs(static_cast<float>(tb) + static_cast<float>(j) * rev32[fi], c, sn);
               const float2 st = step16[fi];
 #pragma unroll
-              for (int pb = 0; pb < kNP; ++pb) {
+              for (int pb = 0; pb < NPA; ++pb) {
                 const float x = acc[e][pb][r], y = acc[NE + e][pb][r];
-                acc[e][pb][r] = x * c - y * s;
-                acc[NE + e][pb][r] = x * s + y * c;
-                const float cn = c * st.x - s * st.y;
-                s = c * st.y + s * st.x;
+                acc[e][pb][r] = x * c - y * sn;
+                acc[NE + e][pb][r] = x * sn + y * c;
+                const float cn = c * st.x - sn * st.y;
+                sn = c * st.y + sn * st.x;
                 c = cn;
               }
             }
         }
         // S^T[pos, h]: lane (head j, grp) holds S^T[P0 + 16pb + 4grp + r][j]
 #pragma unroll
-        for (int pb = 0; pb < kNP; ++pb) {
+        for (int pb = 0; pb < NPA; ++pb) {
           f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int t = 0; t < NB / 2; ++t)
             sc = mfma_bf16(pack_acc(acc[2 * t][pb], acc[2 * t + 1][pb]), qfs[t][lane], sc);
-          if (pb < np) {   // uniform: blocks past the group repeat its last one
+          if (pb < np) {   // uniform
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int off = P0 - c0 + 16 * pb + 4 * grp + r;
@@ -342,7 +369,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
             }
           }
         }
-      }
+      };
+      if (np >= 3) group(IntC<kNP>{});
+      else if (np == 2) group(IntC<2>{});
+      else group(IntC<1>{});
     }
     mx = wave_max_xor(mx, 16);
     mx = wave_max_xor(mx, 32);

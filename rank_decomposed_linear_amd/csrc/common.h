@@ -103,4 +103,18 @@ __device__ __forceinline__ double rope_rev(int i, int d, float theta) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
+// Compile-time loop: f(IntC<0>{}), ..., f(IntC<N - 1>{}), so the index can
+// select register arrays and scheduling groups statically.
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(IntC<I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
 }  // namespace dl
