@@ -13,7 +13,9 @@ A "step" is one dl_decomposed_layer_fwd call over the whole batch. Inputs
 are seeded synthetic data resident in HBM before timing starts; two
 independent device copies of weights and cache are used in turn so the
 256 MB Infinity Cache cannot serve one step from the previous one. Steps are
-replayed from a HIP graph (one per copy) unless --no-graph.
+replayed from one HIP graph that holds one step per copy, as a multi-layer
+model would capture its layers, unless --no-graph; a step count that is not
+a multiple of the copies ends with single-step graphs, so exactly K steps run.
 
 Per-kernel durations come from hipEvents that the library records around
 each of its launches on the launch stream. A traced step is queued behind a
@@ -147,6 +149,7 @@ def run_step(st):
 
 
 def capture_graphs(torch, sets):
+    """One graph per copy, plus one graph that runs the copies in turn."""
     graphs = []
     side = torch.cuda.Stream()
     for st in sets:
@@ -158,8 +161,20 @@ def capture_graphs(torch, sets):
         with torch.cuda.graph(g):
             run_step(st)
         graphs.append(g)
+    chain = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(chain):
+        for st in sets:
+            run_step(st)
     torch.cuda.synchronize()
-    return graphs
+    return graphs, chain
+
+
+def step_fn(graphs, chain, steps):
+    """fn(i) for i < calls runs the steps: chained replays, then singles."""
+    n = len(graphs)
+    full = steps // n
+    calls = full + steps % n
+    return (lambda i: chain.replay() if i < full else graphs[(i - full) % n].replay()), calls
 
 
 def timed(torch, fn, steps, warmup):
@@ -228,9 +243,10 @@ def decode_bench(args, torch, binding, W):
     graphs = None
     if use_graph:
         try:
-            graphs = capture_graphs(torch, sets)
-            for _ in range(3):
-                graphs[0].replay()
+            graphs, chain = capture_graphs(torch, sets)
+            for g in (graphs[0], chain, graphs[0]):
+                sets[0]["y"].zero_()
+                g.replay()
                 torch.cuda.synchronize()
                 err = (sets[0]["y"].float() - y_eager).abs().max().item()
                 if not err <= 1e-2 * y_eager.abs().max().item():
@@ -238,12 +254,17 @@ def decode_bench(args, torch, binding, W):
         except Exception as e:  # keep the eager figure if capture is refused
             log(f"graph capture disabled: {e}")
             use_graph, graphs = False, None
+    log(f"timing {args.steps} steps after {args.warmup} warmup (graph={use_graph})")
     if graphs:
-        fn = lambda i: graphs[i % len(graphs)].replay()
+        fn, calls = step_fn(graphs, chain, args.steps)
+        wfn, wcalls = step_fn(graphs, chain, args.warmup)
+        for i in range(wcalls):
+            wfn(i)
+        ms, wall = timed(torch, fn, calls, 0)
+        ms *= calls / args.steps
     else:
         fn = lambda i: run_step(sets[i % len(sets)])
-    log(f"timing {args.steps} steps after {args.warmup} warmup (graph={use_graph})")
-    ms, wall = timed(torch, fn, args.steps, args.warmup)
+        ms, wall = timed(torch, fn, args.steps, args.warmup)
 
     per = trace_breakdown(torch, binding, sets, args.trace_steps)
     ctx_total = int(sum(int(p) + 1 for p in inp.past_lens))

@@ -711,8 +711,8 @@ struct LayerWS {
   // bf16 small-M path: split-K scratch, bf16 latents, f32 query and residual stream
   int *counters;
   int n_counters;
-  float *part, *q32, *x2f, *x2t;
-  uint16_t *att16, *H16, *a16t;
+  float *part, *q32, *x2f, *ssq;
+  uint16_t *att16, *H16, *a16t, *x2g;
   // bf16 large-M (MFMA GEMM) path
   uint16_t *a16, *b16, *tq16, *q16, *to16, *tg16, *tu16, *G16, *U16, *td16;
 };
@@ -720,11 +720,13 @@ struct LayerWS {
 enum { G_QKV, G_QUP, G_ODOWN, G_OUP, G_GUD, G_GUU, G_DD, G_DU, G_NUM };
 
 // The eight GEMV launches of a small-M layer step:
-//   qkv_down  RMSNorm(x) [A_q A_k A_v]; k, v latents scattered into the cache
+//   (init)    RMSNorm(x) into operand tiles; split-K counters zeroed
+//   qkv_down  x_n [A_q A_k A_v]; k, v latents scattered into the cache
 //   q_up      t_q B_q -> f32 query
 //   o_down    o A_o
-//   o_up      x2 = x + t_o B_o (f32 residual stream; copy to x2_out)
-//   gate_up   RMSNorm(x2) [A_gate A_up]
+//   o_up      x2 = x + t_o B_o (f32 residual stream; copy to x2_out), plus
+//             g_mlp * x2 as bf16 tiles and its row sums of squares per tile
+//   gate_up   (g_mlp * x2) [A_gate A_up], rows scaled by 1 / rms(x2)
 //   gu_up     H = silu(t_g B_gate) * (t_u B_up)   (one paired launch)
 //   down_down H A_down
 //   down_up   y = x2 + t_d B_down
@@ -734,14 +736,10 @@ static void layer_gemvs(const dl_layer *L, const LayerDims &D, const LayerWS &w,
   const int M = D.M, h = D.h, qd = D.qd();
   const int gf32 = L->dt == DL_F32;
   g[G_QKV] = gvargs(M, h, 3);
-  g[G_QKV].norm = 1;
-  g[G_QKV].gamma = L->attn_norm;
-  g[G_QKV].gamma_f32 = gf32;
-  g[G_QKV].eps = L->rms_eps;
   g[G_QKV].past = past;
   g[G_QKV].T = D.T;
   g[G_QKV].L_max = D.L_max;
-  // x arrives row-major; the step's init launch copies it into operand tiles
+  // x arrives row-major; the step's init launch normalises it into operand tiles
   (void)x;
   g[G_QKV].x_tiled = 1;
   g[G_QKV].seg[0] = gvseg_t(L->q.A, w.a16t, h, w.tq16, D.rq, D.rq, GV_OUT_TILED);
@@ -762,17 +760,18 @@ static void layer_gemvs(const dl_layer *L, const LayerDims &D, const LayerWS &w,
   g[G_OUP].seg[0].R = x;
   g[G_OUP].seg[0].ldr = h;
   g[G_OUP].seg[0].out2 = static_cast<float *>(x2_out);
-  g[G_OUP].seg[0].out_t = w.x2t;   // f32 operand tiles for the MLP's down halves
+  g[G_OUP].seg[0].out_nt = w.x2g;   // the MLP norm's input for the down halves
+  g[G_OUP].seg[0].gamma = L->mlp_norm;
+  g[G_OUP].seg[0].gamma_f32 = gf32;
+  g[G_OUP].seg[0].ssq_out = w.ssq;
 
   g[G_GUD] = gvargs(M, h, 2);
-  g[G_GUD].x_f32 = 1;
   g[G_GUD].x_tiled = 1;
-  g[G_GUD].norm = 1;
-  g[G_GUD].gamma = L->mlp_norm;
-  g[G_GUD].gamma_f32 = gf32;
+  g[G_GUD].rs_part = w.ssq;
+  g[G_GUD].rs_cols = h / 16;
   g[G_GUD].eps = L->rms_eps;
-  g[G_GUD].seg[0] = gvseg_t(L->gate.A, w.x2t, h, w.tg16, D.rg, D.rg, GV_OUT_TILED);
-  g[G_GUD].seg[1] = gvseg_t(L->up.A, w.x2t, h, w.tu16, D.ru, D.ru, GV_OUT_TILED);
+  g[G_GUD].seg[0] = gvseg_t(L->gate.A, w.x2g, h, w.tg16, D.rg, D.rg, GV_OUT_TILED);
+  g[G_GUD].seg[1] = gvseg_t(L->up.A, w.x2g, h, w.tu16, D.ru, D.ru, GV_OUT_TILED);
 
   g[G_GUU] = gvargs(M, D.rg, 1);
   g[G_GUU].K2 = D.ru;
@@ -822,7 +821,8 @@ static void carve_layer(Carver &c, const LayerDims &D, const dl_layer *L, LayerW
     // operand-tiled intermediates ([Mpad, cols], Mpad = M rounded up to 16)
     const size_t Mp = mpad(D.M);
     w.a16t = c.take<uint16_t>(Mp * D.h);
-    w.x2t = c.take<float>(Mp * D.h);
+    w.x2g = c.take<uint16_t>(Mp * D.h);
+    w.ssq = c.take<float>(static_cast<size_t>(D.M) * (D.h / 16));
     w.tq16 = c.take<uint16_t>(Mp * D.rq);
     w.q32 = c.take<float>(M * D.qd());
     w.att16 = c.take<uint16_t>(Mp * D.qd());
@@ -956,13 +956,12 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
   if (use_gemv(M)) {
     GvArgs g[G_NUM];
     layer_gemvs(L, D, w, x, y, x2_out, Ck, Cv, past_lens, g);
-    FillRegion tiles{reinterpret_cast<float *>(w.a16t), x, 1, static_cast<int64_t>(mpad(M) * h / 8)};
-    tiles.tile_rows = M;
-    tiles.tile_cols = h;
-    FillRegion init[3] = {tiles, {reinterpret_cast<float *>(w.counters), nullptr, 0, w.n_counters},
+    FillRegion zero[2] = {{reinterpret_cast<float *>(w.counters), nullptr, 0, w.n_counters},
                           {reinterpret_cast<float *>(aw.counters), nullptr, 0, aw.n_counters}};
     set_role(R_INIT);
-    DL_HIP(launch_fill(init, aw.counters ? 3 : 2, s));
+    DL_HIP(launch_norm_tiles(static_cast<const uint16_t *>(x), L->attn_norm, L->dt == DL_F32,
+                             L->rms_eps, w.a16t, M, static_cast<int>(mpad(M)), h, zero,
+                             aw.counters ? 2 : 1, s));
     set_role(R_QKV_DOWN);
     DL_HIP(gemv_run(g[G_QKV], w.part, w.counters, s));
     set_role(R_Q_UP);

@@ -2,6 +2,8 @@
 // initialisation (fills and copies) and float32 -> storage conversion.
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 #include "trace.h"
@@ -75,6 +77,83 @@ __global__ void fill_kernel(FillPack p) {
   }
 }
 
+// Zero the fill regions (src NULL) with the workgroups [b0, gridDim.x).
+__device__ void zero_regions(const FillPack &p, int b0) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x - b0) * blockDim.x;
+  for (int k = 0; k < p.nreg; ++k)
+    for (int64_t i = static_cast<int64_t>(blockIdx.x - b0) * blockDim.x + threadIdx.x; i < p.r[k].n;
+         i += stride)
+      p.r[k].dst[i] = 0.f;
+}
+
+// RMSNorm of row m = blockIdx.x < Mp into bf16 operand tiles (rows >= M
+// zero); workgroups past Mp zero the fill regions. Eight columns per chunk:
+// one 16-byte read of x, one 16-byte write of the tile (columns c .. c + 7
+// of a row are contiguous in a tile when c % 8 == 0).
+__global__ __launch_bounds__(256) void norm_tiles_kernel(const uint16_t *x, const void *gamma,
+                                                         int gamma_f32, float eps, uint16_t *xt,
+                                                         int M, int Mp, int n, FillPack z) {
+  const int m = blockIdx.x;
+  if (m >= Mp) {
+    zero_regions(z, Mp);
+    return;
+  }
+  __shared__ float part[4];
+  const int nch = n >> 3;
+  const uint16_t *row = x + static_cast<size_t>(m) * n;
+  // chunks i = threadIdx.x + 256 c stay in registers between the sum of
+  // squares and the store (up to kCh per thread; longer rows reread the rest)
+  constexpr int kCh = 8;
+  u32x4 v[kCh];
+  float ss = 0.f;
+  auto sumsq = [&](const u32x4 &w) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float lo = bflo(w[q]), hi = bfhi(w[q]);
+      ss = fmaf(lo, lo, ss);
+      ss = fmaf(hi, hi, ss);
+    }
+  };
+#pragma unroll
+  for (int c = 0; c < kCh; ++c) {
+    const int i = threadIdx.x + 256 * c;
+    v[c] = u32x4{0u, 0u, 0u, 0u};
+    if (m < M && i < nch) v[c] = *reinterpret_cast<const u32x4 *>(row + 8 * i);
+  }
+#pragma unroll
+  for (int c = 0; c < kCh; ++c) sumsq(v[c]);
+  if (m < M)
+    for (int i = threadIdx.x + 256 * kCh; i < nch; i += 256) sumsq(*reinterpret_cast<const u32x4 *>(row + 8 * i));
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float rstd = 1.0f / sqrtf((part[0] + part[1] + part[2] + part[3]) / n + eps);
+  auto store = [&](int i, const u32x4 &w) {
+    u32x4 o = {0u, 0u, 0u, 0u};
+    if (m < M) {
+      float f[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f[2 * q] = bflo(w[q]) * rstd;
+        f[2 * q + 1] = bfhi(w[q]) * rstd;
+      }
+      if (gamma) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] *= load_elem(gamma, gamma_f32, 8 * i + e);
+      }
+      o = u32x4{pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
+    }
+    *reinterpret_cast<u32x4 *>(xt + tile_off(m, 8 * i, n)) = o;
+  };
+#pragma unroll
+  for (int c = 0; c < kCh; ++c) {
+    const int i = threadIdx.x + 256 * c;
+    if (i < nch) store(i, v[c]);
+  }
+  for (int i = threadIdx.x + 256 * kCh; i < nch; i += 256)
+    store(i, m < M ? *reinterpret_cast<const u32x4 *>(row + 8 * i) : u32x4{0u, 0u, 0u, 0u});
+}
+
 __global__ void convert_kernel(const float *src, void *dst, int dst_bf16, int64_t n) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
@@ -111,6 +190,22 @@ hipError_t launch_fill(const FillRegion *r, int nreg, hipStream_t s) {
   }
   p.nreg = nreg < 4 ? nreg : 4;
   fill_kernel<<<grid_for(mx), 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_tiles(const uint16_t *x, const void *gamma, int gamma_f32, float eps,
+                             uint16_t *xt, int M, int Mp, int n, const FillRegion *zero, int nzero,
+                             hipStream_t s) {
+  TraceGuard trace_guard(K_RMSNORM, s);
+  FillPack p{};
+  int64_t mx = 0;
+  for (int i = 0; i < nzero && i < 4; ++i) {
+    p.r[i] = zero[i];
+    if (zero[i].n > mx) mx = zero[i].n;
+  }
+  p.nreg = nzero < 4 ? nzero : 4;
+  const int zgrid = p.nreg ? static_cast<int>(std::min<int64_t>((mx + 255) / 256, 64)) : 0;
+  norm_tiles_kernel<<<Mp + zgrid, 256, 0, s>>>(x, gamma, gamma_f32, eps, xt, M, Mp, n, p);
   return hipGetLastError();
 }
 

@@ -15,12 +15,15 @@
 //    16 l .. 16 l + 15, one contiguous 1 KB per instruction): that is the
 //    MFMA A operand, rows n0 + l % 16. The token rows are the B operand,
 //    x[m][k0 + 8 (l / 16) ..]: from an operand-tiled activation (one
-//    contiguous 1 KB again) or from a plain row-major one, optionally
-//    passed through the fused RMSNorm prologue (gain multiply, sum of
-//    squares for the row scale). The accumulator lane (j, g) holds
-//    y[m = j][n0 + 4g + r], so the epilogue stores four consecutive outputs
-//    per lane, row-major or straight into the operand tiles of the next
-//    GEMV.
+//    contiguous 1 KB again) or from a plain row-major one. The accumulator
+//    lane (j, g) holds y[m = j][n0 + 4g + r], so the epilogue stores four
+//    consecutive outputs per lane, row-major or straight into the operand
+//    tiles of the next GEMV.
+//  * RMSNorm stays out of the weight stream: its row scale commutes with
+//    the product, W (g * x / rms(x)) = (W (g * x)) / rms(x). The residual
+//    epilogue that produces x also stores g * x as bf16 operand tiles and
+//    each tile's row sums of squares; the consuming GEMV streams g * x and
+//    multiplies its rows by 1 / rms(x), formed from those sums, at the end.
 //  * The waves of a workgroup take interleaved steps of the item's K range
 //    and keep four steps (4 KB of weights) in flight each; their sums
 //    meet in LDS and are added in wave order.
@@ -31,9 +34,10 @@
 //    loads, sums them in split order (deterministic) and runs the epilogue.
 //    One atomic per workgroup, and no L2 writeback or invalidate (an
 //    agent-scope fence would cost both on every workgroup).
-//  * Epilogues: bf16 / f32 store, scatter into the latent KV cache (row-major
-//    key cache, rank-major value cache), residual add, and SwiGLU for paired
-//    (gate, up) launches whose two halves share the output columns.
+//  * Epilogues: bf16 / f32 store, scatter into the latent KV cache (operand
+//    tiles, key cache position-major, value cache rank-major), residual
+//    add, and SwiGLU for paired (gate, up) launches whose two halves share
+//    the output columns.
 #include <stdlib.h>
 
 #include <algorithm>
@@ -73,94 +77,32 @@ __device__ __forceinline__ int xcd_item(int b, int grid) {
   return (b & 7) * per + (b >> 3);
 }
 
-// Activation modes: row-major bf16, row-major f32, operand-tiled bf16,
-// operand-tiled f32.
-enum XMode : int { XM_BF16 = 0, XM_F32 = 1, XM_TILED = 2, XM_F32_TILED = 3 };
+// Activation modes: row-major bf16, operand-tiled bf16.
+enum XMode : int { XM_BF16 = 0, XM_TILED = 1 };
 
-// Activation rows are loaded raw into the prefetch ring with the weights
-// (so waiting for a step never waits for later prefetches) and converted to
-// the bf16 operand when the step is computed. Row-major modes read row
-// `row` at column k; the tiled mode reads fragment (row block mb, column
-// step k / 32) of an [Mpad, cols] operand-tiled matrix.
+// Activation operands are loaded into the prefetch ring with the weights
+// (so waiting for a step never waits for later prefetches). Row-major mode
+// reads row `row` at column k; tiled mode reads fragment (row block mb,
+// column step k / 32) of an [Mpad, cols] operand-tiled matrix.
 template <int XM>
-__device__ __forceinline__ void load_x_raw(const void *X, int ldx, int row, int mb, int k, int lane,
-                                           u32x4 (&r)[(XM == XM_F32 || XM == XM_F32_TILED) ? 2 : 1]) {
-  if constexpr (XM == XM_F32_TILED) {
-    const float *p = static_cast<const float *>(X) +
-                     (static_cast<size_t>(mb) * (ldx >> 5) + (k >> 5)) * 512 + lane * 4;
-    r[0] = *reinterpret_cast<const u32x4 *>(p);
-    r[1] = *reinterpret_cast<const u32x4 *>(p + 256);
-  } else if constexpr (XM == XM_F32) {
-    const float *p = static_cast<const float *>(X) + static_cast<size_t>(row) * ldx + k;
-    r[0] = *reinterpret_cast<const u32x4 *>(p);
-    r[1] = *reinterpret_cast<const u32x4 *>(p + 4);
-  } else if constexpr (XM == XM_TILED) {
-    r[0] = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(X) +
-                                            frag_off(mb, k >> 5, ldx, lane));
-  } else {
-    r[0] = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(X) +
-                                            static_cast<size_t>(row) * ldx + k);
-  }
+__device__ __forceinline__ u32x4 load_x(const uint16_t *X, int ldx, int row, int mb, int k, int lane) {
+  if constexpr (XM == XM_TILED)
+    return *reinterpret_cast<const u32x4 *>(X + frag_off(mb, k >> 5, ldx, lane));
+  else
+    return *reinterpret_cast<const u32x4 *>(X + static_cast<size_t>(row) * ldx + k);
 }
 
-// Raw row values -> bf16 operand; with NORM, accumulate the sum of squares
-// of the raw values and multiply by the gains (raw gain words in g).
-template <int XF32, int NORM, int GF32>
-__device__ __forceinline__ u32x4 make_x(const u32x4 (&r)[XF32 ? 2 : 1],
-                                        const u32x4 (&g)[GF32 ? 2 : 1], bool has_gamma,
-                                        float &ssq) {
-  if constexpr (!XF32 && !NORM) {
-    return r[0];
-  } else {
-    float v[8];
-    if constexpr (XF32) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[i] = __uint_as_float(r[0][i]);
-        v[4 + i] = __uint_as_float(r[1][i]);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[2 * i] = bflo(r[0][i]);
-        v[2 * i + 1] = bfhi(r[0][i]);
-      }
-    }
-    if constexpr (NORM) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) ssq = fmaf(v[i], v[i], ssq);
-      if (has_gamma) {
-        if constexpr (GF32) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            v[i] *= __uint_as_float(g[0][i]);
-            v[4 + i] *= __uint_as_float(g[1][i]);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            v[2 * i] *= bflo(g[0][i]);
-            v[2 * i + 1] *= bfhi(g[0][i]);
-          }
-        }
-      }
-    }
-    return u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
-  }
-}
-
-template <int MB, int XM, int PAIRED, int NORM, int GF32, int kWaves>
+template <int MB, int XM, int PAIRED, int RS, int kWaves>
 __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
-  constexpr int XF32 = XM == XM_F32 || XM == XM_F32_TILED;
-  constexpr bool XT = XM == XM_TILED || XM == XM_F32_TILED;
+  constexpr bool XT = XM == XM_TILED;
   constexpr int kThreads = kWaves * 64;
   constexpr int HALVES = PAIRED ? 2 : 1;
   constexpr int NACC = HALVES * MB;          // f32x4 accumulators per lane
   constexpr int RED = NACC * 4 * 64;         // floats of one wave's sums
-  constexpr int PART = RED + MB * 16;        // floats of one partial (sums + row ssq)
+  constexpr int PART = RED;                  // floats of one split's partial sums
   __shared__ __attribute__((aligned(16))) float wsum[kWaves][RED];
   __shared__ __attribute__((aligned(16))) float red[PART];
-  __shared__ float ssq_w[kWaves][MB * 16];
+  __shared__ float rscale[MB * 16];
   __shared__ int last_flag;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -185,73 +127,43 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
   for (int h = 0; h < HALVES; ++h)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[h][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float ssq[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) ssq[mb] = 0.f;
-
   // 32-wide steps (weights + activations) in flight per wave
   constexpr int kDepth = MB <= 2 ? 4 : 2;
-  constexpr int XW = XF32 ? 2 : 1;   // raw 16-byte words per activation row chunk
-  constexpr int GW = NORM ? (GF32 ? 2 : 1) : 1;
   struct Stage {
     u32x4 w;
-    u32x4 x[MB][XW];
-    u32x4 g[GW];
+    u32x4 x[MB];
   };
-  const bool has_gamma = NORM && a.gamma != nullptr;
   // every load below is unconditional (rows clamped, pointers selected), so
   // the compiler's wait counts stay exact across the prefetch ring
-  const void *gsrc = has_gamma ? a.gamma : sg.X;
   // this item's row of weight tiles (16 rows x K), lane offset included
   const uint16_t *w1 = sg.W + frag_off(n0 >> 4, 0, a.K, lane);
   const uint16_t *w2 = PAIRED ? sg.W2 + frag_off(n0 >> 4, 0, a.K2, lane) : w1;
   auto load_stage = [&](Stage &sb, int st) {
     int k = st * 32;
     const bool second = PAIRED && k >= a.K;
-    const void *X = second ? sg.X2 : sg.X;
+    const uint16_t *X = static_cast<const uint16_t *>(second ? sg.X2 : sg.X);
     const int ldx = second ? sg.ldx2 : sg.ldx;
     k -= second ? a.K : 0;
     const uint16_t *wp = (second ? w2 : w1) + static_cast<size_t>(k >> 5) * 512;
     sb.w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wp));
-    if constexpr (XT) {
+    if (!XT) k += 8 * grp;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) load_x_raw<XM>(X, ldx, 0, mb, k, lane, sb.x[mb]);
-    }
-    k += 8 * grp;
-    if constexpr (!XT) {
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) load_x_raw<XM>(X, ldx, min(mb * 16 + j, a.M - 1), mb, k, lane, sb.x[mb]);
-    }
-    if constexpr (NORM) {
-      if constexpr (GF32) {
-        const float *gp = static_cast<const float *>(gsrc) + k;
-        sb.g[0] = *reinterpret_cast<const u32x4 *>(gp);
-        sb.g[GW - 1] = *reinterpret_cast<const u32x4 *>(gp + 4);
-      } else {
-        sb.g[0] = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(gsrc) + k);
-      }
-    }
+    for (int mb = 0; mb < MB; ++mb) sb.x[mb] = load_x<XM>(X, ldx, min(mb * 16 + j, a.M - 1), mb, k, lane);
   };
   // `valid` is false for the padding steps at the end of the ring: their
   // activation operand is zeroed (a select, not a branch), so the loop body
-  // stays branch-free and the compiler's wait counts stay exact.
+  // stays branch-free and the compiler's wait counts stay exact. Padding
+  // rows (>= M) of the activation are zeroed the same way.
   auto compute = [&](const Stage &sb, int st, bool valid) {
-    if (PAIRED && st * 32 >= a.K) {
+    const int h = PAIRED && st * 32 >= a.K ? HALVES - 1 : 0;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        u32x4 x = sb.x[mb][0];
-        if (!valid || mb * 16 + j >= a.M) x = u32x4{0u, 0u, 0u, 0u};
-        acc[HALVES - 1][mb] = mfma_bf16(sb.w, x, acc[HALVES - 1][mb]);
-      }
-    } else {
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        float sq = 0.f;
-        u32x4 x = make_x<XF32, NORM, GF32>(sb.x[mb], sb.g, has_gamma, sq);
-        ssq[mb] += valid ? sq : 0.f;
-        if (!valid || mb * 16 + j >= a.M) x = u32x4{0u, 0u, 0u, 0u};
+    for (int mb = 0; mb < MB; ++mb) {
+      u32x4 x = sb.x[mb];
+      if (!valid || mb * 16 + j >= a.M) x = u32x4{0u, 0u, 0u, 0u};
+      if (h == 0)
         acc[0][mb] = mfma_bf16(sb.w, x, acc[0][mb]);
-      }
+      else
+        acc[HALVES - 1][mb] = mfma_bf16(sb.w, x, acc[HALVES - 1][mb]);
     }
   };
 
@@ -261,6 +173,22 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
   const int st0 = s_begin + wave;
   const int nst = st0 < s_end ? (s_end - st0 + kWaves - 1) / kWaves : 0;
   const int st_last = st0 + kWaves * (nst - 1);
+  // RMSNorm row scale (RS): this wave's rows (wave, wave + kWaves, ...) of
+  // the producer's per-tile sums of squares, columns lane + 64 c, requested
+  // before the weight stream with a fixed count (rows and columns clamped,
+  // out-of-range terms dropped by a select), so they arrive while the first
+  // weights do; summed in a fixed order after the main loop.
+  constexpr int RSR = RS ? (MB * 16 + kWaves - 1) / kWaves : 1;
+  constexpr int RSC = MB <= 2 ? 8 : 4;   // columns per lane read up front
+  float rs_acc[RSR][RSC];
+  if constexpr (RS) {
+#pragma unroll
+    for (int i = 0; i < RSR; ++i)
+#pragma unroll
+      for (int c = 0; c < RSC; ++c)
+        rs_acc[i][c] = a.rs_part[static_cast<size_t>(min(wave + kWaves * i, a.M - 1)) * a.rs_cols +
+                                 min(lane + 64 * c, a.rs_cols - 1)];
+  }
   if (nst > 0) {
     Stage ring[kDepth];
 #pragma unroll
@@ -280,18 +208,17 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
       }
     }
   }
-  // ssq of padded rows stays zero: make_x saw clamped copies of row M-1
+  if constexpr (RS) {
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-    if (mb * 16 + j >= a.M) ssq[mb] = 0.f;
-
-  // row sums of squares of this wave: lanes j, j+16, j+32, j+48 hold row j
-  if constexpr (NORM) {
+    for (int i = 0; i < RSR; ++i) {
+      const int m = wave + kWaves * i;
+      float sq = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      float v = wave_sum_xor(ssq[mb], 16);
-      v = wave_sum_xor(v, 32);
-      if (grp == 0) ssq_w[wave][mb * 16 + j] = v;
+      for (int c = 0; c < RSC; ++c) sq += lane + 64 * c < a.rs_cols ? rs_acc[i][c] : 0.f;
+      for (int c = lane + 64 * RSC; c < a.rs_cols; c += 64)   // wider rows
+        sq += a.rs_part[static_cast<size_t>(min(m, a.M - 1)) * a.rs_cols + c];
+      sq = wave_sum(sq);
+      if (lane == 0 && m < a.M) rscale[m] = rsqrtf(sq / static_cast<float>(a.K) + a.eps);
     }
   }
   // per-wave sums -> LDS, then a fixed-order sum over the waves:
@@ -308,14 +235,6 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) v += wsum[w][idx];
     red[idx] = v;
-  }
-  if constexpr (NORM) {
-    for (int m = tid; m < MB * 16; m += kThreads) {
-      float v = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) v += ssq_w[w][m];
-      red[RED + m] = v;
-    }
   }
   __syncthreads();
 
@@ -365,10 +284,9 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
   float v[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) v[r] = red[((0 * MB + mb) * 4 + r) * 64 + ln];
-  if constexpr (NORM) {
-    const float sc = rsqrtf(red[RED + m] / static_cast<float>(a.K) + a.eps);
+  if constexpr (RS) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] *= sc;
+    for (int r = 0; r < 4; ++r) v[r] *= rscale[m];
   }
   const size_t oi = static_cast<size_t>(m) * sg.ldo + n;
   switch (sg.omode) {
@@ -413,7 +331,23 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
       const f32x4 o = f32x4{v[0], v[1], v[2], v[3]};
       *reinterpret_cast<f32x4 *>(static_cast<float *>(sg.out) + oi) = o;
       if (sg.out2) *reinterpret_cast<f32x4 *>(sg.out2 + oi) = o;
-      if (sg.out_t) *reinterpret_cast<f32x4 *>(sg.out_t + tile_off_f32(m, n, sg.N)) = o;
+      if (sg.out_nt) {
+        // next RMSNorm's input: g * o as bf16 operand tiles, and the sum of
+        // squares of o over this tile's 16 columns of row m (the four
+        // threads of the row are lanes 4m .. 4m + 3; N % 16 == 0)
+        float gn[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          gn[r] = sg.gamma ? (sg.gamma_f32 ? static_cast<const float *>(sg.gamma)[n + r]
+                                           : bf2f(static_cast<const uint16_t *>(sg.gamma)[n + r]))
+                           : 1.f;
+        *reinterpret_cast<u32x2 *>(sg.out_nt + tile_off(m, n, sg.N)) =
+            u32x2{pack2(o[0] * gn[0], o[1] * gn[1]), pack2(o[2] * gn[2], o[3] * gn[3])};
+        float sq = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
+        sq += __shfl_xor(sq, 1, 64);
+        sq += __shfl_xor(sq, 2, 64);
+        if (q == 0) sg.ssq_out[static_cast<size_t>(m) * (sg.N >> 4) + (n0 >> 4)] = sq;
+      }
       break;
     }
     case GV_OUT_RES_BF16: {
@@ -434,31 +368,22 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
   }
 }
 
-template <int MB, int XM, int PAIRED, int NORM, int GF32>
+template <int MB, int XM, int PAIRED, int RS>
 hipError_t launch_t(const GvArgs &a, int grid, hipStream_t s) {
   if (a.waves == 4)
-    gemv_kernel<MB, XM, PAIRED, NORM, GF32, 4><<<grid, 4 * 64, 0, s>>>(a);
+    gemv_kernel<MB, XM, PAIRED, RS, 4><<<grid, 4 * 64, 0, s>>>(a);
   else
-    gemv_kernel<MB, XM, PAIRED, NORM, GF32, 8><<<grid, 8 * 64, 0, s>>>(a);
+    gemv_kernel<MB, XM, PAIRED, RS, 8><<<grid, 8 * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
 template <int MB>
 hipError_t launch_mb(const GvArgs &a, int grid, hipStream_t s) {
   if (a.K2 > 0)
-    return a.x_tiled ? launch_t<MB, XM_TILED, 1, 0, 0>(a, grid, s) : launch_t<MB, XM_BF16, 1, 0, 0>(a, grid, s);
-  if (a.norm) {
-    if (a.x_f32 && a.x_tiled)
-      return a.gamma_f32 ? launch_t<MB, XM_F32_TILED, 0, 1, 1>(a, grid, s)
-                         : launch_t<MB, XM_F32_TILED, 0, 1, 0>(a, grid, s);
-    if (a.x_f32)
-      return a.gamma_f32 ? launch_t<MB, XM_F32, 0, 1, 1>(a, grid, s) : launch_t<MB, XM_F32, 0, 1, 0>(a, grid, s);
-    if (a.x_tiled)
-      return a.gamma_f32 ? launch_t<MB, XM_TILED, 0, 1, 1>(a, grid, s) : launch_t<MB, XM_TILED, 0, 1, 0>(a, grid, s);
-    return a.gamma_f32 ? launch_t<MB, XM_BF16, 0, 1, 1>(a, grid, s) : launch_t<MB, XM_BF16, 0, 1, 0>(a, grid, s);
-  }
-  if (a.x_tiled) return launch_t<MB, XM_TILED, 0, 0, 0>(a, grid, s);
-  return a.x_f32 ? launch_t<MB, XM_F32, 0, 0, 0>(a, grid, s) : launch_t<MB, XM_BF16, 0, 0, 0>(a, grid, s);
+    return a.x_tiled ? launch_t<MB, XM_TILED, 1, 0>(a, grid, s) : launch_t<MB, XM_BF16, 1, 0>(a, grid, s);
+  if (a.rs_part)
+    return a.x_tiled ? launch_t<MB, XM_TILED, 0, 1>(a, grid, s) : launch_t<MB, XM_BF16, 0, 1>(a, grid, s);
+  return a.x_tiled ? launch_t<MB, XM_TILED, 0, 0>(a, grid, s) : launch_t<MB, XM_BF16, 0, 0>(a, grid, s);
 }
 
 int env_int(const char *name, int dflt) {
@@ -488,7 +413,7 @@ size_t gemv_plan(GvArgs &a) {
   a.ksplit = (ksteps + sps - 1) / sps;
   const int MB = (a.M + 15) / 16;
   const int halves = a.K2 > 0 ? 2 : 1;
-  const size_t part = static_cast<size_t>(halves) * MB * 4 * 64 + MB * 16;
+  const size_t part = static_cast<size_t>(halves) * MB * 4 * 64;
   return a.ksplit > 1 ? part * a.ntiles * a.ksplit : 0;
 }
 

@@ -32,11 +32,17 @@ enum GvOut : int {
 struct GvSeg {
   const uint16_t *W;   // Wt [N, K] bf16, operand tiles
   const uint16_t *W2;  // paired: second half Wt2 [N, K2]
-  const void *X;       // [M, ldx] bf16 (or f32 with x_f32); tiled: [Mpad, K], ldx = K
+  const void *X;       // bf16 [M, ldx]; tiled: [Mpad, K] operand tiles, ldx = K
   const void *X2;      // paired: second-half activations, like X with K2
   void *out;
   float *out2;         // optional copy (GV_OUT_RES_F32)
-  float *out_t;        // optional f32 operand-tile copy [Mpad, N] (GV_OUT_RES_F32)
+  // GV_OUT_RES_F32, optional: the next RMSNorm's input, gamma * out as bf16
+  // operand tiles [Mpad, N] (gamma [N] or NULL = 1), and the sum of squares
+  // of out over each 16-column tile, ssq_out[m * (N / 16) + n / 16]
+  uint16_t *out_nt;
+  const void *gamma;
+  int gamma_f32;
+  float *ssq_out;
   const void *R;       // residual [M, ldr]
   int N, ldx, ldx2, ldo, ldr;
   int omode, res_f32;
@@ -47,12 +53,12 @@ struct GvArgs {
   GvSeg seg[3];
   int nseg;
   int M, K, K2;           // K2 > 0 only for paired launches (then nseg == 1)
-  int x_f32;              // X is f32 (else bf16); paired launches use bf16
-  int x_tiled;            // X (and X2) are operand-tiled (bf16, or f32 tiles with x_f32)
-  int norm;               // fused RMSNorm: X scaled by gamma, rows of the result by
-                          // 1 / sqrt(mean(X^2) + eps) (mean over the K columns)
-  const void *gamma;      // [K] gains or NULL (= 1)
-  int gamma_f32;
+  int x_tiled;            // X (and X2) are operand-tiled
+  // optional RMSNorm row scale: rows of the result are multiplied by
+  // 1 / sqrt(sum_c rs_part[m * rs_cols + c] / K + eps) (X holds gamma * x;
+  // rs_part the per-tile row sums of squares of x, from GV_OUT_RES_F32)
+  const float *rs_part;
+  int rs_cols;
   float eps;
   const int32_t *past;    // cache scatter (GV_OUT_CACHE)
   int T, L_max;
@@ -204,6 +210,12 @@ struct FillRegion {
   int tile_rows = 0, tile_cols = 0;
 };
 hipError_t launch_fill(const FillRegion *r, int nreg, hipStream_t s);
+// RMSNorm into operand tiles: xt [Mp, n] bf16 tiles, row m < M =
+// x[m] / sqrt(mean(x[m]^2) + eps) * gamma (x bf16 [M, n], gamma [n] or NULL),
+// rows M .. Mp - 1 zero; the same launch zeroes up to four fill regions.
+hipError_t launch_norm_tiles(const uint16_t *x, const void *gamma, int gamma_f32, float eps,
+                             uint16_t *xt, int M, int Mp, int n, const FillRegion *zero, int nzero,
+                             hipStream_t s);
 // dst (bf16 or f32) = src f32
 hipError_t launch_convert_f32(const float *src, void *dst, int dst_bf16, int64_t n, hipStream_t s);
 
