@@ -92,12 +92,12 @@ __device__ __forceinline__ u32x4 load_x(const uint16_t *X, int ldx, int row, int
     return *reinterpret_cast<const u32x4 *>(X + static_cast<size_t>(row) * ldx + k);
 }
 
-template <int MB, int XM, int PAIRED, int RS, int kWaves>
+template <int MB, int XM, int PAIRED, int RS, int R, int kWaves>
 __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
   constexpr bool XT = XM == XM_TILED;
   constexpr int kThreads = kWaves * 64;
   constexpr int HALVES = PAIRED ? 2 : 1;
-  constexpr int NACC = HALVES * MB;          // f32x4 accumulators per lane
+  constexpr int NACC = HALVES * R * MB;      // f32x4 accumulators per lane
   constexpr int RED = NACC * 4 * 64;         // floats of one wave's sums
   constexpr int PART = RED;                  // floats of one split's partial sums
   __shared__ __attribute__((aligned(16))) float wsum[kWaves][RED];
@@ -108,6 +108,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 15, grp = lane >> 4;
+  // work item = (K split, group of R consecutive 16-row tiles of one
+  // segment); `tile` numbers the groups
   const int item = xcd_item(blockIdx.x, gridDim.x);
   if (item >= a.ntiles * a.ksplit) return;
   const int split = item / a.ntiles;
@@ -116,36 +118,48 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
   if (a.nseg > 1 && tile >= a.seg[1].tile_begin) si = 1;
   if (a.nseg > 2 && tile >= a.seg[2].tile_begin) si = 2;
   const GvSeg sg = a.seg[si];
-  const int n0 = (tile - sg.tile_begin) * kRows;
+  const int n0 = (tile - sg.tile_begin) * R * kRows;
+  const int seg_tiles = (sg.N + kRows - 1) / kRows;
 
   const int ksteps = (a.K + a.K2) >> 5;
   const int s_begin = split * a.split_steps;
   const int s_end = min(s_begin + a.split_steps, ksteps);
 
-  f32x4 acc[HALVES][MB];
+  f32x4 acc[HALVES][R][MB];
 #pragma unroll
   for (int h = 0; h < HALVES; ++h)
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[h][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[h][r][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   // 32-wide steps (weights + activations) in flight per wave
   constexpr int kDepth = MB <= 2 ? 4 : 2;
   struct Stage {
-    u32x4 w;
-    u32x4 x[MB];
+    u32x4 w[R];    // one weight tile per row tile, sharing ...
+    u32x4 x[MB];   // ... the activation fragment
   };
   // every load below is unconditional (rows clamped, pointers selected), so
   // the compiler's wait counts stay exact across the prefetch ring
-  // this item's row of weight tiles (16 rows x K), lane offset included
-  const uint16_t *w1 = sg.W + frag_off(n0 >> 4, 0, a.K, lane);
-  const uint16_t *w2 = PAIRED ? sg.W2 + frag_off(n0 >> 4, 0, a.K2, lane) : w1;
+  // this item's rows of weight tiles (16 rows x K each), lane offset
+  // included; tiles past the segment's last repeat it and are not stored
+  const uint16_t *w1[R];
+  const uint16_t *w2[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int tr = min((n0 >> 4) + r, seg_tiles - 1);
+    w1[r] = sg.W + frag_off(tr, 0, a.K, lane);
+    w2[r] = PAIRED ? sg.W2 + frag_off(tr, 0, a.K2, lane) : w1[r];
+  }
   auto load_stage = [&](Stage &sb, int st) {
     int k = st * 32;
     const bool second = PAIRED && k >= a.K;
     const uint16_t *X = static_cast<const uint16_t *>(second ? sg.X2 : sg.X);
     const int ldx = second ? sg.ldx2 : sg.ldx;
     k -= second ? a.K : 0;
-    const uint16_t *wp = (second ? w2 : w1) + static_cast<size_t>(k >> 5) * 512;
-    sb.w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wp));
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      sb.w[r] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4 *>((second ? w2[r] : w1[r]) + static_cast<size_t>(k >> 5) * 512));
     if (!XT) k += 8 * grp;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) sb.x[mb] = load_x<XM>(X, ldx, min(mb * 16 + j, a.M - 1), mb, k, lane);
@@ -160,10 +174,13 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
     for (int mb = 0; mb < MB; ++mb) {
       u32x4 x = sb.x[mb];
       if (!valid || mb * 16 + j >= a.M) x = u32x4{0u, 0u, 0u, 0u};
-      if (h == 0)
-        acc[0][mb] = mfma_bf16(sb.w, x, acc[0][mb]);
-      else
-        acc[HALVES - 1][mb] = mfma_bf16(sb.w, x, acc[HALVES - 1][mb]);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (h == 0)
+          acc[0][r][mb] = mfma_bf16(sb.w[r], x, acc[0][r][mb]);
+        else
+          acc[HALVES - 1][r][mb] = mfma_bf16(sb.w[r], x, acc[HALVES - 1][r][mb]);
+      }
     }
   };
 
@@ -222,13 +239,16 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
     }
   }
   // per-wave sums -> LDS, then a fixed-order sum over the waves:
-  // red[(acc * 4 + r) * 64 + lane]
+  // red[((((h * R + r) * MB + mb) * 4 + e) * 64 + lane]
 #pragma unroll
   for (int h = 0; h < HALVES; ++h)
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) wsum[wave][((h * MB + mb) * 4 + r) * 64 + lane] = acc[h][mb][r];
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          wsum[wave][(((h * R + r) * MB + mb) * 4 + e) * 64 + lane] = acc[h][r][mb][e];
   __syncthreads();
   for (int idx = tid; idx < RED; idx += kThreads) {
     float v = wsum[0][idx];
@@ -274,16 +294,18 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
     __syncthreads();
   }
 
-  // epilogue: thread t writes y[m = t / 4][n0 + 4q .. 4q+3], q = t % 4; the
-  // accumulator lane of (n0 + 4q + r, m) is 16q + m % 16, register r
-  const int m = tid >> 2, q = tid & 3;
-  if (m >= a.M) return;
-  const int n = n0 + 4 * q;
-  if (n >= sg.N) return;
+  // epilogue: unit u = (m * R + rt) * 4 + q writes y[m][n0 + 16 rt + 4q ..
+  // + 3] (four consecutive units share a row and a tile: lanes 4k .. 4k + 3);
+  // the accumulator lane of (column 16 rt + 4q + e, row m) is 16q + m % 16,
+  // register e
+  for (int u = tid; u < a.M * R * 4; u += kThreads) {
+  const int m = u / (R * 4), rt = (u >> 2) % R, q = u & 3;
+  const int n = n0 + 16 * rt + 4 * q;
+  if (n >= sg.N) continue;
   const int mb = m >> 4, ln = 16 * q + (m & 15);
   float v[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) v[r] = red[((0 * MB + mb) * 4 + r) * 64 + ln];
+  for (int r = 0; r < 4; ++r) v[r] = red[(((0 * R + rt) * MB + mb) * 4 + r) * 64 + ln];
   if constexpr (RS) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) v[r] *= rscale[m];
@@ -346,7 +368,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
         float sq = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
         sq += __shfl_xor(sq, 1, 64);
         sq += __shfl_xor(sq, 2, 64);
-        if (q == 0) sg.ssq_out[static_cast<size_t>(m) * (sg.N >> 4) + (n0 >> 4)] = sq;
+        if (q == 0) sg.ssq_out[static_cast<size_t>(m) * (sg.N >> 4) + (n >> 4)] = sq;
       }
       break;
     }
@@ -358,22 +380,25 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
       break;
     }
     default: {  // GV_OUT_SWIGLU, GV_OUT_SWIGLU_TILED
-      float u[4];
+      float g2[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) u[r] = silu(v[r]) * red[((1 * MB + mb) * 4 + r) * 64 + ln];
+      for (int r = 0; r < 4; ++r) g2[r] = silu(v[r]) * red[(((1 * R + rt) * MB + mb) * 4 + r) * 64 + ln];
       const size_t o = sg.omode == GV_OUT_SWIGLU_TILED ? tile_off(m, n, sg.N) : oi;
-      *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(sg.out) + o) = u32x2{pack2(u[0], u[1]), pack2(u[2], u[3])};
+      *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(sg.out) + o) = u32x2{pack2(g2[0], g2[1]), pack2(g2[2], g2[3])};
       break;
     }
+  }
   }
 }
 
 template <int MB, int XM, int PAIRED, int RS>
 hipError_t launch_t(const GvArgs &a, int grid, hipStream_t s) {
-  if (a.waves == 4)
-    gemv_kernel<MB, XM, PAIRED, RS, 4><<<grid, 4 * 64, 0, s>>>(a);
+  if (a.rtiles == 2)
+    gemv_kernel<MB, XM, PAIRED, RS, 2, 4><<<grid, 4 * 64, 0, s>>>(a);
+  else if (a.waves == 4)
+    gemv_kernel<MB, XM, PAIRED, RS, 1, 4><<<grid, 4 * 64, 0, s>>>(a);
   else
-    gemv_kernel<MB, XM, PAIRED, RS, 8><<<grid, 8 * 64, 0, s>>>(a);
+    gemv_kernel<MB, XM, PAIRED, RS, 1, 8><<<grid, 8 * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -394,26 +419,41 @@ int env_int(const char *name, int dflt) {
 
 size_t gemv_plan(GvArgs &a) {
   int tiles = 0;
-  for (int i = 0; i < a.nseg; ++i) {
-    a.seg[i].tile_begin = tiles;
-    tiles += (a.seg[i].N + kRows - 1) / kRows;
-  }
-  a.ntiles = tiles;
+  for (int i = 0; i < a.nseg; ++i) tiles += (a.seg[i].N + kRows - 1) / kRows;
   a.waves = env_int("DL_GEMV_WAVES", 4) == 8 ? 8 : 4;
   const int ksteps = (a.K + a.K2) / 32;
   // K splits: enough work items for about `target` workgroups, but at least
   // `min_steps` steps per wave
   const int target = env_int("DL_GEMV_WGS", 256);
   const int min_steps = std::max(1, env_int("DL_GEMV_MIN_STEPS", 4));
-  int ks = (target + tiles - 1) / tiles;
-  ks = std::min(ks, std::max(1, ksteps / (min_steps * a.waves)));
-  ks = std::max(1, std::min(ks, 64));
-  const int sps = (ksteps + ks - 1) / ks;
+  auto splits = [&](int items) {
+    int ks = (target + items - 1) / items;
+    ks = std::min(ks, std::max(1, ksteps / (min_steps * a.waves)));
+    return std::max(1, std::min(ks, 64));
+  };
+  // Two row tiles per item halve the activation reads (each activation
+  // fragment feeds two weight tiles) where the halved item count still
+  // fills the target without a K split. (Doubling the split of an already
+  // split launch instead measured slower: shorter streams per wave and
+  // larger merges.)
+  int R = 1;
+  if (a.waves == 4) {
+    const int forced = env_int("DL_GEMV_R", 0);
+    R = forced == 1 || forced == 2 ? forced : (tiles >= 2 * target && splits(tiles / 2) == 1 ? 2 : 1);
+  }
+  a.rtiles = R;
+  int items = 0;
+  for (int i = 0; i < a.nseg; ++i) {
+    a.seg[i].tile_begin = items;
+    items += ((a.seg[i].N + kRows - 1) / kRows + R - 1) / R;
+  }
+  a.ntiles = items;
+  const int sps = (ksteps + splits(items) - 1) / splits(items);
   a.split_steps = sps;
   a.ksplit = (ksteps + sps - 1) / sps;
   const int MB = (a.M + 15) / 16;
   const int halves = a.K2 > 0 ? 2 : 1;
-  const size_t part = static_cast<size_t>(halves) * MB * 4 * 64;
+  const size_t part = static_cast<size_t>(halves) * R * MB * 4 * 64;
   return a.ksplit > 1 ? part * a.ntiles * a.ksplit : 0;
 }
 

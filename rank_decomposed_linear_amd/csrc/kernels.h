@@ -46,7 +46,7 @@ struct GvSeg {
   const void *R;       // residual [M, ldr]
   int N, ldx, ldx2, ldo, ldr;
   int omode, res_f32;
-  int tile_begin;      // set by gemv_plan
+  int tile_begin;      // first work item of the segment, set by gemv_plan
 };
 
 struct GvArgs {
@@ -63,7 +63,8 @@ struct GvArgs {
   const int32_t *past;    // cache scatter (GV_OUT_CACHE)
   int T, L_max;
   // set by gemv_plan / the caller
-  int ntiles, ksplit, split_steps;
+  int ntiles, ksplit, split_steps;   // ntiles: work items (groups of rtiles tiles) per split
+  int rtiles;             // 16-row tiles per work item (1 or 2)
   int waves;              // waves per workgroup (4 or 8)
   float *part;            // gemv_plan's return value in floats
   int *counters;          // ntiles ints, zero before the launch (left zero after it)

@@ -132,6 +132,15 @@ def test_small_layer(B, case):
     check_step(dt, x, y, x2, ck, cv, want, past, T)
 
 
+@pytest.mark.parametrize("case", SMALL[:2], ids=[c[0] for c in SMALL[:2]])
+def test_small_layer_row_tiles(B, monkeypatch, case):
+    """The small-M layer with every GEMV on two-tile work items (DL_GEMV_R=2):
+    cache scatter, SwiGLU pairs, residual epilogue with the MLP norm's tiles
+    and row sums, split merges."""
+    monkeypatch.setenv("DL_GEMV_R", "2")
+    test_small_layer(B, case)
+
+
 # ----------------------------------------------------------------------------
 # the five workload configurations
 # ----------------------------------------------------------------------------

@@ -64,6 +64,22 @@ def test_lowrank_linear(B, M, m, k, n, dt):
     assert relerr(to_host(y), want) <= TOL[dt]
 
 
+@pytest.mark.parametrize("R", ["1", "2"])
+@pytest.mark.parametrize("M,m,k,n", [(16, 4096, 1216, 4096), (37, 512, 448, 192), (5, 2048, 128, 1024)])
+def test_lowrank_linear_row_tiles(B, monkeypatch, R, M, m, k, n):
+    """Both GEMV work-item widths (one or two 16-row tiles sharing each
+    activation fragment), forced through DL_GEMV_R, with K splits (the first
+    factor) and without, and multi-block M (bf16 factor pairs have m, k, n
+    multiples of 64, so every item holds two real tiles)."""
+    monkeypatch.setenv("DL_GEMV_R", R)
+    print(f"lowrank_linear R={R} M={M} m={m} k={k} n={n}", flush=True)
+    r = rng(M * 11 + n)
+    x, A, Bf = rand(r, (M, m), 1.0, "bf16"), rand(r, (m, k), 0.02, "bf16"), rand(r, (k, n), 0.02, "bf16")
+    y = B.lowrank_linear(to_dev(x), to_dev(lib_f(A)), to_dev(lib_f(Bf)))
+    want = ref.lowrank_linear(f64(x), f64(A), f64(Bf))
+    assert relerr(to_host(y), want) <= TOL["bf16"]
+
+
 # ----------------------------------------------------------------------------
 # cache append
 # ----------------------------------------------------------------------------
