@@ -13,9 +13,10 @@ A "step" is one dl_decomposed_layer_fwd call over the whole batch. Inputs
 are seeded synthetic data resident in HBM before timing starts; two
 independent device copies of weights and cache are used in turn so the
 256 MB Infinity Cache cannot serve one step from the previous one. Steps are
-replayed from one HIP graph that holds one step per copy, as a multi-layer
-model would capture its layers, unless --no-graph; a step count that is not
-a multiple of the copies ends with single-step graphs, so exactly K steps run.
+replayed from one HIP graph that holds --graph-steps steps (the copies in
+turn), as a multi-layer model captures its layers, unless --no-graph; a step
+count that is not a multiple of that ends with single-step graphs, so exactly
+K steps run.
 
 Per-kernel durations come from hipEvents that the library records around
 each of its launches on the launch stream. A traced step is queued behind a
@@ -63,6 +64,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-graph", action="store_true")
+    p.add_argument("--graph-steps", type=int, default=8,
+                   help="decode steps per graph replay (copies in turn)")
     p.add_argument("--sets", type=int, default=2)
     p.add_argument("--calibrate-copy", action="store_true")
     return p.parse_args()
@@ -148,8 +151,9 @@ def run_step(st):
     st["layer"].forward(st["x"], st["ck"], st["cv"], st["past"], y=st["y"], ws=st["ws"])
 
 
-def capture_graphs(torch, sets):
-    """One graph per copy, plus one graph that runs the copies in turn."""
+def capture_graphs(torch, sets, chain_steps):
+    """One graph per copy, plus one graph of chain_steps steps that runs the
+    copies in turn."""
     graphs = []
     side = torch.cuda.Stream()
     for st in sets:
@@ -163,18 +167,19 @@ def capture_graphs(torch, sets):
         graphs.append(g)
     chain = torch.cuda.CUDAGraph()
     with torch.cuda.graph(chain):
-        for st in sets:
-            run_step(st)
+        for i in range(chain_steps):
+            run_step(sets[i % len(sets)])
     torch.cuda.synchronize()
     return graphs, chain
 
 
-def step_fn(graphs, chain, steps):
-    """fn(i) for i < calls runs the steps: chained replays, then singles."""
-    n = len(graphs)
-    full = steps // n
-    calls = full + steps % n
-    return (lambda i: chain.replay() if i < full else graphs[(i - full) % n].replay()), calls
+def step_fn(graphs, chain, chain_steps, steps):
+    """fn(i) for i < calls runs the steps: chained replays, then singles (the
+    copies continue in turn)."""
+    full = steps // chain_steps
+    calls = full + steps % chain_steps
+    return (lambda i: chain.replay() if i < full else
+            graphs[(full * chain_steps + i - full) % len(graphs)].replay()), calls
 
 
 def timed(torch, fn, steps, warmup):
@@ -241,9 +246,10 @@ def decode_bench(args, torch, binding, W):
     y_eager = sets[0]["y"].float().clone()
     use_graph = not args.no_graph
     graphs = None
+    chain_steps = max(1, args.graph_steps)
     if use_graph:
         try:
-            graphs, chain = capture_graphs(torch, sets)
+            graphs, chain = capture_graphs(torch, sets, chain_steps)
             for g in (graphs[0], chain, graphs[0]):
                 sets[0]["y"].zero_()
                 g.replay()
@@ -256,8 +262,8 @@ def decode_bench(args, torch, binding, W):
             use_graph, graphs = False, None
     log(f"timing {args.steps} steps after {args.warmup} warmup (graph={use_graph})")
     if graphs:
-        fn, calls = step_fn(graphs, chain, args.steps)
-        wfn, wcalls = step_fn(graphs, chain, args.warmup)
+        fn, calls = step_fn(graphs, chain, chain_steps, args.steps)
+        wfn, wcalls = step_fn(graphs, chain, chain_steps, args.warmup)
         for i in range(wcalls):
             wfn(i)
         ms, wall = timed(torch, fn, calls, 0)
@@ -323,6 +329,7 @@ def decode_bench(args, torch, binding, W):
     step_bytes = W.algorithmic_decode_bytes(w.shape, Bsz, ctx_total // Bsz)["total"]
     result = {
         "value": Bsz / (ms * 1e-3), "ms_per_step": ms, "wall_s": wall, "graph": use_graph,
+        "steps_per_graph": chain_steps if use_graph else None,
         "roofline": roof, "roofline_attention": roof_attn, "kernels": breakdown,
         "roles_us_per_step": roles,
         "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -429,7 +436,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(dec["ms_per_step"], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded; random-init factors, pre-filled low-rank cache)",
-        "config": dec["config"], "graph": dec["graph"],
+        "config": dec["config"], "graph": dec["graph"], "steps_per_graph": dec["steps_per_graph"],
         "roofline": dec["roofline"], "roofline_attention": dec["roofline_attention"],
         "step_hbm_frac": dec["step_hbm_frac"], "kernel_source_hash": kernel_source_hash(),
         "cpu_baseline": cpu, "prefill": pre, "kernels": dec["kernels"],

@@ -155,6 +155,47 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
       *reinterpret_cast<u32x4 *>(bs + static_cast<size_t>(u) * 8) = ld16(factor_src(rs0, u));
   };
 
+  // Prologue, ordered so the latencies overlap: this thread's query values
+  // are requested first, then the first batch of the resident factor; the
+  // float64 rotary tables and the query operands are computed while those
+  // loads are in flight; the factor goes to LDS last.
+  //
+  // Score B operands (rotated, scaled queries of this kv head's G heads,
+  // rows >= G zero): entry (t, lane (head j, grp)) holds slots 0..3 =
+  // q[j][dim(2t, 4grp+r)], slots 4..7 = q[j][dim(2t+1, 4grp+r)]; entry tid.
+  constexpr int kQE = (NB / 2) * 64;
+  static_assert(kQE <= kThreads, "one query operand entry per thread");
+  const int qt = tid >> 6, qj = lane & 15, qg = lane >> 4;
+  const bool q_mine = tid < kQE && qj < G;
+  float qlo[8], qhi[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int i = T::dim(2 * qt + (e >> 2), 4 * qg + (e & 3)) % HALF;
+    const size_t off = (static_cast<size_t>(b) * a.n_q + g * G + min(qj, G - 1)) * D + i;
+    if (a.q_f32) {
+      qlo[e] = static_cast<const float *>(a.q)[off];
+      qhi[e] = static_cast<const float *>(a.q)[off + HALF];
+    } else {
+      qlo[e] = bf2f(static_cast<const uint16_t *>(a.q)[off]);
+      qhi[e] = bf2f(static_cast<const uint16_t *>(a.q)[off + HALF]);
+    }
+  }
+  // resident factor: batches of kPer loads per thread in flight before their
+  // LDS stores; the first batch is issued here
+  constexpr int kPer = 32;
+  const int funits = n_rchunks == 1 ? nrs * NB * 64 : 0;
+  u32x4 fv[kPer];
+  auto factor_batch_load = [&](int u0) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) fv[k] = ld16(factor_src(0, min(u0 + tid + kThreads * k, funits - 1)));
+  };
+  auto factor_batch_store = [&](int u0) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+      if (u0 + tid + kThreads * k < funits)
+        *reinterpret_cast<u32x4 *>(bs + static_cast<size_t>(u0 + tid + kThreads * k) * 8) = fv[k];
+  };
+  if (funits > 0) factor_batch_load(0);
   for (int i = tid; i < HALF; i += kThreads) {
     rev64[i] = rope_on ? rope_rev(i, D, a.theta) : 0.0;
     rev32[i] = static_cast<float>(rev64[i]);
@@ -162,54 +203,32 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
     rope_cs(16, rev64[i], c16, s16);
     step16[i] = float2{c16, s16};
   }
-  if (n_rchunks == 1) {
-    // resident factor: batches of 32 loads in flight before their LDS stores
-    constexpr int kPer = 32;
-    const int units = nrs * NB * 64;
-    for (int u0 = 0; u0 < units; u0 += kPer * kThreads) {
-      u32x4 v[kPer];
-#pragma unroll
-      for (int k = 0; k < kPer; ++k) v[k] = ld16(factor_src(0, min(u0 + tid + kThreads * k, units - 1)));
-#pragma unroll
-      for (int k = 0; k < kPer; ++k)
-        if (u0 + tid + kThreads * k < units)
-          *reinterpret_cast<u32x4 *>(bs + static_cast<size_t>(u0 + tid + kThreads * k) * 8) = v[k];
-    }
-  }
   __syncthreads();
-  // rotated, scaled queries of this kv head's G heads (rows >= G are zero),
-  // packed as score B operands: lane (head j, grp) slots 0..3 =
-  // q[j][dim(2t, 4grp+r)], slots 4..7 = q[j][dim(2t+1, 4grp+r)]; one
-  // (t, lane) entry per thread
-  for (int idx = tid; idx < (NB / 2) * 64; idx += kThreads) {
-    const int t = idx >> 6, ln = idx & 63, hj = ln & 15, gq = ln >> 4;
+  if (tid < kQE) {
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int dm = T::dim(2 * t + (e >> 2), 4 * gq + (e & 3));
+      const int dm = T::dim(2 * qt + (e >> 2), 4 * qg + (e & 3));
       float x = 0.f;
-      if (hj < G) {
-        const size_t off = (static_cast<size_t>(b) * a.n_q + g * G + hj) * D;
-        const int i = dm % HALF;
-        float lo, hi;
-        if (a.q_f32) {
-          lo = static_cast<const float *>(a.q)[off + i];
-          hi = static_cast<const float *>(a.q)[off + i + HALF];
-        } else {
-          lo = bf2f(static_cast<const uint16_t *>(a.q)[off + i]);
-          hi = bf2f(static_cast<const uint16_t *>(a.q)[off + i + HALF]);
-        }
+      if (q_mine) {
         if (rope_on) {
-          float c, s;
-          rope_cs(qpos, rev64[i], c, s);
-          x = dm < HALF ? lo * c - hi * s : lo * s + hi * c;
+          float c, sn;
+          rope_cs(qpos, rev64[dm % HALF], c, sn);
+          x = dm < HALF ? qlo[e] * c - qhi[e] * sn : qlo[e] * sn + qhi[e] * c;
         } else {
-          x = dm < HALF ? lo : hi;
+          x = dm < HALF ? qlo[e] : qhi[e];
         }
       }
       v[e] = x * a.scale_log2;
     }
-    qfs[t][ln] = u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
+    qfs[qt][lane] = u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
+  }
+  if (funits > 0) {
+    factor_batch_store(0);
+    for (int u0 = kPer * kThreads; u0 < funits; u0 += kPer * kThreads) {
+      factor_batch_load(u0);
+      factor_batch_store(u0);
+    }
   }
   __syncthreads();
 
