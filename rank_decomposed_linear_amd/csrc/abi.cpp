@@ -1091,15 +1091,17 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
     a.seg[0] = mseg(L->up.B, w.tu16, w.U16, D.f, D.ru, D.f);
     DL_HIP(gemm(a, s));
   }
+  // H = silu(G) * U, in place over G (one streaming pass; recomputing it in
+  // the down GEMM's operand staging would repeat it for every column tile)
+  DL_HIP(launch_swiglu_bf16(w.G16, w.U16, static_cast<int64_t>(M) * D.f, s));
   {
     GemmArgs a{};
     a.nseg = 1;
     a.M = M;
     a.K = D.f;
-    a.xmode = GEMM_X_SWIGLU;
+    a.xmode = GEMM_X_BF16;
     a.omode = GEMM_OUT_BF16;
     a.seg[0] = mseg(L->down.A, w.G16, w.td16, D.rd, D.f, D.rd);
-    a.seg[0].X2 = w.U16;
     set_role(R_DOWN_DOWN);
     DL_HIP(gemm(a, s));
     GemmArgs b{};

@@ -26,18 +26,7 @@ struct Stage {
   u32x4 a[4], b[4];
 };
 
-__device__ __forceinline__ u32x4 swiglu8(u32x4 g, u32x4 u) {
-  u32x4 r;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float a0 = silu(bflo(g[q])) * bflo(u[q]);
-    const float a1 = silu(bfhi(g[q])) * bfhi(u[q]);
-    r[q] = pack2(a0, a1);
-  }
-  return r;
-}
-
-template <int XM, int OM>
+template <int OM>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][kAElems + kBElems];
   const int tid = threadIdx.x;
@@ -67,8 +56,6 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
       if (row < a.M) {
         const size_t off = static_cast<size_t>(row) * sg.ldx + k0 + 8 * kc;
         v = *reinterpret_cast<const u32x4 *>(sg.X + off);
-        if constexpr (XM == GEMM_X_SWIGLU)
-          v = swiglu8(v, *reinterpret_cast<const u32x4 *>(sg.X2 + off));
       }
       st.a[it] = v;
       const int u = tid + 256 * it, tt = u >> 6, nb = tt >> 1, ks = tt & 1;
@@ -165,18 +152,13 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   }
 }
 
-template <int XM>
-hipError_t launch_x(const GemmArgs &a, dim3 grid, hipStream_t s) {
+hipError_t launch_o(const GemmArgs &a, dim3 grid, hipStream_t s) {
   switch (a.omode) {
-    case GEMM_OUT_BF16: gemm_bf16_kernel<XM, GEMM_OUT_BF16><<<grid, kThreads, 0, s>>>(a); break;
-    case GEMM_OUT_BF16_RES_F32:
-      gemm_bf16_kernel<XM, GEMM_OUT_BF16_RES_F32><<<grid, kThreads, 0, s>>>(a);
-      break;
-    case GEMM_OUT_F32_RES_BF16:
-      gemm_bf16_kernel<XM, GEMM_OUT_F32_RES_BF16><<<grid, kThreads, 0, s>>>(a);
-      break;
-    case GEMM_OUT_CACHE: gemm_bf16_kernel<XM, GEMM_OUT_CACHE><<<grid, kThreads, 0, s>>>(a); break;
-    default: gemm_bf16_kernel<XM, GEMM_OUT_CACHE_T><<<grid, kThreads, 0, s>>>(a); break;
+    case GEMM_OUT_BF16: gemm_bf16_kernel<GEMM_OUT_BF16><<<grid, kThreads, 0, s>>>(a); break;
+    case GEMM_OUT_BF16_RES_F32: gemm_bf16_kernel<GEMM_OUT_BF16_RES_F32><<<grid, kThreads, 0, s>>>(a); break;
+    case GEMM_OUT_F32_RES_BF16: gemm_bf16_kernel<GEMM_OUT_F32_RES_BF16><<<grid, kThreads, 0, s>>>(a); break;
+    case GEMM_OUT_CACHE: gemm_bf16_kernel<GEMM_OUT_CACHE><<<grid, kThreads, 0, s>>>(a); break;
+    default: gemm_bf16_kernel<GEMM_OUT_CACHE_T><<<grid, kThreads, 0, s>>>(a); break;
   }
   return hipGetLastError();
 }
@@ -189,8 +171,7 @@ hipError_t launch_gemm_bf16(const GemmArgs &a, hipStream_t s) {
   int tiles = 0;
   for (int i = 0; i < a.nseg; ++i) tiles += gemm_ntiles(a.seg[i].N);
   dim3 grid(tiles, (a.M + BM - 1) / BM);
-  if (a.xmode == GEMM_X_SWIGLU) return launch_x<GEMM_X_SWIGLU>(a, grid, s);
-  return launch_x<GEMM_X_BF16>(a, grid, s);
+  return launch_o(a, grid, s);
 }
 
 }  // namespace dl

@@ -81,8 +81,7 @@ hipError_t launch_gemv(const GvArgs &a, hipStream_t s);
 // three segments.
 // ---------------------------------------------------------------------------
 enum GemmX : int {
-  GEMM_X_BF16 = 0,     // X bf16 [M, ldx]
-  GEMM_X_SWIGLU = 1    // X = silu(X) * X2, both bf16
+  GEMM_X_BF16 = 0      // X bf16 [M, ldx]
 };
 enum GemmOut : int {
   GEMM_OUT_BF16 = 0,        // C bf16 [M, ldc]
@@ -95,7 +94,6 @@ enum GemmOut : int {
 struct GemmSeg {
   const uint16_t *W;  // Wt [N, K], operand tiles
   const uint16_t *X;  // [M, ldx]
-  const uint16_t *X2; // SwiGLU partner
   void *C;            // output
   float *C32;         // optional f32 output
   const void *R;      // residual
@@ -211,6 +209,9 @@ struct FillRegion {
   int tile_rows = 0, tile_cols = 0;
 };
 hipError_t launch_fill(const FillRegion *r, int nreg, hipStream_t s);
+// SwiGLU of two bf16 arrays, in place: g[i] = silu(g[i]) * u[i] (n % 8 == 0,
+// 16-byte aligned)
+hipError_t launch_swiglu_bf16(uint16_t *g, const uint16_t *u, int64_t n, hipStream_t s);
 // RMSNorm into operand tiles: xt [Mp, n] bf16 tiles, row m < M =
 // x[m] / sqrt(mean(x[m]^2) + eps) * gamma (x bf16 [M, n], gamma [n] or NULL),
 // rows M .. Mp - 1 zero; the same launch zeroes up to four fill regions.

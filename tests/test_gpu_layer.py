@@ -110,13 +110,13 @@ SMALL = [
 
 
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
-def test_small_layer(B, case):
+def test_small_layer(B, case, rank_up=None):
     name, dt, h, nq, nkv, d, f, ra, rkv, rm, Bsz, T, past, L_max, theta = case
-    print(f"layer {case}", flush=True)
+    print(f"layer {case} rank_up={rank_up}", flush=True)
     r = np.random.Generator(np.random.PCG64(sum(map(ord, name))))
     if past is None:
         past = list(r.integers(0, L_max - T, size=Bsz))
-    shp_ranks = {"q": ra, "k": rkv, "v": rkv, "o": ra, "gate": rm, "up": rm, "down": rm}
+    shp_ranks = {"q": ra, "k": rkv, "v": rkv, "o": ra, "gate": rm, "up": rank_up or rm, "down": rm}
     shp = W.LayerShape(h, nq, nkv, d, f, tuple((p, shp_ranks[p]) for p in W.PROJECTIONS), dt, theta)
     facs = {}
     for p, (m, n) in shp.shapes().items():
@@ -139,6 +139,14 @@ def test_small_layer_row_tiles(B, monkeypatch, case):
     and row sums, split merges."""
     monkeypatch.setenv("DL_GEMV_R", "2")
     test_small_layer(B, case)
+
+
+@pytest.mark.parametrize("case", [SMALL[2], SMALL[1]], ids=[SMALL[2][0], SMALL[1][0]])
+def test_small_layer_unequal_mlp_ranks(B, case):
+    """Gate and up factors of different rank: the prefill MLP cannot pair them
+    in one launch and applies SwiGLU while staging the down GEMM's operand;
+    the decode GEMV pairs them with different K halves."""
+    test_small_layer(B, case, rank_up=case[9] - 64)
 
 
 # ----------------------------------------------------------------------------
