@@ -417,29 +417,42 @@ int env_int(const char *name, int dflt) {
 }
 }  // namespace
 
+// Compute units of the current device (256 on MI355X).
+int device_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, v = 0;
+    cus = hipGetDevice(&dev) == hipSuccess &&
+                  hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0
+              ? v
+              : 256;
+  }
+  return cus;
+}
+
 size_t gemv_plan(GvArgs &a) {
   int tiles = 0;
   for (int i = 0; i < a.nseg; ++i) tiles += (a.seg[i].N + kRows - 1) / kRows;
   a.waves = env_int("DL_GEMV_WAVES", 4) == 8 ? 8 : 4;
   const int ksteps = (a.K + a.K2) / 32;
-  // K splits: enough work items for about `target` workgroups, but at least
-  // `min_steps` steps per wave
-  const int target = env_int("DL_GEMV_WGS", 256);
+  const int cus = std::max(1, env_int("DL_GEMV_CUS", device_cus()));
   const int min_steps = std::max(1, env_int("DL_GEMV_MIN_STEPS", 4));
-  auto splits = [&](int items) {
-    int ks = (target + items - 1) / items;
-    ks = std::min(ks, std::max(1, ksteps / (min_steps * a.waves)));
-    return std::max(1, std::min(ks, 64));
-  };
+  // K split: the largest that keeps the grid within one workgroup per
+  // compute unit (ks = CUs / items), never more. Measured per launch on
+  // 256 CUs: grids a little over the CU count (264, 304 or 352 workgroups)
+  // are as slow as a whole extra round on the CUs that take two items, and
+  // each split adds a merge; a one-round grid with some CUs idle is faster
+  // (e.g. 136 unsplit tiles of a 4096-wide K, or 116 tiles split in two).
+  const int ks_max = std::max(1, std::min(64, ksteps / (min_steps * a.waves)));
+  auto splits = [&](int items) { return std::max(1, std::min(ks_max, cus / std::max(1, items))); };
   // Two row tiles per item halve the activation reads (each activation
   // fragment feeds two weight tiles) where the halved item count still
-  // fills the target without a K split. (Doubling the split of an already
-  // split launch instead measured slower: shorter streams per wave and
-  // larger merges.)
+  // fills every compute unit. (Pairing tiles of a split launch by doubling
+  // its split measured slower: shorter streams per wave, larger merges.)
   int R = 1;
   if (a.waves == 4) {
     const int forced = env_int("DL_GEMV_R", 0);
-    R = forced == 1 || forced == 2 ? forced : (tiles >= 2 * target && splits(tiles / 2) == 1 ? 2 : 1);
+    R = forced == 1 || forced == 2 ? forced : (tiles >= 2 * cus ? 2 : 1);
   }
   a.rtiles = R;
   int items = 0;
@@ -448,7 +461,9 @@ size_t gemv_plan(GvArgs &a) {
     items += ((a.seg[i].N + kRows - 1) / kRows + R - 1) / R;
   }
   a.ntiles = items;
-  const int sps = (ksteps + splits(items) - 1) / splits(items);
+  const int ks_forced = env_int("DL_GEMV_KS", 0);
+  const int ks = ks_forced > 0 ? std::min(ks_forced, ks_max) : splits(items);
+  const int sps = (ksteps + ks - 1) / ks;
   a.split_steps = sps;
   a.ksplit = (ksteps + sps - 1) / sps;
   const int MB = (a.M + 15) / 16;
