@@ -393,7 +393,9 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
 
 template <int MB, int XM, int PAIRED, int RS>
 hipError_t launch_t(const GvArgs &a, int grid, hipStream_t s) {
-  if (a.rtiles == 2)
+  if (MB <= 2 && a.rtiles == 4)   // (four tiles of four row blocks would overflow LDS)
+    gemv_kernel<MB, XM, PAIRED, RS, MB <= 2 ? 4 : 2, 4><<<grid, 4 * 64, 0, s>>>(a);
+  else if (a.rtiles == 2)
     gemv_kernel<MB, XM, PAIRED, RS, 2, 4><<<grid, 4 * 64, 0, s>>>(a);
   else if (a.waves == 4)
     gemv_kernel<MB, XM, PAIRED, RS, 1, 4><<<grid, 4 * 64, 0, s>>>(a);
@@ -445,14 +447,20 @@ size_t gemv_plan(GvArgs &a) {
   // (e.g. 136 unsplit tiles of a 4096-wide K, or 116 tiles split in two).
   const int ks_max = std::max(1, std::min(64, ksteps / (min_steps * a.waves)));
   auto splits = [&](int items) { return std::max(1, std::min(ks_max, cus / std::max(1, items))); };
-  // Two row tiles per item halve the activation reads (each activation
-  // fragment feeds two weight tiles) where the halved item count still
-  // fills every compute unit. (Pairing tiles of a split launch by doubling
-  // its split measured slower: shorter streams per wave, larger merges.)
+  // Two or four row tiles per item share each activation fragment (halving
+  // or quartering the activation reads): the widest item whose count still
+  // fills 7/8 of the compute units in one unsplit round. (Pairing tiles of a
+  // split launch by raising its split measured slower: shorter streams per
+  // wave, larger merges.) Four tiles only up to 32 token rows (LDS).
   int R = 1;
   if (a.waves == 4) {
     const int forced = env_int("DL_GEMV_R", 0);
-    R = forced == 1 || forced == 2 ? forced : (tiles >= 2 * cus ? 2 : 1);
+    const int fill = (7 * cus + 7) / 8;
+    R = forced == 1 || forced == 2 || forced == 4 ? forced
+        : tiles >= 4 * fill && a.M <= 32        ? 4
+        : tiles >= 2 * fill                     ? 2
+                                                : 1;
+    if (R == 4 && a.M > 32) R = 2;
   }
   a.rtiles = R;
   int items = 0;

@@ -64,7 +64,7 @@ struct GvArgs {
   int T, L_max;
   // set by gemv_plan / the caller
   int ntiles, ksplit, split_steps;   // ntiles: work items (groups of rtiles tiles) per split
-  int rtiles;             // 16-row tiles per work item (1 or 2)
+  int rtiles;             // 16-row tiles per work item (1, 2 or 4)
   int waves;              // waves per workgroup (4 or 8)
   float *part;            // gemv_plan's return value in floats
   int *counters;          // ntiles ints, zero before the launch (left zero after it)

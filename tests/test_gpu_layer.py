@@ -132,12 +132,13 @@ def test_small_layer(B, case, rank_up=None):
     check_step(dt, x, y, x2, ck, cv, want, past, T)
 
 
+@pytest.mark.parametrize("R", ["2", "4"])
 @pytest.mark.parametrize("case", SMALL[:2], ids=[c[0] for c in SMALL[:2]])
-def test_small_layer_row_tiles(B, monkeypatch, case):
-    """The small-M layer with every GEMV on two-tile work items (DL_GEMV_R=2):
-    cache scatter, SwiGLU pairs, residual epilogue with the MLP norm's tiles
-    and row sums, split merges."""
-    monkeypatch.setenv("DL_GEMV_R", "2")
+def test_small_layer_row_tiles(B, monkeypatch, case, R):
+    """The small-M layer with every GEMV on two- or four-tile work items
+    (DL_GEMV_R): cache scatter, SwiGLU pairs, residual epilogue with the MLP
+    norm's tiles and row sums, split merges."""
+    monkeypatch.setenv("DL_GEMV_R", R)
     test_small_layer(B, case)
 
 

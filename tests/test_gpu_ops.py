@@ -64,13 +64,14 @@ def test_lowrank_linear(B, M, m, k, n, dt):
     assert relerr(to_host(y), want) <= TOL[dt]
 
 
-@pytest.mark.parametrize("R", ["1", "2"])
-@pytest.mark.parametrize("M,m,k,n", [(16, 4096, 1216, 4096), (37, 512, 448, 192), (5, 2048, 128, 1024)])
+@pytest.mark.parametrize("R", ["1", "2", "4"])
+@pytest.mark.parametrize("M,m,k,n", [(16, 4096, 1216, 4096), (37, 512, 448, 192), (5, 2048, 128, 1088)])
 def test_lowrank_linear_row_tiles(B, monkeypatch, R, M, m, k, n):
-    """Both GEMV work-item widths (one or two 16-row tiles sharing each
+    """Every GEMV work-item width (one, two or four 16-row tiles sharing each
     activation fragment), forced through DL_GEMV_R, with K splits (the first
-    factor) and without, and multi-block M (bf16 factor pairs have m, k, n
-    multiples of 64, so every item holds two real tiles)."""
+    factor) and without, and multi-block M (four-tile items fall back to two
+    above 32 rows). bf16 factor pairs have m, k, n multiples of 64, so every
+    item's tiles are real."""
     monkeypatch.setenv("DL_GEMV_R", R)
     print(f"lowrank_linear R={R} M={M} m={m} k={k} n={n}", flush=True)
     r = rng(M * 11 + n)
