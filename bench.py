@@ -361,6 +361,7 @@ def prefill_bench(args, torch, binding, W):
            "gemm_TFLOP_per_s": round(gemm_tf, 2) if gemm_tf else None,
            "gemm_mfma_frac": round(gemm_tf / MFMA_BF16_PEAK_TFLOPS, 4) if gemm_tf else None,
            "gemm_ms": round(gemm_ms, 3), "attention_ms": round(attn_ms, 3),
+           "roles_ms": {f"{k}/{r}": round(sum(v), 3) for (k, r), v in sorted(per.items())},
            "steps": args.prefill_steps}
     del sets
     torch.cuda.empty_cache()

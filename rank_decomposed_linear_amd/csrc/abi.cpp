@@ -159,11 +159,8 @@ hipError_t gemv_run(GvArgs &a, float *part, int *counters, hipStream_t s) {
 }
 
 hipError_t gemm(GemmArgs &a, hipStream_t s) {
-  int tiles = 0;
-  for (int i = 0; i < a.nseg; ++i) {
-    a.seg[i].tile_begin = tiles;
-    tiles += gemm_ntiles(a.seg[i].N);
-  }
+  for (int i = 0; i < a.nseg; ++i)
+    if (a.seg[i].omode < 0) a.seg[i].omode = a.omode;
   return launch_gemm_bf16(a, s);
 }
 
@@ -175,6 +172,7 @@ GemmSeg mseg(const void *W, const void *X, void *C, int N, int ldx, int ldc) {
   g.N = N;
   g.ldx = ldx;
   g.ldc = ldc;
+  g.omode = -1;
   return g;
 }
 
@@ -539,7 +537,7 @@ dl_status dl_lowrank_kv_append(const void *x, const void *A_k, const void *A_v, 
     return DL_OK;
   }
   GemmArgs a{};
-  a.nseg = 1;
+  a.nseg = 2;
   a.M = M;
   a.K = mi;
   a.xmode = GEMM_X_BF16;
@@ -548,9 +546,8 @@ dl_status dl_lowrank_kv_append(const void *x, const void *A_k, const void *A_v, 
   a.T = Ti;
   a.L_max = Lm;
   a.seg[0] = mseg(A_k, x, Ck, rk, mi, rk);
-  DL_HIP(gemm(a, s));
-  a.omode = GEMM_OUT_CACHE_T;
-  a.seg[0] = mseg(A_v, x, Cv, rv, mi, rv);
+  a.seg[1] = mseg(A_v, x, Cv, rv, mi, rv);
+  a.seg[1].omode = GEMM_OUT_CACHE_T;
   DL_HIP(gemm(a, s));
   return DL_OK;
 }
@@ -989,27 +986,23 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
   set_role(R_ATTN_NORM);
   DL_HIP(launch_rmsnorm(x, 0, L->attn_norm, gf32, w.a16, 0, M, h, eps, s));
   {
+    // the concatenated down factors [A_q, A_k, A_v] in one launch; the k
+    // and v segments scatter their latents into the caches
     GemmArgs a{};
-    a.nseg = 1;
+    a.nseg = 3;
     a.M = M;
     a.K = h;
     a.omode = GEMM_OUT_BF16;
+    a.past_lens = past_lens;
+    a.T = D.T;
+    a.L_max = D.L_max;
     a.seg[0] = mseg(L->q.A, w.a16, w.tq16, D.rq, h, D.rq);
+    a.seg[1] = mseg(L->k.A, w.a16, Ck, D.rk, h, D.rk);
+    a.seg[1].omode = GEMM_OUT_CACHE;
+    a.seg[2] = mseg(L->v.A, w.a16, Cv, D.rv, h, D.rv);
+    a.seg[2].omode = GEMM_OUT_CACHE_T;
     set_role(R_QKV_DOWN);
     DL_HIP(gemm(a, s));
-    GemmArgs b{};
-    b.nseg = 1;
-    b.M = M;
-    b.K = h;
-    b.omode = GEMM_OUT_CACHE;
-    b.past_lens = past_lens;
-    b.T = D.T;
-    b.L_max = D.L_max;
-    b.seg[0] = mseg(L->k.A, w.a16, Ck, D.rk, h, D.rk);
-    DL_HIP(gemm(b, s));
-    b.omode = GEMM_OUT_CACHE_T;
-    b.seg[0] = mseg(L->v.A, w.a16, Cv, D.rv, h, D.rv);
-    DL_HIP(gemm(b, s));
     GemmArgs q{};
     q.nseg = 1;
     q.M = M;

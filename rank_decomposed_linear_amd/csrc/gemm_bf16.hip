@@ -1,15 +1,22 @@
 // bf16 MFMA GEMM for prefill-sized M: one factor of a decomposed projection
 // (W ~ A B, DeInfer section 2.1, Eq. (1)), C = X W with f32 accumulation.
 //
-// Both factors are stored transposed (Wt[N, K]) in 16 x 32 operand tiles
-// (1 KB, MFMA lane order): the weight block of a workgroup's k step is
-// sixteen such tiles, copied to LDS with contiguous 16-byte loads and read
-// back one 16-byte ds_read per lane and fragment. The activation rows are
-// staged as 16-byte chunks with an XOR swizzle, so their operand reads are
-// conflict-free too.
+// Tile 256 x 256 x 64, 8 waves (two per SIMD, so one wave's LDS traffic and
+// barrier wait hide under the other's MFMAs). Each wave owns a 128 x 64
+// block of C: 8 x 4 accumulator blocks of v_mfma_f32_16x16x32_bf16.
 //
-// Tile 128 x 128 x 64, 4 waves (2 x 2), each wave 64 x 64 = 4 x 4 MFMA
-// blocks; LDS double-buffered (64 KB).
+// Both operands sit in LDS in MFMA operand-tile order (16 rows x 32 k per
+// 1 KB, lane l at byte 16 l), so every operand read is one conflict-free
+// ds_read_b128 of a contiguous 1 KB and every staging write is one too. The
+// factors already live in that order in HBM (Wt [N, K] in 16 x 32 tiles): a
+// weight tile's k step is 32 contiguous 1 KB fragments. Activation rows are
+// row-major: lane l of a staging load fetches row (l % 16), k columns
+// 8 (l / 16) .. +7 of its fragment. LDS double-buffered, 128 KB.
+//
+// Work order: the hardware deals workgroups to the eight XCDs round-robin;
+// the linear index is remapped so each XCD runs a contiguous range of tiles,
+// taken in groups of kGroupM row tiles, so the CUs sharing an XCD's L2 share
+// activation rows and weight columns.
 #include "common.h"
 #include "kernels.h"
 #include "trace.h"
@@ -17,161 +24,202 @@
 namespace dl {
 
 namespace {
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int kThreads = 256;
-constexpr int kAElems = BM * BK;          // bf16 elements of one A tile
-constexpr int kBElems = BN * BK;          // bf16 elements of one weight tile
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int kThreads = 512;
+constexpr int kFrags = (BM / 16) * (BK / 32);  // 1 KB fragments per operand per stage
+constexpr int kStage = 2 * kFrags * 64;        // u32x4 per stage (A then B)
+constexpr int kXcds = 8;
+constexpr int kGroupM = 4;
+constexpr int kEpPitch = 256 + 4;  // f32 row pitch of the epilogue's LDS rows
 
-struct Stage {
-  u32x4 a[4], b[4];
-};
+__device__ __forceinline__ void tile_of(int bid, int total, int tiles_m, int tiles_n, int &tm,
+                                        int &tn) {
+  // bijection: XCD x = bid % 8 runs logical tiles [start_x, start_x + count_x)
+  const int xcd = bid % kXcds, local = bid / kXcds;
+  const int q = total / kXcds, rem = total % kXcds;
+  const int L = xcd < rem ? xcd * (q + 1) + local : rem * (q + 1) + (xcd - rem) * q + local;
+  const int per_group = kGroupM * tiles_n;
+  const int g = L / per_group, w = L - g * per_group;
+  const int gm = min(kGroupM, tiles_m - g * kGroupM);
+  tn = w / gm;
+  tm = g * kGroupM + (w - tn * gm);
+}
 
-template <int OM>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][kAElems + kBElems];
+  __shared__ u32x4 lds[2 * kStage];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int j = lane & 15, grp = lane >> 4;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
 
-  const int bx = blockIdx.x;
+  int tm, tn;
+  tile_of(blockIdx.x, a.tiles_m * a.tiles_n, a.tiles_m, a.tiles_n, tm, tn);
   int si = 0;
-  if (a.nseg > 1 && bx >= a.seg[1].tile_begin) si = 1;
-  if (a.nseg > 2 && bx >= a.seg[2].tile_begin) si = 2;
-  const GemmSeg sg = a.seg[si];
-  const int n0 = (bx - sg.tile_begin) * BN;
-  const int m0 = blockIdx.y * BM;
+  if (a.nseg > 1 && tn >= a.seg[1].tile_begin) si = 1;
+  if (a.nseg > 2 && tn >= a.seg[2].tile_begin) si = 2;
+  const GemmSeg &sg = a.seg[si];
+  const int n0 = (tn - sg.tile_begin) * BN;
+  const int m0 = tm * BM;
+  const int K = a.K;
 
-  // Thread t stages 16-byte chunk (row (t + 256 it) / 8, column chunk t % 8)
-  // of both tiles, it = 0..3.
-  const int kc = tid & 7, r0 = tid >> 3;
-
-  // weight unit u = tid + 256 it (16 bytes): tile T = u / 64 = 2 nb + ks,
-  // lane u % 64; tiles (nb, 0) and (nb, 1) are adjacent in memory
-  auto gload = [&](Stage &st, int k0) {
+  // Staging: thread t moves fragment (wave + 8 i), lane `lane`, of both
+  // operands, i = 0..3. A fragment f = 2 rb + ks holds rows 16 rb .. +15,
+  // k 32 ks .. +31 of the tile; out-of-range rows and weight rows are
+  // clamped (their results are never stored), so every load is issued.
+  const uint16_t *xp[4];
+  const uint16_t *wp[4];
+  const int nblk_last = (sg.N >> 4) - 1;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int row = m0 + r0 + 32 * it;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row < a.M) {
-        const size_t off = static_cast<size_t>(row) * sg.ldx + k0 + 8 * kc;
-        v = *reinterpret_cast<const u32x4 *>(sg.X + off);
-      }
-      st.a[it] = v;
-      const int u = tid + 256 * it, tt = u >> 6, nb = tt >> 1, ks = tt & 1;
-      st.b[it] = n0 + 16 * nb < sg.N
-                     ? *reinterpret_cast<const u32x4 *>(sg.W + frag_off((n0 >> 4) + nb, (k0 >> 5) + ks, a.K, u & 63))
-                     : u32x4{0u, 0u, 0u, 0u};
+  for (int i = 0; i < 4; ++i) {
+    const int f = wave + 8 * i, rb = f >> 1, ks = f & 1;
+    const int row = min(m0 + 16 * rb + (lane & 15), a.M - 1);
+    xp[i] = sg.X + static_cast<size_t>(row) * sg.ldx + 32 * ks + 8 * (lane >> 4);
+    const int nb = min((n0 >> 4) + rb, nblk_last);
+    wp[i] = sg.W + frag_off(nb, ks, K, lane);
+  }
+
+  u32x4 st[8];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      st[i] = *reinterpret_cast<const u32x4 *>(xp[i] + kt * BK);
+      st[4 + i] = *reinterpret_cast<const u32x4 *>(wp[i] + static_cast<size_t>(kt) * 2 * 512);
     }
   };
-  auto sstore = [&](const Stage &st, int buf) {
-    uint16_t *base = lds[buf];
+  auto sstore = [&](int buf) {
+    u32x4 *base = lds + buf * kStage;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int row = r0 + 32 * it;
-      const int chunk = kc ^ (row & 7);
-      *reinterpret_cast<u32x4 *>(base + row * BK + chunk * 8) = st.a[it];
-      *reinterpret_cast<u32x4 *>(base + kAElems + (tid + 256 * it) * 8) = st.b[it];
+    for (int i = 0; i < 4; ++i) {
+      base[(wave + 8 * i) * 64 + lane] = st[i];
+      base[kFrags * 64 + (wave + 8 * i) * 64 + lane] = st[4 + i];
     }
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[8][4];
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
+  for (int x = 0; x < 8; ++x)
 #pragma unroll
     for (int y = 0; y < 4; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int ktiles = a.K / BK;
-  Stage st;
-  gload(st, 0);
-  sstore(st, 0);
+  const int ktiles = K / BK;
+  gload(0);
+  sstore(0);
   __syncthreads();
   for (int kt = 0; kt < ktiles; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < ktiles) gload(st, (kt + 1) * BK);
-    const uint16_t *base = lds[buf];
+    if (kt + 1 < ktiles) gload(kt + 1);
+    const u32x4 *base = lds + buf * kStage;
 #pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      u32x4 af[4], bfr[4];
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4 af[8], bfr[4];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const int row = wm * 64 + mb * 16 + j;
-        const int chunk = (ks * 4 + grp) ^ (row & 7);
-        af[mb] = *reinterpret_cast<const u32x4 *>(base + row * BK + chunk * 8);
-      }
+      for (int nb = 0; nb < 4; ++nb) bfr[nb] = base[kFrags * 64 + ((wn * 4 + nb) * 2 + ks) * 64 + lane];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        bfr[nb] = *reinterpret_cast<const u32x4 *>(base + kAElems + (((wn * 4 + nb) * 2 + ks) * 64 + lane) * 8);
+      for (int mb = 0; mb < 8; ++mb) af[mb] = base[((wm * 8 + mb) * 2 + ks) * 64 + lane];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma_bf16(af[mb], bfr[nb], acc[mb][nb]);
     }
-    if (kt + 1 < ktiles) sstore(st, buf ^ 1);
+    if (kt + 1 < ktiles) sstore(buf ^ 1);
     __syncthreads();
   }
 
-  // Epilogue: lane (j, grp) holds C[m0 + 64wm + 16mb + 4grp + r][n0 + 64wn + 16nb + j].
+  // Epilogue, in four passes of 64 rows: the waves owning the pass's rows
+  // park their f32 accumulators in LDS (row pitch kEpPitch, so the 16-lane
+  // column groups of an accumulator row land in distinct banks), then every
+  // thread takes 8 consecutive columns of a row and applies the segment's
+  // output mode with 16-byte accesses. Lane (j, grp) of block (mb, nb) holds
+  // C[128 wm + 16 mb + 4 grp + r][64 wn + 16 nb + j].
+  const int j = lane & 15, grp = lane >> 4;
+  const int om = sg.omode;
+  float *ep = reinterpret_cast<float *>(lds);
+  const int c8 = 8 * (tid & 31);
+  const int n = n0 + c8;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+  for (int p = 0; p < 4; ++p) {
+    if (wm == (p >> 1)) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = m0 + wm * 64 + mb * 16 + 4 * grp + r;
-      if (m >= a.M) continue;
-      if constexpr (OM == GEMM_OUT_CACHE || OM == GEMM_OUT_CACHE_T) {
-        // key cache tiled [L_max, N] / value cache tiled [N, L_max], per sequence
-        const int b = m / a.T, pos = a.past_lens[b] + (m - b * a.T);
-        uint16_t *seq = static_cast<uint16_t *>(sg.C) + static_cast<size_t>(b) * sg.N * a.L_max;
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int n = n0 + wn * 64 + nb * 16 + j;
-          if (n < sg.N)
-            seq[OM == GEMM_OUT_CACHE ? tile_off(pos, n, sg.N) : tile_off(n, pos, a.L_max)] =
-                f2bf(acc[mb][nb][r]);
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            ep[(mb * 16 + 4 * grp + r) * kEpPitch + wn * 64 + nb * 16 + j] =
+                acc[4 * (p & 1) + mb][nb][r];
+    }
+    __syncthreads();
+    if (n < sg.N) {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int rr = (tid >> 5) + 16 * it;
+        const int m = m0 + 64 * p + rr;
+        if (m >= a.M) continue;
+        const f32x4 lo = *reinterpret_cast<const f32x4 *>(ep + rr * kEpPitch + c8);
+        const f32x4 hi = *reinterpret_cast<const f32x4 *>(ep + rr * kEpPitch + c8 + 4);
+        float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        if (om == GEMM_OUT_CACHE || om == GEMM_OUT_CACHE_T) {
+          // key cache tiled [L_max, N] / value cache tiled [N, L_max], per sequence
+          const int b = m / a.T, pos = a.past_lens[b] + (m - b * a.T);
+          uint16_t *seq = static_cast<uint16_t *>(sg.C) + static_cast<size_t>(b) * sg.N * a.L_max;
+          if (om == GEMM_OUT_CACHE) {
+            *reinterpret_cast<u32x4 *>(seq + tile_off(pos, n, sg.N)) =
+                u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) seq[tile_off(n + e, pos, a.L_max)] = f2bf(v[e]);
+          }
+          continue;
         }
-        continue;
-      }
-      const size_t rowoff = static_cast<size_t>(m) * sg.ldc;
+        const size_t o = static_cast<size_t>(m) * sg.ldc + n;
+        if (om == GEMM_OUT_BF16_RES_F32) {
+          const float *rp = static_cast<const float *>(sg.R) + static_cast<size_t>(m) * sg.ldr + n;
+          const f32x4 r0 = *reinterpret_cast<const f32x4 *>(rp);
+          const f32x4 r1 = *reinterpret_cast<const f32x4 *>(rp + 4);
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int n = n0 + wn * 64 + nb * 16 + j;
-        if (n >= sg.N) continue;
-        float v = acc[mb][nb][r];
-        if constexpr (OM == GEMM_OUT_BF16) {
-          static_cast<uint16_t *>(sg.C)[rowoff + n] = f2bf(v);
-        } else if constexpr (OM == GEMM_OUT_BF16_RES_F32) {
-          v += static_cast<const float *>(sg.R)[static_cast<size_t>(m) * sg.ldr + n];
-          static_cast<uint16_t *>(sg.C)[rowoff + n] = f2bf(v);
-          if (sg.C32) sg.C32[rowoff + n] = v;
-        } else {  // GEMM_OUT_F32_RES_BF16
-          v += bf2f(static_cast<const uint16_t *>(sg.R)[static_cast<size_t>(m) * sg.ldr + n]);
-          sg.C32[rowoff + n] = v;
+          for (int e = 0; e < 4; ++e) {
+            v[e] += r0[e];
+            v[4 + e] += r1[e];
+          }
+          if (sg.C32) {
+            *reinterpret_cast<f32x4 *>(sg.C32 + o) = f32x4{v[0], v[1], v[2], v[3]};
+            *reinterpret_cast<f32x4 *>(sg.C32 + o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+          }
+        } else if (om == GEMM_OUT_F32_RES_BF16) {
+          const u32x4 rb = *reinterpret_cast<const u32x4 *>(
+              static_cast<const uint16_t *>(sg.R) + static_cast<size_t>(m) * sg.ldr + n);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[2 * e] += bflo(rb[e]);
+            v[2 * e + 1] += bfhi(rb[e]);
+          }
+          *reinterpret_cast<f32x4 *>(sg.C32 + o) = f32x4{v[0], v[1], v[2], v[3]};
+          *reinterpret_cast<f32x4 *>(sg.C32 + o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+          continue;
         }
+        *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(sg.C) + o) =
+            u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
       }
     }
+    __syncthreads();
   }
-}
-
-hipError_t launch_o(const GemmArgs &a, dim3 grid, hipStream_t s) {
-  switch (a.omode) {
-    case GEMM_OUT_BF16: gemm_bf16_kernel<GEMM_OUT_BF16><<<grid, kThreads, 0, s>>>(a); break;
-    case GEMM_OUT_BF16_RES_F32: gemm_bf16_kernel<GEMM_OUT_BF16_RES_F32><<<grid, kThreads, 0, s>>>(a); break;
-    case GEMM_OUT_F32_RES_BF16: gemm_bf16_kernel<GEMM_OUT_F32_RES_BF16><<<grid, kThreads, 0, s>>>(a); break;
-    case GEMM_OUT_CACHE: gemm_bf16_kernel<GEMM_OUT_CACHE><<<grid, kThreads, 0, s>>>(a); break;
-    default: gemm_bf16_kernel<GEMM_OUT_CACHE_T><<<grid, kThreads, 0, s>>>(a); break;
-  }
-  return hipGetLastError();
 }
 }  // namespace
 
 int gemm_ntiles(int N) { return (N + BN - 1) / BN; }
 
-hipError_t launch_gemm_bf16(const GemmArgs &a, hipStream_t s) {
+hipError_t launch_gemm_bf16(GemmArgs &a, hipStream_t s) {
   TraceGuard trace_guard(K_GEMM_BF16, s);
   int tiles = 0;
-  for (int i = 0; i < a.nseg; ++i) tiles += gemm_ntiles(a.seg[i].N);
-  dim3 grid(tiles, (a.M + BM - 1) / BM);
-  return launch_o(a, grid, s);
+  for (int i = 0; i < a.nseg; ++i) {
+    a.seg[i].tile_begin = tiles;
+    tiles += gemm_ntiles(a.seg[i].N);
+  }
+  a.tiles_n = tiles;
+  a.tiles_m = (a.M + BM - 1) / BM;
+  const int64_t total = static_cast<int64_t>(a.tiles_n) * a.tiles_m;
+  if (total <= 0 || total > INT32_MAX) return hipErrorInvalidValue;
+  gemm_bf16_kernel<<<dim3(static_cast<unsigned>(total)), kThreads, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 }  // namespace dl

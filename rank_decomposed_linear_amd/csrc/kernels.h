@@ -98,20 +98,23 @@ struct GemmSeg {
   float *C32;         // optional f32 output
   const void *R;      // residual
   int N, ldx, ldc, ldr;
-  int tile_begin;     // first N tile of this segment
+  int omode;          // GemmOut of this segment
+  int tile_begin;     // first N tile of this segment (set by the launcher)
 };
 
 struct GemmArgs {
   GemmSeg seg[3];
   int nseg;
-  int M, K;
-  int xmode, omode;
+  int M, K;           // K % 64 == 0; every segment's N % 16 == 0
+  int xmode, omode;   // omode: default for segments whose own omode is < 0
   // cache scatter
   const int32_t *past_lens;
   int T, L_max;
+  int tiles_m, tiles_n;  // set by the launcher
 };
 
-hipError_t launch_gemm_bf16(const GemmArgs &a, hipStream_t s);
+// Sets the segments' tile_begin and the tile counts, then launches.
+hipError_t launch_gemm_bf16(GemmArgs &a, hipStream_t s);
 int gemm_ntiles(int N);
 
 // ---------------------------------------------------------------------------
