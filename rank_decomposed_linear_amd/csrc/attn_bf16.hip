@@ -10,9 +10,12 @@
 //
 //  prefill  A workgroup owns one kv head and up to 256 (token, head) query
 //           rows; per 64-key tile its eight waves rebuild K (rotated) and
-//           V^T into swizzled LDS, then each wave runs an online-softmax
-//           pass for its 32 query rows.
+//           V^T into swizzled LDS from latents and factor slices staged in
+//           LDS, then each wave runs an online-softmax pass for its 32 query
+//           rows.
 #include <math.h>
+
+#include <algorithm>
 
 #include "common.h"
 #include "kernels.h"
@@ -24,6 +27,15 @@ namespace {
 
 __device__ __forceinline__ u32x4 ld16(const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
+// raw buffer resource over `bytes` bytes at p (loads past the end read zero)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), static_cast<short>(0), bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+
 // operand fragment (rank step rs, d block blk of kv head g) of an up factor
 // stored [n_kv * d, r] in tiles: lane (c, grp) gets B[32rs + 8grp .. +8][16blk + c]
 __device__ __forceinline__ u32x4 frag(const uint16_t *bt, int r, int gblk, int rs, int lane) {
@@ -32,16 +44,42 @@ __device__ __forceinline__ u32x4 frag(const uint16_t *bt, int r, int gblk, int r
 
 // ---------------------------------------------------------------------------
 // Prefill
+//
+// Work item: (sequence b, kv head g, query tile of QT tokens x G heads = 256
+// rows). Per 64-key tile the latents are consumed in chunks of 64 ranks:
+// all 512 threads stage the chunk's key latents, value latents and the head's
+// B_k / B_v slices into LDS with contiguous 16-byte loads, issued one chunk
+// ahead into registers. The value latents arrive rank-major and are
+// transposed to key-major operand tiles as they are written, so both
+// rebuilds reduce over ranks with one ds_read_b128 per operand. Waves 0-3
+// rebuild K^T for d-block pairs (x, x + D/32), the rotary partners, waves
+// 4-7 rebuild V for pairs of adjacent d blocks; each factor fragment is read
+// from LDS once per tile for all its key blocks. After the last chunk the K
+// waves rotate and write K, the V waves write V^T, and all eight waves run
+// the online-softmax pass for their 32 query rows.
 // ---------------------------------------------------------------------------
 template <int DB>
 __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
   constexpr int D = DB * 16, HALF = DB / 2, KT = 64;
-  constexpr int CH = D / 8;  // 16-byte chunks per K row
+  constexpr int CH = D / 8;       // 16-byte chunks per K row
+  constexpr int RS = 2;           // 32-rank steps per chunk
+  constexpr int NP = HALF;        // d-block pairs per side
+  constexpr int NKB = NP;         // key blocks per wave: 4 waves per side = NP pairs x 4 / NP
+  constexpr int U_CK = 4 * RS * 64, U_CV = 4 * RS * 64;  // u32x4 units (64 per 1 KB fragment)
+  constexpr int U_BK = DB * RS * 64, U_BV = DB * RS * 64;
+  constexpr int O_CV = U_CK, O_BK = U_CK + U_CV, O_BV = O_BK + U_BK;
+  constexpr int NU = (O_BV + U_BV) / 512;  // staging units per thread
+  constexpr int I_CV = U_CK / 512, I_BK = O_BK / 512, I_BV = O_BV / 512;
+  __shared__ u32x4 cs[O_BV + U_BV];
   __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * D];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[D * KT];
+  __shared__ u32x4 Qs[8 * 2 * HALF * 64];  // rotated, scaled query fragments of each wave
   __shared__ double revs[D / 2];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // wave is made provably uniform, so every fragment index derived from it
+  // stays scalar and each load is a scalar base plus the lane's 16 bytes
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 15, grp = lane >> 4;
   const int G = a.n_q / a.n_kv;
   const int QT = 256 / G;
@@ -53,13 +91,13 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
   const bool rope_on = a.theta != 0.f;
 
   for (int i = tid; i < D / 2; i += 512) revs[i] = rope_on ? rope_rev(i, D, a.theta) : 0.0;
-  __syncthreads();
 
-  // ---- query fragments: rows rho = 32*wave + 16*qb + (0..15) ----
+  // ---- query fragments: rows rho = 32*wave + 16*qb + (0..15), kept in
+  // LDS (fragment (wave, qb, t)) for the whole work item.
   // B operand of S^T = K Q^T: lane (q = j, grp) holds Q[q][32t + 8grp + e].
-  u32x4 qf[2][HALF];
   int qpos[2];
   bool qok[2];
+  __syncthreads();
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int rho = 32 * wave + 16 * qb + j;
@@ -99,7 +137,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
     }
 #pragma unroll
     for (int t = 0; t < HALF; ++t)
-      qf[qb][t] = u32x4{pack2(x[t][0] * a.scale_log2, x[t][1] * a.scale_log2),
+      Qs[((wave * 2 + qb) * HALF + t) * 64 + lane] = u32x4{pack2(x[t][0] * a.scale_log2, x[t][1] * a.scale_log2),
                         pack2(x[t][2] * a.scale_log2, x[t][3] * a.scale_log2),
                         pack2(x[t][4] * a.scale_log2, x[t][5] * a.scale_log2),
                         pack2(x[t][6] * a.scale_log2, x[t][7] * a.scale_log2)};
@@ -115,99 +153,188 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
   const int qmax_pos = past + min(t0 + QT, a.T) - 1;
   const int nkt = qmax_pos / KT + 1;
   const int rsk = a.r_k / 32, rsv = a.r_v / 32;
+  const int nchunk = max((rsk + RS - 1) / RS, (rsv + RS - 1) / RS);
+  const int nsteps = nkt * nchunk;
   const uint16_t *ck_b = a.ck + static_cast<size_t>(b) * a.L_max * a.r_k;
   const uint16_t *cv_b = a.cv + static_cast<size_t>(b) * a.r_v * a.L_max;
-  const int kb = wave >> 1;  // key block rebuilt by this wave
+  const int kb_last = a.L_max / 16 - 1, ps_last = a.L_max / 32 - 1;
 
-  for (int kt = 0; kt < nkt; ++kt) {
+  // ---- staging: unit i of this thread is u = tid + 512 i, fragment
+  // (u - group start) / 64, lane `lane`. Keys past the last query position
+  // stage zeros (their V rows must not leak NaN into P V). ----
+  // Buffer loads: one scalar resource per array, the lane's 16 bytes as the
+  // only vector offset, the (wave-uniform) fragment offset as soffset.
+  const __amdgpu_buffer_rsrc_t rck = make_rsrc(ck_b, a.L_max * a.r_k * 2);
+  const __amdgpu_buffer_rsrc_t rcv = make_rsrc(cv_b, a.r_v * a.L_max * 2);
+  const __amdgpu_buffer_rsrc_t rbk = make_rsrc(a.bk, a.n_kv * D * a.r_k * 2);
+  const __amdgpu_buffer_rsrc_t rbv = make_rsrc(a.bv, a.n_kv * D * a.r_v * 2);
+  const int lane16 = lane * 16;
+  u32x4 st[NU];
+  auto gload = [&](int kt, int c) {
+    const int k0 = kt * KT, r0 = c * RS;
+    const int nrk = rsk - r0, nrv = rsv - r0;
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      if (i < I_CV) {
+        const int f = wave + 8 * i, kb = f / RS, rs = f % RS;
+        const bool ok = rs < nrk && k0 + 16 * kb + j <= qmax_pos;
+        const int so = 2 * static_cast<int>(frag_off(min((k0 >> 4) + kb, kb_last), r0 + rs, a.r_k, 0));
+        st[i] = ok ? bload(rck, lane16, so) : z;
+      } else if (i < I_BK) {
+        const int f = wave + 8 * (i - I_CV), rb = f >> 1, ps = f & 1;
+        const int so = 2 * static_cast<int>(frag_off(2 * r0 + rb, min((k0 >> 5) + ps, ps_last), a.L_max, 0));
+        st[i] = rb < 2 * nrv ? bload(rcv, lane16, so) : z;
+      } else if (i < I_BV) {
+        const int f = wave + 8 * (i - I_BK), db = f / RS, rs = f % RS;
+        const int so = 2 * static_cast<int>(frag_off(g * DB + db, r0 + rs, a.r_k, 0));
+        st[i] = rs < nrk ? bload(rbk, lane16, so) : z;
+      } else {
+        const int f = wave + 8 * (i - I_BV), db = f / RS, rs = f % RS;
+        const int so = 2 * static_cast<int>(frag_off(g * DB + db, r0 + rs, a.r_v, 0));
+        st[i] = rs < nrv ? bload(rbv, lane16, so) : z;
+      }
+    }
+  };
+  auto swrite = [&](int kt) {
     const int k0 = kt * KT;
-    const int keyrow = k0 + 16 * kb + j;
-    const bool kvalid = keyrow <= qmax_pos;
-    // ---- rebuild K (rotated) for key block kb, d blocks {x, x+HALF} ----
-    {
-      constexpr int NX = HALF / 2 > 0 ? HALF / 2 : 1;
-      f32x4 acc[NX][2];
+    uint16_t *cv16 = reinterpret_cast<uint16_t *>(cs + O_CV);
 #pragma unroll
-      for (int xi = 0; xi < NX; ++xi) acc[xi][0] = acc[xi][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int xbase = (wave & 1) * NX;
-      // key tile of this 16-key block (lanes of keys past the last query
-      // position do not load)
-      const uint16_t *cp = ck_b + frag_off((k0 >> 4) + kb, 0, a.r_k, lane);
-      for (int rs = 0; rs < rsk; ++rs) {
-        const u32x4 c = kvalid ? ld16(cp + 512 * rs) : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < NU; ++i) {
+      if (i >= I_CV && i < I_BK) {
+        // value tile (rank rho, positions p .. p + 7) -> key-major tiles:
+        // key p + e, rank rho at tile (key / 16, rho / 32), lane
+        // key % 16 + 16 ((rho % 32) / 8), slot rho % 8
+        // p % 16 is 0 or 8, so keys p .. p + 7 share a key block and sit
+        // in consecutive lanes of the destination tile: 16 bytes apart
+        const int f = wave + 8 * (i - I_CV), rb = f >> 1, ps = f & 1;
+        const int rho = 16 * rb + j, p = 32 * ps + 8 * grp;
+        const int rs = rho >> 5, hi = (rho & 31) >> 3, slot = rho & 7;
+        uint16_t *dst = cv16 + ((((p >> 4) * RS + rs) * 64 + (p & 15) + 16 * hi) * 8 + slot);
+        const int nvalid = qmax_pos - (k0 + p) + 1;  // keys p + e with e < nvalid are visible
 #pragma unroll
-        for (int xi = 0; xi < NX; ++xi) {
-          acc[xi][0] = mfma_bf16(frag(a.bk, a.r_k, g * DB + xbase + xi, rs, lane), c, acc[xi][0]);
-          acc[xi][1] = mfma_bf16(frag(a.bk, a.r_k, g * DB + xbase + xi + HALF, rs, lane), c, acc[xi][1]);
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t w = st[i][e >> 1];
+          const uint16_t v = e < nvalid ? static_cast<uint16_t>((e & 1) ? (w >> 16) : (w & 0xffffu))
+                                        : static_cast<uint16_t>(0);
+          dst[8 * e] = v;
+        }
+      } else {
+        cs[tid + 512 * i] = st[i];
+      }
+    }
+  };
+
+  const int side = wave >> 2, idx = wave & 3;
+  const int pr = idx % NP, kb0 = (idx / NP) * NKB;
+  f32x4 acc[NKB][2];
+#pragma unroll
+  for (int kk = 0; kk < NKB; ++kk) acc[kk][0] = acc[kk][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  gload(0, 0);
+  for (int s = 0; s < nsteps; ++s) {
+    const int kt = s / nchunk, c = s - kt * nchunk;
+    const int k0 = kt * KT;
+    const bool last = c == nchunk - 1;
+    __syncthreads();
+    swrite(kt);
+    // the next chunk's loads fly under this chunk's products; after a tile's
+    // last chunk they wait for the softmax pass, which needs the registers
+    if (!last) gload(kt, c + 1);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- rebuild products of this chunk ----
+    const int nrs = min(RS, (side == 0 ? rsk : rsv) - c * RS);
+    if (side == 0) {
+      // K^T[d][key] = sum_r B_k^T[d][r] C_k[key][r]
+#pragma unroll 1
+      for (int rs = 0; rs < nrs; ++rs) {
+        {
+          const u32x4 fa = cs[O_BK + (pr * RS + rs) * 64 + lane];
+          const u32x4 fb = cs[O_BK + ((pr + HALF) * RS + rs) * 64 + lane];
+#pragma unroll
+          for (int kk = 0; kk < NKB; ++kk) {
+            const u32x4 cf = cs[((kb0 + kk) * RS + rs) * 64 + lane];
+            acc[kk][0] = mfma_bf16(fa, cf, acc[kk][0]);
+            acc[kk][1] = mfma_bf16(fb, cf, acc[kk][1]);
+          }
         }
       }
-      // lane (key = j, grp) holds K^T[16blk + 4grp + r][keyrow]
+    } else {
+      // V[key][d] = sum_r C_v[key][r] B_v^T[d][r]
+#pragma unroll 1
+      for (int rs = 0; rs < nrs; ++rs) {
+        {
+          const u32x4 f0 = cs[O_BV + ((2 * pr) * RS + rs) * 64 + lane];
+          const u32x4 f1 = cs[O_BV + ((2 * pr + 1) * RS + rs) * 64 + lane];
 #pragma unroll
-      for (int xi = 0; xi < NX; ++xi) {
-        const int blk = xbase + xi;
+          for (int kk = 0; kk < NKB; ++kk) {
+            const u32x4 cf = cs[O_CV + ((kb0 + kk) * RS + rs) * 64 + lane];
+            acc[kk][0] = mfma_bf16(cf, f0, acc[kk][0]);
+            acc[kk][1] = mfma_bf16(cf, f1, acc[kk][1]);
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (!last) continue;
+
+    // ---- K waves: lane (key = j, grp) holds K^T[16 blk + 4 grp + r][16 kb + j]
+    // for blk = pr (acc[.][0]) and its rotary partner pr + HALF (acc[.][1]);
+    // V waves: lane (d = j, grp) holds V[16 kb + 4 grp + r][16 (2 pr + h) + j] ----
+#pragma unroll
+    for (int kk = 0; kk < NKB; ++kk) {
+      const int kb = kb0 + kk;
+      if (side == 0) {
+        const int keyrow = k0 + 16 * kb + j;
         if (rope_on) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            float c, s;
-            rope_cs(keyrow, revs[16 * blk + 4 * grp + r], c, s);
-            const float u = acc[xi][0][r], v = acc[xi][1][r];
-            acc[xi][0][r] = u * c - v * s;
-            acc[xi][1][r] = u * s + v * c;
+            float cc, ss;
+            rope_cs(keyrow, revs[16 * pr + 4 * grp + r], cc, ss);
+            const float u = acc[kk][0][r], v = acc[kk][1][r];
+            acc[kk][0][r] = u * cc - v * ss;
+            acc[kk][1][r] = u * ss + v * cc;
           }
         }
         const int krow = 16 * kb + j;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const int dcol = 16 * (blk + hh * HALF) + 4 * grp;
+          const int dcol = 16 * (pr + hh * HALF) + 4 * grp;
           const int chunk = (dcol >> 3) ^ (krow & (CH - 1));
           *reinterpret_cast<u32x2 *>(&Ks[krow * D + chunk * 8 + (dcol & 7)]) =
-              u32x2{pack2(acc[xi][hh][0], acc[xi][hh][1]), pack2(acc[xi][hh][2], acc[xi][hh][3])};
+              u32x2{pack2(acc[kk][hh][0], acc[kk][hh][1]), pack2(acc[kk][hh][2], acc[kk][hh][3])};
         }
-      }
-    }
-    // ---- rebuild V^T for key block kb, d blocks (wave&1)*HALF .. +HALF ----
-    {
-      f32x4 acc[HALF];
+      } else {
 #pragma unroll
-      for (int x = 0; x < HALF; ++x) acc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int nb0 = (wave & 1) * HALF;
-      // C_v[keyrow][32rs + 8grp + e], e = 0..7, gathered from the value tiles
-      for (int rs = 0; rs < rsv; ++rs) {
-        u32x4 c = {0u, 0u, 0u, 0u};
-        if (kvalid) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            c[q] = static_cast<uint32_t>(cv_b[tile_off(32 * rs + 8 * grp + 2 * q, keyrow, a.L_max)]) |
-                   (static_cast<uint32_t>(cv_b[tile_off(32 * rs + 8 * grp + 2 * q + 1, keyrow, a.L_max)]) << 16);
+        for (int h = 0; h < 2; ++h) {
+          const int dd = 16 * (2 * pr + h) + j;
+          const int unit = (4 * kb + grp) ^ (dd & 15);
+          *reinterpret_cast<u32x2 *>(&Vt[dd * KT + unit * 4]) =
+              u32x2{pack2(acc[kk][h][0], acc[kk][h][1]), pack2(acc[kk][h][2], acc[kk][h][3])};
         }
-#pragma unroll
-        for (int x = 0; x < HALF; ++x) acc[x] = mfma_bf16(c, frag(a.bv, a.r_v, g * DB + nb0 + x, rs, lane), acc[x]);
-      }
-      // lane (d = j, grp) holds V[16kb + 4grp + r][16(nb0+x) + j]
-#pragma unroll
-      for (int x = 0; x < HALF; ++x) {
-        const int dd = 16 * (nb0 + x) + j;
-        const int unit = (4 * kb + grp) ^ (dd & 15);
-        *reinterpret_cast<u32x2 *>(&Vt[dd * KT + unit * 4]) =
-            u32x2{pack2(acc[x][0], acc[x][1]), pack2(acc[x][2], acc[x][3])};
       }
     }
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- attention for this wave's 32 query rows ----
+    // Swizzles depend on the row only through j (rows 16 kk + j, d rows
+    // 16 x + j), so each (t) or (u, half) needs one base and the key block /
+    // d block is a constant offset.
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      f32x4 s[4];
+      f32x4 sc[4];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        s[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int krow = 16 * kk + j;
+      for (int kk = 0; kk < 4; ++kk) sc[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < HALF; ++t) {
-          const int chunk = (4 * t + grp) ^ (krow & (CH - 1));
-          s[kk] = mfma_bf16(*reinterpret_cast<const u32x4 *>(&Ks[krow * D + chunk * 8]), qf[qb][t],
-                            s[kk]);
-        }
+      for (int t = 0; t < HALF; ++t) {
+        const u32x4 qv = Qs[((wave * 2 + qb) * HALF + t) * 64 + lane];
+        const uint16_t *kp = Ks + j * D + (((4 * t + grp) ^ (j & (CH - 1))) * 8);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          sc[kk] = mfma_bf16(*reinterpret_cast<const u32x4 *>(kp + 16 * kk * D), qv, sc[kk]);
       }
       // lane (q = j, grp) holds S^T[k0 + 16kk + 4grp + r][q]
       float mx = -INFINITY;
@@ -215,8 +342,8 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          if (k0 + 16 * kk + 4 * grp + r > qpos[qb]) s[kk][r] = -INFINITY;
-          mx = fmaxf(mx, s[kk][r]);
+          if (k0 + 16 * kk + 4 * grp + r > qpos[qb]) sc[kk][r] = -INFINITY;
+          mx = fmaxf(mx, sc[kk][r]);
         }
       mx = wave_max_xor(mx, 16);
       mx = wave_max_xor(mx, 32);
@@ -227,8 +354,8 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          s[kk][r] = exp2f(s[kk][r] - m_new);
-          psum += s[kk][r];
+          sc[kk][r] = exp2f(sc[kk][r] - m_new);
+          psum += sc[kk][r];
         }
       psum = wave_sum_xor(psum, 16);
       psum = wave_sum_xor(psum, 32);
@@ -238,19 +365,21 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
       for (int x = 0; x < DB; ++x) accO[qb][x] *= alpha;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const u32x4 pf = pack_acc(s[2 * u], s[2 * u + 1]);
+        const u32x4 pf = pack_acc(sc[2 * u], sc[2 * u + 1]);
+        const uint16_t *v0 = Vt + j * KT + (((8 * u + grp) ^ j) * 4);
+        const uint16_t *v1 = Vt + j * KT + (((8 * u + 4 + grp) ^ j) * 4);
 #pragma unroll
         for (int x = 0; x < DB; ++x) {
-          const int dd = 16 * x + j;
-          const int u0 = (4 * (2 * u) + grp) ^ (dd & 15);
-          const int u1 = (4 * (2 * u + 1) + grp) ^ (dd & 15);
-          const u32x2 lo = *reinterpret_cast<const u32x2 *>(&Vt[dd * KT + u0 * 4]);
-          const u32x2 hi = *reinterpret_cast<const u32x2 *>(&Vt[dd * KT + u1 * 4]);
+          const u32x2 lo = *reinterpret_cast<const u32x2 *>(v0 + 16 * x * KT);
+          const u32x2 hi = *reinterpret_cast<const u32x2 *>(v1 + 16 * x * KT);
           accO[qb][x] = mfma_bf16(u32x4{lo.x, lo.y, hi.x, hi.y}, pf, accO[qb][x]);
         }
       }
     }
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < NKB; ++kk) acc[kk][0] = acc[kk][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (s + 1 < nsteps) gload(kt + 1, 0);
   }
 
   // ---- normalise and store: lane (q = j, grp) holds O^T[16x + 4grp + r][q] ----
@@ -276,6 +405,12 @@ hipError_t launch_attn_prefill_bf16(const AttnPrefillArgs &a, hipStream_t s) {
   TraceGuard trace_guard(K_ATTN_PREFILL, s);
   const int G = a.n_q / a.n_kv;
   const int QT = 256 / G;
+  // the kernel addresses one sequence's caches and each factor through
+  // 32-bit buffer offsets
+  const int64_t lim = INT32_MAX;
+  if (static_cast<int64_t>(a.L_max) * std::max(a.r_k, a.r_v) * 2 > lim ||
+      static_cast<int64_t>(a.n_kv) * a.d * std::max(a.r_k, a.r_v) * 2 > lim)
+    return hipErrorInvalidValue;
   dim3 grid((a.T + QT - 1) / QT, a.n_kv, a.Bsz);
   if (a.d == 128)
     attn_prefill_kernel<8><<<grid, 512, 0, s>>>(a);

@@ -100,27 +100,40 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
     for (int y = 0; y < 4; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // One basic block per k tile, so the scheduling groups below can order
+  // it: the next tile's global loads and this tile's operand reads first,
+  // then each A fragment read three fragments ahead of its four MFMAs, and
+  // the next tile's LDS stores among the last MFMAs. The last iteration
+  // reloads its own tile and stores into the idle buffer (never read).
   const int ktiles = K / BK;
   gload(0);
   sstore(0);
   __syncthreads();
   for (int kt = 0; kt < ktiles; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < ktiles) gload(kt + 1);
+    gload(min(kt + 1, ktiles - 1));
     const u32x4 *base = lds + buf * kStage;
+    u32x4 bq[2][4], ar[16];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      u32x4 af[8], bfr[4];
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) bfr[nb] = base[kFrags * 64 + ((wn * 4 + nb) * 2 + ks) * 64 + lane];
+      for (int nb = 0; nb < 4; ++nb) bq[ks][nb] = base[kFrags * 64 + ((wn * 4 + nb) * 2 + ks) * 64 + lane];
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb) af[mb] = base[((wm * 8 + mb) * 2 + ks) * 64 + lane];
+    for (int i = 0; i < 16; ++i) ar[i] = base[((wm * 8 + (i & 7)) * 2 + (i >> 3)) * 64 + lane];
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb)
+    for (int i = 0; i < 16; ++i)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma_bf16(af[mb], bfr[nb], acc[mb][nb]);
+      for (int nb = 0; nb < 4; ++nb) acc[i & 7][nb] = mfma_bf16(ar[i], bq[i >> 3][nb], acc[i & 7][nb]);
+    sstore(buf ^ 1);
+    // groups: 0x008 MFMA, 0x020 VMEM read, 0x100 DS read, 0x200 DS write
+    __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 11, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i + 3 < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      if (i >= 12) __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
     }
-    if (kt + 1 < ktiles) sstore(buf ^ 1);
     __syncthreads();
   }
 
