@@ -369,6 +369,53 @@ def prefill_bench(args, torch, binding, W):
 
 
 # ----------------------------------------------------------------------------
+# Measured peaks (denominators reported beside the published ones)
+# ----------------------------------------------------------------------------
+def measured_peaks(torch, binding):
+    """Rates this GPU sustains: a 1 GiB device-to-device copy ((read + write)
+    bytes per second, best of 5 after a warm-up) and the library's matrix-pipe
+    probe (independent bf16 MFMA chains, best of 3 after a warm-up)."""
+    dev = torch.device("cuda:0")
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best_ms(fn, reps):
+        fn()
+        best = float("inf")
+        for _ in range(reps):
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        return best
+
+    copy_ms = best_ms(lambda: dst.copy_(src), 5)
+    del src, dst
+    blocks, iters = 256 * 8, 4096
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    flops = blocks * 4 * iters * 8 * 16384
+    mfma_ms = best_ms(lambda: binding.probe_mfma_bf16(sink, blocks, iters), 3)
+    return {"hbm_copy_GB_per_s": round(2 * n / (copy_ms * 1e-3) / 1e9, 1),
+            "mfma_bf16_TFLOP_per_s": round(flops / (mfma_ms * 1e-3) / 1e12, 1),
+            "method": "1 GiB device copy, (read + write) bytes / time, best of 5; "
+                      "dl_probe_mfma_bf16 with 2048 workgroups x 4 waves x 4096 rounds of 8 "
+                      "independent 16x16x32 bf16 MFMAs, best of 3"}
+
+
+def with_measured(roof, peaks):
+    """Adds the fraction of the measured peak to a roofline object."""
+    if roof is None or peaks is None:
+        return roof
+    mp = peaks["hbm_copy_GB_per_s"] if roof["unit"] == "GB/s" else peaks["mfma_bf16_TFLOP_per_s"]
+    roof["measured_peak"] = mp
+    roof["frac_of_measured"] = round(roof["achieved"] / mp, 4)
+    return roof
+
+
+# ----------------------------------------------------------------------------
 # CPU oracle baseline
 # ----------------------------------------------------------------------------
 def cpu_baseline(args, W, weights, inp):
@@ -422,11 +469,17 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": n}), flush=True)
         return
     binding.load()
+    peaks = measured_peaks(torch, binding)
+    log(f"measured peaks: {peaks['hbm_copy_GB_per_s']} GB/s copy, "
+        f"{peaks['mfma_bf16_TFLOP_per_s']} TFLOP/s bf16 MFMA")
     dec, weights, inp = decode_bench(args, torch, binding, W)
     log(f"decode: {dec['value']:.0f} tokens/s, {dec['ms_per_step'] * 1e3:.1f} us/step")
     pre = None
     if not args.no_prefill:
         pre = prefill_bench(args, torch, binding, W)
+        pre["mfma_frac_of_measured"] = round(pre["TFLOP_per_s"] / peaks["mfma_bf16_TFLOP_per_s"], 4)
+        if pre["gemm_TFLOP_per_s"]:
+            pre["gemm_frac_of_measured"] = round(pre["gemm_TFLOP_per_s"] / peaks["mfma_bf16_TFLOP_per_s"], 4)
         log(f"prefill: {pre['TFLOP_per_s']} TFLOP/s")
     cpu = None
     if not args.no_cpu_baseline:
@@ -438,7 +491,9 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded; random-init factors, pre-filled low-rank cache)",
         "config": dec["config"], "graph": dec["graph"], "steps_per_graph": dec["steps_per_graph"],
-        "roofline": dec["roofline"], "roofline_attention": dec["roofline_attention"],
+        "roofline": with_measured(dec["roofline"], peaks),
+        "roofline_attention": with_measured(dec["roofline_attention"], peaks),
+        "measured_peaks": peaks,
         "step_hbm_frac": dec["step_hbm_frac"], "kernel_source_hash": kernel_source_hash(),
         "cpu_baseline": cpu, "prefill": pre, "kernels": dec["kernels"],
         "roles_us_per_step": dec["roles_us_per_step"],

@@ -223,6 +223,21 @@ void dl_trace_install(dl_trace *t);
 const char *dl_kernel_kind_name(int32_t kind);
 const char *dl_role_name(int32_t role);
 
+/* ------------------------------------------------------------------------
+ * Matrix-pipe probe (measurement aid; not part of the method).
+ * Launches `blocks` workgroups of four waves; every wave issues `iters`
+ * rounds of eight independent v_mfma_f32_16x16x32_bf16 (16384 flops each),
+ * so the work is blocks * 4 * iters * 8 * 16384 flops with no dependent
+ * issue stalls: timing it gives the bf16 MFMA rate this GPU sustains, the
+ * measured denominator reported next to the published peak.
+ * sink: caller-owned device float[blocks * 256], overwritten (the values
+ * only keep the products live). Asynchronous on `stream`.
+ * Errors: DL_ERR_INVALID_ARG for a null sink or blocks / iters outside
+ * [1, 2^31); DL_ERR_HIP on a launch failure.
+ * ------------------------------------------------------------------------ */
+dl_status dl_probe_mfma_bf16(float *sink, int64_t blocks, int64_t iters,
+                             void *stream);
+
 #ifdef __cplusplus
 }
 #endif

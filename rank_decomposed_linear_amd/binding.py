@@ -36,6 +36,7 @@ EXPORTS = (
     "dl_attn_prefill_workspace", "dl_lowrank_attn_prefill",
     "dl_layer_workspace", "dl_decomposed_layer_fwd",
     "dl_trace_install", "dl_kernel_kind_name", "dl_role_name",
+    "dl_probe_mfma_bf16",
 )
 
 
@@ -105,6 +106,8 @@ def load() -> ctypes.CDLL:
     lib.dl_decomposed_layer_fwd.restype = ctypes.c_int
     lib.dl_decomposed_layer_fwd.argtypes = [ctypes.POINTER(Layer), _vp, _vp, _vp, _vp, _vp, _vp,
                                             _i64, _i64, _i64, _vp, _sz, _vp]
+    lib.dl_probe_mfma_bf16.restype = ctypes.c_int
+    lib.dl_probe_mfma_bf16.argtypes = [_vp, _i64, _i64, _vp]
     lib.dl_trace_install.restype = None
     lib.dl_trace_install.argtypes = [ctypes.POINTER(TraceStruct)]
     lib.dl_kernel_kind_name.restype = ctypes.c_char_p
@@ -201,6 +204,14 @@ def _stream(device) -> int:
 
 def _ws(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def probe_mfma_bf16(sink, blocks, iters):
+    """dl_probe_mfma_bf16 on the current stream of sink's device; returns
+    the flops the launch performs."""
+    assert sink.dtype == torch.float32 and sink.numel() >= blocks * 256
+    _check(load().dl_probe_mfma_bf16(_ptr(sink), blocks, iters, _stream(sink.device)))
+    return blocks * 4 * iters * 8 * 16384
 
 
 def lowrank_linear(x, At, Bt, y=None, ws=None):

@@ -359,6 +359,16 @@ const char *dl_role_name(int32_t role) {
   return (role >= 0 && role < R_NUM_ROLES) ? kRoleNames[role] : "unknown";
 }
 
+dl_status dl_probe_mfma_bf16(float *sink, int64_t blocks, int64_t iters, void *stream) {
+  set_role(R_OTHER);
+  DL_CHECK(sink, DL_ERR_INVALID_ARG, "null sink");
+  DL_CHECK(blocks > 0 && blocks <= INT32_MAX && iters > 0 && iters <= INT32_MAX,
+           DL_ERR_INVALID_ARG, "blocks and iters must lie in [1, 2^31)");
+  DL_HIP(launch_mfma_probe(sink, static_cast<int>(blocks), static_cast<int>(iters),
+                           as_stream(stream)));
+  return DL_OK;
+}
+
 // ===========================================================================
 // dl_lowrank_linear
 // ===========================================================================

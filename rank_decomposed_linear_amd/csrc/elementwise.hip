@@ -42,6 +42,83 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const void *x, int x_f32, 
   }
 }
 
+// Same result for rows of n % 8 == 0 with 16-byte aligned bases: 16-byte
+// accesses, the first kNormCache chunks of 8 per thread kept in registers
+// (one read of x for rows up to 256 * 8 * kNormCache elements).
+constexpr int kNormCache = 8;
+
+__device__ __forceinline__ void load8(const void *p, int f32, size_t i, float v[8]) {
+  if (f32) {
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(static_cast<const float *>(p) + i);
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(static_cast<const float *>(p) + i + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = a[e];
+      v[4 + e] = b[e];
+    }
+  } else {
+    const u32x4 w = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p) + i);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = bflo(w[q]);
+      v[2 * q + 1] = bfhi(w[q]);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void rmsnorm_vec_kernel(const void *x, int x_f32, const void *gamma,
+                                                          int gamma_f32, void *y, int y_f32, int n,
+                                                          float eps) {
+  __shared__ float part[4];
+  const size_t base = static_cast<size_t>(blockIdx.x) * n;
+  const int nc = n >> 3;
+  float v[kNormCache][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < kNormCache; ++k) {
+    const int c = threadIdx.x + 256 * k;
+    if (c < nc) {
+      load8(x, x_f32, base + 8 * c, v[k]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf(v[k][e], v[k][e], ss);
+    }
+  }
+  for (int c = threadIdx.x + 256 * kNormCache; c < nc; c += 256) {
+    float t[8];
+    load8(x, x_f32, base + 8 * c, t);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(t[e], t[e], ss);
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float rstd = 1.0f / sqrtf((part[0] + part[1] + part[2] + part[3]) / n + eps);
+  auto emit = [&](int c, float *t) {
+    float gm[8];
+    if (gamma) load8(gamma, gamma_f32, 8 * static_cast<size_t>(c), gm);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = t[e] * rstd * (gamma ? gm[e] : 1.f);
+    if (y_f32) {
+      float *o = static_cast<float *>(y) + base + 8 * c;
+      *reinterpret_cast<f32x4 *>(o) = f32x4{t[0], t[1], t[2], t[3]};
+      *reinterpret_cast<f32x4 *>(o + 4) = f32x4{t[4], t[5], t[6], t[7]};
+    } else {
+      *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(y) + base + 8 * c) =
+          u32x4{pack2(t[0], t[1]), pack2(t[2], t[3]), pack2(t[4], t[5]), pack2(t[6], t[7])};
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < kNormCache; ++k) {
+    const int c = threadIdx.x + 256 * k;
+    if (c < nc) emit(c, v[k]);
+  }
+  for (int c = threadIdx.x + 256 * kNormCache; c < nc; c += 256) {
+    float t[8];
+    load8(x, x_f32, base + 8 * c, t);
+    emit(c, t);
+  }
+}
+
 struct FillPack {
   FillRegion r[4];
   int nreg;
@@ -190,7 +267,11 @@ int grid_for(int64_t n) {
 hipError_t launch_rmsnorm(const void *x, int x_f32, const void *gamma, int gamma_f32, void *y,
                           int y_f32, int M, int n, float eps, hipStream_t s) {
   TraceGuard trace_guard(K_RMSNORM, s);
-  rmsnorm_kernel<<<M, 256, 0, s>>>(x, x_f32, gamma, gamma_f32, y, y_f32, n, eps);
+  const auto a16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  if (n % 8 == 0 && a16(x) && a16(y) && (!gamma || a16(gamma)))
+    rmsnorm_vec_kernel<<<M, 256, 0, s>>>(x, x_f32, gamma, gamma_f32, y, y_f32, n, eps);
+  else
+    rmsnorm_kernel<<<M, 256, 0, s>>>(x, x_f32, gamma, gamma_f32, y, y_f32, n, eps);
   return hipGetLastError();
 }
 

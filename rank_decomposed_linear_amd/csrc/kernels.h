@@ -221,6 +221,9 @@ hipError_t launch_swiglu_bf16(uint16_t *g, const uint16_t *u, int64_t n, hipStre
 hipError_t launch_norm_tiles(const uint16_t *x, const void *gamma, int gamma_f32, float eps,
                              uint16_t *xt, int M, int Mp, int n, const FillRegion *zero, int nzero,
                              hipStream_t s);
+// Matrix-pipe issue-rate probe (dl_probe_mfma_bf16)
+hipError_t launch_mfma_probe(float *sink, int blocks, int iters, hipStream_t s);
+
 // dst (bf16 or f32) = src f32
 hipError_t launch_convert_f32(const float *src, void *dst, int dst_bf16, int64_t n, hipStream_t s);
 

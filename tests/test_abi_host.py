@@ -138,3 +138,10 @@ def test_layer_validation(lib):
     assert lib.dl_layer_workspace(ctypes.byref(L), 64, 1, 32) > need
     assert lib.dl_layer_workspace(ctypes.byref(_layer(dt=B.DL_F32, rank=5, hidden=20, ffn=30,
                                                       d=10)), 2, 3, 16) > 0
+
+
+def test_probe_rejects_bad_arguments(lib):
+    assert lib.dl_probe_mfma_bf16(None, 1, 1, None) == INVALID
+    assert lib.dl_probe_mfma_bf16(P, 0, 1, None) == INVALID
+    assert lib.dl_probe_mfma_bf16(P, 1, 0, None) == INVALID
+    assert lib.dl_probe_mfma_bf16(P, 1 << 31, 1, None) == INVALID
