@@ -29,7 +29,7 @@ bool g_open = false;
 const char *const kKindNames[K_NUM_KINDS] = {
     "rmsnorm",       "fill",        "convert",      "store_cache_rows",
     "gemv_bf16",     "gemm_bf16",   "gemm_f32",     "pack_up_factor",
-    "attn_decode_bf16", "attn_combine", "attn_prefill_bf16", "attn_f32"};
+    "attn_decode_bf16", "attn_combine", "attn_prefill_bf16", "attn_f32", "swiglu"};
 const char *const kRoleNames[R_NUM_ROLES] = {
     "other",        "attn_norm",    "qkv_down", "kv_store",  "q_up",
     "attention",    "o_down",       "o_up",     "mlp_norm",  "gate_up_down",

@@ -305,7 +305,7 @@ hipError_t launch_norm_tiles(const uint16_t *x, const void *gamma, int gamma_f32
 }
 
 hipError_t launch_swiglu_bf16(uint16_t *g, const uint16_t *u, int64_t n, hipStream_t s) {
-  TraceGuard trace_guard(K_CONVERT, s);
+  TraceGuard trace_guard(K_SWIGLU, s);
   const int64_t n8 = n / 8;
   const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>((n8 + 255) / 256, 8192)));
   swiglu_kernel<<<grid, 256, 0, s>>>(g, u, n8);

@@ -39,6 +39,7 @@ KINDS = (
     ("attn_f32_kernel", "attn_f32"),
     ("pack_up_factor_kernel", "pack_up_factor"),
     ("rmsnorm_kernel", "rmsnorm"),
+    ("rmsnorm_vec_kernel", "rmsnorm"),
     ("norm_tiles_kernel", "rmsnorm"),
     ("fill_kernel", "fill"),
     ("convert_kernel", "convert"),

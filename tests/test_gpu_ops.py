@@ -48,6 +48,7 @@ LINEAR_CASES = [
     (65, 512, 192, 320, "bf16"),
     (300, 256, 128, 448, "bf16"),
     (128, 512, 64, 64, "bf16"),
+    (600, 1024, 320, 1088, "bf16"),     # several 256 x 256 GEMM tiles, ragged in M and N
     (2, 256, 64, 688, "f32"),
     (64, 688, 64, 256, "f32"),
     (100, 70, 9, 33, "f32"),
@@ -186,3 +187,13 @@ def test_explicit_softmax_scale(B):
                                 to_dev(lib_f(Bv)), to_dev(lens), n_kv, 0.3, 1000.0)
     want = ref.attn_decode(f64(q), f64(ck), f64(cv), f64(Bk), f64(Bv), lens, n_kv, 1000.0, 0.3)
     assert relerr(to_host(out), want) <= TOL["bf16"]
+
+
+def test_mfma_probe(B):
+    """The matrix-pipe probe runs, writes every sink entry, and reports its flops."""
+    import torch
+    sink = torch.full((64 * 256,), float("nan"), dtype=torch.float32, device="cuda:0")
+    flops = B.probe_mfma_bf16(sink, 64, 16)
+    torch.cuda.synchronize()
+    assert flops == 64 * 4 * 16 * 8 * 16384
+    assert torch.isfinite(sink).all().item()
