@@ -36,11 +36,6 @@ __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, int voff, int s
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
 }
 
-// operand fragment (rank step rs, d block blk of kv head g) of an up factor
-// stored [n_kv * d, r] in tiles: lane (c, grp) gets B[32rs + 8grp .. +8][16blk + c]
-__device__ __forceinline__ u32x4 frag(const uint16_t *bt, int r, int gblk, int rs, int lane) {
-  return ld16(bt + frag_off(gblk, rs, r, lane));
-}
 
 // ---------------------------------------------------------------------------
 // Prefill
