@@ -29,7 +29,7 @@ bool g_open = false;
 const char *const kKindNames[K_NUM_KINDS] = {
     "rmsnorm",       "fill",        "convert",      "store_cache_rows",
     "gemv_bf16",     "gemm_bf16",   "gemm_f32",     "pack_up_factor",
-    "attn_decode_bf16", "attn_combine", "attn_prefill_bf16", "attn_f32", "swiglu"};
+    "attn_decode_bf16", "attn_combine", "attn_prefill_bf16", "attn_f32"};
 const char *const kRoleNames[R_NUM_ROLES] = {
     "other",        "attn_norm",    "qkv_down", "kv_store",  "q_up",
     "attention",    "o_down",       "o_up",     "mlp_norm",  "gate_up_down",
@@ -721,7 +721,7 @@ struct LayerWS {
   float *part, *q32, *x2f, *ssq;
   uint16_t *att16, *H16, *a16t, *x2g;
   // bf16 large-M (MFMA GEMM) path
-  uint16_t *a16, *b16, *tq16, *q16, *to16, *tg16, *tu16, *G16, *U16, *td16;
+  uint16_t *a16, *b16, *tq16, *q16, *to16, *tg16, *tu16, *G16, *td16;
 };
 
 enum { G_QKV, G_QUP, G_ODOWN, G_OUP, G_GUD, G_GUU, G_DD, G_DU, G_NUM };
@@ -851,7 +851,6 @@ static void carve_layer(Carver &c, const LayerDims &D, const dl_layer *L, LayerW
   w.tg16 = c.take<uint16_t>(M * D.rg);
   w.tu16 = c.take<uint16_t>(M * D.ru);
   w.G16 = c.take<uint16_t>(M * D.f);
-  w.U16 = c.take<uint16_t>(M * D.f);
   w.td16 = c.take<uint16_t>(M * D.rd);
 }
 
@@ -1071,17 +1070,9 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
     set_role(R_GATE_UP_DOWN);
     DL_HIP(gemm(a, s));
   }
-  if (D.rg == D.ru) {
-    GemmArgs a{};
-    a.nseg = 2;
-    a.M = M;
-    a.K = D.rg;
-    a.omode = GEMM_OUT_BF16;
-    a.seg[0] = mseg(L->gate.B, w.tg16, w.G16, D.f, D.rg, D.f);
-    a.seg[1] = mseg(L->up.B, w.tu16, w.U16, D.f, D.ru, D.f);
-    set_role(R_GATE_UP_UP);
-    DL_HIP(gemm(a, s));
-  } else {
+  {
+    // G = t_g B_g, then the up product's epilogue forms H = silu(G) * (t_u B_u)
+    // in place over G
     GemmArgs a{};
     a.nseg = 1;
     a.M = M;
@@ -1091,12 +1082,12 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
     set_role(R_GATE_UP_UP);
     DL_HIP(gemm(a, s));
     a.K = D.ru;
-    a.seg[0] = mseg(L->up.B, w.tu16, w.U16, D.f, D.ru, D.f);
+    a.omode = GEMM_OUT_SWIGLU;
+    a.seg[0] = mseg(L->up.B, w.tu16, w.G16, D.f, D.ru, D.f);
+    a.seg[0].R = w.G16;
+    a.seg[0].ldr = D.f;
     DL_HIP(gemm(a, s));
   }
-  // H = silu(G) * U, in place over G (one streaming pass; recomputing it in
-  // the down GEMM's operand staging would repeat it for every column tile)
-  DL_HIP(launch_swiglu_bf16(w.G16, w.U16, static_cast<int64_t>(M) * D.f, s));
   {
     GemmArgs a{};
     a.nseg = 1;

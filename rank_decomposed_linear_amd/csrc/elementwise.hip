@@ -231,20 +231,6 @@ __global__ __launch_bounds__(256) void norm_tiles_kernel(const uint16_t *x, cons
     store(i, m < M ? *reinterpret_cast<const u32x4 *>(row + 8 * i) : u32x4{0u, 0u, 0u, 0u});
 }
 
-// g[i] = silu(g[i]) * u[i], eight bf16 per thread and step
-__global__ __launch_bounds__(256) void swiglu_kernel(uint16_t *g, const uint16_t *u, int64_t n8) {
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n8; i += stride) {
-    const u32x4 gv = reinterpret_cast<const u32x4 *>(g)[i];
-    const u32x4 uv = reinterpret_cast<const u32x4 *>(u)[i];
-    u32x4 r;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      r[q] = pack2(silu(bflo(gv[q])) * bflo(uv[q]), silu(bfhi(gv[q])) * bfhi(uv[q]));
-    reinterpret_cast<u32x4 *>(g)[i] = r;
-  }
-}
-
 __global__ void convert_kernel(const float *src, void *dst, int dst_bf16, int64_t n) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
@@ -301,14 +287,6 @@ hipError_t launch_norm_tiles(const uint16_t *x, const void *gamma, int gamma_f32
   p.nreg = nzero < 4 ? nzero : 4;
   const int zgrid = p.nreg ? static_cast<int>(std::min<int64_t>((mx + 255) / 256, 64)) : 0;
   norm_tiles_kernel<<<Mp + zgrid, 256, 0, s>>>(x, gamma, gamma_f32, eps, xt, M, Mp, n, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_swiglu_bf16(uint16_t *g, const uint16_t *u, int64_t n, hipStream_t s) {
-  TraceGuard trace_guard(K_SWIGLU, s);
-  const int64_t n8 = n / 8;
-  const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>((n8 + 255) / 256, 8192)));
-  swiglu_kernel<<<grid, 256, 0, s>>>(g, u, n8);
   return hipGetLastError();
 }
 

@@ -184,7 +184,16 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
           continue;
         }
         const size_t o = static_cast<size_t>(m) * sg.ldc + n;
-        if (om == GEMM_OUT_BF16_RES_F32) {
+        if (om == GEMM_OUT_SWIGLU) {
+          // each element of R is read and then overwritten by this thread only
+          const u32x4 gt = *reinterpret_cast<const u32x4 *>(
+              static_cast<const uint16_t *>(sg.R) + static_cast<size_t>(m) * sg.ldr + n);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[2 * e] *= silu(bflo(gt[e]));
+            v[2 * e + 1] *= silu(bfhi(gt[e]));
+          }
+        } else if (om == GEMM_OUT_BF16_RES_F32) {
           const float *rp = static_cast<const float *>(sg.R) + static_cast<size_t>(m) * sg.ldr + n;
           const f32x4 r0 = *reinterpret_cast<const f32x4 *>(rp);
           const f32x4 r1 = *reinterpret_cast<const f32x4 *>(rp + 4);

@@ -88,7 +88,8 @@ enum GemmOut : int {
   GEMM_OUT_BF16_RES_F32 = 1,// C bf16 = acc + R (f32 [M, ldr]); also C32 (f32) if non-null
   GEMM_OUT_F32_RES_BF16 = 2,// C32 f32 = acc + R (bf16 [M, ldr])
   GEMM_OUT_CACHE = 3,       // key cache: row b*T+t -> tiled [L_max, N] of sequence b, row past[b]+t
-  GEMM_OUT_CACHE_T = 4      // value cache: row b*T+t, column n -> tiled [N, L_max], (n, past[b]+t)
+  GEMM_OUT_CACHE_T = 4,     // value cache: row b*T+t, column n -> tiled [N, L_max], (n, past[b]+t)
+  GEMM_OUT_SWIGLU = 5       // C bf16 = silu(R) * acc, R bf16 [M, ldr] (the gate values; C may be R)
 };
 
 struct GemmSeg {
@@ -212,9 +213,6 @@ struct FillRegion {
   int tile_rows = 0, tile_cols = 0;
 };
 hipError_t launch_fill(const FillRegion *r, int nreg, hipStream_t s);
-// SwiGLU of two bf16 arrays, in place: g[i] = silu(g[i]) * u[i] (n % 8 == 0,
-// 16-byte aligned)
-hipError_t launch_swiglu_bf16(uint16_t *g, const uint16_t *u, int64_t n, hipStream_t s);
 // RMSNorm into operand tiles: xt [Mp, n] bf16 tiles, row m < M =
 // x[m] / sqrt(mean(x[m]^2) + eps) * gamma (x bf16 [M, n], gamma [n] or NULL),
 // rows M .. Mp - 1 zero; the same launch zeroes up to four fill regions.

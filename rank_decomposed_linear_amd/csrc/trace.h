@@ -18,7 +18,6 @@ enum KernelKind : int {
   K_ATTN_COMBINE,
   K_ATTN_PREFILL,
   K_ATTN_F32,
-  K_SWIGLU,
   K_NUM_KINDS
 };
 

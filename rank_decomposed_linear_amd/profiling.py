@@ -43,7 +43,6 @@ KINDS = (
     ("norm_tiles_kernel", "rmsnorm"),
     ("fill_kernel", "fill"),
     ("convert_kernel", "convert"),
-    ("swiglu_kernel", "swiglu"),
     ("store_cache_rows_kernel", "store_cache_rows"),
 )
 
