@@ -144,9 +144,9 @@ def test_small_layer_row_tiles(B, monkeypatch, case, R):
 
 @pytest.mark.parametrize("case", [SMALL[2], SMALL[1]], ids=[SMALL[2][0], SMALL[1][0]])
 def test_small_layer_unequal_mlp_ranks(B, case):
-    """Gate and up factors of different rank: the prefill MLP cannot pair them
-    in one launch and applies SwiGLU while staging the down GEMM's operand;
-    the decode GEMV pairs them with different K halves."""
+    """Gate and up factors of different rank: the prefill up GEMM (its own K)
+    applies SwiGLU in its epilogue over the gate output; the decode GEMV pairs
+    them with different K halves."""
     test_small_layer(B, case, rank_up=case[9] - 64)
 
 
