@@ -11,7 +11,11 @@
 // factors already live in that order in HBM (Wt [N, K] in 16 x 32 tiles): a
 // weight tile's k step is 32 contiguous 1 KB fragments. Activation rows are
 // row-major: lane l of a staging load fetches row (l % 16), k columns
-// 8 (l / 16) .. +7 of its fragment. LDS double-buffered, 128 KB.
+// 8 (l / 16) .. +7 of its fragment. Staging is direct to LDS
+// (global_load_lds_dwordx4: lane l of a wave lands at byte 16 l of the
+// wave's 1 KB destination), so no registers or LDS store instructions carry
+// it. Two separately declared 64 KB stage buffers (the compiler then sees
+// that the loads into one do not alias the operand reads from the other).
 //
 // Work order: the hardware deals workgroups to the eight XCDs round-robin;
 // the linear index is remapped so each XCD runs a contiguous range of tiles,
@@ -31,6 +35,7 @@ constexpr int kStage = 2 * kFrags * 64;        // u32x4 per stage (A then B)
 constexpr int kXcds = 8;
 constexpr int kGroupM = 4;
 constexpr int kEpPitch = 256 + 4;  // f32 row pitch of the epilogue's LDS rows
+constexpr int kEpRows = 32;        // rows per epilogue pass (one stage buffer)
 
 __device__ __forceinline__ void tile_of(int bid, int total, int tiles_m, int tiles_n, int &tm,
                                         int &tn) {
@@ -46,7 +51,8 @@ __device__ __forceinline__ void tile_of(int bid, int total, int tiles_m, int til
 }
 
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
-  __shared__ u32x4 lds[2 * kStage];
+  __shared__ u32x4 stage0[kStage];
+  __shared__ u32x4 stage1[kStage];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
@@ -77,22 +83,21 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
     wp[i] = sg.W + frag_off(nb, ks, K, lane);
   }
 
-  u32x4 st[8];
-  auto gload = [&](int kt) {
+  // direct-to-LDS staging of k tile kt into `dst`: unit i of this wave fills
+  // the 1 KB fragment wave + 8 i of each operand
+  typedef const void __attribute__((address_space(1))) *gptr;
+  typedef void __attribute__((address_space(3))) *lptr;
+  auto dma = [&](u32x4 *dst, int kt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      st[i] = *reinterpret_cast<const u32x4 *>(xp[i] + kt * BK);
-      st[4 + i] = *reinterpret_cast<const u32x4 *>(wp[i] + static_cast<size_t>(kt) * 2 * 512);
+      __builtin_amdgcn_global_load_lds((gptr)(xp[i] + kt * BK),
+                                       (lptr)(dst + (wave + 8 * i) * 64), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gptr)(wp[i] + static_cast<size_t>(kt) * 2 * 512),
+                                       (lptr)(dst + kFrags * 64 + (wave + 8 * i) * 64), 16, 0,
+                                       0);
     }
   };
-  auto sstore = [&](int buf) {
-    u32x4 *base = lds + buf * kStage;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      base[(wave + 8 * i) * 64 + lane] = st[i];
-      base[kFrags * 64 + (wave + 8 * i) * 64 + lane] = st[4 + i];
-    }
-  };
+  auto dma_wait = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
   f32x4 acc[8][4];
 #pragma unroll
@@ -101,18 +106,14 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
     for (int y = 0; y < 4; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // One basic block per k tile, so the scheduling groups below can order
-  // it: the next tile's global loads and this tile's operand reads first,
-  // then each A fragment read three fragments ahead of its four MFMAs, and
-  // the next tile's LDS stores among the last MFMAs. The last iteration
-  // reloads its own tile and stores into the idle buffer (never read).
+  // it: the next tile's loads into the other buffer and this tile's B
+  // fragments first, then each A fragment read three fragments ahead of its
+  // four MFMAs; the tile ends with this wave's loads landed and a barrier.
+  // The last iteration reloads its own tile into the idle buffer (never
+  // read). The loop is unrolled by two so each half's buffers are static.
   const int ktiles = K / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < ktiles; ++kt) {
-    const int buf = kt & 1;
-    gload(min(kt + 1, ktiles - 1));
-    const u32x4 *base = lds + buf * kStage;
+  auto ktile = [&](const u32x4 *base, u32x4 *next, int kt) {
+    dma(next, min(kt + 1, ktiles - 1));
     u32x4 bq[2][4], ar[16];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -124,20 +125,26 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
     for (int i = 0; i < 16; ++i)
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) acc[i & 7][nb] = mfma_bf16(ar[i], bq[i >> 3][nb], acc[i & 7][nb]);
-    sstore(buf ^ 1);
-    // groups: 0x008 MFMA, 0x020 VMEM read, 0x100 DS read, 0x200 DS write
+    // groups: 0x008 MFMA, 0x020 VMEM read, 0x100 DS read
     __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 11, 0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if (i + 3 < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      if (i >= 12) __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
     }
+    dma_wait();
     __syncthreads();
+  };
+  dma(stage0, 0);
+  dma_wait();
+  __syncthreads();
+  for (int kt = 0; kt < ktiles; kt += 2) {
+    ktile(stage0, stage1, kt);
+    if (kt + 1 < ktiles) ktile(stage1, stage0, kt + 1);
   }
 
-  // Epilogue, in four passes of 64 rows: the waves owning the pass's rows
+  // Epilogue, in eight passes of 32 rows: the waves owning the pass's rows
   // park their f32 accumulators in LDS (row pitch kEpPitch, so the 16-lane
   // column groups of an accumulator row land in distinct banks), then every
   // thread takes 8 consecutive columns of a row and applies the segment's
@@ -145,27 +152,26 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   // C[128 wm + 16 mb + 4 grp + r][64 wn + 16 nb + j].
   const int j = lane & 15, grp = lane >> 4;
   const int om = sg.omode;
-  float *ep = reinterpret_cast<float *>(lds);
+  float *ep = reinterpret_cast<float *>(stage0);
   const int c8 = 8 * (tid & 31);
   const int n = n0 + c8;
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    if (wm == (p >> 1)) {
+  for (int p = 0; p < BM / kEpRows; ++p) {
+    if (wm == (p >> 2)) {
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mh = 0; mh < 2; ++mh)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            ep[(mb * 16 + 4 * grp + r) * kEpPitch + wn * 64 + nb * 16 + j] =
-                acc[4 * (p & 1) + mb][nb][r];
+            ep[(mh * 16 + 4 * grp + r) * kEpPitch + wn * 64 + nb * 16 + j] = acc[2 * (p & 3) + mh][nb][r];
     }
     __syncthreads();
     if (n < sg.N) {
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
+      for (int it = 0; it < kEpRows / 16; ++it) {
         const int rr = (tid >> 5) + 16 * it;
-        const int m = m0 + 64 * p + rr;
+        const int m = m0 + kEpRows * p + rr;
         if (m >= a.M) continue;
         const f32x4 lo = *reinterpret_cast<const f32x4 *>(ep + rr * kEpPitch + c8);
         const f32x4 hi = *reinterpret_cast<const f32x4 *>(ep + rr * kEpPitch + c8 + 4);
