@@ -18,8 +18,9 @@
 //  * The B_k^T tiles of head g are copied once into LDS, fragment (rank
 //    step rs, d block x) = dimensions 16x .. 16x+15. The rotary partner of
 //    dimension 16x + i is 16(x + d/32) + i: same lane, same register of the
-//    rebuilt keys. (Ranks too large for LDS are staged in rank chunks,
-//    reloaded per context slice.)
+//    rebuilt keys. (For ranks too large for LDS, the leading rank steps
+//    stay resident and the rest are restaged per position group through a
+//    two-step tail area.)
 //  * LDS is sized per launch: the resident factor first, then as long a
 //    context chunk as the rest of the 160 KB holds (scores and
 //    probabilities need 4 G + 32 bytes per position), so a split is
@@ -137,22 +138,26 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
   const int p_end = min(p_begin + a.split_len, ctx);
   const bool rope_on = a.theta != 0.f;
   const int nrs = a.r_k / 32;
-  const int rs_cap = a.rs_cap;
-  const int n_rchunks = (nrs + rs_cap - 1) / rs_cap;
+  // rank steps [0, rs_cap) of the key factor stay in LDS for the whole work
+  // item; the rest (ranks too large for LDS) are restaged per group in
+  // chunks of rs_tail steps into the area after them
+  const int rs_cap = a.rs_cap, rs_tail = a.rs_tail;
+  const int n_tail = rs_tail > 0 ? (nrs - rs_cap + rs_tail - 1) / rs_tail : 0;
   const int nrb = a.r_v / 16;
   const int pitch = a.pitch;   // positions per chunk, a multiple of the slice
   const uint16_t *cv_b = a.cv + static_cast<size_t>(b) * a.r_v * a.L_max;
   const uint16_t *ck_b = a.ck + static_cast<size_t>(b) * a.L_max * a.r_k;
 
-  // up-factor fragments of rank steps [rs0, rs0 + cnt) -> bs[rs - rs0][x][lane][8]
+  // up-factor fragments of rank steps [rs0, rs0 + cnt) -> dst[rs - rs0][x][lane][8]
+  uint16_t *bs_tail = bs + static_cast<size_t>(rs_cap) * NB * 64 * 8;
   auto factor_src = [&](int rs0, int u) {
     const int ln = u & 63, x = (u >> 6) % NB, rs = (u >> 6) / NB;
     return a.bk + frag_off(g * NB + x, rs0 + rs, a.r_k, ln);
   };
-  auto load_factor = [&](int rs0, int cnt) {
+  auto load_factor = [&](uint16_t *dst, int rs0, int cnt) {
     const int units = cnt * NB * 64;
     for (int u = tid; u < units; u += kThreads)
-      *reinterpret_cast<u32x4 *>(bs + static_cast<size_t>(u) * 8) = ld16(factor_src(rs0, u));
+      *reinterpret_cast<u32x4 *>(dst + static_cast<size_t>(u) * 8) = ld16(factor_src(rs0, u));
   };
 
   // Prologue, ordered so the latencies overlap: this thread's query values
@@ -183,7 +188,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
   // resident factor: batches of kPer loads per thread in flight before their
   // LDS stores; the first batch is issued here
   constexpr int kPer = 32;
-  const int funits = n_rchunks == 1 ? nrs * NB * 64 : 0;
+  const int funits = rs_cap * NB * 64;
   u32x4 fv[kPer];
   auto factor_batch_load = [&](int u0) {
 #pragma unroll
@@ -263,18 +268,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
       for (int pb = 0; pb < kNP; ++pb)
         crow[pb] = static_cast<int>(frag_off((c0 >> 4) + min(b_lo + kNP * gi + pb, max(b_hi - 1, 0)), 0, a.r_k, lane));
     };
-    const bool resident = n_rchunks == 1;   // else staged per rank chunk
     for (int gi = 0; gi < ngr; ++gi) {
       const int g0 = b_lo + kNP * gi;
       const int np = max(0, min(kNP, b_hi - g0));   // blocks of this group; a partial group is the wave's last
       if (np == 0) {
-        // no blocks: still take part in the workgroup's factor staging
-        if (!resident) {
-          for (int rc = 0; rc < n_rchunks; ++rc) {
-            __syncthreads();
-            load_factor(rc * rs_cap, min(rs_cap, nrs - rc * rs_cap));
-            __syncthreads();
-          }
+        // no blocks: still take part in the workgroup's tail staging
+        for (int tc = 0; tc < n_tail; ++tc) {
+          const int rs0 = rs_cap + tc * rs_tail;
+          __syncthreads();
+          load_factor(bs_tail, rs0, min(rs_tail, nrs - rs0));
+          __syncthreads();
         }
         continue;
       }
@@ -288,11 +291,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
         for (int x = 0; x < NB; ++x)
 #pragma unroll
           for (int pb = 0; pb < NPA; ++pb) acc[x][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int rc = 0; rc < n_rchunks; ++rc) {
-          const int rs0 = rc * rs_cap, cnt = min(rs_cap, nrs - rs0);
-          if (!resident) {
+        for (int rc = 0; rc <= n_tail; ++rc) {
+          // chunk 0: the resident steps; chunk rc > 0: tail chunk rc - 1
+          const int rs0 = rc == 0 ? 0 : rs_cap + (rc - 1) * rs_tail;
+          const int cnt = rc == 0 ? rs_cap : min(rs_tail, nrs - rs0);
+          const uint16_t *fb = rc == 0 ? bs : bs_tail;
+          if (rc > 0) {
             __syncthreads();
-            load_factor(rs0, cnt);
+            load_factor(bs_tail, rs0, cnt);
             __syncthreads();
           }
           // cache tiles kCDepth rank steps ahead; prefetches past the last
@@ -307,7 +313,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
           u32x4 bop[2][NB];
 #pragma unroll
           for (int x = 0; x < NB; ++x)
-            bop[0][x] = *reinterpret_cast<const u32x4 *>(bs + (static_cast<size_t>(x) * 64 + lane) * 8);
+            bop[0][x] = *reinterpret_cast<const u32x4 *>(fb + (static_cast<size_t>(x) * 64 + lane) * 8);
           // One rank step: next step's factor fragments from LDS, the
           // products of this step (position block by position block, so
           // each cache tile is free for its refill after NB products), the
@@ -316,7 +322,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
           // products instead of issued in runs.
           auto rank_step = [&](auto dc, int s) {
             constexpr int d = decltype(dc)::value;
-            const uint16_t *fr = bs + (static_cast<size_t>(min(s + 1, cnt - 1) * NB) * 64 + lane) * 8;
+            const uint16_t *fr = fb + (static_cast<size_t>(min(s + 1, cnt - 1) * NB) * 64 + lane) * 8;
 #pragma unroll
             for (int x = 0; x < NB; ++x) bop[(d + 1) & 1][x] = *reinterpret_cast<const u32x4 *>(fr + x * 64 * 8);
 #pragma unroll
@@ -599,30 +605,34 @@ int lds_per_block() {
 }
 
 // Dynamic LDS plan: the resident factor (else the largest even number of
-// rank steps that leaves a 512-position chunk), then the longest chunk the
-// rest holds, at most the split length. Returns the dynamic bytes, 0 if the
-// shape does not fit.
+// rank steps that leaves a 256-position chunk and a 2-step tail area, the
+// remaining steps being restaged per group), then the longest chunk the rest
+// holds, at most the split length. Returns the dynamic bytes, 0 if the shape
+// does not fit.
 int plan_lds(AttnDecodeArgs &a, int dyn, int nb) {
   const int G = a.n_q / a.n_kv;
   const int step_bytes = nb * 1024;
   const int nrs = a.r_k / 32;
   const int per_pos = 4 * G + 32;
   const int want = min(kMaxPitch, (a.split_len + kSlice - 1) / kSlice * kSlice);
-  int rs_cap = nrs;
+  int rs_cap = nrs, rs_tail = 0;
   int pitch = ((dyn - nrs * step_bytes) / per_pos) & ~(kSlice - 1);
   if (pitch < kSlice) {
-    pitch = min(want, 512);
-    rs_cap = ((dyn - pitch * per_pos) / step_bytes) & ~1;
+    rs_tail = 2;
+    pitch = min(want, 256);
+    rs_cap = ((dyn - pitch * per_pos - rs_tail * step_bytes) / step_bytes) & ~1;
     if (rs_cap < 2) {
       rs_cap = 2;
-      pitch = ((dyn - 2 * step_bytes) / per_pos) & ~(kSlice - 1);
+      pitch = ((dyn - (rs_cap + rs_tail) * step_bytes) / per_pos) & ~(kSlice - 1);
     }
+    rs_cap = min(rs_cap, nrs);
   }
   pitch = min(pitch, want);
   if (pitch < kSlice || rs_cap < 2 || 64 * a.r_v > dyn) return 0;
   a.rs_cap = rs_cap;
+  a.rs_tail = rs_tail;
   a.pitch = pitch;
-  a.lds_bs = rs_cap * step_bytes;
+  a.lds_bs = (rs_cap + rs_tail) * step_bytes;
   a.lds_s = (G * pitch * 4 + 15) / 16 * 16;
   return dyn;
 }

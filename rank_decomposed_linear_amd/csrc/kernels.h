@@ -135,7 +135,8 @@ struct AttnDecodeArgs {
   int ctx_offset;      // context of sequence b = ctx_lens[b] + ctx_offset
   int nsplit, split_len;  // context positions per split (multiple of attn_decode_split_granule())
   // set by the launcher (LDS plan)
-  int rs_cap, pitch, lds_bs, lds_s;
+  int rs_cap, rs_tail;    // rank steps resident for the whole item; steps per restaged tail chunk (0: none)
+  int pitch, lds_bs, lds_s;
   float scale_log2;    // sm_scale * log2(e)
   float theta;
   int q_f32, out_f32, out_tiled;
