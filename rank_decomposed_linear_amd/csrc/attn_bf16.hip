@@ -79,8 +79,20 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
   const int G = a.n_q / a.n_kv;
   const int QT = 256 / G;
   const int nqt = (a.T + QT - 1) / QT;
-  const int qt = nqt - 1 - static_cast<int>(blockIdx.x);
-  const int g = blockIdx.y, b = blockIdx.z;
+  // Work order: the hardware deals workgroups to the eight XCDs round-robin
+  // in linear order; the index is remapped so each XCD runs all query tiles
+  // of a few (sequence, kv head) pairs, sharing their latents and factor
+  // slices in its L2, heaviest (latest) query tiles first.
+  int qt, g, b;
+  {
+    const int total = static_cast<int>(gridDim.x * gridDim.y * gridDim.z);
+    const int L = static_cast<int>(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+    const int xcd = L & 7, local = L >> 3, q = total >> 3, rem = total & 7;
+    const int Lg = xcd < rem ? xcd * (q + 1) + local : rem * (q + 1) + (xcd - rem) * q + local;
+    qt = nqt - 1 - Lg % nqt;
+    g = (Lg / nqt) % a.n_kv;
+    b = Lg / nqt / a.n_kv;
+  }
   const int t0 = qt * QT;
   const int past = a.past_lens[b];
   const bool rope_on = a.theta != 0.f;
