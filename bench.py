@@ -448,7 +448,7 @@ def cpu_baseline(args, W, weights, inp):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
               f"(requested --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
     import torch

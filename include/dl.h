@@ -70,7 +70,7 @@ extern "C" {
 typedef enum {
   DL_OK = 0,
   DL_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, n_q % n_kv != 0, bad dtype */
-  DL_ERR_UNSUPPORTED = 2,  /* a shape this build does not implement (see each call) */
+  DL_ERR_UNSUPPORTED = 2,  /* a shape the library does not implement (see each call) */
   DL_ERR_ALIGNMENT = 3,    /* a tensor pointer is not 16-byte aligned */
   DL_ERR_WORKSPACE = 4,    /* ws is NULL or ws_bytes is below the required size */
   DL_ERR_HIP = 5           /* a HIP launch failed; dl_last_error() has the text */
