@@ -8,6 +8,11 @@ that bench.py reports in its roofline object.
       per-kernel dispatch count and duration statistics of a
       `rocprofv3 --kernel-trace --stats` run
 
+  python -m rank_decomposed_linear_amd.profiling mfma --pmc DB --trace DB --measured TFLOPS
+      --command CMD
+      executed bf16 MFMA flops per kernel (`rocprofv3 --pmc
+      SQ_INSTS_VALU_MFMA_MOPS_BF16`) over the kernel-trace durations
+
   python -m rank_decomposed_linear_amd.profiling traffic --fetch DB --write DB
       --cal-fetch DB --cal-write DB --copy-bytes N --workload NAME
       --command CMD [--json OUT]
@@ -116,6 +121,48 @@ def _copy_kib(db: str, counter: str) -> float:
     return max(vals)
 
 
+def mfma_table(pmc_db: str, trace_db: str, command: str, peak_tflops: float,
+               measured_tflops: float) -> str:
+    """Executed bf16 MFMA work per kernel from a `rocprofv3 --pmc
+    SQ_INSTS_VALU_MFMA_MOPS_BF16` run (the counter counts operations / 512),
+    over the average duration of the same kernel and grid in a kernel-trace
+    run: the counter-measured matrix-pipe rate."""
+    c = _db(pmc_db)
+    per = collections.OrderedDict()
+    rows = c.execute("select dispatch_id, kernel_name, grid_size_x, grid_size_y, grid_size_z, "
+                     "workgroup_size_x, value from counters_collection where counter_name = ? "
+                     "order by dispatch_id", ("SQ_INSTS_VALU_MFMA_MOPS_BF16",)).fetchall()
+    disp = collections.OrderedDict()
+    for did, name, gx, gy, gz, wx, v in rows:
+        key = (short_name(name), gx // max(wx, 1), gy, gz)
+        disp.setdefault(did, [key, 0.0])[1] += v * 512.0
+    for key, flops in disp.values():
+        per.setdefault(key, []).append(flops)
+    t = _db(trace_db)
+    dur = collections.defaultdict(list)
+    for name, gx, gy, gz, wx, d in t.execute("select name, grid_x, grid_y, grid_z, workgroup_x, duration "
+                                             "from kernels").fetchall():
+        dur[(short_name(name), gx // max(wx, 1), gy, gz)].append(d * 1e-9)
+    out = [f"# bf16 MFMA work from counters: {command}",
+           f"# rate = counter flops per launch / average duration of the same kernel and grid in the kernel trace;",
+           f"# fractions of the published {peak_tflops:.0f} TFLOP/s and of the measured 16x16x32 rate "
+           f"{measured_tflops:.0f} TFLOP/s",
+           "# kernel (workgroups x, y, z): launches, TFLOP per launch, average us, TFLOP/s, published, measured",
+           ""]
+    for (nm, wgx, gy, gz), fl in per.items():
+        f = sum(fl) / len(fl)
+        if f <= 0 or not any(frag in nm for frag, _ in KINDS):
+            continue
+        d = dur.get((nm, wgx, gy, gz))
+        if not d:
+            continue
+        avg = sum(d) / len(d)
+        rate = f / avg / 1e12
+        out.append(f"{nm:40s} ({wgx}, {gy}, {gz})  n={len(fl):3d}  {f / 1e12:8.4f} TF  {avg * 1e6:9.2f} us  "
+                   f"{rate:8.1f} TFLOP/s  {rate / peak_tflops:6.1%}  {rate / measured_tflops:6.1%}")
+    return "\n".join(out) + "\n"
+
+
 def traffic(fetch_db, write_db, cal_fetch_db, cal_write_db, copy_bytes, workload, command):
     fscale = copy_bytes / (_copy_kib(cal_fetch_db, "FETCH_SIZE") * 1024.0)
     wscale = copy_bytes / (_copy_kib(cal_write_db, "WRITE_SIZE") * 1024.0)
@@ -151,9 +198,17 @@ def main(argv=None):
         t.add_argument(a, required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--json")
+    m = sub.add_parser("mfma")
+    for x in ("--pmc", "--trace", "--command"):
+        m.add_argument(x, required=True)
+    m.add_argument("--peak", type=float, default=2500.0)
+    m.add_argument("--measured", type=float, required=True)
     a = p.parse_args(argv)
     if a.cmd == "kernels":
         sys.stdout.write(kernel_table(a.db, a.command))
+        return
+    if a.cmd == "mfma":
+        sys.stdout.write(mfma_table(a.pmc, a.trace, a.command, a.peak, a.measured))
         return
     r = traffic(a.fetch, a.write, a.cal_fetch, a.cal_write, a.copy_bytes, a.workload, a.command)
     if a.json:
