@@ -122,10 +122,14 @@ def _hip_runtime() -> ctypes.CDLL:
     """The HIP runtime already loaded by torch (same soname as libdlayer's)."""
     hip = ctypes.CDLL("libamdhip64.so.7")
     hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
     hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
     hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                         ctypes.c_void_p]
     return hip
+
+
+_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence
 
 
 class KernelTrace:
@@ -140,8 +144,11 @@ class KernelTrace:
         self.events = (ctypes.c_void_p * (2 * capacity))()
         for i in range(2 * capacity):
             ev = ctypes.c_void_p()
-            if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
-                raise RuntimeError("hipEventCreate failed")
+            # timing-only events: no system-scope fence (cache writeback and
+            # invalidate) at each record, which would also slow the next kernel;
+            # records() is read after a device synchronisation
+            if self.hip.hipEventCreateWithFlags(ctypes.byref(ev), _EVENT_DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
             self.events[i] = ev.value
         self.kinds = (ctypes.c_int32 * capacity)()
         self.roles = (ctypes.c_int32 * capacity)()
