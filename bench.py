@@ -1,13 +1,16 @@
 #!/usr/bin/env python3
 """Throughput of one SVD-decomposed transformer layer on one MI355X.
 
-Headline: decode tokens/s of a LLaMA-3-8B-shaped decomposed layer at 40%
-compression (batch 16, 1024 cached tokens, one new token per sequence per
-step), every projection a factor pair (W ~ A B) and attention rebuilding K/V
-from the low-rank cache. The same JSON line carries the prefill figure of a
-LLaMA-3-70B-shaped layer at 50% (8 sequences x 2048 tokens, TFLOP/s), the
-roofline of the dominant decode kernel, a per-kernel breakdown, and the fp64
-CPU oracle timed on a bounded sample of the decode workload.
+Headline: decode tokens/s of a LLaMA-3-70B-shaped decomposed layer at 50%
+compression (batch 32, 8192 cached tokens, one new token per sequence per
+step) -- the largest decode configuration that fits one GPU -- with every
+projection a factor pair (W ~ A B) and attention rebuilding K/V from the
+low-rank cache. The same JSON line carries extra decode legs (the
+LLaMA-3-8B-shaped layer at 40%, batch 16 x 1024, and its 20-60% compression
+sweep at batch 64 x 4096), the prefill figure of the 70B-shaped layer
+(8 sequences x 2048 tokens, TFLOP/s), the roofline of the dominant decode
+kernel, a per-kernel breakdown, and the fp64 CPU oracle timed on bounded
+samples of the decode and prefill workloads.
 
 A "step" is one dl_decomposed_layer_fwd call over the whole batch. Inputs
 are seeded synthetic data resident in HBM before timing starts; two
@@ -56,10 +59,16 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="llama3_8b_c40_decode_b16_l1024")
+    p.add_argument("--workload", default="llama3_70b_c50_decode_b32_l8192")
+    p.add_argument("--legs", default="llama3_8b_c40_decode_b16_l1024,"
+                   + ",".join(f"llama3_8b_c{c}_decode_b64_l4096" for c in (20, 30, 40, 50, 60)),
+                   help="comma-separated extra decode workloads (empty: none)")
+    p.add_argument("--leg-steps", type=int, default=30)
+    p.add_argument("--leg-warmup", type=int, default=5)
+    p.add_argument("--leg-trace-steps", type=int, default=4)
     p.add_argument("--prefill-workload", default="llama3_70b_c50_prefill_8x2048")
     p.add_argument("--prefill-steps", type=int, default=4)
-    p.add_argument("--trace-steps", type=int, default=20)
+    p.add_argument("--trace-steps", type=int, default=10)
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -81,8 +90,16 @@ def log(msg):
 def decode_role_work(shape, M, ctx_total):
     """Per-step algorithmic bytes of each GEMV launch (bf16 weights read once,
     activations in and out at the dtype the layer passes between launches)
-    and of the attention kernel, plus attention flops. ctx_total = sum over
-    sequences of the rows attended."""
+    and of the attention kernel, plus attention flops, counted two ways:
+
+    own   -- the kernel's association: keys rebuilt per attended position
+             (2 r_k n_kv d), scores (2 d per query head), probabilities
+             applied to the value latents (2 r_v per query head), then the
+             value factor once per query head (2 r_v d);
+    pages -- the pages' explicit rebuild of K and V per position
+             (2 (r_k + r_v) n_kv d) plus scores and P V (4 n_q d).
+
+    ctx_total = sum over sequences of the rows attended."""
     h, f, qd, kvd = shape.hidden, shape.ffn, shape.n_q * shape.head_dim, shape.n_kv * shape.head_dim
     r = {p: shape.rank(p) for p in ("q", "k", "v", "o", "gate", "up", "down")}
     b16, f32 = 2, 4
@@ -98,8 +115,10 @@ def decode_role_work(shape, M, ctx_total):
         "down_up": b16 * r["down"] * h + M * r["down"] * b16 + M * h * f32 + M * h * b16,
     }
     attn_bytes = ctx_total * (r["k"] + r["v"]) * b16 + b16 * kvd * (r["k"] + r["v"]) + M * qd * (f32 + b16)
-    attn_flops = ctx_total * (2 * (r["k"] + r["v"]) * kvd + 4 * qd)
-    return gemv, attn_bytes, attn_flops
+    attn_flops_own = (ctx_total * (2 * r["k"] * kvd + shape.n_q * (2 * shape.head_dim + 2 * r["v"]))
+                      + M * shape.n_q * 2 * r["v"] * shape.head_dim)
+    attn_flops_pages = ctx_total * (2 * (r["k"] + r["v"]) * kvd + 4 * qd)
+    return gemv, attn_bytes, attn_flops_own, attn_flops_pages
 
 
 def prefill_flops(shape, Bsz, T):
@@ -234,16 +253,18 @@ def measured_traffic(kernel, workload):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
-def decode_bench(args, torch, binding, W):
-    w = W.by_name(args.workload)
+def decode_bench(args, torch, binding, W, name, steps, warmup, trace_steps, nsets):
+    """Times `steps` decode steps of workload `name` (after `warmup`) and
+    traces `trace_steps` more for the per-kernel breakdown and rooflines."""
+    w = W.by_name(name)
     log(f"decode workload {w.name}: drawing inputs")
     weights, inp = W.draw(w)
-    sets = make_sets(torch, binding, weights, inp, args.sets)
+    sets = make_sets(torch, binding, weights, inp, nsets)
     Bsz = w.batch
     # eager reference output of set 0, then (optionally) graphs
     run_step(sets[0])
     torch.cuda.synchronize()
-    y_eager = sets[0]["y"].float().clone()
+    y_eager = sets[0]["y"].clone()
     use_graph = not args.no_graph
     graphs = None
     chain_steps = max(1, args.graph_steps)
@@ -254,39 +275,39 @@ def decode_bench(args, torch, binding, W):
                 sets[0]["y"].zero_()
                 g.replay()
                 torch.cuda.synchronize()
-                err = (sets[0]["y"].float() - y_eager).abs().max().item()
-                if not err <= 1e-2 * y_eager.abs().max().item():
-                    raise RuntimeError(f"graph replay differs from eager output by {err}")
+                if not torch.equal(sets[0]["y"], y_eager):
+                    raise RuntimeError("graph replay differs from the eager output")
         except Exception as e:  # keep the eager figure if capture is refused
             log(f"graph capture disabled: {e}")
             use_graph, graphs = False, None
-    log(f"timing {args.steps} steps after {args.warmup} warmup (graph={use_graph})")
+    log(f"timing {steps} steps after {warmup} warmup (graph={use_graph})")
     if graphs:
-        fn, calls = step_fn(graphs, chain, chain_steps, args.steps)
-        wfn, wcalls = step_fn(graphs, chain, chain_steps, args.warmup)
+        fn, calls = step_fn(graphs, chain, chain_steps, steps)
+        wfn, wcalls = step_fn(graphs, chain, chain_steps, warmup)
         for i in range(wcalls):
             wfn(i)
         ms, wall = timed(torch, fn, calls, 0)
-        ms *= calls / args.steps
+        ms *= calls / steps
     else:
         fn = lambda i: run_step(sets[i % len(sets)])
-        ms, wall = timed(torch, fn, args.steps, args.warmup)
+        ms, wall = timed(torch, fn, steps, warmup)
 
-    per = trace_breakdown(torch, binding, sets, args.trace_steps)
+    per = trace_breakdown(torch, binding, sets, trace_steps)
     ctx_total = int(sum(int(p) + 1 for p in inp.past_lens))
-    gemv_bytes, attn_bytes, attn_flops = decode_role_work(w.shape, Bsz, ctx_total)
-    n = args.trace_steps
+    gemv_bytes, attn_bytes, attn_own, attn_pages = decode_role_work(w.shape, Bsz, ctx_total)
+    n = trace_steps
     kinds = {}
     for (kind, role), lst in per.items():
         k = kinds.setdefault(kind, {"ms_per_step": 0.0, "launches_per_step": 0, "bytes_per_step": 0,
-                                    "flops_per_step": 0})
+                                    "flops_per_step": 0, "pages_flops_per_step": 0})
         k["ms_per_step"] += sum(lst) / n
         k["launches_per_step"] += len(lst) // n
         if kind == "gemv_bf16":
             k["bytes_per_step"] += gemv_bytes.get(role, 0) * (len(lst) // n)
         if kind == "attn_decode_bf16":
             k["bytes_per_step"] += attn_bytes
-            k["flops_per_step"] += attn_flops
+            k["flops_per_step"] += attn_own
+            k["pages_flops_per_step"] += attn_pages
     breakdown = {}
     for kind, k in sorted(kinds.items(), key=lambda kv: -kv[1]["ms_per_step"]):
         e = {"us_per_step": round(k["ms_per_step"] * 1e3, 2), "launches_per_step": k["launches_per_step"],
@@ -302,44 +323,64 @@ def decode_bench(args, torch, binding, W):
         breakdown[kind] = e
     roles = {f"{kind}/{role}": round(sum(lst) / n * 1e3, 2) for (kind, role), lst in sorted(per.items())}
 
-    # dominant kernel kind of the step (largest share of the step time)
-    def roofline(name):
-        k = kinds[name]
+    def roofline(kname):
+        k = kinds[kname]
         nl = max(k["launches_per_step"], 1)
         avg_s = k["ms_per_step"] * 1e-3 / nl
-        if name == "attn_decode_bf16":
+        if kname == "attn_decode_bf16":
             achieved = k["flops_per_step"] / nl / avg_s / 1e12
-            return {"kernel": name, "bound": "mfma", "achieved": round(achieved, 2),
+            pages = k["pages_flops_per_step"] / nl / avg_s / 1e12
+            return {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 2),
                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                    "traffic": measured_traffic(name, w.name),
+                    "traffic": measured_traffic(kname, w.name),
                     "avg_us": round(avg_s * 1e6, 2), "launches_per_step": nl,
                     "algorithmic_flops_per_launch": int(k["flops_per_step"] / nl),
+                    "flops_counted": "own association: K rebuilt per position, scores, P C_v, "
+                                     "then B_v once per query head",
+                    "pages_explicit_rebuild_flops_per_launch": int(k["pages_flops_per_step"] / nl),
+                    "pages_explicit_rebuild_TFLOP_per_s": round(pages, 2),
+                    "pages_explicit_rebuild_frac": round(pages / MFMA_BF16_PEAK_TFLOPS, 4),
                     "algorithmic_bytes_per_launch": int(k["bytes_per_step"] / nl)}
         achieved = k["bytes_per_step"] / nl / avg_s / 1e9
-        return {"kernel": name, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+        return {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(name, w.name),
+                "traffic": measured_traffic(kname, w.name),
                 "avg_us": round(avg_s * 1e6, 2), "launches_per_step": nl,
                 "algorithmic_bytes_per_launch": int(k["bytes_per_step"] / nl)}
 
+    # dominant kernel kind of the step (largest share of the step time)
     dname = max(kinds.items(), key=lambda kv: kv[1]["ms_per_step"])[0]
     roof = roofline(dname)
     roof_attn = roofline("attn_decode_bf16") if "attn_decode_bf16" in kinds else None
+    roof_gemv = roofline("gemv_bf16") if "gemv_bf16" in kinds else None
     step_bytes = W.algorithmic_decode_bytes(w.shape, Bsz, ctx_total // Bsz)["total"]
     result = {
         "value": Bsz / (ms * 1e-3), "ms_per_step": ms, "wall_s": wall, "graph": use_graph,
         "steps_per_graph": chain_steps if use_graph else None,
-        "roofline": roof, "roofline_attention": roof_attn, "kernels": breakdown,
-        "roles_us_per_step": roles,
+        "roofline": roof, "roofline_attention": roof_attn, "roofline_gemv": roof_gemv,
+        "kernels": breakdown, "roles_us_per_step": roles,
         "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "config": {"workload": w.name, "batch": Bsz, "context": int(inp.past_lens[0]) + 1,
                    "hidden": w.shape.hidden, "n_q": w.shape.n_q, "n_kv": w.shape.n_kv,
                    "head_dim": w.shape.head_dim, "ffn": w.shape.ffn,
                    "compression_pct": w.compression_pct, "ranks": dict(w.shape.ranks),
-                   "weight_sets": args.sets},
+                   "weight_sets": nsets},
     }
+    del sets
+    torch.cuda.empty_cache()
     return result, weights, inp
+
+
+def decode_leg(args, torch, binding, W, name, peaks):
+    r, _, _ = decode_bench(args, torch, binding, W, name, args.leg_steps, args.leg_warmup,
+                           args.leg_trace_steps, args.sets)
+    return {"workload": name, "tokens_per_s": round(r["value"], 1),
+            "ms_per_step": round(r["ms_per_step"], 5), "steps": args.leg_steps,
+            "step_hbm_frac": r["step_hbm_frac"],
+            "roofline_attention": with_measured(r["roofline_attention"], peaks),
+            "roofline_gemv": with_measured(r["roofline_gemv"], peaks),
+            "kernels": r["kernels"], "config": r["config"]}
 
 
 def prefill_bench(args, torch, binding, W):
@@ -365,7 +406,7 @@ def prefill_bench(args, torch, binding, W):
            "steps": args.prefill_steps}
     del sets
     torch.cuda.empty_cache()
-    return out
+    return out, (w, weights, inp)
 
 
 # ----------------------------------------------------------------------------
@@ -418,16 +459,31 @@ def with_measured(roof, peaks):
 # ----------------------------------------------------------------------------
 # CPU oracle baseline
 # ----------------------------------------------------------------------------
-def cpu_baseline(args, W, weights, inp):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(args, W, weights, inp, prefill):
+    """The fp64 oracle as it stands, on the host cores: full decode steps of
+    the headline workload for about --cpu-seconds, then one sequence of the
+    prefill workload (a labelled subset)."""
     import numpy as np
     from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import ref
 
     ncores = len(os.sched_getaffinity(0))
-    F = {p: (W.decode_array(a).astype(np.float64), W.decode_array(b).astype(np.float64))
-         for p, (a, b) in weights.factors.items()}
-    x, ck, cv = (W.decode_array(a).astype(np.float64) for a in (inp.x, inp.ck, inp.cv))
+    f64 = lambda a: W.decode_array(a).astype(np.float64)
+    F = {p: (f64(a), f64(b)) for p, (a, b) in weights.factors.items()}
+    x, ck, cv = (f64(a) for a in (inp.x, inp.ck, inp.cv))
     shp = weights.shape
+    out = {"kind": "oracle", "cpu_model": cpu_model(), "logical_cpus_available": ncores}
     with threadpool_limits(limits=ncores):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
         steps, t0 = 0, time.perf_counter()
@@ -438,11 +494,26 @@ def cpu_baseline(args, W, weights, inp):
             el = time.perf_counter() - t0
             if el >= args.cpu_seconds or steps >= 1000:
                 break
-    Bsz = inp.x.shape[0]
-    return {"value": round(Bsz * steps / el, 3), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{steps} full decode steps of the same workload (batch {Bsz}, "
-                      f"context {int(inp.past_lens[0]) + 1}), fp64 numpy, {el:.1f} s"}
+        Bsz = inp.x.shape[0]
+        out.update({"value": round(Bsz * steps / el, 3), "unit": "tokens/s", "cores": threads,
+                    "sample": f"{steps} full decode steps of the headline workload (batch {Bsz}, "
+                              f"context {int(inp.past_lens[0]) + 1}), fp64 numpy, {el:.1f} s"})
+        del F, x, ck, cv
+        if prefill is not None:
+            w, pw, pin = prefill
+            PF = {p: (f64(a), f64(b)) for p, (a, b) in pw.factors.items()}
+            s1 = slice(0, 1)
+            t0 = time.perf_counter()
+            ref.decomposed_layer(PF, f64(pin.x)[s1], f64(pin.ck)[s1], f64(pin.cv)[s1],
+                                 pin.past_lens[s1], w.shape.n_q, w.shape.n_kv, w.shape.head_dim,
+                                 w.shape.rope_theta, w.shape.rms_eps)
+            el = time.perf_counter() - t0
+            total, _, _ = prefill_flops(w.shape, 1, w.prefill)
+            out["prefill"] = {"value": round(total / el / 1e12, 5), "unit": "TFLOP/s",
+                              "cores": threads,
+                              "sample": f"sequence 0 of {w.name} ({w.prefill} tokens, 1 of "
+                                        f"{w.batch} sequences), fp64 numpy, {el:.1f} s"}
+    return out
 
 
 def main():
@@ -472,11 +543,16 @@ def main():
     peaks = measured_peaks(torch, binding)
     log(f"measured peaks: {peaks['hbm_copy_GB_per_s']} GB/s copy, "
         f"{peaks['mfma_bf16_TFLOP_per_s']} TFLOP/s bf16 MFMA")
-    dec, weights, inp = decode_bench(args, torch, binding, W)
+    dec, weights, inp = decode_bench(args, torch, binding, W, args.workload, args.steps,
+                                     args.warmup, args.trace_steps, args.sets)
     log(f"decode: {dec['value']:.0f} tokens/s, {dec['ms_per_step'] * 1e3:.1f} us/step")
-    pre = None
+    legs = []
+    for name in [n for n in args.legs.split(",") if n]:
+        legs.append(decode_leg(args, torch, binding, W, name, peaks))
+        log(f"leg {name}: {legs[-1]['tokens_per_s']:.0f} tokens/s")
+    pre = pre_inputs = None
     if not args.no_prefill:
-        pre = prefill_bench(args, torch, binding, W)
+        pre, pre_inputs = prefill_bench(args, torch, binding, W)
         pre["mfma_frac_of_measured"] = round(pre["TFLOP_per_s"] / peaks["mfma_bf16_TFLOP_per_s"], 4)
         if pre["gemm_TFLOP_per_s"]:
             pre["gemm_frac_of_measured"] = round(pre["gemm_TFLOP_per_s"] / peaks["mfma_bf16_TFLOP_per_s"], 4)
@@ -484,7 +560,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
-        cpu = cpu_baseline(args, W, weights, inp)
+        cpu = cpu_baseline(args, W, weights, inp, pre_inputs)
     line = {
         "metric": METRIC, "value": round(dec["value"], 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(dec["ms_per_step"], 5),
@@ -493,9 +569,10 @@ def main():
         "config": dec["config"], "graph": dec["graph"], "steps_per_graph": dec["steps_per_graph"],
         "roofline": with_measured(dec["roofline"], peaks),
         "roofline_attention": with_measured(dec["roofline_attention"], peaks),
+        "roofline_gemv": with_measured(dec["roofline_gemv"], peaks),
         "measured_peaks": peaks,
         "step_hbm_frac": dec["step_hbm_frac"], "kernel_source_hash": kernel_source_hash(),
-        "cpu_baseline": cpu, "prefill": pre, "kernels": dec["kernels"],
+        "cpu_baseline": cpu, "prefill": pre, "decode_legs": legs, "kernels": dec["kernels"],
         "roles_us_per_step": dec["roles_us_per_step"],
     }
     print(json.dumps(line), flush=True)

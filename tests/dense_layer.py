@@ -26,20 +26,24 @@ def _rot_matrix(d, pos, theta):
     return R
 
 
-def _rmsnorm_row(v, eps):
+def _rmsnorm_row(v, eps, gain=None):
     ms = sum(float(t) * float(t) for t in v) / len(v)
-    return np.array([float(t) / math.sqrt(ms + eps) for t in v])
+    g = [1.0] * len(v) if gain is None else [float(t) for t in gain]
+    return np.array([float(t) / math.sqrt(ms + eps) * gi for t, gi in zip(v, g)])
 
 
 def _silu(z):
     return z / (1.0 + math.exp(-z))
 
 
-def dense_layer(W, x, cache_in_x, n_q, n_kv, d, theta, eps):
+def dense_layer(W, x, cache_in_x, n_q, n_kv, d, theta, eps, attn_gain=None, mlp_gain=None,
+                sm_scale=None):
     """W: dict of dense [in, out] matrices q, k, v, o, gate, up, down.
     x: [Bsz, T, h] new tokens; cache_in_x: [Bsz, P, h] normalised
     activations of the P tokens already in the cache (or None), whose keys
-    and values are recomputed densely. Returns (y, x2)."""
+    and values are recomputed densely. attn_gain / mlp_gain: per-channel
+    gains of the two RMSNorms (None = 1). Returns (y, x2)."""
+    scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
     Bsz, T, h = x.shape
     group = n_q // n_kv
     y = np.zeros((Bsz, T, h))
@@ -47,7 +51,7 @@ def dense_layer(W, x, cache_in_x, n_q, n_kv, d, theta, eps):
     for b in range(Bsz):
         past = [] if cache_in_x is None else [cache_in_x[b, j] for j in range(cache_in_x.shape[1])]
         P = len(past)
-        normed_new = [_rmsnorm_row(x[b, t], eps) for t in range(T)]
+        normed_new = [_rmsnorm_row(x[b, t], eps, attn_gain) for t in range(T)]
         seq = past + normed_new                     # normalised rows, position = index
         keys = []
         vals = []
@@ -64,7 +68,7 @@ def dense_layer(W, x, cache_in_x, n_q, n_kv, d, theta, eps):
             for hh in range(n_q):
                 g = hh // group
                 qh = _rot_matrix(d, pos, theta) @ qf[hh * d:(hh + 1) * d]
-                scores = [float(qh @ keys[j][g]) / math.sqrt(d) for j in range(pos + 1)]
+                scores = [float(qh @ keys[j][g]) * scale for j in range(pos + 1)]
                 mx = max(scores)
                 ws = [math.exp(s - mx) for s in scores]
                 tot = sum(ws)
@@ -72,7 +76,7 @@ def dense_layer(W, x, cache_in_x, n_q, n_kv, d, theta, eps):
                 heads.append(o)
             att = np.concatenate(heads)
             x2 = x[b, t] + att @ W["o"]
-            bn = _rmsnorm_row(x2, eps)
+            bn = _rmsnorm_row(x2, eps, mlp_gain)
             g_ = bn @ W["gate"]
             u_ = bn @ W["up"]
             hid = np.array([_silu(float(gv)) * float(uv) for gv, uv in zip(g_, u_)])

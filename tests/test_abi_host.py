@@ -99,7 +99,10 @@ def test_attention_validation(lib):
     assert call(scale=-1.0) == INVALID
     assert call(q=BAD) == ALIGN
     assert call(ws=16) == WORKSPACE
-    assert call(d=6, dt=B.DL_F32, ws=0, wsp=None) != UNSUPPORTED or True
+    # f32 accepts any even head_dim: d = 6 passes the shape checks and is
+    # rejected only by the later scale check (no launch is reached)
+    assert call(d=6, dt=B.DL_F32, scale=-1.0) == INVALID
+    assert call(d=7, dt=B.DL_F32, scale=-1.0) == UNSUPPORTED
     assert call(d=258, dt=B.DL_F32) == UNSUPPORTED
     pre = lib.dl_lowrank_attn_prefill
     assert pre(P, P, P, P, P, P, P, 2, 4, 12, 4, 128, 64, 64, 32, 0.0, 0.0, B.DL_BF16, P, 1 << 24,

@@ -5,9 +5,10 @@ lengths) and on the five workload configurations at their full sizes.
 For each check the attention delta (x2 - x) and the MLP delta (y - x2) are
 compared separately, so the residual stream cannot hide an error, and the
 appended cache rows are compared too. Tolerance as in test_gpu_ops.
-Full-size decode configurations compare a sample of sequences (each
-sequence's output depends only on its own rows); the prefill configuration
-compares sequence 0 in full. Inputs are uploaded in the library's storage
+Full-size configurations compare every sequence: the decode
+configurations in one pass, the prefill configuration one sequence per test
+(each sequence's rows depend only on that sequence), after one GPU run shared
+by those tests. Inputs are uploaded in the library's storage
 order (factors transposed, value cache rank-major, bf16 factors and caches
 in operand tiles) and the caches are read back into the oracle's
 [Bsz, L, r] order before comparing."""
@@ -35,16 +36,20 @@ def make_gpu_layer(B, weights: W.LayerWeights):
     shp = weights.shape
     facs = {p: (to_dev(W.to_library_factor(a)), to_dev(W.to_library_factor(b)))
             for p, (a, b) in weights.factors.items()}
+    gain = lambda g: None if g is None else to_dev(g)
     return B.DecomposedLayer(facs, shp.hidden, shp.n_q, shp.n_kv, shp.head_dim, shp.ffn,
-                             shp.rope_theta, shp.rms_eps)
+                             shp.rope_theta, shp.rms_eps, attn_norm=gain(weights.attn_norm),
+                             mlp_norm=gain(weights.mlp_norm))
 
 
 def oracle_layer(weights, x, ck, cv, past, seqs=None):
     shp = weights.shape
     sl = slice(None) if seqs is None else seqs
     F = {p: (f64(a), f64(b)) for p, (a, b) in weights.factors.items()}
+    gain = lambda g: None if g is None else f64(g)
     return ref.decomposed_layer(F, f64(x)[sl], f64(ck)[sl], f64(cv)[sl], np.asarray(past)[sl],
-                                shp.n_q, shp.n_kv, shp.head_dim, shp.rope_theta, shp.rms_eps)
+                                shp.n_q, shp.n_kv, shp.head_dim, shp.rope_theta, shp.rms_eps,
+                                attn_norm=gain(weights.attn_norm), mlp_norm=gain(weights.mlp_norm))
 
 
 #: unit roundoff of the stored outputs; y is stored in the layer dtype
@@ -110,9 +115,9 @@ SMALL = [
 
 
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
-def test_small_layer(B, case, rank_up=None):
+def test_small_layer(B, case, rank_up=None, gains=False):
     name, dt, h, nq, nkv, d, f, ra, rkv, rm, Bsz, T, past, L_max, theta = case
-    print(f"layer {case} rank_up={rank_up}", flush=True)
+    print(f"layer {case} rank_up={rank_up} gains={gains}", flush=True)
     r = np.random.Generator(np.random.PCG64(sum(map(ord, name))))
     if past is None:
         past = list(r.integers(0, L_max - T, size=Bsz))
@@ -122,6 +127,11 @@ def test_small_layer(B, case, rank_up=None):
     for p, (m, n) in shp.shapes().items():
         facs[p] = (rand(r, (m, shp.rank(p)), 0.05, dt), rand(r, (shp.rank(p), n), 0.05, dt))
     weights = W.LayerWeights(shp, facs)
+    if gains:
+        # distinct per-channel gains for the two norms (stored in the layer dtype)
+        enc = lambda a: W.f32_to_bf16_bits(a) if dt == "bf16" else a.astype(np.float32)
+        weights.attn_norm = enc(0.5 + r.random(h, dtype=np.float32))
+        weights.mlp_norm = enc(0.5 + r.random(h, dtype=np.float32) * 1.5)
     x = rand(r, (Bsz, T, h), 1.0, dt)
     ck0 = rand(r, (Bsz, L_max, rkv), 1.0, dt)
     cv0 = rand(r, (Bsz, L_max, rkv), 1.0, dt)
@@ -130,6 +140,15 @@ def test_small_layer(B, case, rank_up=None):
     y, x2 = run_layer(B, layer, x, ck, cv, past)
     want = oracle_layer(weights, x, ck0, cv0, past)
     check_step(dt, x, y, x2, ck, cv, want, past, T)
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_layer_norm_gains(B, case):
+    """Non-unit RMSNorm gains on both norms: the decode path folds the MLP
+    gain into the o pair's residual epilogue (gamma * x2 tiles) and the
+    attention gain into the first normalisation; the prefill path applies
+    both in its row kernels; the f32 path in its own kernels."""
+    test_small_layer(B, case, gains=True)
 
 
 @pytest.mark.parametrize("R", ["2", "4"])
@@ -177,7 +196,7 @@ def test_tiny_chain_prefill_then_decode(B):
     assert relerr(W.from_library_key_cache(to_host(ck), False), ck_ref) <= TOL["f32"]
 
 
-def _decode_config(B, w, seqs):
+def _decode_config(B, w, seqs=None):
     weights, inp = W.draw(w)
     layer = make_gpu_layer(B, weights)
     ck, cv = to_dev(W.to_library_key_cache(inp.ck)), to_dev(W.to_library_value_cache(inp.cv))
@@ -187,27 +206,58 @@ def _decode_config(B, w, seqs):
 
 
 def test_llama3_8b_c40_decode(B):
-    print("llama3_8b_c40_decode full batch", flush=True)
-    _decode_config(B, W.LLAMA3_8B_C40_DECODE, None)
+    print("llama3_8b_c40_decode all sequences", flush=True)
+    _decode_config(B, W.LLAMA3_8B_C40_DECODE)
 
 
 @pytest.mark.parametrize("w", W.LLAMA3_8B_SWEEP, ids=[f"c{w.compression_pct}" for w in W.LLAMA3_8B_SWEEP])
 def test_llama3_8b_sweep_decode(B, w):
-    print(f"{w.name} sampled sequences", flush=True)
-    _decode_config(B, w, np.array([0, 17, 40, 63]))
+    print(f"{w.name} all sequences", flush=True)
+    _decode_config(B, w)
 
 
 def test_llama3_70b_c50_decode(B):
-    print("llama3_70b_c50_decode sampled sequences", flush=True)
-    _decode_config(B, W.LLAMA3_70B_C50_DECODE, np.array([0, 31]))
+    print("llama3_70b_c50_decode all sequences", flush=True)
+    _decode_config(B, W.LLAMA3_70B_C50_DECODE)
 
 
-def test_llama3_70b_c50_prefill(B):
-    print("llama3_70b_c50_prefill sequence 0", flush=True)
+@pytest.fixture(scope="module")
+def prefill_70b(B):
+    """One GPU prefill step of the 70B 8 x 2048 workload; host copies of the
+    outputs and caches, shared by the per-sequence comparisons."""
+    import torch
     w = W.LLAMA3_70B_C50_PREFILL
+    print("llama3_70b_c50_prefill: GPU step", flush=True)
     weights, inp = W.draw(w)
     layer = make_gpu_layer(B, weights)
     ck, cv = to_dev(W.to_library_key_cache(inp.ck)), to_dev(W.to_library_value_cache(inp.cv))
     y, x2 = run_layer(B, layer, inp.x, ck, cv, inp.past_lens)
-    want = oracle_layer(weights, inp.x, inp.ck, inp.cv, inp.past_lens, np.array([0]))
-    check_step("bf16", inp.x, y, x2, ck, cv, want, inp.past_lens, w.prefill, np.array([0]))
+    torch.cuda.synchronize()
+    got = {"y": to_host(y), "x2": to_host(x2),
+           "ck": W.from_library_key_cache(to_host(ck), True),
+           "cv": W.from_library_value_cache(to_host(cv), True)}
+    del layer, ck, cv, y, x2
+    torch.cuda.empty_cache()
+    return w, weights, inp, got
+
+
+@pytest.mark.parametrize("seq", range(8))
+def test_llama3_70b_c50_prefill(prefill_70b, seq):
+    """Every sequence of the prefill batch, all 2048 rows: every row tile of
+    the factor GEMMs, every query tile of the causal attention (including the
+    heaviest-first work order) and every appended cache row."""
+    w, weights, inp, got = prefill_70b
+    print(f"llama3_70b_c50_prefill sequence {seq}", flush=True)
+    sl = np.array([seq])
+    want = oracle_layer(weights, inp.x, inp.ck, inp.cv, inp.past_lens, sl)
+    xh = f64(inp.x)[sl]
+    smax = float(max(np.max(np.abs(want["y"])), np.max(np.abs(want["x2"]))))
+    errs = {
+        "attn_delta": delta_err(got["x2"][sl] - xh, want["x2"] - xh, smax, "f32"),
+        "mlp_delta": delta_err(got["y"][sl] - got["x2"][sl], want["y"] - want["x2"], smax, "bf16"),
+        "y": relerr(got["y"][sl], want["y"]),
+        "ck": relerr(got["ck"][seq, :w.prefill], want["ck"][0, :w.prefill]),
+        "cv": relerr(got["cv"][seq, :w.prefill], want["cv"][0, :w.prefill]),
+    }
+    bad = {k: v for k, v in errs.items() if not v <= TOL["bf16"]}
+    assert not bad, (bad, errs)

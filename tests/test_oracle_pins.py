@@ -99,13 +99,42 @@ def test_layer_matches_dense_at_full_rank(P, T, n_q, n_kv, theta):
     assert np.max(np.abs(out["y"] - y_d)) < 1e-9
 
 
+@pytest.mark.parametrize("P,T", [(0, 4), (5, 1)])
+def test_layer_gains_match_dense_at_full_rank(P, T):
+    """Norm gains: attn_norm scales the attention input and mlp_norm the MLP
+    input. Distinct random gains; the swapped wiring must not match."""
+    h, n_q, n_kv, d, f, Bsz, eps, theta = 16, 4, 2, 8, 24, 2, 1e-5, 10000.0
+    r, W, F = _dense_and_factors(40 + P, h, n_q, n_kv, d, f)
+    g_attn = 0.5 + r.random(h)
+    g_mlp = 0.5 + r.random(h)
+    x = r.standard_normal((Bsz, T, h))
+    past_norm = r.standard_normal((Bsz, P, h)) if P else None
+    L_max = P + T + 1
+    ck = np.zeros((Bsz, L_max, F["k"][0].shape[1]))
+    cv = np.zeros((Bsz, L_max, F["v"][0].shape[1]))
+    if P:
+        ck[:, :P] = past_norm @ F["k"][0]
+        cv[:, :P] = past_norm @ F["v"][0]
+    past = np.full(Bsz, P)
+    out = ref.decomposed_layer(F, x, ck, cv, past, n_q, n_kv, d, theta, eps,
+                               attn_norm=g_attn, mlp_norm=g_mlp)
+    y_d, x2_d = dense_layer(W, x, past_norm, n_q, n_kv, d, theta, eps, attn_gain=g_attn,
+                            mlp_gain=g_mlp)
+    assert np.max(np.abs(out["x2"] - x2_d)) < 1e-9
+    assert np.max(np.abs(out["y"] - y_d)) < 1e-9
+    swapped = ref.decomposed_layer(F, x, ck, cv, past, n_q, n_kv, d, theta, eps,
+                                   attn_norm=g_mlp, mlp_norm=g_attn)
+    assert np.max(np.abs(swapped["y"] - y_d)) > 1e-3
+
+
 # --------------------------------------------------------------------------
 # Attention vs brute force
 # --------------------------------------------------------------------------
-def _brute_attention(q, ck, cv, B_k, B_v, past_lens, n_kv, theta):
+def _brute_attention(q, ck, cv, B_k, B_v, past_lens, n_kv, theta, scale=None):
     """Per query: explicit score row over ALL cache rows with -inf beyond the
     causal limit, math.exp normalisation, explicit rotation by angle."""
     Bsz, T, n_q, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
     half = d // 2
     G = n_q // n_kv
     L_max = ck.shape[1]
@@ -133,7 +162,7 @@ def _brute_attention(q, ck, cv, B_k, B_v, past_lens, n_kv, theta):
                         row.append(-math.inf)
                         continue
                     kv = rot((ck[b, j] @ B_k)[g * d:(g + 1) * d], j)
-                    row.append(sum(qv[i] * kv[i] for i in range(d)) / math.sqrt(d))
+                    row.append(sum(qv[i] * kv[i] for i in range(d)) * scale)
                 mx = max(row)
                 e = [0.0 if s == -math.inf else math.exp(s - mx) for s in row]
                 z = sum(e)
@@ -161,6 +190,27 @@ def test_attention_matches_brute_force_ragged(n_q, n_kv, theta):
     # decode form: the last query of each sequence
     got_dec = ref.attn_decode(q[:, -1], ck, cv, B_k, B_v, past + T, n_kv, theta)
     assert np.max(np.abs(got_dec - want[:, -1])) < 1e-12
+
+
+@pytest.mark.parametrize("scale", [0.05, 1.7])
+def test_attention_explicit_scale_matches_brute_force(scale):
+    """The explicit softmax-scale branch: a scale other than 1/sqrt(d) must
+    reach the scores unchanged (a sharper and a flatter softmax)."""
+    r = rng(6)
+    Bsz, T, n_q, n_kv, d, rk, rv, L_max = 2, 2, 4, 2, 8, 5, 6, 9
+    past = np.array([1, 6])
+    q = r.standard_normal((Bsz, T, n_q, d))
+    ck = r.standard_normal((Bsz, L_max, rk))
+    cv = r.standard_normal((Bsz, L_max, rv))
+    B_k = r.standard_normal((rk, n_kv * d)) * 0.5
+    B_v = r.standard_normal((rv, n_kv * d))
+    got = ref.attn_prefill(q, ck, cv, B_k, B_v, past, n_kv, 1000.0, sm_scale=scale)
+    want = _brute_attention(q, ck, cv, B_k, B_v, past, n_kv, 1000.0, scale=scale)
+    assert np.max(np.abs(got - want)) < 1e-12
+    got_dec = ref.attn_decode(q[:, -1], ck, cv, B_k, B_v, past + T, n_kv, 1000.0, sm_scale=scale)
+    assert np.max(np.abs(got_dec - want[:, -1])) < 1e-12
+    # the default scale gives a different result: the branch is not a no-op
+    assert np.max(np.abs(ref.attn_prefill(q, ck, cv, B_k, B_v, past, n_kv, 1000.0) - want)) > 1e-3
 
 
 def test_prefill_then_decode_equals_longer_prefill():
