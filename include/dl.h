@@ -96,6 +96,26 @@ dl_status dl_lowrank_linear(const void *x, const void *A, const void *B, void *y
                             dl_dtype dt, void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Allocation-free factor-pair projection.
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments, result and kernels as dl_lowrank_linear, but
+ * the workspace is a static device array inside the library (one per GPU,
+ * held from library load until the process ends) of DL_STATIC_SCRATCH_BYTES
+ * (16 MiB). A product whose
+ * dl_lowrank_linear_workspace() exceeds that is rejected with
+ * DL_ERR_WORKSPACE before any device work. The call allocates and frees
+ * nothing. Every call on one GPU uses the same scratch array, and each call
+ * re-initialises what it needs, so sequential calls (any stream order that
+ * serialises them) are safe; calls that overlap in time on one GPU (other
+ * streams, other threads) race on the scratch and give undefined results.
+ * ------------------------------------------------------------------------ */
+#define DL_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+dl_status dl_lowrank_linear_static(const void *x, const void *A, const void *B,
+                                   void *y, int64_t M, int64_t m, int64_t k,
+                                   int64_t n, dl_dtype dt, void *stream);
+
+/* ------------------------------------------------------------------------
  * Low-rank KV-cache append -- section 2.1 (the k/v latents are the cache)
  * and section 4.1 (they are stored as KV cache).
  *   Ck[b, past_lens[b] + t, :] = x[b, t, :] A_k     x   : [Bsz, T, m]

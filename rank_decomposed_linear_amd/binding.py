@@ -25,12 +25,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdlayer.so")
 
 DL_F32, DL_BF16 = 0, 1
+STATIC_SCRATCH_BYTES = 16 << 20   # DL_STATIC_SCRATCH_BYTES
 STATUS = {0: "DL_OK", 1: "DL_ERR_INVALID_ARG", 2: "DL_ERR_UNSUPPORTED", 3: "DL_ERR_ALIGNMENT",
           4: "DL_ERR_WORKSPACE", 5: "DL_ERR_HIP"}
 
 EXPORTS = (
     "dl_last_error",
     "dl_lowrank_linear_workspace", "dl_lowrank_linear",
+    "dl_lowrank_linear_static",
     "dl_kv_append_workspace", "dl_lowrank_kv_append",
     "dl_attn_decode_workspace", "dl_lowrank_attn_decode",
     "dl_attn_prefill_workspace", "dl_lowrank_attn_prefill",
@@ -86,6 +88,9 @@ def load() -> ctypes.CDLL:
     lib.dl_lowrank_linear.restype = ctypes.c_int
     lib.dl_lowrank_linear.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int,
                                       _vp, _sz, _vp]
+    lib.dl_lowrank_linear_static.restype = ctypes.c_int
+    lib.dl_lowrank_linear_static.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                             ctypes.c_int, _vp]
     lib.dl_kv_append_workspace.restype = _sz
     lib.dl_kv_append_workspace.argtypes = [_i64, _i64, _i64, _i64, _i64, ctypes.c_int]
     lib.dl_lowrank_kv_append.restype = ctypes.c_int
@@ -234,6 +239,19 @@ def lowrank_linear(x, At, Bt, y=None, ws=None):
     ws = ws if ws is not None else _ws(need, x.device)
     _check(lib.dl_lowrank_linear(_ptr(x), _ptr(At), _ptr(Bt), _ptr(y), M, m, k, n, dt, _ptr(ws),
                                  ws.numel(), _stream(x.device)))
+    return y
+
+
+def lowrank_linear_static(x, At, Bt, y=None):
+    """dl_lowrank_linear_static: y = (x A) B with the library's static
+    scratch as the workspace (no allocation besides the output)."""
+    lib = load()
+    M, m = x.shape
+    k, n = At.shape[0], Bt.shape[0]
+    if y is None:
+        y = torch.empty((M, n), dtype=x.dtype, device=x.device)
+    _check(lib.dl_lowrank_linear_static(_ptr(x), _ptr(At), _ptr(Bt), _ptr(y), M, m, k, n, _dt(x),
+                                        _stream(x.device)))
     return y
 
 

@@ -9,6 +9,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "dl.h"
@@ -466,6 +467,58 @@ dl_status dl_lowrank_linear(const void *x, const void *A, const void *B, void *y
   b.seg[0] = mseg(B, t, y, ni, ki, ni);
   DL_HIP(gemm(b, s));
   return DL_OK;
+}
+
+// ===========================================================================
+// dl_lowrank_linear_static: the same product with the workspace in a
+// file-scope device array instead of a caller buffer
+// ===========================================================================
+namespace {
+// Scratch of the allocation-free variant. Each device that runs the library
+// holds its own copy from code-object load until the process ends. In host
+// code `scratch` only names the symbol: its device address is looked up once
+// per device with hipGetSymbolAddress and only that address is ever passed
+// to kernels or copies.
+constexpr size_t kScratchBytes = DL_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call per device, with that device current).
+dl_status scratch_on_current_device(void **out) {
+  int dev = -1;
+  DL_HIP(hipGetDevice(&dev));
+  DL_CHECK(dev >= 0 && dev < kMaxDevices, DL_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    DL_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    DL_CHECK(p != nullptr, DL_ERR_HIP, "hipGetSymbolAddress returned a null scratch address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DL_OK;
+}
+}  // namespace
+
+dl_status dl_lowrank_linear_static(const void *x, const void *A, const void *B, void *y,
+                                   int64_t M, int64_t m, int64_t k, int64_t n, dl_dtype dt,
+                                   void *stream) {
+  set_role(R_OTHER);
+  DL_CHECK(valid_dtype(dt), DL_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  DL_CHECK(M > 0 && m > 0 && k > 0 && n > 0, DL_ERR_INVALID_ARG, "dims must be positive");
+  const size_t need = dl_lowrank_linear_workspace(M, m, k, n, dt);
+  DL_CHECK(need <= kScratchBytes, DL_ERR_WORKSPACE,
+           "this product needs %zu bytes of scratch; the static scratch holds %zu "
+           "(use dl_lowrank_linear with a caller workspace)",
+           need, kScratchBytes);
+  void *ws = nullptr;
+  const dl_status st = scratch_on_current_device(&ws);
+  if (st != DL_OK) return st;
+  return dl_lowrank_linear(x, A, B, y, M, m, k, n, dt, ws, kScratchBytes, stream);
 }
 
 // ===========================================================================

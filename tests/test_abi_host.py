@@ -66,6 +66,18 @@ def test_lowrank_linear_validation(lib):
     assert f(P, P, P, P, 3, 5, 7, 9, B.DL_F32, P, need32 - 1, None) == WORKSPACE
 
 
+def test_lowrank_linear_static_validation(lib):
+    """The allocation-free variant rejects bad arguments, and products whose
+    workspace exceeds the static scratch, before touching the device."""
+    f = lib.dl_lowrank_linear_static
+    assert f(P, P, P, P, 16, 64, 64, 64, 7, None) == INVALID
+    assert f(P, P, P, P, 0, 64, 64, 64, B.DL_BF16, None) == INVALID
+    need = lib.dl_lowrank_linear_workspace(4096, 4096, 4096, 64, B.DL_BF16)
+    assert need > B.STATIC_SCRATCH_BYTES
+    assert f(P, P, P, P, 4096, 4096, 4096, 64, B.DL_BF16, None) == WORKSPACE
+    assert "static scratch" in err(lib)
+
+
 def test_kv_append_validation(lib):
     f = lib.dl_lowrank_kv_append
     assert f(P, P, P, P, P, None, 2, 1, 64, 64, 64, 32, B.DL_BF16, P, 1 << 20, None) == INVALID
