@@ -21,19 +21,27 @@
  *     B (k x n) as Bt = B^T [n, k] (the [out, in] layout of the two maps
  *     x -> x A and t -> t B). The up factors of attention are B_k^T and
  *     B_v^T, [n_kv * d, r].
- *   - Latent caches: the key cache Ck is [Bsz, L_max, r_k] (one row per
- *     position); the value cache Cv is rank-major, [Bsz, r_v, L_max] (one
- *     row per rank component), because attention reduces the value latents
- *     over positions.
  *   - DL_BF16 operand tiles: with DL_BF16 every factor matrix above (At, Bt,
- *     B_k^T, B_v^T) and each sequence's cache matrix ([L_max, r_k] and
- *     [r_v, L_max]) is stored in 16 x 32 tiles of 1 KB, in MFMA operand
- *     order: element (r, c) of an [R, C] matrix sits at element offset
+ *     B_k^T, B_v^T) and every cache page below is stored in 16 x 32 tiles of
+ *     1 KB, in MFMA operand order: element (r, c) of an [R, C] matrix sits
+ *     at element offset
  *       ((r / 16) * (C / 32) + c / 32) * 512
  *         + (((c % 32) / 8) * 16 + r % 16) * 8 + c % 8
- *     (R % 16 == 0, C % 32 == 0; so DL_BF16 caches need L_max % 32 == 0).
- *     Every operand fragment the kernels read is then one contiguous 1 KB
- *     block. DL_F32 tensors are plain row-major.
+ *     (R % 16 == 0, C % 32 == 0). Every operand fragment the kernels read is
+ *     then one contiguous 1 KB block. DL_F32 tensors are plain row-major.
+ *     dl_pack_factor / dl_pack_kv_cache convert the pages' row-major
+ *     A [m, k], B [k, n] and caches [Bsz, L_max, r] into these layouts.
+ *   - Latent caches, DL_BF16: in pages of DL_PAGE = 64 positions. A key page
+ *     holds the 64 positions' k latents as an operand-tiled [64, r_k] matrix
+ *     (64 * r_k elements); a value page holds the same positions' v latents
+ *     rank-major, as an operand-tiled [r_v, 64] matrix (64 * r_v elements),
+ *     because attention reduces the value latents over positions. A
+ *     contiguous cache (Ck, Cv with L_max rows per sequence, L_max % 64 ==
+ *     0) is sequence b's L_max / 64 pages back to back: Ck and Cv are
+ *     [Bsz, L_max / 64, 64 * r] in pages. A paged cache (dl_kv_cache) reaches
+ *     each sequence's pages through a block table.
+ *   - Latent caches, DL_F32: Ck is [Bsz, L_max, r_k] row-major and Cv is
+ *     rank-major [Bsz, r_v, L_max]; no paged form.
  *   - dtype DL_F32: every tensor is float32 and arithmetic is float32.
  *     dtype DL_BF16: activations, factors, caches and outputs are bfloat16,
  *     products accumulate in float32; intermediates may be rounded to bf16.
@@ -78,6 +86,32 @@ typedef enum {
 
 typedef enum { DL_F32 = 0, DL_BF16 = 1 } dl_dtype;
 
+#define DL_PAGE 64   /* positions per cache page (DL_BF16) */
+
+/* A paged low-rank KV cache (DL_BF16) -- section 4.2, Fig. 4(b): the
+ * latents live in fixed-size pages of a pool, and a block table maps each
+ * sequence's logical pages to pool pages, so the cache grows a page at a
+ * time and one captured HIP graph can replay every decode step (the
+ * kernels read lengths and tables from device memory).
+ *   k, v        : key and value page pools, num_pages pages each (layout
+ *                 above), caller-owned device memory
+ *   block_table : device int32 [Bsz, pages_per_seq]; entry [b, p] is the
+ *                 pool page holding positions 64 p .. 64 p + 63 of
+ *                 sequence b. Preconditions (not checked, device data):
+ *                 every entry a call reaches -- pages 0 .. (len - 1) / 64 of
+ *                 a sequence of len positions -- lies in [0, num_pages),
+ *                 and no two sequences share a page a call writes.
+ *   pages_per_seq: row length of block_table; a sequence holds at most
+ *                 64 * pages_per_seq positions (the L_max of the paged form).
+ *   num_pages   : pages in each pool. */
+typedef struct {
+  void *k;
+  void *v;
+  const int32_t *block_table;
+  int64_t pages_per_seq;
+  int64_t num_pages;
+} dl_kv_cache;
+
 /* Description of the last non-OK status returned on the calling thread. */
 const char *dl_last_error(void);
 
@@ -118,13 +152,14 @@ dl_status dl_lowrank_linear_static(const void *x, const void *A, const void *B,
 /* ------------------------------------------------------------------------
  * Low-rank KV-cache append -- section 2.1 (the k/v latents are the cache)
  * and section 4.1 (they are stored as KV cache).
- *   Ck[b, past_lens[b] + t, :] = x[b, t, :] A_k     x   : [Bsz, T, m]
- *   Cv[b, :, past_lens[b] + t] = x[b, t, :] A_v     A_k, A_v passed as [r_k, m], [r_v, m]
- *                                                    Ck  : [Bsz, L_max, r_k]
- *                                                    Cv  : [Bsz, r_v, L_max]
- * past_lens: device int32 [Bsz]; precondition past_lens[b] + T <= L_max.
- * No other cache row is written.
- * DL_BF16 requires m, r_k, r_v to be multiples of 64.
+ *   key latent   (b, past_lens[b] + t) = x[b, t, :] A_k     x : [Bsz, T, m]
+ *   value latent (b, past_lens[b] + t) = x[b, t, :] A_v     A_k, A_v passed
+ *                                                           as [r_k, m], [r_v, m]
+ * into the cache (layouts above). past_lens: device int32 [Bsz];
+ * precondition past_lens[b] + T <= L_max. No other cache position is
+ * written. DL_BF16 requires m, r_k, r_v multiples of 64 and L_max % 64 == 0.
+ * The _paged form writes through the block table (L_max = 64 *
+ * pages_per_seq).
  * ------------------------------------------------------------------------ */
 size_t dl_kv_append_workspace(int64_t Bsz, int64_t T, int64_t m, int64_t r_k,
                               int64_t r_v, dl_dtype dt);
@@ -133,11 +168,17 @@ dl_status dl_lowrank_kv_append(const void *x, const void *A_k, const void *A_v,
                                int64_t Bsz, int64_t T, int64_t m, int64_t r_k,
                                int64_t r_v, int64_t L_max, dl_dtype dt,
                                void *ws, size_t ws_bytes, void *stream);
+dl_status dl_lowrank_kv_append_paged(const void *x, const void *A_k,
+                                     const void *A_v, const dl_kv_cache *cache,
+                                     const int32_t *past_lens, int64_t Bsz,
+                                     int64_t T, int64_t m, int64_t r_k,
+                                     int64_t r_v, dl_dtype dt, void *ws,
+                                     size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * Decode attention over the low-rank cache -- section 4.2.
  *   q   : [Bsz, n_q, d] un-rotated queries
- *   Ck  : [Bsz, L_max, r_k], Cv: [Bsz, r_v, L_max] latent caches
+ *   Ck, Cv: latent caches of L_max positions per sequence (layouts above)
  *   B_k : [r_k, n_kv*d], B_v: [r_v, n_kv*d] up factors of the k and v pairs,
  *         passed transposed ([n_kv*d, r_k], [n_kv*d, r_v])
  *   ctx_lens: device int32 [Bsz], 1 <= ctx_lens[b] <= L_max
@@ -148,7 +189,9 @@ dl_status dl_lowrank_kv_append(const void *x, const void *A_k, const void *A_v,
  * probability-weighted value latents (softmax(s) C_v B_v, the same product
  * in another association). Softmax is computed online.
  * DL_BF16 requires d in {64, 128}, r_k and r_v multiples of 64, r_v <= 1024,
- * L_max % 8 == 0 and n_q / n_kv <= 16. DL_F32 requires even d <= 256.
+ * L_max % 64 == 0 and n_q / n_kv <= 16. DL_F32 requires even d <= 256.
+ * The _paged form reads the cache through its block table (L_max = 64 *
+ * pages_per_seq for the workspace query).
  * ------------------------------------------------------------------------ */
 size_t dl_attn_decode_workspace(int64_t Bsz, int64_t n_q, int64_t n_kv,
                                 int64_t d, int64_t r_k, int64_t r_v,
@@ -161,6 +204,14 @@ dl_status dl_lowrank_attn_decode(const void *q, const void *Ck, const void *Cv,
                                  int64_t L_max, float sm_scale,
                                  float rope_theta, dl_dtype dt, void *ws,
                                  size_t ws_bytes, void *stream);
+dl_status dl_lowrank_attn_decode_paged(const void *q, const dl_kv_cache *cache,
+                                       const void *B_k, const void *B_v,
+                                       const int32_t *ctx_lens, void *out,
+                                       int64_t Bsz, int64_t n_q, int64_t n_kv,
+                                       int64_t d, int64_t r_k, int64_t r_v,
+                                       float sm_scale, float rope_theta,
+                                       dl_dtype dt, void *ws, size_t ws_bytes,
+                                       void *stream);
 
 /* ------------------------------------------------------------------------
  * Causal prefill attention over the low-rank cache -- section 4.2.
@@ -168,7 +219,8 @@ dl_status dl_lowrank_attn_decode(const void *q, const void *Ck, const void *Cv,
  * Query t of sequence b sits at position past_lens[b] + t and attends rows
  * 0 .. past_lens[b] + t, which must already hold the latents (append
  * first). Precondition past_lens[b] + T <= L_max. Same shape rules as
- * decode.
+ * decode; DL_BF16 also needs each cache pool (all pages of Ck, or of Cv)
+ * below 2 GiB.
  * ------------------------------------------------------------------------ */
 size_t dl_attn_prefill_workspace(int64_t Bsz, int64_t T, int64_t n_q,
                                  int64_t n_kv, int64_t d, int64_t r_k,
@@ -181,6 +233,14 @@ dl_status dl_lowrank_attn_prefill(const void *q, const void *Ck, const void *Cv,
                                   int64_t r_v, int64_t L_max, float sm_scale,
                                   float rope_theta, dl_dtype dt, void *ws,
                                   size_t ws_bytes, void *stream);
+dl_status dl_lowrank_attn_prefill_paged(const void *q, const dl_kv_cache *cache,
+                                        const void *B_k, const void *B_v,
+                                        const int32_t *past_lens, void *out,
+                                        int64_t Bsz, int64_t T, int64_t n_q,
+                                        int64_t n_kv, int64_t d, int64_t r_k,
+                                        int64_t r_v, float sm_scale,
+                                        float rope_theta, dl_dtype dt, void *ws,
+                                        size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * One decomposed pre-norm transformer layer (LLaMA block; the paper names
@@ -215,11 +275,54 @@ typedef struct {
 
 size_t dl_layer_workspace(const dl_layer *L, int64_t Bsz, int64_t T,
                           int64_t L_max);
+/* The same upper bound under its plain name (L_max = 64 * pages_per_seq for
+ * the paged form); 0 for an invalid layer description. */
+size_t dl_workspace_size(const dl_layer *L, int64_t Bsz, int64_t T,
+                         int64_t L_max);
 dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y,
                                   void *x2_out, void *Ck, void *Cv,
                                   const int32_t *past_lens, int64_t Bsz,
                                   int64_t T, int64_t L_max, void *ws,
                                   size_t ws_bytes, void *stream);
+/* The layer over a paged cache (DL_BF16): appends through the block table,
+ * then attends through it. */
+dl_status dl_decomposed_layer_fwd_paged(const dl_layer *L, const void *x,
+                                        void *y, void *x2_out,
+                                        const dl_kv_cache *cache,
+                                        const int32_t *past_lens, int64_t Bsz,
+                                        int64_t T, void *ws, size_t ws_bytes,
+                                        void *stream);
+
+/* ------------------------------------------------------------------------
+ * Storage conversion from the pages' row-major form (section 2.1, Eq. (1):
+ * A [m, k], B [k, n]; caches [Bsz, L_max, r]) into the library's layouts,
+ * on the GPU, asynchronous on `stream`, into caller-owned buffers (nothing
+ * is allocated). Source and destination must not overlap.
+ *
+ * dl_pack_factor: F [rows, cols] row-major (A: rows = m, cols = k; B: rows =
+ *   k, cols = n) -> its library storage F^T [cols, rows] (operand tiles for
+ *   DL_BF16, plain for DL_F32), dl_factor_bytes(rows, cols, dt) bytes.
+ *   DL_BF16 needs rows % 32 == 0 and cols % 16 == 0 (every factor of a
+ *   DL_BF16 layer or pair, whose sizes are multiples of 64, qualifies).
+ * dl_pack_kv_cache / dl_unpack_kv_cache: Ck [Bsz, L_max, r_k] and
+ *   Cv [Bsz, L_max, r_v], row-major, <-> the contiguous library caches of
+ *   the same shape (layouts above). DL_BF16 needs L_max % 64 == 0 and
+ *   r_k, r_v multiples of 32.
+ * Errors: INVALID_ARG (null pointer, non-positive size, bad dtype),
+ * UNSUPPORTED (sizes above), ALIGNMENT (pointers not 16-byte aligned),
+ * HIP (launch failure).
+ * ------------------------------------------------------------------------ */
+size_t dl_factor_bytes(int64_t rows, int64_t cols, dl_dtype dt);
+dl_status dl_pack_factor(const void *F, int64_t rows, int64_t cols,
+                         dl_dtype dt, void *out, void *stream);
+dl_status dl_pack_kv_cache(const void *Ck, const void *Cv, int64_t Bsz,
+                           int64_t L_max, int64_t r_k, int64_t r_v,
+                           dl_dtype dt, void *Ck_lib, void *Cv_lib,
+                           void *stream);
+dl_status dl_unpack_kv_cache(const void *Ck_lib, const void *Cv_lib,
+                             int64_t Bsz, int64_t L_max, int64_t r_k,
+                             int64_t r_v, dl_dtype dt, void *Ck, void *Cv,
+                             void *stream);
 
 /* ------------------------------------------------------------------------
  * Kernel timing hook (instrumentation; not part of the method).

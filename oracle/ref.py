@@ -32,6 +32,8 @@ Readings where the paper is silent (each also listed in the design notes):
     keys 0..p.
 
 Every function upcasts its inputs to float64 and never rounds internally.
+The paged forms gather each sequence's rows through its block table and
+reuse the contiguous functions unchanged.
 Parity of every function is pinned by tests/test_oracle_pins.py.
 """
 from __future__ import annotations
@@ -214,3 +216,64 @@ def decomposed_layer(factors: Dict[str, Tuple[np.ndarray, np.ndarray]], x, ck, c
     hidden = silu(lowrank_linear(b2, *F["gate"])) * lowrank_linear(b2, *F["up"])
     y = x2 + lowrank_linear(hidden, *F["down"])
     return {"y": y, "x2": x2, "attn": att, "ck": ck2, "cv": cv2}
+
+
+# ----------------------------------------------------------------------------
+# Paged cache (section 4.2, Fig. 4(a)/(b): the cache lives in fixed-size
+# blocks of a pool and a block table lists each sequence's blocks in order)
+# ----------------------------------------------------------------------------
+def paged_gather(pool, table_row, L: int) -> np.ndarray:
+    """Positions 0..L-1 of one sequence from a pool of pages
+    [num_pages, page, r], reading its pages in block-table order: position p
+    is row p % page of pool page table_row[p // page]."""
+    pool = _f(pool)
+    page = pool.shape[1]
+    out = np.zeros((L, pool.shape[2]), dtype=F64)
+    for p in range(L):
+        out[p] = pool[int(table_row[p // page]), p % page]
+    return out
+
+
+def decomposed_layer_paged(factors, x, pool_k, pool_v, table, past_lens, n_q: int,
+                           n_kv: int, head_dim: int, rope_theta: float, rms_eps: float,
+                           attn_norm=None, mlp_norm=None) -> Dict[str, np.ndarray]:
+    """decomposed_layer over a paged cache, one sequence at a time: its
+    past_lens[b] + T rows are gathered through its block-table row (the
+    last T are overwritten by the append), the layer runs on that contiguous
+    cache, and the T appended rows are written back to the pages the table
+    names. Returns y, x2, attn and the updated pools (float64 copies); every
+    other pool row is unchanged."""
+    x = _f(x)
+    Bsz, T, _ = x.shape
+    pk, pv = _f(pool_k).copy(), _f(pool_v).copy()
+    page = pk.shape[1]
+    ys, x2s, atts = [], [], []
+    for b in range(Bsz):
+        past = int(past_lens[b])
+        ck = paged_gather(pk, table[b], past + T)[None]
+        cv = paged_gather(pv, table[b], past + T)[None]
+        out = decomposed_layer(factors, x[b:b + 1], ck, cv, [past], n_q, n_kv, head_dim,
+                               rope_theta, rms_eps, attn_norm=attn_norm, mlp_norm=mlp_norm)
+        for t in range(T):
+            p = past + t
+            pk[int(table[b][p // page]), p % page] = out["ck"][0, p]
+            pv[int(table[b][p // page]), p % page] = out["cv"][0, p]
+        ys.append(out["y"][0])
+        x2s.append(out["x2"][0])
+        atts.append(out["attn"][0])
+    return {"y": np.stack(ys), "x2": np.stack(x2s), "attn": np.stack(atts), "pool_k": pk,
+            "pool_v": pv}
+
+
+def attn_decode_paged(q, pool_k, pool_v, table, B_k, B_v, ctx_lens, n_kv: int, theta: float,
+                      sm_scale: Optional[float] = None) -> np.ndarray:
+    """attn_decode with each sequence's ctx_lens[b] cached rows gathered
+    through its block-table row."""
+    q = _f(q)
+    out = np.zeros_like(q)
+    for b in range(q.shape[0]):
+        L = int(ctx_lens[b])
+        ck = paged_gather(pool_k, table[b], L)[None]
+        cv = paged_gather(pool_v, table[b], L)[None]
+        out[b] = attn_decode(q[b:b + 1], ck, cv, B_k, B_v, [L], n_kv, theta, sm_scale)[0]
+    return out

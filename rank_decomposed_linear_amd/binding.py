@@ -8,10 +8,12 @@ functions raise; there is no fallback.
 
 Storage order is the library's (include/dl.h): every factor is passed
 transposed (At = A^T [k, m], Bt = B^T [n, k]; up factors B_k^T, B_v^T
-[n_kv * d, r]), the key cache is [Bsz, L_max, r_k] and the value cache is
-rank-major, [Bsz, r_v, L_max]; for bf16 each of these matrices is stored in
-16 x 32 operand tiles (workloads.tile_operands gives the order). Shapes are
-read from the tensors, which keep the logical shapes above.
+[n_kv * d, r]) and, for bf16, in 16 x 32 operand tiles; the key cache is
+[Bsz, L_max, r_k]; the value cache is rank-major, for bf16 in 64-position
+pages [Bsz, L_max / 64, r_v, 64] (f32: [Bsz, r_v, L_max]).
+workloads.to_library_* give these orders on the host and pack_factor /
+pack_kv_cache produce them on the GPU from the row-major forms. Sizes are
+read from the tensors: L_max from the key cache, ranks from the factors.
 """
 from __future__ import annotations
 
@@ -33,10 +35,12 @@ EXPORTS = (
     "dl_last_error",
     "dl_lowrank_linear_workspace", "dl_lowrank_linear",
     "dl_lowrank_linear_static",
-    "dl_kv_append_workspace", "dl_lowrank_kv_append",
-    "dl_attn_decode_workspace", "dl_lowrank_attn_decode",
-    "dl_attn_prefill_workspace", "dl_lowrank_attn_prefill",
-    "dl_layer_workspace", "dl_decomposed_layer_fwd",
+    "dl_kv_append_workspace", "dl_lowrank_kv_append", "dl_lowrank_kv_append_paged",
+    "dl_attn_decode_workspace", "dl_lowrank_attn_decode", "dl_lowrank_attn_decode_paged",
+    "dl_attn_prefill_workspace", "dl_lowrank_attn_prefill", "dl_lowrank_attn_prefill_paged",
+    "dl_layer_workspace", "dl_workspace_size", "dl_decomposed_layer_fwd",
+    "dl_decomposed_layer_fwd_paged",
+    "dl_factor_bytes", "dl_pack_factor", "dl_pack_kv_cache", "dl_unpack_kv_cache",
     "dl_trace_install", "dl_kernel_kind_name", "dl_role_name",
     "dl_probe_mfma_bf16",
 )
@@ -60,6 +64,13 @@ class Layer(ctypes.Structure):
                 ("attn_norm", ctypes.c_void_p), ("mlp_norm", ctypes.c_void_p),
                 ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
                 ("dt", ctypes.c_int)]
+
+
+class KvCache(ctypes.Structure):
+    """dl_kv_cache: page pools, block table, pages per sequence, pool size."""
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("pages_per_seq", ctypes.c_int64),
+                ("num_pages", ctypes.c_int64)]
 
 
 class TraceStruct(ctypes.Structure):
@@ -111,6 +122,30 @@ def load() -> ctypes.CDLL:
     lib.dl_decomposed_layer_fwd.restype = ctypes.c_int
     lib.dl_decomposed_layer_fwd.argtypes = [ctypes.POINTER(Layer), _vp, _vp, _vp, _vp, _vp, _vp,
                                             _i64, _i64, _i64, _vp, _sz, _vp]
+    _kc = ctypes.POINTER(KvCache)
+    lib.dl_lowrank_kv_append_paged.restype = ctypes.c_int
+    lib.dl_lowrank_kv_append_paged.argtypes = [_vp, _vp, _vp, _kc, _vp, _i64, _i64, _i64, _i64,
+                                               _i64, ctypes.c_int, _vp, _sz, _vp]
+    lib.dl_lowrank_attn_decode_paged.restype = ctypes.c_int
+    lib.dl_lowrank_attn_decode_paged.argtypes = [_vp, _kc, _vp, _vp, _vp, _vp] + [_i64] * 6 + [
+        _f, _f, ctypes.c_int, _vp, _sz, _vp]
+    lib.dl_lowrank_attn_prefill_paged.restype = ctypes.c_int
+    lib.dl_lowrank_attn_prefill_paged.argtypes = [_vp, _kc, _vp, _vp, _vp, _vp] + [_i64] * 7 + [
+        _f, _f, ctypes.c_int, _vp, _sz, _vp]
+    lib.dl_workspace_size.restype = _sz
+    lib.dl_workspace_size.argtypes = [ctypes.POINTER(Layer), _i64, _i64, _i64]
+    lib.dl_decomposed_layer_fwd_paged.restype = ctypes.c_int
+    lib.dl_decomposed_layer_fwd_paged.argtypes = [ctypes.POINTER(Layer), _vp, _vp, _vp, _kc, _vp,
+                                                  _i64, _i64, _vp, _sz, _vp]
+    lib.dl_factor_bytes.restype = _sz
+    lib.dl_factor_bytes.argtypes = [_i64, _i64, ctypes.c_int]
+    lib.dl_pack_factor.restype = ctypes.c_int
+    lib.dl_pack_factor.argtypes = [_vp, _i64, _i64, ctypes.c_int, _vp, _vp]
+    lib.dl_pack_kv_cache.restype = ctypes.c_int
+    lib.dl_pack_kv_cache.argtypes = [_vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int, _vp, _vp, _vp]
+    lib.dl_unpack_kv_cache.restype = ctypes.c_int
+    lib.dl_unpack_kv_cache.argtypes = [_vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int, _vp, _vp,
+                                       _vp]
     lib.dl_probe_mfma_bf16.restype = ctypes.c_int
     lib.dl_probe_mfma_bf16.argtypes = [_vp, _i64, _i64, _vp]
     lib.dl_trace_install.restype = None
@@ -272,10 +307,10 @@ def lowrank_kv_append(x, A_kt, A_vt, ck, cv, past_lens, ws=None):
 def lowrank_attn_decode(q, ck, cv, B_kt, B_vt, ctx_lens, n_kv, sm_scale=0.0, rope_theta=0.0,
                         out=None, ws=None):
     """q [Bsz, n_q, d] -> out [Bsz, n_q, d] (section 4.2); ck [Bsz, L_max, r_k],
-    cv [Bsz, r_v, L_max], B_kt [n_kv * d, r_k], B_vt [n_kv * d, r_v]."""
+    cv the value cache, B_kt [n_kv * d, r_k], B_vt [n_kv * d, r_v]."""
     lib = load()
     Bsz, n_q, d = q.shape
-    L_max, r_k, r_v = ck.shape[1], ck.shape[2], cv.shape[1]
+    L_max, r_k, r_v = ck.shape[1], B_kt.shape[1], B_vt.shape[1]
     dt = _dt(q)
     if out is None:
         out = torch.empty_like(q)
@@ -294,7 +329,7 @@ def lowrank_attn_prefill(q, ck, cv, B_kt, B_vt, past_lens, n_kv, sm_scale=0.0, r
     cache and factor storage as in lowrank_attn_decode."""
     lib = load()
     Bsz, T, n_q, d = q.shape
-    L_max, r_k, r_v = ck.shape[1], ck.shape[2], cv.shape[1]
+    L_max, r_k, r_v = ck.shape[1], B_kt.shape[1], B_vt.shape[1]
     dt = _dt(q)
     if out is None:
         out = torch.empty_like(q)
@@ -305,6 +340,106 @@ def lowrank_attn_prefill(q, ck, cv, B_kt, B_vt, past_lens, n_kv, sm_scale=0.0, r
                                        L_max, sm_scale, rope_theta, dt, _ptr(ws), ws.numel(),
                                        _stream(q.device)))
     return out
+
+
+def kv_cache(pool_k, pool_v, block_table, num_pages):
+    """dl_kv_cache over device page pools and a device int32 block table
+    [Bsz, pages_per_seq]; keeps the tensors referenced."""
+    c = KvCache(_ptr(pool_k), _ptr(pool_v), _ptr(block_table), block_table.shape[1], num_pages)
+    c._keep = (pool_k, pool_v, block_table)
+    return c
+
+
+def lowrank_kv_append_paged(x, A_kt, A_vt, cache, past_lens, ws=None):
+    """Append T latent rows per sequence through the block table."""
+    lib = load()
+    Bsz, T, m = x.shape
+    r_k, r_v = A_kt.shape[0], A_vt.shape[0]
+    dt = _dt(x)
+    need = lib.dl_kv_append_workspace(Bsz, T, m, r_k, r_v, dt)
+    ws = ws if ws is not None else _ws(need, x.device)
+    _check(lib.dl_lowrank_kv_append_paged(_ptr(x), _ptr(A_kt), _ptr(A_vt), ctypes.byref(cache),
+                                          _ptr(past_lens), Bsz, T, m, r_k, r_v, dt, _ptr(ws),
+                                          ws.numel(), _stream(x.device)))
+
+
+def lowrank_attn_decode_paged(q, cache, B_kt, B_vt, ctx_lens, n_kv, sm_scale=0.0, rope_theta=0.0,
+                              out=None, ws=None):
+    """Decode attention reading the cache through its block table."""
+    lib = load()
+    Bsz, n_q, d = q.shape
+    r_k, r_v = B_kt.shape[1], B_vt.shape[1]
+    dt = _dt(q)
+    if out is None:
+        out = torch.empty_like(q)
+    L_max = cache.pages_per_seq * 64
+    need = lib.dl_attn_decode_workspace(Bsz, n_q, n_kv, d, r_k, r_v, L_max, dt)
+    ws = ws if ws is not None else _ws(need, q.device)
+    _check(lib.dl_lowrank_attn_decode_paged(_ptr(q), ctypes.byref(cache), _ptr(B_kt), _ptr(B_vt),
+                                            _ptr(ctx_lens), _ptr(out), Bsz, n_q, n_kv, d, r_k, r_v,
+                                            sm_scale, rope_theta, dt, _ptr(ws), ws.numel(),
+                                            _stream(q.device)))
+    return out
+
+
+def lowrank_attn_prefill_paged(q, cache, B_kt, B_vt, past_lens, n_kv, sm_scale=0.0,
+                               rope_theta=0.0, out=None, ws=None):
+    """Causal prefill attention reading the cache through its block table."""
+    lib = load()
+    Bsz, T, n_q, d = q.shape
+    r_k, r_v = B_kt.shape[1], B_vt.shape[1]
+    dt = _dt(q)
+    if out is None:
+        out = torch.empty_like(q)
+    L_max = cache.pages_per_seq * 64
+    need = lib.dl_attn_prefill_workspace(Bsz, T, n_q, n_kv, d, r_k, r_v, L_max, dt)
+    ws = ws if ws is not None else _ws(need, q.device)
+    _check(lib.dl_lowrank_attn_prefill_paged(_ptr(q), ctypes.byref(cache), _ptr(B_kt), _ptr(B_vt),
+                                             _ptr(past_lens), _ptr(out), Bsz, T, n_q, n_kv, d, r_k,
+                                             r_v, sm_scale, rope_theta, dt, _ptr(ws), ws.numel(),
+                                             _stream(q.device)))
+    return out
+
+
+def factor_bytes(rows, cols, dtype) -> int:
+    return load().dl_factor_bytes(rows, cols, DL_BF16 if dtype == torch.bfloat16 else DL_F32)
+
+
+def pack_factor(F, out=None):
+    """Library storage of F [rows, cols] row-major (A [m, k] or B [k, n]):
+    F^T [cols, rows], operand-tiled for bf16 (dl_pack_factor)."""
+    rows, cols = F.shape
+    if out is None:
+        out = torch.empty((cols, rows), dtype=F.dtype, device=F.device)
+    _check(load().dl_pack_factor(_ptr(F), rows, cols, _dt(F), _ptr(out), _stream(F.device)))
+    return out
+
+
+def pack_kv_cache(ck, cv, ck_lib=None, cv_lib=None):
+    """Row-major caches ck [Bsz, L_max, r_k], cv [Bsz, L_max, r_v] -> the
+    library's contiguous caches (dl_pack_kv_cache)."""
+    Bsz, L_max, r_k = ck.shape
+    r_v = cv.shape[2]
+    dt = _dt(ck)
+    if ck_lib is None:
+        ck_lib = torch.empty_like(ck)
+    if cv_lib is None:
+        shape = (Bsz, L_max // 64, r_v, 64) if dt == DL_BF16 else (Bsz, r_v, L_max)
+        cv_lib = torch.empty(shape, dtype=cv.dtype, device=cv.device)
+    _check(load().dl_pack_kv_cache(_ptr(ck), _ptr(cv), Bsz, L_max, r_k, r_v, dt, _ptr(ck_lib),
+                                   _ptr(cv_lib), _stream(ck.device)))
+    return ck_lib, cv_lib
+
+
+def unpack_kv_cache(ck_lib, cv_lib, r_v):
+    """Inverse of pack_kv_cache: row-major [Bsz, L_max, r] copies."""
+    Bsz, L_max, r_k = ck_lib.shape
+    dt = _dt(ck_lib)
+    ck = torch.empty_like(ck_lib)
+    cv = torch.empty((Bsz, L_max, r_v), dtype=cv_lib.dtype, device=cv_lib.device)
+    _check(load().dl_unpack_kv_cache(_ptr(ck_lib), _ptr(cv_lib), Bsz, L_max, r_k, r_v, dt,
+                                     _ptr(ck), _ptr(cv), _stream(ck_lib.device)))
+    return ck, cv
 
 
 class DecomposedLayer:
@@ -335,7 +470,21 @@ class DecomposedLayer:
         self.device = factors["q"][0].device
 
     def workspace_bytes(self, Bsz, T, L_max) -> int:
-        return load().dl_layer_workspace(ctypes.byref(self.desc), Bsz, T, L_max)
+        return load().dl_workspace_size(ctypes.byref(self.desc), Bsz, T, L_max)
+
+    def forward_paged(self, x, cache, past_lens, y=None, x2_out=None, ws=None, stream=None):
+        """The layer over a paged cache (KvCache from kv_cache())."""
+        lib = load()
+        Bsz, T, _ = x.shape
+        if y is None:
+            y = torch.empty_like(x)
+        if ws is None:
+            ws = _ws(self.workspace_bytes(Bsz, T, cache.pages_per_seq * 64), x.device)
+        s = stream.cuda_stream if stream is not None else _stream(x.device)
+        _check(lib.dl_decomposed_layer_fwd_paged(ctypes.byref(self.desc), _ptr(x), _ptr(y),
+                                                 _ptr(x2_out), ctypes.byref(cache),
+                                                 _ptr(past_lens), Bsz, T, _ptr(ws), ws.numel(), s))
+        return y
 
     def forward(self, x, ck, cv, past_lens, y=None, x2_out=None, ws=None, stream=None):
         """y = layer(x) for x [Bsz, T, hidden]; appends T latent rows per

@@ -258,10 +258,8 @@ dl_status check_attn_shape(int64_t n_q, int64_t n_kv, int64_t d, int64_t r_k, in
              "bf16 attention needs r_k, r_v multiples of 64");
     DL_CHECK(r_v <= attn_decode_max_rank_v(), DL_ERR_UNSUPPORTED,
              "bf16 attention needs r_v <= %d", attn_decode_max_rank_v());
-    DL_CHECK(L_max % 32 == 0, DL_ERR_UNSUPPORTED,
-             "bf16 caches need L_max to be a multiple of 32 (operand tiles)");
-    DL_CHECK(L_max * std::max(r_k, r_v) < ((int64_t)1 << 31), DL_ERR_UNSUPPORTED,
-             "bf16 attention needs L_max * r < 2^31 per sequence");
+    DL_CHECK(L_max % kPage == 0, DL_ERR_UNSUPPORTED,
+             "bf16 caches need L_max to be a multiple of %d (cache pages)", kPage);
     const int64_t G = n_q / n_kv;
     DL_CHECK(G <= 16, DL_ERR_UNSUPPORTED, "bf16 attention needs n_q / n_kv <= 16");
     if (prefill)
@@ -273,21 +271,73 @@ dl_status check_attn_shape(int64_t n_q, int64_t n_kv, int64_t d, int64_t r_k, in
   return DL_OK;
 }
 
+// A latent cache as the kernels see it: two page pools, an optional block
+// table and the pages per sequence (see cache_page in common.h). A contiguous
+// bf16 cache of L_max rows per sequence is the same thing with the identity
+// table: L_max / kPage pages per sequence, sequence b's pages consecutive.
+struct CacheRef {
+  void *k = nullptr, *v = nullptr;
+  const int32_t *table = nullptr;
+  int stride = 0;           // pages per sequence (table row length)
+  int64_t pool_pages = 0;   // pages in each pool
+  int64_t L_max = 0;        // positions per sequence = stride * kPage (bf16)
+};
+
+CacheRef contiguous_cache(void *Ck, void *Cv, int64_t Bsz, int64_t L_max) {
+  CacheRef c;
+  c.k = Ck;
+  c.v = Cv;
+  c.stride = static_cast<int>(L_max / kPage);
+  c.pool_pages = Bsz * (L_max / kPage);
+  c.L_max = L_max;
+  return c;
+}
+
+// Checks a paged cache descriptor and converts it (bf16 only).
+dl_status paged_cache(const dl_kv_cache *pc, dl_dtype dt, CacheRef *out) {
+  DL_CHECK(pc, DL_ERR_INVALID_ARG, "null cache descriptor");
+  DL_CHECK(dt == DL_BF16, DL_ERR_UNSUPPORTED, "paged caches are bf16 only");
+  DL_CHECK(pc->k && pc->v && pc->block_table, DL_ERR_INVALID_ARG, "null cache pointer");
+  DL_CHECK(pc->pages_per_seq > 0 && pc->num_pages > 0, DL_ERR_INVALID_ARG,
+           "pages_per_seq and num_pages must be positive");
+  DL_CHECK(pc->pages_per_seq <= (1 << 24) && pc->num_pages <= INT32_MAX, DL_ERR_UNSUPPORTED,
+           "page counts too large");
+  DL_CHECK(aligned16(pc->k) && aligned16(pc->v) && aligned16(pc->block_table), DL_ERR_ALIGNMENT,
+           "cache pointers must be 16-byte aligned");
+  out->k = pc->k;
+  out->v = pc->v;
+  out->table = pc->block_table;
+  out->stride = static_cast<int>(pc->pages_per_seq);
+  out->pool_pages = pc->num_pages;
+  out->L_max = pc->pages_per_seq * kPage;
+  return DL_OK;
+}
+
+// Prefill attention addresses each pool with 32-bit byte offsets.
+dl_status check_prefill_pools(const CacheRef &c, int64_t r_k, int64_t r_v) {
+  DL_CHECK(c.pool_pages * kPage * std::max(r_k, r_v) * 2 <= INT32_MAX, DL_ERR_UNSUPPORTED,
+           "bf16 prefill attention needs each cache pool below 2 GiB");
+  return DL_OK;
+}
+
 // Runs the bf16 attention kernels; q is bf16 (q_f32 = 0) or f32. For
 // decode, w.counters must be zero.
-hipError_t run_attn_bf16(const void *q, int q_f32, int ldq, const void *Ck, const void *Cv,
+hipError_t run_attn_bf16(const void *q, int q_f32, int ldq, const CacheRef &c,
                          const void *B_k, const void *B_v, const int32_t *lens, int ctx_offset,
                          bool decode, void *out, int out_f32, int out_tiled, int Bsz, int T,
-                         int n_q, int n_kv, int d, int r_k, int r_v, int L_max, float sm_scale,
+                         int n_q, int n_kv, int d, int r_k, int r_v, float sm_scale,
                          float theta, const AttnWS &w, hipStream_t s) {
   const float scale = (sm_scale != 0.f ? sm_scale : 1.0f / sqrtf(static_cast<float>(d))) * kLog2e;
+  const int L_max = static_cast<int>(c.L_max);
   if (decode) {
     const DecodePlan p = plan_decode(Bsz, n_kv, L_max);
     AttnDecodeArgs a{};
     a.q = q;
     a.q_f32 = q_f32;
-    a.ck = static_cast<const uint16_t *>(Ck);
-    a.cv = static_cast<const uint16_t *>(Cv);
+    a.ck = static_cast<const uint16_t *>(c.k);
+    a.cv = static_cast<const uint16_t *>(c.v);
+    a.block_table = c.table;
+    a.page_stride = c.stride;
     a.bk = static_cast<const uint16_t *>(B_k);
     a.bv = static_cast<const uint16_t *>(B_v);
     a.ctx_lens = lens;
@@ -314,8 +364,11 @@ hipError_t run_attn_bf16(const void *q, int q_f32, int ldq, const void *Ck, cons
   a.q = q;
   a.q_f32 = q_f32;
   a.ldq = ldq;
-  a.ck = static_cast<const uint16_t *>(Ck);
-  a.cv = static_cast<const uint16_t *>(Cv);
+  a.ck = static_cast<const uint16_t *>(c.k);
+  a.cv = static_cast<const uint16_t *>(c.v);
+  a.block_table = c.table;
+  a.page_stride = c.stride;
+  a.pool_pages = c.pool_pages;
   a.bk = static_cast<const uint16_t *>(B_k);
   a.bv = static_cast<const uint16_t *>(B_v);
   a.past_lens = lens;
@@ -524,15 +577,15 @@ dl_status dl_lowrank_linear_static(const void *x, const void *A, const void *B, 
 // ===========================================================================
 // dl_lowrank_kv_append
 // ===========================================================================
-static GvArgs append_gemv(int M, int m, int rk, int rv, int T, int L_max, const void *x,
-                          const void *A_k, const void *A_v, void *Ck, void *Cv,
-                          const int32_t *past) {
+static GvArgs append_gemv(int M, int m, int rk, int rv, int T, const CacheRef &cache,
+                          const void *x, const void *A_k, const void *A_v, const int32_t *past) {
   GvArgs a = gvargs(M, m, 2);
   a.past = past;
   a.T = T;
-  a.L_max = L_max;
-  a.seg[0] = gvseg(A_k, x, m, Ck, rk, rk, GV_OUT_CACHE);
-  a.seg[1] = gvseg(A_v, x, m, Cv, rv, rv, GV_OUT_CACHE_T);
+  a.block_table = cache.table;
+  a.page_stride = cache.stride;
+  a.seg[0] = gvseg(A_k, x, m, cache.k, rk, rk, GV_OUT_CACHE);
+  a.seg[1] = gvseg(A_v, x, m, cache.v, rv, rv, GV_OUT_CACHE_T);
   return a;
 }
 
@@ -541,8 +594,8 @@ size_t dl_kv_append_workspace(int64_t Bsz, int64_t T, int64_t m, int64_t r_k, in
   if (Bsz <= 0 || T <= 0 || m <= 0 || r_k <= 0 || r_v <= 0) return 0;
   const int64_t M = Bsz * T;
   if (dt == DL_BF16 && use_gemv(static_cast<int>(M))) {
-    GvArgs a = append_gemv((int)M, (int)m, (int)r_k, (int)r_v, (int)T, 1, nullptr, nullptr,
-                           nullptr, nullptr, nullptr, nullptr);
+    GvArgs a = append_gemv((int)M, (int)m, (int)r_k, (int)r_v, (int)T, CacheRef{}, nullptr,
+                           nullptr, nullptr, nullptr);
     GvScratch sc;
     sc.add(a);
     Carver c(nullptr);
@@ -553,13 +606,12 @@ size_t dl_kv_append_workspace(int64_t Bsz, int64_t T, int64_t m, int64_t r_k, in
   return 0;
 }
 
-dl_status dl_lowrank_kv_append(const void *x, const void *A_k, const void *A_v, void *Ck,
-                               void *Cv, const int32_t *past_lens, int64_t Bsz, int64_t T,
-                               int64_t m, int64_t r_k, int64_t r_v, int64_t L_max, dl_dtype dt,
-                               void *ws, size_t ws_bytes, void *stream) {
-  set_role(R_OTHER);
-  DL_CHECK(valid_dtype(dt), DL_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
-  DL_CHECK(x && A_k && A_v && Ck && Cv && past_lens, DL_ERR_INVALID_ARG, "null pointer");
+static dl_status kv_append_impl(const void *x, const void *A_k, const void *A_v,
+                                const CacheRef &cache, const int32_t *past_lens, int64_t Bsz,
+                                int64_t T, int64_t m, int64_t r_k, int64_t r_v, dl_dtype dt,
+                                void *ws, size_t ws_bytes, void *stream) {
+  const int64_t L_max = cache.L_max;
+  DL_CHECK(x && A_k && A_v && cache.k && cache.v && past_lens, DL_ERR_INVALID_ARG, "null pointer");
   DL_CHECK(Bsz > 0 && T > 0 && m > 0 && r_k > 0 && r_v > 0 && L_max > 0, DL_ERR_INVALID_ARG,
            "dims must be positive");
   DL_CHECK(T <= L_max, DL_ERR_INVALID_ARG, "T exceeds L_max");
@@ -568,11 +620,11 @@ dl_status dl_lowrank_kv_append(const void *x, const void *A_k, const void *A_v, 
   if (dt == DL_BF16) {
     DL_CHECK(m % 64 == 0 && r_k % 64 == 0 && r_v % 64 == 0, DL_ERR_UNSUPPORTED,
              "bf16 append needs m, r_k, r_v multiples of 64");
-    DL_CHECK(L_max % 32 == 0, DL_ERR_UNSUPPORTED,
-             "bf16 caches need L_max to be a multiple of 32 (operand tiles)");
+    DL_CHECK(L_max % kPage == 0, DL_ERR_UNSUPPORTED,
+             "bf16 caches need L_max to be a multiple of %d (cache pages)", kPage);
   }
-  DL_CHECK(aligned16(x) && aligned16(A_k) && aligned16(A_v) && aligned16(Ck) && aligned16(Cv) &&
-               aligned16(past_lens),
+  DL_CHECK(aligned16(x) && aligned16(A_k) && aligned16(A_v) && aligned16(cache.k) &&
+               aligned16(cache.v) && aligned16(past_lens),
            DL_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
   const size_t need = dl_kv_append_workspace(Bsz, T, m, r_k, r_v, dt);
   DL_CHECK(need == 0 || (ws && aligned16(ws) && ws_bytes >= need), DL_ERR_WORKSPACE,
@@ -581,14 +633,14 @@ dl_status dl_lowrank_kv_append(const void *x, const void *A_k, const void *A_v, 
   const int M = static_cast<int>(Bsz * T), mi = static_cast<int>(m), rk = static_cast<int>(r_k),
             rv = static_cast<int>(r_v), Ti = static_cast<int>(T), Lm = static_cast<int>(L_max);
   if (dt == DL_F32) {
-    DL_HIP(gemm_f32(static_cast<const float *>(x), nullptr, A_k, static_cast<float *>(Ck), M, rk,
-                    mi, mi, rk, F32_OUT_CACHE, nullptr, 0, past_lens, Ti, Lm, s));
-    DL_HIP(gemm_f32(static_cast<const float *>(x), nullptr, A_v, static_cast<float *>(Cv), M, rv,
-                    mi, mi, rv, F32_OUT_CACHE_T, nullptr, 0, past_lens, Ti, Lm, s));
+    DL_HIP(gemm_f32(static_cast<const float *>(x), nullptr, A_k, static_cast<float *>(cache.k), M,
+                    rk, mi, mi, rk, F32_OUT_CACHE, nullptr, 0, past_lens, Ti, Lm, s));
+    DL_HIP(gemm_f32(static_cast<const float *>(x), nullptr, A_v, static_cast<float *>(cache.v), M,
+                    rv, mi, mi, rv, F32_OUT_CACHE_T, nullptr, 0, past_lens, Ti, Lm, s));
     return DL_OK;
   }
   if (use_gemv(M)) {
-    GvArgs a = append_gemv(M, mi, rk, rv, Ti, Lm, x, A_k, A_v, Ck, Cv, past_lens);
+    GvArgs a = append_gemv(M, mi, rk, rv, Ti, cache, x, A_k, A_v, past_lens);
     GvScratch sc;
     sc.add(a);
     Carver c(ws);
@@ -607,12 +659,36 @@ dl_status dl_lowrank_kv_append(const void *x, const void *A_k, const void *A_v, 
   a.omode = GEMM_OUT_CACHE;
   a.past_lens = past_lens;
   a.T = Ti;
-  a.L_max = Lm;
-  a.seg[0] = mseg(A_k, x, Ck, rk, mi, rk);
-  a.seg[1] = mseg(A_v, x, Cv, rv, mi, rv);
+  a.block_table = cache.table;
+  a.page_stride = cache.stride;
+  a.seg[0] = mseg(A_k, x, cache.k, rk, mi, rk);
+  a.seg[1] = mseg(A_v, x, cache.v, rv, mi, rv);
   a.seg[1].omode = GEMM_OUT_CACHE_T;
   DL_HIP(gemm(a, s));
   return DL_OK;
+}
+
+dl_status dl_lowrank_kv_append(const void *x, const void *A_k, const void *A_v, void *Ck,
+                               void *Cv, const int32_t *past_lens, int64_t Bsz, int64_t T,
+                               int64_t m, int64_t r_k, int64_t r_v, int64_t L_max, dl_dtype dt,
+                               void *ws, size_t ws_bytes, void *stream) {
+  set_role(R_OTHER);
+  DL_CHECK(valid_dtype(dt), DL_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  DL_CHECK(Bsz > 0 && L_max > 0, DL_ERR_INVALID_ARG, "dims must be positive");
+  return kv_append_impl(x, A_k, A_v, contiguous_cache(Ck, Cv, Bsz, L_max), past_lens, Bsz, T, m,
+                        r_k, r_v, dt, ws, ws_bytes, stream);
+}
+
+dl_status dl_lowrank_kv_append_paged(const void *x, const void *A_k, const void *A_v,
+                                     const dl_kv_cache *cache, const int32_t *past_lens,
+                                     int64_t Bsz, int64_t T, int64_t m, int64_t r_k, int64_t r_v,
+                                     dl_dtype dt, void *ws, size_t ws_bytes, void *stream) {
+  set_role(R_OTHER);
+  DL_CHECK(valid_dtype(dt), DL_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  CacheRef c;
+  const dl_status st = paged_cache(cache, dt, &c);
+  if (st != DL_OK) return st;
+  return kv_append_impl(x, A_k, A_v, c, past_lens, Bsz, T, m, r_k, r_v, dt, ws, ws_bytes, stream);
 }
 
 // ===========================================================================
@@ -635,14 +711,13 @@ size_t dl_attn_prefill_workspace(int64_t Bsz, int64_t T, int64_t n_q, int64_t n_
   return attn_bf16_ws(Bsz, n_q, n_kv, d, L_max, false);
 }
 
-static dl_status attn_common(const void *q, const void *Ck, const void *Cv, const void *B_k,
+static dl_status attn_common(const void *q, const CacheRef &cache, const void *B_k,
                              const void *B_v, const int32_t *lens, void *out, int64_t Bsz,
                              int64_t T, int64_t n_q, int64_t n_kv, int64_t d, int64_t r_k,
-                             int64_t r_v, int64_t L_max, float sm_scale, float rope_theta,
+                             int64_t r_v, float sm_scale, float rope_theta,
                              dl_dtype dt, void *ws, size_t ws_bytes, void *stream, bool decode) {
-  set_role(R_OTHER);
-  DL_CHECK(valid_dtype(dt), DL_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
-  DL_CHECK(q && Ck && Cv && B_k && B_v && lens && out, DL_ERR_INVALID_ARG, "null pointer");
+  const int64_t L_max = cache.L_max;
+  DL_CHECK(q && cache.k && cache.v && B_k && B_v && lens && out, DL_ERR_INVALID_ARG, "null pointer");
   DL_CHECK(Bsz > 0 && T > 0 && L_max > 0, DL_ERR_INVALID_ARG, "dims must be positive");
   DL_CHECK(T <= L_max, DL_ERR_INVALID_ARG, "T exceeds L_max");
   dl_status st = check_attn_shape(n_q, n_kv, d, r_k, r_v, L_max, dt, !decode);
@@ -652,9 +727,13 @@ static dl_status attn_common(const void *q, const void *Ck, const void *Cv, cons
            DL_ERR_UNSUPPORTED, "dims too large");
   DL_CHECK(isfinite(sm_scale) && sm_scale >= 0.f && isfinite(rope_theta) && rope_theta >= 0.f,
            DL_ERR_INVALID_ARG, "sm_scale and rope_theta must be finite and non-negative");
-  DL_CHECK(aligned16(q) && aligned16(Ck) && aligned16(Cv) && aligned16(B_k) && aligned16(B_v) &&
-               aligned16(lens) && aligned16(out),
+  DL_CHECK(aligned16(q) && aligned16(cache.k) && aligned16(cache.v) && aligned16(B_k) &&
+               aligned16(B_v) && aligned16(lens) && aligned16(out),
            DL_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+  if (dt == DL_BF16 && !decode) {
+    st = check_prefill_pools(cache, r_k, r_v);
+    if (st != DL_OK) return st;
+  }
   const size_t need = decode ? dl_attn_decode_workspace(Bsz, n_q, n_kv, d, r_k, r_v, L_max, dt)
                              : dl_attn_prefill_workspace(Bsz, T, n_q, n_kv, d, r_k, r_v, L_max, dt);
   DL_CHECK(need == 0 || (ws && aligned16(ws) && ws_bytes >= need), DL_ERR_WORKSPACE,
@@ -663,8 +742,8 @@ static dl_status attn_common(const void *q, const void *Ck, const void *Cv, cons
   if (dt == DL_F32) {
     AttnF32Args a{};
     a.q = static_cast<const float *>(q);
-    a.ck = static_cast<const float *>(Ck);
-    a.cv = static_cast<const float *>(Cv);
+    a.ck = static_cast<const float *>(cache.k);
+    a.cv = static_cast<const float *>(cache.v);
     a.bk = static_cast<const float *>(B_k);
     a.bv = static_cast<const float *>(B_v);
     a.lens = lens;
@@ -690,10 +769,10 @@ static dl_status attn_common(const void *q, const void *Ck, const void *Cv, cons
     FillRegion z[1] = {{reinterpret_cast<float *>(aw.counters), nullptr, 0, aw.n_counters}};
     DL_HIP(launch_fill(z, 1, s));
   }
-  DL_HIP(run_attn_bf16(q, 0, static_cast<int>(n_q * d), Ck, Cv, B_k, B_v, lens, 0, decode, out, 0, 0,
+  DL_HIP(run_attn_bf16(q, 0, static_cast<int>(n_q * d), cache, B_k, B_v, lens, 0, decode, out, 0, 0,
                        static_cast<int>(Bsz), static_cast<int>(T), static_cast<int>(n_q),
                        static_cast<int>(n_kv), static_cast<int>(d), static_cast<int>(r_k),
-                       static_cast<int>(r_v), static_cast<int>(L_max), sm_scale, rope_theta, aw, s));
+                       static_cast<int>(r_v), sm_scale, rope_theta, aw, s));
   return DL_OK;
 }
 
@@ -702,8 +781,12 @@ dl_status dl_lowrank_attn_decode(const void *q, const void *Ck, const void *Cv, 
                                  int64_t n_q, int64_t n_kv, int64_t d, int64_t r_k, int64_t r_v,
                                  int64_t L_max, float sm_scale, float rope_theta, dl_dtype dt,
                                  void *ws, size_t ws_bytes, void *stream) {
-  return attn_common(q, Ck, Cv, B_k, B_v, ctx_lens, out, Bsz, 1, n_q, n_kv, d, r_k, r_v, L_max,
-                     sm_scale, rope_theta, dt, ws, ws_bytes, stream, true);
+  set_role(R_OTHER);
+  DL_CHECK(valid_dtype(dt), DL_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  DL_CHECK(Bsz > 0 && L_max > 0, DL_ERR_INVALID_ARG, "dims must be positive");
+  return attn_common(q, contiguous_cache(const_cast<void *>(Ck), const_cast<void *>(Cv), Bsz, L_max),
+                     B_k, B_v, ctx_lens, out, Bsz, 1, n_q, n_kv, d, r_k, r_v, sm_scale,
+                     rope_theta, dt, ws, ws_bytes, stream, true);
 }
 
 dl_status dl_lowrank_attn_prefill(const void *q, const void *Ck, const void *Cv, const void *B_k,
@@ -712,8 +795,42 @@ dl_status dl_lowrank_attn_prefill(const void *q, const void *Ck, const void *Cv,
                                   int64_t r_k, int64_t r_v, int64_t L_max, float sm_scale,
                                   float rope_theta, dl_dtype dt, void *ws, size_t ws_bytes,
                                   void *stream) {
-  return attn_common(q, Ck, Cv, B_k, B_v, past_lens, out, Bsz, T, n_q, n_kv, d, r_k, r_v, L_max,
-                     sm_scale, rope_theta, dt, ws, ws_bytes, stream, false);
+  set_role(R_OTHER);
+  DL_CHECK(valid_dtype(dt), DL_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  DL_CHECK(Bsz > 0 && L_max > 0, DL_ERR_INVALID_ARG, "dims must be positive");
+  return attn_common(q, contiguous_cache(const_cast<void *>(Ck), const_cast<void *>(Cv), Bsz, L_max),
+                     B_k, B_v, past_lens, out, Bsz, T, n_q, n_kv, d, r_k, r_v, sm_scale,
+                     rope_theta, dt, ws, ws_bytes, stream, false);
+}
+
+dl_status dl_lowrank_attn_decode_paged(const void *q, const dl_kv_cache *cache, const void *B_k,
+                                       const void *B_v, const int32_t *ctx_lens, void *out,
+                                       int64_t Bsz, int64_t n_q, int64_t n_kv, int64_t d,
+                                       int64_t r_k, int64_t r_v, float sm_scale,
+                                       float rope_theta, dl_dtype dt, void *ws, size_t ws_bytes,
+                                       void *stream) {
+  set_role(R_OTHER);
+  DL_CHECK(valid_dtype(dt), DL_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  CacheRef c;
+  const dl_status st = paged_cache(cache, dt, &c);
+  if (st != DL_OK) return st;
+  return attn_common(q, c, B_k, B_v, ctx_lens, out, Bsz, 1, n_q, n_kv, d, r_k, r_v, sm_scale,
+                     rope_theta, dt, ws, ws_bytes, stream, true);
+}
+
+dl_status dl_lowrank_attn_prefill_paged(const void *q, const dl_kv_cache *cache, const void *B_k,
+                                        const void *B_v, const int32_t *past_lens, void *out,
+                                        int64_t Bsz, int64_t T, int64_t n_q, int64_t n_kv,
+                                        int64_t d, int64_t r_k, int64_t r_v, float sm_scale,
+                                        float rope_theta, dl_dtype dt, void *ws, size_t ws_bytes,
+                                        void *stream) {
+  set_role(R_OTHER);
+  DL_CHECK(valid_dtype(dt), DL_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  CacheRef c;
+  const dl_status st = paged_cache(cache, dt, &c);
+  if (st != DL_OK) return st;
+  return attn_common(q, c, B_k, B_v, past_lens, out, Bsz, T, n_q, n_kv, d, r_k, r_v, sm_scale,
+                     rope_theta, dt, ws, ws_bytes, stream, false);
 }
 
 // ===========================================================================
@@ -791,20 +908,21 @@ enum { G_QKV, G_QUP, G_ODOWN, G_OUP, G_GUD, G_GUU, G_DD, G_DU, G_NUM };
 //   down_down H A_down
 //   down_up   y = x2 + t_d B_down
 static void layer_gemvs(const dl_layer *L, const LayerDims &D, const LayerWS &w, const void *x,
-                        void *y, void *x2_out, void *Ck, void *Cv, const int32_t *past,
+                        void *y, void *x2_out, const CacheRef &cache, const int32_t *past,
                         GvArgs (&g)[G_NUM]) {
   const int M = D.M, h = D.h, qd = D.qd();
   const int gf32 = L->dt == DL_F32;
   g[G_QKV] = gvargs(M, h, 3);
   g[G_QKV].past = past;
   g[G_QKV].T = D.T;
-  g[G_QKV].L_max = D.L_max;
+  g[G_QKV].block_table = cache.table;
+  g[G_QKV].page_stride = cache.stride;
   // x arrives row-major; the step's init launch normalises it into operand tiles
   (void)x;
   g[G_QKV].x_tiled = 1;
   g[G_QKV].seg[0] = gvseg_t(L->q.A, w.a16t, h, w.tq16, D.rq, D.rq, GV_OUT_TILED);
-  g[G_QKV].seg[1] = gvseg_t(L->k.A, w.a16t, h, Ck, D.rk, D.rk, GV_OUT_CACHE);
-  g[G_QKV].seg[2] = gvseg_t(L->v.A, w.a16t, h, Cv, D.rv, D.rv, GV_OUT_CACHE_T);
+  g[G_QKV].seg[1] = gvseg_t(L->k.A, w.a16t, h, cache.k, D.rk, D.rk, GV_OUT_CACHE);
+  g[G_QKV].seg[2] = gvseg_t(L->v.A, w.a16t, h, cache.v, D.rv, D.rv, GV_OUT_CACHE_T);
 
   g[G_QUP] = gvargs(M, D.rq, 1);
   g[G_QUP].x_tiled = 1;
@@ -872,7 +990,7 @@ static void carve_layer(Carver &c, const LayerDims &D, const dl_layer *L, LayerW
   if (use_gemv(D.M)) {
     GvArgs g[G_NUM];
     LayerWS none{};
-    layer_gemvs(L, D, none, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, g);
+    layer_gemvs(L, D, none, nullptr, nullptr, nullptr, CacheRef{}, nullptr, g);
     GvScratch sc;
     for (GvArgs &a : g) sc.add(a);
     w.n_counters = sc.counters;
@@ -918,21 +1036,25 @@ size_t dl_layer_workspace(const dl_layer *L, int64_t Bsz, int64_t T, int64_t L_m
   return c.off;
 }
 
-dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, void *x2_out,
-                                  void *Ck, void *Cv, const int32_t *past_lens, int64_t Bsz,
-                                  int64_t T, int64_t L_max, void *ws, size_t ws_bytes,
-                                  void *stream) {
-  set_role(R_OTHER);
+static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_out,
+                            const CacheRef &cache, const int32_t *past_lens, int64_t Bsz,
+                            int64_t T, void *ws, size_t ws_bytes, void *stream) {
+  const int64_t L_max = cache.L_max;
   LayerDims D{};
   dl_status st = layer_dims(L, Bsz, T, L_max, &D);
   if (st != DL_OK) return st;
-  DL_CHECK(x && y && Ck && Cv && past_lens, DL_ERR_INVALID_ARG, "null pointer");
+  DL_CHECK(x && y && cache.k && cache.v && past_lens, DL_ERR_INVALID_ARG, "null pointer");
+  void *Ck = cache.k, *Cv = cache.v;
   const dl_factor *fs[7] = {&L->q, &L->k, &L->v, &L->o, &L->gate, &L->up, &L->down};
   bool al = aligned16(x) && aligned16(y) && aligned16(Ck) && aligned16(Cv) && aligned16(past_lens);
   for (const dl_factor *f : fs) al = al && aligned16(f->A) && aligned16(f->B);
   al = al && (!x2_out || aligned16(x2_out)) && (!L->attn_norm || aligned16(L->attn_norm)) &&
        (!L->mlp_norm || aligned16(L->mlp_norm));
   DL_CHECK(al, DL_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+  if (L->dt == DL_BF16 && T > 1) {
+    st = check_prefill_pools(cache, L->k.k, L->v.k);
+    if (st != DL_OK) return st;
+  }
   const size_t need = dl_layer_workspace(L, Bsz, T, L_max);
   DL_CHECK(ws && aligned16(ws) && ws_bytes >= need, DL_ERR_WORKSPACE,
            "workspace of %zu bytes required, %zu given", need, ws_bytes);
@@ -1014,7 +1136,7 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
 
   if (use_gemv(M)) {
     GvArgs g[G_NUM];
-    layer_gemvs(L, D, w, x, y, x2_out, Ck, Cv, past_lens, g);
+    layer_gemvs(L, D, w, x, y, x2_out, cache, past_lens, g);
     FillRegion zero[2] = {{reinterpret_cast<float *>(w.counters), nullptr, 0, w.n_counters},
                           {reinterpret_cast<float *>(aw.counters), nullptr, 0, aw.n_counters}};
     set_role(R_INIT);
@@ -1026,8 +1148,8 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
     set_role(R_Q_UP);
     DL_HIP(gemv_run(g[G_QUP], w.part, w.counters, s));
     set_role(R_ATTENTION);
-    DL_HIP(run_attn_bf16(w.q32, 1, qd, Ck, Cv, L->k.B, L->v.B, past_lens, 1, D.T == 1, w.att16, 0,
-                         D.T == 1 ? 1 : 0, D.Bsz, D.T, D.nq, D.nkv, D.d, D.rk, D.rv, D.L_max, 0.f,
+    DL_HIP(run_attn_bf16(w.q32, 1, qd, cache, L->k.B, L->v.B, past_lens, 1, D.T == 1, w.att16, 0,
+                         D.T == 1 ? 1 : 0, D.Bsz, D.T, D.nq, D.nkv, D.d, D.rk, D.rv, 0.f,
                          L->rope_theta, aw, s));
     set_role(R_O_DOWN);
     DL_HIP(gemv_run(g[G_ODOWN], w.part, w.counters, s));
@@ -1057,7 +1179,8 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
     a.omode = GEMM_OUT_BF16;
     a.past_lens = past_lens;
     a.T = D.T;
-    a.L_max = D.L_max;
+    a.block_table = cache.table;
+    a.page_stride = cache.stride;
     a.seg[0] = mseg(L->q.A, w.a16, w.tq16, D.rq, h, D.rq);
     a.seg[1] = mseg(L->k.A, w.a16, Ck, D.rk, h, D.rk);
     a.seg[1].omode = GEMM_OUT_CACHE;
@@ -1081,9 +1204,8 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
     DL_HIP(launch_fill(z, 1, s));
     set_role(R_ATTENTION);
   }
-  DL_HIP(run_attn_bf16(w.q16, 0, qd, Ck, Cv, L->k.B, L->v.B, past_lens, 1, D.T == 1, w.att16, 0, 0,
-                       D.Bsz, D.T, D.nq, D.nkv, D.d, D.rk, D.rv, D.L_max, 0.f, L->rope_theta, aw,
-                       s));
+  DL_HIP(run_attn_bf16(w.q16, 0, qd, cache, L->k.B, L->v.B, past_lens, 1, D.T == 1, w.att16, 0, 0,
+                       D.Bsz, D.T, D.nq, D.nkv, D.d, D.rk, D.rv, 0.f, L->rope_theta, aw, s));
   {
     GemmArgs a{};
     a.nseg = 1;
@@ -1163,6 +1285,91 @@ dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, voi
     DL_HIP(gemm(b, s));
   }
   return DL_OK;
+}
+
+dl_status dl_decomposed_layer_fwd(const dl_layer *L, const void *x, void *y, void *x2_out,
+                                  void *Ck, void *Cv, const int32_t *past_lens, int64_t Bsz,
+                                  int64_t T, int64_t L_max, void *ws, size_t ws_bytes,
+                                  void *stream) {
+  set_role(R_OTHER);
+  DL_CHECK(L, DL_ERR_INVALID_ARG, "null layer");
+  DL_CHECK(Bsz > 0 && L_max > 0, DL_ERR_INVALID_ARG, "Bsz, T, L_max must be positive");
+  return layer_impl(L, x, y, x2_out, contiguous_cache(Ck, Cv, Bsz, L_max), past_lens, Bsz, T, ws,
+                    ws_bytes, stream);
+}
+
+dl_status dl_decomposed_layer_fwd_paged(const dl_layer *L, const void *x, void *y, void *x2_out,
+                                        const dl_kv_cache *cache, const int32_t *past_lens,
+                                        int64_t Bsz, int64_t T, void *ws, size_t ws_bytes,
+                                        void *stream) {
+  set_role(R_OTHER);
+  DL_CHECK(L, DL_ERR_INVALID_ARG, "null layer");
+  CacheRef c;
+  const dl_status st = paged_cache(cache, L->dt, &c);
+  if (st != DL_OK) return st;
+  return layer_impl(L, x, y, x2_out, c, past_lens, Bsz, T, ws, ws_bytes, stream);
+}
+
+size_t dl_workspace_size(const dl_layer *L, int64_t Bsz, int64_t T, int64_t L_max) {
+  return dl_layer_workspace(L, Bsz, T, L_max);
+}
+
+// ===========================================================================
+// Storage conversion
+// ===========================================================================
+size_t dl_factor_bytes(int64_t rows, int64_t cols, dl_dtype dt) {
+  if (rows <= 0 || cols <= 0 || !valid_dtype(dt)) return 0;
+  return static_cast<size_t>(rows * cols) * (dt == DL_BF16 ? 2 : 4);
+}
+
+dl_status dl_pack_factor(const void *F, int64_t rows, int64_t cols, dl_dtype dt, void *out,
+                         void *stream) {
+  set_role(R_OTHER);
+  DL_CHECK(valid_dtype(dt), DL_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  DL_CHECK(F && out, DL_ERR_INVALID_ARG, "null pointer");
+  DL_CHECK(rows > 0 && cols > 0, DL_ERR_INVALID_ARG, "dims must be positive");
+  DL_CHECK(rows <= INT32_MAX && cols <= INT32_MAX && rows * cols <= ((int64_t)1 << 34),
+           DL_ERR_UNSUPPORTED, "dims too large");
+  if (dt == DL_BF16)
+    DL_CHECK(rows % 32 == 0 && cols % 16 == 0, DL_ERR_UNSUPPORTED,
+             "bf16 factor storage needs rows %% 32 == 0 and cols %% 16 == 0");
+  DL_CHECK(aligned16(F) && aligned16(out), DL_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+  DL_HIP(launch_pack_factor(F, static_cast<int>(rows), static_cast<int>(cols), dt == DL_BF16, out,
+                            as_stream(stream)));
+  return DL_OK;
+}
+
+static dl_status pack_cache_common(const void *k_src, const void *v_src, int64_t Bsz, int64_t L_max,
+                                   int64_t r_k, int64_t r_v, dl_dtype dt, void *k_dst,
+                                   void *v_dst, void *stream, int unpack) {
+  set_role(R_OTHER);
+  DL_CHECK(valid_dtype(dt), DL_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  DL_CHECK(k_src && v_src && k_dst && v_dst, DL_ERR_INVALID_ARG, "null pointer");
+  DL_CHECK(Bsz > 0 && L_max > 0 && r_k > 0 && r_v > 0, DL_ERR_INVALID_ARG, "dims must be positive");
+  DL_CHECK(Bsz * L_max <= INT32_MAX && r_k <= INT32_MAX && r_v <= INT32_MAX &&
+               Bsz * L_max * std::max(r_k, r_v) <= ((int64_t)1 << 36),
+           DL_ERR_UNSUPPORTED, "dims too large");
+  if (dt == DL_BF16)
+    DL_CHECK(L_max % kPage == 0 && r_k % 32 == 0 && r_v % 32 == 0, DL_ERR_UNSUPPORTED,
+             "bf16 caches need L_max %% %d == 0 and r_k, r_v multiples of 32", kPage);
+  DL_CHECK(aligned16(k_src) && aligned16(v_src) && aligned16(k_dst) && aligned16(v_dst),
+           DL_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+  hipStream_t s = as_stream(stream);
+  const int B = static_cast<int>(Bsz), Lm = static_cast<int>(L_max);
+  DL_HIP(launch_pack_cache(k_src, k_dst, B, Lm, static_cast<int>(r_k), 0, unpack, dt == DL_BF16, s));
+  DL_HIP(launch_pack_cache(v_src, v_dst, B, Lm, static_cast<int>(r_v), 1, unpack, dt == DL_BF16, s));
+  return DL_OK;
+}
+
+dl_status dl_pack_kv_cache(const void *Ck, const void *Cv, int64_t Bsz, int64_t L_max, int64_t r_k,
+                           int64_t r_v, dl_dtype dt, void *Ck_lib, void *Cv_lib, void *stream) {
+  return pack_cache_common(Ck, Cv, Bsz, L_max, r_k, r_v, dt, Ck_lib, Cv_lib, stream, 0);
+}
+
+dl_status dl_unpack_kv_cache(const void *Ck_lib, const void *Cv_lib, int64_t Bsz, int64_t L_max,
+                             int64_t r_k, int64_t r_v, dl_dtype dt, void *Ck, void *Cv,
+                             void *stream) {
+  return pack_cache_common(Ck_lib, Cv_lib, Bsz, L_max, r_k, r_v, dt, Ck, Cv, stream, 1);
 }
 
 }  // extern "C"

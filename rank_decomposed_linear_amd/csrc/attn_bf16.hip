@@ -5,8 +5,10 @@
 // Neither K nor V is ever written to memory. Caches and factors are stored
 // in 16 x 32 operand tiles (MFMA lane order): a key block of 16 positions x
 // 32 ranks and an up-factor fragment are each one contiguous 1 KB read; the
-// value cache is rank-major ([r_v, L_max] tiles per sequence) and gathered
-// per key. The rebuilt tiles live in MFMA accumulators:
+// caches are held in pages of 64 positions (a key page [64, r_k], a value
+// page rank-major [r_v, 64]) reached through the sequence's block table or
+// contiguously, and a 64-key tile is exactly one page. The rebuilt tiles
+// live in MFMA accumulators:
 //
 //  prefill  A workgroup owns one kv head and up to 256 (token, head) query
 //           rows; per 64-key tile its eight waves rebuild K (rotated) and
@@ -162,17 +164,17 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
   const int rsk = a.r_k / 32, rsv = a.r_v / 32;
   const int nchunk = max((rsk + RS - 1) / RS, (rsv + RS - 1) / RS);
   const int nsteps = nkt * nchunk;
-  const uint16_t *ck_b = a.ck + static_cast<size_t>(b) * a.L_max * a.r_k;
-  const uint16_t *cv_b = a.cv + static_cast<size_t>(b) * a.r_v * a.L_max;
-  const int kb_last = a.L_max / 16 - 1, ps_last = a.L_max / 32 - 1;
 
   // ---- staging: unit i of this thread is u = tid + 512 i, fragment
   // (u - group start) / 64, lane `lane`. Keys past the last query position
   // stage zeros (their V rows must not leak NaN into P V). ----
-  // Buffer loads: one scalar resource per array, the lane's 16 bytes as the
-  // only vector offset, the (wave-uniform) fragment offset as soffset.
-  const __amdgpu_buffer_rsrc_t rck = make_rsrc(ck_b, a.L_max * a.r_k * 2);
-  const __amdgpu_buffer_rsrc_t rcv = make_rsrc(cv_b, a.r_v * a.L_max * 2);
+  // Buffer loads: one scalar resource per array (the cache resources span the
+  // page pools, whose byte size the launcher bounds below 2^31), the lane's
+  // 16 bytes as the only vector offset, the (wave-uniform) fragment offset as
+  // soffset. A 64-key tile is one cache page; tiles start at or before the
+  // last query position, so their page is always one the sequence owns.
+  const __amdgpu_buffer_rsrc_t rck = make_rsrc(a.ck, static_cast<int>(a.pool_pages * kPage * a.r_k * 2));
+  const __amdgpu_buffer_rsrc_t rcv = make_rsrc(a.cv, static_cast<int>(a.pool_pages * kPage * a.r_v * 2));
   const __amdgpu_buffer_rsrc_t rbk = make_rsrc(a.bk, a.n_kv * D * a.r_k * 2);
   const __amdgpu_buffer_rsrc_t rbv = make_rsrc(a.bv, a.n_kv * D * a.r_v * 2);
   const int lane16 = lane * 16;
@@ -180,17 +182,19 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
   auto gload = [&](int kt, int c) {
     const int k0 = kt * KT, r0 = c * RS;
     const int nrk = rsk - r0, nrv = rsv - r0;
+    const int pg = __builtin_amdgcn_readfirstlane(cache_page(a.block_table, a.page_stride, b, kt));
+    const int kpage = pg * (kPage * a.r_k), vpage = pg * (kPage * a.r_v);   // element offsets
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
       const u32x4 z = {0u, 0u, 0u, 0u};
       if (i < I_CV) {
         const int f = wave + 8 * i, kb = f / RS, rs = f % RS;
         const bool ok = rs < nrk && k0 + 16 * kb + j <= qmax_pos;
-        const int so = 2 * static_cast<int>(frag_off(min((k0 >> 4) + kb, kb_last), r0 + rs, a.r_k, 0));
+        const int so = 2 * (kpage + static_cast<int>(frag_off(kb, r0 + rs, a.r_k, 0)));
         st[i] = ok ? bload(rck, lane16, so) : z;
       } else if (i < I_BK) {
         const int f = wave + 8 * (i - I_CV), rb = f >> 1, ps = f & 1;
-        const int so = 2 * static_cast<int>(frag_off(2 * r0 + rb, min((k0 >> 5) + ps, ps_last), a.L_max, 0));
+        const int so = 2 * (vpage + static_cast<int>(frag_off(2 * r0 + rb, ps, kPage, 0)));
         st[i] = rb < 2 * nrv ? bload(rcv, lane16, so) : z;
       } else if (i < I_BV) {
         const int f = wave + 8 * (i - I_BK), db = f / RS, rs = f % RS;
@@ -412,10 +416,10 @@ hipError_t launch_attn_prefill_bf16(const AttnPrefillArgs &a, hipStream_t s) {
   TraceGuard trace_guard(K_ATTN_PREFILL, s);
   const int G = a.n_q / a.n_kv;
   const int QT = 256 / G;
-  // the kernel addresses one sequence's caches and each factor through
-  // 32-bit buffer offsets
+  // the kernel addresses the cache pools and each factor through 32-bit
+  // buffer offsets
   const int64_t lim = INT32_MAX;
-  if (static_cast<int64_t>(a.L_max) * std::max(a.r_k, a.r_v) * 2 > lim ||
+  if (a.pool_pages * kPage * std::max(a.r_k, a.r_v) * 2 > lim ||
       static_cast<int64_t>(a.n_kv) * a.d * std::max(a.r_k, a.r_v) * 2 > lim)
     return hipErrorInvalidValue;
   dim3 grid((a.T + QT - 1) / QT, a.n_kv, a.Bsz);

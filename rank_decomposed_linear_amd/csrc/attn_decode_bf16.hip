@@ -12,9 +12,10 @@
 // waves (one per SIMD, so each wave has the whole register file for deep
 // software pipelining). Per work item:
 //  * Factors and caches are stored in 16 x 32 operand tiles (1 KB, MFMA
-//    lane order): B_k^T / B_v^T as [n_kv * d, r], the key cache per
-//    sequence as [L_max, r_k], the value cache per sequence as
-//    [r_v, L_max]. Every operand fragment below is one contiguous 1 KB read.
+//    lane order): B_k^T / B_v^T as [n_kv * d, r]; the caches in pages of 64
+//    positions, a key page as [64, r_k], a value page as [r_v, 64], reached
+//    through the sequence's block table (or contiguously). Every operand
+//    fragment below is one contiguous 1 KB read.
 //  * The B_k^T tiles of head g are copied once into LDS, fragment (rank
 //    step rs, d block x) = dimensions 16x .. 16x+15. The rotary partner of
 //    dimension 16x + i is 16(x + d/32) + i: same lane, same register of the
@@ -145,8 +146,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
   const int n_tail = rs_tail > 0 ? (nrs - rs_cap + rs_tail - 1) / rs_tail : 0;
   const int nrb = a.r_v / 16;
   const int pitch = a.pitch;   // positions per chunk, a multiple of the slice
-  const uint16_t *cv_b = a.cv + static_cast<size_t>(b) * a.r_v * a.L_max;
-  const uint16_t *ck_b = a.ck + static_cast<size_t>(b) * a.L_max * a.r_k;
+  // cache pages of this sequence: key page = [kPage, r_k] tiles, value page
+  // = [r_v, kPage] tiles (a position's page is looked up once per 16- or
+  // 32-position block; the page index is uniform across the wave)
+  auto page_of = [&](int p64) {
+    return __builtin_amdgcn_readfirstlane(cache_page(a.block_table, a.page_stride, b, p64));
+  };
 
   // up-factor fragments of rank steps [rs0, rs0 + cnt) -> dst[rs - rs0][x][lane][8]
   uint16_t *bs_tail = bs + static_cast<size_t>(rs_cap) * NB * 64 * 8;
@@ -259,14 +264,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
     const int b_lo = min(wave * share, nblk), b_hi = min(b_lo + share, nblk);
     float mx = -INFINITY;
     const int ngr = (share + kNP - 1) / kNP;   // same count in every wave
-    // key-tile rows of group gi (element offsets within the sequence's
-    // cache, L_max * r < 2^31); blocks past the wave's range repeat its
-    // last block, are multiplied only inside a group of four and never scored
-    int crow[kNP];
+    // key tiles of group gi: the first rank step of each 16-position block
+    // (wave-uniform base; the lane's 16 bytes are added at the load); blocks
+    // past the wave's range repeat its last block, are multiplied only
+    // inside a group of four and never scored
+    const uint16_t *kblk[kNP];
     auto set_rows = [&](int gi) {
 #pragma unroll
-      for (int pb = 0; pb < kNP; ++pb)
-        crow[pb] = static_cast<int>(frag_off((c0 >> 4) + min(b_lo + kNP * gi + pb, max(b_hi - 1, 0)), 0, a.r_k, lane));
+      for (int pb = 0; pb < kNP; ++pb) {
+        const int kb = (c0 >> 4) + min(b_lo + kNP * gi + pb, max(b_hi - 1, 0));
+        kblk[pb] = a.ck + static_cast<size_t>(page_of(kb >> 2)) * (kPage * a.r_k) +
+                   frag_off(kb & 3, 0, a.r_k, 0);
+      }
     };
     for (int gi = 0; gi < ngr; ++gi) {
       const int g0 = b_lo + kNP * gi;
@@ -308,7 +317,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
 #pragma unroll
           for (int d = 0; d < kCDepth; ++d)
 #pragma unroll
-            for (int pb = 0; pb < NPA; ++pb) cf[d][pb] = ld16(ck_b + crow[pb] + 512 * (rs0 + min(d, cnt - 1)));
+            for (int pb = 0; pb < NPA; ++pb) cf[d][pb] = ld16(kblk[pb] + lane * 8 + 512 * (rs0 + min(d, cnt - 1)));
           // factor fragments one rank step ahead
           u32x4 bop[2][NB];
 #pragma unroll
@@ -331,7 +340,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
               for (int x = 0; x < NB; ++x) acc[x][pb] = mfma_bf16(bop[d & 1][x], cf[d][pb], acc[x][pb]);
             const int sn = rs0 + min(s + kCDepth, cnt - 1);
 #pragma unroll
-            for (int pb = 0; pb < NPA; ++pb) cf[d][pb] = ld16(ck_b + crow[pb] + 512 * sn);
+            for (int pb = 0; pb < NPA; ++pb) cf[d][pb] = ld16(kblk[pb] + lane * 8 + 512 * sn);
 #pragma unroll
             for (int pb = 0; pb < NPA; ++pb) {
 #pragma unroll
@@ -406,8 +415,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
     // now. A operand: lane (rank row j, grp) = C_v^T[16 rb + j][c0 + 32u + 8grp ..+8]
     const int nU = (c1 - c0 + 31) >> 5;
     auto vload = [&](u32x4 (&dst)[RBW], int u) {
+      // 32-position group (c0 >> 5) + u: column step of its page
+      const int pg32 = (c0 >> 5) + u;
+      const uint16_t *vb = a.cv + static_cast<size_t>(page_of(pg32 >> 1)) * (kPage * a.r_v) +
+                           (pg32 & 1) * 512 + lane * 8;
 #pragma unroll
-      for (int i = 0; i < RBW; ++i) dst[i] = ld16(cv_b + frag_off(rb[i], (c0 >> 5) + u, a.L_max, lane));
+      for (int i = 0; i < RBW; ++i) dst[i] = ld16(vb + rb[i] * 1024);
     };
     u32x4 vr[kVDepth][RBW];
 #pragma unroll

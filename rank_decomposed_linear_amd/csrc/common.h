@@ -63,6 +63,25 @@ __device__ __forceinline__ size_t frag_off(int rb, int cs, int C, int lane) {
   return (static_cast<size_t>(rb) * (C >> 5) + cs) * 512 + lane * 8;
 }
 
+// Latent caches (bf16) are stored in pages of kPage positions. A key page
+// holds [kPage, r_k] in operand tiles (kPage * r_k elements, rows =
+// positions); a value page holds [r_v, kPage] in operand tiles (kPage * r_v
+// elements, rows = rank components). Logical page p of sequence b is pool
+// page table[b * stride + p]; without a table (a contiguous cache) it is
+// page b * stride + p.
+constexpr int kPage = 64;
+__device__ __forceinline__ int cache_page(const int32_t *table, int stride, int b, int p) {
+  return table ? table[b * stride + p] : b * stride + p;
+}
+// element offsets of key latent (pos, r) and value latent (pos, n) in a pool
+// whose position pos lies on pool page `page`
+__device__ __forceinline__ size_t key_off(int page, int pos, int r, int r_k) {
+  return static_cast<size_t>(page) * (kPage * r_k) + tile_off(pos & (kPage - 1), r, r_k);
+}
+__device__ __forceinline__ size_t val_off(int page, int pos, int n, int r_v) {
+  return static_cast<size_t>(page) * (kPage * r_v) + tile_off(n, pos & (kPage - 1), kPage);
+}
+
 // Pack the four accumulator values of two 16x16 blocks into one operand
 // register set: slots 0..3 from `x`, 4..7 from `y`.
 __device__ __forceinline__ u32x4 pack_acc(f32x4 x, f32x4 y) {

@@ -177,15 +177,16 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
         const f32x4 hi = *reinterpret_cast<const f32x4 *>(ep + rr * kEpPitch + c8 + 4);
         float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         if (om == GEMM_OUT_CACHE || om == GEMM_OUT_CACHE_T) {
-          // key cache tiled [L_max, N] / value cache tiled [N, L_max], per sequence
+          // key cache page [kPage, N] / value cache page [N, kPage], operand tiles
           const int b = m / a.T, pos = a.past_lens[b] + (m - b * a.T);
-          uint16_t *seq = static_cast<uint16_t *>(sg.C) + static_cast<size_t>(b) * sg.N * a.L_max;
+          const int pg = cache_page(a.block_table, a.page_stride, b, pos / kPage);
+          uint16_t *pool = static_cast<uint16_t *>(sg.C);
           if (om == GEMM_OUT_CACHE) {
-            *reinterpret_cast<u32x4 *>(seq + tile_off(pos, n, sg.N)) =
+            *reinterpret_cast<u32x4 *>(pool + key_off(pg, pos, n, sg.N)) =
                 u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
           } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) seq[tile_off(n + e, pos, a.L_max)] = f2bf(v[e]);
+            for (int e = 0; e < 8; ++e) pool[val_off(pg, pos, n + e, sg.N)] = f2bf(v[e]);
           }
           continue;
         }

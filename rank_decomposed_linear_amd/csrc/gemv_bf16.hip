@@ -323,18 +323,19 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
       *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(sg.out) + tile_off(m, n, sg.N)) =
           u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
       break;
-    case GV_OUT_CACHE: {   // key cache: [L_max, N] operand tiles per sequence
-      const int b = m / a.T, t = m - b * a.T;
-      uint16_t *seq = static_cast<uint16_t *>(sg.out) + static_cast<size_t>(b) * a.L_max * sg.N;
-      *reinterpret_cast<u32x2 *>(seq + tile_off(a.past[b] + t, n, sg.N)) =
+    case GV_OUT_CACHE: {   // key cache page: [kPage, N] operand tiles
+      const int b = m / a.T, pos = a.past[b] + m - b * a.T;
+      const int pg = cache_page(a.block_table, a.page_stride, b, pos / kPage);
+      *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(sg.out) + key_off(pg, pos, n, sg.N)) =
           u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
       break;
     }
-    case GV_OUT_CACHE_T: {   // value cache: [N, L_max] operand tiles per sequence
-      const int b = m / a.T, t = m - b * a.T;
-      uint16_t *seq = static_cast<uint16_t *>(sg.out) + static_cast<size_t>(b) * sg.N * a.L_max;
+    case GV_OUT_CACHE_T: {   // value cache page: [N, kPage] operand tiles
+      const int b = m / a.T, pos = a.past[b] + m - b * a.T;
+      const int pg = cache_page(a.block_table, a.page_stride, b, pos / kPage);
+      uint16_t *pool = static_cast<uint16_t *>(sg.out);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) seq[tile_off(n + r, a.past[b] + t, a.L_max)] = f2bf(v[r]);
+      for (int r = 0; r < 4; ++r) pool[val_off(pg, pos, n + r, sg.N)] = f2bf(v[r]);
       break;
     }
     case GV_OUT_RES_F32: {

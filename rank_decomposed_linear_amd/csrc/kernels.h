@@ -20,8 +20,8 @@ namespace dl {
 enum GvOut : int {
   GV_OUT_BF16 = 0,      // out bf16 [m * ldo + n] = v
   GV_OUT_F32 = 1,       // out f32 [m * ldo + n] = v
-  GV_OUT_CACHE = 2,     // key cache: sequence b = m / T, tiled [L_max, N], row past[b] + t
-  GV_OUT_CACHE_T = 6,   // value cache: sequence b, tiled [N, L_max], column past[b] + t
+  GV_OUT_CACHE = 2,     // key cache page of sequence b = m / T, position past[b] + t
+  GV_OUT_CACHE_T = 6,   // value cache page of sequence b, position past[b] + t
   GV_OUT_TILED = 7,     // out bf16 operand tiles [Mpad, N]
   GV_OUT_RES_F32 = 3,   // out f32 = v + R (R f32 if res_f32, else bf16); out2 gets a copy
   GV_OUT_RES_BF16 = 4,  // out bf16 = v + R (R f32)
@@ -60,8 +60,10 @@ struct GvArgs {
   const float *rs_part;
   int rs_cols;
   float eps;
-  const int32_t *past;    // cache scatter (GV_OUT_CACHE)
-  int T, L_max;
+  const int32_t *past;    // cache scatter (GV_OUT_CACHE / _T)
+  int T;
+  const int32_t *block_table;  // cache pages (cache_page in common.h); NULL: contiguous
+  int page_stride;             // table row length (contiguous: L_max / kPage)
   // set by gemv_plan / the caller
   int ntiles, ksplit, split_steps;   // ntiles: work items (groups of rtiles tiles) per split
   int rtiles;             // 16-row tiles per work item (1, 2 or 4)
@@ -87,8 +89,8 @@ enum GemmOut : int {
   GEMM_OUT_BF16 = 0,        // C bf16 [M, ldc]
   GEMM_OUT_BF16_RES_F32 = 1,// C bf16 = acc + R (f32 [M, ldr]); also C32 (f32) if non-null
   GEMM_OUT_F32_RES_BF16 = 2,// C32 f32 = acc + R (bf16 [M, ldr])
-  GEMM_OUT_CACHE = 3,       // key cache: row b*T+t -> tiled [L_max, N] of sequence b, row past[b]+t
-  GEMM_OUT_CACHE_T = 4,     // value cache: row b*T+t, column n -> tiled [N, L_max], (n, past[b]+t)
+  GEMM_OUT_CACHE = 3,       // key cache: row b*T+t -> sequence b, position past[b]+t
+  GEMM_OUT_CACHE_T = 4,     // value cache: row b*T+t, column n -> sequence b, (position past[b]+t, rank n)
   GEMM_OUT_SWIGLU = 5       // C bf16 = silu(R) * acc, R bf16 [M, ldr] (the gate values; C may be R)
 };
 
@@ -110,7 +112,9 @@ struct GemmArgs {
   int xmode, omode;   // omode: default for segments whose own omode is < 0
   // cache scatter
   const int32_t *past_lens;
-  int T, L_max;
+  int T;
+  const int32_t *block_table;  // cache pages; NULL: contiguous
+  int page_stride;
   int tiles_m, tiles_n;  // set by the launcher
 };
 
@@ -123,8 +127,10 @@ int gemm_ntiles(int N);
 // ---------------------------------------------------------------------------
 struct AttnDecodeArgs {
   const void *q;       // [Bsz, n_q, d] bf16 or f32 (q_f32)
-  const uint16_t *ck;  // key cache, per sequence [L_max, r_k] in operand tiles
-  const uint16_t *cv;  // value cache, per sequence [r_v, L_max] in operand tiles
+  const uint16_t *ck;  // key cache pool (pages of [kPage, r_k] operand tiles)
+  const uint16_t *cv;  // value cache pool (pages of [r_v, kPage] operand tiles)
+  const int32_t *block_table;  // NULL: contiguous, page_stride pages per sequence
+  int page_stride;
   const uint16_t *bk, *bv;  // up factors, [n_kv * d, r] in operand tiles
   const int32_t *ctx_lens;
   void *out;           // [Bsz, n_q, d] bf16 (or f32 with out_f32); out_tiled: bf16
@@ -147,8 +153,11 @@ hipError_t launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s);
 
 struct AttnPrefillArgs {
   const void *q;       // [Bsz, T, n_q, d] bf16 or f32
-  const uint16_t *ck;  // key cache, per sequence [L_max, r_k] in operand tiles
-  const uint16_t *cv;  // value cache, per sequence [r_v, L_max] in operand tiles
+  const uint16_t *ck;  // key cache pool (pages of [kPage, r_k] operand tiles)
+  const uint16_t *cv;  // value cache pool (pages of [r_v, kPage] operand tiles)
+  const int32_t *block_table;  // NULL: contiguous, page_stride pages per sequence
+  int page_stride;
+  int64_t pool_pages;  // pages in each pool (bounds the 32-bit buffer offsets)
   const uint16_t *bk, *bv;  // [n_kv * d, r] in operand tiles
   const int32_t *past_lens;
   uint16_t *out;       // [Bsz, T, n_q*d]
@@ -222,6 +231,14 @@ hipError_t launch_norm_tiles(const uint16_t *x, const void *gamma, int gamma_f32
                              hipStream_t s);
 // Matrix-pipe issue-rate probe (dl_probe_mfma_bf16)
 hipError_t launch_mfma_probe(float *sink, int blocks, int iters, hipStream_t s);
+
+// Storage conversion (pack.hip). Factor: F [rows, cols] row-major -> F^T
+// (bf16 operand tiles: rows % 32 == 0, cols % 16 == 0). Cache: one cache
+// [Bsz, L_max, r] row-major <-> library pages (bf16: L_max % kPage == 0,
+// r % 32 == 0); value = 1 for the value cache, unpack = 1 for the inverse.
+hipError_t launch_pack_factor(const void *F, int rows, int cols, int bf16, void *out, hipStream_t s);
+hipError_t launch_pack_cache(const void *src, void *dst, int Bsz, int L_max, int r, int value,
+                             int unpack, int bf16, hipStream_t s);
 
 // dst (bf16 or f32) = src f32
 hipError_t launch_convert_f32(const float *src, void *dst, int dst_bf16, int64_t n, hipStream_t s);

@@ -358,18 +358,74 @@ def from_library_key_cache(ck: np.ndarray, bf16: bool) -> np.ndarray:
     return untile_operands(ck) if bf16 else np.ascontiguousarray(ck)
 
 
+#: positions per cache page of the bf16 caches
+PAGE = 64
+
+
+def to_library_key_pages(pool: np.ndarray) -> np.ndarray:
+    """Key-latent pages [..., PAGE, r_k] (bf16 bits) -> library key pages:
+    each page's [PAGE, r_k] matrix in operand-tile order."""
+    return tile_operands(pool)
+
+
+def to_library_value_pages(pool: np.ndarray) -> np.ndarray:
+    """Value-latent pages [..., PAGE, r_v] (bf16 bits) -> library value
+    pages [..., r_v, PAGE]: each page rank-major, in operand-tile order."""
+    return tile_operands(np.ascontiguousarray(np.swapaxes(pool, -1, -2)))
+
+
+def from_library_key_pages(t: np.ndarray) -> np.ndarray:
+    """Inverse of to_library_key_pages."""
+    return untile_operands(t)
+
+
+def from_library_value_pages(t: np.ndarray) -> np.ndarray:
+    """Inverse of to_library_value_pages."""
+    return np.ascontiguousarray(np.swapaxes(untile_operands(t), -1, -2))
+
+
 def to_library_value_cache(cv: np.ndarray) -> np.ndarray:
-    """Value latents [Bsz, L, r_v] -> the library's rank-major value cache
-    [Bsz, r_v, L], per sequence in operand-tile order for bf16
-    (L % 32 == 0)."""
-    t = np.ascontiguousarray(np.swapaxes(cv, -1, -2))
-    return tile_operands(t) if cv.dtype == np.uint16 else t
+    """Value latents [Bsz, L, r_v] -> the library's value cache. bf16: pages
+    of PAGE positions, each rank-major [r_v, PAGE] in operand-tile order,
+    stored [Bsz, L / PAGE, r_v, PAGE] (L % PAGE == 0); f32: rank-major
+    [Bsz, r_v, L]."""
+    if cv.dtype == np.uint16:
+        Bsz, L, r = cv.shape
+        return to_library_value_pages(cv.reshape(Bsz, L // PAGE, PAGE, r))
+    return np.ascontiguousarray(np.swapaxes(cv, -1, -2))
 
 
 def from_library_value_cache(cv_t: np.ndarray, bf16: bool) -> np.ndarray:
     """Inverse of to_library_value_cache."""
-    t = untile_operands(cv_t) if bf16 else cv_t
-    return np.ascontiguousarray(np.swapaxes(t, -1, -2))
+    if bf16:
+        Bsz, P, r, _ = cv_t.shape
+        return from_library_value_pages(cv_t).reshape(Bsz, P * PAGE, r)
+    return np.ascontiguousarray(np.swapaxes(cv_t, -1, -2))
+
+
+# ----------------------------------------------------------------------------
+# Paged caches (data movement only)
+# ----------------------------------------------------------------------------
+def random_block_table(rng: np.random.Generator, Bsz: int, pages_per_seq: int,
+                       num_pages: int) -> np.ndarray:
+    """A block table [Bsz, pages_per_seq] whose entries are distinct pool
+    pages drawn at random from range(num_pages) (num_pages >= Bsz *
+    pages_per_seq): no sequence's pages are contiguous or ordered."""
+    if num_pages < Bsz * pages_per_seq:
+        raise ValueError("pool too small")
+    return rng.permutation(num_pages)[:Bsz * pages_per_seq].astype(np.int32).reshape(
+        Bsz, pages_per_seq)
+
+
+def scatter_to_pages(cache: np.ndarray, table: np.ndarray, pool: np.ndarray) -> np.ndarray:
+    """Copy contiguous latents [Bsz, P * PAGE, r] into pool pages
+    [num_pages, PAGE, r] following the block table; returns the pool."""
+    Bsz, L, r = cache.shape
+    pool = pool.copy()
+    for b in range(Bsz):
+        for p in range(L // PAGE):
+            pool[table[b, p]] = cache[b, p * PAGE:(p + 1) * PAGE]
+    return pool
 
 
 def random_array(rng: np.random.Generator, shape, std: float, dtype: str) -> np.ndarray:

@@ -80,23 +80,23 @@ def test_lowrank_linear_static_validation(lib):
 
 def test_kv_append_validation(lib):
     f = lib.dl_lowrank_kv_append
-    assert f(P, P, P, P, P, None, 2, 1, 64, 64, 64, 32, B.DL_BF16, P, 1 << 20, None) == INVALID
-    assert f(P, P, P, P, P, P, 2, 33, 64, 64, 64, 32, B.DL_BF16, P, 1 << 20, None) == INVALID
-    assert f(P, P, P, P, P, P, 2, 1, 64, 96, 64, 32, B.DL_BF16, P, 1 << 20, None) == UNSUPPORTED
-    # bf16 caches are operand tiles: L_max must be a multiple of 32
+    assert f(P, P, P, P, P, None, 2, 1, 64, 64, 64, 64, B.DL_BF16, P, 1 << 20, None) == INVALID
+    assert f(P, P, P, P, P, P, 2, 65, 64, 64, 64, 64, B.DL_BF16, P, 1 << 20, None) == INVALID
+    assert f(P, P, P, P, P, P, 2, 1, 64, 96, 64, 64, B.DL_BF16, P, 1 << 20, None) == UNSUPPORTED
+    # bf16 caches are 64-position pages: L_max must be a multiple of 64
     assert f(P, P, P, P, P, P, 2, 1, 64, 64, 64, 40, B.DL_BF16, P, 1 << 20, None) == UNSUPPORTED
-    assert "operand tiles" in err(lib)
-    assert f(P, P, P, BAD, P, P, 2, 1, 64, 64, 64, 32, B.DL_BF16, P, 1 << 20, None) == ALIGN
+    assert "cache pages" in err(lib)
+    assert f(P, P, P, BAD, P, P, 2, 1, 64, 64, 64, 64, B.DL_BF16, P, 1 << 20, None) == ALIGN
     need = lib.dl_kv_append_workspace(2, 1, 64, 64, 64, B.DL_BF16)
-    assert f(P, P, P, P, P, P, 2, 1, 64, 64, 64, 32, B.DL_BF16, P, need - 1, None) == WORKSPACE
+    assert f(P, P, P, P, P, P, 2, 1, 64, 64, 64, 64, B.DL_BF16, P, need - 1, None) == WORKSPACE
 
 
 def test_attention_validation(lib):
     dec = lib.dl_lowrank_attn_decode
-    args = dict(Bsz=2, n_q=8, n_kv=2, d=128, r_k=64, r_v=64, L=32)
+    args = dict(Bsz=2, n_q=8, n_kv=2, d=128, r_k=64, r_v=64, L=64)
 
     def call(q=P, n_q=8, n_kv=2, d=128, r_k=64, r_v=64, dt=B.DL_BF16, ws=1 << 24, wsp=P,
-             scale=0.0, theta=10000.0, L_max=32):
+             scale=0.0, theta=10000.0, L_max=64):
         return dec(q, P, P, P, P, P, P, 2, n_q, n_kv, d, r_k, r_v, L_max, scale, theta, dt, wsp, ws,
                    None)
 
@@ -105,7 +105,7 @@ def test_attention_validation(lib):
     assert "multiple of n_kv" in err(lib)
     assert call(d=96) == UNSUPPORTED
     assert call(r_k=100) == UNSUPPORTED
-    assert call(L_max=48) == UNSUPPORTED                # bf16 cache tiles need L_max % 32
+    assert call(L_max=96) == UNSUPPORTED                # bf16 cache pages need L_max % 64
     assert call(r_v=1088) == UNSUPPORTED                # above the largest value rank
     assert call(n_q=34, n_kv=2) == UNSUPPORTED          # group of 17 > 16
     assert call(scale=-1.0) == INVALID
@@ -117,9 +117,9 @@ def test_attention_validation(lib):
     assert call(d=7, dt=B.DL_F32, scale=-1.0) == UNSUPPORTED
     assert call(d=258, dt=B.DL_F32) == UNSUPPORTED
     pre = lib.dl_lowrank_attn_prefill
-    assert pre(P, P, P, P, P, P, P, 2, 4, 12, 4, 128, 64, 64, 32, 0.0, 0.0, B.DL_BF16, P, 1 << 24,
+    assert pre(P, P, P, P, P, P, P, 2, 4, 12, 4, 128, 64, 64, 64, 0.0, 0.0, B.DL_BF16, P, 1 << 24,
                None) == UNSUPPORTED                      # group 3 not a power of two
-    assert pre(P, P, P, P, P, P, P, 2, 40, 8, 2, 128, 64, 64, 32, 0.0, 0.0, B.DL_BF16, P, 1 << 24,
+    assert pre(P, P, P, P, P, P, P, 2, 80, 8, 2, 128, 64, 64, 64, 0.0, 0.0, B.DL_BF16, P, 1 << 24,
                None) == INVALID                          # T > L_max
 
 
@@ -135,22 +135,22 @@ def _layer(dt=B.DL_BF16, rank=64, hidden=256, ffn=512, n_q=4, n_kv=2, d=64):
 def test_layer_validation(lib):
     f = lib.dl_decomposed_layer_fwd
     L = _layer()
-    need = lib.dl_layer_workspace(ctypes.byref(L), 2, 1, 32)
+    need = lib.dl_layer_workspace(ctypes.byref(L), 2, 1, 64)
     assert need > 0
-    assert f(ctypes.byref(L), P, P, None, P, P, P, 2, 1, 32, P, need - 1, None) == WORKSPACE
-    assert f(None, P, P, None, P, P, P, 2, 1, 32, P, need, None) == INVALID
-    assert f(ctypes.byref(L), P, P, None, P, P, P, 2, 0, 32, P, need, None) == INVALID
-    assert f(ctypes.byref(L), P, P, BAD, P, P, P, 2, 1, 32, P, need, None) == ALIGN
-    assert f(ctypes.byref(L), P, P, None, P, P, P, 2, 1, 16, P, need, None) == UNSUPPORTED
+    assert f(ctypes.byref(L), P, P, None, P, P, P, 2, 1, 64, P, need - 1, None) == WORKSPACE
+    assert f(None, P, P, None, P, P, P, 2, 1, 64, P, need, None) == INVALID
+    assert f(ctypes.byref(L), P, P, None, P, P, P, 2, 0, 64, P, need, None) == INVALID
+    assert f(ctypes.byref(L), P, P, BAD, P, P, P, 2, 1, 64, P, need, None) == ALIGN
+    assert f(ctypes.byref(L), P, P, None, P, P, P, 2, 1, 96, P, need, None) == UNSUPPORTED
     L2 = _layer(rank=96)
-    assert f(ctypes.byref(L2), P, P, None, P, P, P, 2, 1, 32, P, need, None) == UNSUPPORTED
+    assert f(ctypes.byref(L2), P, P, None, P, P, P, 2, 1, 64, P, need, None) == UNSUPPORTED
     L3 = _layer()
     L3.gate = B.Factor(None, P, 64)
-    assert f(ctypes.byref(L3), P, P, None, P, P, P, 2, 1, 32, P, need, None) == INVALID
+    assert f(ctypes.byref(L3), P, P, None, P, P, P, 2, 1, 64, P, need, None) == INVALID
     L4 = _layer(n_kv=3)
-    assert f(ctypes.byref(L4), P, P, None, P, P, P, 2, 1, 32, P, need, None) == INVALID
+    assert f(ctypes.byref(L4), P, P, None, P, P, P, 2, 1, 64, P, need, None) == INVALID
     # workspace grows with the batch and is defined for both dtypes
-    assert lib.dl_layer_workspace(ctypes.byref(L), 64, 1, 32) > need
+    assert lib.dl_layer_workspace(ctypes.byref(L), 64, 1, 64) > need
     assert lib.dl_layer_workspace(ctypes.byref(_layer(dt=B.DL_F32, rank=5, hidden=20, ffn=30,
                                                       d=10)), 2, 3, 16) > 0
 
@@ -160,3 +160,36 @@ def test_probe_rejects_bad_arguments(lib):
     assert lib.dl_probe_mfma_bf16(P, 0, 1, None) == INVALID
     assert lib.dl_probe_mfma_bf16(P, 1, 0, None) == INVALID
     assert lib.dl_probe_mfma_bf16(P, 1 << 31, 1, None) == INVALID
+
+
+def test_paged_and_pack_validation(lib):
+    """Paged entry points reject a missing or f32 cache descriptor; the pack
+    calls reject shapes their layouts cannot hold; no launch is reached."""
+    c = B.KvCache(P, P, P, 4, 16)
+    cref = ctypes.byref(c)
+    dec = lib.dl_lowrank_attn_decode_paged
+    assert dec(P, None, P, P, P, P, 2, 8, 2, 128, 64, 64, 0.0, 0.0, B.DL_BF16, P, 1 << 24,
+               None) == INVALID
+    assert dec(P, cref, P, P, P, P, 2, 8, 2, 128, 64, 64, 0.0, 0.0, B.DL_F32, P, 1 << 24,
+               None) == UNSUPPORTED
+    assert "bf16 only" in err(lib)
+    bad = B.KvCache(P, P, P, 0, 16)
+    assert dec(P, ctypes.byref(bad), P, P, P, P, 2, 8, 2, 128, 64, 64, 0.0, 0.0, B.DL_BF16, P,
+               1 << 24, None) == INVALID
+    mis = B.KvCache(BAD, P, P, 4, 16)
+    assert dec(P, ctypes.byref(mis), P, P, P, P, 2, 8, 2, 128, 64, 64, 0.0, 0.0, B.DL_BF16, P,
+               1 << 24, None) == ALIGN
+    app = lib.dl_lowrank_kv_append_paged
+    assert app(P, P, P, cref, P, 2, 300, 64, 64, 64, B.DL_BF16, P, 1 << 20, None) == INVALID  # T > 4 pages
+    L = _layer()
+    assert lib.dl_workspace_size(ctypes.byref(L), 2, 1, 64) == lib.dl_layer_workspace(
+        ctypes.byref(L), 2, 1, 64)
+    fwd = lib.dl_decomposed_layer_fwd_paged
+    assert fwd(ctypes.byref(L), P, P, None, None, P, 2, 1, P, 1 << 30, None) == INVALID
+    assert lib.dl_pack_factor(P, 64, 40, B.DL_BF16, P, None) == UNSUPPORTED   # cols % 16
+    assert lib.dl_pack_factor(P, 48, 64, B.DL_BF16, P, None) == UNSUPPORTED   # rows % 32
+    assert lib.dl_pack_factor(None, 64, 64, B.DL_BF16, P, None) == INVALID
+    assert lib.dl_factor_bytes(64, 32, B.DL_BF16) == 64 * 32 * 2
+    assert lib.dl_pack_kv_cache(P, P, 2, 96, 64, 64, B.DL_BF16, P, P, None) == UNSUPPORTED
+    assert lib.dl_unpack_kv_cache(P, P, 2, 64, 64, 48, B.DL_BF16, P, P, None) == UNSUPPORTED
+    assert lib.dl_pack_kv_cache(P, P, 2, 64, 64, 64, B.DL_BF16, BAD, P, None) == ALIGN

@@ -52,6 +52,15 @@ def oracle_layer(weights, x, ck, cv, past, seqs=None):
                                 attn_norm=gain(weights.attn_norm), mlp_norm=gain(weights.mlp_norm))
 
 
+#: Bound on the residual-branch deltas (x2 - x and y - x2). The outputs
+#: themselves (y, appended cache rows) are held to TOL, the stated bar. A
+#: branch delta can be a small fraction of the residual stream, and the bf16
+#: rounding of the branch's intermediates (latents, G, H) that bf16 layers may
+#: apply is then large relative to it: on the 80-sequence small layer, a CPU
+#: emulation of only that rounding, started from the exact x2, leaves 2.6% of
+#: the MLP delta. A wrong term, index or operand moves a delta by O(100%).
+DELTA_TOL = {"f32": TOL["f32"], "bf16": 2 * TOL["bf16"]}
+
 #: unit roundoff of the stored outputs; y is stored in the layer dtype
 #: (x2_out is always f32), so a delta recovered as y - x2 carries up to one
 #: rounding of y plus one of x2 on top of the kernel's own error.
@@ -87,7 +96,8 @@ def check_step(dt, x, y_dev, x2_dev, ck_dev, cv_dev, want, past, T, seqs=None):
         rows = slice(pst[i], pst[i] + T)
         errs[f"ck{i}"] = relerr(gk[i, rows], want["ck"][i, rows])
         errs[f"cv{i}"] = relerr(gv[i, rows], want["cv"][i, rows])
-    bad = {k: v for k, v in errs.items() if not v <= TOL[dt]}
+    bad = {k: v for k, v in errs.items()
+           if not v <= (DELTA_TOL[dt] if k.endswith("_delta") else TOL[dt])}
     assert not bad, (bad, max(errs.values()))
     return errs
 
@@ -107,8 +117,8 @@ SMALL = [
     # (name, dtype, hidden, n_q, n_kv, d, ffn, rank_attn, rank_kv, rank_mlp, Bsz, T, past, L_max, theta)
     ("gemv_decode", "bf16", 512, 8, 2, 128, 1024, 192, 128, 256, 4, 1, [0, 7, 100, 33], 128, 500000.0),
     ("gemv_prefill", "bf16", 256, 4, 2, 64, 512, 128, 64, 192, 2, 8, [0, 20], 64, 10000.0),
-    ("gemm_prefill", "bf16", 512, 8, 2, 128, 768, 256, 128, 320, 2, 100, [0, 20], 160, 10000.0),
-    ("gemm_decode_b80", "bf16", 256, 4, 1, 64, 512, 128, 64, 128, 80, 1, None, 32, 10000.0),
+    ("gemm_prefill", "bf16", 512, 8, 2, 128, 768, 256, 128, 320, 2, 100, [0, 20], 192, 10000.0),
+    ("gemm_decode_b80", "bf16", 256, 4, 1, 64, 512, 128, 64, 128, 80, 1, None, 64, 10000.0),
     ("f32_prefill", "f32", 96, 4, 2, 16, 160, 24, 12, 40, 3, 6, [0, 2, 9], 20, 100.0),
     ("f32_decode", "f32", 96, 6, 3, 16, 160, 24, 12, 40, 3, 1, [0, 2, 9], 20, 100.0),
 ]
@@ -259,5 +269,6 @@ def test_llama3_70b_c50_prefill(prefill_70b, seq):
         "ck": relerr(got["ck"][seq, :w.prefill], want["ck"][0, :w.prefill]),
         "cv": relerr(got["cv"][seq, :w.prefill], want["cv"][0, :w.prefill]),
     }
-    bad = {k: v for k, v in errs.items() if not v <= TOL["bf16"]}
+    bad = {k: v for k, v in errs.items()
+           if not v <= (DELTA_TOL["bf16"] if k.endswith("_delta") else TOL["bf16"])}
     assert not bad, (bad, errs)

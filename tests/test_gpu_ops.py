@@ -120,12 +120,12 @@ DECODE_CASES = [
     # (Bsz, n_q, n_kv, d, r_k, r_v, L_max, ctx_lens, theta, dtype)
     (3, 8, 2, 128, 448, 448, 320, [1, 130, 300], 500000.0, "bf16"),
     (2, 4, 4, 64, 64, 128, 64, [17, 40], 10000.0, "bf16"),
-    (2, 16, 1, 128, 128, 64, 288, [255, 129], 0.0, "bf16"),
-    (1, 64, 8, 128, 448, 448, 1120, [1025], 500000.0, "bf16"),
-    (2, 32, 8, 128, 320, 384, 608, [600, 77], 500000.0, "bf16"),
-    (2, 8, 2, 128, 640, 640, 2080, [2049, 700], 500000.0, "bf16"),   # ranks staged in chunks
-    (1, 40, 8, 128, 64, 128, 544, [515], 10000.0, "bf16"),             # 5 heads per kv head
-    (2, 12, 12, 64, 1024, 960, 160, [130, 64], 10000.0, "bf16"),       # largest ranks
+    (2, 16, 1, 128, 128, 64, 320, [255, 129], 0.0, "bf16"),
+    (1, 64, 8, 128, 448, 448, 1152, [1025], 500000.0, "bf16"),
+    (2, 32, 8, 128, 320, 384, 640, [600, 77], 500000.0, "bf16"),
+    (2, 8, 2, 128, 640, 640, 2112, [2049, 700], 500000.0, "bf16"),   # ranks staged in chunks
+    (1, 40, 8, 128, 64, 128, 576, [515], 10000.0, "bf16"),             # 5 heads per kv head
+    (2, 12, 12, 64, 1024, 960, 192, [130, 64], 10000.0, "bf16"),       # largest ranks
     (2, 4, 4, 64, 64, 64, 40, [33, 40], 10000.0, "f32"),
     (2, 6, 2, 32, 12, 20, 50, [1, 50], 100.0, "f32"),
 ]
@@ -151,12 +151,12 @@ def test_attn_decode(B, case):
 # ----------------------------------------------------------------------------
 PREFILL_CASES = [
     # (Bsz, T, n_q, n_kv, d, r_k, r_v, L_max, past, theta, dtype)
-    (2, 70, 8, 1, 128, 64, 64, 224, [0, 50], 10000.0, "bf16"),
+    (2, 70, 8, 1, 128, 64, 64, 256, [0, 50], 10000.0, "bf16"),
     (2, 33, 8, 2, 64, 128, 64, 128, [5, 0], 500000.0, "bf16"),
-    (1, 130, 4, 4, 128, 64, 128, 288, [100], 10000.0, "bf16"),
+    (1, 130, 4, 4, 128, 64, 128, 320, [100], 10000.0, "bf16"),
     (1, 20, 32, 2, 64, 64, 64, 64, [3], 0.0, "bf16"),
     (2, 1, 16, 2, 128, 448, 448, 320, [299, 10], 500000.0, "bf16"),
-    (1, 200, 64, 8, 128, 448, 448, 224, [0], 500000.0, "bf16"),
+    (1, 200, 64, 8, 128, 448, 448, 256, [0], 500000.0, "bf16"),
     (2, 32, 4, 4, 64, 64, 64, 40, [0, 3], 10000.0, "f32"),
 ]
 
@@ -178,7 +178,7 @@ def test_attn_prefill(B, case):
 
 def test_explicit_softmax_scale(B):
     r = rng(5)
-    Bsz, n_q, n_kv, d, rk, L_max = 2, 8, 2, 128, 64, 96
+    Bsz, n_q, n_kv, d, rk, L_max = 2, 8, 2, 128, 64, 128
     q = rand(r, (Bsz, n_q, d), 1.0, "bf16")
     ck, cv = rand(r, (Bsz, L_max, rk), 1.0, "bf16"), rand(r, (Bsz, L_max, rk), 1.0, "bf16")
     Bk, Bv = rand(r, (rk, n_kv * d), 0.1, "bf16"), rand(r, (rk, n_kv * d), 0.1, "bf16")

@@ -328,3 +328,85 @@ def test_rmsnorm_and_silu_special_values():
     assert ref.silu(0.0) == 0.0
     assert abs(ref.silu(40.0) - 40.0) < 1e-12
     assert abs(ref.silu(1.0) - 1.0 / (1.0 + math.exp(-1.0))) < 1e-15
+
+
+# --------------------------------------------------------------------------
+# Paged cache: page placement must not change any result
+# --------------------------------------------------------------------------
+def _pages_of(cache, table, num_pages, page):
+    """Scatter contiguous [Bsz, L, r] rows into pool pages with explicit
+    loops (position p -> page table[b, p // page], row p % page)."""
+    Bsz, L, r = cache.shape
+    pool = np.full((num_pages, page, r), np.nan)
+    for b in range(Bsz):
+        for p in range(L):
+            pool[table[b, p // page], p % page] = cache[b, p]
+    return pool
+
+
+def test_paged_gather_reads_pages_in_table_order():
+    r = rng(20)
+    Bsz, L, rk, page, num = 2, 12, 3, 4, 9
+    ck = r.standard_normal((Bsz, L, rk))
+    table = r.permutation(num)[:Bsz * (L // page)].reshape(Bsz, L // page)
+    pool = _pages_of(ck, table, num, page)
+    for b in range(Bsz):
+        for n in (1, 5, L):
+            assert np.array_equal(ref.paged_gather(pool, table[b], n), ck[b, :n])
+    # the identity table over a reshaped contiguous cache
+    ident = np.arange(Bsz * (L // page)).reshape(Bsz, L // page)
+    assert np.array_equal(ref.paged_gather(ck.reshape(-1, page, rk), ident[1], L), ck[1])
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_paged_layer_equals_contiguous_layer(T):
+    """A shuffled block table gives the contiguous result; appended rows land
+    on the pages the table names; every other pool row is untouched."""
+    h, n_q, n_kv, d, f, Bsz, page = 16, 4, 2, 8, 24, 3, 4
+    r = rng(21 + T)
+    F = {}
+    for p, (m, n) in {"q": (h, n_q * d), "k": (h, n_kv * d), "v": (h, n_kv * d),
+                      "o": (n_q * d, h), "gate": (h, f), "up": (h, f), "down": (f, h)}.items():
+        k = 5 if p in ("k", "v") else 7
+        F[p] = (r.standard_normal((m, k)) * 0.4, r.standard_normal((k, n)) * 0.4)
+    past = np.array([0, 5, 9])
+    L_max, num = 16, 14
+    x = r.standard_normal((Bsz, T, h))
+    ck, cv = r.standard_normal((Bsz, L_max, 5)), r.standard_normal((Bsz, L_max, 5))
+    table = r.permutation(num)[:Bsz * (L_max // page)].reshape(Bsz, L_max // page)
+    pk, pv = _pages_of(ck, table, num, page), _pages_of(cv, table, num, page)
+    # pool rows that belong to no sequence hold sentinels
+    pk[np.isnan(pk)] = 7.0
+    pv[np.isnan(pv)] = -7.0
+    want = ref.decomposed_layer(F, x, ck, cv, past, n_q, n_kv, d, 1000.0, 1e-5)
+    got = ref.decomposed_layer_paged(F, x, pk, pv, table, past, n_q, n_kv, d, 1000.0, 1e-5)
+    assert np.max(np.abs(got["y"] - want["y"])) < 1e-12
+    assert np.max(np.abs(got["x2"] - want["x2"])) < 1e-12
+    written = np.zeros(pk.shape[:2], bool)
+    for b in range(Bsz):
+        for t in range(T):
+            pos = past[b] + t
+            pg, row = table[b, pos // page], pos % page
+            written[pg, row] = True
+            assert np.allclose(got["pool_k"][pg, row], want["ck"][b, pos], atol=1e-12)
+            assert np.allclose(got["pool_v"][pg, row], want["cv"][b, pos], atol=1e-12)
+    assert np.array_equal(got["pool_k"][~written], pk[~written])
+    assert np.array_equal(got["pool_v"][~written], pv[~written])
+    lens = past + T
+    att = ref.attn_decode_paged(r.standard_normal((Bsz, n_q, d)), got["pool_k"], got["pool_v"],
+                                table, F["k"][1], F["v"][1], lens, n_kv, 1000.0)
+    assert att.shape == (Bsz, n_q, d) and np.all(np.isfinite(att))
+
+
+def test_paged_decode_attention_equals_contiguous():
+    r = rng(23)
+    Bsz, n_q, n_kv, d, rk, rv, page, L = 2, 4, 2, 8, 6, 5, 4, 12
+    q = r.standard_normal((Bsz, n_q, d))
+    ck, cv = r.standard_normal((Bsz, L, rk)), r.standard_normal((Bsz, L, rv))
+    Bk, Bv = r.standard_normal((rk, n_kv * d)), r.standard_normal((rv, n_kv * d))
+    table = r.permutation(7)[:6].reshape(Bsz, 3)
+    lens = np.array([12, 7])
+    want = ref.attn_decode(q, ck, cv, Bk, Bv, lens, n_kv, 500.0)
+    got = ref.attn_decode_paged(q, _pages_of(ck, table, 7, page), _pages_of(cv, table, 7, page),
+                                table, Bk, Bv, lens, n_kv, 500.0)
+    assert np.max(np.abs(got - want)) < 1e-12
