@@ -114,6 +114,10 @@ def decode_role_work(shape, M, ctx_total):
         "down_down": b16 * f * r["down"] + M * f * b16 + M * r["down"] * b16,
         "down_up": b16 * r["down"] * h + M * r["down"] * b16 + M * h * f32 + M * h * b16,
     }
+    # the fused chains: [A_q A_k A_v] then B_q; the o pair through the down pair
+    gemv["qkv_chain"] = gemv["qkv_down"] + gemv["q_up"]
+    gemv["o_mlp_chain"] = sum(gemv[k] for k in ("o_down", "o_up", "gate_up_down", "gate_up_up",
+                                                "down_down", "down_up"))
     attn_bytes = ctx_total * (r["k"] + r["v"]) * b16 + b16 * kvd * (r["k"] + r["v"]) + M * qd * (f32 + b16)
     attn_flops_own = (ctx_total * (2 * r["k"] * kvd + shape.n_q * (2 * shape.head_dim + 2 * r["v"]))
                       + M * shape.n_q * 2 * r["v"] * shape.head_dim)
@@ -302,7 +306,7 @@ def decode_bench(args, torch, binding, W, name, steps, warmup, trace_steps, nset
                                     "flops_per_step": 0, "pages_flops_per_step": 0})
         k["ms_per_step"] += sum(lst) / n
         k["launches_per_step"] += len(lst) // n
-        if kind == "gemv_bf16":
+        if kind in ("gemv_bf16", "gemv_chain"):
             k["bytes_per_step"] += gemv_bytes.get(role, 0) * (len(lst) // n)
         if kind == "attn_decode_bf16":
             k["bytes_per_step"] += attn_bytes
@@ -353,7 +357,8 @@ def decode_bench(args, torch, binding, W, name, steps, warmup, trace_steps, nset
     dname = max(kinds.items(), key=lambda kv: kv[1]["ms_per_step"])[0]
     roof = roofline(dname)
     roof_attn = roofline("attn_decode_bf16") if "attn_decode_bf16" in kinds else None
-    roof_gemv = roofline("gemv_bf16") if "gemv_bf16" in kinds else None
+    gname = "gemv_chain" if "gemv_chain" in kinds else "gemv_bf16"
+    roof_gemv = roofline(gname) if gname in kinds else None
     step_bytes = W.algorithmic_decode_bytes(w.shape, Bsz, ctx_total // Bsz)["total"]
     result = {
         "value": Bsz / (ms * 1e-3), "ms_per_step": ms, "wall_s": wall, "graph": use_graph,
@@ -407,6 +412,63 @@ def prefill_bench(args, torch, binding, W):
     del sets
     torch.cuda.empty_cache()
     return out, (w, weights, inp)
+
+
+# ----------------------------------------------------------------------------
+# Fused factor pair (decode-sized M): one persistent launch vs two launches
+# ----------------------------------------------------------------------------
+PAIR_SHAPES = (("llama3_8b_c40_o_pair", 16, 4096, 1216, 4096),
+               ("llama3_70b_c50_o_pair", 32, 8192, 2048, 8192),
+               ("llama3_70b_c50_gate_pair", 32, 8192, 3136, 28672))
+
+
+def fused_pair_bench(torch, binding, calls=40):
+    """dl_lowrank_linear y = (x A) B at decode sizes, timed from a captured
+    graph of `calls` calls over enough independent weight copies that the
+    Infinity Cache cannot hold them, with the pair fused into one launch
+    (DL_FUSED_CHAIN=pair) and as two launches (none). Bytes are the factor
+    bytes plus x and y."""
+    out = []
+    for name, M, m, k, n in PAIR_SHAPES:
+        nbytes = 2 * (m * k + k * n)
+        copies = max(2, -(-640_000_000 // nbytes))
+        dev = "cuda:0"
+        x = torch.randn(M, m, device=dev).to(torch.bfloat16)
+        ws_list = [(torch.randn(k, m, device=dev).mul_(0.02).to(torch.bfloat16),
+                    torch.randn(n, k, device=dev).mul_(0.02).to(torch.bfloat16)) for _ in range(copies)]
+        y = torch.empty(M, n, dtype=torch.bfloat16, device=dev)
+        res = {"pair": name, "M": M, "m": m, "k": k, "n": n, "weight_copies": copies}
+        for mode in ("pair", "none"):
+            os.environ["DL_FUSED_CHAIN"] = mode
+            need = binding.load().dl_lowrank_linear_workspace(M, m, k, n, binding.DL_BF16)
+            ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                binding.lowrank_linear(x, *ws_list[0], y=y, ws=ws)
+            torch.cuda.current_stream().wait_stream(side)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(calls):
+                    binding.lowrank_linear(x, *ws_list[i % copies], y=y, ws=ws)
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(3):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (3 * calls)
+            gbs = (nbytes + 2 * M * (m + n)) / (us * 1e-6) / 1e9
+            res["fused_us" if mode == "pair" else "separate_us"] = round(us, 2)
+            res["fused_GB_per_s" if mode == "pair" else "separate_GB_per_s"] = round(gbs, 1)
+            del g
+        os.environ.pop("DL_FUSED_CHAIN", None)
+        out.append(res)
+        del ws_list
+        torch.cuda.empty_cache()
+    return out
 
 
 # ----------------------------------------------------------------------------
@@ -550,6 +612,9 @@ def main():
     for name in [n for n in args.legs.split(",") if n]:
         legs.append(decode_leg(args, torch, binding, W, name, peaks))
         log(f"leg {name}: {legs[-1]['tokens_per_s']:.0f} tokens/s")
+    pairs = fused_pair_bench(torch, binding)
+    for p in pairs:
+        log(f"factor pair {p['pair']}: fused {p['fused_us']} us, separate {p['separate_us']} us")
     pre = pre_inputs = None
     if not args.no_prefill:
         pre, pre_inputs = prefill_bench(args, torch, binding, W)
@@ -572,7 +637,8 @@ def main():
         "roofline_gemv": with_measured(dec["roofline_gemv"], peaks),
         "measured_peaks": peaks,
         "step_hbm_frac": dec["step_hbm_frac"], "kernel_source_hash": kernel_source_hash(),
-        "cpu_baseline": cpu, "prefill": pre, "decode_legs": legs, "kernels": dec["kernels"],
+        "cpu_baseline": cpu, "prefill": pre, "decode_legs": legs, "factor_pairs": pairs,
+        "kernels": dec["kernels"],
         "roles_us_per_step": dec["roles_us_per_step"],
     }
     print(json.dumps(line), flush=True)

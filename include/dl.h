@@ -62,6 +62,22 @@
  *     must not share a workspace.
  *   - Host-side validation runs before any launch. On failure nothing is
  *     enqueued and a status is returned; dl_last_error() then describes it.
+ *   - Tuning switches, read from the environment at each call (results are
+ *     the same whatever they are set to; only timing changes):
+ *       DL_FUSED_CHAIN      "all" (default): decode-sized factor pairs and
+ *                           the dependent GEMV stages of a decode step run
+ *                           as persistent fused launches; "pair": only
+ *                           dl_lowrank_linear's pair; "none": one launch
+ *                           per factor.
+ *       DL_CHAIN_WGS_PER_CU persistent workgroups per compute unit of a
+ *                           fused launch (default 1).
+ *       DL_GEMV_R           force 1, 2 or 4 16-row weight tiles per GEMV
+ *                           work item (default: chosen per launch).
+ *       DL_GEMV_KS, DL_GEMV_MIN_STEPS, DL_GEMV_CUS, DL_GEMV_WAVES
+ *                           GEMV K-split cap, minimum steps per split,
+ *                           compute units assumed, waves per workgroup.
+ *       DL_ATTN_TARGET_WGS  decode-attention workgroups aimed for when
+ *                           choosing the context splits (default 256).
  *   - Device-resident lengths (past_lens, ctx_lens) are not checked (that
  *     would need a synchronisation); their stated ranges are preconditions.
  */
@@ -118,9 +134,11 @@ const char *dl_last_error(void);
 /* ------------------------------------------------------------------------
  * Factor-pair projection -- section 2.1, Eq. (1).
  *   y[M, n] = (x[M, m] A[m, k]) B[k, n]      A passed as At [k, m], B as Bt [n, k]
- * The rank-k intermediate x A lives only in the workspace. For M <= 64 the
- * pair runs as two weight-streaming MFMA GEMV passes; for larger M as two
- * MFMA GEMMs.
+ * For M <= 64 the pair is one fused launch: a persistent grid streams A,
+ * hands the rank-k intermediate x A to the B stage through the
+ * device-coherent cache level, and streams B (MFMA GEMV passes on 16-row
+ * tiles); for larger M it runs as two MFMA GEMMs with the intermediate in
+ * the workspace.
  * DL_BF16 requires m, k, n to be multiples of 64 (else UNSUPPORTED).
  * ------------------------------------------------------------------------ */
 size_t dl_lowrank_linear_workspace(int64_t M, int64_t m, int64_t k, int64_t n,

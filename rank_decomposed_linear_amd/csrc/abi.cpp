@@ -7,6 +7,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include <algorithm>
 #include <mutex>
@@ -30,11 +31,12 @@ bool g_open = false;
 const char *const kKindNames[K_NUM_KINDS] = {
     "rmsnorm",       "fill",        "convert",      "store_cache_rows",
     "gemv_bf16",     "gemm_bf16",   "gemm_f32",     "pack_up_factor",
-    "attn_decode_bf16", "attn_combine", "attn_prefill_bf16", "attn_f32"};
+    "attn_decode_bf16", "attn_combine", "attn_prefill_bf16", "attn_f32", "gemv_chain"};
 const char *const kRoleNames[R_NUM_ROLES] = {
     "other",        "attn_norm",    "qkv_down", "kv_store",  "q_up",
     "attention",    "o_down",       "o_up",     "mlp_norm",  "gate_up_down",
-    "gate_up_up",   "down_down",    "down_up",  "output",    "init"};
+    "gate_up_up",   "down_down",    "down_up",  "output",    "init",
+    "qkv_chain",    "o_mlp_chain",  "pair_chain"};
 }  // namespace
 
 namespace dl {
@@ -157,6 +159,50 @@ hipError_t gemv_run(GvArgs &a, float *part, int *counters, hipStream_t s) {
   a.part = part;
   a.counters = counters;
   return launch_gemv(a, s);
+}
+
+// Runs GEMV stages in order, each reading the previous one's output: as
+// one persistent chain launch per maximal run of stages whose inputs after
+// the first are operand-tiled (a stage reading row-major activations starts
+// a new run). Stages share `part` / `counters` (a stage's merges finish
+// before the next stage passes its wait). sync: kChainSyncInts zero ints per
+// run (runs <= max_runs).
+hipError_t gemv_sequence(GvArgs *g, int n, float *part, int *counters, int *sync, int max_runs,
+                         bool fuse, const int *roles, int chain_role, hipStream_t s) {
+  int i = 0, run = 0;
+  while (i < n) {
+    int j = i + 1;
+    while (fuse && j < n && j - i < kMaxChain && g[j].x_tiled) ++j;
+    if (j - i > 1 && run >= max_runs) return hipErrorInvalidValue;
+    GvChain c{};
+    c.nst = j - i;
+    c.sync = sync + run * kChainSyncInts;
+    for (int k = i; k < j; ++k) {
+      gemv_plan(g[k]);
+      g[k].part = part;
+      g[k].counters = counters;
+      c.st[k - i] = g[k];
+    }
+    set_role(c.nst == 1 ? roles[i] : chain_role);
+    const hipError_t e = c.nst == 1 ? launch_gemv(c.st[0], s) : launch_gemv_chain(c, s);
+    if (e != hipSuccess) return e;
+    if (c.nst > 1) ++run;
+    i = j;
+  }
+  return hipSuccess;
+}
+
+// Where decode-sized factor pairs run fused (one persistent launch per chain
+// of dependent GEMV stages) instead of one launch per stage:
+// DL_FUSED_CHAIN = "all" (default: the pair of dl_lowrank_linear and the
+// stages of a decode step) | "pair" (dl_lowrank_linear only) | "none".
+enum FuseMode { FUSE_NONE = 0, FUSE_PAIR = 1, FUSE_ALL = 2 };
+int fuse_mode() {
+  const char *v = getenv("DL_FUSED_CHAIN");
+  if (!v || !*v) return FUSE_ALL;
+  if (!strcmp(v, "none")) return FUSE_NONE;
+  if (!strcmp(v, "pair")) return FUSE_PAIR;
+  return FUSE_ALL;
 }
 
 hipError_t gemm(GemmArgs &a, hipStream_t s) {
@@ -448,7 +494,7 @@ size_t dl_lowrank_linear_workspace(int64_t M, int64_t m, int64_t k, int64_t n, d
     GvScratch sc;
     sc.add(g1);
     sc.add(g2);
-    c.take<int>(sc.counters);
+    c.take<int>(sc.counters + kChainSyncInts);
     c.take<float>(sc.part_floats);
     c.take<uint16_t>(mpad(M) * k);
   } else {
@@ -492,14 +538,19 @@ dl_status dl_lowrank_linear(const void *x, const void *A, const void *B, void *y
     GvScratch sc;
     sc.add(g1);
     sc.add(g2);
-    int *counters = c.take<int>(sc.counters);
+    int *counters = c.take<int>(sc.counters + kChainSyncInts);
     float *part = c.take<float>(sc.part_floats);
     uint16_t *t = c.take<uint16_t>(mpad(M) * k);
     linear_gemvs(Mi, mi, ki, ni, x, A, B, t, y, g1, g2);
-    FillRegion z[1] = {{reinterpret_cast<float *>(counters), nullptr, 0, sc.counters}};
+    // the fused pair: x A and then t B in one persistent launch, the rank-k
+    // intermediate t handed over on chip (split counters and the chain's
+    // ticket / done counters zeroed first)
+    FillRegion z[1] = {{reinterpret_cast<float *>(counters), nullptr, 0, sc.counters + kChainSyncInts}};
     DL_HIP(launch_fill(z, 1, s));
-    DL_HIP(gemv_run(g1, part, counters, s));
-    DL_HIP(gemv_run(g2, part, counters, s));
+    GvArgs g[2] = {g1, g2};
+    const int roles[2] = {R_OTHER, R_OTHER};
+    DL_HIP(gemv_sequence(g, 2, part, counters, counters + sc.counters, 1, fuse_mode() >= FUSE_PAIR,
+                         roles, R_PAIR_CHAIN, s));
     return DL_OK;
   }
   uint16_t *t = c.take<uint16_t>(static_cast<size_t>(M * k));
@@ -888,6 +939,7 @@ struct LayerWS {
   // bf16 small-M path: split-K scratch, bf16 latents, f32 query and residual stream
   int *counters;
   int n_counters;
+  int *chain_sync;
   float *part, *q32, *x2f, *ssq;
   uint16_t *att16, *H16, *a16t, *x2g;
   // bf16 large-M (MFMA GEMM) path
@@ -993,8 +1045,11 @@ static void carve_layer(Carver &c, const LayerDims &D, const dl_layer *L, LayerW
     layer_gemvs(L, D, none, nullptr, nullptr, nullptr, CacheRef{}, nullptr, g);
     GvScratch sc;
     for (GvArgs &a : g) sc.add(a);
-    w.n_counters = sc.counters;
-    w.counters = c.take<int>(sc.counters);
+    // split counters, then the sync ints of up to three chain runs; all
+    // zeroed by the step's first kernel
+    w.n_counters = sc.counters + 3 * kChainSyncInts;
+    w.counters = c.take<int>(w.n_counters);
+    w.chain_sync = w.counters + sc.counters;
     w.part = c.take<float>(sc.part_floats);
     // operand-tiled intermediates ([Mpad, cols], Mpad = M rounded up to 16)
     const size_t Mp = mpad(D.M);
@@ -1143,26 +1198,21 @@ static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_
     DL_HIP(launch_norm_tiles(static_cast<const uint16_t *>(x), L->attn_norm, L->dt == DL_F32,
                              L->rms_eps, w.a16t, M, static_cast<int>(mpad(M)), h, zero,
                              aw.counters ? 2 : 1, s));
-    set_role(R_QKV_DOWN);
-    DL_HIP(gemv_run(g[G_QKV], w.part, w.counters, s));
-    set_role(R_Q_UP);
-    DL_HIP(gemv_run(g[G_QUP], w.part, w.counters, s));
+    // [A_q A_k A_v] then B_q as one chain (the query latents stay on chip)
+    const bool fuse = fuse_mode() == FUSE_ALL;
+    static const int roles[G_NUM] = {R_QKV_DOWN, R_Q_UP, R_O_DOWN, R_O_UP,
+                                     R_GATE_UP_DOWN, R_GATE_UP_UP, R_DOWN_DOWN, R_DOWN_UP};
+    DL_HIP(gemv_sequence(&g[G_QKV], 2, w.part, w.counters, w.chain_sync, 1, fuse, &roles[G_QKV],
+                         R_QKV_CHAIN, s));
     set_role(R_ATTENTION);
     DL_HIP(run_attn_bf16(w.q32, 1, qd, cache, L->k.B, L->v.B, past_lens, 1, D.T == 1, w.att16, 0,
                          D.T == 1 ? 1 : 0, D.Bsz, D.T, D.nq, D.nkv, D.d, D.rk, D.rv, 0.f,
                          L->rope_theta, aw, s));
-    set_role(R_O_DOWN);
-    DL_HIP(gemv_run(g[G_ODOWN], w.part, w.counters, s));
-    set_role(R_O_UP);
-    DL_HIP(gemv_run(g[G_OUP], w.part, w.counters, s));
-    set_role(R_GATE_UP_DOWN);
-    DL_HIP(gemv_run(g[G_GUD], w.part, w.counters, s));
-    set_role(R_GATE_UP_UP);
-    DL_HIP(gemv_run(g[G_GUU], w.part, w.counters, s));
-    set_role(R_DOWN_DOWN);
-    DL_HIP(gemv_run(g[G_DD], w.part, w.counters, s));
-    set_role(R_DOWN_UP);
-    DL_HIP(gemv_run(g[G_DU], w.part, w.counters, s));
+    // the o pair, the MLP norm, the gate/up pairs with SwiGLU and the down
+    // pair: six dependent GEMV stages in one chain (two runs when the
+    // attention output arrives row-major, T > 1)
+    DL_HIP(gemv_sequence(&g[G_ODOWN], 6, w.part, w.counters, w.chain_sync + kChainSyncInts, 2, fuse,
+                         &roles[G_ODOWN], R_O_MLP_CHAIN, s));
     return DL_OK;
   }
 

@@ -38,6 +38,31 @@
 //    tiles, key cache position-major, value cache rank-major), residual
 //    add, and SwiGLU for paired (gate, up) launches whose two halves share
 //    the output columns.
+//  * Fused chains (the factor pair of Eq. (1) and the consecutive pairs of a
+//    decode step in one launch): a persistent grid takes work items from an
+//    atomic ticket counter in stage order -- every item of stage s before
+//    any item of stage s + 1. An item first issues its first weight steps
+//    (weights never depend on an earlier stage), then waits until every item
+//    of the previous stage has counted itself done, then loads its
+//    activations and finishes; so the next stage's weight stream starts
+//    while the previous stage's last items and merges drain, with no launch
+//    in between, and the rank-k intermediate passes from one stage to the
+//    next through the device-coherent level (it is a few tens of KB at
+//    decode sizes) without a kernel boundary. A waiting item only ever waits
+//    for items with smaller tickets, which were handed to workgroups already
+//    running and which never wait for a larger ticket, so every wait ends
+//    whatever the number of resident workgroups; the wait is bounded anyway
+//    (a time-out poisons the item's outputs with NaN instead of hanging).
+//    Data that a later stage of the same launch reads is written with
+//    agent-scope atomic stores (written through to the device-coherent
+//    level, like the split-K partials) and published with the same store /
+//    wait / counter sequence. It is read with plain, cacheable loads: each
+//    such buffer is written by exactly one stage of a launch and no
+//    workgroup touches it before observing that stage complete, so no cache
+//    of any XCD can hold an older copy from this launch (kernel boundaries
+//    invalidate copies from earlier ones), and its reads -- as many bytes as
+//    the weights for one-tile items -- stay in L2 instead of each going to
+//    the memory side.
 #include <stdlib.h>
 
 #include <algorithm>
@@ -70,6 +95,68 @@ __device__ __forceinline__ void load_coherent(const float *p, float &a, float &b
 // "memory" clobber keeps the compiler from moving accesses across it.
 __device__ __forceinline__ void wait_memory() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Accesses of data that another workgroup of the same launch produces or
+// consumes (COH = 1: agent-scope relaxed atomics, compiled to plain accesses
+// with the device-coherence bit; COH = 0: plain accesses).
+template <int COH>
+__device__ __forceinline__ u32x4 ld16c(const uint16_t *p) {
+  if constexpr (COH) {
+    const uint64_t *q = reinterpret_cast<const uint64_t *>(p);
+    const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return u32x4{static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32), static_cast<uint32_t>(b),
+                 static_cast<uint32_t>(b >> 32)};
+  } else {
+    return *reinterpret_cast<const u32x4 *>(p);
+  }
+}
+template <int COH>
+__device__ __forceinline__ u32x2 ld8c(const uint16_t *p) {
+  if constexpr (COH) {
+    const uint64_t a = __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    return u32x2{static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32)};
+  } else {
+    return *reinterpret_cast<const u32x2 *>(p);
+  }
+}
+template <int COH>
+__device__ __forceinline__ f32x4 ld16fc(const float *p) {
+  const u32x4 v = ld16c<COH>(reinterpret_cast<const uint16_t *>(p));
+  return f32x4{__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+}
+template <int COH>
+__device__ __forceinline__ float ldfc(const float *p) {
+  if constexpr (COH)
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    return *p;
+}
+template <int COH>
+__device__ __forceinline__ void st8c(uint16_t *p, u32x2 v) {
+  if constexpr (COH)
+    __hip_atomic_store(reinterpret_cast<uint64_t *>(p), static_cast<uint64_t>(v.x) | (static_cast<uint64_t>(v.y) << 32),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *reinterpret_cast<u32x2 *>(p) = v;
+}
+template <int COH>
+__device__ __forceinline__ void st16fc(float *p, f32x4 v) {
+  if constexpr (COH) {
+    store_coherent(p, v[0], v[1]);
+    store_coherent(p + 2, v[2], v[3]);
+  } else {
+    *reinterpret_cast<f32x4 *>(p) = v;
+  }
+}
+template <int COH>
+__device__ __forceinline__ void stfc(float *p, float v) {
+  if constexpr (COH)
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = v;
+}
+
 // Interleave the 8 XCDs: dispatch hands workgroup b to XCD b % 8; give each
 // XCD a contiguous range of items, i.e. neighbouring weight tiles.
 __device__ __forceinline__ int xcd_item(int b, int grid) {
@@ -84,34 +171,67 @@ enum XMode : int { XM_BF16 = 0, XM_TILED = 1 };
 // (so waiting for a step never waits for later prefetches). Row-major mode
 // reads row `row` at column k; tiled mode reads fragment (row block mb,
 // column step k / 32) of an [Mpad, cols] operand-tiled matrix.
-template <int XM>
+template <int XM, int COH>
 __device__ __forceinline__ u32x4 load_x(const uint16_t *X, int ldx, int row, int mb, int k, int lane) {
   if constexpr (XM == XM_TILED)
-    return *reinterpret_cast<const u32x4 *>(X + frag_off(mb, k >> 5, ldx, lane));
+    return ld16c<COH>(X + frag_off(mb, k >> 5, ldx, lane));
   else
-    return *reinterpret_cast<const u32x4 *>(X + static_cast<size_t>(row) * ldx + k);
+    return ld16c<COH>(X + static_cast<size_t>(row) * ldx + k);
 }
 
-template <int MB, int XM, int PAIRED, int RS, int R, int kWaves>
-__global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
+// LDS of one work item: per-wave sums [kWaves][RED], their total [RED],
+// the RMSNorm row scales and a broadcast flag.
+struct GvLds {
+  float *wsum;
+  float *red;
+  float *rscale;
+  int *flag;
+};
+// Chain hooks of one work item (all null outside a chain): wait until the
+// kChainQueues counters at wait_done (kSyncStride apart) sum to wait_need
+// after the first weight loads; count the item in *done when finished;
+// *err records a wait time-out.
+struct GvSync {
+  const int *wait_done;
+  int wait_need;
+  int *done;
+  int *err;
+};
+// Sum of the kChainQueues done counters at d, read by the lanes of one wave
+// (one coherent load per lane) and added across the wave.
+__device__ __forceinline__ int chain_done_sum(const int *d, int lane) {
+  static_assert(kChainQueues <= 64, "one counter per lane");
+  int v = lane < kChainQueues
+              ? __hip_atomic_load(d + kSyncStride * lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+              : 0;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+// Polls (each one to two microseconds) before a chain wait gives up: far
+// beyond any stage's duration; reached only if the launch's ticket and
+// counters were not zero at the start.
+constexpr int kSpinLimit = 1 << 21;
+
+// One work item of a GEMV launch (or of one chain stage).
+template <int MB, int XM, int PAIRED, int RS, int R, int kWaves, int COH>
+__device__ __forceinline__ void gemv_item(const GvArgs &a, const int item, const GvLds &L,
+                                          const GvSync &sy) {
   constexpr bool XT = XM == XM_TILED;
   constexpr int kThreads = kWaves * 64;
   constexpr int HALVES = PAIRED ? 2 : 1;
   constexpr int NACC = HALVES * R * MB;      // f32x4 accumulators per lane
   constexpr int RED = NACC * 4 * 64;         // floats of one wave's sums
   constexpr int PART = RED;                  // floats of one split's partial sums
-  __shared__ __attribute__((aligned(16))) float wsum[kWaves][RED];
-  __shared__ __attribute__((aligned(16))) float red[PART];
-  __shared__ float rscale[MB * 16];
-  __shared__ int last_flag;
+  float *const red = L.red;
+  float *const rscale = L.rscale;
+  int &last_flag = *L.flag;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 15, grp = lane >> 4;
   // work item = (K split, group of R consecutive 16-row tiles of one
   // segment); `tile` numbers the groups
-  const int item = xcd_item(blockIdx.x, gridDim.x);
-  if (item >= a.ntiles * a.ksplit) return;
   const int split = item / a.ntiles;
   const int tile = item - split * a.ntiles;
   int si = 0;
@@ -133,6 +253,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) acc[h][r][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   // 32-wide steps (weights + activations) in flight per wave
+  // 32-wide steps (weights + activations) in flight per wave (a ring twice
+  // or four times as deep measured the same)
   constexpr int kDepth = MB <= 2 ? 4 : 2;
   struct Stage {
     u32x4 w[R];    // one weight tile per row tile, sharing ...
@@ -150,19 +272,29 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
     w1[r] = sg.W + frag_off(tr, 0, a.K, lane);
     w2[r] = PAIRED ? sg.W2 + frag_off(tr, 0, a.K2, lane) : w1[r];
   }
-  auto load_stage = [&](Stage &sb, int st) {
+  auto load_w = [&](Stage &sb, int st) {
     int k = st * 32;
     const bool second = PAIRED && k >= a.K;
-    const uint16_t *X = static_cast<const uint16_t *>(second ? sg.X2 : sg.X);
-    const int ldx = second ? sg.ldx2 : sg.ldx;
     k -= second ? a.K : 0;
 #pragma unroll
     for (int r = 0; r < R; ++r)
       sb.w[r] = __builtin_nontemporal_load(
           reinterpret_cast<const u32x4 *>((second ? w2[r] : w1[r]) + static_cast<size_t>(k >> 5) * 512));
+  };
+  auto load_xs = [&](Stage &sb, int st) {
+    int k = st * 32;
+    const bool second = PAIRED && k >= a.K;
+    const uint16_t *X = static_cast<const uint16_t *>(second ? sg.X2 : sg.X);
+    const int ldx = second ? sg.ldx2 : sg.ldx;
+    k -= second ? a.K : 0;
     if (!XT) k += 8 * grp;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) sb.x[mb] = load_x<XM>(X, ldx, min(mb * 16 + j, a.M - 1), mb, k, lane);
+    for (int mb = 0; mb < MB; ++mb)
+      sb.x[mb] = load_x<XM, 0>(X, ldx, min(mb * 16 + j, a.M - 1), mb, k, lane);
+  };
+  auto load_stage = [&](Stage &sb, int st) {
+    load_w(sb, st);
+    load_xs(sb, st);
   };
   // `valid` is false for the padding steps at the end of the ring: their
   // activation operand is zeroed (a select, not a branch), so the loop body
@@ -198,20 +330,46 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
   constexpr int RSR = RS ? (MB * 16 + kWaves - 1) / kWaves : 1;
   constexpr int RSC = MB <= 2 ? 8 : 4;   // columns per lane read up front
   float rs_acc[RSR][RSC];
+  // the ring's first weights, then (in a chain) the wait for the producing
+  // stage, then everything that stage wrote: row sums and activations
+  Stage ring[kDepth];
+  if (nst > 0) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      load_w(ring[d], min(st0 + kWaves * d, st_last));
+      __builtin_amdgcn_sched_barrier(0);   // stages issue in ring order
+    }
+  }
+  bool poison = false;
+  if (sy.wait_done) {
+    if (wave == 0) {   // the whole wave polls (the loop condition is wave-uniform)
+      int spins = 0;
+      while (chain_done_sum(sy.wait_done, lane) < sy.wait_need) {
+        __builtin_amdgcn_s_sleep(8);
+        if (++spins == kSpinLimit) {
+          if (lane == 0) __hip_atomic_store(sy.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+      if (lane == 0) last_flag = spins == kSpinLimit;
+    }
+    __syncthreads();
+    poison = last_flag;
+    __syncthreads();   // last_flag is reused by the split merge
+  }
   if constexpr (RS) {
 #pragma unroll
     for (int i = 0; i < RSR; ++i)
 #pragma unroll
       for (int c = 0; c < RSC; ++c)
-        rs_acc[i][c] = a.rs_part[static_cast<size_t>(min(wave + kWaves * i, a.M - 1)) * a.rs_cols +
-                                 min(lane + 64 * c, a.rs_cols - 1)];
+        rs_acc[i][c] = ldfc<0>(a.rs_part + static_cast<size_t>(min(wave + kWaves * i, a.M - 1)) * a.rs_cols +
+                                 min(lane + 64 * c, a.rs_cols - 1));
   }
   if (nst > 0) {
-    Stage ring[kDepth];
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) {
-      load_stage(ring[d], min(st0 + kWaves * d, st_last));
-      __builtin_amdgcn_sched_barrier(0);   // stages issue in ring order
+      load_xs(ring[d], min(st0 + kWaves * d, st_last));
+      __builtin_amdgcn_sched_barrier(0);
     }
     for (int i = 0; i < nst; i += kDepth) {
 #pragma unroll
@@ -233,7 +391,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
 #pragma unroll
       for (int c = 0; c < RSC; ++c) sq += lane + 64 * c < a.rs_cols ? rs_acc[i][c] : 0.f;
       for (int c = lane + 64 * RSC; c < a.rs_cols; c += 64)   // wider rows
-        sq += a.rs_part[static_cast<size_t>(min(m, a.M - 1)) * a.rs_cols + c];
+        sq += ldfc<0>(a.rs_part + static_cast<size_t>(min(m, a.M - 1)) * a.rs_cols + c);
       sq = wave_sum(sq);
       if (lane == 0 && m < a.M) rscale[m] = rsqrtf(sq / static_cast<float>(a.K) + a.eps);
     }
@@ -248,12 +406,12 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          wsum[wave][(((h * R + r) * MB + mb) * 4 + e) * 64 + lane] = acc[h][r][mb][e];
+          L.wsum[wave * RED + (((h * R + r) * MB + mb) * 4 + e) * 64 + lane] = acc[h][r][mb][e];
   __syncthreads();
   for (int idx = tid; idx < RED; idx += kThreads) {
-    float v = wsum[0][idx];
+    float v = L.wsum[idx];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) v += wsum[w][idx];
+    for (int w = 1; w < kWaves; ++w) v += L.wsum[w * RED + idx];
     red[idx] = v;
   }
   __syncthreads();
@@ -267,7 +425,11 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
       last_flag = __hip_atomic_fetch_add(&a.counters[tile], 1, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT) == a.ksplit - 1;
     __syncthreads();
-    if (!last_flag) return;
+    if (!last_flag) {
+      // this item is done: its partials are published
+      if (sy.done && tid == 0) __hip_atomic_fetch_add(sy.done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
     // eight partials in flight per thread (indices clamped, loads
     // unconditional), summed in split order
     const float *base = a.part + static_cast<size_t>(tile) * a.ksplit * PART;
@@ -310,18 +472,21 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) v[r] *= rscale[m];
   }
+  if (poison) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = __builtin_nanf("");
+  }
   const size_t oi = static_cast<size_t>(m) * sg.ldo + n;
   switch (sg.omode) {
     case GV_OUT_BF16:
-      *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(sg.out) + oi) =
-          u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
+      st8c<COH>(static_cast<uint16_t *>(sg.out) + oi, u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])});
       break;
     case GV_OUT_F32:
-      *reinterpret_cast<f32x4 *>(static_cast<float *>(sg.out) + oi) = f32x4{v[0], v[1], v[2], v[3]};
+      st16fc<COH>(static_cast<float *>(sg.out) + oi, f32x4{v[0], v[1], v[2], v[3]});
       break;
     case GV_OUT_TILED:
-      *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(sg.out) + tile_off(m, n, sg.N)) =
-          u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
+      st8c<COH>(static_cast<uint16_t *>(sg.out) + tile_off(m, n, sg.N),
+                u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])});
       break;
     case GV_OUT_CACHE: {   // key cache page: [kPage, N] operand tiles
       const int b = m / a.T, pos = a.past[b] + m - b * a.T;
@@ -341,19 +506,19 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
     case GV_OUT_RES_F32: {
       const size_t ri = static_cast<size_t>(m) * sg.ldr + n;
       if (sg.res_f32) {
-        const f32x4 rr = *reinterpret_cast<const f32x4 *>(static_cast<const float *>(sg.R) + ri);
+        const f32x4 rr = ld16fc<0>(static_cast<const float *>(sg.R) + ri);
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] += rr[r];
       } else {
-        const u32x2 rr = *reinterpret_cast<const u32x2 *>(static_cast<const uint16_t *>(sg.R) + ri);
+        const u32x2 rr = ld8c<0>(static_cast<const uint16_t *>(sg.R) + ri);
         v[0] += bflo(rr.x);
         v[1] += bfhi(rr.x);
         v[2] += bflo(rr.y);
         v[3] += bfhi(rr.y);
       }
       const f32x4 o = f32x4{v[0], v[1], v[2], v[3]};
-      *reinterpret_cast<f32x4 *>(static_cast<float *>(sg.out) + oi) = o;
-      if (sg.out2) *reinterpret_cast<f32x4 *>(sg.out2 + oi) = o;
+      st16fc<COH>(static_cast<float *>(sg.out) + oi, o);
+      if (sg.out2) *reinterpret_cast<f32x4 *>(sg.out2 + oi) = o;   // read after the launch only
       if (sg.out_nt) {
         // next RMSNorm's input: g * o as bf16 operand tiles, and the sum of
         // squares of o over this tile's 16 columns of row m (the four
@@ -364,20 +529,19 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
           gn[r] = sg.gamma ? (sg.gamma_f32 ? static_cast<const float *>(sg.gamma)[n + r]
                                            : bf2f(static_cast<const uint16_t *>(sg.gamma)[n + r]))
                            : 1.f;
-        *reinterpret_cast<u32x2 *>(sg.out_nt + tile_off(m, n, sg.N)) =
-            u32x2{pack2(o[0] * gn[0], o[1] * gn[1]), pack2(o[2] * gn[2], o[3] * gn[3])};
+        st8c<COH>(sg.out_nt + tile_off(m, n, sg.N),
+                  u32x2{pack2(o[0] * gn[0], o[1] * gn[1]), pack2(o[2] * gn[2], o[3] * gn[3])});
         float sq = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
         sq += __shfl_xor(sq, 1, 64);
         sq += __shfl_xor(sq, 2, 64);
-        if (q == 0) sg.ssq_out[static_cast<size_t>(m) * (sg.N >> 4) + (n >> 4)] = sq;
+        if (q == 0) stfc<COH>(sg.ssq_out + static_cast<size_t>(m) * (sg.N >> 4) + (n >> 4), sq);
       }
       break;
     }
     case GV_OUT_RES_BF16: {
-      const f32x4 rr = *reinterpret_cast<const f32x4 *>(static_cast<const float *>(sg.R) +
-                                                         static_cast<size_t>(m) * sg.ldr + n);
-      *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(sg.out) + oi) =
-          u32x2{pack2(v[0] + rr[0], v[1] + rr[1]), pack2(v[2] + rr[2], v[3] + rr[3])};
+      const f32x4 rr = ld16fc<0>(static_cast<const float *>(sg.R) + static_cast<size_t>(m) * sg.ldr + n);
+      st8c<COH>(static_cast<uint16_t *>(sg.out) + oi,
+                u32x2{pack2(v[0] + rr[0], v[1] + rr[1]), pack2(v[2] + rr[2], v[3] + rr[3])});
       break;
     }
     default: {  // GV_OUT_SWIGLU, GV_OUT_SWIGLU_TILED
@@ -385,11 +549,114 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) g2[r] = silu(v[r]) * red[(((1 * R + rt) * MB + mb) * 4 + r) * 64 + ln];
       const size_t o = sg.omode == GV_OUT_SWIGLU_TILED ? tile_off(m, n, sg.N) : oi;
-      *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(sg.out) + o) = u32x2{pack2(g2[0], g2[1]), pack2(g2[2], g2[3])};
+      st8c<COH>(static_cast<uint16_t *>(sg.out) + o, u32x2{pack2(g2[0], g2[1]), pack2(g2[2], g2[3])});
       break;
     }
   }
   }
+  if (sy.done) {
+    // every output of this item is stored (and device-visible: its stores
+    // are coherent ones and have completed) before the item counts as done
+    wait_memory();
+    __syncthreads();
+    if (tid == 0) __hip_atomic_fetch_add(sy.done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <int MB, int XM, int PAIRED, int RS, int R, int kWaves>
+__global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GvArgs a) {
+  constexpr int RED = (PAIRED ? 2 : 1) * R * MB * 4 * 64;
+  __shared__ __attribute__((aligned(16))) float wsum[kWaves * RED];
+  __shared__ __attribute__((aligned(16))) float red[RED];
+  __shared__ float rscale[MB * 16];
+  __shared__ int flag;
+  const int item = xcd_item(blockIdx.x, gridDim.x);
+  if (item >= a.ntiles * a.ksplit) return;
+  gemv_item<MB, XM, PAIRED, RS, R, kWaves, 0>(a, item, GvLds{wsum, red, rscale, &flag},
+                                              GvSync{nullptr, 0, nullptr, nullptr});
+}
+
+// Persistent chain: stage s's items i with i % kChainQueues == q form queue
+// q's share of the stage; workgroup b takes tickets of queue b %
+// kChainQueues, whose items run stage by stage. An item of stage s > 0
+// waits for all of stage s - 1 (and so, transitively, for every earlier
+// stage). Each wait is for items that precede it in every queue: in its own
+// queue they were handed out before it to running workgroups, and in any
+// other queue they are reached before that queue's stage-s items, by
+// workgroups that only ever wait for still earlier stages, so by induction
+// on the stage every wait ends. Dynamic LDS: per-wave sums and their total
+// for the largest stage, (4 + 1) * red_max floats.
+template <int MB>
+__global__ __launch_bounds__(256) void gemv_chain_kernel(GvChain c) {
+  extern __shared__ __attribute__((aligned(16))) float dyn[];
+  __shared__ float rscale[MB * 16];
+  __shared__ int flag, ticket;
+  int red_max = 0;
+  for (int s = 0; s < c.nst; ++s)
+    red_max = max(red_max, (c.st[s].K2 > 0 ? 2 : 1) * c.st[s].rtiles * MB * 4 * 64);
+  const GvLds L{dyn, dyn + 4 * red_max, rscale, &flag};
+  const int queue = blockIdx.x % kChainQueues;
+  for (;;) {
+    if (threadIdx.x == 0)
+      ticket = __hip_atomic_fetch_add(c.sync + kSyncStride * queue, 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    int t = ticket;
+    __syncthreads();   // the ticket is read before the next one is taken
+    // queue ticket -> (stage, item): the queue's share of stage s is items
+    // queue, queue + kChainQueues, ...
+    int s = 0;
+    for (; s < c.nst; ++s) {
+      const int n = c.st[s].ntiles * c.st[s].ksplit;
+      const int share = n > queue ? (n - queue + kChainQueues - 1) / kChainQueues : 0;
+      if (t < share) break;
+      t -= share;
+    }
+    if (s == c.nst) return;   // every item of this queue is taken
+    s = __builtin_amdgcn_readfirstlane(s);
+    t = queue + kChainQueues * t;
+    const GvArgs &a = c.st[s];
+    const GvSync sy{s > 0 ? c.sync + kSyncStride * (kChainQueues * s) : nullptr,
+                    s > 0 ? c.st[s - 1].ntiles * c.st[s - 1].ksplit : 0,
+                    c.sync + kSyncStride * (kChainQueues * (1 + s) + queue),
+                    c.sync + kSyncStride * (kChainQueues * (1 + kMaxChain))};
+    const int R = a.rtiles;
+    if (!a.x_tiled) {   // first stage only: row-major activations from outside the chain
+      if (R == 1) gemv_item<MB, XM_BF16, 0, 0, 1, 4, 1>(a, t, L, sy);
+      else if (R == 2) gemv_item<MB, XM_BF16, 0, 0, 2, 4, 1>(a, t, L, sy);
+      else if constexpr (MB <= 2) gemv_item<MB, XM_BF16, 0, 0, 4, 4, 1>(a, t, L, sy);
+    } else if (a.K2 > 0) {
+      if (R == 1) gemv_item<MB, XM_TILED, 1, 0, 1, 4, 1>(a, t, L, sy);
+      else if (R == 2) gemv_item<MB, XM_TILED, 1, 0, 2, 4, 1>(a, t, L, sy);
+      else if constexpr (MB <= 2) gemv_item<MB, XM_TILED, 1, 0, 4, 4, 1>(a, t, L, sy);
+    } else if (a.rs_part) {
+      if (R == 1) gemv_item<MB, XM_TILED, 0, 1, 1, 4, 1>(a, t, L, sy);
+      else if (R == 2) gemv_item<MB, XM_TILED, 0, 1, 2, 4, 1>(a, t, L, sy);
+      else if constexpr (MB <= 2) gemv_item<MB, XM_TILED, 0, 1, 4, 4, 1>(a, t, L, sy);
+    } else {
+      if (R == 1) gemv_item<MB, XM_TILED, 0, 0, 1, 4, 1>(a, t, L, sy);
+      else if (R == 2) gemv_item<MB, XM_TILED, 0, 0, 2, 4, 1>(a, t, L, sy);
+      else if constexpr (MB <= 2) gemv_item<MB, XM_TILED, 0, 0, 4, 4, 1>(a, t, L, sy);
+    }
+    __syncthreads();   // LDS is reused by the next item
+  }
+}
+
+template <int MB>
+hipError_t launch_chain_mb(const GvChain &c, int grid, hipStream_t s) {
+  int red_max = 0;
+  for (int i = 0; i < c.nst; ++i)
+    red_max = std::max(red_max, (c.st[i].K2 > 0 ? 2 : 1) * c.st[i].rtiles * MB * 4 * 64);
+  const int dyn = 5 * red_max * static_cast<int>(sizeof(float));
+  const void *fn = reinterpret_cast<const void *>(&gemv_chain_kernel<MB>);
+  static int dyn_set = 0;   // largest dynamic LDS allowed so far for this instantiation
+  if (dyn > dyn_set && dyn > 65536) {
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, dyn);
+    if (e != hipSuccess) return e;
+    dyn_set = dyn;
+  }
+  gemv_chain_kernel<MB><<<grid, 256, dyn, s>>>(c);
+  return hipGetLastError();
 }
 
 template <int MB, int XM, int PAIRED, int RS>
@@ -479,6 +746,34 @@ size_t gemv_plan(GvArgs &a) {
   const int halves = a.K2 > 0 ? 2 : 1;
   const size_t part = static_cast<size_t>(halves) * R * MB * 4 * 64;
   return a.ksplit > 1 ? part * a.ntiles * a.ksplit : 0;
+}
+
+// the chain's stage table travels as the kernel argument (4 KB at most)
+static_assert(sizeof(GvChain) <= 4096, "chain stage table exceeds the kernel-argument limit");
+
+hipError_t launch_gemv_chain(const GvChain &c, hipStream_t s) {
+  TraceGuard trace_guard(K_GEMV_CHAIN, s);
+  if (c.nst < 1 || c.nst > kMaxChain) return hipErrorInvalidValue;
+  int total = 0;
+  for (int i = 0; i < c.nst; ++i) {
+    const GvArgs &a = c.st[i];
+    // the chain runs four waves per item, stages of one M, tiled inputs after
+    // the first, and at most four row tiles per item for two row blocks
+    if (a.waves != 4 || a.M != c.st[0].M || (i > 0 && !a.x_tiled) || (a.rtiles == 4 && a.M > 32))
+      return hipErrorInvalidValue;
+    total += a.ntiles * a.ksplit;
+  }
+  // one persistent workgroup per compute unit: measured fastest (a second,
+  // waiting workgroup per unit slowed the running stage down)
+  const int per_cu = std::max(1, std::min(8, env_int("DL_CHAIN_WGS_PER_CU", 1)));
+  // at least one workgroup per queue
+  const int grid = std::max(kChainQueues, std::min(total, per_cu * device_cus()));
+  switch ((c.st[0].M + 15) / 16) {
+    case 1: return launch_chain_mb<1>(c, grid, s);
+    case 2: return launch_chain_mb<2>(c, grid, s);
+    case 3: return launch_chain_mb<3>(c, grid, s);
+    default: return launch_chain_mb<4>(c, grid, s);
+  }
 }
 
 hipError_t launch_gemv(const GvArgs &a, hipStream_t s) {

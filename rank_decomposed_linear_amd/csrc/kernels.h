@@ -77,6 +77,27 @@ struct GvArgs {
 size_t gemv_plan(GvArgs &a);
 hipError_t launch_gemv(const GvArgs &a, hipStream_t s);
 
+// A chain of GEMV stages in one persistent launch (stage s + 1 reads what
+// stage s writes): every stage planned by gemv_plan, with its own part /
+// counters; stages after the first read operand-tiled activations; all
+// stages share M. sync points to kChainSyncInts ints that must be zero on
+// entry, one counter per 256-byte line: the work is dealt to kChainQueues
+// queues (workgroup b serves queue b % kChainQueues), each with its own
+// ticket counter [kSyncStride * q] and done counter per stage
+// [kSyncStride * (kChainQueues + s * kChainQueues + q)], so no counter is
+// hit by more than a queue's workgroups; [kSyncStride * (kChainQueues * (1 +
+// kMaxChain))] is set if a wait timed out (the affected outputs are NaN).
+constexpr int kMaxChain = 6;
+constexpr int kChainQueues = 32;
+constexpr int kSyncStride = 64;
+constexpr int kChainSyncInts = kSyncStride * (kChainQueues * (1 + kMaxChain) + 1);
+struct GvChain {
+  GvArgs st[kMaxChain];
+  int nst;
+  int *sync;
+};
+hipError_t launch_gemv_chain(const GvChain &c, hipStream_t s);
+
 // ---------------------------------------------------------------------------
 // bf16 MFMA GEMM for large M (prefill): C_s[M, N_s] = X_s[M, K] W_s with
 // W_s stored transposed, Wt[N_s, K] row-major; per-launch epilogue. Up to

@@ -18,6 +18,7 @@ enum KernelKind : int {
   K_ATTN_COMBINE,
   K_ATTN_PREFILL,
   K_ATTN_F32,
+  K_GEMV_CHAIN,
   K_NUM_KINDS
 };
 
@@ -37,6 +38,9 @@ enum Role : int {
   R_DOWN_UP,
   R_OUTPUT,
   R_INIT,
+  R_QKV_CHAIN,
+  R_O_MLP_CHAIN,
+  R_PAIR_CHAIN,
   R_NUM_ROLES
 };
 

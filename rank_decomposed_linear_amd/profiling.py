@@ -36,6 +36,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 # device function name fragment -> kernel kind (the launch trace's names)
 KINDS = (
+    ("gemv_chain_kernel", "gemv_chain"),
     ("gemv_kernel", "gemv_bf16"),
     ("attn_decode_kernel", "attn_decode_bf16"),
     ("attn_prefill_kernel", "attn_prefill_bf16"),

@@ -272,3 +272,36 @@ def test_llama3_70b_c50_prefill(prefill_70b, seq):
     bad = {k: v for k, v in errs.items()
            if not v <= (DELTA_TOL["bf16"] if k.endswith("_delta") else TOL["bf16"])}
     assert not bad, (bad, errs)
+
+
+@pytest.mark.parametrize("case", SMALL[:2], ids=[c[0] for c in SMALL[:2]])
+def test_small_layer_fused_chains(B, monkeypatch, case):
+    """The decode step's GEMV stages fused into two persistent launches
+    (DL_FUSED_CHAIN=all): [A_q A_k A_v] -> B_q and o -> MLP norm -> gate/up
+    -> SwiGLU -> down, including a first stage that reads row-major
+    activations (T > 1)."""
+    monkeypatch.setenv("DL_FUSED_CHAIN", "all")
+    test_small_layer(B, case, gains=True)
+
+
+def test_llama3_8b_c40_decode_fused_chains_bitwise(B, monkeypatch):
+    """Full 8B decode step with the fused chains against the separate-launch
+    path: identical bits for y, x2 and the appended cache rows, and the
+    oracle for every sequence."""
+    import torch
+    w = W.LLAMA3_8B_C40_DECODE
+    print(f"{w.name}: fused chains vs separate launches", flush=True)
+    weights, inp = W.draw(w)
+    layer = make_gpu_layer(B, weights)
+    outs = []
+    for mode in ("all", "none"):
+        monkeypatch.setenv("DL_FUSED_CHAIN", mode)
+        ck, cv = to_dev(W.to_library_key_cache(inp.ck)), to_dev(W.to_library_value_cache(inp.cv))
+        y, x2 = run_layer(B, layer, inp.x, ck, cv, inp.past_lens)
+        torch.cuda.synchronize()
+        outs.append((y, x2, ck, cv))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
+    y, x2, ck, cv = outs[0]
+    want = oracle_layer(weights, inp.x, inp.ck, inp.cv, inp.past_lens)
+    check_step("bf16", inp.x, y, x2, ck, cv, want, inp.past_lens, 1)

@@ -197,3 +197,25 @@ def test_mfma_probe(B):
     torch.cuda.synchronize()
     assert flops == 64 * 4 * 16 * 8 * 16384
     assert torch.isfinite(sink).all().item()
+
+
+@pytest.mark.parametrize("R", ["1", "4"])
+@pytest.mark.parametrize("M,m,k,n", [(16, 4096, 1216, 4096), (32, 8192, 448, 1024), (48, 1024, 320, 576)])
+def test_fused_pair_matches_separate_launches(B, monkeypatch, R, M, m, k, n):
+    """The decode-sized factor pair as one persistent launch (x A, then t B
+    after an on-chip handoff, DL_FUSED_CHAIN=pair) and as two launches
+    (none): the same work items, the same split order, so the same bits;
+    both within tolerance of the oracle."""
+    import torch
+    monkeypatch.setenv("DL_GEMV_R", R)
+    print(f"fused pair R={R} M={M} m={m} k={k} n={n}", flush=True)
+    r = rng(M * 13 + k)
+    x, A, Bf = rand(r, (M, m), 1.0, "bf16"), rand(r, (m, k), 0.02, "bf16"), rand(r, (k, n), 0.02, "bf16")
+    xd, Ad, Bd = to_dev(x), to_dev(lib_f(A)), to_dev(lib_f(Bf))
+    monkeypatch.setenv("DL_FUSED_CHAIN", "pair")
+    y_fused = B.lowrank_linear(xd, Ad, Bd)
+    monkeypatch.setenv("DL_FUSED_CHAIN", "none")
+    y_sep = B.lowrank_linear(xd, Ad, Bd)
+    torch.cuda.synchronize()
+    assert torch.equal(y_fused, y_sep)
+    assert relerr(to_host(y_fused), ref.lowrank_linear(f64(x), f64(A), f64(Bf))) <= TOL["bf16"]
