@@ -16,8 +16,9 @@ Large Language Models" (Huang, Huang, Liao, Wen; DAC '26):
   * section 4.2 / Fig. 4(b): attention rebuilds K and V by multiplying the
     cached latents with the up factors, applies rotary position embedding to
     the rebuilt keys, then attends.
-  * Table 2: MHA, MQA and GQA attention, GLU-based MLP, rotary embedding;
-    Fig. 3(b) shows SiLU as the MLP activation.
+  * Table 2: MHA, MQA and GQA attention, GLU-based and non-GLU MLPs,
+    rotary embedding; Fig. 3(b) shows SiLU as the MLP activation; section
+    5.1 names OPT-30B as the non-GLU model.
 
 Readings where the paper is silent (each also listed in the design notes):
   * row-vector convention, head-major projection outputs (head j occupies
@@ -25,6 +26,9 @@ Readings where the paper is silent (each also listed in the design notes):
     h // (n_q / n_kv);
   * LLaMA pre-norm block: RMSNorm -> attention -> residual -> RMSNorm ->
     SwiGLU MLP (silu(x A_g B_g) * (x A_u B_u)) -> residual;
+  * the non-GLU MLP is OPT's fc1 -> ReLU -> fc2, i.e. relu(x A_u B_u)
+    A_d B_d with the up and down pairs (same block around it: OPT's
+    LayerNorm, biases and learned positions are outside this reading);
   * RoPE pairs (i, i + d/2) rotated by pos * theta^(-2i/d), applied to the
     query and to the rebuilt keys, never to the cached latents; theta == 0
     disables it;
@@ -192,13 +196,19 @@ def silu(z) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
 
+def relu(z) -> np.ndarray:
+    return np.maximum(_f(z), 0.0)
+
+
 def decomposed_layer(factors: Dict[str, Tuple[np.ndarray, np.ndarray]], x, ck, cv,
                      past_lens, n_q: int, n_kv: int, head_dim: int,
                      rope_theta: float, rms_eps: float, attn_norm=None,
-                     mlp_norm=None) -> Dict[str, np.ndarray]:
+                     mlp_norm=None, mlp: str = "glu") -> Dict[str, np.ndarray]:
     """Forward pass of one decomposed pre-norm layer for T new tokens per
     sequence. x [Bsz, T, h]; the T new latents are stored at rows
     past_lens[b] .. past_lens[b] + T - 1 before attention reads them.
+    mlp: "glu" (silu(gate) * up, then down) or "relu" (the non-GLU form:
+    relu(up), then down; the gate pair is not used).
 
     Returns y (layer output), x2 (residual stream after attention), attn
     (attention output before the o pair) and the updated caches."""
@@ -213,7 +223,12 @@ def decomposed_layer(factors: Dict[str, Tuple[np.ndarray, np.ndarray]], x, ck, c
     att = att.reshape(Bsz, T, n_q * head_dim)
     x2 = x + lowrank_linear(att, *F["o"])
     b2 = rmsnorm(x2, mlp_norm, rms_eps)
-    hidden = silu(lowrank_linear(b2, *F["gate"])) * lowrank_linear(b2, *F["up"])
+    if mlp == "glu":
+        hidden = silu(lowrank_linear(b2, *F["gate"])) * lowrank_linear(b2, *F["up"])
+    elif mlp == "relu":
+        hidden = relu(lowrank_linear(b2, *F["up"]))
+    else:
+        raise ValueError(f"unknown MLP kind {mlp!r}")
     y = x2 + lowrank_linear(hidden, *F["down"])
     return {"y": y, "x2": x2, "attn": att, "ck": ck2, "cv": cv2}
 
@@ -236,7 +251,7 @@ def paged_gather(pool, table_row, L: int) -> np.ndarray:
 
 def decomposed_layer_paged(factors, x, pool_k, pool_v, table, past_lens, n_q: int,
                            n_kv: int, head_dim: int, rope_theta: float, rms_eps: float,
-                           attn_norm=None, mlp_norm=None) -> Dict[str, np.ndarray]:
+                           attn_norm=None, mlp_norm=None, mlp: str = "glu") -> Dict[str, np.ndarray]:
     """decomposed_layer over a paged cache, one sequence at a time: its
     past_lens[b] + T rows are gathered through its block-table row (the
     last T are overwritten by the append), the layer runs on that contiguous
@@ -253,7 +268,8 @@ def decomposed_layer_paged(factors, x, pool_k, pool_v, table, past_lens, n_q: in
         ck = paged_gather(pk, table[b], past + T)[None]
         cv = paged_gather(pv, table[b], past + T)[None]
         out = decomposed_layer(factors, x[b:b + 1], ck, cv, [past], n_q, n_kv, head_dim,
-                               rope_theta, rms_eps, attn_norm=attn_norm, mlp_norm=mlp_norm)
+                               rope_theta, rms_eps, attn_norm=attn_norm, mlp_norm=mlp_norm,
+                               mlp=mlp)
         for t in range(T):
             p = past + t
             pk[int(table[b][p // page]), p % page] = out["ck"][0, p]

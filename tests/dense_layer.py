@@ -37,8 +37,10 @@ def _silu(z):
 
 
 def dense_layer(W, x, cache_in_x, n_q, n_kv, d, theta, eps, attn_gain=None, mlp_gain=None,
-                sm_scale=None):
-    """W: dict of dense [in, out] matrices q, k, v, o, gate, up, down.
+                sm_scale=None, relu_mlp=False):
+    """W: dict of dense [in, out] matrices q, k, v, o, gate, up, down
+    (relu_mlp: the MLP is down(max(up(b), 0)), OPT's fc1 / ReLU / fc2, and
+    W["gate"] is not read).
     x: [Bsz, T, h] new tokens; cache_in_x: [Bsz, P, h] normalised
     activations of the P tokens already in the cache (or None), whose keys
     and values are recomputed densely. attn_gain / mlp_gain: per-channel
@@ -77,9 +79,12 @@ def dense_layer(W, x, cache_in_x, n_q, n_kv, d, theta, eps, attn_gain=None, mlp_
             att = np.concatenate(heads)
             x2 = x[b, t] + att @ W["o"]
             bn = _rmsnorm_row(x2, eps, mlp_gain)
-            g_ = bn @ W["gate"]
             u_ = bn @ W["up"]
-            hid = np.array([_silu(float(gv)) * float(uv) for gv, uv in zip(g_, u_)])
+            if relu_mlp:
+                hid = np.array([float(uv) if float(uv) > 0.0 else 0.0 for uv in u_])
+            else:
+                g_ = bn @ W["gate"]
+                hid = np.array([_silu(float(gv)) * float(uv) for gv, uv in zip(g_, u_)])
             y[b, t] = x2 + hid @ W["down"]
             x2_all[b, t] = x2
     return y, x2_all

@@ -99,6 +99,34 @@ def test_layer_matches_dense_at_full_rank(P, T, n_q, n_kv, theta):
     assert np.max(np.abs(out["y"] - y_d)) < 1e-9
 
 
+@pytest.mark.parametrize("P,T,theta", [(0, 5, 0.0), (4, 1, 0.0), (3, 2, 10000.0)])
+def test_relu_mlp_layer_matches_dense_at_full_rank(P, T, theta):
+    """The non-GLU MLP (OPT's fc1 -> ReLU -> fc2; Table 2 and section 5.1 of
+    the pages) at full rank equals the dense layer with a ReLU MLP; the GLU
+    form on the same factors must not."""
+    h, n_q, n_kv, d, f, Bsz, eps = 16, 4, 4, 8, 24, 2, 1e-5
+    r, W, F = _dense_and_factors(60 + P + T, h, n_q, n_kv, d, f)
+    x = r.standard_normal((Bsz, T, h))
+    past_norm = r.standard_normal((Bsz, P, h)) if P else None
+    L_max = P + T + 1
+    ck = np.zeros((Bsz, L_max, F["k"][0].shape[1]))
+    cv = np.zeros((Bsz, L_max, F["v"][0].shape[1]))
+    if P:
+        ck[:, :P] = past_norm @ F["k"][0]
+        cv[:, :P] = past_norm @ F["v"][0]
+    past = np.full(Bsz, P)
+    out = ref.decomposed_layer(F, x, ck, cv, past, n_q, n_kv, d, theta, eps, mlp="relu")
+    y_d, x2_d = dense_layer(W, x, past_norm, n_q, n_kv, d, theta, eps, relu_mlp=True)
+    assert np.max(np.abs(out["x2"] - x2_d)) < 1e-9
+    assert np.max(np.abs(out["y"] - y_d)) < 1e-9
+    glu = ref.decomposed_layer(F, x, ck, cv, past, n_q, n_kv, d, theta, eps)
+    assert np.max(np.abs(glu["y"] - y_d)) > 1e-3
+    # about half the hidden units are clipped, so the activation matters
+    b2 = ref.rmsnorm(out["x2"], None, eps)
+    u = ref.lowrank_linear(b2, *F["up"])
+    assert 0.2 < float(np.mean(u < 0)) < 0.8
+
+
 @pytest.mark.parametrize("P,T", [(0, 4), (5, 1)])
 def test_layer_gains_match_dense_at_full_rank(P, T):
     """Norm gains: attn_norm scales the attention input and mlp_norm the MLP
