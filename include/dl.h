@@ -11,7 +11,8 @@
  *   - section 4.2: attention rebuilds K = C_k B_k and V = C_v B_v from the
  *     cache, applies rotary position embedding to the rebuilt keys, then
  *     attends;
- *   - Table 2: MHA / MQA / GQA attention, GLU-based MLP, rotary embedding.
+ *   - Table 2: MHA / MQA / GQA attention, GLU-based and non-GLU MLPs,
+ *     rotary embedding (section 5.1: OPT-30B is the non-GLU model).
  *
  * Conventions shared by every entry point
  *   - Tensors are dense, row-major, contiguous. Every pointer argument is a
@@ -270,16 +271,25 @@ dl_status dl_lowrank_attn_prefill_paged(const void *q, const dl_kv_cache *cache,
  *   x2  = x + (o A_o) B_o
  *   b   = RMSNorm(x2) * mlp_norm
  *   y   = x2 + ((silu((b A_gate) B_gate) * ((b A_up) B_up)) A_down) B_down
+ *                                                   (mlp == DL_MLP_GLU)
+ *   y   = x2 + (relu((b A_up) B_up) A_down) B_down  (mlp == DL_MLP_RELU)
  * x, y: [Bsz, T, hidden]. T == 1 uses decode attention (query at position
  * past_lens[b]), T > 1 causal prefill attention. past_lens is not advanced
  * (the caller does). x2_out (optional, float32 [Bsz, T, hidden]) receives
  * x2. Factor shapes follow dl_factor; norm gains may be NULL (= 1).
+ * DL_MLP_RELU is the non-GLU MLP of Table 2, OPT's fc1 -> ReLU -> fc2 with
+ * fc1 = the up pair and fc2 = the down pair (section 5.1); its gate factor
+ * is not read and may be {NULL, NULL, 0}. OPT's LayerNorm, biases and
+ * learned positions are outside this block (rope_theta = 0 turns the rotary
+ * embedding off).
  * ------------------------------------------------------------------------ */
 typedef struct {
   const void *A;   /* A^T, [k, m] */
   const void *B;   /* B^T, [n, k] */
   int64_t k;
 } dl_factor;
+
+typedef enum { DL_MLP_GLU = 0, DL_MLP_RELU = 1 } dl_mlp;
 
 typedef struct {
   int64_t hidden, n_q, n_kv, head_dim, ffn;
@@ -289,6 +299,7 @@ typedef struct {
   float rms_eps;
   float rope_theta;
   dl_dtype dt;
+  dl_mlp mlp;             /* DL_MLP_GLU (SwiGLU) or DL_MLP_RELU (non-GLU) */
 } dl_layer;
 
 size_t dl_layer_workspace(const dl_layer *L, int64_t Bsz, int64_t T,

@@ -63,7 +63,9 @@ class Layer(ctypes.Structure):
                 ("gate", Factor), ("up", Factor), ("down", Factor),
                 ("attn_norm", ctypes.c_void_p), ("mlp_norm", ctypes.c_void_p),
                 ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
-                ("dt", ctypes.c_int)]
+                ("dt", ctypes.c_int), ("mlp", ctypes.c_int)]
+
+MLP_KINDS = {"glu": 0, "relu": 1}   # dl_mlp: DL_MLP_GLU, DL_MLP_RELU
 
 
 class KvCache(ctypes.Structure):
@@ -447,20 +449,24 @@ class DecomposedLayer:
 
     factors: dict name -> (At [k, m], Bt [n, k]) torch tensors on the GPU
     (each factor stored transposed) for q, k, v, o, gate, up, down; norm
-    gains optional."""
+    gains optional. mlp: "glu" (SwiGLU) or "relu" (the non-GLU MLP; no gate
+    factor needed)."""
 
     NAMES = ("q", "k", "v", "o", "gate", "up", "down")
 
     def __init__(self, factors, hidden, n_q, n_kv, head_dim, ffn, rope_theta, rms_eps=1e-5,
-                 attn_norm=None, mlp_norm=None):
+                 attn_norm=None, mlp_norm=None, mlp="glu"):
         self.factors = factors
         self.attn_norm, self.mlp_norm = attn_norm, mlp_norm
         dt = _dt(factors["q"][0])
         L = Layer()
         L.hidden, L.n_q, L.n_kv, L.head_dim, L.ffn = hidden, n_q, n_kv, head_dim, ffn
         for nm in self.NAMES:
+            if nm not in factors:
+                continue
             At, Bt = factors[nm]
             setattr(L, nm, Factor(_ptr(At), _ptr(Bt), At.shape[0]))
+        L.mlp = MLP_KINDS[mlp]
         L.attn_norm = _ptr(attn_norm)
         L.mlp_norm = _ptr(mlp_norm)
         L.rms_eps = rms_eps

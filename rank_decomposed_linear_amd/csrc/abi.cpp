@@ -437,8 +437,22 @@ hipError_t run_attn_bf16(const void *q, int q_f32, int ldq, const CacheRef &c,
 // ---------------------------------------------------------------------------
 struct LayerDims {
   int M, T, Bsz, h, nq, nkv, d, f, rq, rk, rv, ro, rg, ru, rd, L_max;
+  bool relu;   // non-GLU MLP: relu(up), no gate pair
   int qd() const { return nq * d; }
 };
+
+// The factor pairs a layer reads (the gate pair only with the GLU MLP).
+int layer_factors(const dl_layer *L, const dl_factor *(&fs)[7]) {
+  int n = 0;
+  fs[n++] = &L->q;
+  fs[n++] = &L->k;
+  fs[n++] = &L->v;
+  fs[n++] = &L->o;
+  if (L->mlp != DL_MLP_RELU) fs[n++] = &L->gate;
+  fs[n++] = &L->up;
+  fs[n++] = &L->down;
+  return n;
+}
 
 bool use_gemv(int M) { return M <= 64; }
 
@@ -895,16 +909,19 @@ static dl_status layer_dims(const dl_layer *L, int64_t Bsz, int64_t T, int64_t L
   DL_CHECK(T <= L_max, DL_ERR_INVALID_ARG, "T exceeds L_max");
   DL_CHECK(L->hidden > 0 && L->n_q > 0 && L->n_kv > 0 && L->head_dim > 0 && L->ffn > 0,
            DL_ERR_INVALID_ARG, "layer dims must be positive");
-  const dl_factor *fs[7] = {&L->q, &L->k, &L->v, &L->o, &L->gate, &L->up, &L->down};
-  for (const dl_factor *f : fs) {
-    DL_CHECK(f->A && f->B, DL_ERR_INVALID_ARG, "null factor pointer");
-    DL_CHECK(f->k > 0, DL_ERR_INVALID_ARG, "factor rank must be positive");
+  DL_CHECK(L->mlp == DL_MLP_GLU || L->mlp == DL_MLP_RELU, DL_ERR_INVALID_ARG, "unknown MLP kind %d",
+           (int)L->mlp);
+  const dl_factor *fs[7];
+  const int nf = layer_factors(L, fs);
+  for (int i = 0; i < nf; ++i) {
+    DL_CHECK(fs[i]->A && fs[i]->B, DL_ERR_INVALID_ARG, "null factor pointer");
+    DL_CHECK(fs[i]->k > 0, DL_ERR_INVALID_ARG, "factor rank must be positive");
   }
   dl_status st = check_attn_shape(L->n_q, L->n_kv, L->head_dim, L->k.k, L->v.k, L_max, L->dt, T > 1);
   if (st != DL_OK) return st;
   if (L->dt == DL_BF16) {
     bool ok = L->hidden % 64 == 0 && L->ffn % 64 == 0;
-    for (const dl_factor *f : fs) ok = ok && f->k % 64 == 0;
+    for (int i = 0; i < nf; ++i) ok = ok && fs[i]->k % 64 == 0;
     DL_CHECK(ok, DL_ERR_UNSUPPORTED, "bf16 layer needs hidden, ffn and every rank multiples of 64");
   }
   DL_CHECK(Bsz * T <= (1 << 24) && L->hidden <= (1 << 20) && L->ffn <= (1 << 20) &&
@@ -925,7 +942,8 @@ static dl_status layer_dims(const dl_layer *L, int64_t Bsz, int64_t T, int64_t L
   o->rk = static_cast<int>(L->k.k);
   o->rv = static_cast<int>(L->v.k);
   o->ro = static_cast<int>(L->o.k);
-  o->rg = static_cast<int>(L->gate.k);
+  o->relu = L->mlp == DL_MLP_RELU;
+  o->rg = o->relu ? 0 : static_cast<int>(L->gate.k);
   o->ru = static_cast<int>(L->up.k);
   o->rd = static_cast<int>(L->down.k);
   o->L_max = static_cast<int>(L_max);
@@ -995,21 +1013,28 @@ static void layer_gemvs(const dl_layer *L, const LayerDims &D, const LayerWS &w,
   g[G_OUP].seg[0].gamma_f32 = gf32;
   g[G_OUP].seg[0].ssq_out = w.ssq;
 
-  g[G_GUD] = gvargs(M, h, 2);
+  g[G_GUD] = gvargs(M, h, D.relu ? 1 : 2);
   g[G_GUD].x_tiled = 1;
   g[G_GUD].rs_part = w.ssq;
   g[G_GUD].rs_cols = h / 16;
   g[G_GUD].eps = L->rms_eps;
-  g[G_GUD].seg[0] = gvseg_t(L->gate.A, w.x2g, h, w.tg16, D.rg, D.rg, GV_OUT_TILED);
-  g[G_GUD].seg[1] = gvseg_t(L->up.A, w.x2g, h, w.tu16, D.ru, D.ru, GV_OUT_TILED);
-
-  g[G_GUU] = gvargs(M, D.rg, 1);
-  g[G_GUU].K2 = D.ru;
-  g[G_GUU].x_tiled = 1;
-  g[G_GUU].seg[0] = gvseg_t(L->gate.B, w.tg16, D.rg, w.H16, D.f, D.f, GV_OUT_SWIGLU_TILED);
-  g[G_GUU].seg[0].W2 = static_cast<const uint16_t *>(L->up.B);
-  g[G_GUU].seg[0].X2 = w.tu16;
-  g[G_GUU].seg[0].ldx2 = D.ru;
+  if (D.relu) {
+    // non-GLU MLP: H = relu(t_u B_up)
+    g[G_GUD].seg[0] = gvseg_t(L->up.A, w.x2g, h, w.tu16, D.ru, D.ru, GV_OUT_TILED);
+    g[G_GUU] = gvargs(M, D.ru, 1);
+    g[G_GUU].x_tiled = 1;
+    g[G_GUU].seg[0] = gvseg_t(L->up.B, w.tu16, D.ru, w.H16, D.f, D.f, GV_OUT_RELU_TILED);
+  } else {
+    g[G_GUD].seg[0] = gvseg_t(L->gate.A, w.x2g, h, w.tg16, D.rg, D.rg, GV_OUT_TILED);
+    g[G_GUD].seg[1] = gvseg_t(L->up.A, w.x2g, h, w.tu16, D.ru, D.ru, GV_OUT_TILED);
+    g[G_GUU] = gvargs(M, D.rg, 1);
+    g[G_GUU].K2 = D.ru;
+    g[G_GUU].x_tiled = 1;
+    g[G_GUU].seg[0] = gvseg_t(L->gate.B, w.tg16, D.rg, w.H16, D.f, D.f, GV_OUT_SWIGLU_TILED);
+    g[G_GUU].seg[0].W2 = static_cast<const uint16_t *>(L->up.B);
+    g[G_GUU].seg[0].X2 = w.tu16;
+    g[G_GUU].seg[0].ldx2 = D.ru;
+  }
 
   g[G_DD] = gvargs(M, D.f, 1);
   g[G_DD].x_tiled = 1;
@@ -1100,9 +1125,10 @@ static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_
   if (st != DL_OK) return st;
   DL_CHECK(x && y && cache.k && cache.v && past_lens, DL_ERR_INVALID_ARG, "null pointer");
   void *Ck = cache.k, *Cv = cache.v;
-  const dl_factor *fs[7] = {&L->q, &L->k, &L->v, &L->o, &L->gate, &L->up, &L->down};
+  const dl_factor *fs[7];
+  const int nf = layer_factors(L, fs);
   bool al = aligned16(x) && aligned16(y) && aligned16(Ck) && aligned16(Cv) && aligned16(past_lens);
-  for (const dl_factor *f : fs) al = al && aligned16(f->A) && aligned16(f->B);
+  for (int i = 0; i < nf; ++i) al = al && aligned16(fs[i]->A) && aligned16(fs[i]->B);
   al = al && (!x2_out || aligned16(x2_out)) && (!L->attn_norm || aligned16(L->attn_norm)) &&
        (!L->mlp_norm || aligned16(L->mlp_norm));
   DL_CHECK(al, DL_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
@@ -1171,18 +1197,21 @@ static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_
     set_role(R_MLP_NORM);
     DL_HIP(launch_rmsnorm(x2, 1, L->mlp_norm, 1, w.b, 1, M, h, eps, s));
     set_role(R_GATE_UP_DOWN);
-    DL_HIP(gemm_f32(w.b, nullptr, L->gate.A, w.tg, M, D.rg, h, h, D.rg, F32_OUT_STORE, nullptr, 0,
-                    nullptr, 1, 0, s));
+    if (!D.relu)
+      DL_HIP(gemm_f32(w.b, nullptr, L->gate.A, w.tg, M, D.rg, h, h, D.rg, F32_OUT_STORE, nullptr, 0,
+                      nullptr, 1, 0, s));
     DL_HIP(gemm_f32(w.b, nullptr, L->up.A, w.tu, M, D.ru, h, h, D.ru, F32_OUT_STORE, nullptr, 0,
                     nullptr, 1, 0, s));
     set_role(R_GATE_UP_UP);
-    DL_HIP(gemm_f32(w.tg, nullptr, L->gate.B, w.G, M, D.f, D.rg, D.rg, D.f, F32_OUT_STORE, nullptr,
-                    0, nullptr, 1, 0, s));
-    DL_HIP(gemm_f32(w.tu, nullptr, L->up.B, w.U, M, D.f, D.ru, D.ru, D.f, F32_OUT_STORE, nullptr, 0,
-                    nullptr, 1, 0, s));
+    if (!D.relu)
+      DL_HIP(gemm_f32(w.tg, nullptr, L->gate.B, w.G, M, D.f, D.rg, D.rg, D.f, F32_OUT_STORE, nullptr,
+                      0, nullptr, 1, 0, s));
+    DL_HIP(gemm_f32(w.tu, nullptr, L->up.B, w.U, M, D.f, D.ru, D.ru, D.f,
+                    D.relu ? F32_OUT_RELU : F32_OUT_STORE, nullptr, 0, nullptr, 1, 0, s));
     set_role(R_DOWN_DOWN);
-    DL_HIP(gemm_f32(w.G, w.U, L->down.A, w.td, M, D.rd, D.f, D.f, D.rd, F32_OUT_STORE, nullptr, 0,
-                    nullptr, 1, 0, s));
+    // GLU: the down pair reads silu(G) * U, formed as it loads; non-GLU: relu(U)
+    DL_HIP(gemm_f32(D.relu ? w.U : w.G, D.relu ? nullptr : w.U, L->down.A, w.td, M, D.rd, D.f, D.f,
+                    D.rd, F32_OUT_STORE, nullptr, 0, nullptr, 1, 0, s));
     set_role(R_DOWN_UP);
     DL_HIP(gemm_f32(w.td, nullptr, L->down.B, static_cast<float *>(y), M, h, D.rd, D.rd, h,
                     F32_OUT_RESID, x2, h, nullptr, 1, 0, s));
@@ -1286,16 +1315,30 @@ static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_
   DL_HIP(launch_rmsnorm(w.x2f, 1, L->mlp_norm, gf32, w.b16, 0, M, h, eps, s));
   {
     GemmArgs a{};
-    a.nseg = 2;
+    a.nseg = D.relu ? 1 : 2;
     a.M = M;
     a.K = h;
     a.omode = GEMM_OUT_BF16;
-    a.seg[0] = mseg(L->gate.A, w.b16, w.tg16, D.rg, h, D.rg);
-    a.seg[1] = mseg(L->up.A, w.b16, w.tu16, D.ru, h, D.ru);
+    if (D.relu) {
+      a.seg[0] = mseg(L->up.A, w.b16, w.tu16, D.ru, h, D.ru);
+    } else {
+      a.seg[0] = mseg(L->gate.A, w.b16, w.tg16, D.rg, h, D.rg);
+      a.seg[1] = mseg(L->up.A, w.b16, w.tu16, D.ru, h, D.ru);
+    }
     set_role(R_GATE_UP_DOWN);
     DL_HIP(gemm(a, s));
   }
-  {
+  if (D.relu) {
+    // non-GLU MLP: H = relu(t_u B_up), into the buffer the down pair reads
+    GemmArgs a{};
+    a.nseg = 1;
+    a.M = M;
+    a.K = D.ru;
+    a.omode = GEMM_OUT_RELU;
+    a.seg[0] = mseg(L->up.B, w.tu16, w.G16, D.f, D.ru, D.f);
+    set_role(R_GATE_UP_UP);
+    DL_HIP(gemm(a, s));
+  } else {
     // G = t_g B_g, then the up product's epilogue forms H = silu(G) * (t_u B_u)
     // in place over G
     GemmArgs a{};

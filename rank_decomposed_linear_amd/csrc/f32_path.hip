@@ -82,6 +82,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args a) {
       if (n >= a.N) continue;
       float v = acc[i][jj];
       if (a.omode == F32_OUT_RESID) v += a.R[static_cast<size_t>(m) * a.ldr + n];
+      if (a.omode == F32_OUT_RELU) v = fmaxf(v, 0.f);
       a.C[rowoff + n] = v;
     }
   }

@@ -191,7 +191,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
           continue;
         }
         const size_t o = static_cast<size_t>(m) * sg.ldc + n;
-        if (om == GEMM_OUT_SWIGLU) {
+        if (om == GEMM_OUT_RELU) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = fmaxf(v[e], 0.f);
+        } else if (om == GEMM_OUT_SWIGLU) {
           // each element of R is read and then overwritten by this thread only
           const u32x4 gt = *reinterpret_cast<const u32x4 *>(
               static_cast<const uint16_t *>(sg.R) + static_cast<size_t>(m) * sg.ldr + n);

@@ -488,6 +488,10 @@ __device__ __forceinline__ void gemv_item(const GvArgs &a, const int item, const
       st8c<COH>(static_cast<uint16_t *>(sg.out) + tile_off(m, n, sg.N),
                 u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])});
       break;
+    case GV_OUT_RELU_TILED:
+      st8c<COH>(static_cast<uint16_t *>(sg.out) + tile_off(m, n, sg.N),
+                u32x2{pack2(fmaxf(v[0], 0.f), fmaxf(v[1], 0.f)), pack2(fmaxf(v[2], 0.f), fmaxf(v[3], 0.f))});
+      break;
     case GV_OUT_CACHE: {   // key cache page: [kPage, N] operand tiles
       const int b = m / a.T, pos = a.past[b] + m - b * a.T;
       const int pg = cache_page(a.block_table, a.page_stride, b, pos / kPage);

@@ -26,7 +26,8 @@ enum GvOut : int {
   GV_OUT_RES_F32 = 3,   // out f32 = v + R (R f32 if res_f32, else bf16); out2 gets a copy
   GV_OUT_RES_BF16 = 4,  // out bf16 = v + R (R f32)
   GV_OUT_SWIGLU = 5,    // paired: out bf16 = silu(v_first) * v_second
-  GV_OUT_SWIGLU_TILED = 8  // paired, stored as operand tiles [Mpad, N]
+  GV_OUT_SWIGLU_TILED = 8, // paired, stored as operand tiles [Mpad, N]
+  GV_OUT_RELU_TILED = 9    // out bf16 operand tiles [Mpad, N] = max(v, 0)
 };
 
 struct GvSeg {
@@ -112,7 +113,8 @@ enum GemmOut : int {
   GEMM_OUT_F32_RES_BF16 = 2,// C32 f32 = acc + R (bf16 [M, ldr])
   GEMM_OUT_CACHE = 3,       // key cache: row b*T+t -> sequence b, position past[b]+t
   GEMM_OUT_CACHE_T = 4,     // value cache: row b*T+t, column n -> sequence b, (position past[b]+t, rank n)
-  GEMM_OUT_SWIGLU = 5       // C bf16 = silu(R) * acc, R bf16 [M, ldr] (the gate values; C may be R)
+  GEMM_OUT_SWIGLU = 5,      // C bf16 = silu(R) * acc, R bf16 [M, ldr] (the gate values; C may be R)
+  GEMM_OUT_RELU = 6         // C bf16 = max(acc, 0)
 };
 
 struct GemmSeg {
@@ -197,7 +199,8 @@ enum F32Out : int {
   F32_OUT_STORE = 0,     // C = acc
   F32_OUT_RESID = 1,     // C = acc + R
   F32_OUT_CACHE = 2,     // row b*T+t -> cache[b, past[b]+t]
-  F32_OUT_CACHE_T = 3    // row b*T+t, column n -> cache[b, n, past[b]+t]
+  F32_OUT_CACHE_T = 3,   // row b*T+t, column n -> cache[b, n, past[b]+t]
+  F32_OUT_RELU = 4       // C = max(acc, 0)
 };
 struct GemmF32Args {
   const float *X, *X2;   // X2 non-null: X = silu(X) * X2

@@ -114,13 +114,18 @@ class LayerShape:
     dtype: str                           # "f32" or "bf16"
     rope_theta: float
     rms_eps: float = 1e-5
+    mlp: str = "glu"                     # "glu" (SwiGLU) or "relu" (non-GLU, no gate pair)
 
     def rank(self, name: str) -> int:
         return dict(self.ranks)[name]
 
+    def projections(self) -> Tuple[str, ...]:
+        """The factor pairs the layer has (no gate pair in a non-GLU MLP)."""
+        return tuple(p for p in PROJECTIONS if not (p == "gate" and self.mlp == "relu"))
+
     def shapes(self) -> Dict[str, Tuple[int, int]]:
-        return projection_shapes(self.hidden, self.n_q, self.n_kv,
-                                 self.head_dim, self.ffn)
+        shp = projection_shapes(self.hidden, self.n_q, self.n_kv, self.head_dim, self.ffn)
+        return {p: shp[p] for p in self.projections()}
 
     def weight_elements(self) -> int:
         return sum(factor_params(m, n, self.rank(p))
@@ -129,15 +134,17 @@ class LayerShape:
 
 def make_shape(hidden, n_q, n_kv, head_dim, ffn, dtype, rope_theta,
                compression_pct: Optional[int] = None,
-               fixed_rank: Optional[int] = None) -> LayerShape:
+               fixed_rank: Optional[int] = None, mlp: str = "glu") -> LayerShape:
     shp = projection_shapes(hidden, n_q, n_kv, head_dim, ffn)
     ranks = []
     for p in PROJECTIONS:
+        if p == "gate" and mlp == "relu":
+            continue
         m, n = shp[p]
         k = fixed_rank if fixed_rank is not None else rank_floor64(m, n, compression_pct)
         ranks.append((p, k))
     return LayerShape(hidden, n_q, n_kv, head_dim, ffn, tuple(ranks), dtype,
-                      rope_theta)
+                      rope_theta, mlp=mlp)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -234,7 +241,7 @@ def draw_weights(w: Workload, rng: np.random.Generator) -> LayerWeights:
     by i^-1/2 before encoding."""
     shp = w.shape
     out = {}
-    for p in PROJECTIONS:
+    for p in shp.projections():
         m, n = shp.shapes()[p]
         k = shp.rank(p)
         A = _normal(rng, (m, k), w.factor_std)

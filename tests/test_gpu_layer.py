@@ -39,7 +39,7 @@ def make_gpu_layer(B, weights: W.LayerWeights):
     gain = lambda g: None if g is None else to_dev(g)
     return B.DecomposedLayer(facs, shp.hidden, shp.n_q, shp.n_kv, shp.head_dim, shp.ffn,
                              shp.rope_theta, shp.rms_eps, attn_norm=gain(weights.attn_norm),
-                             mlp_norm=gain(weights.mlp_norm))
+                             mlp_norm=gain(weights.mlp_norm), mlp=shp.mlp)
 
 
 def oracle_layer(weights, x, ck, cv, past, seqs=None):
@@ -49,7 +49,8 @@ def oracle_layer(weights, x, ck, cv, past, seqs=None):
     gain = lambda g: None if g is None else f64(g)
     return ref.decomposed_layer(F, f64(x)[sl], f64(ck)[sl], f64(cv)[sl], np.asarray(past)[sl],
                                 shp.n_q, shp.n_kv, shp.head_dim, shp.rope_theta, shp.rms_eps,
-                                attn_norm=gain(weights.attn_norm), mlp_norm=gain(weights.mlp_norm))
+                                attn_norm=gain(weights.attn_norm), mlp_norm=gain(weights.mlp_norm),
+                                mlp=shp.mlp)
 
 
 #: Bound on the residual-branch deltas (x2 - x and y - x2). The outputs
@@ -125,14 +126,16 @@ SMALL = [
 
 
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
-def test_small_layer(B, case, rank_up=None, gains=False):
+def test_small_layer(B, case, rank_up=None, gains=False, mlp="glu"):
     name, dt, h, nq, nkv, d, f, ra, rkv, rm, Bsz, T, past, L_max, theta = case
-    print(f"layer {case} rank_up={rank_up} gains={gains}", flush=True)
+    print(f"layer {case} rank_up={rank_up} gains={gains} mlp={mlp}", flush=True)
     r = np.random.Generator(np.random.PCG64(sum(map(ord, name))))
     if past is None:
         past = list(r.integers(0, L_max - T, size=Bsz))
     shp_ranks = {"q": ra, "k": rkv, "v": rkv, "o": ra, "gate": rm, "up": rank_up or rm, "down": rm}
-    shp = W.LayerShape(h, nq, nkv, d, f, tuple((p, shp_ranks[p]) for p in W.PROJECTIONS), dt, theta)
+    projs = [p for p in W.PROJECTIONS if not (p == "gate" and mlp == "relu")]
+    shp = W.LayerShape(h, nq, nkv, d, f, tuple((p, shp_ranks[p]) for p in projs), dt, theta,
+                       mlp=mlp)
     facs = {}
     for p, (m, n) in shp.shapes().items():
         facs[p] = (rand(r, (m, shp.rank(p)), 0.05, dt), rand(r, (shp.rank(p), n), 0.05, dt))
@@ -150,6 +153,14 @@ def test_small_layer(B, case, rank_up=None, gains=False):
     y, x2 = run_layer(B, layer, x, ck, cv, past)
     want = oracle_layer(weights, x, ck0, cv0, past)
     check_step(dt, x, y, x2, ck, cv, want, past, T)
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_layer_relu_mlp(B, case):
+    """The non-GLU MLP (relu of the up pair, then the down pair; no gate
+    factor) on every path: the decode GEMV chain's ReLU tile epilogue, the
+    prefill GEMM's ReLU epilogue, the f32 kernels."""
+    test_small_layer(B, case, mlp="relu", gains=True)
 
 
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])

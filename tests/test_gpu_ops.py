@@ -126,6 +126,17 @@ DECODE_CASES = [
     (2, 8, 2, 128, 640, 640, 2112, [2049, 700], 500000.0, "bf16"),   # ranks staged in chunks
     (1, 40, 8, 128, 64, 128, 576, [515], 10000.0, "bf16"),             # 5 heads per kv head
     (2, 12, 12, 64, 1024, 960, 192, [130, 64], 10000.0, "bf16"),       # largest ranks
+    # several 64-position groups per wave: the running max shared across
+    # groups, value products two groups behind, key tiles requested by the
+    # group before (rank-step counts that are and are not multiples of the
+    # prefetch depth), ragged and partial last groups
+    (8, 32, 8, 128, 448, 448, 1088, [1025, 1000, 700, 1025, 513, 64, 1025, 999], 500000.0, "bf16"),
+    (8, 16, 4, 128, 640, 640, 2112, [2049, 2049, 1900, 2000, 1, 2049, 1500, 2049], 500000.0,
+     "bf16"),                                                          # ranks staged in chunks
+    (16, 16, 4, 128, 64, 128, 2112, [2049] * 8 + [1111] * 8, 10000.0, "bf16"),   # 2 rank steps
+    (16, 32, 8, 128, 128, 256, 1088, [1025] * 15 + [300], 500000.0, "bf16"),     # 4 rank steps
+    (16, 8, 8, 128, 256, 256, 1088, [1025] * 16, 0.0, "bf16"),                   # MHA
+    (8, 12, 12, 64, 1024, 960, 1088, [1025] * 7 + [777], 10000.0, "bf16"),
     (2, 4, 4, 64, 64, 64, 40, [33, 40], 10000.0, "f32"),
     (2, 6, 2, 32, 12, 20, 50, [1, 50], 100.0, "f32"),
 ]

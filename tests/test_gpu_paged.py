@@ -224,6 +224,30 @@ def test_paged_attention_ops(B, G, theta):
         assert relerr(to_host(outp)[b:b + 1], wb) <= TOL["bf16"]
 
 
+def test_paged_decode_attention_long(B):
+    """Paged decode attention where every wave walks several position groups
+    (16 sequences of up to 17 pages on a shuffled pool)."""
+    import torch
+    print("paged decode attention, long contexts", flush=True)
+    r = np.random.Generator(np.random.PCG64(85))
+    n_kv, G, d, rk, rv = 8, 4, 128, 448, 448
+    n_q = G * n_kv
+    Bsz, pages_per_seq = 16, 17
+    num_pages = Bsz * pages_per_seq + 3
+    table, pk, pv = make_pool(r, Bsz, pages_per_seq, num_pages, rk, rv)
+    gk, gv, gt, cache = dev_pool(B, pk, pv, table)
+    Bk, Bv = rand(r, (rk, n_kv * d), 0.05, "bf16"), rand(r, (rv, n_kv * d), 0.05, "bf16")
+    lens = np.array([1025, 1088, 900, 65, 1025, 1025, 1, 640] * 2, np.int32)
+    q = rand(r, (Bsz, n_q, d), 1.0, "bf16")
+    out = B.lowrank_attn_decode_paged(to_dev(q), cache, to_dev(W.to_library_factor(Bk)),
+                                      to_dev(W.to_library_factor(Bv)), to_dev(lens), n_kv, 0.0,
+                                      500000.0)
+    torch.cuda.synchronize()
+    want = ref.attn_decode_paged(f64(q), f64(pk), f64(pv), table, f64(Bk), f64(Bv), lens, n_kv,
+                                 500000.0)
+    assert relerr(to_host(out), want) <= TOL["bf16"]
+
+
 def test_paged_decode_graph_replay(B):
     """One decode step captured in a HIP graph, replayed six times while the
     device-resident inputs, lengths and block table advance (two sequences
