@@ -31,7 +31,8 @@ bool g_open = false;
 const char *const kKindNames[K_NUM_KINDS] = {
     "rmsnorm",       "fill",        "convert",      "store_cache_rows",
     "gemv_bf16",     "gemm_bf16",   "gemm_f32",     "pack_up_factor",
-    "attn_decode_bf16", "attn_combine", "attn_prefill_bf16", "attn_f32", "gemv_chain"};
+    "attn_decode_bf16", "attn_combine", "attn_prefill_bf16", "attn_f32", "gemv_chain",
+    "attn_latent"};
 const char *const kRoleNames[R_NUM_ROLES] = {
     "other",        "attn_norm",    "qkv_down", "kv_store",  "q_up",
     "attention",    "o_down",       "o_up",     "mlp_norm",  "gate_up_down",
@@ -266,34 +267,77 @@ DecodePlan plan_decode(int64_t Bsz, int64_t n_kv, int64_t L_max) {
   return {ns, len};
 }
 
-// Attention scratch: split partials and merge counters (decode). The
-// counters must be zero before the launch.
+// Latent-space decode attention (rotary embedding off): groups of 16 query
+// heads; splits no longer than one workgroup's LDS holds, enough of them
+// for about one workgroup per CU.
+constexpr int kLatentHeads = 16;
+struct LatentPlan {
+  int ngroups = 0, nsplit = 0, split_len = 0;   // nsplit == 0: not available
+};
+LatentPlan plan_latent(int64_t Bsz, int64_t n_q, int64_t r_k, int64_t L_max) {
+  LatentPlan p;
+  const int maxs = latent_attn_max_split(static_cast<int>(r_k));
+  if (maxs < 64) return p;
+  p.ngroups = static_cast<int>((n_q + kLatentHeads - 1) / kLatentHeads);
+  const int target = env_int("DL_ATTN_TARGET_WGS", 256);
+  int ns = static_cast<int>((target + Bsz * p.ngroups - 1) / (Bsz * p.ngroups));
+  ns = std::max<int64_t>(ns, (L_max + maxs - 1) / maxs);
+  ns = std::min<int64_t>(ns, (L_max + 63) / 64);
+  int len = static_cast<int>((L_max + ns - 1) / ns);
+  len = std::min((len + 63) / 64 * 64, maxs);
+  p.nsplit = static_cast<int>((L_max + len - 1) / len);
+  p.split_len = len;
+  return p;
+}
+
+// Attention scratch: split partials and merge counters (decode; the
+// counters must be zero before the launch), plus the latent path's
+// absorbed queries, normalised U rows and partials.
 struct AttnWS {
   float *part = nullptr;
   int *counters = nullptr;
   int n_counters = 0;
+  uint16_t *lat_q = nullptr, *lat_u = nullptr;
+  float *lat_part = nullptr;
+  int *lat_counters = nullptr;
 };
 
-AttnWS carve_attn(Carver &c, int64_t Bsz, int64_t n_q, int64_t n_kv, int64_t d, int64_t L_max,
-                  bool decode) {
+AttnWS carve_attn(Carver &c, int64_t Bsz, int64_t n_q, int64_t n_kv, int64_t d, int64_t r_k,
+                  int64_t r_v, int64_t L_max, bool decode) {
   AttnWS w;
   if (decode) {
     const DecodePlan p = plan_decode(Bsz, n_kv, L_max);
+    const LatentPlan lp = plan_latent(Bsz, n_q, r_k, L_max);
     w.part = c.take<float>(static_cast<size_t>(Bsz * n_q * p.nsplit * (d + 2)));
-    w.n_counters = static_cast<int>(Bsz * n_kv);
+    w.n_counters = static_cast<int>(Bsz * n_kv + (lp.nsplit ? Bsz * lp.ngroups : 0));
     w.counters = c.take<int>(static_cast<size_t>(w.n_counters));
+    if (lp.nsplit) {
+      w.lat_counters = w.counters + Bsz * n_kv;
+      w.lat_q = c.take<uint16_t>(static_cast<size_t>(Bsz * lp.ngroups * kLatentHeads * r_k));
+      w.lat_u = c.take<uint16_t>(static_cast<size_t>(Bsz * n_q * r_v));
+      if (lp.nsplit > 1)
+        w.lat_part = c.take<float>(static_cast<size_t>(Bsz * lp.ngroups) * lp.nsplit * kLatentHeads *
+                                   (r_v + 2));
+    }
   }
   return w;
 }
 
-size_t attn_bf16_ws(int64_t Bsz, int64_t n_q, int64_t n_kv, int64_t d, int64_t L_max, bool decode) {
+size_t attn_bf16_ws(int64_t Bsz, int64_t n_q, int64_t n_kv, int64_t d, int64_t r_k, int64_t r_v,
+                    int64_t L_max, bool decode) {
   Carver c(nullptr);
-  carve_attn(c, Bsz, n_q, n_kv, d, L_max, decode);
+  carve_attn(c, Bsz, n_q, n_kv, d, r_k, r_v, L_max, decode);
   return c.off;
 }
 
+// Decode attention without the rotary embedding runs in the latent space
+// when one workgroup's LDS holds the group's absorbed queries.
+bool use_latent_decode(float theta, int64_t r_k) {
+  return theta == 0.f && latent_attn_max_split(static_cast<int>(r_k)) >= 64;
+}
+
 dl_status check_attn_shape(int64_t n_q, int64_t n_kv, int64_t d, int64_t r_k, int64_t r_v,
-                           int64_t L_max, dl_dtype dt, bool prefill) {
+                           int64_t L_max, dl_dtype dt, bool prefill, float theta) {
   DL_CHECK(n_q > 0 && n_kv > 0 && d > 0 && r_k > 0 && r_v > 0, DL_ERR_INVALID_ARG,
            "attention dims must be positive");
   DL_CHECK(n_q % n_kv == 0, DL_ERR_INVALID_ARG, "n_q (%lld) must be a multiple of n_kv (%lld)",
@@ -302,8 +346,11 @@ dl_status check_attn_shape(int64_t n_q, int64_t n_kv, int64_t d, int64_t r_k, in
     DL_CHECK(d == 64 || d == 128, DL_ERR_UNSUPPORTED, "bf16 attention needs head_dim 64 or 128");
     DL_CHECK(r_k % 64 == 0 && r_v % 64 == 0, DL_ERR_UNSUPPORTED,
              "bf16 attention needs r_k, r_v multiples of 64");
-    DL_CHECK(r_v <= attn_decode_max_rank_v(), DL_ERR_UNSUPPORTED,
-             "bf16 attention needs r_v <= %d", attn_decode_max_rank_v());
+    // (the rebuilding decode kernel keeps U for r_v ranks in registers; the
+    // latent decode kernel and the prefill kernel stream any rank)
+    DL_CHECK(prefill || use_latent_decode(theta, r_k) || r_v <= attn_decode_max_rank_v(),
+             DL_ERR_UNSUPPORTED, "bf16 decode attention with the rotary embedding needs r_v <= %d",
+             attn_decode_max_rank_v());
     DL_CHECK(L_max % kPage == 0, DL_ERR_UNSUPPORTED,
              "bf16 caches need L_max to be a multiple of %d (cache pages)", kPage);
     const int64_t G = n_q / n_kv;
@@ -375,6 +422,39 @@ hipError_t run_attn_bf16(const void *q, int q_f32, int ldq, const CacheRef &c,
                          float theta, const AttnWS &w, hipStream_t s) {
   const float scale = (sm_scale != 0.f ? sm_scale : 1.0f / sqrtf(static_cast<float>(d))) * kLog2e;
   const int L_max = static_cast<int>(c.L_max);
+  if (decode && use_latent_decode(theta, r_k)) {
+    const LatentPlan p = plan_latent(Bsz, n_q, r_k, L_max);
+    LatentAttnArgs a{};
+    a.q = q;
+    a.q_f32 = q_f32;
+    a.ck = static_cast<const uint16_t *>(c.k);
+    a.cv = static_cast<const uint16_t *>(c.v);
+    a.block_table = c.table;
+    a.page_stride = c.stride;
+    a.bk = static_cast<const uint16_t *>(B_k);
+    a.bv = static_cast<const uint16_t *>(B_v);
+    a.ctx_lens = lens;
+    a.ctx_offset = ctx_offset;
+    a.out = out;
+    a.out_f32 = out_f32;
+    a.out_tiled = out_tiled;
+    a.qt = w.lat_q;
+    a.u = w.lat_u;
+    a.part = w.lat_part;
+    a.counters = w.lat_counters;
+    a.Bsz = Bsz;
+    a.n_q = n_q;
+    a.n_kv = n_kv;
+    a.d = d;
+    a.r_k = r_k;
+    a.r_v = r_v;
+    a.L_max = L_max;
+    a.ngroups = p.ngroups;
+    a.nsplit = p.nsplit;
+    a.split_len = p.split_len;
+    a.scale_log2 = scale;
+    return launch_latent_attn_bf16(a, s);
+  }
   if (decode) {
     const DecodePlan p = plan_decode(Bsz, n_kv, L_max);
     AttnDecodeArgs a{};
@@ -762,18 +842,14 @@ dl_status dl_lowrank_kv_append_paged(const void *x, const void *A_k, const void 
 size_t dl_attn_decode_workspace(int64_t Bsz, int64_t n_q, int64_t n_kv, int64_t d, int64_t r_k,
                                 int64_t r_v, int64_t L_max, dl_dtype dt) {
   if (dt != DL_BF16 || Bsz <= 0 || n_kv <= 0 || L_max <= 0) return 0;
-  (void)r_k;
-  (void)r_v;
-  return attn_bf16_ws(Bsz, n_q, n_kv, d, L_max, true);
+  return attn_bf16_ws(Bsz, n_q, n_kv, d, r_k, r_v, L_max, true);
 }
 
 size_t dl_attn_prefill_workspace(int64_t Bsz, int64_t T, int64_t n_q, int64_t n_kv, int64_t d,
                                  int64_t r_k, int64_t r_v, int64_t L_max, dl_dtype dt) {
   (void)T;
   if (dt != DL_BF16 || Bsz <= 0 || n_kv <= 0 || L_max <= 0) return 0;
-  (void)r_k;
-  (void)r_v;
-  return attn_bf16_ws(Bsz, n_q, n_kv, d, L_max, false);
+  return attn_bf16_ws(Bsz, n_q, n_kv, d, r_k, r_v, L_max, false);
 }
 
 static dl_status attn_common(const void *q, const CacheRef &cache, const void *B_k,
@@ -785,7 +861,7 @@ static dl_status attn_common(const void *q, const CacheRef &cache, const void *B
   DL_CHECK(q && cache.k && cache.v && B_k && B_v && lens && out, DL_ERR_INVALID_ARG, "null pointer");
   DL_CHECK(Bsz > 0 && T > 0 && L_max > 0, DL_ERR_INVALID_ARG, "dims must be positive");
   DL_CHECK(T <= L_max, DL_ERR_INVALID_ARG, "T exceeds L_max");
-  dl_status st = check_attn_shape(n_q, n_kv, d, r_k, r_v, L_max, dt, !decode);
+  dl_status st = check_attn_shape(n_q, n_kv, d, r_k, r_v, L_max, dt, !decode, rope_theta);
   if (st != DL_OK) return st;
   DL_CHECK(Bsz * L_max * std::max(r_k, r_v) <= ((int64_t)1 << 40) && Bsz * T * n_q * d <= INT32_MAX &&
                L_max <= INT32_MAX / 2,
@@ -829,7 +905,7 @@ static dl_status attn_common(const void *q, const CacheRef &cache, const void *B
     return DL_OK;
   }
   Carver c(ws);
-  const AttnWS aw = carve_attn(c, Bsz, n_q, n_kv, d, L_max, decode);
+  const AttnWS aw = carve_attn(c, Bsz, n_q, n_kv, d, r_k, r_v, L_max, decode);
   if (aw.counters) {
     FillRegion z[1] = {{reinterpret_cast<float *>(aw.counters), nullptr, 0, aw.n_counters}};
     DL_HIP(launch_fill(z, 1, s));
@@ -917,7 +993,8 @@ static dl_status layer_dims(const dl_layer *L, int64_t Bsz, int64_t T, int64_t L
     DL_CHECK(fs[i]->A && fs[i]->B, DL_ERR_INVALID_ARG, "null factor pointer");
     DL_CHECK(fs[i]->k > 0, DL_ERR_INVALID_ARG, "factor rank must be positive");
   }
-  dl_status st = check_attn_shape(L->n_q, L->n_kv, L->head_dim, L->k.k, L->v.k, L_max, L->dt, T > 1);
+  dl_status st = check_attn_shape(L->n_q, L->n_kv, L->head_dim, L->k.k, L->v.k, L_max, L->dt, T > 1,
+                                  L->rope_theta);
   if (st != DL_OK) return st;
   if (L->dt == DL_BF16) {
     bool ok = L->hidden % 64 == 0 && L->ffn % 64 == 0;
@@ -1112,7 +1189,7 @@ size_t dl_layer_workspace(const dl_layer *L, int64_t Bsz, int64_t T, int64_t L_m
   LayerWS w{};
   carve_layer(c, D, L, w);
   if (L->dt == DL_BF16)
-    c.off += attn_bf16_ws(D.Bsz, D.nq, D.nkv, D.d, D.L_max, D.T == 1) + kAlign;
+    c.off += attn_bf16_ws(D.Bsz, D.nq, D.nkv, D.d, D.rk, D.rv, D.L_max, D.T == 1) + kAlign;
   return c.off;
 }
 
@@ -1145,7 +1222,7 @@ static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_
   LayerWS w{};
   carve_layer(c, D, L, w);
   AttnWS aw;
-  if (L->dt == DL_BF16) aw = carve_attn(c, D.Bsz, D.nq, D.nkv, D.d, D.L_max, D.T == 1);
+  if (L->dt == DL_BF16) aw = carve_attn(c, D.Bsz, D.nq, D.nkv, D.d, D.rk, D.rv, D.L_max, D.T == 1);
   const int M = D.M, h = D.h, qd = D.qd();
   const float eps = L->rms_eps;
   const int gf32 = L->dt == DL_F32;

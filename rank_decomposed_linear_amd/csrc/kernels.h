@@ -170,6 +170,31 @@ struct AttnDecodeArgs {
   float theta;
   int q_f32, out_f32, out_tiled;
 };
+// Decode attention in the latent space (rotary embedding off): Q~ = B_k q,
+// S = C_k Q~, U = softmax(S) C_v, o = U B_v (three launches).
+struct LatentAttnArgs {
+  const void *q;       // [Bsz, n_q, d] bf16 or f32 (q_f32)
+  const uint16_t *ck, *cv;        // cache pools (pages, as AttnDecodeArgs)
+  const int32_t *block_table;     // NULL: contiguous, page_stride pages per sequence
+  int page_stride;
+  const uint16_t *bk, *bv;        // up factors, [n_kv * d, r] in operand tiles
+  const int32_t *ctx_lens;
+  void *out;           // [Bsz, n_q, d] bf16 (f32 with out_f32; operand tiles with out_tiled)
+  uint16_t *qt;        // workspace [Bsz, ngroups, 16, r_k] bf16 operand tiles (Q~, scaled)
+  uint16_t *u;         // workspace [Bsz, n_q, r_v] bf16 (U / l)
+  float *part;         // workspace [Bsz, ngroups, nsplit, 16, r_v + 2] (nsplit > 1)
+  int *counters;       // [Bsz * ngroups], zero on entry, left zero
+  int Bsz, n_q, n_kv, d, r_k, r_v, L_max;
+  int ctx_offset;
+  int ngroups, nsplit, split_len;
+  int pitch, lds_q, lds_s;   // set by the launcher
+  float scale_log2;
+  int q_f32, out_f32, out_tiled;
+};
+// longest context split one latent-attention workgroup holds (0: r_k too large)
+int latent_attn_max_split(int r_k);
+hipError_t launch_latent_attn_bf16(LatentAttnArgs a, hipStream_t s);
+
 int attn_decode_split_granule();
 int attn_decode_max_rank_v();   // largest r_v the decode kernel accepts
 hipError_t launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s);

@@ -19,6 +19,7 @@ enum KernelKind : int {
   K_ATTN_PREFILL,
   K_ATTN_F32,
   K_GEMV_CHAIN,
+  K_ATTN_LATENT,
   K_NUM_KINDS
 };
 

@@ -137,6 +137,13 @@ DECODE_CASES = [
     (16, 32, 8, 128, 128, 256, 1088, [1025] * 15 + [300], 500000.0, "bf16"),     # 4 rank steps
     (16, 8, 8, 128, 256, 256, 1088, [1025] * 16, 0.0, "bf16"),                   # MHA
     (8, 12, 12, 64, 1024, 960, 1088, [1025] * 7 + [777], 10000.0, "bf16"),
+    # rotary embedding off: attention in the latent space (B_k absorbed into
+    # the query, B_v applied to P C_v); MHA with ranks past the rebuilding
+    # kernel's limit, several context splits, head groups of 16 with a
+    # partial last group, d = 64
+    (4, 56, 56, 128, 2112, 2112, 576, [512, 100, 1, 575], 0.0, "bf16"),
+    (2, 64, 8, 128, 448, 448, 8256, [8193, 3000], 0.0, "bf16"),
+    (3, 40, 8, 64, 512, 640, 1088, [1025, 17, 700], 0.0, "bf16"),
     (2, 4, 4, 64, 64, 64, 40, [33, 40], 10000.0, "f32"),
     (2, 6, 2, 32, 12, 20, 50, [1, 50], 100.0, "f32"),
 ]
