@@ -295,6 +295,7 @@ LatentPlan plan_latent(int64_t Bsz, int64_t n_q, int64_t r_k, int64_t L_max) {
 // absorbed queries, normalised U rows and partials.
 struct AttnWS {
   float *part = nullptr;
+  float *uglob = nullptr;   // rebuilding decode kernel's U between chunks (r_v > 512)
   int *counters = nullptr;
   int n_counters = 0;
   uint16_t *lat_q = nullptr, *lat_u = nullptr;
@@ -309,6 +310,8 @@ AttnWS carve_attn(Carver &c, int64_t Bsz, int64_t n_q, int64_t n_kv, int64_t d, 
     const DecodePlan p = plan_decode(Bsz, n_kv, L_max);
     const LatentPlan lp = plan_latent(Bsz, n_q, r_k, L_max);
     w.part = c.take<float>(static_cast<size_t>(Bsz * n_q * p.nsplit * (d + 2)));
+    if (attn_decode_value_passes(static_cast<int>(r_v)) > 1)
+      w.uglob = c.take<float>(static_cast<size_t>(Bsz * n_kv * p.nsplit) * 16 * r_v);
     w.n_counters = static_cast<int>(Bsz * n_kv + (lp.nsplit ? Bsz * lp.ngroups : 0));
     w.counters = c.take<int>(static_cast<size_t>(w.n_counters));
     if (lp.nsplit) {
@@ -346,11 +349,7 @@ dl_status check_attn_shape(int64_t n_q, int64_t n_kv, int64_t d, int64_t r_k, in
     DL_CHECK(d == 64 || d == 128, DL_ERR_UNSUPPORTED, "bf16 attention needs head_dim 64 or 128");
     DL_CHECK(r_k % 64 == 0 && r_v % 64 == 0, DL_ERR_UNSUPPORTED,
              "bf16 attention needs r_k, r_v multiples of 64");
-    // (the rebuilding decode kernel keeps U for r_v ranks in registers; the
-    // latent decode kernel and the prefill kernel stream any rank)
-    DL_CHECK(prefill || use_latent_decode(theta, r_k) || r_v <= attn_decode_max_rank_v(),
-             DL_ERR_UNSUPPORTED, "bf16 decode attention with the rotary embedding needs r_v <= %d",
-             attn_decode_max_rank_v());
+    DL_CHECK(r_k <= 8192 && r_v <= 8192, DL_ERR_UNSUPPORTED, "bf16 attention needs r_k, r_v <= 8192");
     DL_CHECK(L_max % kPage == 0, DL_ERR_UNSUPPORTED,
              "bf16 caches need L_max to be a multiple of %d (cache pages)", kPage);
     const int64_t G = n_q / n_kv;
@@ -472,6 +471,7 @@ hipError_t run_attn_bf16(const void *q, int q_f32, int ldq, const CacheRef &c,
     a.out_f32 = out_f32;
     a.out_tiled = out_tiled;
     a.part = w.part;
+    a.uglob = w.uglob;
     a.counters = w.counters;
     a.Bsz = Bsz;
     a.n_q = n_q;

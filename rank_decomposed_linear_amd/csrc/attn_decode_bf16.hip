@@ -63,6 +63,13 @@ __device__ __forceinline__ float load_coherent(const float *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void wait_memory() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ f32x4 load4_coherent(const float *p) {
+  return f32x4{load_coherent(p), load_coherent(p + 1), load_coherent(p + 2), load_coherent(p + 3)};
+}
+__device__ __forceinline__ void store4_coherent(float *p, f32x4 v) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) store_coherent(p + r, v[r]);
+}
 
 // XCD-aware order: consecutive work items (the kv heads of one context
 // split of one sequence, which read the same cache rows) share an XCD.
@@ -252,6 +259,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
   int rb[RBW];
 #pragma unroll
   for (int i = 0; i < RBW; ++i) rb[i] = min(wave + kNW * i, nrb - 1);
+  // More rank blocks than the accumulators hold (r_v > 64 RBW): phase 2
+  // runs in passes of kNW * RBW blocks and U lives in the workspace between
+  // chunks (row j of this work item's [16, r_v] block; each lane reads and
+  // writes only its own elements until the final product).
+  const int npass = a.vpasses;
+  float *ug = npass > 1 ? a.uglob + (static_cast<size_t>(w) * 16 + j) * a.r_v : nullptr;
 
   for (int c0 = p_begin; c0 < p_end; c0 += pitch) {
     const int c1 = min(c0 + pitch, p_end);
@@ -456,8 +469,27 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
 #pragma unroll
     for (int wv = 0; wv < kNW; ++wv) lsum += psw[wv][j];
     l_run = l_run * alpha + lsum;
+    for (int pass = 0; pass < npass; ++pass) {
+    if (npass > 1) {
+      if (pass > 0) {
 #pragma unroll
-    for (int i = 0; i < RBW; ++i) uacc[i] *= alpha;
+        for (int i = 0; i < RBW; ++i) rb[i] = min(wave + kNW * (RBW * pass + i), nrb - 1);
+#pragma unroll
+        for (int d = 0; d < kVDepth; ++d) {
+          vload(vr[d], min(d, nU - 1));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // these blocks' U so far (none before the first chunk), rescaled
+#pragma unroll
+      for (int i = 0; i < RBW; ++i) {
+        const f32x4 prev = c0 != p_begin ? load4_coherent(ug + 16 * rb[i] + 4 * grp) : f32x4{0.f, 0.f, 0.f, 0.f};
+        uacc[i] = prev * alpha;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < RBW; ++i) uacc[i] *= alpha;
+    }
     for (int u0 = 0; u0 < nU; u0 += kVDepth) {
 #pragma unroll
       for (int d = 0; d < kVDepth; ++d) {
@@ -478,16 +510,30 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    if (npass > 1) {
+#pragma unroll
+      for (int i = 0; i < RBW; ++i)
+        if (wave + kNW * (RBW * pass + i) < nrb) store4_coherent(ug + 16 * rb[i] + 4 * grp, uacc[i]);
+    }
+    }   // passes
+    if (npass > 1) {
+      // the next chunk's early value loads are for the first pass
+#pragma unroll
+      for (int i = 0; i < RBW; ++i) rb[i] = min(wave + kNW * i, nrb - 1);
+    }
   }
 
   // ---------------- O^T = B_v^T U^T (MFMA, U rounded to bf16) ----------------
+  if (npass > 1) wait_memory();   // U rows of the other waves complete before the barrier
   __syncthreads();   // LDS is reused for U
   float *ulds = reinterpret_cast<float *>(dlds);   // [16][r_v], rows >= G zero
   // lane (head j, grp) holds U^T[16 rb + 4grp + r][j]
+  if (npass == 1) {
 #pragma unroll
-  for (int i = 0; i < RBW; ++i)
+    for (int i = 0; i < RBW; ++i)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) ulds[j * a.r_v + 16 * rb[i] + 4 * grp + r] = j < G ? uacc[i][r] : 0.f;
+      for (int r = 0; r < 4; ++r) ulds[j * a.r_v + 16 * rb[i] + 4 * grp + r] = j < G ? uacc[i][r] : 0.f;
+  }
   if (wave == 0 && grp == 0) {
     mfin[j] = m_run;
     lfin[j] = l_run;
@@ -501,6 +547,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
 #pragma unroll
     for (int x = 0; x < OBW; ++x) oacc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
     const float *urow = ulds + j * a.r_v + 8 * grp;
+    const float *urow_g = npass > 1 ? a.uglob + (static_cast<size_t>(w) * 16 + j) * a.r_v + 8 * grp : nullptr;
     for (int s0 = 0; s0 < a.r_v / 32; s0 += 2) {   // r_v / 32 is even
       u32x4 av[2][OBW];
 #pragma unroll
@@ -510,8 +557,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
           av[q][x] = ld16(a.bv + frag_off(g * NB + OBW * wave + x, s0 + q, a.r_v, lane));
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const f32x4 u0 = *reinterpret_cast<const f32x4 *>(urow + 32 * (s0 + q));
-        const f32x4 u1 = *reinterpret_cast<const f32x4 *>(urow + 32 * (s0 + q) + 4);
+        f32x4 u0, u1;
+        if (npass > 1) {   // (rows j >= G hold finite values; their outputs are not stored)
+          u0 = load4_coherent(urow_g + 32 * (s0 + q));
+          u1 = load4_coherent(urow_g + 32 * (s0 + q) + 4);
+        } else {
+          u0 = *reinterpret_cast<const f32x4 *>(urow + 32 * (s0 + q));
+          u1 = *reinterpret_cast<const f32x4 *>(urow + 32 * (s0 + q) + 4);
+        }
         const u32x4 bop = u32x4{pack2(u0[0], u0[1]), pack2(u0[2], u0[3]), pack2(u1[0], u1[1]), pack2(u1[2], u1[3])};
 #pragma unroll
         for (int x = 0; x < OBW; ++x) oacc[x] = mfma_bf16(av[q][x], bop, oacc[x]);
@@ -641,7 +694,7 @@ int plan_lds(AttnDecodeArgs &a, int dyn, int nb) {
     rs_cap = min(rs_cap, nrs);
   }
   pitch = min(pitch, want);
-  if (pitch < kSlice || rs_cap < 2 || 64 * a.r_v > dyn) return 0;
+  if (pitch < kSlice || rs_cap < 2 || (a.vpasses == 1 && 64 * a.r_v > dyn)) return 0;
   a.rs_cap = rs_cap;
   a.rs_tail = rs_tail;
   a.pitch = pitch;
@@ -669,15 +722,24 @@ hipError_t launch_cfg(AttnDecodeArgs a, int grid, hipStream_t s) {
 }
 
 template <int D>
-hipError_t launch_d(const AttnDecodeArgs &a, int grid, hipStream_t s) {
-  if (a.r_v / 16 <= 8 * kNW) return launch_cfg<D, 8>(a, grid, s);
+hipError_t launch_d(AttnDecodeArgs a, int grid, hipStream_t s) {
+  const int nrb = a.r_v / 16;
+  if (nrb <= 8 * kNW) {
+    a.vpasses = 1;
+    return launch_cfg<D, 8>(a, grid, s);
+  }
+  a.vpasses = attn_decode_value_passes(a.r_v);
+  if (a.vpasses > 1 && !a.uglob) return hipErrorInvalidValue;
   return launch_cfg<D, 16>(a, grid, s);
 }
 
 }  // namespace
 
 int attn_decode_split_granule() { return kSlice; }
-int attn_decode_max_rank_v() { return 16 * 16 * kNW; }
+int attn_decode_value_passes(int r_v) {
+  const int nrb = r_v / 16;
+  return nrb <= 8 * kNW ? 1 : (nrb + 16 * kNW - 1) / (16 * kNW);
+}
 
 hipError_t launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s) {
   TraceGuard trace_guard(K_ATTN_DECODE, s);

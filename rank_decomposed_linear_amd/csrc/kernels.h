@@ -166,6 +166,8 @@ struct AttnDecodeArgs {
   // set by the launcher (LDS plan)
   int rs_cap, rs_tail;    // rank steps resident for the whole item; steps per restaged tail chunk (0: none)
   int pitch, lds_bs, lds_s;
+  int vpasses;         // value-side passes (set by the launcher)
+  float *uglob;        // [Bsz, n_kv, nsplit, 16, r_v] f32 when passes > 1
   float scale_log2;    // sm_scale * log2(e)
   float theta;
   int q_f32, out_f32, out_tiled;
@@ -196,7 +198,9 @@ int latent_attn_max_split(int r_k);
 hipError_t launch_latent_attn_bf16(LatentAttnArgs a, hipStream_t s);
 
 int attn_decode_split_granule();
-int attn_decode_max_rank_v();   // largest r_v the decode kernel accepts
+// value-side passes of the decode kernel for r_v (more than one keeps U in
+// the workspace between context chunks)
+int attn_decode_value_passes(int r_v);
 hipError_t launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s);
 
 struct AttnPrefillArgs {

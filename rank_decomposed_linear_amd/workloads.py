@@ -195,8 +195,33 @@ LLAMA3_70B_C50_PREFILL = Workload("llama3_70b_c50_prefill_8x2048", _llama3_70b(5
                                   batch=8, phase="prefill", prefill=2048, seed=4,
                                   compression_pct=50)
 
+# The other foundation models of section 5.1, at the 40% compression of
+# Tables 3 and 4, in the pages' second throughput setting (batch 64 for
+# LLaMA-65B and 192 for OPT-30B, 64 prefill tokens, sequences up to 512):
+# LLaMA-65B is a 64-head MHA LLaMA block; OPT-30B (56-head MHA) has the
+# non-GLU MLP and no rotary embedding (its learned positions are outside the
+# block).
+def _llama_65b(pct):
+    return make_shape(8192, 64, 64, 128, 22016, "bf16", 10000.0, compression_pct=pct)
+
+
+def _opt_30b(pct):
+    return make_shape(7168, 56, 56, 128, 28672, "bf16", 0.0, compression_pct=pct, mlp="relu")
+
+
+LLAMA65B_C40_DECODE = Workload("llama65b_c40_decode_b64_l512", _llama_65b(40), batch=64,
+                               phase="decode", context=511, seed=5, compression_pct=40)
+LLAMA65B_C40_PREFILL = Workload("llama65b_c40_prefill_64x64", _llama_65b(40), batch=64,
+                                phase="prefill", prefill=64, seed=6, compression_pct=40)
+OPT30B_C40_DECODE = Workload("opt30b_c40_decode_b192_l512", _opt_30b(40), batch=192,
+                             phase="decode", context=511, seed=7, compression_pct=40)
+OPT30B_C40_PREFILL = Workload("opt30b_c40_prefill_192x64", _opt_30b(40), batch=192,
+                              phase="prefill", prefill=64, seed=8, compression_pct=40)
+
 ALL_WORKLOADS: List[Workload] = [TINY, LLAMA3_8B_C40_DECODE, *LLAMA3_8B_SWEEP,
-                                 LLAMA3_70B_C50_DECODE, LLAMA3_70B_C50_PREFILL]
+                                 LLAMA3_70B_C50_DECODE, LLAMA3_70B_C50_PREFILL,
+                                 LLAMA65B_C40_DECODE, LLAMA65B_C40_PREFILL,
+                                 OPT30B_C40_DECODE, OPT30B_C40_PREFILL]
 
 
 def by_name(name: str) -> Workload:

@@ -193,7 +193,7 @@ def test_small_layer_unequal_mlp_ranks(B, case):
 
 
 # ----------------------------------------------------------------------------
-# the five workload configurations
+# the workload configurations
 # ----------------------------------------------------------------------------
 def test_tiny_chain_prefill_then_decode(B):
     """Tiny MHA layer, f32: prefill 32 tokens, then 8 decode steps on fresh
@@ -242,6 +242,37 @@ def test_llama3_8b_sweep_decode(B, w):
 def test_llama3_70b_c50_decode(B):
     print("llama3_70b_c50_decode all sequences", flush=True)
     _decode_config(B, W.LLAMA3_70B_C50_DECODE)
+
+
+# The other foundation models of section 5.1 (MHA; OPT-30B with the non-GLU
+# MLP and no rotary embedding) at their full layer sizes. The GPU runs the
+# whole batch; the oracle, whose explicit K and V rebuild costs about 40
+# GFLOP per sequence here, checks the listed sequences.
+def test_llama65b_c40_decode(B):
+    print("llama65b_c40_decode sequences 0 17 42 63", flush=True)
+    _decode_config(B, W.LLAMA65B_C40_DECODE, np.array([0, 17, 42, 63]))
+
+
+def test_opt30b_c40_decode(B):
+    print("opt30b_c40_decode sequences 0 77 150 191", flush=True)
+    _decode_config(B, W.OPT30B_C40_DECODE, np.array([0, 77, 150, 191]))
+
+
+@pytest.mark.parametrize("w,seqs", [(W.LLAMA65B_C40_PREFILL, [0, 31, 63]),
+                                    (W.OPT30B_C40_PREFILL, [0, 100, 191])],
+                         ids=["llama65b_c40", "opt30b_c40"])
+def test_mha_prefill_configs(B, w, seqs):
+    import torch
+    print(f"{w.name} sequences {seqs}", flush=True)
+    weights, inp = W.draw(w)
+    layer = make_gpu_layer(B, weights)
+    ck, cv = to_dev(W.to_library_key_cache(inp.ck)), to_dev(W.to_library_value_cache(inp.cv))
+    y, x2 = run_layer(B, layer, inp.x, ck, cv, inp.past_lens)
+    sl = np.array(seqs)
+    want = oracle_layer(weights, inp.x, inp.ck, inp.cv, inp.past_lens, sl)
+    check_step("bf16", inp.x, y, x2, ck, cv, want, inp.past_lens, w.prefill, sl)
+    del layer, ck, cv, y, x2
+    torch.cuda.empty_cache()
 
 
 @pytest.fixture(scope="module")

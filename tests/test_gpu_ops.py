@@ -137,6 +137,11 @@ DECODE_CASES = [
     (16, 32, 8, 128, 128, 256, 1088, [1025] * 15 + [300], 500000.0, "bf16"),     # 4 rank steps
     (16, 8, 8, 128, 256, 256, 1088, [1025] * 16, 0.0, "bf16"),                   # MHA
     (8, 12, 12, 64, 1024, 960, 1088, [1025] * 7 + [777], 10000.0, "bf16"),
+    # value ranks past the accumulators (r_v > 1024): U kept in the
+    # workspace between context chunks, several value passes; MHA with the
+    # LLaMA-65B ranks at 40% compression, d = 64
+    (2, 8, 8, 128, 2432, 2432, 576, [512, 200], 10000.0, "bf16"),
+    (3, 4, 4, 64, 1280, 1152, 640, [600, 1, 333], 10000.0, "bf16"),
     # rotary embedding off: attention in the latent space (B_k absorbed into
     # the query, B_v applied to P C_v); MHA with ranks past the rebuilding
     # kernel's limit, several context splits, head groups of 16 with a
