@@ -106,7 +106,7 @@ def test_attention_validation(lib):
     assert call(d=96) == UNSUPPORTED
     assert call(r_k=100) == UNSUPPORTED
     assert call(L_max=96) == UNSUPPORTED                # bf16 cache pages need L_max % 64
-    assert call(r_v=1088) == UNSUPPORTED                # above the largest value rank
+    assert call(r_v=8256) == UNSUPPORTED                # above the largest rank (8192)
     assert call(n_q=34, n_kv=2) == UNSUPPORTED          # group of 17 > 16
     assert call(scale=-1.0) == INVALID
     assert call(q=BAD) == ALIGN
