@@ -239,7 +239,10 @@ dl_status dl_lowrank_attn_decode_paged(const void *q, const dl_kv_cache *cache,
  * 0 .. past_lens[b] + t, which must already hold the latents (append
  * first). Precondition past_lens[b] + T <= L_max. Same shape rules as
  * decode; DL_BF16 also needs each cache pool (all pages of Ck, or of Cv)
- * below 2 GiB.
+ * below 2 GiB. DL_BF16 runs in the section's order, rebuild then attend:
+ * every cached key up to past_lens[b] + T - 1 is rebuilt once (K rotated,
+ * and V) into the workspace, Bsz * n_kv * L_max * d * 4 bytes of it, then
+ * the causal pass reads those tiles.
  * ------------------------------------------------------------------------ */
 size_t dl_attn_prefill_workspace(int64_t Bsz, int64_t T, int64_t n_q,
                                  int64_t n_kv, int64_t d, int64_t r_k,

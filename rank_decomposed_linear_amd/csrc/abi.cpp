@@ -301,6 +301,7 @@ struct AttnWS {
   uint16_t *lat_q = nullptr, *lat_u = nullptr;
   float *lat_part = nullptr;
   int *lat_counters = nullptr;
+  uint16_t *kv_tiles = nullptr;   // prefill: rebuilt K / V^T tile images
 };
 
 AttnWS carve_attn(Carver &c, int64_t Bsz, int64_t n_q, int64_t n_kv, int64_t d, int64_t r_k,
@@ -322,6 +323,8 @@ AttnWS carve_attn(Carver &c, int64_t Bsz, int64_t n_q, int64_t n_kv, int64_t d, 
         w.lat_part = c.take<float>(static_cast<size_t>(Bsz * lp.ngroups) * lp.nsplit * kLatentHeads *
                                    (r_v + 2));
     }
+  } else {
+    w.kv_tiles = c.take<uint16_t>(static_cast<size_t>(Bsz * n_kv * (L_max / kPage)) * 2 * kPage * d);
   }
   return w;
 }
@@ -499,6 +502,7 @@ hipError_t run_attn_bf16(const void *q, int q_f32, int ldq, const CacheRef &c,
   a.bv = static_cast<const uint16_t *>(B_v);
   a.past_lens = lens;
   a.out = static_cast<uint16_t *>(out);
+  a.kv = w.kv_tiles;
   a.Bsz = Bsz;
   a.T = T;
   a.n_q = n_q;

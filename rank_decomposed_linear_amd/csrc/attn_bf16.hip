@@ -56,7 +56,7 @@ __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, int voff, int s
 // the online-softmax pass for their 32 query rows.
 // ---------------------------------------------------------------------------
 template <int DB>
-__global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
+__global__ __launch_bounds__(512) void attn_rebuild_kernel(AttnPrefillArgs a) {
   constexpr int D = DB * 16, HALF = DB / 2, KT = 64;
   constexpr int CH = D / 8;       // 16-byte chunks per K row
   constexpr int RS = 2;           // 32-rank steps per chunk
@@ -70,6 +70,201 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
   __shared__ u32x4 cs[O_BV + U_BV];
   __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * D];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[D * KT];
+  __shared__ double revs[D / 2];
+
+  // wave is made provably uniform, so every fragment index derived from it
+  // stays scalar and each load is a scalar base plus the lane's 16 bytes
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 15, grp = lane >> 4;
+  const int ktile = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int past = a.past_lens[b];
+  // every key up to the last query position is rebuilt (later tiles are
+  // never read)
+  const int qmax_pos = past + a.T - 1;
+  if (ktile * KT > qmax_pos) return;
+  const bool rope_on = a.theta != 0.f;
+  for (int i = tid; i < D / 2; i += 512) revs[i] = rope_on ? rope_rev(i, D, a.theta) : 0.0;
+  const int rsk = a.r_k / 32, rsv = a.r_v / 32;
+  const int nchunk = max((rsk + RS - 1) / RS, (rsv + RS - 1) / RS);
+
+  // ---- staging: unit i of this thread is u = tid + 512 i, fragment
+  // (u - group start) / 64, lane `lane`. Keys past the last query position
+  // stage zeros (their V rows must not leak NaN into P V). ----
+  // Buffer loads: one scalar resource per array (the cache resources span the
+  // page pools, whose byte size the launcher bounds below 2^31), the lane's
+  // 16 bytes as the only vector offset, the (wave-uniform) fragment offset as
+  // soffset. A 64-key tile is one cache page; tiles start at or before the
+  // last query position, so their page is always one the sequence owns.
+  const __amdgpu_buffer_rsrc_t rck = make_rsrc(a.ck, static_cast<int>(a.pool_pages * kPage * a.r_k * 2));
+  const __amdgpu_buffer_rsrc_t rcv = make_rsrc(a.cv, static_cast<int>(a.pool_pages * kPage * a.r_v * 2));
+  const __amdgpu_buffer_rsrc_t rbk = make_rsrc(a.bk, a.n_kv * D * a.r_k * 2);
+  const __amdgpu_buffer_rsrc_t rbv = make_rsrc(a.bv, a.n_kv * D * a.r_v * 2);
+  const int lane16 = lane * 16;
+  u32x4 st[NU];
+  auto gload = [&](int kt, int c) {
+    const int k0 = kt * KT, r0 = c * RS;
+    const int nrk = rsk - r0, nrv = rsv - r0;
+    const int pg = __builtin_amdgcn_readfirstlane(cache_page(a.block_table, a.page_stride, b, kt));
+    const int kpage = pg * (kPage * a.r_k), vpage = pg * (kPage * a.r_v);   // element offsets
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      if (i < I_CV) {
+        const int f = wave + 8 * i, kb = f / RS, rs = f % RS;
+        const bool ok = rs < nrk && k0 + 16 * kb + j <= qmax_pos;
+        const int so = 2 * (kpage + static_cast<int>(frag_off(kb, r0 + rs, a.r_k, 0)));
+        st[i] = ok ? bload(rck, lane16, so) : z;
+      } else if (i < I_BK) {
+        const int f = wave + 8 * (i - I_CV), rb = f >> 1, ps = f & 1;
+        const int so = 2 * (vpage + static_cast<int>(frag_off(2 * r0 + rb, ps, kPage, 0)));
+        st[i] = rb < 2 * nrv ? bload(rcv, lane16, so) : z;
+      } else if (i < I_BV) {
+        const int f = wave + 8 * (i - I_BK), db = f / RS, rs = f % RS;
+        const int so = 2 * static_cast<int>(frag_off(g * DB + db, r0 + rs, a.r_k, 0));
+        st[i] = rs < nrk ? bload(rbk, lane16, so) : z;
+      } else {
+        const int f = wave + 8 * (i - I_BV), db = f / RS, rs = f % RS;
+        const int so = 2 * static_cast<int>(frag_off(g * DB + db, r0 + rs, a.r_v, 0));
+        st[i] = rs < nrv ? bload(rbv, lane16, so) : z;
+      }
+    }
+  };
+  auto swrite = [&](int kt) {
+    const int k0 = kt * KT;
+    uint16_t *cv16 = reinterpret_cast<uint16_t *>(cs + O_CV);
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      if (i >= I_CV && i < I_BK) {
+        // value tile (rank rho, positions p .. p + 7) -> key-major tiles:
+        // key p + e, rank rho at tile (key / 16, rho / 32), lane
+        // key % 16 + 16 ((rho % 32) / 8), slot rho % 8
+        // p % 16 is 0 or 8, so keys p .. p + 7 share a key block and sit
+        // in consecutive lanes of the destination tile: 16 bytes apart
+        const int f = wave + 8 * (i - I_CV), rb = f >> 1, ps = f & 1;
+        const int rho = 16 * rb + j, p = 32 * ps + 8 * grp;
+        const int rs = rho >> 5, hi = (rho & 31) >> 3, slot = rho & 7;
+        uint16_t *dst = cv16 + ((((p >> 4) * RS + rs) * 64 + (p & 15) + 16 * hi) * 8 + slot);
+        const int nvalid = qmax_pos - (k0 + p) + 1;  // keys p + e with e < nvalid are visible
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t w = st[i][e >> 1];
+          const uint16_t v = e < nvalid ? static_cast<uint16_t>((e & 1) ? (w >> 16) : (w & 0xffffu))
+                                        : static_cast<uint16_t>(0);
+          dst[8 * e] = v;
+        }
+      } else {
+        cs[tid + 512 * i] = st[i];
+      }
+    }
+  };
+
+  const int side = wave >> 2, idx = wave & 3;
+  const int pr = idx % NP, kb0 = (idx / NP) * NKB;
+  f32x4 acc[NKB][2];
+#pragma unroll
+  for (int kk = 0; kk < NKB; ++kk) acc[kk][0] = acc[kk][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int kt = ktile, k0 = kt * KT;
+  gload(kt, 0);
+  for (int c = 0; c < nchunk; ++c) {
+    const bool last = c == nchunk - 1;
+    __syncthreads();
+    swrite(kt);
+    // the next chunk's loads fly under this chunk's products
+    if (!last) gload(kt, c + 1);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- rebuild products of this chunk ----
+    const int nrs = min(RS, (side == 0 ? rsk : rsv) - c * RS);
+    if (side == 0) {
+      // K^T[d][key] = sum_r B_k^T[d][r] C_k[key][r]
+#pragma unroll 1
+      for (int rs = 0; rs < nrs; ++rs) {
+        {
+          const u32x4 fa = cs[O_BK + (pr * RS + rs) * 64 + lane];
+          const u32x4 fb = cs[O_BK + ((pr + HALF) * RS + rs) * 64 + lane];
+#pragma unroll
+          for (int kk = 0; kk < NKB; ++kk) {
+            const u32x4 cf = cs[((kb0 + kk) * RS + rs) * 64 + lane];
+            acc[kk][0] = mfma_bf16(fa, cf, acc[kk][0]);
+            acc[kk][1] = mfma_bf16(fb, cf, acc[kk][1]);
+          }
+        }
+      }
+    } else {
+      // V[key][d] = sum_r C_v[key][r] B_v^T[d][r]
+#pragma unroll 1
+      for (int rs = 0; rs < nrs; ++rs) {
+        {
+          const u32x4 f0 = cs[O_BV + ((2 * pr) * RS + rs) * 64 + lane];
+          const u32x4 f1 = cs[O_BV + ((2 * pr + 1) * RS + rs) * 64 + lane];
+#pragma unroll
+          for (int kk = 0; kk < NKB; ++kk) {
+            const u32x4 cf = cs[O_CV + ((kb0 + kk) * RS + rs) * 64 + lane];
+            acc[kk][0] = mfma_bf16(cf, f0, acc[kk][0]);
+            acc[kk][1] = mfma_bf16(cf, f1, acc[kk][1]);
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (!last) continue;
+
+    // ---- K waves: lane (key = j, grp) holds K^T[16 blk + 4 grp + r][16 kb + j]
+    // for blk = pr (acc[.][0]) and its rotary partner pr + HALF (acc[.][1]);
+    // V waves: lane (d = j, grp) holds V[16 kb + 4 grp + r][16 (2 pr + h) + j] ----
+#pragma unroll
+    for (int kk = 0; kk < NKB; ++kk) {
+      const int kb = kb0 + kk;
+      if (side == 0) {
+        const int keyrow = k0 + 16 * kb + j;
+        if (rope_on) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float cc, ss;
+            rope_cs(keyrow, revs[16 * pr + 4 * grp + r], cc, ss);
+            const float u = acc[kk][0][r], v = acc[kk][1][r];
+            acc[kk][0][r] = u * cc - v * ss;
+            acc[kk][1][r] = u * ss + v * cc;
+          }
+        }
+        const int krow = 16 * kb + j;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int dcol = 16 * (pr + hh * HALF) + 4 * grp;
+          const int chunk = (dcol >> 3) ^ (krow & (CH - 1));
+          *reinterpret_cast<u32x2 *>(&Ks[krow * D + chunk * 8 + (dcol & 7)]) =
+              u32x2{pack2(acc[kk][hh][0], acc[kk][hh][1]), pack2(acc[kk][hh][2], acc[kk][hh][3])};
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int dd = 16 * (2 * pr + h) + j;
+          const int unit = (4 * kb + grp) ^ (dd & 15);
+          *reinterpret_cast<u32x2 *>(&Vt[dd * KT + unit * 4]) =
+              u32x2{pack2(acc[kk][h][0], acc[kk][h][1]), pack2(acc[kk][h][2], acc[kk][h][3])};
+        }
+      }
+    }
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    // the tile's image: K rows (rotated, swizzled) then V^T rows (swizzled)
+    uint16_t *img = a.kv + ((static_cast<size_t>(b) * a.n_kv + g) * (a.L_max / KT) + kt) * (2 * KT * D);
+    for (int u = tid; u < KT * D / 8; u += 512) {
+      *reinterpret_cast<u32x4 *>(img + 8 * u) = *reinterpret_cast<const u32x4 *>(Ks + 8 * u);
+      *reinterpret_cast<u32x4 *>(img + KT * D + 8 * u) = *reinterpret_cast<const u32x4 *>(Vt + 8 * u);
+    }
+  }
+}
+
+template <int DB>
+__global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
+  constexpr int D = DB * 16, HALF = DB / 2, KT = 64;
+  constexpr int CH = D / 8;       // 16-byte chunks per K row
+  constexpr int IMG = 2 * KT * D;           // elements of one key tile's image
+  constexpr int NI = IMG / 8 / 512;         // 16-byte units per thread
+  __shared__ __attribute__((aligned(16))) uint16_t KVs[2][IMG];   // double-buffered images
   __shared__ u32x4 Qs[8 * 2 * HALF * 64];  // rotated, scaled query fragments of each wave
   __shared__ double revs[D / 2];
 
@@ -161,175 +356,25 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
 
   const int qmax_pos = past + min(t0 + QT, a.T) - 1;
   const int nkt = qmax_pos / KT + 1;
-  const int rsk = a.r_k / 32, rsv = a.r_v / 32;
-  const int nchunk = max((rsk + RS - 1) / RS, (rsv + RS - 1) / RS);
-  const int nsteps = nkt * nchunk;
-
-  // ---- staging: unit i of this thread is u = tid + 512 i, fragment
-  // (u - group start) / 64, lane `lane`. Keys past the last query position
-  // stage zeros (their V rows must not leak NaN into P V). ----
-  // Buffer loads: one scalar resource per array (the cache resources span the
-  // page pools, whose byte size the launcher bounds below 2^31), the lane's
-  // 16 bytes as the only vector offset, the (wave-uniform) fragment offset as
-  // soffset. A 64-key tile is one cache page; tiles start at or before the
-  // last query position, so their page is always one the sequence owns.
-  const __amdgpu_buffer_rsrc_t rck = make_rsrc(a.ck, static_cast<int>(a.pool_pages * kPage * a.r_k * 2));
-  const __amdgpu_buffer_rsrc_t rcv = make_rsrc(a.cv, static_cast<int>(a.pool_pages * kPage * a.r_v * 2));
-  const __amdgpu_buffer_rsrc_t rbk = make_rsrc(a.bk, a.n_kv * D * a.r_k * 2);
-  const __amdgpu_buffer_rsrc_t rbv = make_rsrc(a.bv, a.n_kv * D * a.r_v * 2);
-  const int lane16 = lane * 16;
-  u32x4 st[NU];
-  auto gload = [&](int kt, int c) {
-    const int k0 = kt * KT, r0 = c * RS;
-    const int nrk = rsk - r0, nrv = rsv - r0;
-    const int pg = __builtin_amdgcn_readfirstlane(cache_page(a.block_table, a.page_stride, b, kt));
-    const int kpage = pg * (kPage * a.r_k), vpage = pg * (kPage * a.r_v);   // element offsets
+  const uint16_t *imgs = a.kv + (static_cast<size_t>(b) * a.n_kv + g) * (a.L_max / KT) * IMG;
+  u32x4 st[NI];
+  auto iload = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < NU; ++i) {
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      if (i < I_CV) {
-        const int f = wave + 8 * i, kb = f / RS, rs = f % RS;
-        const bool ok = rs < nrk && k0 + 16 * kb + j <= qmax_pos;
-        const int so = 2 * (kpage + static_cast<int>(frag_off(kb, r0 + rs, a.r_k, 0)));
-        st[i] = ok ? bload(rck, lane16, so) : z;
-      } else if (i < I_BK) {
-        const int f = wave + 8 * (i - I_CV), rb = f >> 1, ps = f & 1;
-        const int so = 2 * (vpage + static_cast<int>(frag_off(2 * r0 + rb, ps, kPage, 0)));
-        st[i] = rb < 2 * nrv ? bload(rcv, lane16, so) : z;
-      } else if (i < I_BV) {
-        const int f = wave + 8 * (i - I_BK), db = f / RS, rs = f % RS;
-        const int so = 2 * static_cast<int>(frag_off(g * DB + db, r0 + rs, a.r_k, 0));
-        st[i] = rs < nrk ? bload(rbk, lane16, so) : z;
-      } else {
-        const int f = wave + 8 * (i - I_BV), db = f / RS, rs = f % RS;
-        const int so = 2 * static_cast<int>(frag_off(g * DB + db, r0 + rs, a.r_v, 0));
-        st[i] = rs < nrv ? bload(rbv, lane16, so) : z;
-      }
-    }
+    for (int i = 0; i < NI; ++i) st[i] = ld16(imgs + static_cast<size_t>(kt) * IMG + 8 * (tid + 512 * i));
   };
-  auto swrite = [&](int kt) {
-    const int k0 = kt * KT;
-    uint16_t *cv16 = reinterpret_cast<uint16_t *>(cs + O_CV);
+  auto istore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < NU; ++i) {
-      if (i >= I_CV && i < I_BK) {
-        // value tile (rank rho, positions p .. p + 7) -> key-major tiles:
-        // key p + e, rank rho at tile (key / 16, rho / 32), lane
-        // key % 16 + 16 ((rho % 32) / 8), slot rho % 8
-        // p % 16 is 0 or 8, so keys p .. p + 7 share a key block and sit
-        // in consecutive lanes of the destination tile: 16 bytes apart
-        const int f = wave + 8 * (i - I_CV), rb = f >> 1, ps = f & 1;
-        const int rho = 16 * rb + j, p = 32 * ps + 8 * grp;
-        const int rs = rho >> 5, hi = (rho & 31) >> 3, slot = rho & 7;
-        uint16_t *dst = cv16 + ((((p >> 4) * RS + rs) * 64 + (p & 15) + 16 * hi) * 8 + slot);
-        const int nvalid = qmax_pos - (k0 + p) + 1;  // keys p + e with e < nvalid are visible
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t w = st[i][e >> 1];
-          const uint16_t v = e < nvalid ? static_cast<uint16_t>((e & 1) ? (w >> 16) : (w & 0xffffu))
-                                        : static_cast<uint16_t>(0);
-          dst[8 * e] = v;
-        }
-      } else {
-        cs[tid + 512 * i] = st[i];
-      }
-    }
+    for (int i = 0; i < NI; ++i) *reinterpret_cast<u32x4 *>(&KVs[buf][8 * (tid + 512 * i)]) = st[i];
   };
-
-  const int side = wave >> 2, idx = wave & 3;
-  const int pr = idx % NP, kb0 = (idx / NP) * NKB;
-  f32x4 acc[NKB][2];
-#pragma unroll
-  for (int kk = 0; kk < NKB; ++kk) acc[kk][0] = acc[kk][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  gload(0, 0);
-  for (int s = 0; s < nsteps; ++s) {
-    const int kt = s / nchunk, c = s - kt * nchunk;
+  iload(0);
+  __syncthreads();   // (Qs complete)
+  istore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
     const int k0 = kt * KT;
-    const bool last = c == nchunk - 1;
-    __syncthreads();
-    swrite(kt);
-    // the next chunk's loads fly under this chunk's products; after a tile's
-    // last chunk they wait for the softmax pass, which needs the registers
-    if (!last) gload(kt, c + 1);
-    __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- rebuild products of this chunk ----
-    const int nrs = min(RS, (side == 0 ? rsk : rsv) - c * RS);
-    if (side == 0) {
-      // K^T[d][key] = sum_r B_k^T[d][r] C_k[key][r]
-#pragma unroll 1
-      for (int rs = 0; rs < nrs; ++rs) {
-        {
-          const u32x4 fa = cs[O_BK + (pr * RS + rs) * 64 + lane];
-          const u32x4 fb = cs[O_BK + ((pr + HALF) * RS + rs) * 64 + lane];
-#pragma unroll
-          for (int kk = 0; kk < NKB; ++kk) {
-            const u32x4 cf = cs[((kb0 + kk) * RS + rs) * 64 + lane];
-            acc[kk][0] = mfma_bf16(fa, cf, acc[kk][0]);
-            acc[kk][1] = mfma_bf16(fb, cf, acc[kk][1]);
-          }
-        }
-      }
-    } else {
-      // V[key][d] = sum_r C_v[key][r] B_v^T[d][r]
-#pragma unroll 1
-      for (int rs = 0; rs < nrs; ++rs) {
-        {
-          const u32x4 f0 = cs[O_BV + ((2 * pr) * RS + rs) * 64 + lane];
-          const u32x4 f1 = cs[O_BV + ((2 * pr + 1) * RS + rs) * 64 + lane];
-#pragma unroll
-          for (int kk = 0; kk < NKB; ++kk) {
-            const u32x4 cf = cs[O_CV + ((kb0 + kk) * RS + rs) * 64 + lane];
-            acc[kk][0] = mfma_bf16(cf, f0, acc[kk][0]);
-            acc[kk][1] = mfma_bf16(cf, f1, acc[kk][1]);
-          }
-        }
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (!last) continue;
-
-    // ---- K waves: lane (key = j, grp) holds K^T[16 blk + 4 grp + r][16 kb + j]
-    // for blk = pr (acc[.][0]) and its rotary partner pr + HALF (acc[.][1]);
-    // V waves: lane (d = j, grp) holds V[16 kb + 4 grp + r][16 (2 pr + h) + j] ----
-#pragma unroll
-    for (int kk = 0; kk < NKB; ++kk) {
-      const int kb = kb0 + kk;
-      if (side == 0) {
-        const int keyrow = k0 + 16 * kb + j;
-        if (rope_on) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float cc, ss;
-            rope_cs(keyrow, revs[16 * pr + 4 * grp + r], cc, ss);
-            const float u = acc[kk][0][r], v = acc[kk][1][r];
-            acc[kk][0][r] = u * cc - v * ss;
-            acc[kk][1][r] = u * ss + v * cc;
-          }
-        }
-        const int krow = 16 * kb + j;
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int dcol = 16 * (pr + hh * HALF) + 4 * grp;
-          const int chunk = (dcol >> 3) ^ (krow & (CH - 1));
-          *reinterpret_cast<u32x2 *>(&Ks[krow * D + chunk * 8 + (dcol & 7)]) =
-              u32x2{pack2(acc[kk][hh][0], acc[kk][hh][1]), pack2(acc[kk][hh][2], acc[kk][hh][3])};
-        }
-      } else {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int dd = 16 * (2 * pr + h) + j;
-          const int unit = (4 * kb + grp) ^ (dd & 15);
-          *reinterpret_cast<u32x2 *>(&Vt[dd * KT + unit * 4]) =
-              u32x2{pack2(acc[kk][h][0], acc[kk][h][1]), pack2(acc[kk][h][2], acc[kk][h][3])};
-        }
-      }
-    }
-    __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
-
+    if (kt + 1 < nkt) iload(kt + 1);   // in flight under this tile's work
+    const uint16_t *Ks = KVs[kt & 1];
+    const uint16_t *Vt = KVs[kt & 1] + KT * D;
     // ---- attention for this wave's 32 query rows ----
     // Swizzles depend on the row only through j (rows 16 kk + j, d rows
     // 16 x + j), so each (t) or (u, half) needs one base and the key block /
@@ -388,9 +433,8 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kk = 0; kk < NKB; ++kk) acc[kk][0] = acc[kk][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (s + 1 < nsteps) gload(kt + 1, 0);
+    if (kt + 1 < nkt) istore((kt + 1) & 1);
+    __syncthreads();
   }
 
   // ---- normalise and store: lane (q = j, grp) holds O^T[16x + 4grp + r][q] ----
@@ -422,6 +466,14 @@ hipError_t launch_attn_prefill_bf16(const AttnPrefillArgs &a, hipStream_t s) {
   if (a.pool_pages * kPage * std::max(a.r_k, a.r_v) * 2 > lim ||
       static_cast<int64_t>(a.n_kv) * a.d * std::max(a.r_k, a.r_v) * 2 > lim)
     return hipErrorInvalidValue;
+  if (!a.kv) return hipErrorInvalidValue;
+  dim3 rgrid(a.L_max / kPage, a.n_kv, a.Bsz);
+  if (a.d == 128)
+    attn_rebuild_kernel<8><<<rgrid, 512, 0, s>>>(a);
+  else
+    attn_rebuild_kernel<4><<<rgrid, 512, 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   dim3 grid((a.T + QT - 1) / QT, a.n_kv, a.Bsz);
   if (a.d == 128)
     attn_prefill_kernel<8><<<grid, 512, 0, s>>>(a);

@@ -213,6 +213,8 @@ struct AttnPrefillArgs {
   const uint16_t *bk, *bv;  // [n_kv * d, r] in operand tiles
   const int32_t *past_lens;
   uint16_t *out;       // [Bsz, T, n_q*d]
+  uint16_t *kv;        // workspace: rebuilt key tiles, [Bsz, n_kv, L_max / 64, 2 * 64 * d]
+                       // (per 64-key tile: K rows rotated and swizzled, then V^T rows)
   int Bsz, T, n_q, n_kv, d, r_k, r_v, L_max;
   int ldq;             // elements between consecutive tokens of q
   int q_f32;           // q is f32 instead of bf16
