@@ -61,7 +61,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="llama3_70b_c50_decode_b32_l8192")
     p.add_argument("--legs", default="llama3_8b_c40_decode_b16_l1024,"
-                   + ",".join(f"llama3_8b_c{c}_decode_b64_l4096" for c in (20, 30, 40, 50, 60)),
+                   + ",".join(f"llama3_8b_c{c}_decode_b64_l4096" for c in (20, 30, 40, 50, 60))
+                   + ",opt30b_c40_decode_b192_l512",
                    help="comma-separated extra decode workloads (empty: none)")
     p.add_argument("--leg-steps", type=int, default=30)
     p.add_argument("--leg-warmup", type=int, default=5)
@@ -77,6 +78,8 @@ def parse():
                    help="decode steps per graph replay (copies in turn)")
     p.add_argument("--sets", type=int, default=2)
     p.add_argument("--calibrate-copy", action="store_true")
+    p.add_argument("--no-pairs", action="store_true",
+                   help="skip the fused-versus-separate factor-pair timings")
     return p.parse_args()
 
 
@@ -101,9 +104,9 @@ def decode_role_work(shape, M, ctx_total):
 
     ctx_total = sum over sequences of the rows attended."""
     h, f, qd, kvd = shape.hidden, shape.ffn, shape.n_q * shape.head_dim, shape.n_kv * shape.head_dim
-    r = {p: shape.rank(p) for p in ("q", "k", "v", "o", "gate", "up", "down")}
+    r = {p: shape.rank(p) for p in shape.projections()}
     b16, f32 = 2, 4
-    rqkv, rgu = r["q"] + r["k"] + r["v"], r["gate"] + r["up"]
+    rqkv, rgu = r["q"] + r["k"] + r["v"], r.get("gate", 0) + r["up"]
     gemv = {
         "qkv_down": b16 * h * rqkv + M * h * b16 + M * rqkv * b16,
         "q_up": b16 * r["q"] * qd + M * r["q"] * b16 + M * qd * f32,
@@ -119,8 +122,14 @@ def decode_role_work(shape, M, ctx_total):
     gemv["o_mlp_chain"] = sum(gemv[k] for k in ("o_down", "o_up", "gate_up_down", "gate_up_up",
                                                 "down_down", "down_up"))
     attn_bytes = ctx_total * (r["k"] + r["v"]) * b16 + b16 * kvd * (r["k"] + r["v"]) + M * qd * (f32 + b16)
-    attn_flops_own = (ctx_total * (2 * r["k"] * kvd + shape.n_q * (2 * shape.head_dim + 2 * r["v"]))
-                      + M * shape.n_q * 2 * r["v"] * shape.head_dim)
+    if shape.rope_theta == 0:
+        # latent path: B_k into the query, scores and P C_v on the latents,
+        # B_v once per query head
+        attn_flops_own = (ctx_total * shape.n_q * 2 * (r["k"] + r["v"])
+                          + M * shape.n_q * 2 * shape.head_dim * (r["k"] + r["v"]))
+    else:
+        attn_flops_own = (ctx_total * (2 * r["k"] * kvd + shape.n_q * (2 * shape.head_dim + 2 * r["v"]))
+                          + M * shape.n_q * 2 * r["v"] * shape.head_dim)
     attn_flops_pages = ctx_total * (2 * (r["k"] + r["v"]) * kvd + 4 * qd)
     return gemv, attn_bytes, attn_flops_own, attn_flops_pages
 
@@ -159,7 +168,7 @@ def make_sets(torch, binding, weights, inp, nsets):
         lf = W.to_library_factor
         facs = {p: (to_dev(torch, lf(a)), to_dev(torch, lf(b))) for p, (a, b) in weights.factors.items()}
         layer = binding.DecomposedLayer(facs, shp.hidden, shp.n_q, shp.n_kv, shp.head_dim, shp.ffn,
-                                        shp.rope_theta, shp.rms_eps)
+                                        shp.rope_theta, shp.rms_eps, mlp=shp.mlp)
         st = dict(layer=layer, x=to_dev(torch, inp.x), ck=to_dev(torch, W.to_library_key_cache(inp.ck)),
                   cv=to_dev(torch, W.to_library_value_cache(inp.cv)),
                   past=to_dev(torch, inp.past_lens))
@@ -306,9 +315,9 @@ def decode_bench(args, torch, binding, W, name, steps, warmup, trace_steps, nset
                                     "flops_per_step": 0, "pages_flops_per_step": 0})
         k["ms_per_step"] += sum(lst) / n
         k["launches_per_step"] += len(lst) // n
-        if kind in ("gemv_bf16", "gemv_chain"):
+        if kind in ("gemv_bf16", "gemv_chain", "gemm_bf16"):
             k["bytes_per_step"] += gemv_bytes.get(role, 0) * (len(lst) // n)
-        if kind == "attn_decode_bf16":
+        if kind in ("attn_decode_bf16", "attn_latent"):
             k["bytes_per_step"] += attn_bytes
             k["flops_per_step"] += attn_own
             k["pages_flops_per_step"] += attn_pages
@@ -331,6 +340,19 @@ def decode_bench(args, torch, binding, W, name, steps, warmup, trace_steps, nset
         k = kinds[kname]
         nl = max(k["launches_per_step"], 1)
         avg_s = k["ms_per_step"] * 1e-3 / nl
+        if kname == "attn_latent":
+            # HBM-bound: the latents once per head group, plus the factors
+            achieved = k["bytes_per_step"] / nl / avg_s / 1e9
+            tf = k["flops_per_step"] / nl / avg_s / 1e12
+            return {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic(kname, w.name),
+                    "avg_us": round(avg_s * 1e6, 2), "launches_per_step": nl,
+                    "algorithmic_bytes_per_launch": int(k["bytes_per_step"] / nl),
+                    "algorithmic_flops_per_launch": int(k["flops_per_step"] / nl),
+                    "TFLOP_per_s": round(tf, 2),
+                    "flops_counted": "latent association: B_k into the query, scores and P C_v on "
+                                     "the cached latents, B_v once per query head"}
         if kname == "attn_decode_bf16":
             achieved = k["flops_per_step"] / nl / avg_s / 1e12
             pages = k["pages_flops_per_step"] / nl / avg_s / 1e12
@@ -356,8 +378,10 @@ def decode_bench(args, torch, binding, W, name, steps, warmup, trace_steps, nset
     # dominant kernel kind of the step (largest share of the step time)
     dname = max(kinds.items(), key=lambda kv: kv[1]["ms_per_step"])[0]
     roof = roofline(dname)
-    roof_attn = roofline("attn_decode_bf16") if "attn_decode_bf16" in kinds else None
-    gname = "gemv_chain" if "gemv_chain" in kinds else "gemv_bf16"
+    aname = "attn_latent" if "attn_latent" in kinds else "attn_decode_bf16"
+    roof_attn = roofline(aname) if aname in kinds else None
+    gname = ("gemv_chain" if "gemv_chain" in kinds else
+             "gemv_bf16" if "gemv_bf16" in kinds else "gemm_bf16")
     roof_gemv = roofline(gname) if gname in kinds else None
     step_bytes = W.algorithmic_decode_bytes(w.shape, Bsz, ctx_total // Bsz)["total"]
     result = {
@@ -612,8 +636,8 @@ def main():
     for name in [n for n in args.legs.split(",") if n]:
         legs.append(decode_leg(args, torch, binding, W, name, peaks))
         log(f"leg {name}: {legs[-1]['tokens_per_s']:.0f} tokens/s")
-    pairs = fused_pair_bench(torch, binding)
-    for p in pairs:
+    pairs = None if args.no_pairs else fused_pair_bench(torch, binding)
+    for p in pairs or []:
         log(f"factor pair {p['pair']}: fused {p['fused_us']} us, separate {p['separate_us']} us")
     pre = pre_inputs = None
     if not args.no_prefill:

@@ -40,6 +40,10 @@ KINDS = (
     ("gemv_kernel", "gemv_bf16"),
     ("attn_decode_kernel", "attn_decode_bf16"),
     ("attn_prefill_kernel", "attn_prefill_bf16"),
+    ("attn_rebuild_kernel", "attn_prefill_bf16"),
+    ("latent_query_kernel", "attn_latent"),
+    ("latent_attn_kernel", "attn_latent"),
+    ("latent_out_kernel", "attn_latent"),
     ("gemm_bf16_kernel", "gemm_bf16"),
     ("gemm_f32_kernel", "gemm_f32"),
     ("attn_f32_kernel", "attn_f32"),
@@ -52,8 +56,8 @@ KINDS = (
     ("store_cache_rows_kernel", "store_cache_rows"),
 )
 
-KERNEL_SOURCES = ("gemv_bf16.hip", "attn_decode_bf16.hip", "attn_bf16.hip", "gemm_bf16.hip",
-                  "elementwise.hip", "common.h", "kernels.h")
+KERNEL_SOURCES = ("gemv_bf16.hip", "attn_decode_bf16.hip", "attn_bf16.hip", "attn_latent_bf16.hip",
+                  "gemm_bf16.hip", "elementwise.hip", "common.h", "kernels.h")
 
 
 def source_hash() -> str:
