@@ -1186,7 +1186,21 @@ static void carve_layer(Carver &c, const LayerDims &D, const dl_layer *L, LayerW
   w.td16 = c.take<uint16_t>(M * D.rd);
 }
 
+// Decode batches of 65 .. 512 sequences run as chunks of 64 sequences on
+// the GEMV path (each chunk reads the weights once): the GEMM's 256-row
+// tiles leave most of the GPU idle at such M. Sequences are independent in
+// decode, so a chunk is the same layer on a sub-batch.
+constexpr int64_t kDecodeChunk = 64, kDecodeChunkedMax = 512;
+bool chunked_decode(const dl_layer *L, int64_t Bsz, int64_t T) {
+  return L && L->dt == DL_BF16 && T == 1 && Bsz > kDecodeChunk && Bsz <= kDecodeChunkedMax;
+}
+
 size_t dl_layer_workspace(const dl_layer *L, int64_t Bsz, int64_t T, int64_t L_max) {
+  if (chunked_decode(L, Bsz, T)) {
+    LayerDims D{};
+    if (layer_dims(L, Bsz, T, L_max, &D) != DL_OK) return 0;
+    return dl_layer_workspace(L, kDecodeChunk, T, L_max);
+  }
   LayerDims D{};
   if (layer_dims(L, Bsz, T, L_max, &D) != DL_OK) return 0;
   Carver c(nullptr);
@@ -1205,6 +1219,27 @@ static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_
   dl_status st = layer_dims(L, Bsz, T, L_max, &D);
   if (st != DL_OK) return st;
   DL_CHECK(x && y && cache.k && cache.v && past_lens, DL_ERR_INVALID_ARG, "null pointer");
+  if (chunked_decode(L, Bsz, T)) {
+    // chunks of kDecodeChunk sequences in order on the stream; each sees its
+    // rows of x, y, x2_out and past_lens, and its pages of the cache
+    const int64_t h = L->hidden;
+    for (int64_t b0 = 0; b0 < Bsz; b0 += kDecodeChunk) {
+      const int64_t nb = std::min(kDecodeChunk, Bsz - b0);
+      CacheRef c = cache;
+      if (c.table) {
+        c.table += b0 * c.stride;
+      } else {
+        c.k = static_cast<uint16_t *>(c.k) + b0 * c.stride * kPage * L->k.k;
+        c.v = static_cast<uint16_t *>(c.v) + b0 * c.stride * kPage * L->v.k;
+        c.pool_pages = nb * c.stride;
+      }
+      st = layer_impl(L, static_cast<const uint16_t *>(x) + b0 * h, static_cast<uint16_t *>(y) + b0 * h,
+                      x2_out ? static_cast<float *>(x2_out) + b0 * h : nullptr, c, past_lens + b0, nb,
+                      T, ws, ws_bytes, stream);
+      if (st != DL_OK) return st;
+    }
+    return DL_OK;
+  }
   void *Ck = cache.k, *Cv = cache.v;
   const dl_factor *fs[7];
   const int nf = layer_factors(L, fs);
