@@ -1,7 +1,7 @@
 // bf16 MFMA GEMM for prefill-sized M: one factor of a decomposed projection
 // (W ~ A B, DeInfer section 2.1, Eq. (1)), C = X W with f32 accumulation.
 //
-// Tile 256 x 256 x 64, 8 waves (two per SIMD, so one wave's LDS traffic and
+// Tile 256 x 256 x 32, 8 waves (two per SIMD, so one wave's LDS traffic and
 // barrier wait hide under the other's MFMAs). Each wave owns a 128 x 64
 // block of C: 8 x 4 accumulator blocks of v_mfma_f32_16x16x32_bf16.
 //
@@ -9,13 +9,15 @@
 // 1 KB, lane l at byte 16 l), so every operand read is one conflict-free
 // ds_read_b128 of a contiguous 1 KB and every staging write is one too. The
 // factors already live in that order in HBM (Wt [N, K] in 16 x 32 tiles): a
-// weight tile's k step is 32 contiguous 1 KB fragments. Activation rows are
+// weight tile's k step is 16 contiguous 1 KB fragments. Activation rows are
 // row-major: lane l of a staging load fetches row (l % 16), k columns
 // 8 (l / 16) .. +7 of its fragment. Staging is direct to LDS
 // (global_load_lds_dwordx4: lane l of a wave lands at byte 16 l of the
 // wave's 1 KB destination), so no registers or LDS store instructions carry
-// it. Two separately declared 64 KB stage buffers (the compiler then sees
-// that the loads into one do not alias the operand reads from the other).
+// it. Four separately declared 32 KB stage buffers (the compiler then sees
+// that the loads into one do not alias the operand reads from another):
+// tile kt + 3 is in flight while tile kt is multiplied, which hides the
+// load latency that a two-buffer pipeline leaves exposed at every k step.
 //
 // Work order: the hardware deals workgroups to the eight XCDs round-robin;
 // the linear index is remapped so each XCD runs a contiguous range of tiles,
@@ -28,7 +30,7 @@
 namespace dl {
 
 namespace {
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BM = 256, BN = 256, BK = 32;
 constexpr int kThreads = 512;
 constexpr int kFrags = (BM / 16) * (BK / 32);  // 1 KB fragments per operand per stage
 constexpr int kStage = 2 * kFrags * 64;        // u32x4 per stage (A then B)
@@ -50,9 +52,12 @@ __device__ __forceinline__ void tile_of(int bid, int total, int tiles_m, int til
   tm = g * kGroupM + (w - tn * gm);
 }
 
+constexpr int kEpU4 = (kEpRows * kEpPitch + 3) / 4;  // epilogue rows in u32x4 units
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
-  __shared__ u32x4 stage0[kStage];
+  __shared__ u32x4 stage0[kStage > kEpU4 ? kStage : kEpU4];
   __shared__ u32x4 stage1[kStage];
+  __shared__ u32x4 stage2[kStage];
+  __shared__ u32x4 stage3[kStage];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
@@ -68,36 +73,34 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   const int K = a.K;
 
   // Staging: thread t moves fragment (wave + 8 i), lane `lane`, of both
-  // operands, i = 0..3. A fragment f = 2 rb + ks holds rows 16 rb .. +15,
-  // k 32 ks .. +31 of the tile; out-of-range rows and weight rows are
-  // clamped (their results are never stored), so every load is issued.
-  const uint16_t *xp[4];
-  const uint16_t *wp[4];
+  // operands, i = 0..1: row block wave + 8 i of the 32-wide k tile.
+  // Out-of-range rows and weight rows are clamped (their results are never
+  // stored), so every load is issued.
+  const uint16_t *xp[2];
+  const uint16_t *wp[2];
   const int nblk_last = (sg.N >> 4) - 1;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int f = wave + 8 * i, rb = f >> 1, ks = f & 1;
+  for (int i = 0; i < 2; ++i) {
+    const int rb = wave + 8 * i;
     const int row = min(m0 + 16 * rb + (lane & 15), a.M - 1);
-    xp[i] = sg.X + static_cast<size_t>(row) * sg.ldx + 32 * ks + 8 * (lane >> 4);
+    xp[i] = sg.X + static_cast<size_t>(row) * sg.ldx + 8 * (lane >> 4);
     const int nb = min((n0 >> 4) + rb, nblk_last);
-    wp[i] = sg.W + frag_off(nb, ks, K, lane);
+    wp[i] = sg.W + frag_off(nb, 0, K, lane);
   }
-
   // direct-to-LDS staging of k tile kt into `dst`: unit i of this wave fills
   // the 1 KB fragment wave + 8 i of each operand
   typedef const void __attribute__((address_space(1))) *gptr;
   typedef void __attribute__((address_space(3))) *lptr;
   auto dma = [&](u32x4 *dst, int kt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
       __builtin_amdgcn_global_load_lds((gptr)(xp[i] + kt * BK),
                                        (lptr)(dst + (wave + 8 * i) * 64), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((gptr)(wp[i] + static_cast<size_t>(kt) * 2 * 512),
+      __builtin_amdgcn_global_load_lds((gptr)(wp[i] + static_cast<size_t>(kt) * 512),
                                        (lptr)(dst + kFrags * 64 + (wave + 8 * i) * 64), 16, 0,
                                        0);
     }
   };
-  auto dma_wait = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
   f32x4 acc[8][4];
 #pragma unroll
@@ -106,43 +109,62 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
     for (int y = 0; y < 4; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // One basic block per k tile, so the scheduling groups below can order
-  // it: the next tile's loads into the other buffer and this tile's B
-  // fragments first, then each A fragment read three fragments ahead of its
-  // four MFMAs; the tile ends with this wave's loads landed and a barrier.
-  // The last iteration reloads its own tile into the idle buffer (never
-  // read). The loop is unrolled by two so each half's buffers are static.
+  // it: the loads of tile kt + 3 and this tile's B fragments first, then each
+  // A fragment read three fragments ahead of its four MFMAs. The tile ends
+  // when this wave's loads of tile kt + 1 have landed (loads complete in
+  // issue order, so the 8 loads of tiles kt + 2 and kt + 3 may remain) and a
+  // barrier. Near the end, the loads of tiles past the last reload the last
+  // tile into a buffer that is not read again. The loop is unrolled by four
+  // so every buffer is static.
   const int ktiles = K / BK;
+  // s_waitcnt vmcnt(8) lgkmcnt(0) (gfx9 encoding: vmcnt bits 3:0 and 15:14,
+  // expcnt 6:4, lgkmcnt 11:8), then a barrier without a memory fence. The
+  // builtin wait is visible to the compiler's own wait insertion.
+  auto bar_after_wait = [] {
+    __builtin_amdgcn_s_waitcnt(0x0078);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
   auto ktile = [&](const u32x4 *base, u32x4 *next, int kt) {
-    dma(next, min(kt + 1, ktiles - 1));
-    u32x4 bq[2][4], ar[16];
+    dma(next, min(kt + 3, ktiles - 1));
+    u32x4 bq[4], ar[8];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int nb = 0; nb < 4; ++nb) bq[nb] = base[kFrags * 64 + (wn * 4 + nb) * 64 + lane];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) bq[ks][nb] = base[kFrags * 64 + ((wn * 4 + nb) * 2 + ks) * 64 + lane];
+    for (int i = 0; i < 8; ++i) ar[i] = base[(wm * 8 + i) * 64 + lane];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ar[i] = base[((wm * 8 + (i & 7)) * 2 + (i >> 3)) * 64 + lane];
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) acc[i & 7][nb] = mfma_bf16(ar[i], bq[i >> 3][nb], acc[i & 7][nb]);
+      for (int nb = 0; nb < 4; ++nb) acc[i][nb] = mfma_bf16(ar[i], bq[nb], acc[i][nb]);
     // groups: 0x008 MFMA, 0x020 VMEM read, 0x100 DS read
-    __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 11, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 7, 0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i + 3 < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int i = 0; i < 8; ++i) {
+      if (i + 3 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
-    dma_wait();
-    __syncthreads();
+    // this wave's tile kt + 1 has landed and its operand reads of tile kt
+    // have returned; no memory fence (which would wait for every load)
+    bar_after_wait();
   };
   dma(stage0, 0);
-  dma_wait();
-  __syncthreads();
-  for (int kt = 0; kt < ktiles; kt += 2) {
-    ktile(stage0, stage1, kt);
-    if (kt + 1 < ktiles) ktile(stage1, stage0, kt + 1);
+  dma(stage1, min(1, ktiles - 1));
+  dma(stage2, min(2, ktiles - 1));
+  bar_after_wait();
+  int kt = 0;
+  for (; kt + 3 < ktiles; kt += 4) {
+    ktile(stage0, stage3, kt);
+    ktile(stage1, stage0, kt + 1);
+    ktile(stage2, stage1, kt + 2);
+    ktile(stage3, stage2, kt + 3);
   }
+  if (kt < ktiles) ktile(stage0, stage3, kt);
+  if (kt + 1 < ktiles) ktile(stage1, stage0, kt + 1);
+  if (kt + 2 < ktiles) ktile(stage2, stage1, kt + 2);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 
   // Epilogue, in eight passes of 32 rows: the waves owning the pass's rows
   // park their f32 accumulators in LDS (row pitch kEpPitch, so the 16-lane
