@@ -720,18 +720,25 @@ size_t gemv_plan(GvArgs &a) {
   const int ks_max = std::max(1, std::min(64, ksteps / (min_steps * a.waves)));
   auto splits = [&](int items) { return std::max(1, std::min(ks_max, cus / std::max(1, items))); };
   // Two or four row tiles per item share each activation fragment (halving
-  // or quartering the activation reads): the widest item whose count still
-  // fills 7/8 of the compute units in one unsplit round. (Pairing tiles of a
-  // split launch by raising its split measured slower: shorter streams per
-  // wave, larger merges.) Four tiles only up to 32 token rows (LDS).
+  // or quartering the activation reads, which otherwise cost twice the
+  // weight bytes per step at 32 rows). Four tiles only up to 32 token rows
+  // (LDS).
   int R = 1;
   if (a.waves == 4) {
     const int forced = env_int("DL_GEMV_R", 0);
-    const int fill = (7 * cus + 7) / 8;
-    R = forced == 1 || forced == 2 || forced == 4 ? forced
-        : tiles >= 4 * fill && a.M <= 32        ? 4
-        : tiles >= 2 * fill                     ? 2
-                                                : 1;
+    // the widest item (four tiles up to 32 token rows, else two) whose K
+    // stream, after the one-round split, still has at least 64 steps:
+    // long-K factors gain (54 -> 37 us for the 70B A_down at 32 rows), while
+    // short-K ones lose to the shorter streams and larger merges
+    R = forced == 1 || forced == 2 || forced == 4 ? forced : 1;
+    for (int r = 4; r >= 2 && forced == 0; r /= 2) {
+      if ((r == 4 && a.M > 32) || tiles < r) continue;
+      const int ks_r = splits((tiles + r - 1) / r);
+      if ((ksteps + ks_r - 1) / ks_r >= 64) {
+        R = r;
+        break;
+      }
+    }
     if (R == 4 && a.M > 32) R = 2;
   }
   a.rtiles = R;
