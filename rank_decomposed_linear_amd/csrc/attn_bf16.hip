@@ -105,7 +105,7 @@ __global__ __launch_bounds__(512) void attn_rebuild_kernel(AttnPrefillArgs a) {
   auto gload = [&](int kt, int c) {
     const int k0 = kt * KT, r0 = c * RS;
     const int nrk = rsk - r0, nrv = rsv - r0;
-    const int pg = __builtin_amdgcn_readfirstlane(cache_page(a.block_table, a.page_stride, b, kt));
+    const int pg = cache_page_uniform(a.block_table, a.page_stride, b, kt);
     const int kpage = pg * (kPage * a.r_k), vpage = pg * (kPage * a.r_v);   // element offsets
 #pragma unroll
     for (int i = 0; i < NU; ++i) {

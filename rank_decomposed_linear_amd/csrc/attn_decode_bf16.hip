@@ -157,7 +157,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
   // = [r_v, kPage] tiles (a position's page is looked up once per 16- or
   // 32-position block; the page index is uniform across the wave)
   auto page_of = [&](int p64) {
-    return __builtin_amdgcn_readfirstlane(cache_page(a.block_table, a.page_stride, b, p64));
+    return cache_page_uniform(a.block_table, a.page_stride, b, p64);
   };
 
   // up-factor fragments of rank steps [rs0, rs0 + cnt) -> dst[rs - rs0][x][lane][8]
@@ -497,14 +497,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
         u32x4 pop = pbuf[u * 64 + lane];
         if (u0 + d >= nU) pop = u32x4{0u, 0u, 0u, 0u};
         // value rows at positions >= ctx (unwritten cache) are zeroed: the
-        // probabilities there are zero, but 0 * NaN would not be
-        const int nv = ctx - (c0 + 32 * u + 8 * grp);
-        const bool ragged = c0 + 32 * u + 32 > ctx;   // uniform across the wave
+        // probabilities there are zero, but 0 * NaN would not be. Only the
+        // context's last group can be ragged: a branch (uniform across the
+        // wave), not a select, so the other groups carry no masking work.
+        if (c0 + 32 * u + 32 > ctx) {
+          const int nv = ctx - (c0 + 32 * u + 8 * grp);
 #pragma unroll
-        for (int i = 0; i < RBW; ++i) {
-          const u32x4 aop = ragged ? keep_first(vr[d][i], nv) : vr[d][i];
-          uacc[i] = mfma_bf16(aop, pop, uacc[i]);
+          for (int i = 0; i < RBW; ++i) vr[d][i] = keep_first(vr[d][i], nv);
         }
+#pragma unroll
+        for (int i = 0; i < RBW; ++i) uacc[i] = mfma_bf16(vr[d][i], pop, uacc[i]);
         __builtin_amdgcn_sched_barrier(0);
         vload(vr[d], min(u0 + d + kVDepth, nU - 1));
         __builtin_amdgcn_sched_barrier(0);

@@ -168,7 +168,7 @@ __global__ __launch_bounds__(kThreads, 1) void latent_attn_kernel(LatentAttnArgs
   const int nrs = a.r_k / 32, nrb = a.r_v / 16;
   const int heads_here = min(kHG, a.n_q - kHG * hg);
   auto page_of = [&](int p64) {
-    return __builtin_amdgcn_readfirstlane(cache_page(a.block_table, a.page_stride, b, p64));
+    return cache_page_uniform(a.block_table, a.page_stride, b, p64);
   };
 
   // Q~ of the group into LDS (rows of heads past n_q are zero)

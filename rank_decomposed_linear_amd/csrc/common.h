@@ -73,6 +73,17 @@ constexpr int kPage = 64;
 __device__ __forceinline__ int cache_page(const int32_t *table, int stride, int b, int p) {
   return table ? table[b * stride + p] : b * stride + p;
 }
+// The same lookup for a (b, p) that is uniform across the wave, through the
+// scalar cache: a vector load here would make the compiler wait for every
+// vector load in flight (vmcnt counts in issue order) before the page is
+// known, draining any prefetch ring around it; a scalar load waits on
+// lgkmcnt instead. The table is read-only while a kernel runs.
+__device__ __forceinline__ int cache_page_uniform(const int32_t *table, int stride, int b, int p) {
+  const int idx = __builtin_amdgcn_readfirstlane(b * stride + p);
+  if (!table) return idx;
+  typedef const int32_t __attribute__((address_space(4))) *cptr;
+  return __builtin_amdgcn_readfirstlane(((cptr)table)[idx]);
+}
 // element offsets of key latent (pos, r) and value latent (pos, n) in a pool
 // whose position pos lies on pool page `page`
 __device__ __forceinline__ size_t key_off(int page, int pos, int r, int r_k) {
