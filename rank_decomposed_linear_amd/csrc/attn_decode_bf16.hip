@@ -84,6 +84,11 @@ __device__ __forceinline__ void turn_cs(float t, float &c, float &s) {
   __sincosf(t * 6.283185307179586f, &s, &c);
 }
 
+// s_waitcnt immediate that waits until at most n vector loads are in flight
+// and leaves the other counters free (gfx9 encoding: vmcnt bits 3:0 and
+// 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 // zero the bf16 elements e >= nv of an 8-element operand
 __device__ __forceinline__ u32x4 keep_first(u32x4 v, int nv) {
 #pragma unroll
@@ -342,8 +347,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
           // refills. With one wave per SIMD nothing else fills the matrix
           // pipe, so the LDS reads and loads are spread between the
           // products instead of issued in runs.
-          auto rank_step = [&](auto dc, int s) {
+          auto rank_step = [&](auto dc, int s, auto refill) {
             constexpr int d = decltype(dc)::value;
+            constexpr bool kRefill = decltype(refill)::value;
             const uint16_t *fr = fb + (static_cast<size_t>(min(s + 1, cnt - 1) * NB) * 64 + lane) * 8;
 #pragma unroll
             for (int x = 0; x < NB; ++x) bop[(d + 1) & 1][x] = *reinterpret_cast<const u32x4 *>(fr + x * 64 * 8);
@@ -351,9 +357,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
             for (int pb = 0; pb < NPA; ++pb)
 #pragma unroll
               for (int x = 0; x < NB; ++x) acc[x][pb] = mfma_bf16(bop[d & 1][x], cf[d][pb], acc[x][pb]);
-            const int sn = rs0 + min(s + kCDepth, cnt - 1);
+            if constexpr (kRefill) {
+              const int sn = rs0 + min(s + kCDepth, cnt - 1);
 #pragma unroll
-            for (int pb = 0; pb < NPA; ++pb) cf[d][pb] = ld16(kblk[pb] + lane * 8 + 512 * sn);
+              for (int pb = 0; pb < NPA; ++pb) cf[d][pb] = ld16(kblk[pb] + lane * 8 + 512 * sn);
+            }
 #pragma unroll
             for (int pb = 0; pb < NPA; ++pb) {
 #pragma unroll
@@ -361,16 +369,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
                 __builtin_amdgcn_sched_group_barrier(0x008, NPA, 0);   // MFMA
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // LDS read
               }
-              __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);   // VALU (load address)
-              __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+              if constexpr (kRefill) {
+                __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);   // VALU (load address)
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+              }
             }
           };
+          // Whole rounds of kCDepth steps refill the ring; the remaining
+          // steps (their tiles already in flight) issue no loads, so taking
+          // or skipping one leaves the same loads outstanding and the
+          // compiler's per-step waits stay exact instead of draining the ring.
           int s0 = 0;
           for (; s0 + kCDepth <= cnt; s0 += kCDepth) {
-            static_for<kCDepth>([&](auto dc) { rank_step(dc, s0 + decltype(dc)::value); });
+            static_for<kCDepth>([&](auto dc) { rank_step(dc, s0 + decltype(dc)::value, IntC<1>{}); });
           }
           static_for<kCDepth>([&](auto dc) {
-            if (s0 + decltype(dc)::value < cnt) rank_step(dc, s0 + decltype(dc)::value);
+            constexpr int d = decltype(dc)::value;
+            if (s0 + d < cnt) {
+              // this step's tiles are the (kCDepth - d)-th newest loads
+              // group: the ones issued after them may stay in flight
+              __builtin_amdgcn_s_waitcnt(vmcnt_only((kCDepth - 1 - d) * NPA));
+              rank_step(dc, s0 + d, IntC<0>{});
+            }
           });
         }
         // lane (pos j, grp) holds K^T[16x + 4grp + r][P0 + 16pb + j]; block
