@@ -140,11 +140,15 @@ __global__ __launch_bounds__(kThreads) void latent_query_kernel(LatentAttnArgs a
 // attention over the latents
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads, 1) void latent_attn_kernel(LatentAttnArgs a) {
-  // dynamic LDS: Q~ [16, r_k] operand tiles, scores [16][pitch] f32,
+  // dynamic LDS: Q~ [16, r_k] operand tiles, scores [16][pitch + 1] f32,
   // probabilities [pitch / 32][64] operand words
   extern __shared__ __attribute__((aligned(16))) char dlds[];
   uint16_t *qs = reinterpret_cast<uint16_t *>(dlds);
   float *sS = reinterpret_cast<float *>(dlds + a.lds_q);
+  // score row stride one float longer than the split, so the 16 heads' rows
+  // (read and written at one column by lanes j = head) start in different
+  // LDS banks
+  const int spitch = a.pitch + 1;
   u32x4 *pbuf = reinterpret_cast<u32x4 *>(dlds + a.lds_q + a.lds_s);
   __shared__ float smax[kNW][16], psw[kNW][16];
   __shared__ float cmb_m[16], cmb_l[16];
@@ -230,7 +234,7 @@ __global__ __launch_bounds__(kThreads, 1) void latent_attn_kernel(LatentAttnArgs
         const int off = 16 * (g0 + pb) + 4 * grp + r;
         const float v = p_begin + off < p_end ? acc[pb][r] : -INFINITY;
         mx = fmaxf(mx, v);
-        sS[j * a.pitch + off] = v;
+        sS[j * spitch + off] = v;
       }
     }
   }
@@ -251,7 +255,7 @@ __global__ __launch_bounds__(kThreads, 1) void latent_attn_kernel(LatentAttnArgs
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       v[e] = 0.f;
-      if (off + e < npos && m_all != -INFINITY) v[e] = exp2f(sS[j * a.pitch + off + e] - m_all);
+      if (off + e < npos && m_all != -INFINITY) v[e] = exp2f(sS[j * spitch + off + e] - m_all);
       ps += v[e];
     }
     pbuf[u * 64 + lane] = u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
@@ -298,15 +302,17 @@ __global__ __launch_bounds__(kThreads, 1) void latent_attn_kernel(LatentAttnArgs
         u32x4 pop = pbuf[u * 64 + lane];
         if (u0 + d >= nU) pop = u32x4{0u, 0u, 0u, 0u};
         // value rows at positions >= ctx (unwritten cache) are zeroed: the
-        // probabilities there are zero, but 0 * NaN would not be
+        // probabilities there are zero, but 0 * NaN would not be. Only the
+        // context's last group can be ragged: a branch (uniform across the
+        // wave), not a select, so the other groups carry no masking work.
         const int p = p_begin + 32 * u;
-        const bool ragged = p + 32 > ctx;   // uniform
-        const int nv = ctx - (p + 8 * grp);
+        if (p + 32 > ctx) {
+          const int nv = ctx - (p + 8 * grp);
 #pragma unroll
-        for (int i = 0; i < kRB; ++i) {
-          const u32x4 aop = ragged ? keep_first(vr[d][i], nv) : vr[d][i];
-          uacc[i] = mfma_bf16(aop, pop, uacc[i]);
+          for (int i = 0; i < kRB; ++i) vr[d][i] = keep_first(vr[d][i], nv);
         }
+#pragma unroll
+        for (int i = 0; i < kRB; ++i) uacc[i] = mfma_bf16(vr[d][i], pop, uacc[i]);
         __builtin_amdgcn_sched_barrier(0);
         vload(vr[d], min(u0 + d + kVDepth, nU - 1));
         __builtin_amdgcn_sched_barrier(0);
@@ -444,7 +450,7 @@ int attn_static_lds() {
 
 int latent_attn_max_split(int r_k) {
   const int dyn = lds_per_block() - attn_static_lds() - kHG * r_k * 2;
-  const int pitch = (dyn / kPerPos) & ~63;
+  const int pitch = ((dyn - kHG * 4 - 16) / kPerPos) & ~63;
   return pitch < 64 ? 0 : std::min(pitch, 4096);
 }
 
@@ -473,7 +479,7 @@ hipError_t launch_latent_attn_bf16(LatentAttnArgs a, hipStream_t s) {
     }
     a.pitch = (a.split_len + 63) / 64 * 64;
     a.lds_q = kHG * a.r_k * 2;
-    a.lds_s = kHG * a.pitch * 4;
+    a.lds_s = (kHG * (a.pitch + 1) * 4 + 15) / 16 * 16;
     const int need = a.lds_q + a.lds_s + a.pitch * 32;
     if (need > dyn) return hipErrorInvalidValue;
     const int total = a.Bsz * a.ngroups * a.nsplit;
