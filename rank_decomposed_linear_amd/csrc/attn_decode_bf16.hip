@@ -275,8 +275,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
   const int npass = a.vpasses;
   float *ug = npass > 1 ? a.uglob + (static_cast<size_t>(w) * 16 + j) * a.r_v : nullptr;
 
-  for (int c0 = p_begin; c0 < p_end; c0 += pitch) {
-    const int c1 = min(c0 + pitch, p_end);
+  // Work items w = 1, 2, 3 (mod 4) take a first chunk shorter by a quarter,
+  // a half and three quarters, so the value phases of a quarter of the
+  // workgroups fall within the key phases of the rest: all workgroups start
+  // together, and in step every value phase would pull its tiles from L2
+  // at the same time.
+  const int first_len = max(kSlice, (pitch - (w & 3) * (pitch / 4)) & ~(kSlice - 1));
+  for (int c0 = p_begin, c1; c0 < p_end; c0 = c1) {
+    c1 = min(c0 + (c0 == p_begin ? first_len : pitch), p_end);
     // ------------------------------ phase 1 ------------------------------
     // the chunk's 16-position blocks are shared out evenly, a contiguous
     // range per wave, taken kNP blocks at a time (the last group may be
