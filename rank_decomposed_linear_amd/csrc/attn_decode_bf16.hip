@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
   constexpr int NB = T::NB, NE = T::NE, HALF = T::HALF;
   constexpr int OBW = NB / kNW;          // output d blocks per wave
   // dynamic LDS: factor fragments [rs_cap][NB][64][8] bf16, scores
-  // [G][pitch + 1] f32, probabilities [pitch / 32][64] operand words
+  // [G][pitch + 4] f32, probabilities [pitch / 32][64] operand words
   extern __shared__ __attribute__((aligned(16))) char dlds[];
   uint16_t *bs = reinterpret_cast<uint16_t *>(dlds);
   float *sS = reinterpret_cast<float *>(dlds + a.lds_bs);
@@ -158,10 +158,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
   const int n_tail = rs_tail > 0 ? (nrs - rs_cap + rs_tail - 1) / rs_tail : 0;
   const int nrb = a.r_v / 16;
   const int pitch = a.pitch;   // positions per chunk, a multiple of the slice
-  // score row stride: one float more than the chunk, so the rows of the
+  // score row stride: four floats more than the chunk, so the rows of the
   // heads (read and written at the same column by lanes j = head) start in
-  // different LDS banks; a multiple of 64 floats would put them all in one
-  const int spitch = pitch + 1;
+  // different LDS banks (a multiple of 64 floats would put them all in one)
+  // and stay 16-byte aligned
+  const int spitch = pitch + 4;
   // cache pages of this sequence: key page = [kPage, r_k] tiles, value page
   // = [r_v, kPage] tiles (a position's page is looked up once per 16- or
   // 32-position block; the page index is uniform across the wave)
@@ -480,12 +481,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
     m_run = m_new;
     float ps = 0.f;
     for (int u = wave; u < nU; u += kNW) {
-      float v[8];
+      // eight scores of a valid row, read unconditionally (two 16-byte
+      // reads); masked entries become exp2(-inf) = 0 by a select, so the
+      // lanes do not branch around each read and wait on it separately
       const int off = 32 * u + 8 * grp;
+      const float *srow = sS + min(j, G - 1) * spitch + off;
+      const f32x4 sa = *reinterpret_cast<const f32x4 *>(srow);
+      const f32x4 sb = *reinterpret_cast<const f32x4 *>(srow + 4);
+      const float sv[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+      float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        v[e] = 0.f;
-        if (j < G && c0 + off + e < c1) v[e] = exp2f(sS[j * spitch + off + e] - m_new);
+        v[e] = exp2f(j < G && c0 + off + e < c1 ? sv[e] - m_new : -INFINITY);
         ps += v[e];
       }
       pbuf[u * 64 + lane] = u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
@@ -712,7 +719,7 @@ int plan_lds(AttnDecodeArgs &a, int dyn, int nb) {
   const int step_bytes = nb * 1024;
   const int nrs = a.r_k / 32;
   const int per_pos = 4 * G + 32;
-  const int pad = 4 * G + 16;   // one float more per score row, rounding
+  const int pad = 16 * G + 16;   // four floats more per score row, rounding
   const int want = min(kMaxPitch, (a.split_len + kSlice - 1) / kSlice * kSlice);
   int rs_cap = nrs, rs_tail = 0;
   int pitch = ((dyn - pad - nrs * step_bytes) / per_pos) & ~(kSlice - 1);
@@ -732,7 +739,7 @@ int plan_lds(AttnDecodeArgs &a, int dyn, int nb) {
   a.rs_tail = rs_tail;
   a.pitch = pitch;
   a.lds_bs = (rs_cap + rs_tail) * step_bytes;
-  a.lds_s = (G * (pitch + 1) * 4 + 15) / 16 * 16;
+  a.lds_s = G * (pitch + 4) * 4;
   return dyn;
 }
 

@@ -140,15 +140,15 @@ __global__ __launch_bounds__(kThreads) void latent_query_kernel(LatentAttnArgs a
 // attention over the latents
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads, 1) void latent_attn_kernel(LatentAttnArgs a) {
-  // dynamic LDS: Q~ [16, r_k] operand tiles, scores [16][pitch + 1] f32,
+  // dynamic LDS: Q~ [16, r_k] operand tiles, scores [16][pitch + 4] f32,
   // probabilities [pitch / 32][64] operand words
   extern __shared__ __attribute__((aligned(16))) char dlds[];
   uint16_t *qs = reinterpret_cast<uint16_t *>(dlds);
   float *sS = reinterpret_cast<float *>(dlds + a.lds_q);
-  // score row stride one float longer than the split, so the 16 heads' rows
-  // (read and written at one column by lanes j = head) start in different
-  // LDS banks
-  const int spitch = a.pitch + 1;
+  // score row stride four floats longer than the split, so the 16 heads'
+  // rows (read and written at one column by lanes j = head) start in
+  // different LDS banks and stay 16-byte aligned
+  const int spitch = a.pitch + 4;
   u32x4 *pbuf = reinterpret_cast<u32x4 *>(dlds + a.lds_q + a.lds_s);
   __shared__ float smax[kNW][16], psw[kNW][16];
   __shared__ float cmb_m[16], cmb_l[16];
@@ -250,12 +250,18 @@ __global__ __launch_bounds__(kThreads, 1) void latent_attn_kernel(LatentAttnArgs
   const int nU = (npos + 31) >> 5;
   float ps = 0.f;
   for (int u = wave; u < nU; u += kNW) {
-    float v[8];
+    // eight scores read unconditionally (two 16-byte reads); masked
+    // entries become exp2(-inf) = 0 by a select, so the lanes do not branch
+    // around each read and wait on it separately
     const int off = 32 * u + 8 * grp;
+    const float *srow = sS + j * spitch + off;
+    const f32x4 sa = *reinterpret_cast<const f32x4 *>(srow);
+    const f32x4 sb = *reinterpret_cast<const f32x4 *>(srow + 4);
+    const float sv[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+    float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      v[e] = 0.f;
-      if (off + e < npos && m_all != -INFINITY) v[e] = exp2f(sS[j * spitch + off + e] - m_all);
+      v[e] = exp2f(off + e < npos && m_all != -INFINITY ? sv[e] - m_all : -INFINITY);
       ps += v[e];
     }
     pbuf[u * 64 + lane] = u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
@@ -450,7 +456,7 @@ int attn_static_lds() {
 
 int latent_attn_max_split(int r_k) {
   const int dyn = lds_per_block() - attn_static_lds() - kHG * r_k * 2;
-  const int pitch = ((dyn - kHG * 4 - 16) / kPerPos) & ~63;
+  const int pitch = ((dyn - kHG * 16) / kPerPos) & ~63;
   return pitch < 64 ? 0 : std::min(pitch, 4096);
 }
 
@@ -479,7 +485,7 @@ hipError_t launch_latent_attn_bf16(LatentAttnArgs a, hipStream_t s) {
     }
     a.pitch = (a.split_len + 63) / 64 * 64;
     a.lds_q = kHG * a.r_k * 2;
-    a.lds_s = (kHG * (a.pitch + 1) * 4 + 15) / 16 * 16;
+    a.lds_s = kHG * (a.pitch + 4) * 4;
     const int need = a.lds_q + a.lds_s + a.pitch * 32;
     if (need > dyn) return hipErrorInvalidValue;
     const int total = a.Bsz * a.ngroups * a.nsplit;
