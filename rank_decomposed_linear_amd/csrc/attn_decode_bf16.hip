@@ -45,6 +45,7 @@
 //    per-slice base reduced exactly in float64 and a small float32 offset,
 //    so float32 sin/cos see an argument in [-pi, pi] at any position.
 #include <math.h>
+#include <stdlib.h>
 
 #include "common.h"
 #include "kernels.h"
@@ -115,6 +116,142 @@ struct Tile {
   static constexpr int HALF = D / 2;
   __device__ static constexpr int dim(int blk, int row) { return 16 * blk + row; }
 };
+
+
+// The end of a work item (every thread of the workgroup calls it after a
+// barrier): O^T = B_v^T U^T on MFMA by waves 0..3 (U rounded to bf16, read
+// from LDS [16][r_v] at the start of dlds, or from this item's rows of the
+// workspace when ugi is set), normalised into the output, or stored as the
+// split's partial (O, max, sum) with device-coherent stores; then the last
+// workgroup of (b, g) to arrive merges the splits.
+template <int D, int NT>
+__device__ __forceinline__ void finish_item(const AttnDecodeArgs &a, char *dlds, const float *ugi, const float *mfin,
+                                            const float *lfin, float *cmb_m, float *cmb_l, int *last_flag, int w,
+                                            int b, int g, int split) {
+  using T = Tile<D>;
+  constexpr int NB = T::NB;
+  constexpr int OBW = NB / kNW;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 15, grp = lane >> 4;
+  const int G = a.n_q / a.n_kv;
+  const float *ulds = reinterpret_cast<const float *>(dlds);
+  const int D2 = D + 2;
+  float *part = a.part + ((static_cast<size_t>(b) * a.n_q + g * G) * a.nsplit) * D2;
+  if (wave < kNW) {
+    // wave owns d blocks OBW * wave .. +OBW; A = B_v^T tiles, B = U (bf16)
+    f32x4 oacc[OBW];
+#pragma unroll
+    for (int x = 0; x < OBW; ++x) oacc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float *urow = ulds + j * a.r_v + 8 * grp;
+    const float *urow_g = ugi ? ugi + static_cast<size_t>(j) * a.r_v + 8 * grp : nullptr;
+    for (int s0 = 0; s0 < a.r_v / 32; s0 += 2) {   // r_v / 32 is even
+      u32x4 av[2][OBW];
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int x = 0; x < OBW; ++x)
+          av[q][x] = ld16(a.bv + frag_off(g * NB + OBW * wave + x, s0 + q, a.r_v, lane));
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        f32x4 u0, u1;
+        if (ugi) {   // (rows j >= G hold finite values; their outputs are not stored)
+          u0 = load4_coherent(urow_g + 32 * (s0 + q));
+          u1 = load4_coherent(urow_g + 32 * (s0 + q) + 4);
+        } else {
+          u0 = *reinterpret_cast<const f32x4 *>(urow + 32 * (s0 + q));
+          u1 = *reinterpret_cast<const f32x4 *>(urow + 32 * (s0 + q) + 4);
+        }
+        const u32x4 bop = u32x4{pack2(u0[0], u0[1]), pack2(u0[2], u0[3]), pack2(u1[0], u1[1]), pack2(u1[2], u1[3])};
+#pragma unroll
+        for (int x = 0; x < OBW; ++x) oacc[x] = mfma_bf16(av[q][x], bop, oacc[x]);
+      }
+    }
+    // lane (head j, grp) holds O^T[16 (OBW wave + x) + 4grp + r][j]
+    if (j < G) {
+#pragma unroll
+      for (int x = 0; x < OBW; ++x) {
+        const int dd = 16 * (OBW * wave + x) + 4 * grp;
+        if (a.nsplit == 1) {
+          const float il = 1.f / lfin[j];
+          const int col = (g * G + j) * D + dd;
+          const size_t oi = a.out_tiled ? tile_off(b, col, a.n_q * D) : static_cast<size_t>(b) * a.n_q * D + col;
+          if (a.out_f32)
+            *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + oi) = oacc[x] * il;
+          else
+            *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(a.out) + oi) =
+                u32x2{pack2(oacc[x][0] * il, oacc[x][1] * il), pack2(oacc[x][2] * il, oacc[x][3] * il)};
+        } else {
+          float *dst = part + (static_cast<size_t>(j) * a.nsplit + split) * D2;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) store_coherent(dst + dd + r, oacc[x][r]);
+          if (dd == 0) {
+            store_coherent(dst + D, mfin[j]);
+            store_coherent(dst + D + 1, lfin[j]);
+          }
+        }
+      }
+    }
+  }
+  if (a.nsplit == 1) return;
+
+  // ---------------- last workgroup of (b, g) merges the splits ----------------
+  wait_memory();
+  __syncthreads();
+  int *counter = a.counters + b * a.n_kv + g;
+  if (tid == 0)
+    *last_flag = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                a.nsplit - 1;
+  __syncthreads();
+  if (!*last_flag) return;
+  // split statistics -> LDS (reused): sm[h][s], sl[h][s]
+  float *sm = reinterpret_cast<float *>(dlds), *sl = sm + 16 * a.nsplit;
+  for (int idx = tid; idx < G * a.nsplit; idx += NT) {
+    const int h = idx / a.nsplit, sp = idx % a.nsplit;
+    const float *src = part + (static_cast<size_t>(h) * a.nsplit + sp) * D2;
+    sm[idx] = load_coherent(src + D);
+    sl[idx] = load_coherent(src + D + 1);
+  }
+  __syncthreads();
+  if (tid < G) {
+    float M = -INFINITY;
+    for (int sp = 0; sp < a.nsplit; ++sp) M = fmaxf(M, sm[tid * a.nsplit + sp]);
+    float L = 0.f;
+    for (int sp = 0; sp < a.nsplit; ++sp) {
+      const float m = sm[tid * a.nsplit + sp];
+      if (m != -INFINITY) L += exp2f(m - M) * sl[tid * a.nsplit + sp];
+    }
+    cmb_m[tid] = M;
+    cmb_l[tid] = L;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += NT) {
+    const int h = idx / D, dd = idx % D;
+    const float M = cmb_m[h];
+    float o = 0.f;
+    for (int sp0 = 0; sp0 < a.nsplit; sp0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = load_coherent(part + (static_cast<size_t>(h) * a.nsplit + min(sp0 + u, a.nsplit - 1)) * D2 + dd);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int sp = sp0 + u;
+        if (sp < a.nsplit) {
+          const float m = sm[h * a.nsplit + sp];
+          if (m != -INFINITY) o += exp2f(m - M) * v[u];
+        }
+      }
+    }
+    const int col = (g * G + h) * D + dd;
+    const size_t oi = a.out_tiled ? tile_off(b, col, a.n_q * D) : static_cast<size_t>(b) * a.n_q * D + col;
+    if (a.out_f32)
+      static_cast<float *>(a.out)[oi] = o / cmb_l[h];
+    else
+      static_cast<uint16_t *>(a.out)[oi] = f2bf(o / cmb_l[h]);
+  }
+  if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 template <int D, int RBW>
 __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs a) {
@@ -577,122 +714,367 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
     mfin[j] = m_run;
     lfin[j] = l_run;
   }
+  const float *ugi = npass > 1 ? a.uglob + static_cast<size_t>(w) * 16 * a.r_v : nullptr;
   __syncthreads();
-  const int D2 = D + 2;
-  float *part = a.part + ((static_cast<size_t>(b) * a.n_q + g * G) * a.nsplit) * D2;
-  {
-    // wave owns d blocks OBW * wave .. +OBW; A = B_v^T tiles, B = U (bf16)
-    f32x4 oacc[OBW];
+  finish_item<D, kThreads>(a, dlds, ugi, mfin, lfin, cmb_m, cmb_l, &last_flag, w, b, g, split);
+}
+
+// ---------------------------------------------------------------------------
+// Warp-specialised variant (r_v <= 512, whole key factor in LDS): eight
+// waves, two per SIMD. Waves 0..3 (producers) run phase 1 of chunk t (key
+// rebuild, rotation, scores into one of two score buffers) while waves 4..7
+// (consumers) run the softmax and the value products of chunk t - 1 from the
+// other buffer; one workgroup barrier per chunk hands the buffers over. The
+// consumers' value loads, exponentials and MFMAs fill the issue slots that
+// the producers' VALU epilogue and load waits leave on the same SIMD. Each
+// consumer forms the probabilities it multiplies straight from the scores,
+// so the consumers never wait for one another.
+// ---------------------------------------------------------------------------
+constexpr int kWsWaves = 2 * kNW;
+constexpr int kWsThreads = 64 * kWsWaves;
+constexpr int kWsGran = 128;   // chunk lengths are multiples of this (whole value-ring rounds)
+constexpr int kWsVDepth = 4;   // consumer value-ring depth (32-position groups)
+
+template <int D, int NPA, int CD>
+__global__ __launch_bounds__(kWsThreads, 1) void attn_decode_ws_kernel(AttnDecodeArgs a) {
+  using T = Tile<D>;
+  constexpr int NB = T::NB, NE = T::NE, HALF = T::HALF;
+  constexpr int RBW = 8;
+  // dynamic LDS: factor fragments [nrs][NB][64][8] bf16, then scores
+  // [2][G][pitch + 4] f32
+  extern __shared__ __attribute__((aligned(16))) char dlds[];
+  uint16_t *bs = reinterpret_cast<uint16_t *>(dlds);
+  float *sSall = reinterpret_cast<float *>(dlds + a.lds_bs);
+  __shared__ __attribute__((aligned(16))) u32x4 qfs[NB / 2][64];   // score operands, lane order
+  __shared__ double rev64[HALF];
+  __shared__ float rev32[HALF];
+  __shared__ float2 step16[HALF];
+  __shared__ float smax[2][kNW][16];
+  __shared__ float mfin[16], lfin[16], cmb_m[16], cmb_l[16];
+  __shared__ int last_flag;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool producer = wave < kNW;   // uniform across the wave
+  const int rw = wave & (kNW - 1);     // wave index within its role
+  const int j = lane & 15, grp = lane >> 4;
+  const int total = a.Bsz * a.n_kv * a.nsplit;
+  const int w = xcd_item(blockIdx.x, gridDim.x);
+  if (w >= total) return;
+  const int g = w % a.n_kv;
+  const int split = (w / a.n_kv) % a.nsplit;
+  const int b = w / (a.n_kv * a.nsplit);
+  const int G = a.n_q / a.n_kv;
+  const int ctx = a.ctx_lens[b] + a.ctx_offset;
+  const int qpos = ctx - 1;
+  const int p_begin = split * a.split_len;
+  const int p_end = min(p_begin + a.split_len, ctx);
+  const bool rope_on = a.theta != 0.f;
+  const int nrs = a.r_k / 32;
+  const int nrb = a.r_v / 16;
+  const int pitch = a.pitch;          // chunk length, a multiple of kWsGran
+  const int spitch = pitch + 4;       // score row stride (bank spread, 16-byte rows)
+  auto page_of = [&](int p64) { return cache_page_uniform(a.block_table, a.page_stride, b, p64); };
+
+  // ------------------------------ prologue ------------------------------
+  // query values first, then the factor in batches (loads in flight while
+  // the rotary tables and the query operands are formed)
+  constexpr int kQE = (NB / 2) * 64;
+  static_assert(kQE <= kWsThreads, "one query operand entry per thread");
+  const int qt = min(tid >> 6, NB / 2 - 1), qj = lane & 15, qg = lane >> 4;
+  const bool q_mine = tid < kQE && qj < G;
+  float qlo[8], qhi[8];
 #pragma unroll
-    for (int x = 0; x < OBW; ++x) oacc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const float *urow = ulds + j * a.r_v + 8 * grp;
-    const float *urow_g = npass > 1 ? a.uglob + (static_cast<size_t>(w) * 16 + j) * a.r_v + 8 * grp : nullptr;
-    for (int s0 = 0; s0 < a.r_v / 32; s0 += 2) {   // r_v / 32 is even
-      u32x4 av[2][OBW];
+  for (int e = 0; e < 8; ++e) {
+    const int i = T::dim(2 * qt + (e >> 2), 4 * qg + (e & 3)) % HALF;
+    const size_t off = (static_cast<size_t>(b) * a.n_q + g * G + min(qj, G - 1)) * D + i;
+    if (a.q_f32) {
+      qlo[e] = static_cast<const float *>(a.q)[off];
+      qhi[e] = static_cast<const float *>(a.q)[off + HALF];
+    } else {
+      qlo[e] = bf2f(static_cast<const uint16_t *>(a.q)[off]);
+      qhi[e] = bf2f(static_cast<const uint16_t *>(a.q)[off + HALF]);
+    }
+  }
+  constexpr int kPer = 16;
+  const int funits = nrs * NB * 64;
+  auto factor_src = [&](int u) {
+    const int ln = u & 63, x = (u >> 6) % NB, rs = (u >> 6) / NB;
+    return a.bk + frag_off(g * NB + x, rs, a.r_k, ln);
+  };
+  u32x4 fv[kPer];
+  auto factor_batch_load = [&](int u0) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
+    for (int k = 0; k < kPer; ++k) fv[k] = ld16(factor_src(min(u0 + tid + kWsThreads * k, funits - 1)));
+  };
+  auto factor_batch_store = [&](int u0) {
 #pragma unroll
-        for (int x = 0; x < OBW; ++x)
-          av[q][x] = ld16(a.bv + frag_off(g * NB + OBW * wave + x, s0 + q, a.r_v, lane));
+    for (int k = 0; k < kPer; ++k)
+      if (u0 + tid + kWsThreads * k < funits)
+        *reinterpret_cast<u32x4 *>(bs + static_cast<size_t>(u0 + tid + kWsThreads * k) * 8) = fv[k];
+  };
+  factor_batch_load(0);
+  for (int i = tid; i < HALF; i += kWsThreads) {
+    rev64[i] = rope_on ? rope_rev(i, D, a.theta) : 0.0;
+    rev32[i] = static_cast<float>(rev64[i]);
+    float c16, s16;
+    rope_cs(16, rev64[i], c16, s16);
+    step16[i] = float2{c16, s16};
+  }
+  __syncthreads();
+  if (tid < kQE) {
+    float v[8];
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        f32x4 u0, u1;
-        if (npass > 1) {   // (rows j >= G hold finite values; their outputs are not stored)
-          u0 = load4_coherent(urow_g + 32 * (s0 + q));
-          u1 = load4_coherent(urow_g + 32 * (s0 + q) + 4);
+    for (int e = 0; e < 8; ++e) {
+      const int dm = T::dim(2 * qt + (e >> 2), 4 * qg + (e & 3));
+      float x = 0.f;
+      if (q_mine) {
+        if (rope_on) {
+          float c, sn;
+          rope_cs(qpos, rev64[dm % HALF], c, sn);
+          x = dm < HALF ? qlo[e] * c - qhi[e] * sn : qlo[e] * sn + qhi[e] * c;
         } else {
-          u0 = *reinterpret_cast<const f32x4 *>(urow + 32 * (s0 + q));
-          u1 = *reinterpret_cast<const f32x4 *>(urow + 32 * (s0 + q) + 4);
+          x = dm < HALF ? qlo[e] : qhi[e];
         }
-        const u32x4 bop = u32x4{pack2(u0[0], u0[1]), pack2(u0[2], u0[3]), pack2(u1[0], u1[1]), pack2(u1[2], u1[3])};
+      }
+      v[e] = x * a.scale_log2;
+    }
+    qfs[qt][lane] = u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
+  }
+  factor_batch_store(0);
+  for (int u0 = kPer * kWsThreads; u0 < funits; u0 += kPer * kWsThreads) {
+    factor_batch_load(u0);
+    factor_batch_store(u0);
+  }
+  __syncthreads();
+
+  // chunks: the first shorter by w % 4 quarters (workgroups start together;
+  // staggered, their value phases do not all pull from L2 at once), then
+  // whole chunks; every chunk but the last is a multiple of kWsGran long
+  const int span = max(0, p_end - p_begin);
+  const int first_len = max(kWsGran, (pitch - (w & 3) * (pitch / 4)) & ~(kWsGran - 1));
+  const int nch = span == 0 ? 0 : 1 + max(0, (span - first_len + pitch - 1) / pitch);
+  auto chunk_lo = [&](int t) { return t == 0 ? p_begin : p_begin + first_len + (t - 1) * pitch; };
+  auto chunk_hi = [&](int t) { return min(t == 0 ? p_begin + first_len : chunk_lo(t) + pitch, p_end); };
+
+  // Each role runs its own loop over the chunks (its state stays out of the
+  // other's register budget), with one barrier per iteration in both.
+  float *ulds = reinterpret_cast<float *>(dlds);   // [16][r_v] at the end, rows >= G zero
+  if (producer) {
+    for (int it = 0; it <= nch; ++it) {
+      if (it < nch) {
+        // --------------------- phase 1 of chunk it ---------------------
+        const int c0 = chunk_lo(it), c1 = chunk_hi(it);
+        float *sS = sSall + (it & 1) * G * spitch;
+        const int nblk = (c1 - c0 + 15) >> 4;
+        const int share = (nblk + kNW - 1) / kNW;
+        const int b_lo = min(rw * share, nblk), b_hi = min(b_lo + share, nblk);
+        float mx = -INFINITY;
+        const int ngr = (share + NPA - 1) / NPA;
+        const uint16_t *kblk[NPA];
+        for (int gi = 0; gi < ngr; ++gi) {
+          const int g0 = b_lo + NPA * gi;
+          const int np = max(0, min(NPA, b_hi - g0));
+          if (np == 0) continue;
+          const int P0 = c0 + 16 * g0;
 #pragma unroll
-        for (int x = 0; x < OBW; ++x) oacc[x] = mfma_bf16(av[q][x], bop, oacc[x]);
+          for (int pb = 0; pb < NPA; ++pb) {
+            const int kb = (c0 >> 4) + min(g0 + pb, max(b_hi - 1, 0));
+            kblk[pb] = a.ck + static_cast<size_t>(page_of(kb >> 2)) * (kPage * a.r_k) + frag_off(kb & 3, 0, a.r_k, 0);
+          }
+          auto group = [&](auto npc) {
+            constexpr int NPG = decltype(npc)::value;
+            f32x4 acc[NB][NPG];
+#pragma unroll
+            for (int x = 0; x < NB; ++x)
+#pragma unroll
+              for (int pb = 0; pb < NPG; ++pb) acc[x][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int cnt = nrs;
+            u32x4 cf[CD][NPG];
+#pragma unroll
+            for (int d = 0; d < CD; ++d)
+#pragma unroll
+              for (int pb = 0; pb < NPG; ++pb) cf[d][pb] = ld16(kblk[pb] + lane * 8 + 512 * min(d, cnt - 1));
+            u32x4 bop[2][NB];
+#pragma unroll
+            for (int x = 0; x < NB; ++x)
+              bop[0][x] = *reinterpret_cast<const u32x4 *>(bs + (static_cast<size_t>(x) * 64 + lane) * 8);
+            auto rank_step = [&](auto dc, int s, auto refill) {
+              constexpr int d = decltype(dc)::value;
+              constexpr bool kRefill = decltype(refill)::value;
+              const uint16_t *fr = bs + (static_cast<size_t>(min(s + 1, cnt - 1) * NB) * 64 + lane) * 8;
+#pragma unroll
+              for (int x = 0; x < NB; ++x) bop[(d + 1) & 1][x] = *reinterpret_cast<const u32x4 *>(fr + x * 64 * 8);
+#pragma unroll
+              for (int pb = 0; pb < NPG; ++pb)
+#pragma unroll
+                for (int x = 0; x < NB; ++x) acc[x][pb] = mfma_bf16(bop[d & 1][x], cf[d][pb], acc[x][pb]);
+              if constexpr (kRefill) {
+                const int sn = min(s + CD, cnt - 1);
+#pragma unroll
+                for (int pb = 0; pb < NPG; ++pb) cf[d][pb] = ld16(kblk[pb] + lane * 8 + 512 * sn);
+              }
+            };
+            int s0 = 0;
+            for (; s0 + CD <= cnt; s0 += CD) {
+              static_for<CD>([&](auto dc) { rank_step(dc, s0 + decltype(dc)::value, IntC<1>{}); });
+            }
+            static_for<CD>([&](auto dc) {
+              constexpr int d = decltype(dc)::value;
+              if (s0 + d < cnt) {
+                __builtin_amdgcn_s_waitcnt(vmcnt_only((CD - 1 - d) * NPG));
+                rank_step(dc, s0 + d, IntC<0>{});
+              }
+            });
+            // rotation (as in the one-role kernel), then scores
+            if (rope_on) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int e = 0; e < NE; ++e) {
+                  const int fi = 16 * e + 4 * grp + r;
+                  double tb = static_cast<double>(P0) * rev64[fi];
+                  tb -= rint(tb);
+                  float c, sn;
+                  turn_cs(static_cast<float>(tb) + static_cast<float>(j) * rev32[fi], c, sn);
+                  const float2 st = step16[fi];
+#pragma unroll
+                  for (int pb = 0; pb < NPG; ++pb) {
+                    const float x = acc[e][pb][r], y = acc[NE + e][pb][r];
+                    acc[e][pb][r] = x * c - y * sn;
+                    acc[NE + e][pb][r] = x * sn + y * c;
+                    const float cn = c * st.x - sn * st.y;
+                    sn = c * st.y + sn * st.x;
+                    c = cn;
+                  }
+                }
+            }
+#pragma unroll
+            for (int pb = 0; pb < NPG; ++pb) {
+              f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int t = 0; t < NB / 2; ++t)
+                sc = mfma_bf16(pack_acc(acc[2 * t][pb], acc[2 * t + 1][pb]), qfs[t][lane], sc);
+              if (pb < np) {   // uniform
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                  const int off = P0 - c0 + 16 * pb + 4 * grp + r;
+                  const float v = c0 + off < c1 ? sc[r] : -INFINITY;
+                  mx = fmaxf(mx, v);
+                  if (j < G) sS[j * spitch + off] = v;
+                }
+              }
+            }
+          };
+          if constexpr (NPA == 4) {
+            if (np >= 3) group(IntC<4>{});
+            else if (np == 2) group(IntC<2>{});
+            else group(IntC<1>{});
+          } else {
+            if (np == 2) group(IntC<2>{});
+            else group(IntC<1>{});
+          }
+        }
+        mx = wave_max_xor(mx, 16);
+        mx = wave_max_xor(mx, 32);
+        if (grp == 0) smax[it & 1][rw][j] = mx;
+      }
+      __syncthreads();
+    }
+  } else {
+    // ------------------------- consumer state -------------------------
+    float m_run = -INFINITY, l_part = 0.f;   // running max; this lane's share of the running sum
+    f32x4 uacc[RBW];
+#pragma unroll
+    for (int i = 0; i < RBW; ++i) uacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int rb[RBW];
+#pragma unroll
+    for (int i = 0; i < RBW; ++i) rb[i] = min(rw + kNW * i, nrb - 1);
+    // value ring over the split's 32-position groups: slot d holds group
+    // gu0 + d; groups past the last repeat it (never multiplied by a nonzero
+    // probability)
+    const int ngu = (span + 31) >> 5;
+    u32x4 vr[kWsVDepth][RBW];
+    auto vload = [&](u32x4 (&dst)[RBW], int gu) {
+      const int pg32 = (p_begin >> 5) + min(gu, max(ngu - 1, 0));
+      const uint16_t *vb = a.cv + static_cast<size_t>(page_of(pg32 >> 1)) * (kPage * a.r_v) +
+                           (pg32 & 1) * 512 + lane * 8;
+#pragma unroll
+      for (int i = 0; i < RBW; ++i) dst[i] = ld16(vb + rb[i] * 1024);
+    };
+    if (span > 0) {
+#pragma unroll
+      for (int d = 0; d < kWsVDepth; ++d) {
+        vload(vr[d], d);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // lane (head j, grp) holds O^T[16 (OBW wave + x) + 4grp + r][j]
-    if (j < G) {
-#pragma unroll
-      for (int x = 0; x < OBW; ++x) {
-        const int dd = 16 * (OBW * wave + x) + 4 * grp;
-        if (a.nsplit == 1) {
-          const float il = 1.f / lfin[j];
-          const int col = (g * G + j) * D + dd;
-          const size_t oi = a.out_tiled ? tile_off(b, col, a.n_q * D) : static_cast<size_t>(b) * a.n_q * D + col;
-          if (a.out_f32)
-            *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + oi) = oacc[x] * il;
-          else
-            *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(a.out) + oi) =
-                u32x2{pack2(oacc[x][0] * il, oacc[x][1] * il), pack2(oacc[x][2] * il, oacc[x][3] * il)};
-        } else {
-          float *dst = part + (static_cast<size_t>(j) * a.nsplit + split) * D2;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) store_coherent(dst + dd + r, oacc[x][r]);
-          if (dd == 0) {
-            store_coherent(dst + D, mfin[j]);
-            store_coherent(dst + D + 1, lfin[j]);
+
+    for (int it = 0; it <= nch; ++it) {
+      if (it > 0) {
+        // ------------- softmax and value products of chunk it - 1 -------------
+        const int t = it - 1;
+        const int c0 = chunk_lo(t), c1 = chunk_hi(t);
+        const float *sS = sSall + (t & 1) * G * spitch;
+        float m_new = m_run;
+  #pragma unroll
+        for (int wv = 0; wv < kNW; ++wv) m_new = fmaxf(m_new, smax[t & 1][wv][j]);
+        const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+        m_run = m_new;
+        l_part *= alpha;
+  #pragma unroll
+        for (int i = 0; i < RBW; ++i) uacc[i] *= alpha;
+        const float *srow = sS + min(j, G - 1) * spitch + 8 * grp;
+        const int gu_lo = (c0 - p_begin) >> 5;
+        const int nU = (c1 - c0 + 31) >> 5;   // a multiple of kWsVDepth except in the last chunk
+        for (int u0 = 0; u0 < nU; u0 += kWsVDepth) {
+  #pragma unroll
+          for (int d = 0; d < kWsVDepth; ++d) {
+            const int u = u0 + d;
+            // probabilities of this lane's 8 positions for head j (operand
+            // order), from the scores; positions past the chunk are zero
+            const int off = 32 * u;
+            const f32x4 sa = *reinterpret_cast<const f32x4 *>(srow + min(off, pitch - 32));
+            const f32x4 sb = *reinterpret_cast<const f32x4 *>(srow + min(off, pitch - 32) + 4);
+            const float sv[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+            float v[8];
+  #pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              v[e] = exp2f(j < G && u < nU && c0 + off + 8 * grp + e < c1 ? sv[e] - m_new : -INFINITY);
+              l_part += v[e];
+            }
+            const u32x4 pop = u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
+            // value rows at positions >= ctx (unwritten cache) are zeroed: the
+            // probabilities there are zero, but 0 * NaN would not be
+            if (c0 + off + 32 > ctx) {   // uniform; only the context's last group
+              const int nv = ctx - (c0 + off + 8 * grp);
+  #pragma unroll
+              for (int i = 0; i < RBW; ++i) vr[d][i] = keep_first(vr[d][i], nv);
+            }
+  #pragma unroll
+            for (int i = 0; i < RBW; ++i) uacc[i] = mfma_bf16(vr[d][i], pop, uacc[i]);
+            __builtin_amdgcn_sched_barrier(0);
+            vload(vr[d], gu_lo + u + kWsVDepth);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
       }
+      __syncthreads();
     }
-  }
-  if (a.nsplit == 1) return;
-
-  // ---------------- last workgroup of (b, g) merges the splits ----------------
-  wait_memory();
-  __syncthreads();
-  int *counter = a.counters + b * a.n_kv + g;
-  if (tid == 0)
-    last_flag = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                a.nsplit - 1;
-  __syncthreads();
-  if (!last_flag) return;
-  // split statistics -> LDS (reused): sm[h][s], sl[h][s]
-  float *sm = reinterpret_cast<float *>(dlds), *sl = sm + 16 * a.nsplit;
-  for (int idx = tid; idx < G * a.nsplit; idx += kThreads) {
-    const int h = idx / a.nsplit, sp = idx % a.nsplit;
-    const float *src = part + (static_cast<size_t>(h) * a.nsplit + sp) * D2;
-    sm[idx] = load_coherent(src + D);
-    sl[idx] = load_coherent(src + D + 1);
-  }
-  __syncthreads();
-  if (tid < G) {
-    float M = -INFINITY;
-    for (int sp = 0; sp < a.nsplit; ++sp) M = fmaxf(M, sm[tid * a.nsplit + sp]);
-    float L = 0.f;
-    for (int sp = 0; sp < a.nsplit; ++sp) {
-      const float m = sm[tid * a.nsplit + sp];
-      if (m != -INFINITY) L += exp2f(m - M) * sl[tid * a.nsplit + sp];
-    }
-    cmb_m[tid] = M;
-    cmb_l[tid] = L;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < G * D; idx += kThreads) {
-    const int h = idx / D, dd = idx % D;
-    const float M = cmb_m[h];
-    float o = 0.f;
-    for (int sp0 = 0; sp0 < a.nsplit; sp0 += 8) {
-      float v[8];
+    l_part = wave_sum_xor(l_part, 16);
+    l_part = wave_sum_xor(l_part, 32);
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        v[u] = load_coherent(part + (static_cast<size_t>(h) * a.nsplit + min(sp0 + u, a.nsplit - 1)) * D2 + dd);
+    for (int i = 0; i < RBW; ++i)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int sp = sp0 + u;
-        if (sp < a.nsplit) {
-          const float m = sm[h * a.nsplit + sp];
-          if (m != -INFINITY) o += exp2f(m - M) * v[u];
-        }
-      }
+      for (int r = 0; r < 4; ++r) ulds[j * a.r_v + 16 * rb[i] + 4 * grp + r] = j < G ? uacc[i][r] : 0.f;
+    if (rw == 0 && grp == 0) {
+      mfin[j] = m_run;
+      lfin[j] = l_part;
     }
-    const int col = (g * G + h) * D + dd;
-    const size_t oi = a.out_tiled ? tile_off(b, col, a.n_q * D) : static_cast<size_t>(b) * a.n_q * D + col;
-    if (a.out_f32)
-      static_cast<float *>(a.out)[oi] = o / cmb_l[h];
-    else
-      static_cast<uint16_t *>(a.out)[oi] = f2bf(o / cmb_l[h]);
   }
-  if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // ---------------------------- finish ----------------------------
+  __syncthreads();
+  finish_item<D, kWsThreads>(a, dlds, nullptr, mfin, lfin, cmb_m, cmb_l, &last_flag, w, b, g, split);
 }
 
 // LDS of one workgroup on this device (160 KB on gfx950)
@@ -761,10 +1143,57 @@ hipError_t launch_cfg(AttnDecodeArgs a, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Warp-specialised kernel: the whole key factor in LDS and two score buffers
+// of at least two chunk granules each; DL_ATTN_WS=0 selects the one-role
+// kernel, DL_ATTN_WS_NPA=2 or 4 the producers' group size.
+int env_or(const char *name, int dflt) {
+  const char *v = getenv(name);
+  return (v && *v) ? atoi(v) : dflt;
+}
+template <int D, int NPA, int CD>
+hipError_t launch_ws_cfg(AttnDecodeArgs a, int grid, hipStream_t s) {
+  const void *fn = reinterpret_cast<const void *>(&attn_decode_ws_kernel<D, NPA, CD>);
+  static int dyn = -1;
+  if (dyn < 0) {
+    hipFuncAttributes fa;
+    hipError_t e = hipFuncGetAttributes(&fa, fn);
+    if (e != hipSuccess) return e;
+    const int d = lds_per_block() - static_cast<int>(fa.sharedSizeBytes);
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, d);
+    if (e != hipSuccess) return e;
+    dyn = d;
+  }
+  const int G = a.n_q / a.n_kv;
+  a.lds_bs = (a.r_k / 32) * Tile<D>::NB * 1024;
+  const int want = min(kMaxPitch, (a.split_len + kWsGran - 1) / kWsGran * kWsGran);
+  int pitch = ((dyn - a.lds_bs - 2 * 16 * G) / (2 * 4 * G)) & ~(kWsGran - 1);
+  pitch = min(pitch, want);
+  if (pitch < 2 * kWsGran || 64 * a.r_v > dyn) return hipErrorNotSupported;
+  a.pitch = pitch;
+  a.lds_s = 2 * G * (pitch + 4) * 4;
+  a.rs_cap = a.r_k / 32;
+  a.rs_tail = 0;
+  a.vpasses = 1;
+  attn_decode_ws_kernel<D, NPA, CD><<<grid, kWsThreads, dyn, s>>>(a);
+  return hipGetLastError();
+}
+template <int D>
+hipError_t launch_ws(const AttnDecodeArgs &a, int grid, hipStream_t s) {
+  if (a.r_v / 16 > 8 * kNW || env_or("DL_ATTN_WS", 1) == 0) return hipErrorNotSupported;
+  // producers: groups of two 16-position blocks and an 8-step key ring at
+  // d = 128 (four blocks and a 4-step ring do not fit 256 registers), four
+  // blocks at d = 64
+  const int npa = env_or("DL_ATTN_WS_NPA", D == 128 ? 2 : 4);
+  if (npa == 2) return launch_ws_cfg<D, 2, 8>(a, grid, s);
+  return launch_ws_cfg<D, 4, 4>(a, grid, s);
+}
+
 template <int D>
 hipError_t launch_d(AttnDecodeArgs a, int grid, hipStream_t s) {
   const int nrb = a.r_v / 16;
   if (nrb <= 8 * kNW) {
+    const hipError_t e = launch_ws<D>(a, grid, s);
+    if (e != hipErrorNotSupported) return e;
     a.vpasses = 1;
     return launch_cfg<D, 8>(a, grid, s);
   }
