@@ -39,6 +39,7 @@ KINDS = (
     ("gemv_chain_kernel", "gemv_chain"),
     ("gemv_kernel", "gemv_bf16"),
     ("attn_decode_kernel", "attn_decode_bf16"),
+    ("attn_decode_ws_kernel", "attn_decode_bf16"),
     ("attn_prefill_kernel", "attn_prefill_bf16"),
     ("attn_rebuild_kernel", "attn_prefill_bf16"),
     ("latent_query_kernel", "attn_latent"),
