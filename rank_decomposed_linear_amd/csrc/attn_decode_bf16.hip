@@ -720,23 +720,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
 }
 
 // ---------------------------------------------------------------------------
-// Warp-specialised variant (r_v <= 512, whole key factor in LDS): eight
-// waves, two per SIMD. Waves 0..3 (producers) run phase 1 of chunk t (key
-// rebuild, rotation, scores into one of two score buffers) while waves 4..7
-// (consumers) run the softmax and the value products of chunk t - 1 from the
-// other buffer; one workgroup barrier per chunk hands the buffers over. The
-// consumers' value loads, exponentials and MFMAs fill the issue slots that
-// the producers' VALU epilogue and load waits leave on the same SIMD. Each
+// Warp-specialised variant (r_v <= 512, whole key factor in LDS): PW
+// producer waves and four consumer waves. The producers run phase 1 of
+// chunk t (key rebuild, rotation, scores into one of two score buffers)
+// while the consumers run the softmax and the value products of chunk t - 1
+// from the other buffer; one workgroup barrier per chunk hands the buffers
+// over. With PW = 8 each SIMD holds two producers and one consumer: one
+// producer's VALU epilogue and load waits overlap the other's MFMAs, and the
+// consumer's value loads, exponentials and MFMAs fill what is left. Each
 // consumer forms the probabilities it multiplies straight from the scores,
 // so the consumers never wait for one another.
 // ---------------------------------------------------------------------------
-constexpr int kWsWaves = 2 * kNW;
-constexpr int kWsThreads = 64 * kWsWaves;
 constexpr int kWsGran = 128;   // chunk lengths are multiples of this (whole value-ring rounds)
 constexpr int kWsVDepth = 4;   // consumer value-ring depth (32-position groups)
 
-template <int D, int NPA, int CD>
-__global__ __launch_bounds__(kWsThreads, 1) void attn_decode_ws_kernel(AttnDecodeArgs a) {
+template <int D, int NPA, int CD, int PW, int VD, int BD>
+__global__ __launch_bounds__(64 * (PW + kNW), 1) void attn_decode_ws_kernel(AttnDecodeArgs a) {
+  constexpr int kT = 64 * (PW + kNW);   // PW producer waves, then kNW consumer waves
   using T = Tile<D>;
   constexpr int NB = T::NB, NE = T::NE, HALF = T::HALF;
   constexpr int RBW = 8;
@@ -749,14 +749,14 @@ __global__ __launch_bounds__(kWsThreads, 1) void attn_decode_ws_kernel(AttnDecod
   __shared__ double rev64[HALF];
   __shared__ float rev32[HALF];
   __shared__ float2 step16[HALF];
-  __shared__ float smax[2][kNW][16];
+  __shared__ float smax[2][PW][16];
   __shared__ float mfin[16], lfin[16], cmb_m[16], cmb_l[16];
   __shared__ int last_flag;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool producer = wave < kNW;   // uniform across the wave
-  const int rw = wave & (kNW - 1);     // wave index within its role
+  const bool producer = wave < PW;   // uniform across the wave
+  const int rw = producer ? wave : wave - PW;   // wave index within its role
   const int j = lane & 15, grp = lane >> 4;
   const int total = a.Bsz * a.n_kv * a.nsplit;
   const int w = xcd_item(blockIdx.x, gridDim.x);
@@ -780,7 +780,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void attn_decode_ws_kernel(AttnDecod
   // query values first, then the factor in batches (loads in flight while
   // the rotary tables and the query operands are formed)
   constexpr int kQE = (NB / 2) * 64;
-  static_assert(kQE <= kWsThreads, "one query operand entry per thread");
+  static_assert(kQE <= kT, "one query operand entry per thread");
   const int qt = min(tid >> 6, NB / 2 - 1), qj = lane & 15, qg = lane >> 4;
   const bool q_mine = tid < kQE && qj < G;
   float qlo[8], qhi[8];
@@ -805,16 +805,16 @@ __global__ __launch_bounds__(kWsThreads, 1) void attn_decode_ws_kernel(AttnDecod
   u32x4 fv[kPer];
   auto factor_batch_load = [&](int u0) {
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) fv[k] = ld16(factor_src(min(u0 + tid + kWsThreads * k, funits - 1)));
+    for (int k = 0; k < kPer; ++k) fv[k] = ld16(factor_src(min(u0 + tid + kT * k, funits - 1)));
   };
   auto factor_batch_store = [&](int u0) {
 #pragma unroll
     for (int k = 0; k < kPer; ++k)
-      if (u0 + tid + kWsThreads * k < funits)
-        *reinterpret_cast<u32x4 *>(bs + static_cast<size_t>(u0 + tid + kWsThreads * k) * 8) = fv[k];
+      if (u0 + tid + kT * k < funits)
+        *reinterpret_cast<u32x4 *>(bs + static_cast<size_t>(u0 + tid + kT * k) * 8) = fv[k];
   };
   factor_batch_load(0);
-  for (int i = tid; i < HALF; i += kWsThreads) {
+  for (int i = tid; i < HALF; i += kT) {
     rev64[i] = rope_on ? rope_rev(i, D, a.theta) : 0.0;
     rev32[i] = static_cast<float>(rev64[i]);
     float c16, s16;
@@ -842,7 +842,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void attn_decode_ws_kernel(AttnDecod
     qfs[qt][lane] = u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
   }
   factor_batch_store(0);
-  for (int u0 = kPer * kWsThreads; u0 < funits; u0 += kPer * kWsThreads) {
+  for (int u0 = kPer * kT; u0 < funits; u0 += kPer * kT) {
     factor_batch_load(u0);
     factor_batch_store(u0);
   }
@@ -867,7 +867,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void attn_decode_ws_kernel(AttnDecod
         const int c0 = chunk_lo(it), c1 = chunk_hi(it);
         float *sS = sSall + (it & 1) * G * spitch;
         const int nblk = (c1 - c0 + 15) >> 4;
-        const int share = (nblk + kNW - 1) / kNW;
+        const int share = (nblk + PW - 1) / PW;
         const int b_lo = min(rw * share, nblk), b_hi = min(b_lo + share, nblk);
         float mx = -INFINITY;
         const int ngr = (share + NPA - 1) / NPA;
@@ -895,20 +895,28 @@ __global__ __launch_bounds__(kWsThreads, 1) void attn_decode_ws_kernel(AttnDecod
             for (int d = 0; d < CD; ++d)
 #pragma unroll
               for (int pb = 0; pb < NPG; ++pb) cf[d][pb] = ld16(kblk[pb] + lane * 8 + 512 * min(d, cnt - 1));
-            u32x4 bop[2][NB];
+            // factor fragments: BD = 2 reads the next step's during this one;
+            // BD = 1 reads each step's at its start (other waves on the SIMD
+            // cover the latency)
+            u32x4 bop[BD][NB];
+            if constexpr (BD == 2) {
 #pragma unroll
-            for (int x = 0; x < NB; ++x)
-              bop[0][x] = *reinterpret_cast<const u32x4 *>(bs + (static_cast<size_t>(x) * 64 + lane) * 8);
+              for (int x = 0; x < NB; ++x)
+                bop[0][x] = *reinterpret_cast<const u32x4 *>(bs + (static_cast<size_t>(x) * 64 + lane) * 8);
+            }
             auto rank_step = [&](auto dc, int s, auto refill) {
               constexpr int d = decltype(dc)::value;
               constexpr bool kRefill = decltype(refill)::value;
-              const uint16_t *fr = bs + (static_cast<size_t>(min(s + 1, cnt - 1) * NB) * 64 + lane) * 8;
+              constexpr int cur = BD == 2 ? (d & 1) : 0;
+              const uint16_t *fr =
+                  bs + (static_cast<size_t>((BD == 2 ? min(s + 1, cnt - 1) : s) * NB) * 64 + lane) * 8;
 #pragma unroll
-              for (int x = 0; x < NB; ++x) bop[(d + 1) & 1][x] = *reinterpret_cast<const u32x4 *>(fr + x * 64 * 8);
+              for (int x = 0; x < NB; ++x)
+                bop[BD == 2 ? (d + 1) & 1 : 0][x] = *reinterpret_cast<const u32x4 *>(fr + x * 64 * 8);
 #pragma unroll
               for (int pb = 0; pb < NPG; ++pb)
 #pragma unroll
-                for (int x = 0; x < NB; ++x) acc[x][pb] = mfma_bf16(bop[d & 1][x], cf[d][pb], acc[x][pb]);
+                for (int x = 0; x < NB; ++x) acc[x][pb] = mfma_bf16(bop[cur][x], cf[d][pb], acc[x][pb]);
               if constexpr (kRefill) {
                 const int sn = min(s + CD, cnt - 1);
 #pragma unroll
@@ -994,7 +1002,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void attn_decode_ws_kernel(AttnDecod
     // gu0 + d; groups past the last repeat it (never multiplied by a nonzero
     // probability)
     const int ngu = (span + 31) >> 5;
-    u32x4 vr[kWsVDepth][RBW];
+    u32x4 vr[VD][RBW];
     auto vload = [&](u32x4 (&dst)[RBW], int gu) {
       const int pg32 = (p_begin >> 5) + min(gu, max(ngu - 1, 0));
       const uint16_t *vb = a.cv + static_cast<size_t>(page_of(pg32 >> 1)) * (kPage * a.r_v) +
@@ -1004,7 +1012,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void attn_decode_ws_kernel(AttnDecod
     };
     if (span > 0) {
 #pragma unroll
-      for (int d = 0; d < kWsVDepth; ++d) {
+      for (int d = 0; d < VD; ++d) {
         vload(vr[d], d);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -1018,7 +1026,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void attn_decode_ws_kernel(AttnDecod
         const float *sS = sSall + (t & 1) * G * spitch;
         float m_new = m_run;
   #pragma unroll
-        for (int wv = 0; wv < kNW; ++wv) m_new = fmaxf(m_new, smax[t & 1][wv][j]);
+        for (int wv = 0; wv < PW; ++wv) m_new = fmaxf(m_new, smax[t & 1][wv][j]);
         const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
         m_run = m_new;
         l_part *= alpha;
@@ -1026,10 +1034,10 @@ __global__ __launch_bounds__(kWsThreads, 1) void attn_decode_ws_kernel(AttnDecod
         for (int i = 0; i < RBW; ++i) uacc[i] *= alpha;
         const float *srow = sS + min(j, G - 1) * spitch + 8 * grp;
         const int gu_lo = (c0 - p_begin) >> 5;
-        const int nU = (c1 - c0 + 31) >> 5;   // a multiple of kWsVDepth except in the last chunk
-        for (int u0 = 0; u0 < nU; u0 += kWsVDepth) {
+        const int nU = (c1 - c0 + 31) >> 5;   // a multiple of VD except in the last chunk
+        for (int u0 = 0; u0 < nU; u0 += VD) {
   #pragma unroll
-          for (int d = 0; d < kWsVDepth; ++d) {
+          for (int d = 0; d < VD; ++d) {
             const int u = u0 + d;
             // probabilities of this lane's 8 positions for head j (operand
             // order), from the scores; positions past the chunk are zero
@@ -1054,7 +1062,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void attn_decode_ws_kernel(AttnDecod
   #pragma unroll
             for (int i = 0; i < RBW; ++i) uacc[i] = mfma_bf16(vr[d][i], pop, uacc[i]);
             __builtin_amdgcn_sched_barrier(0);
-            vload(vr[d], gu_lo + u + kWsVDepth);
+            vload(vr[d], gu_lo + u + VD);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
@@ -1074,7 +1082,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void attn_decode_ws_kernel(AttnDecod
   }
   // ---------------------------- finish ----------------------------
   __syncthreads();
-  finish_item<D, kWsThreads>(a, dlds, nullptr, mfin, lfin, cmb_m, cmb_l, &last_flag, w, b, g, split);
+  finish_item<D, kT>(a, dlds, nullptr, mfin, lfin, cmb_m, cmb_l, &last_flag, w, b, g, split);
 }
 
 // LDS of one workgroup on this device (160 KB on gfx950)
@@ -1144,15 +1152,18 @@ hipError_t launch_cfg(AttnDecodeArgs a, int grid, hipStream_t s) {
 }
 
 // Warp-specialised kernel: the whole key factor in LDS and two score buffers
-// of at least two chunk granules each; DL_ATTN_WS=0 selects the one-role
-// kernel, DL_ATTN_WS_NPA=2 or 4 the producers' group size.
+// of at least two chunk granules each. Default: 8 producers (groups of two
+// 16-position blocks, a 4-step key ring, factor fragments read per step) and
+// consumers with a 2-group value ring, 161 registers for three waves per SIMD;
+// DL_ATTN_WS_PW=4 selects 4 producers (8-step key ring, double-buffered
+// factor fragments, 4-group value ring), DL_ATTN_WS=0 the one-role kernel.
 int env_or(const char *name, int dflt) {
   const char *v = getenv(name);
   return (v && *v) ? atoi(v) : dflt;
 }
-template <int D, int NPA, int CD>
+template <int D, int NPA, int CD, int PW, int VD, int BD>
 hipError_t launch_ws_cfg(AttnDecodeArgs a, int grid, hipStream_t s) {
-  const void *fn = reinterpret_cast<const void *>(&attn_decode_ws_kernel<D, NPA, CD>);
+  const void *fn = reinterpret_cast<const void *>(&attn_decode_ws_kernel<D, NPA, CD, PW, VD, BD>);
   static int dyn = -1;
   if (dyn < 0) {
     hipFuncAttributes fa;
@@ -1174,7 +1185,7 @@ hipError_t launch_ws_cfg(AttnDecodeArgs a, int grid, hipStream_t s) {
   a.rs_cap = a.r_k / 32;
   a.rs_tail = 0;
   a.vpasses = 1;
-  attn_decode_ws_kernel<D, NPA, CD><<<grid, kWsThreads, dyn, s>>>(a);
+  attn_decode_ws_kernel<D, NPA, CD, PW, VD, BD><<<grid, 64 * (PW + kNW), dyn, s>>>(a);
   return hipGetLastError();
 }
 template <int D>
@@ -1183,9 +1194,10 @@ hipError_t launch_ws(const AttnDecodeArgs &a, int grid, hipStream_t s) {
   // producers: groups of two 16-position blocks and an 8-step key ring at
   // d = 128 (four blocks and a 4-step ring do not fit 256 registers), four
   // blocks at d = 64
+  if (env_or("DL_ATTN_WS_PW", 8) == 8) return launch_ws_cfg<D, 2, 4, 8, 2, 1>(a, grid, s);
   const int npa = env_or("DL_ATTN_WS_NPA", D == 128 ? 2 : 4);
-  if (npa == 2) return launch_ws_cfg<D, 2, 8>(a, grid, s);
-  return launch_ws_cfg<D, 4, 4>(a, grid, s);
+  if (npa == 2) return launch_ws_cfg<D, 2, 8, 4, 4, 2>(a, grid, s);
+  return launch_ws_cfg<D, 4, 4, 4, 4, 2>(a, grid, s);
 }
 
 template <int D>
