@@ -732,7 +732,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
 // so the consumers never wait for one another.
 // ---------------------------------------------------------------------------
 constexpr int kWsGran = 128;   // chunk lengths are multiples of this (whole value-ring rounds)
-constexpr int kWsVDepth = 4;   // consumer value-ring depth (32-position groups)
 
 template <int D, int NPA, int CD, int PW, int VD, int BD>
 __global__ __launch_bounds__(64 * (PW + kNW), 1) void attn_decode_ws_kernel(AttnDecodeArgs a) {
