@@ -739,16 +739,19 @@ __global__ __launch_bounds__(64 * (PW + kNW), 1) void attn_decode_ws_kernel(Attn
   using T = Tile<D>;
   constexpr int NB = T::NB, NE = T::NE, HALF = T::HALF;
   constexpr int RBW = 8;
-  // dynamic LDS: factor fragments [nrs][NB][64][8] bf16, then scores
-  // [2][G][pitch + 4] f32
+  // dynamic LDS: factor fragments [nrs][NB][64][8] bf16, scores
+  // [2][G][pitch + 4] f32, probabilities [pitch / 32][64] operand words
   extern __shared__ __attribute__((aligned(16))) char dlds[];
   uint16_t *bs = reinterpret_cast<uint16_t *>(dlds);
   float *sSall = reinterpret_cast<float *>(dlds + a.lds_bs);
+  u32x4 *pbuf = reinterpret_cast<u32x4 *>(dlds + a.lds_bs + a.lds_s);
   __shared__ __attribute__((aligned(16))) u32x4 qfs[NB / 2][64];   // score operands, lane order
   __shared__ double rev64[HALF];
   __shared__ float rev32[HALF];
   __shared__ float2 step16[HALF];
   __shared__ float smax[2][PW][16];
+  __shared__ float lpart[kNW][16];
+  __shared__ int pdone;   // consumer probability shares published so far
   __shared__ float mfin[16], lfin[16], cmb_m[16], cmb_l[16];
   __shared__ int last_flag;
 
@@ -813,6 +816,7 @@ __global__ __launch_bounds__(64 * (PW + kNW), 1) void attn_decode_ws_kernel(Attn
         *reinterpret_cast<u32x4 *>(bs + static_cast<size_t>(u0 + tid + kT * k) * 8) = fv[k];
   };
   factor_batch_load(0);
+  if (tid == 0) pdone = 0;
   for (int i = tid; i < HALF; i += kT) {
     rev64[i] = rope_on ? rope_rev(i, D, a.theta) : 0.0;
     rev32[i] = static_cast<float>(rev64[i]);
@@ -1034,23 +1038,41 @@ __global__ __launch_bounds__(64 * (PW + kNW), 1) void attn_decode_ws_kernel(Attn
         const float *srow = sS + min(j, G - 1) * spitch + 8 * grp;
         const int gu_lo = (c0 - p_begin) >> 5;
         const int nU = (c1 - c0 + 31) >> 5;   // a multiple of VD except in the last chunk
+        // this consumer's share of the probabilities (32-position groups
+        // u = rw, rw + 4, ...), in operand order: lane (head j, grp) holds
+        // positions 32 u + 8 grp .. +7; positions past the chunk are zero
+        for (int u = rw; u < nU; u += kNW) {
+          const int off = 32 * u;
+          const f32x4 sa = *reinterpret_cast<const f32x4 *>(srow + off);
+          const f32x4 sb = *reinterpret_cast<const f32x4 *>(srow + off + 4);
+          const float sv[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+          float v[8];
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            v[e] = exp2f(j < G && c0 + off + 8 * grp + e < c1 ? sv[e] - m_new : -INFINITY);
+            l_part += v[e];
+          }
+          pbuf[u * 64 + lane] = u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
+        }
+        // publish the share (this wave's LDS writes complete, then one count),
+        // then wait for the other consumers' shares of this chunk; the wait is
+        // bounded (a missing count would give wrong results, not a hang)
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0); vmcnt, expcnt free
+        if (lane == 0) __hip_atomic_fetch_add(&pdone, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        for (int spin = 0; spin < (1 << 20); ++spin) {
+          const int n = __builtin_amdgcn_readfirstlane(
+              __hip_atomic_load(&pdone, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+          if (n >= kNW * it) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        asm volatile("" ::: "memory");
         for (int u0 = 0; u0 < nU; u0 += VD) {
   #pragma unroll
           for (int d = 0; d < VD; ++d) {
             const int u = u0 + d;
-            // probabilities of this lane's 8 positions for head j (operand
-            // order), from the scores; positions past the chunk are zero
             const int off = 32 * u;
-            const f32x4 sa = *reinterpret_cast<const f32x4 *>(srow + min(off, pitch - 32));
-            const f32x4 sb = *reinterpret_cast<const f32x4 *>(srow + min(off, pitch - 32) + 4);
-            const float sv[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
-            float v[8];
-  #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              v[e] = exp2f(j < G && u < nU && c0 + off + 8 * grp + e < c1 ? sv[e] - m_new : -INFINITY);
-              l_part += v[e];
-            }
-            const u32x4 pop = u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
+            u32x4 pop = pbuf[min(u, nU - 1) * 64 + lane];
+            if (u >= nU) pop = u32x4{0u, 0u, 0u, 0u};
             // value rows at positions >= ctx (unwritten cache) are zeroed: the
             // probabilities there are zero, but 0 * NaN would not be
             if (c0 + off + 32 > ctx) {   // uniform; only the context's last group
@@ -1074,12 +1096,17 @@ __global__ __launch_bounds__(64 * (PW + kNW), 1) void attn_decode_ws_kernel(Attn
     for (int i = 0; i < RBW; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) ulds[j * a.r_v + 16 * rb[i] + 4 * grp + r] = j < G ? uacc[i][r] : 0.f;
-    if (rw == 0 && grp == 0) {
-      mfin[j] = m_run;
-      lfin[j] = l_part;
-    }
+    if (grp == 0) lpart[rw][j] = l_part;   // this consumer's share of the sums
+    if (rw == 0 && grp == 0) mfin[j] = m_run;
   }
   // ---------------------------- finish ----------------------------
+  __syncthreads();
+  if (tid < 16) {
+    float l = 0.f;
+#pragma unroll
+    for (int c = 0; c < kNW; ++c) l += lpart[c][tid];
+    lfin[tid] = l;
+  }
   __syncthreads();
   finish_item<D, kT>(a, dlds, nullptr, mfin, lfin, cmb_m, cmb_l, &last_flag, w, b, g, split);
 }
@@ -1176,7 +1203,9 @@ hipError_t launch_ws_cfg(AttnDecodeArgs a, int grid, hipStream_t s) {
   const int G = a.n_q / a.n_kv;
   a.lds_bs = (a.r_k / 32) * Tile<D>::NB * 1024;
   const int want = min(kMaxPitch, (a.split_len + kWsGran - 1) / kWsGran * kWsGran);
-  int pitch = ((dyn - a.lds_bs - 2 * 16 * G) / (2 * 4 * G)) & ~(kWsGran - 1);
+  // two score buffers (4 G bytes per position, rows padded by 16 bytes) and
+  // one probability buffer (32 bytes per position)
+  int pitch = ((dyn - a.lds_bs - 2 * 16 * G) / (2 * 4 * G + 32)) & ~(kWsGran - 1);
   pitch = min(pitch, want);
   if (pitch < 2 * kWsGran || 64 * a.r_v > dyn) return hipErrorNotSupported;
   a.pitch = pitch;
