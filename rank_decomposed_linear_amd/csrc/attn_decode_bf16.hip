@@ -1202,12 +1202,17 @@ hipError_t launch_ws_cfg(AttnDecodeArgs a, int grid, hipStream_t s) {
   }
   const int G = a.n_q / a.n_kv;
   a.lds_bs = (a.r_k / 32) * Tile<D>::NB * 1024;
-  const int want = min(kMaxPitch, (a.split_len + kWsGran - 1) / kWsGran * kWsGran);
+  // chunk granule: one group per producer, so every producer gets the same
+  // number of whole groups (a chunk of 384 positions gave 8 producers one
+  // full and one single-block group each: 310 against 288 us at 256), and at
+  // least kWsGran (whole value-ring rounds)
+  const int gran = max(kWsGran, 16 * NPA * PW);
+  const int want = min(kMaxPitch, (a.split_len + gran - 1) / gran * gran);
   // two score buffers (4 G bytes per position, rows padded by 16 bytes) and
   // one probability buffer (32 bytes per position)
-  int pitch = ((dyn - a.lds_bs - 2 * 16 * G) / (2 * 4 * G + 32)) & ~(kWsGran - 1);
+  int pitch = ((dyn - a.lds_bs - 2 * 16 * G) / (2 * 4 * G + 32)) / gran * gran;
   pitch = min(pitch, want);
-  if (pitch < 2 * kWsGran || 64 * a.r_v > dyn) return hipErrorNotSupported;
+  if (pitch < max(gran, 2 * kWsGran) || 64 * a.r_v > dyn) return hipErrorNotSupported;
   a.pitch = pitch;
   a.lds_s = 2 * G * (pitch + 4) * 4;
   a.rs_cap = a.r_k / 32;
