@@ -206,10 +206,19 @@ int fuse_mode() {
   return FUSE_ALL;
 }
 
-hipError_t gemm(GemmArgs &a, hipStream_t s) {
+// `part`: f32 scratch for the remainder split (NULL: the GEMM runs unsplit)
+hipError_t gemm(GemmArgs &a, hipStream_t s, float *part = nullptr, size_t part_bytes = 0) {
   for (int i = 0; i < a.nseg; ++i)
     if (a.seg[i].omode < 0) a.seg[i].omode = a.omode;
+  a.part = part;
+  a.part_bytes = part_bytes;
   return launch_gemm_bf16(a, s);
+}
+
+// Partial bytes of the two GEMMs of a factor pair at prefill-sized M.
+size_t pair_part_bytes(int64_t M, int64_t m, int64_t k, int64_t n) {
+  return std::max(gemm_part_bytes((int)M, gemm_ntiles((int)k), (int)m),
+                  gemm_part_bytes((int)M, gemm_ntiles((int)n), (int)k));
 }
 
 GemmSeg mseg(const void *W, const void *X, void *C, int N, int ldx, int ldc) {
@@ -597,6 +606,7 @@ size_t dl_lowrank_linear_workspace(int64_t M, int64_t m, int64_t k, int64_t n, d
     c.take<uint16_t>(mpad(M) * k);
   } else {
     c.take<uint16_t>(static_cast<size_t>(M * k));
+    c.take<float>(pair_part_bytes(M, m, k, n) / sizeof(float));
   }
   return c.off;
 }
@@ -652,6 +662,8 @@ dl_status dl_lowrank_linear(const void *x, const void *A, const void *B, void *y
     return DL_OK;
   }
   uint16_t *t = c.take<uint16_t>(static_cast<size_t>(M * k));
+  const size_t pb = pair_part_bytes(M, m, k, n);
+  float *part = c.take<float>(pb / sizeof(float));
   GemmArgs a{};
   a.nseg = 1;
   a.M = Mi;
@@ -659,7 +671,7 @@ dl_status dl_lowrank_linear(const void *x, const void *A, const void *B, void *y
   a.xmode = GEMM_X_BF16;
   a.omode = GEMM_OUT_BF16;
   a.seg[0] = mseg(A, x, t, ki, mi, ki);
-  DL_HIP(gemm(a, s));
+  DL_HIP(gemm(a, s, part, pb));
   GemmArgs b{};
   b.nseg = 1;
   b.M = Mi;
@@ -667,7 +679,7 @@ dl_status dl_lowrank_linear(const void *x, const void *A, const void *B, void *y
   b.xmode = GEMM_X_BF16;
   b.omode = GEMM_OUT_BF16;
   b.seg[0] = mseg(B, t, y, ni, ki, ni);
-  DL_HIP(gemm(b, s));
+  DL_HIP(gemm(b, s, part, pb));
   return DL_OK;
 }
 
@@ -1043,6 +1055,8 @@ struct LayerWS {
   uint16_t *att16, *H16, *a16t, *x2g;
   // bf16 large-M (MFMA GEMM) path
   uint16_t *a16, *b16, *tq16, *q16, *to16, *tg16, *tu16, *G16, *td16;
+  float *gpart;         // f32 partials of the GEMMs' remainder split
+  size_t gpart_bytes;
 };
 
 enum { G_QKV, G_QUP, G_ODOWN, G_OUP, G_GUD, G_GUU, G_DD, G_DU, G_NUM };
@@ -1184,6 +1198,23 @@ static void carve_layer(Carver &c, const LayerDims &D, const dl_layer *L, LayerW
   w.tu16 = c.take<uint16_t>(M * D.ru);
   w.G16 = c.take<uint16_t>(M * D.f);
   w.td16 = c.take<uint16_t>(M * D.rd);
+  // one partial buffer for the step's GEMMs (they run in order on one
+  // stream): the largest need over their shapes, (column tiles, depth)
+  const int nt = gemm_ntiles(D.rq) + gemm_ntiles(D.rk) + gemm_ntiles(D.rv);
+  const int gud = D.relu ? gemm_ntiles(D.ru) : gemm_ntiles(D.rg) + gemm_ntiles(D.ru);
+  const int shapes[][2] = {{nt, D.h},
+                           {gemm_ntiles(D.qd()), D.rq},
+                           {gemm_ntiles(D.ro), D.qd()},
+                           {gemm_ntiles(D.h), D.ro},
+                           {gud, D.h},
+                           {gemm_ntiles(D.f), D.rg},
+                           {gemm_ntiles(D.f), D.ru},
+                           {gemm_ntiles(D.rd), D.f},
+                           {gemm_ntiles(D.h), D.rd}};
+  size_t pb = 0;
+  for (const auto &sh : shapes) pb = std::max(pb, gemm_part_bytes(D.M, sh[0], sh[1]));
+  w.gpart_bytes = pb;
+  w.gpart = c.take<float>(pb / sizeof(float));
 }
 
 // Decode batches of 65 .. 512 sequences run as chunks of 64 sequences on
@@ -1382,7 +1413,7 @@ static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_
     a.seg[2] = mseg(L->v.A, w.a16, Cv, D.rv, h, D.rv);
     a.seg[2].omode = GEMM_OUT_CACHE_T;
     set_role(R_QKV_DOWN);
-    DL_HIP(gemm(a, s));
+    DL_HIP(gemm(a, s, w.gpart, w.gpart_bytes));
     GemmArgs q{};
     q.nseg = 1;
     q.M = M;
@@ -1390,7 +1421,7 @@ static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_
     q.omode = GEMM_OUT_BF16;
     q.seg[0] = mseg(L->q.B, w.tq16, w.q16, qd, D.rq, qd);
     set_role(R_Q_UP);
-    DL_HIP(gemm(q, s));
+    DL_HIP(gemm(q, s, w.gpart, w.gpart_bytes));
   }
   set_role(R_ATTENTION);
   if (aw.counters) {
@@ -1409,7 +1440,7 @@ static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_
     a.omode = GEMM_OUT_BF16;
     a.seg[0] = mseg(L->o.A, w.att16, w.to16, D.ro, qd, D.ro);
     set_role(R_O_DOWN);
-    DL_HIP(gemm(a, s));
+    DL_HIP(gemm(a, s, w.gpart, w.gpart_bytes));
     GemmArgs b{};
     b.nseg = 1;
     b.M = M;
@@ -1420,7 +1451,7 @@ static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_
     b.seg[0].R = x;
     b.seg[0].ldr = h;
     set_role(R_O_UP);
-    DL_HIP(gemm(b, s));
+    DL_HIP(gemm(b, s, w.gpart, w.gpart_bytes));
   }
   if (x2_out) {
     FillRegion cp[1] = {{static_cast<float *>(x2_out), w.x2f, 0, (int64_t)M * h}};
@@ -1442,7 +1473,7 @@ static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_
       a.seg[1] = mseg(L->up.A, w.b16, w.tu16, D.ru, h, D.ru);
     }
     set_role(R_GATE_UP_DOWN);
-    DL_HIP(gemm(a, s));
+    DL_HIP(gemm(a, s, w.gpart, w.gpart_bytes));
   }
   if (D.relu) {
     // non-GLU MLP: H = relu(t_u B_up), into the buffer the down pair reads
@@ -1453,7 +1484,7 @@ static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_
     a.omode = GEMM_OUT_RELU;
     a.seg[0] = mseg(L->up.B, w.tu16, w.G16, D.f, D.ru, D.f);
     set_role(R_GATE_UP_UP);
-    DL_HIP(gemm(a, s));
+    DL_HIP(gemm(a, s, w.gpart, w.gpart_bytes));
   } else {
     // G = t_g B_g, then the up product's epilogue forms H = silu(G) * (t_u B_u)
     // in place over G
@@ -1464,13 +1495,13 @@ static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_
     a.omode = GEMM_OUT_BF16;
     a.seg[0] = mseg(L->gate.B, w.tg16, w.G16, D.f, D.rg, D.f);
     set_role(R_GATE_UP_UP);
-    DL_HIP(gemm(a, s));
+    DL_HIP(gemm(a, s, w.gpart, w.gpart_bytes));
     a.K = D.ru;
     a.omode = GEMM_OUT_SWIGLU;
     a.seg[0] = mseg(L->up.B, w.tu16, w.G16, D.f, D.ru, D.f);
     a.seg[0].R = w.G16;
     a.seg[0].ldr = D.f;
-    DL_HIP(gemm(a, s));
+    DL_HIP(gemm(a, s, w.gpart, w.gpart_bytes));
   }
   {
     GemmArgs a{};
@@ -1481,7 +1512,7 @@ static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_
     a.omode = GEMM_OUT_BF16;
     a.seg[0] = mseg(L->down.A, w.G16, w.td16, D.rd, D.f, D.rd);
     set_role(R_DOWN_DOWN);
-    DL_HIP(gemm(a, s));
+    DL_HIP(gemm(a, s, w.gpart, w.gpart_bytes));
     GemmArgs b{};
     b.nseg = 1;
     b.M = M;
@@ -1491,7 +1522,7 @@ static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_
     b.seg[0].R = w.x2f;
     b.seg[0].ldr = h;
     set_role(R_DOWN_UP);
-    DL_HIP(gemm(b, s));
+    DL_HIP(gemm(b, s, w.gpart, w.gpart_bytes));
   }
   return DL_OK;
 }

@@ -23,6 +23,9 @@
 // the linear index is remapped so each XCD runs a contiguous range of tiles,
 // taken in groups of kGroupM row tiles, so the CUs sharing an XCD's L2 share
 // activation rows and weight columns.
+#include <algorithm>
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 #include "trace.h"
@@ -39,17 +42,89 @@ constexpr int kGroupM = 4;
 constexpr int kEpPitch = 256 + 4;  // f32 row pitch of the epilogue's LDS rows
 constexpr int kEpRows = 32;        // rows per epilogue pass (one stage buffer)
 
-__device__ __forceinline__ void tile_of(int bid, int total, int tiles_m, int tiles_n, int &tm,
-                                        int &tn) {
-  // bijection: XCD x = bid % 8 runs logical tiles [start_x, start_x + count_x)
+// Linear tile index of workgroup `bid` among `total`: the XCD x = bid % 8
+// runs the contiguous range [start_x, start_x + count_x) (a bijection).
+__device__ __forceinline__ int xcd_linear(int bid, int total) {
   const int xcd = bid % kXcds, local = bid / kXcds;
   const int q = total / kXcds, rem = total % kXcds;
-  const int L = xcd < rem ? xcd * (q + 1) + local : rem * (q + 1) + (xcd - rem) * q + local;
+  return xcd < rem ? xcd * (q + 1) + local : rem * (q + 1) + (xcd - rem) * q + local;
+}
+
+// Linear tile index -> (row tile, column tile), in groups of kGroupM row tiles.
+__device__ __forceinline__ void tile_rc(int L, int tiles_m, int tiles_n, int &tm, int &tn) {
   const int per_group = kGroupM * tiles_n;
   const int g = L / per_group, w = L - g * per_group;
   const int gm = min(kGroupM, tiles_m - g * kGroupM);
   tn = w / gm;
   tm = g * kGroupM + (w - tn * gm);
+}
+
+__device__ __forceinline__ int seg_of(const GemmArgs &a, int tn) {
+  int si = 0;
+  if (a.nseg > 1 && tn >= a.seg[1].tile_begin) si = 1;
+  if (a.nseg > 2 && tn >= a.seg[2].tile_begin) si = 2;
+  return si;
+}
+
+// Applies the segment's output mode to the f32 results of row m, columns
+// n .. n + 7, and stores them.
+__device__ __forceinline__ void epi_store(const GemmArgs &a, const GemmSeg &sg, int m, int n,
+                                          float (&v)[8]) {
+  const int om = sg.omode;
+  if (om == GEMM_OUT_CACHE || om == GEMM_OUT_CACHE_T) {
+    // key cache page [kPage, N] / value cache page [N, kPage], operand tiles
+    const int b = m / a.T, pos = a.past_lens[b] + (m - b * a.T);
+    const int pg = cache_page(a.block_table, a.page_stride, b, pos / kPage);
+    uint16_t *pool = static_cast<uint16_t *>(sg.C);
+    if (om == GEMM_OUT_CACHE) {
+      *reinterpret_cast<u32x4 *>(pool + key_off(pg, pos, n, sg.N)) =
+          u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pool[val_off(pg, pos, n + e, sg.N)] = f2bf(v[e]);
+    }
+    return;
+  }
+  const size_t o = static_cast<size_t>(m) * sg.ldc + n;
+  if (om == GEMM_OUT_RELU) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = fmaxf(v[e], 0.f);
+  } else if (om == GEMM_OUT_SWIGLU) {
+    // each element of R is read and then overwritten by this thread only
+    const u32x4 gt = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(sg.R) +
+                                                      static_cast<size_t>(m) * sg.ldr + n);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] *= silu(bflo(gt[e]));
+      v[2 * e + 1] *= silu(bfhi(gt[e]));
+    }
+  } else if (om == GEMM_OUT_BF16_RES_F32) {
+    const float *rp = static_cast<const float *>(sg.R) + static_cast<size_t>(m) * sg.ldr + n;
+    const f32x4 r0 = *reinterpret_cast<const f32x4 *>(rp);
+    const f32x4 r1 = *reinterpret_cast<const f32x4 *>(rp + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] += r0[e];
+      v[4 + e] += r1[e];
+    }
+    if (sg.C32) {
+      *reinterpret_cast<f32x4 *>(sg.C32 + o) = f32x4{v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<f32x4 *>(sg.C32 + o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    }
+  } else if (om == GEMM_OUT_F32_RES_BF16) {
+    const u32x4 rb = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(sg.R) +
+                                                      static_cast<size_t>(m) * sg.ldr + n);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] += bflo(rb[e]);
+      v[2 * e + 1] += bfhi(rb[e]);
+    }
+    *reinterpret_cast<f32x4 *>(sg.C32 + o) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4 *>(sg.C32 + o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    return;
+  }
+  *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(sg.C) + o) =
+      u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
 }
 
 constexpr int kEpU4 = (kEpRows * kEpPitch + 3) / 4;  // epilogue rows in u32x4 units
@@ -62,12 +137,22 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
 
+  // Workgroups below a.full run whole tiles; the rest are the split units:
+  // unit u takes part u % split of the k tiles of tile a.full + u / split.
+  const int ktiles_all = a.K / BK;
+  int L, kbeg = 0, ktiles = ktiles_all, unit = -1;
+  if (static_cast<int>(blockIdx.x) < a.full) {
+    L = xcd_linear(blockIdx.x, a.full);
+  } else {
+    unit = blockIdx.x - a.full;
+    const int part = unit % a.split;
+    L = a.full + unit / a.split;
+    kbeg = part * ktiles_all / a.split;
+    ktiles = (part + 1) * ktiles_all / a.split - kbeg;
+  }
   int tm, tn;
-  tile_of(blockIdx.x, a.tiles_m * a.tiles_n, a.tiles_m, a.tiles_n, tm, tn);
-  int si = 0;
-  if (a.nseg > 1 && tn >= a.seg[1].tile_begin) si = 1;
-  if (a.nseg > 2 && tn >= a.seg[2].tile_begin) si = 2;
-  const GemmSeg &sg = a.seg[si];
+  tile_rc(L, a.tiles_m, a.tiles_n, tm, tn);
+  const GemmSeg &sg = a.seg[seg_of(a, tn)];
   const int n0 = (tn - sg.tile_begin) * BN;
   const int m0 = tm * BM;
   const int K = a.K;
@@ -83,9 +168,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   for (int i = 0; i < 2; ++i) {
     const int rb = wave + 8 * i;
     const int row = min(m0 + 16 * rb + (lane & 15), a.M - 1);
-    xp[i] = sg.X + static_cast<size_t>(row) * sg.ldx + 8 * (lane >> 4);
+    xp[i] = sg.X + static_cast<size_t>(row) * sg.ldx + 8 * (lane >> 4) + kbeg * BK;
     const int nb = min((n0 >> 4) + rb, nblk_last);
-    wp[i] = sg.W + frag_off(nb, 0, K, lane);
+    wp[i] = sg.W + frag_off(nb, kbeg, K, lane);
   }
   // direct-to-LDS staging of k tile kt into `dst`: unit i of this wave fills
   // the 1 KB fragment wave + 8 i of each operand
@@ -116,7 +201,6 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   // barrier. Near the end, the loads of tiles past the last reload the last
   // tile into a buffer that is not read again. The loop is unrolled by four
   // so every buffer is static.
-  const int ktiles = K / BK;
   // s_waitcnt vmcnt(8) lgkmcnt(0) (gfx9 encoding: vmcnt bits 3:0 and 15:14,
   // expcnt 6:4, lgkmcnt 11:8), then a barrier without a memory fence. The
   // builtin wait is visible to the compiler's own wait insertion.
@@ -173,7 +257,6 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   // output mode with 16-byte accesses. Lane (j, grp) of block (mb, nb) holds
   // C[128 wm + 16 mb + 4 grp + r][64 wn + 16 nb + j].
   const int j = lane & 15, grp = lane >> 4;
-  const int om = sg.omode;
   float *ep = reinterpret_cast<float *>(stage0);
   const int c8 = 8 * (tid & 31);
   const int n = n0 + c8;
@@ -198,66 +281,100 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
         const f32x4 lo = *reinterpret_cast<const f32x4 *>(ep + rr * kEpPitch + c8);
         const f32x4 hi = *reinterpret_cast<const f32x4 *>(ep + rr * kEpPitch + c8 + 4);
         float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        if (om == GEMM_OUT_CACHE || om == GEMM_OUT_CACHE_T) {
-          // key cache page [kPage, N] / value cache page [N, kPage], operand tiles
-          const int b = m / a.T, pos = a.past_lens[b] + (m - b * a.T);
-          const int pg = cache_page(a.block_table, a.page_stride, b, pos / kPage);
-          uint16_t *pool = static_cast<uint16_t *>(sg.C);
-          if (om == GEMM_OUT_CACHE) {
-            *reinterpret_cast<u32x4 *>(pool + key_off(pg, pos, n, sg.N)) =
-                u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pool[val_off(pg, pos, n + e, sg.N)] = f2bf(v[e]);
-          }
+        if (unit >= 0) {
+          // split unit: the f32 partial tile, row-major [BM, BN]
+          float *pp = a.part + (static_cast<size_t>(unit) * BM + kEpRows * p + rr) * BN + c8;
+          *reinterpret_cast<f32x4 *>(pp) = lo;
+          *reinterpret_cast<f32x4 *>(pp + 4) = hi;
           continue;
         }
-        const size_t o = static_cast<size_t>(m) * sg.ldc + n;
-        if (om == GEMM_OUT_RELU) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = fmaxf(v[e], 0.f);
-        } else if (om == GEMM_OUT_SWIGLU) {
-          // each element of R is read and then overwritten by this thread only
-          const u32x4 gt = *reinterpret_cast<const u32x4 *>(
-              static_cast<const uint16_t *>(sg.R) + static_cast<size_t>(m) * sg.ldr + n);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[2 * e] *= silu(bflo(gt[e]));
-            v[2 * e + 1] *= silu(bfhi(gt[e]));
-          }
-        } else if (om == GEMM_OUT_BF16_RES_F32) {
-          const float *rp = static_cast<const float *>(sg.R) + static_cast<size_t>(m) * sg.ldr + n;
-          const f32x4 r0 = *reinterpret_cast<const f32x4 *>(rp);
-          const f32x4 r1 = *reinterpret_cast<const f32x4 *>(rp + 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[e] += r0[e];
-            v[4 + e] += r1[e];
-          }
-          if (sg.C32) {
-            *reinterpret_cast<f32x4 *>(sg.C32 + o) = f32x4{v[0], v[1], v[2], v[3]};
-            *reinterpret_cast<f32x4 *>(sg.C32 + o + 4) = f32x4{v[4], v[5], v[6], v[7]};
-          }
-        } else if (om == GEMM_OUT_F32_RES_BF16) {
-          const u32x4 rb = *reinterpret_cast<const u32x4 *>(
-              static_cast<const uint16_t *>(sg.R) + static_cast<size_t>(m) * sg.ldr + n);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[2 * e] += bflo(rb[e]);
-            v[2 * e + 1] += bfhi(rb[e]);
-          }
-          *reinterpret_cast<f32x4 *>(sg.C32 + o) = f32x4{v[0], v[1], v[2], v[3]};
-          *reinterpret_cast<f32x4 *>(sg.C32 + o + 4) = f32x4{v[4], v[5], v[6], v[7]};
-          continue;
-        }
-        *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(sg.C) + o) =
-            u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
+        epi_store(a, sg, m, n, v);
       }
     }
     __syncthreads();
   }
 }
+
+// Sum of the split tiles' partials and the output mode: workgroup (i, rb)
+// takes rows 8 rb .. 8 rb + 7 of split tile i, thread t row t / 32 of them
+// and columns 8 (t % 32) .. +7; the parts are added in order.
+constexpr int kFixThreads = 256, kFixRows = kFixThreads / 32;
+__global__ __launch_bounds__(kFixThreads) void gemm_bf16_fixup_kernel(GemmArgs a) {
+  const int i = blockIdx.x / (BM / kFixRows), rb = blockIdx.x % (BM / kFixRows);
+  int tm, tn;
+  tile_rc(a.full + i, a.tiles_m, a.tiles_n, tm, tn);
+  const GemmSeg &sg = a.seg[seg_of(a, tn)];
+  const int row = rb * kFixRows + (threadIdx.x >> 5), c8 = 8 * (threadIdx.x & 31);
+  const int m = tm * BM + row, n = (tn - sg.tile_begin) * BN + c8;
+  if (m >= a.M || n >= sg.N) return;
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < a.split; ++q) {
+    const float *pp = a.part + (static_cast<size_t>(i * a.split + q) * BM + row) * BN + c8;
+    const f32x4 lo = *reinterpret_cast<const f32x4 *>(pp);
+    const f32x4 hi = *reinterpret_cast<const f32x4 *>(pp + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] += lo[e];
+      v[4 + e] += hi[e];
+    }
+  }
+  epi_store(a, sg, m, n, v);
+}
+
+// Compute units of the current device (256 when it cannot be asked).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Remainder split. With one workgroup per compute unit (the stage buffers
+// fill the LDS), `tiles` tiles run in rounds of C; the last round has only
+// r = tiles % C of them. Cutting each of those r tiles into s parts of its k
+// range gives r s units that take ceil(r s / C) rounds of 1 / s the length,
+// at the price of writing and re-reading an f32 partial tile per unit and a
+// fixup launch. Cost model in k steps of a whole tile (about 0.9 us at the
+// measured MFMA rate): a partial tile's 512 KB of traffic is about 0.1 of
+// one, the fixup launch about 5. The best s in 2..8 (each part at least 16
+// k steps) is taken when it saves at least 10 k steps.
+constexpr int kMaxSplit = 8, kMinPartK = 16;
+constexpr double kPartCost = 0.1, kFixCost = 5.0, kMinGain = 10.0;
+struct SplitPlan {
+  int full, split;
+};
+SplitPlan split_plan(int tiles, int ktiles) {
+  const int C = device_cus(), r = tiles % C;
+  SplitPlan p{tiles, 1};
+  if (r == 0) return p;
+  double best = kMinGain;
+  for (int s = 2; s <= kMaxSplit && ktiles / s >= kMinPartK; ++s) {
+    const int units = r * s, rounds = (units + C - 1) / C;
+    const double gain = ktiles * (1.0 - static_cast<double>(rounds) / s) - units * kPartCost - kFixCost;
+    if (gain > best) {
+      best = gain;
+      p.full = tiles - r;
+      p.split = s;
+    }
+  }
+  return p;
+}
 }  // namespace
+
+size_t gemm_part_bytes(int M, int ntiles_n, int K) {
+  if (M <= 0 || ntiles_n <= 0 || K < BK) return 0;
+  const int64_t tiles = static_cast<int64_t>(ntiles_n) * ((M + BM - 1) / BM);
+  if (tiles > INT32_MAX) return 0;
+  const SplitPlan p = split_plan(static_cast<int>(tiles), K / BK);
+  return static_cast<size_t>(tiles - p.full) * p.split * BM * BN * sizeof(float);
+}
 
 int gemm_ntiles(int N) { return (N + BN - 1) / BN; }
 
@@ -271,8 +388,23 @@ hipError_t launch_gemm_bf16(GemmArgs &a, hipStream_t s) {
   a.tiles_n = tiles;
   a.tiles_m = (a.M + BM - 1) / BM;
   const int64_t total = static_cast<int64_t>(a.tiles_n) * a.tiles_m;
-  if (total <= 0 || total > INT32_MAX) return hipErrorInvalidValue;
-  gemm_bf16_kernel<<<dim3(static_cast<unsigned>(total)), kThreads, 0, s>>>(a);
+  if (total <= 0 || total > INT32_MAX || a.K < BK) return hipErrorInvalidValue;
+  a.full = static_cast<int>(total);
+  a.split = 1;
+  const size_t need = gemm_part_bytes(a.M, a.tiles_n, a.K);
+  if (need > 0 && a.part && a.part_bytes >= need) {
+    const SplitPlan p = split_plan(static_cast<int>(total), a.K / BK);
+    a.full = p.full;
+    a.split = p.split;
+  }
+  const int64_t grid = a.full + static_cast<int64_t>(total - a.full) * a.split;
+  gemm_bf16_kernel<<<dim3(static_cast<unsigned>(grid)), kThreads, 0, s>>>(a);
+  if (a.split > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned fix = static_cast<unsigned>(total - a.full) * (BM / kFixRows);
+    gemm_bf16_fixup_kernel<<<dim3(fix), kFixThreads, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -139,11 +139,22 @@ struct GemmArgs {
   const int32_t *block_table;  // cache pages; NULL: contiguous
   int page_stride;
   int tiles_m, tiles_n;  // set by the launcher
+  // Remainder split: f32 partial tiles of the split units (NULL: no split).
+  // The launcher splits the k range of the tiles of an underfilled last
+  // round when gemm_part_bytes() of the shape is nonzero and fits.
+  float *part;
+  size_t part_bytes;
+  int full, split;       // set by the launcher: tiles run whole, parts per split tile
 };
 
-// Sets the segments' tile_begin and the tile counts, then launches.
+// Sets the segments' tile_begin and the tile counts, then launches (the
+// GEMM, and the fixup that sums split tiles' partials when it splits).
 hipError_t launch_gemm_bf16(GemmArgs &a, hipStream_t s);
 int gemm_ntiles(int N);
+// Partial-tile bytes the launcher needs to split a GEMM of M rows,
+// ntiles_n column tiles (the sum over segments of gemm_ntiles) and depth K
+// on the current device; 0 when it runs unsplit.
+size_t gemm_part_bytes(int M, int ntiles_n, int K);
 
 // ---------------------------------------------------------------------------
 // Attention over the low-rank cache (bf16 MFMA).

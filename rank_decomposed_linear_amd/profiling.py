@@ -46,6 +46,7 @@ KINDS = (
     ("latent_attn_kernel", "attn_latent"),
     ("latent_out_kernel", "attn_latent"),
     ("gemm_bf16_kernel", "gemm_bf16"),
+    ("gemm_bf16_fixup_kernel", "gemm_bf16"),
     ("gemm_f32_kernel", "gemm_f32"),
     ("attn_f32_kernel", "attn_f32"),
     ("pack_up_factor_kernel", "pack_up_factor"),

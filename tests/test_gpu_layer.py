@@ -119,6 +119,11 @@ SMALL = [
     ("gemv_decode", "bf16", 512, 8, 2, 128, 1024, 192, 128, 256, 4, 1, [0, 7, 100, 33], 128, 500000.0),
     ("gemv_prefill", "bf16", 256, 4, 2, 64, 512, 128, 64, 192, 2, 8, [0, 20], 64, 10000.0),
     ("gemm_prefill", "bf16", 512, 8, 2, 128, 768, 256, 128, 320, 2, 100, [0, 20], 192, 10000.0),
+    # hidden and FFN 4096 over 200 rows: the GEMMs with 4096-deep k ranges
+    # (the latent scatter into the caches among them) run as k parts plus a
+    # fixup that sums them
+    ("gemm_prefill_ksplit", "bf16", 4096, 8, 2, 128, 4096, 256, 128, 320, 2, 100, [0, 20], 192,
+     10000.0),
     ("gemm_decode_b80", "bf16", 256, 4, 1, 64, 512, 128, 64, 128, 80, 1, None, 64, 10000.0),
     ("gemv_decode_norope", "bf16", 512, 8, 2, 128, 1024, 192, 128, 256, 4, 1, [0, 7, 100, 33], 128, 0.0),
     ("gemm_decode_norope", "bf16", 256, 4, 1, 64, 512, 128, 64, 128, 80, 1, None, 64, 0.0),

@@ -49,6 +49,11 @@ LINEAR_CASES = [
     (300, 256, 128, 448, "bf16"),
     (128, 512, 64, 64, "bf16"),
     (600, 1024, 320, 1088, "bf16"),     # several 256 x 256 GEMM tiles, ragged in M and N
+    # long k ranges on few tiles: the GEMMs' k ranges are cut into parts
+    # whose f32 partials a fixup kernel sums (all tiles: fewer than one
+    # round; 2560 rows: 260 tiles of the first product, so a remainder of 4)
+    (300, 8192, 1088, 320, "bf16"),
+    (2560, 4096, 6656, 64, "bf16"),
     (2, 256, 64, 688, "f32"),
     (64, 688, 64, 256, "f32"),
     (100, 70, 9, 33, "f32"),
@@ -63,6 +68,16 @@ def test_lowrank_linear(B, M, m, k, n, dt):
     y = B.lowrank_linear(to_dev(x), to_dev(lib_f(A)), to_dev(lib_f(Bf)))
     want = ref.lowrank_linear(f64(x), f64(A), f64(Bf))
     assert relerr(to_host(y), want) <= TOL[dt]
+
+
+def test_lowrank_linear_split_plan(B):
+    """The prefill GEMMs of the long-k cases above do take the remainder
+    split: their workspace holds f32 partial tiles beyond the bf16
+    intermediate (the cut is chosen by the device's compute-unit count)."""
+    lib = B.load()
+    for M, m, k, n in [(300, 8192, 1088, 320), (2560, 4096, 6656, 64)]:
+        need = lib.dl_lowrank_linear_workspace(M, m, k, n, B.DL_BF16)
+        assert need >= M * k * 2 + 2 * 256 * 256 * 4, (M, m, k, n, need)
 
 
 @pytest.mark.parametrize("R", ["1", "2", "4"])
