@@ -66,11 +66,36 @@ __device__ __forceinline__ int seg_of(const GemmArgs &a, int tn) {
   return si;
 }
 
-// Applies the segment's output mode to the f32 results of row m, columns
-// n .. n + 7, and stores them.
+// Output modes that read a second operand R at the output positions.
+__host__ __device__ constexpr bool reads_r(int om) {
+  return om == GEMM_OUT_SWIGLU || om == GEMM_OUT_BF16_RES_F32 || om == GEMM_OUT_F32_RES_BF16;
+}
+
+// R at row m, columns n .. n + 7: 16 bytes of bf16 in r[0], or 32 bytes of
+// f32 in r[0], r[1].
+__device__ __forceinline__ void load_r(const GemmSeg &sg, int om, int m, int n, u32x4 (&r)[2]) {
+  if (om == GEMM_OUT_BF16_RES_F32) {
+    const u32x4 *rp = reinterpret_cast<const u32x4 *>(static_cast<const float *>(sg.R) +
+                                                      static_cast<size_t>(m) * sg.ldr + n);
+    r[0] = rp[0];
+    r[1] = rp[1];
+  } else if (om == GEMM_OUT_SWIGLU || om == GEMM_OUT_F32_RES_BF16) {
+    r[0] = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(sg.R) +
+                                            static_cast<size_t>(m) * sg.ldr + n);
+  }
+}
+
+// Applies the output mode to the f32 results of row m, columns n .. n + 7
+// (r: R there, from load_r, for the modes that read it), and stores them.
+// OM >= 0: every segment of the launch has mode OM, so only its code is
+// compiled (no other mode's loads whose pending registers would make the
+// compiler wait for every earlier store); OM < 0: the segment's own.
+// Results that are not read again soon are stored non-temporally (they
+// would otherwise evict the operand tiles the CUs of an XCD share from L2).
+template <int OM>
 __device__ __forceinline__ void epi_store(const GemmArgs &a, const GemmSeg &sg, int m, int n,
-                                          float (&v)[8]) {
-  const int om = sg.omode;
+                                          float (&v)[8], const u32x4 (&r)[2]) {
+  const int om = OM >= 0 ? OM : sg.omode;
   if (om == GEMM_OUT_CACHE || om == GEMM_OUT_CACHE_T) {
     // key cache page [kPage, N] / value cache page [N, kPage], operand tiles
     const int b = m / a.T, pos = a.past_lens[b] + (m - b * a.T);
@@ -90,44 +115,44 @@ __device__ __forceinline__ void epi_store(const GemmArgs &a, const GemmSeg &sg, 
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = fmaxf(v[e], 0.f);
   } else if (om == GEMM_OUT_SWIGLU) {
-    // each element of R is read and then overwritten by this thread only
-    const u32x4 gt = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(sg.R) +
-                                                      static_cast<size_t>(m) * sg.ldr + n);
+    // R (the gate values) may be C itself: each element is read and then
+    // overwritten by this thread only
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      v[2 * e] *= silu(bflo(gt[e]));
-      v[2 * e + 1] *= silu(bfhi(gt[e]));
+      v[2 * e] *= silu(bflo(r[0][e]));
+      v[2 * e + 1] *= silu(bfhi(r[0][e]));
     }
   } else if (om == GEMM_OUT_BF16_RES_F32) {
-    const float *rp = static_cast<const float *>(sg.R) + static_cast<size_t>(m) * sg.ldr + n;
-    const f32x4 r0 = *reinterpret_cast<const f32x4 *>(rp);
-    const f32x4 r1 = *reinterpret_cast<const f32x4 *>(rp + 4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      v[e] += r0[e];
-      v[4 + e] += r1[e];
+      v[e] += __uint_as_float(r[0][e]);
+      v[4 + e] += __uint_as_float(r[1][e]);
     }
     if (sg.C32) {
-      *reinterpret_cast<f32x4 *>(sg.C32 + o) = f32x4{v[0], v[1], v[2], v[3]};
-      *reinterpret_cast<f32x4 *>(sg.C32 + o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+      __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]},
+                                  reinterpret_cast<f32x4 *>(sg.C32 + o));
+      __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]},
+                                  reinterpret_cast<f32x4 *>(sg.C32 + o + 4));
     }
   } else if (om == GEMM_OUT_F32_RES_BF16) {
-    const u32x4 rb = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(sg.R) +
-                                                      static_cast<size_t>(m) * sg.ldr + n);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      v[2 * e] += bflo(rb[e]);
-      v[2 * e + 1] += bfhi(rb[e]);
+      v[2 * e] += bflo(r[0][e]);
+      v[2 * e + 1] += bfhi(r[0][e]);
     }
-    *reinterpret_cast<f32x4 *>(sg.C32 + o) = f32x4{v[0], v[1], v[2], v[3]};
-    *reinterpret_cast<f32x4 *>(sg.C32 + o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]},
+                                reinterpret_cast<f32x4 *>(sg.C32 + o));
+    __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]},
+                                reinterpret_cast<f32x4 *>(sg.C32 + o + 4));
     return;
   }
-  *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(sg.C) + o) =
-      u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
+  __builtin_nontemporal_store(
+      u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])},
+      reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(sg.C) + o));
 }
 
 constexpr int kEpU4 = (kEpRows * kEpPitch + 3) / 4;  // epilogue rows in u32x4 units
+template <int OM>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   __shared__ u32x4 stage0[kStage > kEpU4 ? kStage : kEpU4];
   __shared__ u32x4 stage1[kStage];
@@ -256,10 +281,33 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   // thread takes 8 consecutive columns of a row and applies the segment's
   // output mode with 16-byte accesses. Lane (j, grp) of block (mb, nb) holds
   // C[128 wm + 16 mb + 4 grp + r][64 wn + 16 nb + j].
+  // Pass barriers order LDS accesses only: s_waitcnt lgkmcnt(0), then
+  // s_barrier without a fence, so each pass's global stores stay in flight
+  // under the next pass (a fenced barrier waits for them).
+  auto bar_lds = [] {
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
   const int j = lane & 15, grp = lane >> 4;
   float *ep = reinterpret_cast<float *>(stage0);
   const int c8 = 8 * (tid & 31);
   const int n = n0 + c8;
+  // R of this thread's two rows of a pass, loaded one pass ahead (before the
+  // previous pass's stores, so waiting for it leaves those stores in flight)
+  constexpr bool kR = OM >= 0 && reads_r(OM);
+  u32x4 rq[2][2][2];
+  // (rows and columns clamped into R, so every load is issued and no
+  // branch splits the wait counting; clamped values are not used)
+  auto fetch_r = [&](int p, u32x4 (&dst)[2][2]) {
+#pragma unroll
+    for (int it = 0; it < kEpRows / 16; ++it) {
+      const int m = min(m0 + kEpRows * p + (tid >> 5) + 16 * it, a.M - 1);
+      load_r(sg, OM, m, min(n, sg.N - 8), dst[it]);
+    }
+  };
+  if constexpr (kR) fetch_r(0, rq[0]);
 #pragma unroll
   for (int p = 0; p < BM / kEpRows; ++p) {
     if (wm == (p >> 2)) {
@@ -271,7 +319,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
           for (int r = 0; r < 4; ++r)
             ep[(mh * 16 + 4 * grp + r) * kEpPitch + wn * 64 + nb * 16 + j] = acc[2 * (p & 3) + mh][nb][r];
     }
-    __syncthreads();
+    bar_lds();
+    if constexpr (kR) {
+      if (p + 1 < BM / kEpRows) fetch_r(p + 1, rq[(p + 1) & 1]);
+    }
     if (n < sg.N) {
 #pragma unroll
       for (int it = 0; it < kEpRows / 16; ++it) {
@@ -288,10 +339,16 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
           *reinterpret_cast<f32x4 *>(pp + 4) = hi;
           continue;
         }
-        epi_store(a, sg, m, n, v);
+        if constexpr (kR) {
+          epi_store<OM>(a, sg, m, n, v, rq[p & 1][it]);
+        } else {
+          u32x4 r[2];
+          load_r(sg, OM >= 0 ? OM : sg.omode, m, n, r);
+          epi_store<OM>(a, sg, m, n, v, r);
+        }
       }
     }
-    __syncthreads();
+    bar_lds();
   }
 }
 
@@ -318,7 +375,9 @@ __global__ __launch_bounds__(kFixThreads) void gemm_bf16_fixup_kernel(GemmArgs a
       v[4 + e] += hi[e];
     }
   }
-  epi_store(a, sg, m, n, v);
+  u32x4 r[2];
+  load_r(sg, sg.omode, m, n, r);
+  epi_store<-1>(a, sg, m, n, v, r);
 }
 
 // Compute units of the current device (256 when it cannot be asked).
@@ -398,7 +457,18 @@ hipError_t launch_gemm_bf16(GemmArgs &a, hipStream_t s) {
     a.split = p.split;
   }
   const int64_t grid = a.full + static_cast<int64_t>(total - a.full) * a.split;
-  gemm_bf16_kernel<<<dim3(static_cast<unsigned>(grid)), kThreads, 0, s>>>(a);
+  int om = a.seg[0].omode;
+  for (int i = 1; i < a.nseg; ++i)
+    if (a.seg[i].omode != om) om = -1;
+  const dim3 g(static_cast<unsigned>(grid));
+  switch (om) {
+    case GEMM_OUT_BF16: gemm_bf16_kernel<GEMM_OUT_BF16><<<g, kThreads, 0, s>>>(a); break;
+    case GEMM_OUT_SWIGLU: gemm_bf16_kernel<GEMM_OUT_SWIGLU><<<g, kThreads, 0, s>>>(a); break;
+    case GEMM_OUT_RELU: gemm_bf16_kernel<GEMM_OUT_RELU><<<g, kThreads, 0, s>>>(a); break;
+    case GEMM_OUT_BF16_RES_F32: gemm_bf16_kernel<GEMM_OUT_BF16_RES_F32><<<g, kThreads, 0, s>>>(a); break;
+    case GEMM_OUT_F32_RES_BF16: gemm_bf16_kernel<GEMM_OUT_F32_RES_BF16><<<g, kThreads, 0, s>>>(a); break;
+    default: gemm_bf16_kernel<-1><<<g, kThreads, 0, s>>>(a); break;
+  }
   if (a.split > 1) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
