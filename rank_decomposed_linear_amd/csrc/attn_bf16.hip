@@ -2,7 +2,9 @@
 // rebuild K = C_k B_k and V = C_v B_v from the cached latents, rotate the
 // rebuilt keys, attend).
 //
-// Neither K nor V is ever written to memory. Caches and factors are stored
+// The rebuilt K and V never leave the chip in decode; in prefill each
+// 64-key tile is rebuilt once into a workspace image that all query tiles
+// of its (sequence, kv head) then read. Caches and factors are stored
 // in 16 x 32 operand tiles (MFMA lane order): a key block of 16 positions x
 // 32 ranks and an up-factor fragment are each one contiguous 1 KB read; the
 // caches are held in pages of 64 positions (a key page [64, r_k], a value
@@ -10,11 +12,13 @@
 // contiguously, and a 64-key tile is exactly one page. The rebuilt tiles
 // live in MFMA accumulators:
 //
-//  prefill  A workgroup owns one kv head and up to 256 (token, head) query
-//           rows; per 64-key tile its eight waves rebuild K (rotated) and
-//           V^T into swizzled LDS from latents and factor slices staged in
-//           LDS, then each wave runs an online-softmax pass for its 32 query
-//           rows.
+//  prefill  A rebuild workgroup turns one 64-key tile of latents into its
+//           image: K (rotated) and V^T, swizzled, from latents and factor
+//           slices staged in LDS. An attention workgroup owns one kv head
+//           and up to 256 (token, head) query rows; per key tile it loads
+//           the image into LDS and each wave runs an online-softmax pass
+//           for its 32 query rows, its query fragments in registers and
+//           each K / V fragment read once for both of its 16-row blocks.
 #include <math.h>
 
 #include <algorithm>
@@ -265,7 +269,6 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
   constexpr int IMG = 2 * KT * D;           // elements of one key tile's image
   constexpr int NI = IMG / 8 / 512;         // 16-byte units per thread
   __shared__ __attribute__((aligned(16))) uint16_t KVs[2][IMG];   // double-buffered images
-  __shared__ u32x4 Qs[8 * 2 * HALF * 64];  // rotated, scaled query fragments of each wave
   __shared__ double revs[D / 2];
 
   // wave is made provably uniform, so every fragment index derived from it
@@ -296,11 +299,12 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
 
   for (int i = tid; i < D / 2; i += 512) revs[i] = rope_on ? rope_rev(i, D, a.theta) : 0.0;
 
-  // ---- query fragments: rows rho = 32*wave + 16*qb + (0..15), kept in
-  // LDS (fragment (wave, qb, t)) for the whole work item.
+  // ---- query fragments: rows rho = 32*wave + 16*qb + (0..15), rotated
+  // and scaled, kept in registers for the whole work item.
   // B operand of S^T = K Q^T: lane (q = j, grp) holds Q[q][32t + 8grp + e].
   int qpos[2];
   bool qok[2];
+  u32x4 qf[2][HALF];
   __syncthreads();
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -341,7 +345,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
     }
 #pragma unroll
     for (int t = 0; t < HALF; ++t)
-      Qs[((wave * 2 + qb) * HALF + t) * 64 + lane] = u32x4{pack2(x[t][0] * a.scale_log2, x[t][1] * a.scale_log2),
+      qf[qb][t] = u32x4{pack2(x[t][0] * a.scale_log2, x[t][1] * a.scale_log2),
                         pack2(x[t][2] * a.scale_log2, x[t][3] * a.scale_log2),
                         pack2(x[t][4] * a.scale_log2, x[t][5] * a.scale_log2),
                         pack2(x[t][6] * a.scale_log2, x[t][7] * a.scale_log2)};
@@ -355,6 +359,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
     for (int x = 0; x < DB; ++x) accO[qb][x] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int qmax_pos = past + min(t0 + QT, a.T) - 1;
+  const int qpos_lo = min(qpos[0], qpos[1]);  // this lane's earliest query position
   const int nkt = qmax_pos / KT + 1;
   const uint16_t *imgs = a.kv + (static_cast<size_t>(b) * a.n_kv + g) * (a.L_max / KT) * IMG;
   u32x4 st[NI];
@@ -367,7 +372,6 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
     for (int i = 0; i < NI; ++i) *reinterpret_cast<u32x4 *>(&KVs[buf][8 * (tid + 512 * i)]) = st[i];
   };
   iload(0);
-  __syncthreads();   // (Qs complete)
   istore(0);
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
@@ -375,31 +379,38 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
     if (kt + 1 < nkt) iload(kt + 1);   // in flight under this tile's work
     const uint16_t *Ks = KVs[kt & 1];
     const uint16_t *Vt = KVs[kt & 1] + KT * D;
-    // ---- attention for this wave's 32 query rows ----
-    // Swizzles depend on the row only through j (rows 16 kk + j, d rows
-    // 16 x + j), so each (t) or (u, half) needs one base and the key block /
-    // d block is a constant offset.
+    // ---- attention for this wave's 32 query rows (two blocks of 16) ----
+    // Each K and V fragment is read from LDS once and feeds the MFMAs of
+    // both query blocks. Swizzles depend on the row only through j (rows
+    // 16 kk + j, d rows 16 x + j), so each (t) or (u, half) needs one base
+    // and the key block / d block is a constant offset.
+    f32x4 sc[2][4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) sc[qb][kk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < HALF; ++t) {
+      const uint16_t *kp = Ks + j * D + (((4 * t + grp) ^ (j & (CH - 1))) * 8);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const u32x4 kf = *reinterpret_cast<const u32x4 *>(kp + 16 * kk * D);
+        sc[0][kk] = mfma_bf16(kf, qf[0][t], sc[0][kk]);
+        sc[1][kk] = mfma_bf16(kf, qf[1][t], sc[1][kk]);
+      }
+    }
+    // lane (q = j, grp) holds S^T[k0 + 16kk + 4grp + r][q]; only tiles that
+    // reach past a query's position need the causal mask
+    const bool diag = k0 + KT - 1 > qpos_lo;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      f32x4 sc[4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) sc[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int t = 0; t < HALF; ++t) {
-        const u32x4 qv = Qs[((wave * 2 + qb) * HALF + t) * 64 + lane];
-        const uint16_t *kp = Ks + j * D + (((4 * t + grp) ^ (j & (CH - 1))) * 8);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          sc[kk] = mfma_bf16(*reinterpret_cast<const u32x4 *>(kp + 16 * kk * D), qv, sc[kk]);
-      }
-      // lane (q = j, grp) holds S^T[k0 + 16kk + 4grp + r][q]
       float mx = -INFINITY;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          if (k0 + 16 * kk + 4 * grp + r > qpos[qb]) sc[kk][r] = -INFINITY;
-          mx = fmaxf(mx, sc[kk][r]);
+          if (diag && k0 + 16 * kk + 4 * grp + r > qpos[qb]) sc[qb][kk][r] = -INFINITY;
+          mx = fmaxf(mx, sc[qb][kk][r]);
         }
       mx = wave_max_xor(mx, 16);
       mx = wave_max_xor(mx, 32);
@@ -410,8 +421,8 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          sc[kk][r] = exp2f(sc[kk][r] - m_new);
-          psum += sc[kk][r];
+          sc[qb][kk][r] = exp2f(sc[qb][kk][r] - m_new);
+          psum += sc[qb][kk][r];
         }
       psum = wave_sum_xor(psum, 16);
       psum = wave_sum_xor(psum, 32);
@@ -419,17 +430,20 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
       m_run[qb] = m_new;
 #pragma unroll
       for (int x = 0; x < DB; ++x) accO[qb][x] *= alpha;
+    }
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const u32x4 pf = pack_acc(sc[2 * u], sc[2 * u + 1]);
-        const uint16_t *v0 = Vt + j * KT + (((8 * u + grp) ^ j) * 4);
-        const uint16_t *v1 = Vt + j * KT + (((8 * u + 4 + grp) ^ j) * 4);
+    for (int u = 0; u < 2; ++u) {
+      const u32x4 pf0 = pack_acc(sc[0][2 * u], sc[0][2 * u + 1]);
+      const u32x4 pf1 = pack_acc(sc[1][2 * u], sc[1][2 * u + 1]);
+      const uint16_t *v0 = Vt + j * KT + (((8 * u + grp) ^ j) * 4);
+      const uint16_t *v1 = Vt + j * KT + (((8 * u + 4 + grp) ^ j) * 4);
 #pragma unroll
-        for (int x = 0; x < DB; ++x) {
-          const u32x2 lo = *reinterpret_cast<const u32x2 *>(v0 + 16 * x * KT);
-          const u32x2 hi = *reinterpret_cast<const u32x2 *>(v1 + 16 * x * KT);
-          accO[qb][x] = mfma_bf16(u32x4{lo.x, lo.y, hi.x, hi.y}, pf, accO[qb][x]);
-        }
+      for (int x = 0; x < DB; ++x) {
+        const u32x2 lo = *reinterpret_cast<const u32x2 *>(v0 + 16 * x * KT);
+        const u32x2 hi = *reinterpret_cast<const u32x2 *>(v1 + 16 * x * KT);
+        const u32x4 vf = u32x4{lo.x, lo.y, hi.x, hi.y};
+        accO[0][x] = mfma_bf16(vf, pf0, accO[0][x]);
+        accO[1][x] = mfma_bf16(vf, pf1, accO[1][x]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
