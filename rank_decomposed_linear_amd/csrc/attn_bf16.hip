@@ -242,11 +242,15 @@ __global__ __launch_bounds__(512) void attn_rebuild_kernel(AttnPrefillArgs a) {
               u32x2{pack2(acc[kk][hh][0], acc[kk][hh][1]), pack2(acc[kk][hh][2], acc[kk][hh][3])};
         }
       } else {
+        // V^T row dd holds each 32-key half u with key 32u + 16hk + 4grp + r
+        // at 32u + 8grp + 4hk + r: the eight keys one lane of the P V
+        // product takes are one 16-byte chunk (4u + grp), XOR-swizzled by
+        // the row's low three bits
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int dd = 16 * (2 * pr + h) + j;
-          const int unit = (4 * kb + grp) ^ (dd & 15);
-          *reinterpret_cast<u32x2 *>(&Vt[dd * KT + unit * 4]) =
+          const int chunk = (4 * (kb >> 1) + grp) ^ (dd & 7);
+          *reinterpret_cast<u32x2 *>(&Vt[dd * KT + chunk * 8 + 4 * (kb & 1)]) =
               u32x2{pack2(acc[kk][h][0], acc[kk][h][1]), pack2(acc[kk][h][2], acc[kk][h][3])};
         }
       }
@@ -399,49 +403,62 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
         sc[1][kk] = mfma_bf16(kf, qf[1][t], sc[1][kk]);
       }
     }
-    // lane (q = j, grp) holds S^T[k0 + 16kk + 4grp + r][q]; only tiles that
-    // reach past a query's position need the causal mask
-    const bool diag = k0 + KT - 1 > qpos_lo;
+    // lane (q = j, grp) holds S^T[k0 + 16kk + 4grp + r][q]. Only tiles that
+    // reach past the wave's earliest query position (past + t0: its rows are
+    // tokens t0 .. t0 + 31 of one head) need the causal mask.
+    if (k0 + KT - 1 > past + t0) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (k0 + 16 * kk + 4 * grp + r > qpos[qb]) sc[qb][kk][r] = -INFINITY;
+    }
+    float alpha[2];
+    bool grew = false;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (diag && k0 + 16 * kk + 4 * grp + r > qpos[qb]) sc[qb][kk][r] = -INFINITY;
-          mx = fmaxf(mx, sc[qb][kk][r]);
-        }
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[qb][kk][r]);
       mx = wave_max_xor(mx, 16);
       mx = wave_max_xor(mx, 32);
       const float m_new = fmaxf(m_run[qb], mx);
-      const float alpha = exp2f(m_run[qb] - m_new);
+      grew |= m_new > m_run[qb];
+      alpha[qb] = exp2_hw(m_run[qb] - m_new);
       float psum = 0.f;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          sc[qb][kk][r] = exp2f(sc[qb][kk][r] - m_new);
+          sc[qb][kk][r] = exp2_hw(sc[qb][kk][r] - m_new);
           psum += sc[qb][kk][r];
         }
       psum = wave_sum_xor(psum, 16);
       psum = wave_sum_xor(psum, 32);
-      l_run[qb] = l_run[qb] * alpha + psum;
+      l_run[qb] = l_run[qb] * alpha[qb] + psum;
       m_run[qb] = m_new;
+    }
+    // the output rescale only when some row's running maximum rose
+    if (__builtin_amdgcn_ballot_w64(grew)) {
 #pragma unroll
-      for (int x = 0; x < DB; ++x) accO[qb][x] *= alpha;
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int x = 0; x < DB; ++x) accO[qb][x] *= alpha[qb];
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const u32x4 pf0 = pack_acc(sc[0][2 * u], sc[0][2 * u + 1]);
       const u32x4 pf1 = pack_acc(sc[1][2 * u], sc[1][2 * u + 1]);
-      const uint16_t *v0 = Vt + j * KT + (((8 * u + grp) ^ j) * 4);
-      const uint16_t *v1 = Vt + j * KT + (((8 * u + 4 + grp) ^ j) * 4);
+      // keys 32u + 4grp + r and 32u + 16 + 4grp + r of d row 16x + j: one
+      // swizzled chunk of the image
+      const uint16_t *vp = Vt + j * KT + 8 * ((4 * u + grp) ^ (j & 7));
 #pragma unroll
       for (int x = 0; x < DB; ++x) {
-        const u32x2 lo = *reinterpret_cast<const u32x2 *>(v0 + 16 * x * KT);
-        const u32x2 hi = *reinterpret_cast<const u32x2 *>(v1 + 16 * x * KT);
-        const u32x4 vf = u32x4{lo.x, lo.y, hi.x, hi.y};
+        const u32x4 vf = *reinterpret_cast<const u32x4 *>(vp + 16 * x * KT);
         accO[0][x] = mfma_bf16(vf, pf0, accO[0][x]);
         accO[1][x] = mfma_bf16(vf, pf1, accO[1][x]);
       }

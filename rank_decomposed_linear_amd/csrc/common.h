@@ -133,6 +133,11 @@ __device__ __forceinline__ double rope_rev(int i, int d, float theta) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
+// 2^x by the hardware instruction alone (v_exp_f32): results below the
+// normal range flush to zero, which softmax weights may do; exp2f adds a
+// range reduction for them (four more instructions per call).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Compile-time loop: f(IntC<0>{}), ..., f(IntC<N - 1>{}), so the index can
 // select register arrays and scheduling groups statically.
 template <int V>
