@@ -437,8 +437,8 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
           sc[qb][kk][r] = exp2_hw(sc[qb][kk][r] - m_new);
           psum += sc[qb][kk][r];
         }
-      psum = wave_sum_xor(psum, 16);
-      psum = wave_sum_xor(psum, 32);
+      // per-lane partial sums: the four lanes of a row share alpha, so they
+      // are added across lanes once, after the last tile
       l_run[qb] = l_run[qb] * alpha[qb] + psum;
       m_run[qb] = m_new;
     }
@@ -469,12 +469,15 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
   }
 
   // ---- normalise and store: lane (q = j, grp) holds O^T[16x + 4grp + r][q] ----
+  float lsum[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) lsum[qb] = wave_sum_xor(wave_sum_xor(l_run[qb], 16), 32);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     if (!qok[qb]) continue;
     const int rho = 32 * wave + 16 * qb + j;
     const int hl = rho / QT, tt = t0 + rho % QT;
-    const float inv = 1.f / l_run[qb];
+    const float inv = 1.f / lsum[qb];
     uint16_t *dst = a.out + (static_cast<size_t>(b) * a.T + tt) * a.n_q * D +
                     static_cast<size_t>(g * G + hl) * D;
 #pragma unroll

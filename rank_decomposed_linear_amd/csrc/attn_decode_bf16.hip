@@ -614,7 +614,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
     float m_new = m_run;
 #pragma unroll
     for (int wv = 0; wv < kNW; ++wv) m_new = fmaxf(m_new, smax[wv][j]);
-    const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+    const float alpha = m_run == -INFINITY ? 0.f : exp2_hw(m_run - m_new);
     m_run = m_new;
     float ps = 0.f;
     for (int u = wave; u < nU; u += kNW) {
@@ -629,7 +629,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(AttnDecodeArgs
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        v[e] = exp2f(j < G && c0 + off + e < c1 ? sv[e] - m_new : -INFINITY);
+        v[e] = exp2_hw(j < G && c0 + off + e < c1 ? sv[e] - m_new : -INFINITY);
         ps += v[e];
       }
       pbuf[u * 64 + lane] = u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
@@ -1030,7 +1030,7 @@ __global__ __launch_bounds__(64 * (PW + kNW), 1) void attn_decode_ws_kernel(Attn
         float m_new = m_run;
   #pragma unroll
         for (int wv = 0; wv < PW; ++wv) m_new = fmaxf(m_new, smax[t & 1][wv][j]);
-        const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+        const float alpha = m_run == -INFINITY ? 0.f : exp2_hw(m_run - m_new);
         m_run = m_new;
         l_part *= alpha;
   #pragma unroll
@@ -1049,7 +1049,7 @@ __global__ __launch_bounds__(64 * (PW + kNW), 1) void attn_decode_ws_kernel(Attn
           float v[8];
   #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            v[e] = exp2f(j < G && c0 + off + 8 * grp + e < c1 ? sv[e] - m_new : -INFINITY);
+            v[e] = exp2_hw(j < G && c0 + off + 8 * grp + e < c1 ? sv[e] - m_new : -INFINITY);
             l_part += v[e];
           }
           pbuf[u * 64 + lane] = u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};

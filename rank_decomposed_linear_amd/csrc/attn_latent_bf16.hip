@@ -261,7 +261,7 @@ __global__ __launch_bounds__(kThreads, 1) void latent_attn_kernel(LatentAttnArgs
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      v[e] = exp2f(off + e < npos && m_all != -INFINITY ? sv[e] - m_all : -INFINITY);
+      v[e] = exp2_hw(off + e < npos && m_all != -INFINITY ? sv[e] - m_all : -INFINITY);
       ps += v[e];
     }
     pbuf[u * 64 + lane] = u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
