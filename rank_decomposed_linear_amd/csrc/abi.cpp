@@ -511,6 +511,7 @@ hipError_t run_attn_bf16(const void *q, int q_f32, int ldq, const CacheRef &c,
   a.bv = static_cast<const uint16_t *>(B_v);
   a.past_lens = lens;
   a.out = static_cast<uint16_t *>(out);
+  a.out_tiled = out_tiled;
   a.kv = w.kv_tiles;
   a.Bsz = Bsz;
   a.T = T;
@@ -605,7 +606,7 @@ size_t dl_lowrank_linear_workspace(int64_t M, int64_t m, int64_t k, int64_t n, d
     c.take<float>(sc.part_floats);
     c.take<uint16_t>(mpad(M) * k);
   } else {
-    c.take<uint16_t>(static_cast<size_t>(M * k));
+    c.take<uint16_t>(mpad(M) * k);
     c.take<float>(pair_part_bytes(M, m, k, n) / sizeof(float));
   }
   return c.off;
@@ -661,7 +662,8 @@ dl_status dl_lowrank_linear(const void *x, const void *A, const void *B, void *y
                          roles, R_PAIR_CHAIN, s));
     return DL_OK;
   }
-  uint16_t *t = c.take<uint16_t>(static_cast<size_t>(M * k));
+  // the rank-k intermediate in operand tiles (M rounded up to 16 rows)
+  uint16_t *t = c.take<uint16_t>(mpad(M) * k);
   const size_t pb = pair_part_bytes(M, m, k, n);
   float *part = c.take<float>(pb / sizeof(float));
   GemmArgs a{};
@@ -671,12 +673,13 @@ dl_status dl_lowrank_linear(const void *x, const void *A, const void *B, void *y
   a.xmode = GEMM_X_BF16;
   a.omode = GEMM_OUT_BF16;
   a.seg[0] = mseg(A, x, t, ki, mi, ki);
+  a.seg[0].c_tiled = 1;
   DL_HIP(gemm(a, s, part, pb));
   GemmArgs b{};
   b.nseg = 1;
   b.M = Mi;
   b.K = ki;
-  b.xmode = GEMM_X_BF16;
+  b.xmode = GEMM_X_TILED;
   b.omode = GEMM_OUT_BF16;
   b.seg[0] = mseg(B, t, y, ni, ki, ni);
   DL_HIP(gemm(b, s, part, pb));
@@ -1187,17 +1190,19 @@ static void carve_layer(Carver &c, const LayerDims &D, const dl_layer *L, LayerW
     w.td16 = c.take<uint16_t>(Mp * D.rd);
     return;
   }
-  w.a16 = c.take<uint16_t>(M * D.h);
-  w.tq16 = c.take<uint16_t>(M * D.rq);
+  // operand-tiled activations: M rounded up to 16 rows
+  const size_t Mt = mpad(D.M);
+  w.a16 = c.take<uint16_t>(Mt * D.h);
+  w.tq16 = c.take<uint16_t>(Mt * D.rq);
   w.q16 = c.take<uint16_t>(M * D.qd());
-  w.att16 = c.take<uint16_t>(M * D.qd());
-  w.to16 = c.take<uint16_t>(M * D.ro);
+  w.att16 = c.take<uint16_t>(Mt * D.qd());
+  w.to16 = c.take<uint16_t>(Mt * D.ro);
   w.x2f = c.take<float>(M * D.h);
-  w.b16 = c.take<uint16_t>(M * D.h);
-  w.tg16 = c.take<uint16_t>(M * D.rg);
-  w.tu16 = c.take<uint16_t>(M * D.ru);
-  w.G16 = c.take<uint16_t>(M * D.f);
-  w.td16 = c.take<uint16_t>(M * D.rd);
+  w.b16 = c.take<uint16_t>(Mt * D.h);
+  w.tg16 = c.take<uint16_t>(Mt * D.rg);
+  w.tu16 = c.take<uint16_t>(Mt * D.ru);
+  w.G16 = c.take<uint16_t>(Mt * D.f);
+  w.td16 = c.take<uint16_t>(Mt * D.rd);
   // one partial buffer for the step's GEMMs (they run in order on one
   // stream): the largest need over their shapes, (column tiles, depth)
   const int nt = gemm_ntiles(D.rq) + gemm_ntiles(D.rk) + gemm_ntiles(D.rv);
@@ -1392,9 +1397,11 @@ static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_
     return DL_OK;
   }
 
-  // bf16 GEMM path
+  // bf16 GEMM path. Every activation the step produces and a GEMM reads is
+  // stored in operand tiles (a16, tq16, att16, to16, b16, tg16, tu16, G16,
+  // td16), so the GEMMs stage each activation fragment as one contiguous 1 KB.
   set_role(R_ATTN_NORM);
-  DL_HIP(launch_rmsnorm(x, 0, L->attn_norm, gf32, w.a16, 0, M, h, eps, s));
+  DL_HIP(launch_rmsnorm(x, 0, L->attn_norm, gf32, w.a16, RMS_Y_TILED, M, h, eps, s));
   {
     // the concatenated down factors [A_q, A_k, A_v] in one launch; the k
     // and v segments scatter their latents into the caches
@@ -1407,7 +1414,9 @@ static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_
     a.T = D.T;
     a.block_table = cache.table;
     a.page_stride = cache.stride;
+    a.xmode = GEMM_X_TILED;
     a.seg[0] = mseg(L->q.A, w.a16, w.tq16, D.rq, h, D.rq);
+    a.seg[0].c_tiled = 1;
     a.seg[1] = mseg(L->k.A, w.a16, Ck, D.rk, h, D.rk);
     a.seg[1].omode = GEMM_OUT_CACHE;
     a.seg[2] = mseg(L->v.A, w.a16, Cv, D.rv, h, D.rv);
@@ -1419,6 +1428,7 @@ static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_
     q.M = M;
     q.K = D.rq;
     q.omode = GEMM_OUT_BF16;
+    q.xmode = GEMM_X_TILED;
     q.seg[0] = mseg(L->q.B, w.tq16, w.q16, qd, D.rq, qd);
     set_role(R_Q_UP);
     DL_HIP(gemm(q, s, w.gpart, w.gpart_bytes));
@@ -1430,7 +1440,7 @@ static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_
     DL_HIP(launch_fill(z, 1, s));
     set_role(R_ATTENTION);
   }
-  DL_HIP(run_attn_bf16(w.q16, 0, qd, cache, L->k.B, L->v.B, past_lens, 1, D.T == 1, w.att16, 0, 0,
+  DL_HIP(run_attn_bf16(w.q16, 0, qd, cache, L->k.B, L->v.B, past_lens, 1, D.T == 1, w.att16, 0, 1,
                        D.Bsz, D.T, D.nq, D.nkv, D.d, D.rk, D.rv, 0.f, L->rope_theta, aw, s));
   {
     GemmArgs a{};
@@ -1438,7 +1448,9 @@ static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_
     a.M = M;
     a.K = qd;
     a.omode = GEMM_OUT_BF16;
+    a.xmode = GEMM_X_TILED;
     a.seg[0] = mseg(L->o.A, w.att16, w.to16, D.ro, qd, D.ro);
+    a.seg[0].c_tiled = 1;
     set_role(R_O_DOWN);
     DL_HIP(gemm(a, s, w.gpart, w.gpart_bytes));
     GemmArgs b{};
@@ -1446,6 +1458,7 @@ static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_
     b.M = M;
     b.K = D.ro;
     b.omode = GEMM_OUT_F32_RES_BF16;
+    b.xmode = GEMM_X_TILED;
     b.seg[0] = mseg(L->o.B, w.to16, nullptr, h, D.ro, h);
     b.seg[0].C32 = w.x2f;
     b.seg[0].R = x;
@@ -1459,7 +1472,7 @@ static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_
     DL_HIP(launch_fill(cp, 1, s));
   }
   set_role(R_MLP_NORM);
-  DL_HIP(launch_rmsnorm(w.x2f, 1, L->mlp_norm, gf32, w.b16, 0, M, h, eps, s));
+  DL_HIP(launch_rmsnorm(w.x2f, 1, L->mlp_norm, gf32, w.b16, RMS_Y_TILED, M, h, eps, s));
   {
     GemmArgs a{};
     a.nseg = D.relu ? 1 : 2;
@@ -1472,6 +1485,8 @@ static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_
       a.seg[0] = mseg(L->gate.A, w.b16, w.tg16, D.rg, h, D.rg);
       a.seg[1] = mseg(L->up.A, w.b16, w.tu16, D.ru, h, D.ru);
     }
+    a.xmode = GEMM_X_TILED;
+    a.seg[0].c_tiled = a.seg[1].c_tiled = 1;
     set_role(R_GATE_UP_DOWN);
     DL_HIP(gemm(a, s, w.gpart, w.gpart_bytes));
   }
@@ -1482,7 +1497,9 @@ static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_
     a.M = M;
     a.K = D.ru;
     a.omode = GEMM_OUT_RELU;
+    a.xmode = GEMM_X_TILED;
     a.seg[0] = mseg(L->up.B, w.tu16, w.G16, D.f, D.ru, D.f);
+    a.seg[0].c_tiled = 1;
     set_role(R_GATE_UP_UP);
     DL_HIP(gemm(a, s, w.gpart, w.gpart_bytes));
   } else {
@@ -1493,12 +1510,15 @@ static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_
     a.M = M;
     a.K = D.rg;
     a.omode = GEMM_OUT_BF16;
+    a.xmode = GEMM_X_TILED;
     a.seg[0] = mseg(L->gate.B, w.tg16, w.G16, D.f, D.rg, D.f);
+    a.seg[0].c_tiled = 1;
     set_role(R_GATE_UP_UP);
     DL_HIP(gemm(a, s, w.gpart, w.gpart_bytes));
     a.K = D.ru;
     a.omode = GEMM_OUT_SWIGLU;
     a.seg[0] = mseg(L->up.B, w.tu16, w.G16, D.f, D.ru, D.f);
+    a.seg[0].c_tiled = a.seg[0].r_tiled = 1;
     a.seg[0].R = w.G16;
     a.seg[0].ldr = D.f;
     DL_HIP(gemm(a, s, w.gpart, w.gpart_bytes));
@@ -1508,9 +1528,10 @@ static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_
     a.nseg = 1;
     a.M = M;
     a.K = D.f;
-    a.xmode = GEMM_X_BF16;
+    a.xmode = GEMM_X_TILED;
     a.omode = GEMM_OUT_BF16;
     a.seg[0] = mseg(L->down.A, w.G16, w.td16, D.rd, D.f, D.rd);
+    a.seg[0].c_tiled = 1;
     set_role(R_DOWN_DOWN);
     DL_HIP(gemm(a, s, w.gpart, w.gpart_bytes));
     GemmArgs b{};
@@ -1518,6 +1539,7 @@ static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_
     b.M = M;
     b.K = D.rd;
     b.omode = GEMM_OUT_BF16_RES_F32;
+    b.xmode = GEMM_X_TILED;
     b.seg[0] = mseg(L->down.B, w.td16, y, h, D.rd, h);
     b.seg[0].R = w.x2f;
     b.seg[0].ldr = h;

@@ -478,13 +478,18 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnPrefillArgs a) {
     const int rho = 32 * wave + 16 * qb + j;
     const int hl = rho / QT, tt = t0 + rho % QT;
     const float inv = 1.f / lsum[qb];
-    uint16_t *dst = a.out + (static_cast<size_t>(b) * a.T + tt) * a.n_q * D +
-                    static_cast<size_t>(g * G + hl) * D;
+    // row b T + tt, columns (g G + hl) D + 16 x + 4 grp .. +3: four
+    // contiguous elements row-major and in operand tiles alike
+    const int orow = b * a.T + tt, ocol = (g * G + hl) * D + 4 * grp;
+    const int ncol = a.n_q * D;
 #pragma unroll
-    for (int x = 0; x < DB; ++x)
-      *reinterpret_cast<u32x2 *>(dst + 16 * x + 4 * grp) =
+    for (int x = 0; x < DB; ++x) {
+      const size_t o = a.out_tiled ? tile_off(orow, ocol + 16 * x, ncol)
+                                   : static_cast<size_t>(orow) * ncol + ocol + 16 * x;
+      *reinterpret_cast<u32x2 *>(a.out + o) =
           u32x2{pack2(accO[qb][x][0] * inv, accO[qb][x][1] * inv),
                 pack2(accO[qb][x][2] * inv, accO[qb][x][3] * inv)};
+    }
   }
 }
 

@@ -66,11 +66,20 @@ __device__ __forceinline__ void load8(const void *p, int f32, size_t i, float v[
   }
 }
 
+// Row of workgroup `bid` among M: the hardware deals workgroups to the
+// eight XCDs round-robin; XCD x takes a contiguous range of rows, so the 16
+// rows of an operand tile are written through one L2 (a bijection).
+__device__ __forceinline__ int xcd_row(int bid, int M) {
+  const int xcd = bid & 7, local = bid >> 3, q = M >> 3, rem = M & 7;
+  return xcd < rem ? xcd * (q + 1) + local : rem * (q + 1) + (xcd - rem) * q + local;
+}
+
 __global__ __launch_bounds__(256) void rmsnorm_vec_kernel(const void *x, int x_f32, const void *gamma,
-                                                          int gamma_f32, void *y, int y_f32, int n,
+                                                          int gamma_f32, void *y, int y_mode, int n,
                                                           float eps) {
   __shared__ float part[4];
-  const size_t base = static_cast<size_t>(blockIdx.x) * n;
+  const int row = xcd_row(blockIdx.x, gridDim.x);
+  const size_t base = static_cast<size_t>(row) * n;
   const int nc = n >> 3;
   float v[kNormCache][8];
   float ss = 0.f;
@@ -98,10 +107,14 @@ __global__ __launch_bounds__(256) void rmsnorm_vec_kernel(const void *x, int x_f
     if (gamma) load8(gamma, gamma_f32, 8 * static_cast<size_t>(c), gm);
 #pragma unroll
     for (int e = 0; e < 8; ++e) t[e] = t[e] * rstd * (gamma ? gm[e] : 1.f);
-    if (y_f32) {
+    if (y_mode == RMS_Y_F32) {
       float *o = static_cast<float *>(y) + base + 8 * c;
       *reinterpret_cast<f32x4 *>(o) = f32x4{t[0], t[1], t[2], t[3]};
       *reinterpret_cast<f32x4 *>(o + 4) = f32x4{t[4], t[5], t[6], t[7]};
+    } else if (y_mode == RMS_Y_TILED) {
+      // the eight columns 8c .. 8c + 7 of this row are contiguous in its tile
+      *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(y) + tile_off(row, 8 * c, n)) =
+          u32x4{pack2(t[0], t[1]), pack2(t[2], t[3]), pack2(t[4], t[5]), pack2(t[6], t[7])};
     } else {
       *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(y) + base + 8 * c) =
           u32x4{pack2(t[0], t[1]), pack2(t[2], t[3]), pack2(t[4], t[5]), pack2(t[6], t[7])};
@@ -251,13 +264,15 @@ int grid_for(int64_t n) {
 }  // namespace
 
 hipError_t launch_rmsnorm(const void *x, int x_f32, const void *gamma, int gamma_f32, void *y,
-                          int y_f32, int M, int n, float eps, hipStream_t s) {
+                          int y_mode, int M, int n, float eps, hipStream_t s) {
   TraceGuard trace_guard(K_RMSNORM, s);
   const auto a16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
-  if (n % 8 == 0 && a16(x) && a16(y) && (!gamma || a16(gamma)))
-    rmsnorm_vec_kernel<<<M, 256, 0, s>>>(x, x_f32, gamma, gamma_f32, y, y_f32, n, eps);
+  const bool vec = n % 8 == 0 && a16(x) && a16(y) && (!gamma || a16(gamma));
+  if (y_mode == RMS_Y_TILED && (!vec || n % 32 != 0)) return hipErrorInvalidValue;
+  if (vec)
+    rmsnorm_vec_kernel<<<M, 256, 0, s>>>(x, x_f32, gamma, gamma_f32, y, y_mode, n, eps);
   else
-    rmsnorm_kernel<<<M, 256, 0, s>>>(x, x_f32, gamma, gamma_f32, y, y_f32, n, eps);
+    rmsnorm_kernel<<<M, 256, 0, s>>>(x, x_f32, gamma, gamma_f32, y, y_mode, n, eps);
   return hipGetLastError();
 }
 

@@ -9,9 +9,13 @@
 // 1 KB, lane l at byte 16 l), so every operand read is one conflict-free
 // ds_read_b128 of a contiguous 1 KB and every staging write is one too. The
 // factors already live in that order in HBM (Wt [N, K] in 16 x 32 tiles): a
-// weight tile's k step is 16 contiguous 1 KB fragments. Activation rows are
-// row-major: lane l of a staging load fetches row (l % 16), k columns
-// 8 (l / 16) .. +7 of its fragment. Staging is direct to LDS
+// weight tile's k step is 16 contiguous 1 KB fragments. Activations that
+// the layer produces itself are stored in the same tiles, so their
+// fragments are contiguous too (16 rows x 64 bytes per fragment in
+// row-major activations touch half of 16 cache lines, and staging them cost
+// about a tenth of the GEMM's rate); row-major activations from the caller
+// are read with lane l fetching row (l % 16), k columns 8 (l / 16) .. +7 of
+// its fragment. Staging is direct to LDS
 // (global_load_lds_dwordx4: lane l of a wave lands at byte 16 l of the
 // wave's 1 KB destination), so no registers or LDS store instructions carry
 // it. Four separately declared 32 KB stage buffers (the compiler then sees
@@ -80,8 +84,8 @@ __device__ __forceinline__ void load_r(const GemmSeg &sg, int om, int m, int n, 
     r[0] = rp[0];
     r[1] = rp[1];
   } else if (om == GEMM_OUT_SWIGLU || om == GEMM_OUT_F32_RES_BF16) {
-    r[0] = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(sg.R) +
-                                            static_cast<size_t>(m) * sg.ldr + n);
+    const size_t o = sg.r_tiled ? tile_off(m, n, sg.ldr) : static_cast<size_t>(m) * sg.ldr + n;
+    r[0] = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(sg.R) + o);
   }
 }
 
@@ -146,9 +150,12 @@ __device__ __forceinline__ void epi_store(const GemmArgs &a, const GemmSeg &sg, 
                                 reinterpret_cast<f32x4 *>(sg.C32 + o + 4));
     return;
   }
+  // bf16 C: the eight columns n .. n + 7 of row m are contiguous in both
+  // layouts
+  const size_t oc = sg.c_tiled ? tile_off(m, n, sg.ldc) : o;
   __builtin_nontemporal_store(
       u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])},
-      reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(sg.C) + o));
+      reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(sg.C) + oc));
 }
 
 constexpr int kEpU4 = (kEpRows * kEpPitch + 3) / 4;  // epilogue rows in u32x4 units
@@ -186,14 +193,24 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   // operands, i = 0..1: row block wave + 8 i of the 32-wide k tile.
   // Out-of-range rows and weight rows are clamped (their results are never
   // stored), so every load is issued.
+  // Row-major X: lane l fetches row (l % 16), k columns 8 (l / 16) .. +7 of
+  // the fragment (16 rows x 64 bytes); tiled X: the fragment is one
+  // contiguous 1 KB, lane l its bytes 16 l .. 16 l + 15.
   const uint16_t *xp[2];
   const uint16_t *wp[2];
   const int nblk_last = (sg.N >> 4) - 1;
+  const bool xt = a.xmode == GEMM_X_TILED;
+  const int xstep = xt ? 512 : BK;   // elements from one k tile to the next
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int rb = wave + 8 * i;
-    const int row = min(m0 + 16 * rb + (lane & 15), a.M - 1);
-    xp[i] = sg.X + static_cast<size_t>(row) * sg.ldx + 8 * (lane >> 4) + kbeg * BK;
+    if (xt) {
+      const int rbk = min((m0 >> 4) + rb, (a.M - 1) >> 4);
+      xp[i] = sg.X + frag_off(rbk, kbeg, sg.ldx, lane);
+    } else {
+      const int row = min(m0 + 16 * rb + (lane & 15), a.M - 1);
+      xp[i] = sg.X + static_cast<size_t>(row) * sg.ldx + 8 * (lane >> 4) + kbeg * BK;
+    }
     const int nb = min((n0 >> 4) + rb, nblk_last);
     wp[i] = sg.W + frag_off(nb, kbeg, K, lane);
   }
@@ -204,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   auto dma = [&](u32x4 *dst, int kt) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      __builtin_amdgcn_global_load_lds((gptr)(xp[i] + kt * BK),
+      __builtin_amdgcn_global_load_lds((gptr)(xp[i] + static_cast<size_t>(kt) * xstep),
                                        (lptr)(dst + (wave + 8 * i) * 64), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((gptr)(wp[i] + static_cast<size_t>(kt) * 512),
                                        (lptr)(dst + kFrags * 64 + (wave + 8 * i) * 64), 16, 0,

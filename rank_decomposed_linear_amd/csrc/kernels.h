@@ -105,7 +105,9 @@ hipError_t launch_gemv_chain(const GvChain &c, hipStream_t s);
 // three segments.
 // ---------------------------------------------------------------------------
 enum GemmX : int {
-  GEMM_X_BF16 = 0      // X bf16 [M, ldx]
+  GEMM_X_BF16 = 0,     // X bf16 [M, ldx]
+  GEMM_X_TILED = 1     // X bf16 operand tiles [M rounded up to 16, ldx = K]: each 16-row, 32-k
+                       // fragment is one contiguous 1 KB (rows past M are read, never stored)
 };
 enum GemmOut : int {
   GEMM_OUT_BF16 = 0,        // C bf16 [M, ldc]
@@ -126,6 +128,8 @@ struct GemmSeg {
   int N, ldx, ldc, ldr;
   int omode;          // GemmOut of this segment
   int tile_begin;     // first N tile of this segment (set by the launcher)
+  int c_tiled;        // bf16 C stored as operand tiles [M rounded up to 16, ldc]
+  int r_tiled;        // bf16 R read from operand tiles [M rounded up to 16, ldr]
 };
 
 struct GemmArgs {
@@ -223,7 +227,8 @@ struct AttnPrefillArgs {
   int64_t pool_pages;  // pages in each pool (bounds the 32-bit buffer offsets)
   const uint16_t *bk, *bv;  // [n_kv * d, r] in operand tiles
   const int32_t *past_lens;
-  uint16_t *out;       // [Bsz, T, n_q*d]
+  uint16_t *out;       // [Bsz, T, n_q*d]; out_tiled: operand tiles [Bsz*T rounded up to 16, n_q*d]
+  int out_tiled;
   uint16_t *kv;        // workspace: rebuilt key tiles, [Bsz, n_kv, L_max / 64, 2 * 64 * d]
                        // (per 64-key tile: K rows rotated and swizzled, then V^T rows)
   int Bsz, T, n_q, n_kv, d, r_k, r_v, L_max;
@@ -272,10 +277,13 @@ hipError_t launch_attn_f32(const AttnF32Args &a, hipStream_t s);
 // ---------------------------------------------------------------------------
 // Elementwise helpers.
 // ---------------------------------------------------------------------------
-// y[M, n] = x / rms(x) * gamma; x and y are bf16 or f32 (flags), gamma is
-// in the storage dtype of the layer (gamma_f32) or NULL.
+// y[M, n] = x / rms(x) * gamma; x is bf16 or f32 (flag); y is bf16 (y_mode
+// RMS_Y_BF16), f32 (RMS_Y_F32) or bf16 operand tiles [M rounded up to 16, n]
+// (RMS_Y_TILED, n % 8 == 0); gamma is in the storage dtype of the layer
+// (gamma_f32) or NULL.
+enum RmsY : int { RMS_Y_BF16 = 0, RMS_Y_F32 = 1, RMS_Y_TILED = 2 };
 hipError_t launch_rmsnorm(const void *x, int x_f32, const void *gamma, int gamma_f32, void *y,
-                          int y_f32, int M, int n, float eps, hipStream_t s);
+                          int y_mode, int M, int n, float eps, hipStream_t s);
 // Up to four f32 regions: region i gets zero (src == NULL) or a copy of a
 // bf16 source (src_bf16 != NULL) or an f32 source. With tile_cols > 0 the
 // region is instead a bf16 operand-tile copy: src bf16 row-major
