@@ -521,15 +521,16 @@ def measured_peaks(torch, binding):
 
     copy_ms = best_ms(lambda: dst.copy_(src), 5)
     del src, dst
-    blocks, iters = 256 * 8, 4096
-    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
-    flops = blocks * 4 * iters * 8 * 16384
+    blocks, iters = 256 * 4, 2048
+    sink = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+    flops = blocks * 8 * iters * 32 * 16384
     mfma_ms = best_ms(lambda: binding.probe_mfma_bf16(sink, blocks, iters), 3)
     return {"hbm_copy_GB_per_s": round(2 * n / (copy_ms * 1e-3) / 1e9, 1),
             "mfma_bf16_TFLOP_per_s": round(flops / (mfma_ms * 1e-3) / 1e12, 1),
             "method": "1 GiB device copy, (read + write) bytes / time, best of 5; "
-                      "dl_probe_mfma_bf16 with 2048 workgroups x 4 waves x 4096 rounds of 8 "
-                      "independent 16x16x32 bf16 MFMAs, best of 3"}
+                      "dl_probe_mfma_bf16 with 1024 workgroups x 8 waves x 2048 rounds of 12 "
+                      "LDS operand reads and 32 independent 16x16x32 bf16 MFMAs (the prefill "
+                      "GEMM's mix, random operands), best of 3"}
 
 
 def with_measured(roof, peaks):

@@ -380,12 +380,14 @@ const char *dl_role_name(int32_t role);
 
 /* ------------------------------------------------------------------------
  * Matrix-pipe probe (measurement aid; not part of the method).
- * Launches `blocks` workgroups of four waves; every wave issues `iters`
- * rounds of eight independent v_mfma_f32_16x16x32_bf16 (16384 flops each),
- * so the work is blocks * 4 * iters * 8 * 16384 flops with no dependent
- * issue stalls: timing it gives the bf16 MFMA rate this GPU sustains, the
- * measured denominator reported next to the published peak.
- * sink: caller-owned device float[blocks * 256], overwritten (the values
+ * Launches `blocks` workgroups of eight waves; every wave runs `iters`
+ * rounds of twelve 1 KB operand reads from LDS and 32 independent
+ * v_mfma_f32_16x16x32_bf16 (16384 flops each) into an 8 x 4 block of
+ * accumulators, the prefill GEMM's mix, on random operands that change from
+ * round to round. The work is blocks * 8 * iters * 32 * 16384 flops: timing
+ * it gives the bf16 MFMA rate this GPU sustains for such a mix, the measured
+ * denominator reported next to the published peak.
+ * sink: caller-owned device float[blocks * 512], overwritten (the values
  * only keep the products live). Asynchronous on `stream`.
  * Errors: DL_ERR_INVALID_ARG for a null sink or blocks / iters outside
  * [1, 2^31); DL_ERR_HIP on a launch failure.

@@ -258,9 +258,9 @@ def _ws(nbytes: int, device) -> torch.Tensor:
 def probe_mfma_bf16(sink, blocks, iters):
     """dl_probe_mfma_bf16 on the current stream of sink's device; returns
     the flops the launch performs."""
-    assert sink.dtype == torch.float32 and sink.numel() >= blocks * 256
+    assert sink.dtype == torch.float32 and sink.numel() >= blocks * 512
     _check(load().dl_probe_mfma_bf16(_ptr(sink), blocks, iters, _stream(sink.device)))
-    return blocks * 4 * iters * 8 * 16384
+    return blocks * 8 * iters * 32 * 16384
 
 
 def lowrank_linear(x, At, Bt, y=None, ws=None):

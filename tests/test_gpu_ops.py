@@ -230,10 +230,10 @@ def test_explicit_softmax_scale(B):
 def test_mfma_probe(B):
     """The matrix-pipe probe runs, writes every sink entry, and reports its flops."""
     import torch
-    sink = torch.full((64 * 256,), float("nan"), dtype=torch.float32, device="cuda:0")
+    sink = torch.full((64 * 512,), float("nan"), dtype=torch.float32, device="cuda:0")
     flops = B.probe_mfma_bf16(sink, 64, 16)
     torch.cuda.synchronize()
-    assert flops == 64 * 4 * 16 * 8 * 16384
+    assert flops == 64 * 8 * 16 * 32 * 16384
     assert torch.isfinite(sink).all().item()
 
 
