@@ -152,7 +152,7 @@ def mfma_table(pmc_db: str, trace_db: str, command: str, peak_tflops: float,
         dur[(short_name(name), gx // max(wx, 1), gy, gz)].append(d * 1e-9)
     out = [f"# bf16 MFMA work from counters: {command}",
            f"# rate = counter flops per launch / average duration of the same kernel and grid in the kernel trace;",
-           f"# fractions of the published {peak_tflops:.0f} TFLOP/s and of the measured 16x16x32 rate "
+           f"# fractions of the published {peak_tflops:.0f} TFLOP/s and of the measured 16x16x32 GEMM-mix rate "
            f"{measured_tflops:.0f} TFLOP/s",
            "# kernel (workgroups x, y, z): launches, TFLOP per launch, average us, TFLOP/s, published, measured",
            ""]
