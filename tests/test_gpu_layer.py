@@ -125,6 +125,9 @@ SMALL = [
     ("gemm_prefill_ksplit", "bf16", 4096, 8, 2, 128, 4096, 256, 128, 320, 2, 100, [0, 20], 192,
      10000.0),
     ("gemm_decode_b80", "bf16", 256, 4, 1, 64, 512, 128, 64, 128, 80, 1, None, 64, 10000.0),
+    # beyond 512 sequences decode runs on the GEMM path (tiled activations
+    # from the decode attention into the o pair)
+    ("gemm_decode_b520", "bf16", 256, 4, 1, 64, 512, 128, 64, 128, 520, 1, None, 64, 10000.0),
     ("gemv_decode_norope", "bf16", 512, 8, 2, 128, 1024, 192, 128, 256, 4, 1, [0, 7, 100, 33], 128, 0.0),
     ("gemm_decode_norope", "bf16", 256, 4, 1, 64, 512, 128, 64, 128, 80, 1, None, 64, 0.0),
     ("f32_prefill", "f32", 96, 4, 2, 16, 160, 24, 12, 40, 3, 6, [0, 2, 9], 20, 100.0),
