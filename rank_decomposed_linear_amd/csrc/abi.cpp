@@ -1233,9 +1233,16 @@ bool chunked_decode(const dl_layer *L, int64_t Bsz, int64_t T) {
 
 size_t dl_layer_workspace(const dl_layer *L, int64_t Bsz, int64_t T, int64_t L_max) {
   if (chunked_decode(L, Bsz, T)) {
+    // one chunk's workspace, then the batch's queries, attention output and
+    // attention workspace (the carve of layer_impl's chunked branch)
     LayerDims D{};
     if (layer_dims(L, Bsz, T, L_max, &D) != DL_OK) return 0;
-    return dl_layer_workspace(L, kDecodeChunk, T, L_max);
+    Carver c(nullptr);
+    c.take<char>(dl_layer_workspace(L, kDecodeChunk, T, L_max));
+    c.take<float>(static_cast<size_t>(Bsz * D.qd()));
+    c.take<uint16_t>(mpad(Bsz) * D.qd());
+    carve_attn(c, D.Bsz, D.nq, D.nkv, D.d, D.rk, D.rv, D.L_max, true);
+    return c.off;
   }
   LayerDims D{};
   if (layer_dims(L, Bsz, T, L_max, &D) != DL_OK) return 0;
@@ -1247,19 +1254,39 @@ size_t dl_layer_workspace(const dl_layer *L, int64_t Bsz, int64_t T, int64_t L_m
   return c.off;
 }
 
+// Phases of a small-M (GEMV) layer step: the norm and the q / k / v chain,
+// the attention, the o / MLP chain. A chunked decode runs the first and the
+// last per chunk and the attention once over all chunks.
+enum { PH_PRE = 1, PH_ATTN = 2, PH_POST = 4, PH_ALL = 7 };
+
 static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_out,
                             const CacheRef &cache, const int32_t *past_lens, int64_t Bsz,
-                            int64_t T, void *ws, size_t ws_bytes, void *stream) {
+                            int64_t T, void *ws, size_t ws_bytes, void *stream, int phases = PH_ALL,
+                            float *q_ext = nullptr, uint16_t *att_ext = nullptr,
+                            const AttnWS *aw_zero = nullptr) {
   const int64_t L_max = cache.L_max;
   LayerDims D{};
   dl_status st = layer_dims(L, Bsz, T, L_max, &D);
   if (st != DL_OK) return st;
   DL_CHECK(x && y && cache.k && cache.v && past_lens, DL_ERR_INVALID_ARG, "null pointer");
   if (chunked_decode(L, Bsz, T)) {
-    // chunks of kDecodeChunk sequences in order on the stream; each sees its
-    // rows of x, y, x2_out and past_lens, and its pages of the cache
+    // Chunks of kDecodeChunk sequences: each chunk's norm and q / k / v chain
+    // (its queries into one buffer for the batch), then one attention launch
+    // over every sequence (a fuller GPU than one per chunk), then each
+    // chunk's o / MLP chain on its rows of the attention output. A chunk sees
+    // its rows of x, y, x2_out and past_lens and its pages of the cache; the
+    // chunks reuse one per-chunk workspace in stream order.
+    const size_t chunk_ws = dl_layer_workspace(L, kDecodeChunk, T, L_max);
+    const int64_t qd = D.qd();
+    Carver cw(ws);
+    cw.take<char>(chunk_ws);
+    float *q_all = cw.take<float>(static_cast<size_t>(Bsz * qd));
+    uint16_t *att_all = cw.take<uint16_t>(mpad(Bsz) * qd);
+    const AttnWS aw_all = carve_attn(cw, D.Bsz, D.nq, D.nkv, D.d, D.rk, D.rv, D.L_max, true);
+    DL_CHECK(ws && aligned16(ws) && ws_bytes >= cw.off, DL_ERR_WORKSPACE,
+             "workspace of %zu bytes required, %zu given", cw.off, ws_bytes);
     const int64_t h = L->hidden;
-    for (int64_t b0 = 0; b0 < Bsz; b0 += kDecodeChunk) {
+    auto chunk = [&](int64_t b0, int ph) {
       const int64_t nb = std::min(kDecodeChunk, Bsz - b0);
       CacheRef c = cache;
       if (c.table) {
@@ -1269,11 +1296,21 @@ static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_
         c.v = static_cast<uint16_t *>(c.v) + b0 * c.stride * kPage * L->v.k;
         c.pool_pages = nb * c.stride;
       }
-      st = layer_impl(L, static_cast<const uint16_t *>(x) + b0 * h, static_cast<uint16_t *>(y) + b0 * h,
-                      x2_out ? static_cast<float *>(x2_out) + b0 * h : nullptr, c, past_lens + b0, nb,
-                      T, ws, ws_bytes, stream);
-      if (st != DL_OK) return st;
-    }
+      // the batch buffers: queries f32 row-major, attention output in operand
+      // tiles (b0 is a multiple of 16, so a chunk's tiles start at row b0)
+      return layer_impl(L, static_cast<const uint16_t *>(x) + b0 * h, static_cast<uint16_t *>(y) + b0 * h,
+                        x2_out ? static_cast<float *>(x2_out) + b0 * h : nullptr, c, past_lens + b0, nb,
+                        T, ws, chunk_ws, stream, ph, q_all + b0 * qd, att_all + b0 * qd,
+                        b0 == 0 ? &aw_all : nullptr);
+    };
+    for (int64_t b0 = 0; b0 < Bsz; b0 += kDecodeChunk)
+      if ((st = chunk(b0, PH_PRE)) != DL_OK) return st;
+    set_role(R_ATTENTION);
+    DL_HIP(run_attn_bf16(q_all, 1, static_cast<int>(qd), cache, L->k.B, L->v.B, past_lens, 1, true,
+                         att_all, 0, 1, D.Bsz, D.T, D.nq, D.nkv, D.d, D.rk, D.rv, 0.f, L->rope_theta,
+                         aw_all, as_stream(stream)));
+    for (int64_t b0 = 0; b0 < Bsz; b0 += kDecodeChunk)
+      if ((st = chunk(b0, PH_POST)) != DL_OK) return st;
     return DL_OK;
   }
   void *Ck = cache.k, *Cv = cache.v;
@@ -1371,29 +1408,47 @@ static dl_status layer_impl(const dl_layer *L, const void *x, void *y, void *x2_
   }
 
   if (use_gemv(M)) {
+    // a chunk of a chunked decode: the batch's query and attention buffers
+    if (q_ext) w.q32 = q_ext;
+    if (att_ext) w.att16 = att_ext;
     GvArgs g[G_NUM];
     layer_gemvs(L, D, w, x, y, x2_out, cache, past_lens, g);
-    FillRegion zero[2] = {{reinterpret_cast<float *>(w.counters), nullptr, 0, w.n_counters},
-                          {reinterpret_cast<float *>(aw.counters), nullptr, 0, aw.n_counters}};
-    set_role(R_INIT);
-    DL_HIP(launch_norm_tiles(static_cast<const uint16_t *>(x), L->attn_norm, L->dt == DL_F32,
-                             L->rms_eps, w.a16t, M, static_cast<int>(mpad(M)), h, zero,
-                             aw.counters ? 2 : 1, s));
-    // [A_q A_k A_v] then B_q as one chain (the query latents stay on chip)
     const bool fuse = fuse_mode() == FUSE_ALL;
     static const int roles[G_NUM] = {R_QKV_DOWN, R_Q_UP, R_O_DOWN, R_O_UP,
                                      R_GATE_UP_DOWN, R_GATE_UP_UP, R_DOWN_DOWN, R_DOWN_UP};
-    DL_HIP(gemv_sequence(&g[G_QKV], 2, w.part, w.counters, w.chain_sync, 1, fuse, &roles[G_QKV],
-                         R_QKV_CHAIN, s));
-    set_role(R_ATTENTION);
-    DL_HIP(run_attn_bf16(w.q32, 1, qd, cache, L->k.B, L->v.B, past_lens, 1, D.T == 1, w.att16, 0,
-                         D.T == 1 ? 1 : 0, D.Bsz, D.T, D.nq, D.nkv, D.d, D.rk, D.rv, 0.f,
-                         L->rope_theta, aw, s));
-    // the o pair, the MLP norm, the gate/up pairs with SwiGLU and the down
-    // pair: six dependent GEMV stages in one chain (two runs when the
-    // attention output arrives row-major, T > 1)
-    DL_HIP(gemv_sequence(&g[G_ODOWN], 6, w.part, w.counters, w.chain_sync + kChainSyncInts, 2, fuse,
-                         &roles[G_ODOWN], R_O_MLP_CHAIN, s));
+    if (phases & PH_PRE) {
+      // the attention counters zeroed here are those of the launch that
+      // follows: this step's, or the batch's (first chunk of a chunked decode)
+      const AttnWS &az = aw_zero ? *aw_zero : aw;
+      FillRegion zero[2] = {{reinterpret_cast<float *>(w.counters), nullptr, 0, w.n_counters},
+                            {reinterpret_cast<float *>(az.counters), nullptr, 0, az.n_counters}};
+      set_role(R_INIT);
+      DL_HIP(launch_norm_tiles(static_cast<const uint16_t *>(x), L->attn_norm, L->dt == DL_F32,
+                               L->rms_eps, w.a16t, M, static_cast<int>(mpad(M)), h, zero,
+                               az.counters ? 2 : 1, s));
+      // [A_q A_k A_v] then B_q as one chain (the query latents stay on chip)
+      DL_HIP(gemv_sequence(&g[G_QKV], 2, w.part, w.counters, w.chain_sync, 1, fuse, &roles[G_QKV],
+                           R_QKV_CHAIN, s));
+    }
+    if (phases & PH_ATTN) {
+      set_role(R_ATTENTION);
+      DL_HIP(run_attn_bf16(w.q32, 1, qd, cache, L->k.B, L->v.B, past_lens, 1, D.T == 1, w.att16, 0,
+                           D.T == 1 ? 1 : 0, D.Bsz, D.T, D.nq, D.nkv, D.d, D.rk, D.rv, 0.f,
+                           L->rope_theta, aw, s));
+    }
+    if (phases & PH_POST) {
+      if (!(phases & PH_PRE)) {
+        // other chunks' chains ran since this chunk's counters were zeroed
+        FillRegion z[1] = {{reinterpret_cast<float *>(w.counters), nullptr, 0, w.n_counters}};
+        set_role(R_INIT);
+        DL_HIP(launch_fill(z, 1, s));
+      }
+      // the o pair, the MLP norm, the gate/up pairs with SwiGLU and the down
+      // pair: six dependent GEMV stages in one chain (two runs when the
+      // attention output arrives row-major, T > 1)
+      DL_HIP(gemv_sequence(&g[G_ODOWN], 6, w.part, w.counters, w.chain_sync + kChainSyncInts, 2,
+                           fuse, &roles[G_ODOWN], R_O_MLP_CHAIN, s));
+    }
     return DL_OK;
   }
 
