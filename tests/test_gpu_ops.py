@@ -54,6 +54,9 @@ LINEAR_CASES = [
     # round; 2560 rows: 260 tiles of the first product, so a remainder of 4)
     (300, 8192, 1088, 320, "bf16"),
     (2560, 4096, 6656, 64, "bf16"),
+    # 17 x 32 tiles of the second product: more than two rounds of tiles
+    # over the compute units, ragged in M and N, four k tiles each
+    (4100, 1024, 128, 8000, "bf16"),
     (2, 256, 64, 688, "f32"),
     (64, 688, 64, 256, "f32"),
     (100, 70, 9, 33, "f32"),
